@@ -1,0 +1,368 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV decode hot path on one MI355X.
+
+A step is one decode step of a Qwen3-4B-like model's attention over all 36
+layers: for each layer, ``pkv_append`` of the batch's new K/V rows and
+``pkv_decode`` of one query row per entry (batch 64, 32 query / 8 KV heads,
+head_dim 128, page_size 16, lengths log-uniform in [64, 4096]).  Inputs are
+seeded synthetic data resident in HBM before timing starts.  The step is
+captured once as a HIP graph and replayed.
+
+Printed: ONE JSON line with the whole-step throughput (algorithmic bytes per
+second), the decode kernel's roofline figures measured live with HIP events on
+its own stream, and the fp64 oracle timed on the host cores on a bounded
+sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--chunk-pages P] [--no-cpu-baseline]
+                  [--no-check] [--probe-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + decode rows/sec"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--chunk-pages", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU work of the oracle baseline sample")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--probe-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter scale)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def probe_copy(torch):
+    """Plain device-to-device copy of a known size, for counter calibration."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = 20
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n,
+                      "ms": dt * 1e3, "GBs": 2 * n / dt / 1e9}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if args.probe_copy:
+        probe_copy(torch)
+        return 0
+
+    import paged_kv_decode_pkv_amd as pkv
+    import workloads
+
+    spec = workloads.CONFIGS[args.config]
+    table = workloads.make_table(spec)
+    nl, b = spec.num_layers, table.batch
+    hq, hkv, d, ps = spec.num_qo_heads, spec.num_kv_heads, spec.head_dim, spec.page_size
+    dev = torch.device("cuda:0")
+    log(f"workload {spec.name}: batch {b}, layers {nl}, pool {table.num_pages} pages, "
+        f"max pages/entry {table.max_pages_per_req}")
+
+    # ---- inputs, resident in HBM before timing
+    cache = torch.zeros((nl, table.num_pages, 2, ps, hkv, d), dtype=torch.bfloat16,
+                        device=dev)
+    Q = torch.empty((nl, b, hq, d), dtype=torch.bfloat16, device=dev)
+    KN = torch.empty((nl, b, hkv, d), dtype=torch.bfloat16, device=dev)
+    VN = torch.empty_like(KN)
+    offs = workloads.k_offsets(spec)
+    for layer in range(nl):
+        q, kn, vn = workloads.draw_layer_device(cache[layer], table,
+                                                [1000 * spec.cfg + layer, b], hq,
+                                                spec.sigma, offs)
+        Q[layer], KN[layer], VN[layer] = q, kn, vn
+    tabs = [torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
+            for x in (table.indptr, table.indices, table.last_len)]
+    out = torch.empty((nl, b, hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((nl, b, hq), dtype=torch.float32, device=dev)
+    maxp = table.max_pages_per_req
+    chunk = args.chunk_pages or pkv.default_chunk_pages()
+    ws_bytes = pkv.workspace_size(b, hq, d, maxp, chunk)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs resident: cache {cache.numel() * 2 / 2**30:.1f} GiB, "
+        f"chunk {chunk} pages, workspace {ws_bytes / 2**20:.1f} MiB")
+
+    # ---- pre-marshalled C-ABI calls (the binding's arguments, built once)
+    desc = pkv.cache_desc(cache)
+    vp = ctypes.c_void_p
+    tab_ptrs = [vp(t.data_ptr()) for t in tabs]
+
+    def calls_for(stream_handle):
+        s = vp(stream_handle)
+        app, dec = [], []
+        for layer in range(nl):
+            app.append((vp(cache.data_ptr()), desc, layer, vp(KN[layer].data_ptr()),
+                        vp(VN[layer].data_ptr()), *tab_ptrs, b, s))
+            dec.append((vp(cache.data_ptr()), desc, layer, vp(Q[layer].data_ptr()), hq,
+                        *tab_ptrs, b, ctypes.c_float(spec.sm_scale),
+                        vp(out[layer].data_ptr()), vp(lse[layer].data_ptr()), maxp, chunk,
+                        vp(ws.data_ptr()), ws.numel(), s))
+        return app, dec
+
+    def run_step(app, dec, events=None):
+        for layer in range(nl):
+            rc = pkv.lib.pkv_append(*app[layer])
+            if rc:
+                raise pkv.PkvError(rc, "pkv_append")
+            if events is not None:
+                events[layer][0].record()
+            rc = pkv.lib.pkv_decode(*dec[layer])
+            if rc:
+                raise pkv.PkvError(rc, "pkv_decode")
+            if events is not None:
+                events[layer][1].record()
+
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        app, dec = calls_for(stream.cuda_stream)
+        for _ in range(2):
+            run_step(app, dec)
+    torch.cuda.synchronize()
+
+    # ---- the step as one HIP graph
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            capp, cdec = calls_for(cap.cuda_stream)
+            run_step(capp, cdec)
+        torch.cuda.synchronize()
+
+    def replay():
+        if graph is not None:
+            graph.replay()
+        else:
+            run_step(app, dec)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            replay()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+    with torch.cuda.stream(stream):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(args.steps):
+            replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ms_step_ev = e0.elapsed_time(e1) / args.steps
+    log(f"step: {ms_step:.4f} ms wall, {ms_step_ev:.4f} ms events")
+
+    # ---- live per-launch timing of pkv_decode (events on its own stream)
+    ksteps = max(1, min(args.steps, 20))
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(nl)] for _ in range(ksteps)]
+    with torch.cuda.stream(stream):
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(20_000_000)   # let the host queue run ahead of the GPU
+        for k in range(ksteps):
+            run_step(app, dec, events=evs[k])
+    torch.cuda.synchronize()
+    durs = np.array([[a.elapsed_time(z) for a, z in row] for row in evs]) * 1e3   # us
+    dec_us = float(durs.mean())
+
+    by = workloads.algorithmic_bytes(table, hq, hkv, d)
+    step_bytes = nl * by["total"]
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    rows_per_s = int(table.active.sum()) / (ms_step * 1e-3)
+    dec_gbs = by["decode"] / (dec_us * 1e-6) / 1e9
+    log(f"decode launch avg {dec_us:.2f} us -> {dec_gbs:.0f} GB/s algorithmic; "
+        f"step {gbs:.0f} GB/s")
+
+    result = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": spec.name, "batch": b, "active": int(table.active.sum()),
+                   "layers": nl, "num_qo_heads": hq, "num_kv_heads": hkv, "head_dim": d,
+                   "page_size": ps, "lengths": "log-uniform [64, 4096]",
+                   "kv_chunk_pages": chunk, "hip_graph": graph is not None,
+                   "step_bytes": step_bytes},
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "decode_rows_per_s": round(rows_per_s, 1),
+        "ms_per_step_events": round(ms_step_ev, 5),
+        "roofline": {"bound": "hbm", "kernel": "pkv_decode (split pass + LSE merge)",
+                     "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": by["decode"], "avg_launch_us": round(dec_us, 3),
+                     "launches": int(durs.size)},
+    }
+
+    if not args.no_check:
+        result["parity"] = check_sample(spec, table, cache, Q, KN, VN, out, lse, torch)
+        log(f"parity on sampled rows: {result['parity']}")
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(spec, table, cache, Q, KN, VN, torch,
+                                              args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def _host_entries(table, cache_layer, entries, torch):
+    """Compact host copy of some entries' pages (ids renumbered from 1)."""
+    pages = [table.indices[table.indptr[e]:table.indptr[e + 1]] for e in entries]
+    flat = np.concatenate(pages).astype(np.int64)
+    hp = cache_layer[torch.from_numpy(flat).to(cache_layer.device)]
+    hp = hp.view(torch.int16).cpu().numpy().view(np.uint16)
+    mini = np.zeros((1, 1 + len(flat)) + hp.shape[1:], dtype=np.uint16)
+    mini[0, 1:] = hp
+    indptr = np.concatenate([[0], np.cumsum([len(p) for p in pages])]).astype(np.int32)
+    indices = np.arange(1, 1 + len(flat), dtype=np.int32)
+    last = np.asarray(table.last_len)[list(entries)].astype(np.int32)
+    return mini, indptr, indices, last
+
+
+def _u16(t):
+    return t.contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+
+
+def check_sample(spec, table, cache, Q, KN, VN, out, lse, torch):
+    """Sampled rows of the benchmarked step against the oracle (layers 0, mid, last).
+
+    The timed steps re-append the same rows, so the cache now holds the
+    post-append state; the oracle appends again (a no-op on those bytes) from
+    the same k_new / v_new."""
+    import oracle
+    from workloads import bf16_to_f32
+    act = np.flatnonzero(table.active)
+    order = act[np.argsort(table.lengths[act])]
+    entries = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+    heads = [0, spec.num_qo_heads // 2, spec.num_qo_heads - 1]
+    worst = {"out_max": 0.0, "out_mean": 0.0, "lse_max": 0.0, "rows": 0}
+    for layer in sorted({0, spec.num_layers // 2, spec.num_layers - 1}):
+        mini, ip, ix, ll = _host_entries(table, cache[layer], entries, torch)
+        oracle.append(mini, 0, _u16(KN[layer])[entries], _u16(VN[layer])[entries], ip, ix,
+                      ll)
+        rb = np.repeat(np.arange(len(entries)), len(heads))
+        rh = np.tile(heads, len(entries))
+        ro, rl = oracle.decode_rows(mini, 0, _u16(Q[layer])[entries], ip, ix, ll,
+                                    spec.sm_scale, rb, rh)
+        eb = np.asarray(entries)[rb]
+        og = bf16_to_f32(_u16(out[layer])[eb, rh]).astype(np.float64)
+        lg = lse[layer].cpu().numpy()[eb, rh].astype(np.float64)
+        e = np.abs(og - ro)
+        worst["out_max"] = max(worst["out_max"], float(e.max()))
+        worst["out_mean"] = max(worst["out_mean"], float(e.mean()))
+        worst["lse_max"] = max(worst["lse_max"], float(np.abs(lg - rl).max()))
+        worst["rows"] += len(rb)
+    worst["pass"] = bool(worst["out_max"] <= 1e-2 and worst["out_mean"] <= 1e-3
+                         and worst["lse_max"] <= 1e-3)
+    return worst
+
+
+def cpu_baseline(spec, table, cache, Q, KN, VN, torch, seconds):
+    """The fp64 oracle (as it stands) on a bounded sample of the workload.
+
+    Sample: layer 0, every query head of a seeded random subset of active
+    entries sized to roughly ``seconds`` of single-thread work; the entries run
+    concurrently on a thread pool (the oracle releases the GIL).  The rate uses
+    the same algorithmic-byte formula as the GPU figure."""
+    import oracle
+    hq, hkv, d = spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
+    rng = np.random.default_rng(11)
+    act = rng.permutation(np.flatnonzero(table.active))
+    # calibrate: one short entry, all heads
+    e0 = int(act[0])
+    mini, ip, ix, ll = _host_entries(table, cache[0], [e0], torch)
+    q0 = _u16(Q[0])[[e0]]
+    t = time.perf_counter()
+    oracle.decode(mini, 0, q0, ip, ix, ll, spec.sm_scale)
+    per_token = (time.perf_counter() - t) / float(table.lengths[e0])
+    threads = max(1, min(16, os.cpu_count() or 1))
+    budget_tokens = seconds * threads / max(per_token, 1e-9)
+    chosen, tot = [], 0
+    for e in act:
+        if tot >= budget_tokens and chosen:
+            break
+        chosen.append(int(e))
+        tot += int(table.lengths[e])
+    qh = _u16(Q[0])
+    kn, vn = _u16(KN[0]), _u16(VN[0])
+    jobs = []
+    for e in chosen:
+        mini, ip, ix, ll = _host_entries(table, cache[0], [e], torch)
+        jobs.append((mini, ip, ix, ll, qh[[e]], kn[[e]], vn[[e]]))
+
+    def run(job):
+        mini, ip, ix, ll, q, k, v = job
+        oracle.append(mini, 0, k, v, ip, ix, ll)
+        oracle.decode(mini, 0, q, ip, ix, ll, spec.sm_scale)
+
+    t = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(run, jobs))
+    dt = time.perf_counter() - t
+    lens = table.lengths[chosen]
+    nbytes = (int(lens.sum()) * 2 * hkv * d * 2 + len(chosen) * hq * d * 2 * 2
+              + len(chosen) * hq * 4 + len(chosen) * 2 * 2 * hkv * d * 2)
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"layer 0, all {hq} query heads of {len(chosen)} of "
+                      f"{int(table.active.sum())} active entries ({int(lens.sum())} "
+                      f"tokens), append + fp64 decode, {dt:.1f} s on {threads} threads",
+            "decode_rows_per_s_equiv": round(len(chosen) / dt / spec.num_layers, 3),
+            "cpu_model": cpu_model}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

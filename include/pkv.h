@@ -1,0 +1,175 @@
+/*
+ * pkv.h -- C ABI of libpkv: paged-KV append and decode attention on MI355X.
+ *
+ * The operation is the decode step of a speech-token LM served from a paged
+ * KV cache, as the vox-serve "Adding a Model" page describes it: each layer
+ * writes this step's keys and values into the paged cache
+ * (set_kv_cache(kv_cache, k, v)) and then attends one query row per request
+ * over that request's pages (run(q, kv_cache)); section 1 "The model code"
+ * fixes the cache layout, and "How a program runs" fixes the per-step KV page
+ * tables and the padding entries that point at scratch KV page 0.
+ *
+ * Conventions shared by every call:
+ *  - Pointers are DEVICE pointers unless a parameter says "host".  The caller
+ *    owns every buffer; the library keeps no pointer after a call returns.
+ *  - Calls only validate host-side arguments and enqueue kernels on `stream`.
+ *    They never synchronise, never read device memory from the host and never
+ *    allocate, so they may be captured into a HIP graph.
+ *  - Invalid host arguments return a negative pkv_status_t before anything is
+ *    enqueued.  A failed launch returns PKV_ERR_HIP.  No C++ exception crosses
+ *    this boundary.  batch == 0 is a no-op that returns PKV_OK.
+ *  - Device-side preconditions are the caller's (checked on host copies by
+ *    pkv_validate_page_table, never on the fast path): every entry lists at
+ *    least one page, 1 <= last_page_len <= page_size, page ids lie in
+ *    [0, num_pages), and no entry lists more than max_pages_per_req pages.
+ *  - bf16 means IEEE bfloat16 stored as 16-bit words; every bf16 array and the
+ *    cache must be 16-byte aligned.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_NULL_PTR = -1,    /* a required pointer is NULL                  */
+    PKV_ERR_BAD_SHAPE = -2,   /* a size, index or scale is out of range      */
+    PKV_ERR_UNSUPPORTED = -3, /* valid but not built: head_dim, group, ...   */
+    PKV_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required  */
+    PKV_ERR_HIP = -5,         /* the HIP runtime refused a launch            */
+    PKV_ERR_ALIGNMENT = -6,   /* a bf16 array is not 16-byte aligned         */
+    PKV_ERR_BAD_TABLE = -7    /* pkv_validate_page_table found a bad entry   */
+} pkv_status_t;
+
+/*
+ * Shape of the paged cache, passed by value.  The cache is one contiguous
+ * bf16 array [num_layers, num_pages, 2, page_size, num_kv_heads, head_dim]
+ * ("Adding a Model", section 1); index 0 of the third axis holds keys and
+ * index 1 values.  Token t of a request lives in page
+ * page_indices[page_indptr[b] + t / page_size], slot t % page_size.
+ * Page 0 is the scratch page that padding entries point at.
+ * Supported: page_size a power of two in [1, 256]; head_dim 64 or 128 for
+ * pkv_decode, any multiple of 8 for pkv_append.
+ */
+typedef struct {
+    int32_t num_layers;
+    int32_t num_pages;
+    int32_t page_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+} pkv_cache_desc_t;
+
+/*
+ * pkv_append -- write this step's K and V rows into the cache
+ * ("Adding a Model", section 1: set_kv_cache).
+ *
+ * For each entry b in [0, batch): page p = page_indices[page_indptr[b+1]-1]
+ * (its last listed page), slot s = last_page_len[b] - 1, and
+ *   cache[layer, p, 0, s, :, :] = k_new[b, :, :]
+ *   cache[layer, p, 1, s, :, :] = v_new[b, :, :]
+ * as a bit copy.  The page table therefore already counts the new row.
+ *  kv_cache       bf16 cache described by `desc`, modified in place.
+ *  k_new, v_new   bf16 [batch, num_kv_heads, head_dim], contiguous.
+ *  page_indptr    int32 [batch + 1], page_indptr[0] == 0, non-decreasing.
+ *  page_indices   int32 [page_indptr[batch]].
+ *  last_page_len  int32 [batch], rows used in the last page after the append.
+ * Padding entries list page 0 with last_page_len 1 and write only its slot 0;
+ * when several do, any one of their rows may remain there.  Two real entries
+ * must not share a last page slot.
+ */
+int pkv_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+               const void *k_new, const void *v_new,
+               const int32_t *page_indptr, const int32_t *page_indices,
+               const int32_t *last_page_len, int32_t batch, hipStream_t stream);
+
+/*
+ * pkv_decode_workspace_size -- bytes of device workspace pkv_decode needs for
+ * these arguments (0 when no entry can span more than one KV chunk, in which
+ * case workspace may be NULL).  Host function; no device work.
+ * kv_chunk_pages == 0 selects pkv_default_chunk_pages().
+ */
+size_t pkv_decode_workspace_size(int32_t batch, int32_t num_qo_heads,
+                                 int32_t head_dim, int32_t max_pages_per_req,
+                                 int32_t kv_chunk_pages);
+
+/* The KV chunk length, in pages, that kv_chunk_pages == 0 selects. */
+int32_t pkv_default_chunk_pages(void);
+
+/*
+ * pkv_decode -- grouped-query attention of one query row per entry over its
+ * pages ("Adding a Model", section 1: run(q, kv_cache); "How a program
+ * runs": lm_decode is one row per request).
+ *
+ * For entry b with n = page_indptr[b+1] - page_indptr[b] pages and
+ * L = (n - 1) * page_size + last_page_len[b] tokens, and for query head hq
+ * reading KV head h = hq / (num_qo_heads / num_kv_heads):
+ *   s_t = sm_scale * dot(q[b, hq, :], K_t[h, :])          t = 0 .. L-1
+ *   lse[b, hq] = ln(sum_t exp(s_t))                         natural log
+ *   out[b, hq, :] = sum_t exp(s_t - lse[b, hq]) * V_t[h, :]
+ * Accumulation is fp32; out is rounded once to bf16 (nearest even).
+ * Long entries are split into runs of kv_chunk_pages pages whose partial
+ * (output, lse) pairs are merged by log-sum-exp, the way partial attentions
+ * are merged on the "Supported Models" page (LTX-2.5 notes).  The split
+ * depends only on the entry's own length, so an entry's result does not
+ * depend on the rest of the batch.
+ *  kv_cache           bf16 cache described by `desc` (read only).
+ *  q                  bf16 [batch, num_qo_heads, head_dim], RoPE applied.
+ *  page_indptr/page_indices/last_page_len   as for pkv_append.
+ *  sm_scale           finite softmax scale, e.g. 1/sqrt(head_dim).
+ *  out                bf16 [batch, num_qo_heads, head_dim], written.
+ *  lse                fp32 [batch, num_qo_heads], written; may be NULL.
+ *  max_pages_per_req  host upper bound on any entry's page count (sizes the
+ *                     launch; an entry above it would be cut short).
+ *  kv_chunk_pages     chunk length in pages, 1..64; 0 = library default.
+ *  workspace          device scratch of workspace_bytes >=
+ *                     pkv_decode_workspace_size(...); may be NULL when that
+ *                     size is 0.  Its contents need no initialisation.
+ * Supported: head_dim 64 or 128, num_qo_heads / num_kv_heads in 1..8.
+ * Rows of padding entries are computed over scratch page 0 and are garbage by
+ * design; they never fault and never touch other entries' rows.
+ */
+int pkv_decode(const void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+               const void *q, int32_t num_qo_heads,
+               const int32_t *page_indptr, const int32_t *page_indices,
+               const int32_t *last_page_len, int32_t batch, float sm_scale,
+               void *out, float *lse, int32_t max_pages_per_req,
+               int32_t kv_chunk_pages, void *workspace, size_t workspace_bytes,
+               hipStream_t stream);
+
+/*
+ * pkv_validate_page_table -- debug check of HOST copies of a page table
+ * against the device-side preconditions above.  Returns PKV_OK or
+ * PKV_ERR_BAD_TABLE (with *bad_entry set to the first offending entry, or -1
+ * for a problem with page_indptr[0]); PKV_ERR_NULL_PTR / PKV_ERR_BAD_SHAPE
+ * for bad arguments.  Checks: indptr starts at 0 and never decreases; every
+ * entry has 1..max_pages_per_req pages (max_pages_per_req <= 0 disables that
+ * bound); 1 <= last_page_len <= page_size; ids in [0, num_pages); an entry
+ * that lists page 0 is a padding entry (one page, last_page_len 1); no two
+ * entries append into the same real page slot.
+ */
+int pkv_validate_page_table(const int32_t *page_indptr, const int32_t *page_indices,
+                            const int32_t *last_page_len, int32_t batch,
+                            int32_t num_pages, int32_t page_size,
+                            int32_t max_pages_per_req, int32_t *bad_entry);
+
+/*
+ * pkv_last_hip_error -- the hipError_t code behind the most recent
+ * PKV_ERR_HIP returned on the calling thread (0 if there was none).  Host
+ * function; diagnostics only.
+ */
+int pkv_last_hip_error(void);
+
+/* Static, human-readable name of a pkv_status_t value. */
+const char *pkv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,241 @@
+"""Python binding of libpkv: paged-KV append and decode attention on MI355X.
+
+Argument marshalling only.  Every step of the path runs in the gfx950 kernels
+behind the C ABI of ``include/pkv.h``; this module checks tensor dtypes,
+devices and shapes, allocates outputs or workspace with torch when the caller
+does not pass them, and hands raw device pointers and the current HIP stream
+to the library.  There is no fallback: importing this package fails if
+``libpkv.so`` has not been built (``python paged_kv_decode_pkv_amd/build.py``).
+
+The calls follow the per-layer API on the vox-serve "Adding a Model" page
+(section 1): :func:`append` is ``set_kv_cache(kv_cache, k, v)`` and
+:func:`decode` is ``run(q, kv_cache)``, with the step's page table passed in
+CSR form (``page_indptr``, ``page_indices``, ``last_page_len``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "pkv.h")
+
+PKV_OK = 0
+STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL_PTR", -2: "PKV_ERR_BAD_SHAPE",
+          -3: "PKV_ERR_UNSUPPORTED", -4: "PKV_ERR_WORKSPACE", -5: "PKV_ERR_HIP",
+          -6: "PKV_ERR_ALIGNMENT", -7: "PKV_ERR_BAD_TABLE"}
+
+
+class CacheDesc(ctypes.Structure):
+    """Mirror of pkv_cache_desc_t."""
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32)]
+
+
+class PkvError(RuntimeError):
+    """A libpkv call returned a negative status."""
+
+    def __init__(self, code: int, what: str):
+        self.code = code
+        extra = ""
+        if code == -5:
+            self.hip_error = int(lib.pkv_last_hip_error())
+            extra = f", hipError_t {self.hip_error}"
+        super().__init__(f"{what}: {status_string(code)} ({code}{extra})")
+
+
+def _hip_runtimes() -> set[str]:
+    """Distinct HIP runtime files mapped into this process (Linux)."""
+    found = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                path = line.split()[-1]
+                if "libamdhip64.so" in os.path.basename(path):
+                    found.add(os.path.realpath(path))
+    except OSError:
+        pass
+    return found
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python paged_kv_decode_pkv_amd/build.py` (no fallback path exists)")
+    # torch owns the device memory and the streams handed to the library, so
+    # libpkv must bind to torch's HIP runtime: importing torch first makes the
+    # dynamic loader resolve libpkv's libamdhip64.so.7 to the one torch loaded.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise ImportError(
+            "two HIP runtimes are loaded in this process "
+            f"({sorted(runtimes)}); import torch before anything that loads "
+            "another libamdhip64")
+    p, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.pkv_append.argtypes = [p, CacheDesc, i32, p, p, p, p, p, i32, p]
+    lib.pkv_append.restype = ctypes.c_int
+    lib.pkv_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.pkv_decode_workspace_size.restype = sz
+    lib.pkv_default_chunk_pages.argtypes = []
+    lib.pkv_default_chunk_pages.restype = i32
+    lib.pkv_decode.argtypes = [p, CacheDesc, i32, p, i32, p, p, p, i32, ctypes.c_float,
+                               p, p, i32, i32, p, sz, p]
+    lib.pkv_decode.restype = ctypes.c_int
+    lib.pkv_validate_page_table.argtypes = [p, p, p, i32, i32, i32, i32,
+                                            ctypes.POINTER(i32)]
+    lib.pkv_validate_page_table.restype = ctypes.c_int
+    lib.pkv_last_hip_error.argtypes = []
+    lib.pkv_last_hip_error.restype = ctypes.c_int
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def declared_functions(header: str = HEADER) -> list[str]:
+    """Names of the functions ``include/pkv.h`` declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*(pkv_[a-z_0-9]+)\s*\(",
+                      text, flags=re.M)
+
+
+def status_string(code: int) -> str:
+    return lib.pkv_status_string(int(code)).decode()
+
+
+def default_chunk_pages() -> int:
+    return int(lib.pkv_default_chunk_pages())
+
+
+def workspace_size(batch: int, num_qo_heads: int, head_dim: int, max_pages_per_req: int,
+                   kv_chunk_pages: int = 0) -> int:
+    return int(lib.pkv_decode_workspace_size(batch, num_qo_heads, head_dim,
+                                             max_pages_per_req, kv_chunk_pages))
+
+
+def cache_desc(kv_cache) -> CacheDesc:
+    shape = tuple(kv_cache.shape)
+    if len(shape) != 6 or shape[2] != 2:
+        raise ValueError("kv_cache must be [num_layers, num_pages, 2, page_size, "
+                         f"num_kv_heads, head_dim], got {shape}")
+    nl, npg, _, ps, hkv, d = shape
+    return CacheDesc(nl, npg, ps, hkv, d)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream")
+                           else int(stream))
+
+
+def _dev_ptr(t, name, dtype=None, device=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live in GPU memory")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _tables(kv_cache, page_indptr, page_indices, last_page_len):
+    import torch
+    dev = kv_cache.device
+    return (_dev_ptr(page_indptr, "page_indptr", torch.int32, dev),
+            _dev_ptr(page_indices, "page_indices", torch.int32, dev),
+            _dev_ptr(last_page_len, "last_page_len", torch.int32, dev))
+
+
+def append(kv_cache, layer: int, k_new, v_new, page_indptr, page_indices, last_page_len,
+           stream=None) -> None:
+    """Write k_new / v_new [batch, Hkv, D] (bf16) into each entry's last page slot."""
+    import torch
+    desc = cache_desc(kv_cache)
+    batch = int(last_page_len.shape[0])
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (batch, desc.num_kv_heads, desc.head_dim):
+            raise ValueError(f"{name} must be [batch, Hkv, D], got {tuple(t.shape)}")
+    dev = kv_cache.device
+    rc = lib.pkv_append(_dev_ptr(kv_cache, "kv_cache", torch.bfloat16), desc, int(layer),
+                        _dev_ptr(k_new, "k_new", torch.bfloat16, dev),
+                        _dev_ptr(v_new, "v_new", torch.bfloat16, dev),
+                        *_tables(kv_cache, page_indptr, page_indices, last_page_len),
+                        batch, _stream(stream))
+    if rc != PKV_OK:
+        raise PkvError(rc, "pkv_append")
+
+
+def decode(kv_cache, layer: int, q, page_indptr, page_indices, last_page_len,
+           sm_scale: float, max_pages_per_req: int, kv_chunk_pages: int = 0, out=None,
+           lse=None, with_lse: bool = True, workspace=None, stream=None):
+    """Attention of one query row per entry over its pages; returns (out, lse).
+
+    ``q`` is bf16 [batch, Hq, D]; ``out`` (bf16, same shape) and ``lse`` (fp32
+    [batch, Hq], natural log) are allocated when not given; ``lse`` is None
+    when ``with_lse`` is False and none is passed.  ``max_pages_per_req`` is
+    the host-side bound on any entry's page count.
+    """
+    import torch
+    desc = cache_desc(kv_cache)
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError(f"q must be [batch, Hq, {desc.head_dim}], got {tuple(q.shape)}")
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    dev = kv_cache.device
+    if out is None:
+        out = torch.empty((batch, hq, desc.head_dim), dtype=torch.bfloat16, device=dev)
+    if lse is None and with_lse:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    if tuple(out.shape) != (batch, hq, desc.head_dim):
+        raise ValueError("out must match q")
+    if lse is not None and tuple(lse.shape) != (batch, hq):
+        raise ValueError("lse must be [batch, Hq]")
+    need = workspace_size(batch, hq, desc.head_dim, max_pages_per_req, kv_chunk_pages)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = ctypes.c_void_p(0) if workspace is None else _dev_ptr(workspace, "workspace",
+                                                                   device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lse_ptr = ctypes.c_void_p(0) if lse is None else _dev_ptr(lse, "lse", torch.float32,
+                                                              dev)
+    rc = lib.pkv_decode(_dev_ptr(kv_cache, "kv_cache", torch.bfloat16), desc, int(layer),
+                        _dev_ptr(q, "q", torch.bfloat16, dev), hq,
+                        *_tables(kv_cache, page_indptr, page_indices, last_page_len),
+                        batch, float(sm_scale),
+                        _dev_ptr(out, "out", torch.bfloat16, dev), lse_ptr,
+                        int(max_pages_per_req), int(kv_chunk_pages), ws_ptr, ws_bytes,
+                        _stream(stream))
+    if rc != PKV_OK:
+        raise PkvError(rc, "pkv_decode")
+    return out, lse
+
+
+def validate_page_table(page_indptr, page_indices, last_page_len, num_pages: int,
+                        page_size: int, max_pages_per_req: int = 0):
+    """Check HOST copies of a page table; returns (status, first bad entry)."""
+    ip = np.ascontiguousarray(page_indptr, dtype=np.int32)
+    ix = np.ascontiguousarray(page_indices, dtype=np.int32)
+    ll = np.ascontiguousarray(last_page_len, dtype=np.int32)
+    bad = ctypes.c_int32(-1)
+    rc = lib.pkv_validate_page_table(ip.ctypes.data_as(ctypes.c_void_p),
+                                     ix.ctypes.data_as(ctypes.c_void_p),
+                                     ll.ctypes.data_as(ctypes.c_void_p), len(ll),
+                                     int(num_pages), int(page_size),
+                                     int(max_pages_per_req), ctypes.byref(bad))
+    return int(rc), int(bad.value)

@@ -1,0 +1,123 @@
+"""The C ABI loads and validates host arguments without a GPU (CPU only).
+
+Only calls that must fail validation (or are no-ops) are made here: nothing
+reaches the HIP runtime.
+"""
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+
+import paged_kv_decode_pkv_amd as pkv
+from paged_kv_decode_pkv_amd import CacheDesc, lib
+
+FAKE = ctypes.c_void_p(0x100000)      # never dereferenced: validation fails first
+NULL = ctypes.c_void_p(0)
+DESC = CacheDesc(2, 64, 16, 2, 64)
+
+
+def test_every_declared_symbol_is_exported():
+    names = pkv.declared_functions()
+    assert set(names) == {"pkv_append", "pkv_decode_workspace_size",
+                          "pkv_default_chunk_pages", "pkv_decode",
+                          "pkv_validate_page_table", "pkv_status_string",
+                          "pkv_last_hip_error"}
+    for n in names:
+        assert hasattr(lib, n), n
+    dyn = subprocess.run(["nm", "-D", "--defined-only", pkv.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in dyn.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_status_strings():
+    for code, name in pkv.STATUS.items():
+        assert pkv.status_string(code).startswith(name)
+    assert pkv.status_string(12345) == "unknown pkv status"
+
+
+def test_workspace_size():
+    k = pkv.default_chunk_pages()
+    assert 1 <= k <= 64
+    assert pkv.workspace_size(64, 32, 128, k, 0) == 0          # one chunk: no split
+    ws = pkv.workspace_size(8, 32, 128, 2048, 32)
+    rows = 8 * 64 * 32
+    assert ws >= rows * 128 * 4 + rows * 4 and ws % 256 == 0
+    assert pkv.workspace_size(0, 32, 128, 2048, 32) == 0
+
+
+def _decode(desc=DESC, layer=0, q=FAKE, hq=4, batch=3, scale=0.125, out=FAKE, lse=NULL,
+            maxp=4, chunk=0, ws=NULL, wsb=0, tables=(FAKE, FAKE, FAKE)):
+    return lib.pkv_decode(FAKE, desc, layer, q, hq, *tables, batch, scale, out, lse, maxp,
+                          chunk, ws, wsb, NULL)
+
+
+def _append(desc=DESC, layer=0, batch=3, k=FAKE, v=FAKE, tables=(FAKE, FAKE, FAKE),
+            cache=FAKE):
+    return lib.pkv_append(cache, desc, layer, k, v, *tables, batch, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layer=2), -2), (dict(layer=-1), -2), (dict(batch=-1), -2),
+    (dict(desc=CacheDesc(2, 64, 12, 2, 64)), -3), (dict(desc=CacheDesc(2, 64, 0, 2, 64)), -2),
+    (dict(desc=CacheDesc(2, 64, 512, 2, 64)), -3), (dict(desc=CacheDesc(0, 64, 16, 2, 64)), -2),
+    (dict(desc=CacheDesc(2, 64, 16, 2, 60)), -3),
+    (dict(k=NULL), -1), (dict(tables=(FAKE, NULL, FAKE)), -1), (dict(cache=NULL), -1),
+    (dict(k=ctypes.c_void_p(0x100008)), -6),
+])
+def test_append_validation(kw, code):
+    assert _append(**kw) == code
+
+
+def test_append_batch_zero_is_noop():
+    assert _append(batch=0, k=NULL, v=NULL, cache=NULL) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layer=5), -2), (dict(batch=-2), -2), (dict(hq=3), -2), (dict(hq=0), -2),
+    (dict(scale=float("nan")), -2), (dict(scale=float("inf")), -2), (dict(maxp=0), -2),
+    (dict(chunk=-1), -2), (dict(chunk=65), -3), (dict(hq=18), -3),
+    (dict(desc=CacheDesc(2, 64, 16, 2, 96)), -3), (dict(desc=CacheDesc(2, 64, 6, 2, 64)), -3),
+    (dict(q=NULL), -1), (dict(out=NULL), -1), (dict(tables=(FAKE, FAKE, NULL)), -1),
+    (dict(maxp=40, chunk=16), -4),
+    (dict(maxp=40, chunk=16, ws=FAKE, wsb=16), -4),
+    (dict(out=ctypes.c_void_p(0x100004)), -6),
+])
+def test_decode_validation(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_decode_batch_zero_is_noop():
+    assert _decode(batch=0, q=NULL, out=NULL, tables=(NULL, NULL, NULL)) == 0
+
+
+def test_validate_page_table():
+    indptr = np.array([0, 2, 3, 4])
+    indices = np.array([5, 7, 0, 9])
+    last = np.array([3, 1, 16])
+    assert pkv.validate_page_table(indptr, indices, last, 16, 16, 4) == (0, -1)
+    bad = [
+        (np.array([1, 2, 3, 4]), indices, last, -1),          # indptr[0] != 0
+        (np.array([0, 2, 2, 4]), indices, last, 1),           # empty entry
+        (indptr, indices, np.array([3, 2, 16]), 1),           # padding with 2 rows
+        (indptr, np.array([5, 0, 0, 9]), last, 0),            # page 0 in a real entry
+        (indptr, np.array([5, 7, 0, 16]), last, 2),           # id out of range
+        (indptr, indices, np.array([0, 1, 16]), 0),           # last_len 0
+        (indptr, indices, np.array([3, 1, 17]), 2),           # last_len > page_size
+        (indptr, np.array([5, 7, 0, 7]), last, 2),            # two appends into page 7
+    ]
+    for ip, ix, ll, entry in bad:
+        assert pkv.validate_page_table(ip, ix, ll, 16, 16, 4) == (-7, entry)
+    assert pkv.validate_page_table(indptr, indices, last, 16, 16, 1) == (-7, 0)
+
+
+def test_single_hip_runtime_shared_with_torch():
+    # torch's streams and allocations are only meaningful to torch's own HIP
+    # runtime instance; libpkv must resolve to that same instance.
+    import os
+    import torch
+    rts = pkv._hip_runtimes()
+    assert len(rts) == 1
+    assert os.path.dirname(next(iter(rts))) == os.path.realpath(
+        os.path.join(os.path.dirname(torch.__file__), "lib"))

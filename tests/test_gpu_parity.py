@@ -1,0 +1,350 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on the GPU.
+
+Bars: pkv_append bit-exact; pkv_decode out within max |err| 1e-2 and mean
+|err| 1e-3 (bf16 output against fp64), lse within 1e-3, over active rows.
+Inputs are the seeded workloads of ``workloads`` (host numpy for the small
+configurations, torch's seeded GPU generator for the multi-gigabyte ones).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_decode_pkv_amd as pkv
+import workloads
+from golden_cases import build_case, load_cases
+from gpu_util import (DEV, compare, gpu_step, host_layer_case, oracle_rows_from_device,
+                      table_to_dev, to_dev_u16, to_host_u16)
+from workloads import CONFIGS, bf16_to_f32, make_table, table_from_lengths
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def _full_cache(spec_or_shape, table, layer_data_list):
+    """Device cache [L, NP, 2, PS, Hkv, D] from per-layer host slabs."""
+    slabs = np.stack([ld.cache for ld in layer_data_list])
+    return to_dev_u16(slabs)
+
+
+def _oracle_full(cache_host, layer, ld, table, scale, chunk=0):
+    oracle.append(cache_host, layer, ld.k_new, ld.v_new, table.indptr, table.indices,
+                  table.last_len)
+    return oracle.decode(cache_host, layer, ld.q, table.indptr, table.indices,
+                         table.last_len, scale, chunk)
+
+
+# ---------------------------------------------------------------- golden cases
+@pytest.mark.parametrize("chunk", [0, 1])
+def test_golden_cases(chunk):
+    for case in load_cases():
+        g = build_case(case)
+        cache = to_dev_u16(g["cache"])
+        tables = tuple(torch.from_numpy(x).to(DEV)
+                       for x in (g["indptr"], g["indices"], g["last_len"]))
+        q = to_dev_u16(g["q"])
+        maxp = int(np.diff(g["indptr"]).max())
+        out, lse = pkv.decode(cache, 0, q, *tables, g["sm_scale"], max_pages_per_req=maxp,
+                              kv_chunk_pages=chunk)
+        m = g["checked"]
+        compare(out, lse, g["out"][m], g["lse"][m], rows=m, what=case["name"])
+
+
+# ------------------------------------------------------------ random shapes
+SHAPES = [
+    # hq, hkv, d, page_size, lengths, active
+    (1, 1, 64, 16, [1, 17, 200], None),
+    (2, 2, 128, 16, [5, 64, 300, 16], [1, 1, 0, 1]),
+    (3, 1, 128, 8, [100, 1, 33], None),
+    (4, 2, 64, 1, [9, 40, 3], None),
+    (5, 1, 64, 2, [77, 2], None),
+    (6, 3, 128, 4, [51, 18, 1, 250], [1, 1, 0, 1]),
+    (7, 1, 64, 32, [500, 31, 32, 33], None),
+    (8, 2, 128, 128, [129, 700, 1], None),
+    (14, 2, 64, 16, [256, 255, 1, 97], [1, 0, 1, 1]),
+    (32, 8, 128, 16, [1024, 4096, 64, 3], None),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SHAPES)))
+@pytest.mark.parametrize("chunk", [0, 1, 3, 64])
+def test_random_shapes(idx, chunk):
+    hq, hkv, d, ps, lengths, active = SHAPES[idx]
+    rng = np.random.default_rng(1000 + idx)
+    act = np.ones(len(lengths), bool) if active is None else np.asarray(active, bool)
+    table = table_from_lengths(lengths, act, ps, None, rng)
+    lds = [workloads.draw_layer(rng, table, hq, hkv, d, 1.0, stale="nan", unused="nan")
+           for _ in range(2)]
+    cache_host = np.stack([ld.cache for ld in lds])
+    cache = to_dev_u16(cache_host)
+    tables = table_to_dev(table)
+    scale = 1.0 / math.sqrt(d)
+    for layer in (1, 0):
+        ld = lds[layer]
+        dev = (to_dev_u16(ld.q), to_dev_u16(ld.k_new), to_dev_u16(ld.v_new))
+        out, lse = gpu_step(cache, layer, dev, tables, table, scale, chunk=chunk)
+        ro, rl = _oracle_full(cache_host, layer, ld, table, scale)
+        compare(out, lse, ro[act], rl[act], rows=act, what=f"shape {idx} layer {layer}")
+
+
+# ------------------------------------------------------------------- append
+@pytest.mark.parametrize("idx", range(len(SHAPES)))
+def test_append_bit_exact(idx):
+    hq, hkv, d, ps, lengths, active = SHAPES[idx]
+    rng = np.random.default_rng(2000 + idx)
+    act = np.ones(len(lengths), bool) if active is None else np.asarray(active, bool)
+    table = table_from_lengths(lengths, act, ps, None, rng)
+    lds = [workloads.draw_layer(rng, table, hq, hkv, d, 1.0) for _ in range(3)]
+    cache_host = np.stack([ld.cache for ld in lds])
+    cache = to_dev_u16(cache_host)
+    tables = table_to_dev(table)
+    for layer in (2, 0):
+        ld = lds[layer]
+        pkv.append(cache, layer, to_dev_u16(ld.k_new), to_dev_u16(ld.v_new), *tables)
+        oracle.append(cache_host, layer, ld.k_new, ld.v_new, table.indptr, table.indices,
+                      table.last_len)
+        got = to_host_u16(cache)
+        pad = np.flatnonzero(~act)
+        if len(pad):   # padding entries race on page 0 slot 0: any of theirs may win
+            cands = [ld.k_new[b] for b in pad]
+            assert any(np.array_equal(got[layer, 0, 0, 0], c) for c in cands)
+            got[layer, 0] = cache_host[layer, 0]
+        np.testing.assert_array_equal(got, cache_host, err_msg=f"shape {idx} layer {layer}")
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_append_bit_exact_configs(cfg):
+    spec = CONFIGS[cfg]
+    table = make_table(spec)
+    ld, dev = host_layer_case(spec, table, 0)
+    cache_host = ld.cache[None].copy()
+    cache = to_dev_u16(cache_host)
+    tables = table_to_dev(table)
+    pkv.append(cache, 0, dev[1], dev[2], *tables)
+    oracle.append(cache_host, 0, ld.k_new, ld.v_new, table.indptr, table.indices,
+                  table.last_len)
+    got = to_host_u16(cache)
+    got[0, 0] = cache_host[0, 0]
+    np.testing.assert_array_equal(got, cache_host)
+
+
+# ------------------------------------------------------------- configs 1, 2
+@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("chunk", [0, 1, 4, 16, 64])
+def test_decode_config(cfg, chunk):
+    spec = CONFIGS[cfg]
+    table = make_table(spec)
+    ld, dev = host_layer_case(spec, table, 0, stale="nan")
+    cache_host = ld.cache[None].copy()
+    cache = to_dev_u16(cache_host)
+    out, lse = gpu_step(cache, 0, dev, table_to_dev(table), table, spec.sm_scale, chunk)
+    ro, rl = _oracle_full(cache_host, 0, ld, table, spec.sm_scale)
+    act = table.active
+    compare(out, lse, ro[act], rl[act], rows=act, what=f"cfg{cfg} chunk{chunk}")
+
+
+# ------------------------------------------------------ device-drawn configs
+def _device_case(spec, batch=None, layers=(0,), extra_layers=0):
+    """Cache on the GPU drawn with the device generator; host copies of q/k/v."""
+    table = make_table(spec, batch)
+    nl = max(layers) + 1 + extra_layers
+    cache = torch.zeros((nl, table.num_pages, 2, spec.page_size, spec.num_kv_heads,
+                         spec.head_dim), dtype=torch.bfloat16, device=DEV)
+    per_layer = {}
+    for layer in layers:
+        q, kn, vn = workloads.draw_layer_device(
+            cache[layer], table, [1000 * spec.cfg + layer, table.batch],
+            spec.num_qo_heads, spec.sigma, workloads.k_offsets(spec))
+        per_layer[layer] = (q, kn, vn)
+    return table, cache, per_layer
+
+
+class _HostRows:
+    def __init__(self, q, kn, vn):
+        self.q, self.k_new, self.v_new = to_host_u16(q), to_host_u16(kn), to_host_u16(vn)
+
+
+def _sampled_check(spec, table, cache, layer, dev, entries, heads, chunk=0, what=""):
+    """Run append+decode of one layer; compare sampled rows with the oracle."""
+    host_rows = _HostRows(*dev)
+    ro, rl, (rb, rh) = oracle_rows_from_device(cache[layer], host_rows, table, entries,
+                                               heads, spec.sm_scale)
+    out, lse = gpu_step(cache, layer, dev, table_to_dev(table), table, spec.sm_scale,
+                        chunk)
+    og = out[torch.from_numpy(rb).to(DEV), torch.from_numpy(rh).to(DEV)]
+    lg = lse[torch.from_numpy(rb).to(DEV), torch.from_numpy(rh).to(DEV)]
+    return compare(og, lg, ro, rl, what=what)
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 0])
+def test_decode_config5_long_context(chunk):
+    spec = CONFIGS[5]
+    table, cache, per_layer = _device_case(spec)
+    _sampled_check(spec, table, cache, 0, per_layer[0], range(spec.batch),
+                   [0, 3, 4, 17, 31], chunk=chunk, what=f"cfg5 chunk{chunk}")
+
+
+def _pick_entries(table, n):
+    act = np.flatnonzero(table.active)
+    order = act[np.argsort(table.lengths[act])]
+    picks = {int(order[0]), int(order[-1]), int(order[len(order) // 2])}
+    rng = np.random.default_rng(7)
+    picks |= set(int(x) for x in rng.choice(act, size=min(n, len(act)), replace=False))
+    return sorted(picks)
+
+
+def test_decode_config3_all_layers_sampled():
+    """Qwen3-4B-like step: 36 layers, batch 64, in the benchmark's launch shape
+    (default chunking, one append + decode per layer); sampled rows of three
+    layers are checked against the oracle."""
+    spec = CONFIGS[3]
+    table = make_table(spec)
+    check = {0, 17, 35}
+    cache = torch.zeros((spec.num_layers, table.num_pages, 2, 16, 8, 128),
+                        dtype=torch.bfloat16, device=DEV)
+    tables = table_to_dev(table)
+    entries = _pick_entries(table, 5)
+    for layer in range(spec.num_layers):
+        dev = workloads.draw_layer_device(cache[layer], table, [3000 + layer, 64], 32,
+                                          1.0, None)
+        if layer in check:
+            _sampled_check(spec, table, cache, layer, dev, entries, [0, 9, 22, 31],
+                           what=f"cfg3 layer {layer}")
+        else:
+            gpu_step(cache, layer, dev, tables, table, spec.sm_scale)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("batch", workloads.CFG4_SWEEP)
+def test_decode_config4_sweep_sampled(batch):
+    spec = CONFIGS[4]
+    table, cache, per_layer = _device_case(spec, batch, layers=(0, 27))
+    entries = _pick_entries(table, 4)
+    for layer in (0, 27):
+        _sampled_check(spec, table, cache, layer, per_layer[layer], entries, [0, 7, 15],
+                       what=f"cfg4 B={batch} layer {layer}")
+
+
+# ------------------------------------------------------------ invariances
+def test_batch_invariance_bit_exact():
+    """An entry's rows are bit-identical alone, in sub-batches and in the full
+    batch (cfg-4 shapes): the split depends only on the entry's own length."""
+    spec = CONFIGS[4]
+    table, cache, per_layer = _device_case(spec, 256)
+    q, kn, vn = per_layer[0]
+    tables = table_to_dev(table)
+    pkv.append(cache, 0, kn, vn, *tables)
+    full_out, full_lse = pkv.decode(cache, 0, q, *tables, spec.sm_scale,
+                                    max_pages_per_req=table.max_pages_per_req)
+    rng = np.random.default_rng(3)
+    act = np.flatnonzero(table.active)
+    for size in (1, 2, 4, 16, 64):
+        sel = rng.choice(act, size=size, replace=False)
+        n = np.diff(table.indptr)[sel]
+        ip = np.zeros(size + 1, np.int32)
+        ip[1:] = np.cumsum(n)
+        ix = np.concatenate([table.indices[table.indptr[b]:table.indptr[b + 1]] for b in sel])
+        sub = tuple(torch.from_numpy(x.astype(np.int32)).to(DEV)
+                    for x in (ip, ix, table.last_len[sel]))
+        o, l_ = pkv.decode(cache, 0, q[torch.from_numpy(sel).to(DEV)].contiguous(), *sub,
+                           spec.sm_scale, max_pages_per_req=int(n.max()) + 7)
+        sel_t = torch.from_numpy(sel).to(DEV)
+        assert torch.equal(o.view(torch.int16), full_out[sel_t].view(torch.int16))
+        assert torch.equal(l_, full_lse[sel_t])
+
+
+def test_page_relabel_bit_exact():
+    spec = CONFIGS[2]
+    table = make_table(spec)
+    ld, dev = host_layer_case(spec, table, 0)
+    cache_host = ld.cache[None].copy()
+    cache = to_dev_u16(cache_host)
+    out0, lse0 = gpu_step(cache, 0, dev, table_to_dev(table), table, spec.sm_scale)
+    perm = np.concatenate([[0], 1 + np.random.default_rng(5).permutation(
+        table.num_pages - 1)])
+    moved = np.empty_like(cache_host)
+    moved[:, perm] = cache_host
+    t2 = workloads.PageTable(table.lengths, table.active, table.indptr,
+                             perm[table.indices].astype(np.int32), table.last_len,
+                             table.num_pages, table.page_size)
+    out1, lse1 = gpu_step(to_dev_u16(moved), 0, dev, table_to_dev(t2), t2, spec.sm_scale)
+    act = torch.from_numpy(np.flatnonzero(table.active)).to(DEV)
+    assert torch.equal(out0[act].view(torch.int16), out1[act].view(torch.int16))
+    assert torch.equal(lse0[act], lse1[act])
+
+
+def test_padding_isolation():
+    """Append touches only the entries' target slots and page 0; adding
+    padding entries leaves the active rows bit-identical."""
+    spec = CONFIGS[2]
+    table = make_table(spec)
+    ld, dev = host_layer_case(spec, table, 0)
+    cache = to_dev_u16(ld.cache[None].copy())
+    before = to_host_u16(cache)
+    tables = table_to_dev(table)
+    pkv.append(cache, 0, dev[1], dev[2], *tables)
+    after = to_host_u16(cache)
+    changed = np.argwhere(np.any(before != after, axis=(2, 4, 5)))   # (layer, page, slot)
+    allowed = {(0, 0, 0)}
+    for b in range(table.batch):
+        allowed.add((0, int(table.indices[table.indptr[b + 1] - 1]),
+                     int(table.last_len[b]) - 1))
+    assert {tuple(map(int, x)) for x in changed} <= allowed
+    out0, lse0 = pkv.decode(cache, 0, dev[0], *tables, spec.sm_scale,
+                            max_pages_per_req=table.max_pages_per_req)
+    # the same active entries without any padding entry
+    act = np.flatnonzero(table.active)
+    n = np.diff(table.indptr)[act]
+    ip = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    ix = np.concatenate([table.indices[table.indptr[b]:table.indptr[b + 1]] for b in act])
+    sub = tuple(torch.from_numpy(x.astype(np.int32)).to(DEV)
+                for x in (ip, ix, table.last_len[act]))
+    act_t = torch.from_numpy(act).to(DEV)
+    o1, l1 = pkv.decode(cache, 0, dev[0][act_t].contiguous(), *sub, spec.sm_scale,
+                        max_pages_per_req=table.max_pages_per_req)
+    assert torch.equal(o1.view(torch.int16), out0[act_t].view(torch.int16))
+    assert torch.equal(l1, lse0[act_t])
+
+
+# ------------------------------------------------------------ closed forms
+def test_closed_forms():
+    spec = CONFIGS[2]
+    table = make_table(spec)
+    ld, dev = host_layer_case(spec, table, 0)
+    act = table.active
+    tables = table_to_dev(table)
+    # V = 1 everywhere: every convex combination is exactly 1.
+    cache_host = ld.cache[None].copy()
+    cache_host[:, :, 1] = 0x3F80
+    out, _ = gpu_step(to_dev_u16(cache_host), 0,
+                      (dev[0], dev[1], torch.ones_like(dev[2])), tables, table,
+                      spec.sm_scale)
+    assert torch.all(out[torch.from_numpy(np.flatnonzero(act)).to(DEV)] == 1.0)
+    # q = 0: lse = ln L and out = mean of V.
+    q0 = torch.zeros_like(dev[0])
+    cache = to_dev_u16(ld.cache[None].copy())
+    _, lse = gpu_step(cache, 0, (q0, dev[1], dev[2]), tables, table, spec.sm_scale)
+    want = np.log(table.lengths[act].astype(np.float64))[:, None]
+    got = lse.cpu().numpy()[act]
+    assert np.max(np.abs(got - want)) < 1e-3
+    # L = 1 for every entry: out is v_new of its KV head, bit for bit.
+    t1 = table_from_lengths([1] * 8, np.ones(8, bool), 16, 64, np.random.default_rng(1))
+    l1 = workloads.draw_layer(np.random.default_rng(2), t1, 24, 8, 128, stale="nan",
+                              unused="nan")
+    d1 = (to_dev_u16(l1.q), to_dev_u16(l1.k_new), to_dev_u16(l1.v_new))
+    out, lse = gpu_step(to_dev_u16(l1.cache[None].copy()), 0, d1, table_to_dev(t1), t1,
+                        0.1)
+    want = np.repeat(l1.v_new, 3, axis=1)
+    np.testing.assert_array_equal(to_host_u16(out), want)
