@@ -48,6 +48,8 @@ def parse():
                     help="approximate CPU work of the oracle baseline sample")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="call pkv_append then pkv_decode instead of pkv_append_decode")
     ap.add_argument("--probe-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter scale)")
     return ap.parse_args()
@@ -119,8 +121,8 @@ def main():
     out = torch.empty((nl, b, hq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((nl, b, hq), dtype=torch.float32, device=dev)
     maxp = table.max_pages_per_req
-    chunk = args.chunk_pages or pkv.default_chunk_pages()
-    ws_bytes = pkv.workspace_size(b, hq, d, maxp, chunk)
+    chunk = args.chunk_pages
+    ws_bytes = pkv.workspace_size(pkv.cache_desc(cache), hq, b, maxp, chunk)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"inputs resident: cache {cache.numel() * 2 / 2**30:.1f} GiB, "
@@ -135,24 +137,32 @@ def main():
         s = vp(stream_handle)
         app, dec = [], []
         for layer in range(nl):
-            app.append((vp(cache.data_ptr()), desc, layer, vp(KN[layer].data_ptr()),
-                        vp(VN[layer].data_ptr()), *tab_ptrs, b, s))
-            dec.append((vp(cache.data_ptr()), desc, layer, vp(Q[layer].data_ptr()), hq,
-                        *tab_ptrs, b, ctypes.c_float(spec.sm_scale),
-                        vp(out[layer].data_ptr()), vp(lse[layer].data_ptr()), maxp, chunk,
-                        vp(ws.data_ptr()), ws.numel(), s))
+            kn, vn = vp(KN[layer].data_ptr()), vp(VN[layer].data_ptr())
+            tail = (b, ctypes.c_float(spec.sm_scale), vp(out[layer].data_ptr()),
+                    vp(lse[layer].data_ptr()), maxp, chunk, vp(ws.data_ptr()), ws.numel(), s)
+            if args.separate:
+                app.append((vp(cache.data_ptr()), desc, layer, kn, vn, *tab_ptrs, b, s))
+                dec.append((vp(cache.data_ptr()), desc, layer, vp(Q[layer].data_ptr()), hq,
+                            *tab_ptrs, *tail))
+            else:
+                dec.append((vp(cache.data_ptr()), desc, layer, kn, vn,
+                            vp(Q[layer].data_ptr()), hq, *tab_ptrs, *tail))
         return app, dec
+
+    decode_fn = pkv.lib.pkv_decode if args.separate else pkv.lib.pkv_append_decode
+    decode_name = "pkv_decode" if args.separate else "pkv_append_decode"
 
     def run_step(app, dec, events=None):
         for layer in range(nl):
-            rc = pkv.lib.pkv_append(*app[layer])
-            if rc:
-                raise pkv.PkvError(rc, "pkv_append")
+            if app:
+                rc = pkv.lib.pkv_append(*app[layer])
+                if rc:
+                    raise pkv.PkvError(rc, "pkv_append")
             if events is not None:
                 events[layer][0].record()
-            rc = pkv.lib.pkv_decode(*dec[layer])
+            rc = decode_fn(*dec[layer])
             if rc:
-                raise pkv.PkvError(rc, "pkv_decode")
+                raise pkv.PkvError(rc, decode_name)
             if events is not None:
                 events[layer][1].record()
 
@@ -216,7 +226,8 @@ def main():
     step_bytes = nl * by["total"]
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     rows_per_s = int(table.active.sum()) / (ms_step * 1e-3)
-    dec_gbs = by["decode"] / (dec_us * 1e-6) / 1e9
+    launch_bytes = by["decode"] if args.separate else by["total"]
+    dec_gbs = launch_bytes / (dec_us * 1e-6) / 1e9
     log(f"decode launch avg {dec_us:.2f} us -> {dec_gbs:.0f} GB/s algorithmic; "
         f"step {gbs:.0f} GB/s")
 
@@ -229,14 +240,15 @@ def main():
                    "layers": nl, "num_qo_heads": hq, "num_kv_heads": hkv, "head_dim": d,
                    "page_size": ps, "lengths": "log-uniform [64, 4096]",
                    "kv_chunk_pages": chunk, "hip_graph": graph is not None,
+                   "call": "pkv_append + pkv_decode" if args.separate else "pkv_append_decode",
                    "step_bytes": step_bytes},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "decode_rows_per_s": round(rows_per_s, 1),
         "ms_per_step_events": round(ms_step_ev, 5),
-        "roofline": {"bound": "hbm", "kernel": "pkv_decode (split pass + LSE merge)",
+        "roofline": {"bound": "hbm", "kernel": f"{decode_name} (decode pass + LSE merge)",
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": by["decode"], "avg_launch_us": round(dec_us, 3),
+                     "bytes_per_launch": launch_bytes, "avg_launch_us": round(dec_us, 3),
                      "launches": int(durs.size)},
     }
 

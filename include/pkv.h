@@ -23,7 +23,7 @@
  *    least one page, 1 <= last_page_len <= page_size, page ids lie in
  *    [0, num_pages), and no entry lists more than max_pages_per_req pages.
  *  - bf16 means IEEE bfloat16 stored as 16-bit words; every bf16 array and the
- *    cache must be 16-byte aligned.
+ *    cache must be 16-byte aligned, a workspace 256-byte aligned.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -43,7 +43,7 @@ typedef enum {
     PKV_ERR_UNSUPPORTED = -3, /* valid but not built: head_dim, group, ...   */
     PKV_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required  */
     PKV_ERR_HIP = -5,         /* the HIP runtime refused a launch            */
-    PKV_ERR_ALIGNMENT = -6,   /* a bf16 array is not 16-byte aligned         */
+    PKV_ERR_ALIGNMENT = -6,   /* an array is not aligned as required         */
     PKV_ERR_BAD_TABLE = -7    /* pkv_validate_page_table found a bad entry   */
 } pkv_status_t;
 
@@ -89,17 +89,14 @@ int pkv_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
                const int32_t *last_page_len, int32_t batch, hipStream_t stream);
 
 /*
- * pkv_decode_workspace_size -- bytes of device workspace pkv_decode needs for
- * these arguments (0 when no entry can span more than one KV chunk, in which
- * case workspace may be NULL).  Host function; no device work.
- * kv_chunk_pages == 0 selects pkv_default_chunk_pages().
+ * pkv_decode_workspace_size -- bytes of device workspace pkv_decode and
+ * pkv_append_decode need for these arguments; 0 when none is needed (then
+ * workspace may be NULL).  Host function; no device work.  Returns 0 for
+ * arguments pkv_decode would reject.
  */
-size_t pkv_decode_workspace_size(int32_t batch, int32_t num_qo_heads,
-                                 int32_t head_dim, int32_t max_pages_per_req,
+size_t pkv_decode_workspace_size(pkv_cache_desc_t desc, int32_t num_qo_heads,
+                                 int32_t batch, int32_t max_pages_per_req,
                                  int32_t kv_chunk_pages);
-
-/* The KV chunk length, in pages, that kv_chunk_pages == 0 selects. */
-int32_t pkv_default_chunk_pages(void);
 
 /*
  * pkv_decode -- grouped-query attention of one query row per entry over its
@@ -113,11 +110,18 @@ int32_t pkv_default_chunk_pages(void);
  *   lse[b, hq] = ln(sum_t exp(s_t))                         natural log
  *   out[b, hq, :] = sum_t exp(s_t - lse[b, hq]) * V_t[h, :]
  * Accumulation is fp32; out is rounded once to bf16 (nearest even).
- * Long entries are split into runs of kv_chunk_pages pages whose partial
- * (output, lse) pairs are merged by log-sum-exp, the way partial attentions
- * are merged on the "Supported Models" page (LTX-2.5 notes).  The split
- * depends only on the entry's own length, so an entry's result does not
- * depend on the rest of the batch.
+ * Work is split into runs of tokens whose partial (output, lse) pairs are
+ * merged by log-sum-exp, the way partial attentions are merged on the
+ * "Supported Models" page (LTX-2.5 notes):
+ *   kv_chunk_pages == 0  balanced: the tokens of the whole batch are shared
+ *                        evenly among the workgroups the GPU holds at once.
+ *                        Fastest; the split, so the last bits of a row, can
+ *                        change with the rest of the batch.
+ *   kv_chunk_pages  > 0  fixed: each entry is cut into runs of
+ *                        kv_chunk_pages pages (rounded up to whole 8-token
+ *                        tiles); a row is bit-identical whatever else is in
+ *                        the batch.  At most 65536.
+ * Batches above 8192 entries use fixed runs of 16 pages.
  *  kv_cache           bf16 cache described by `desc` (read only).
  *  q                  bf16 [batch, num_qo_heads, head_dim], RoPE applied.
  *  page_indptr/page_indices/last_page_len   as for pkv_append.
@@ -125,14 +129,15 @@ int32_t pkv_default_chunk_pages(void);
  *  out                bf16 [batch, num_qo_heads, head_dim], written.
  *  lse                fp32 [batch, num_qo_heads], written; may be NULL.
  *  max_pages_per_req  host upper bound on any entry's page count (sizes the
- *                     launch; an entry above it would be cut short).
- *  kv_chunk_pages     chunk length in pages, 1..64; 0 = library default.
- *  workspace          device scratch of workspace_bytes >=
+ *                     fixed-mode launch; in fixed mode an entry above it gets
+ *                     NaN rows instead of a truncated result).
+ *  workspace          device scratch, 256-byte aligned, of workspace_bytes >=
  *                     pkv_decode_workspace_size(...); may be NULL when that
  *                     size is 0.  Its contents need no initialisation.
- * Supported: head_dim 64 or 128, num_qo_heads / num_kv_heads in 1..8.
- * Rows of padding entries are computed over scratch page 0 and are garbage by
- * design; they never fault and never touch other entries' rows.
+ * Supported: head_dim 64 or 128, num_kv_heads <= 16, num_qo_heads /
+ * num_kv_heads in 1..8.  Rows of padding entries are computed over scratch
+ * page 0 and are garbage by design; they never fault and never touch other
+ * entries' rows.  The balanced split is sized for the current HIP device.
  */
 int pkv_decode(const void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
                const void *q, int32_t num_qo_heads,
@@ -141,6 +146,25 @@ int pkv_decode(const void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
                void *out, float *lse, int32_t max_pages_per_req,
                int32_t kv_chunk_pages, void *workspace, size_t workspace_bytes,
                hipStream_t stream);
+
+/*
+ * pkv_append_decode -- pkv_append followed by pkv_decode for one layer, in
+ * one pass: the same two calls the "Adding a Model" page makes per layer
+ * (set_kv_cache, then run).  The workgroup that attends over an entry's new
+ * token takes that row from k_new / v_new and writes it into the cache slot
+ * pkv_append would write, so the cache afterwards is bit-identical to
+ * pkv_append's and out / lse equal pkv_decode's on that cache (the two
+ * calls' bounds, arguments and errors combined; k_new and v_new are
+ * required).  Several padding entries writing scratch page 0 race exactly as
+ * in pkv_append.
+ */
+int pkv_append_decode(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+                      const void *k_new, const void *v_new, const void *q,
+                      int32_t num_qo_heads, const int32_t *page_indptr,
+                      const int32_t *page_indices, const int32_t *last_page_len,
+                      int32_t batch, float sm_scale, void *out, float *lse,
+                      int32_t max_pages_per_req, int32_t kv_chunk_pages,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * pkv_validate_page_table -- debug check of HOST copies of a page table

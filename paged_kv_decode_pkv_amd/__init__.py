@@ -82,13 +82,14 @@ def _load():
     p, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.pkv_append.argtypes = [p, CacheDesc, i32, p, p, p, p, p, i32, p]
     lib.pkv_append.restype = ctypes.c_int
-    lib.pkv_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.pkv_decode_workspace_size.argtypes = [CacheDesc, i32, i32, i32, i32]
     lib.pkv_decode_workspace_size.restype = sz
-    lib.pkv_default_chunk_pages.argtypes = []
-    lib.pkv_default_chunk_pages.restype = i32
     lib.pkv_decode.argtypes = [p, CacheDesc, i32, p, i32, p, p, p, i32, ctypes.c_float,
                                p, p, i32, i32, p, sz, p]
     lib.pkv_decode.restype = ctypes.c_int
+    lib.pkv_append_decode.argtypes = [p, CacheDesc, i32, p, p, p, i32, p, p, p, i32,
+                                      ctypes.c_float, p, p, i32, i32, p, sz, p]
+    lib.pkv_append_decode.restype = ctypes.c_int
     lib.pkv_validate_page_table.argtypes = [p, p, p, i32, i32, i32, i32,
                                             ctypes.POINTER(i32)]
     lib.pkv_validate_page_table.restype = ctypes.c_int
@@ -113,14 +114,11 @@ def status_string(code: int) -> str:
     return lib.pkv_status_string(int(code)).decode()
 
 
-def default_chunk_pages() -> int:
-    return int(lib.pkv_default_chunk_pages())
-
-
-def workspace_size(batch: int, num_qo_heads: int, head_dim: int, max_pages_per_req: int,
-                   kv_chunk_pages: int = 0) -> int:
-    return int(lib.pkv_decode_workspace_size(batch, num_qo_heads, head_dim,
-                                             max_pages_per_req, kv_chunk_pages))
+def workspace_size(desc: CacheDesc, num_qo_heads: int, batch: int,
+                   max_pages_per_req: int, kv_chunk_pages: int = 0) -> int:
+    """Bytes of workspace pkv_decode / pkv_append_decode need (0: none)."""
+    return int(lib.pkv_decode_workspace_size(desc, num_qo_heads, batch, max_pages_per_req,
+                                             kv_chunk_pages))
 
 
 def cache_desc(kv_cache) -> CacheDesc:
@@ -182,16 +180,8 @@ def append(kv_cache, layer: int, k_new, v_new, page_indptr, page_indices, last_p
         raise PkvError(rc, "pkv_append")
 
 
-def decode(kv_cache, layer: int, q, page_indptr, page_indices, last_page_len,
-           sm_scale: float, max_pages_per_req: int, kv_chunk_pages: int = 0, out=None,
-           lse=None, with_lse: bool = True, workspace=None, stream=None):
-    """Attention of one query row per entry over its pages; returns (out, lse).
-
-    ``q`` is bf16 [batch, Hq, D]; ``out`` (bf16, same shape) and ``lse`` (fp32
-    [batch, Hq], natural log) are allocated when not given; ``lse`` is None
-    when ``with_lse`` is False and none is passed.  ``max_pages_per_req`` is
-    the host-side bound on any entry's page count.
-    """
+def _decode_outputs(kv_cache, q, out, lse, with_lse, workspace, max_pages_per_req,
+                    kv_chunk_pages):
     import torch
     desc = cache_desc(kv_cache)
     if q.dim() != 3 or q.shape[2] != desc.head_dim:
@@ -206,7 +196,7 @@ def decode(kv_cache, layer: int, q, page_indptr, page_indices, last_page_len,
         raise ValueError("out must match q")
     if lse is not None and tuple(lse.shape) != (batch, hq):
         raise ValueError("lse must be [batch, Hq]")
-    need = workspace_size(batch, hq, desc.head_dim, max_pages_per_req, kv_chunk_pages)
+    need = workspace_size(desc, hq, batch, max_pages_per_req, kv_chunk_pages)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = ctypes.c_void_p(0) if workspace is None else _dev_ptr(workspace, "workspace",
@@ -214,6 +204,26 @@ def decode(kv_cache, layer: int, q, page_indptr, page_indices, last_page_len,
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lse_ptr = ctypes.c_void_p(0) if lse is None else _dev_ptr(lse, "lse", torch.float32,
                                                               dev)
+    return desc, batch, hq, out, lse, lse_ptr, ws_ptr, ws_bytes
+
+
+def decode(kv_cache, layer: int, q, page_indptr, page_indices, last_page_len,
+           sm_scale: float, max_pages_per_req: int, kv_chunk_pages: int = 0, out=None,
+           lse=None, with_lse: bool = True, workspace=None, stream=None):
+    """Attention of one query row per entry over its pages; returns (out, lse).
+
+    ``q`` is bf16 [batch, Hq, D]; ``out`` (bf16, same shape) and ``lse`` (fp32
+    [batch, Hq], natural log) are allocated when not given; ``lse`` is None
+    when ``with_lse`` is False and none is passed.  ``max_pages_per_req`` is
+    the host-side bound on any entry's page count.  ``kv_chunk_pages`` 0 shares
+    the batch's tokens evenly over the GPU; > 0 cuts each entry into runs of
+    that many pages, which makes every row independent of the rest of the
+    batch, bit for bit.
+    """
+    import torch
+    desc, batch, hq, out, lse, lse_ptr, ws_ptr, ws_bytes = _decode_outputs(
+        kv_cache, q, out, lse, with_lse, workspace, max_pages_per_req, kv_chunk_pages)
+    dev = kv_cache.device
     rc = lib.pkv_decode(_dev_ptr(kv_cache, "kv_cache", torch.bfloat16), desc, int(layer),
                         _dev_ptr(q, "q", torch.bfloat16, dev), hq,
                         *_tables(kv_cache, page_indptr, page_indices, last_page_len),
@@ -223,6 +233,32 @@ def decode(kv_cache, layer: int, q, page_indptr, page_indices, last_page_len,
                         _stream(stream))
     if rc != PKV_OK:
         raise PkvError(rc, "pkv_decode")
+    return out, lse
+
+
+def append_decode(kv_cache, layer: int, k_new, v_new, q, page_indptr, page_indices,
+                  last_page_len, sm_scale: float, max_pages_per_req: int,
+                  kv_chunk_pages: int = 0, out=None, lse=None, with_lse: bool = True,
+                  workspace=None, stream=None):
+    """:func:`append` then :func:`decode` of one layer in a single pass."""
+    import torch
+    desc, batch, hq, out, lse, lse_ptr, ws_ptr, ws_bytes = _decode_outputs(
+        kv_cache, q, out, lse, with_lse, workspace, max_pages_per_req, kv_chunk_pages)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (batch, desc.num_kv_heads, desc.head_dim):
+            raise ValueError(f"{name} must be [batch, Hkv, D], got {tuple(t.shape)}")
+    dev = kv_cache.device
+    rc = lib.pkv_append_decode(_dev_ptr(kv_cache, "kv_cache", torch.bfloat16), desc,
+                               int(layer), _dev_ptr(k_new, "k_new", torch.bfloat16, dev),
+                               _dev_ptr(v_new, "v_new", torch.bfloat16, dev),
+                               _dev_ptr(q, "q", torch.bfloat16, dev), hq,
+                               *_tables(kv_cache, page_indptr, page_indices, last_page_len),
+                               batch, float(sm_scale),
+                               _dev_ptr(out, "out", torch.bfloat16, dev), lse_ptr,
+                               int(max_pages_per_req), int(kv_chunk_pages), ws_ptr,
+                               ws_bytes, _stream(stream))
+    if rc != PKV_OK:
+        raise PkvError(rc, "pkv_append_decode")
     return out, lse
 
 

@@ -33,6 +33,8 @@ int log2_int(int32_t x) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
 int check_desc(const pkv_cache_desc_t &d) {
     if (d.num_layers < 1 || d.num_pages < 1 || d.num_kv_heads < 1 || d.head_dim < 1)
         return PKV_ERR_BAD_SHAPE;
@@ -45,15 +47,130 @@ int64_t page_elems(const pkv_cache_desc_t &d) {
     return 2 * (int64_t)d.page_size * d.num_kv_heads * d.head_dim;
 }
 
-int32_t effective_chunk(int32_t kv_chunk_pages) {
-    return kv_chunk_pages == 0 ? pkv::kDefaultChunkPages : kv_chunk_pages;
+// How one pkv_decode call splits its work, and the workspace that needs.
+struct Plan {
+    int32_t chunk_tiles = 0;   // 0: balanced
+    int32_t max_chunks = 1;
+    int64_t slots = 0;         // partial rows per query head
+    int64_t ws_bytes = 0;
+    int64_t off_lse = 0, off_start = 0;
+};
+
+Plan make_plan(const pkv_cache_desc_t &d, int32_t num_qo_heads, int32_t batch,
+               int32_t max_pages_per_req, int32_t kv_chunk_pages) {
+    Plan p;
+    int32_t chunk_pages = kv_chunk_pages;
+    if (chunk_pages == 0 && batch > pkv::kMaxBalancedBatch)
+        chunk_pages = pkv::kFallbackChunkPages;
+    if (chunk_pages > 0) {
+        const int64_t tt = pkv::kTileTokens;
+        p.chunk_tiles = (int32_t)(((int64_t)chunk_pages * d.page_size + tt - 1) / tt);
+        const int64_t max_tiles = ((int64_t)max_pages_per_req * d.page_size + tt - 1) / tt;
+        p.max_chunks = (int32_t)((max_tiles + p.chunk_tiles - 1) / p.chunk_tiles);
+        if (p.max_chunks < 1)
+            p.max_chunks = 1;
+        p.slots = p.max_chunks > 1 ? (int64_t)batch * p.max_chunks : 0;
+    } else {
+        p.slots = pkv::balanced_groups_bound(d.num_kv_heads) + batch;
+    }
+    const int64_t rows = p.slots * num_qo_heads;
+    p.off_lse = align256(rows * d.head_dim * 4);
+    p.off_start = p.off_lse + align256(rows * 4);
+    const int64_t start_bytes = p.chunk_tiles > 0 ? 0 : align256(((int64_t)batch + 1) * 4);
+    p.ws_bytes = p.slots > 0 || start_bytes > 0 ? p.off_start + start_bytes : 0;
+    return p;
+}
+
+int check_decode_args(const pkv_cache_desc_t &desc, int32_t layer, int32_t num_qo_heads,
+                      int32_t batch, float sm_scale, int32_t max_pages_per_req,
+                      int32_t kv_chunk_pages) {
+    int rc = check_desc(desc);
+    if (rc != PKV_OK)
+        return rc;
+    if (layer < 0 || layer >= desc.num_layers || batch < 0 || num_qo_heads < 1 ||
+        num_qo_heads % desc.num_kv_heads != 0 || !isfinite(sm_scale) ||
+        max_pages_per_req < 1 || kv_chunk_pages < 0)
+        return PKV_ERR_BAD_SHAPE;
+    if (kv_chunk_pages > pkv::kMaxChunkPages)
+        return PKV_ERR_UNSUPPORTED;
+    const int group = num_qo_heads / desc.num_kv_heads;
+    if ((desc.head_dim != 64 && desc.head_dim != 128) || group > 8 ||
+        desc.num_kv_heads > pkv::kMaxKvHeads)
+        return PKV_ERR_UNSUPPORTED;
+    return PKV_OK;
+}
+
+int decode_common(const void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+                  const void *k_new, const void *v_new, const void *q, int32_t num_qo_heads,
+                  const int32_t *page_indptr, const int32_t *page_indices,
+                  const int32_t *last_page_len, int32_t batch, float sm_scale, void *out,
+                  float *lse, int32_t max_pages_per_req, int32_t kv_chunk_pages,
+                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_decode_args(desc, layer, num_qo_heads, batch, sm_scale, max_pages_per_req,
+                               kv_chunk_pages);
+    if (rc != PKV_OK)
+        return rc;
+    const bool fused = k_new != nullptr || v_new != nullptr;
+    if (batch == 0)
+        return PKV_OK;
+    if (!kv_cache || !q || !page_indptr || !page_indices || !last_page_len || !out ||
+        (fused && (!k_new || !v_new)))
+        return PKV_ERR_NULL_PTR;
+    if (!aligned16(kv_cache) || !aligned16(q) || !aligned16(out) ||
+        (fused && (!aligned16(k_new) || !aligned16(v_new))))
+        return PKV_ERR_ALIGNMENT;
+    const Plan plan = make_plan(desc, num_qo_heads, batch, max_pages_per_req, kv_chunk_pages);
+    if (plan.chunk_tiles > 0 && (int64_t)batch * plan.max_chunks > 0x7fffffffLL)
+        return PKV_ERR_BAD_SHAPE;
+    if (plan.ws_bytes > 0 &&
+        (workspace == nullptr || workspace_bytes < (size_t)plan.ws_bytes))
+        return PKV_ERR_WORKSPACE;
+    if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return PKV_ERR_ALIGNMENT;
+
+    pkv::DecodeArgs a;
+    const int64_t layer_off = (int64_t)layer * desc.num_pages * page_elems(desc);
+    a.cache = static_cast<const uint16_t *>(kv_cache) + layer_off;
+    a.cache_w = fused ? const_cast<uint16_t *>(a.cache) : nullptr;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k_new = static_cast<const uint16_t *>(k_new);
+    a.v_new = static_cast<const uint16_t *>(v_new);
+    a.indptr = page_indptr;
+    a.indices = page_indices;
+    a.last_len = last_page_len;
+    a.out = static_cast<uint16_t *>(out);
+    a.lse = lse;
+    char *ws = static_cast<char *>(workspace);
+    a.part_o = plan.slots ? reinterpret_cast<float *>(ws) : nullptr;
+    a.part_lse = plan.slots ? reinterpret_cast<float *>(ws + plan.off_lse) : nullptr;
+    a.tile_start = plan.chunk_tiles > 0 ? nullptr
+                                        : reinterpret_cast<int32_t *>(ws + plan.off_start);
+    a.page_stride = page_elems(desc);
+    a.half_stride = desc.page_size * desc.num_kv_heads * desc.head_dim;
+    a.row_stride = desc.num_kv_heads * desc.head_dim;
+    a.num_qo_heads = num_qo_heads;
+    a.num_kv_heads = desc.num_kv_heads;
+    a.num_pages = desc.num_pages;
+    a.batch = batch;
+    a.page_size = desc.page_size;
+    a.log2_page = log2_int(desc.page_size);
+    a.chunk_tiles = plan.chunk_tiles;
+    a.max_chunks = plan.max_chunks;
+    a.num_groups = 0;
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    const int group = num_qo_heads / desc.num_kv_heads;
+    if (plan.chunk_tiles == 0) {
+        hipError_t err = pkv::balanced_groups(desc.head_dim, group, desc.num_kv_heads,
+                                              desc.page_size, batch, &a.num_groups);
+        if (err != hipSuccess)
+            return hip_status(err);
+    }
+    return hip_status(pkv::launch_decode(a, desc.head_dim, group, stream));
 }
 
 }  // namespace
 
 extern "C" {
-
-int32_t pkv_default_chunk_pages(void) { return pkv::kDefaultChunkPages; }
 
 int pkv_last_hip_error(void) { return g_last_hip_error; }
 
@@ -62,10 +179,11 @@ const char *pkv_status_string(int status) {
     case PKV_OK: return "PKV_OK: success";
     case PKV_ERR_NULL_PTR: return "PKV_ERR_NULL_PTR: a required pointer is NULL";
     case PKV_ERR_BAD_SHAPE: return "PKV_ERR_BAD_SHAPE: a size, index or scale is out of range";
-    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED: shape not built (head_dim, group or page_size)";
+    case PKV_ERR_UNSUPPORTED:
+        return "PKV_ERR_UNSUPPORTED: shape not built (head_dim, group, heads or page_size)";
     case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE: workspace missing or too small";
     case PKV_ERR_HIP: return "PKV_ERR_HIP: the HIP runtime refused a launch";
-    case PKV_ERR_ALIGNMENT: return "PKV_ERR_ALIGNMENT: a bf16 array is not 16-byte aligned";
+    case PKV_ERR_ALIGNMENT: return "PKV_ERR_ALIGNMENT: an array is not aligned as required";
     case PKV_ERR_BAD_TABLE: return "PKV_ERR_BAD_TABLE: the page table breaks a precondition";
     default: return "unknown pkv status";
     }
@@ -102,17 +220,13 @@ int pkv_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void 
     return hip_status(pkv::launch_append(a, batch, stream));
 }
 
-size_t pkv_decode_workspace_size(int32_t batch, int32_t num_qo_heads, int32_t head_dim,
+size_t pkv_decode_workspace_size(pkv_cache_desc_t desc, int32_t num_qo_heads, int32_t batch,
                                  int32_t max_pages_per_req, int32_t kv_chunk_pages) {
-    const int32_t k = effective_chunk(kv_chunk_pages);
-    if (batch <= 0 || num_qo_heads <= 0 || head_dim <= 0 || max_pages_per_req <= 0 || k <= 0)
+    if (check_desc(desc) != PKV_OK || batch <= 0 || num_qo_heads <= 0 ||
+        max_pages_per_req <= 0 || kv_chunk_pages < 0)
         return 0;
-    const int64_t chunks = (max_pages_per_req + (int64_t)k - 1) / k;
-    if (chunks <= 1)
-        return 0;
-    const int64_t rows = (int64_t)batch * chunks * num_qo_heads;
-    const int64_t bytes = rows * head_dim * 4 + rows * 4 + 256;
-    return (size_t)((bytes + 255) / 256 * 256);
+    return (size_t)make_plan(desc, num_qo_heads, batch, max_pages_per_req, kv_chunk_pages)
+        .ws_bytes;
 }
 
 int pkv_decode(const void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *q,
@@ -120,59 +234,28 @@ int pkv_decode(const void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const
                const int32_t *last_page_len, int32_t batch, float sm_scale, void *out,
                float *lse, int32_t max_pages_per_req, int32_t kv_chunk_pages, void *workspace,
                size_t workspace_bytes, hipStream_t stream) {
-    int rc = check_desc(desc);
+    return decode_common(kv_cache, desc, layer, nullptr, nullptr, q, num_qo_heads,
+                         page_indptr, page_indices, last_page_len, batch, sm_scale, out, lse,
+                         max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes,
+                         stream);
+}
+
+int pkv_append_decode(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *k_new,
+                      const void *v_new, const void *q, int32_t num_qo_heads,
+                      const int32_t *page_indptr, const int32_t *page_indices,
+                      const int32_t *last_page_len, int32_t batch, float sm_scale, void *out,
+                      float *lse, int32_t max_pages_per_req, int32_t kv_chunk_pages,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    const int rc = check_decode_args(desc, layer, num_qo_heads, batch, sm_scale,
+                                     max_pages_per_req, kv_chunk_pages);
     if (rc != PKV_OK)
         return rc;
-    if (layer < 0 || layer >= desc.num_layers || batch < 0 || num_qo_heads < 1 ||
-        num_qo_heads % desc.num_kv_heads != 0 || !isfinite(sm_scale) ||
-        max_pages_per_req < 1 || kv_chunk_pages < 0)
-        return PKV_ERR_BAD_SHAPE;
-    const int32_t chunk = effective_chunk(kv_chunk_pages);
-    if (chunk > pkv::kMaxChunkPages)
-        return PKV_ERR_UNSUPPORTED;
-    const int group = num_qo_heads / desc.num_kv_heads;
-    if ((desc.head_dim != 64 && desc.head_dim != 128) || group > 8)
-        return PKV_ERR_UNSUPPORTED;
-    if (batch == 0)
-        return PKV_OK;
-    if (!kv_cache || !q || !page_indptr || !page_indices || !last_page_len || !out)
+    if (batch > 0 && (k_new == nullptr || v_new == nullptr))
         return PKV_ERR_NULL_PTR;
-    if (!aligned16(kv_cache) || !aligned16(q) || !aligned16(out))
-        return PKV_ERR_ALIGNMENT;
-    const int64_t max_chunks = (max_pages_per_req + (int64_t)chunk - 1) / chunk;
-    if ((int64_t)desc.num_kv_heads * max_chunks * batch > 0x7fffffffLL)
-        return PKV_ERR_BAD_SHAPE;
-    const size_t need = pkv_decode_workspace_size(batch, num_qo_heads, desc.head_dim,
-                                                  max_pages_per_req, kv_chunk_pages);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-        return PKV_ERR_WORKSPACE;
-    if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return PKV_ERR_ALIGNMENT;
-
-    pkv::DecodeArgs a;
-    a.cache = static_cast<const uint16_t *>(kv_cache) +
-              (int64_t)layer * desc.num_pages * page_elems(desc);
-    a.q = static_cast<const uint16_t *>(q);
-    a.indptr = page_indptr;
-    a.indices = page_indices;
-    a.last_len = last_page_len;
-    a.out = static_cast<uint16_t *>(out);
-    a.lse = lse;
-    const int64_t rows = (int64_t)batch * max_chunks * num_qo_heads;
-    a.part_o = need ? static_cast<float *>(workspace) : nullptr;
-    a.part_lse = need ? static_cast<float *>(workspace) + rows * desc.head_dim : nullptr;
-    a.page_stride = page_elems(desc);
-    a.half_stride = desc.page_size * desc.num_kv_heads * desc.head_dim;
-    a.row_stride = desc.num_kv_heads * desc.head_dim;
-    a.num_qo_heads = num_qo_heads;
-    a.num_kv_heads = desc.num_kv_heads;
-    a.num_pages = desc.num_pages;
-    a.max_chunks = (int32_t)max_chunks;
-    a.chunk_pages = chunk;
-    a.page_size = desc.page_size;
-    a.log2_page = log2_int(desc.page_size);
-    a.scale_log2 = sm_scale * 1.4426950408889634f;
-    return hip_status(pkv::launch_decode(a, desc.head_dim, group, batch, stream));
+    return decode_common(kv_cache, desc, layer, k_new, v_new, q, num_qo_heads, page_indptr,
+                         page_indices, last_page_len, batch, sm_scale, out, lse,
+                         max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes,
+                         stream);
 }
 
 int pkv_validate_page_table(const int32_t *page_indptr, const int32_t *page_indices,
@@ -188,8 +271,7 @@ int pkv_validate_page_table(const int32_t *page_indptr, const int32_t *page_indi
         return PKV_ERR_NULL_PTR;
     if (page_indptr[0] != 0)
         return PKV_ERR_BAD_TABLE;
-    // slot owner per (page, slot) of real pages, to catch two appends landing
-    // on one slot; sized on demand
+    // which entry appends into each real page (tail pages only)
     int32_t *owner = static_cast<int32_t *>(malloc(sizeof(int32_t) * (size_t)num_pages));
     if (!owner)
         return PKV_ERR_BAD_SHAPE;
@@ -210,10 +292,9 @@ int pkv_validate_page_table(const int32_t *page_indptr, const int32_t *page_indi
         if (ok && uses_zero)
             ok = n == 1 && last == 1;   // a padding entry
         if (ok && !uses_zero) {
+            // the append target is (tail page, last - 1); a real table never
+            // lets two entries share a tail page, so any repeat is reported
             const int32_t tail = page_indices[page_indptr[b + 1] - 1];
-            // the append target is (tail, last - 1); two entries may share a
-            // tail page only at different slots, which a real table never
-            // does, so any repeat of a tail page is reported
             ok = owner[tail] < 0;
             owner[tail] = b;
         }

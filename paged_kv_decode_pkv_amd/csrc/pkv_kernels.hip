@@ -8,31 +8,43 @@
 //
 //  * Decode streams K/V once from HBM and is bandwidth-bound (about g flops
 //    per byte for a GQA group of g query heads), so it uses the vector ALUs,
-//    not MFMA.  q.k runs on v_dot2_f32_bf16 straight from the bf16 words:
-//    no conversion of K, products exact, fp32 accumulation.
-//  * Eight lanes cover one token row of one KV head; each lane owns D/8
-//    contiguous elements.  One 16-byte load per lane then reads 8 whole rows
-//    of 128 bytes (D = 64) or the first or second half of 8 rows of 256 bytes
-//    (D = 128): every request is full cache-line segments.
-//  * The 8-lane partial dot products are summed with three DPP steps
-//    (quad_perm, quad_perm, row_half_mirror), so every lane of a row holds
-//    the score without LDS traffic.
-//  * Each group of 8 lanes (a "row group") keeps its own online-softmax state
-//    in the exp2 domain.  The running maximum is raised only when a new score
-//    exceeds it by more than kTau (log2 units): between raises no rescaling
-//    is done, and exp2 arguments stay <= kTau, so nothing overflows.
-//  * A workgroup owns one (entry, KV head, chunk of pages); its waves take
-//    the chunk's 8-token tiles round robin with a two-block register
-//    pipeline (the next block's loads are in flight while the current one is
-//    computed).  Row groups and waves are merged through DPP/LDS at the end.
-//  * A chunk is a fixed run of pages, so how an entry is split depends only
-//    on its own length: results do not depend on the rest of the batch.
-//    Entries with one chunk write bf16 out / fp32 lse directly; longer ones
-//    write fp32 partials that the merge kernel combines by log-sum-exp.
+//    not MFMA.  q.k runs on v_dot2_f32_bf16 straight from the bf16 words: no
+//    conversion of K, exact products, fp32 accumulation.
+//  * A workgroup has one wavefront per KV head.  In a wave, eight lanes cover
+//    one token row of its head (D/8 contiguous elements each) and the eight
+//    8-lane row groups cover 8 consecutive tokens: an 8-token "tile".  One
+//    16-byte load per lane reads 8 rows x 128 bytes, and the workgroup as a
+//    whole reads each tile's K rows and V rows of all heads, 16 KiB apiece
+//    for 8 heads of 128, as contiguous runs.
+//  * Partial dot products of a row are summed with three DPP steps
+//    (quad_perm, quad_perm, row_half_mirror): no LDS traffic.
+//  * Each row group keeps its own online-softmax state in the exp2 domain.
+//    The running maximum is raised only when a new score passes it by more
+//    than kTau (log2 units); between raises nothing is rescaled and exp2
+//    arguments stay <= kTau.  Row groups are merged once per segment.
+//  * Loads run two blocks of TB tiles ahead in registers (three rotating
+//    buffers; see run_segment).
+//
+// Work split.  Balanced mode (default): the tiles of all entries are laid end
+// to end and each of W workgroups takes an equal run of them (W = what the
+// chip holds at once), so every compute unit streams the same number of
+// bytes.  A run may cover several entries and an entry may span several runs;
+// each (run, entry) segment writes either the final row (entry entirely in
+// the run) or a partial (output, lse) into slot run + entry, and the merge
+// kernel combines an entry's partials by log-sum-exp.  The split then depends
+// on the whole batch.  Fixed mode (chunk_tiles > 0): each entry is cut into
+// chunks of a fixed number of tiles, one workgroup each, so how an entry is
+// split depends only on its own length and its rows are bit-identical in any
+// batch.
+//
+// The fused append (k_new != null) treats the tile holding token L-1 of each
+// entry specially: that row is read from k_new/v_new and written into the
+// cache by the one workgroup that processes it, which is append followed by
+// decode without a second pass over memory.
 //
 // All cache offsets are 64-bit.  Page ids outside [0, num_pages) are read as
-// scratch page 0 and an append with an out-of-range page or slot writes
-// nothing, so a malformed table can give wrong rows but never a fault.
+// scratch page 0, and an append with an out-of-range page or slot writes
+// nothing: a malformed table can give wrong rows but never a fault.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -80,19 +92,16 @@ __device__ __forceinline__ float sum_row8(float x) {
 }
 
 // Reductions across the 8 row groups of a wave (lanes with equal lane % 8).
-__device__ __forceinline__ float xor_rows(float x, int mask) {
-    return __shfl_xor(x, mask, 64);
-}
 __device__ __forceinline__ float max_across_rows(float x) {
     x = fmaxf(x, dpp<0x128>(x));        // row_ror:8 within 16 lanes = lane ^ 8
-    x = fmaxf(x, xor_rows(x, 16));
-    x = fmaxf(x, xor_rows(x, 32));
+    x = fmaxf(x, __shfl_xor(x, 16, 64));
+    x = fmaxf(x, __shfl_xor(x, 32, 64));
     return x;
 }
 __device__ __forceinline__ float sum_across_rows(float x) {
     x += dpp<0x128>(x);
-    x += xor_rows(x, 16);
-    x += xor_rows(x, 32);
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
     return x;
 }
 
@@ -103,9 +112,19 @@ __device__ __forceinline__ uint4 load16(const uint16_t *p) {
     return *reinterpret_cast<const uint4 *>(p);
 }
 
+// Tiles (8 tokens) of entry b; 0 for a malformed entry with no page.
+__device__ __forceinline__ int entry_tiles(const DecodeArgs &a, int b) {
+    const int n = a.indptr[b + 1] - a.indptr[b];
+    if (n < 1)
+        return 0;
+    int last = a.last_len[b];
+    last = last < 1 ? 1 : (last > a.page_size ? a.page_size : last);
+    return ((n - 1) * a.page_size + last + kTileTokens - 1) / kTileTokens;
+}
+
 // ---------------------------------------------------------------------------
-// Append: one workgroup per entry copies its K row then its V row, 16 bytes a
-// thread.
+// Standalone append: one workgroup per entry copies its K row then its V row,
+// 16 bytes a thread.
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int b = blockIdx.x;
     const int end = a.indptr[b + 1];
@@ -128,59 +147,38 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split decode pass.  Grid: one workgroup per (KV head h, chunk c, entry b),
-// h fastest.  D: head dim (64 | 128); G: query heads per KV head; NW: waves
-// per workgroup; TB: tiles per pipeline block; SMALL_PAGE: page_size < 8, so
-// one 8-token tile may span several pages.
-template <int D, int G, int NW, int TB, bool SMALL_PAGE>
-__global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a) {
+// Attention of KV head h's G query heads over tiles [lt0, lt1) of entry b,
+// run by one wavefront.  Writes the final rows when `whole`, else a partial
+// into `slot`.
+//
+// Pipeline: three rotating register buffers of TB tiles (A, B, C); while one
+// block is computed the next two are in flight.  Every load is issued
+// unconditionally -- a tile past the end of the segment reloads its last tile,
+// a cache hit, and is masked -- so at each compute the same two blocks are
+// outstanding on every path and the compiler's waits keep them in flight.
+template <int D, int G, int TB, bool SMALL_PAGE>
+__device__ __forceinline__ void run_segment(const DecodeArgs &a, int b, int h, int lt0,
+                                            int lt1, bool whole, int slot) {
     constexpr int NLD = D / 64;   // 16-byte words per lane per token row
-    __shared__ float sm_m[NW][G];
-    __shared__ float sm_l[NW][G];
-    __shared__ float sm_acc[NW][G][D];
-
+    // segment bounds are uniform across the wave: keep them in SGPRs
+    b = __builtin_amdgcn_readfirstlane(b);
+    lt0 = __builtin_amdgcn_readfirstlane(lt0);
+    lt1 = __builtin_amdgcn_readfirstlane(lt1);
+    slot = __builtin_amdgcn_readfirstlane(slot);
+    whole = __builtin_amdgcn_readfirstlane((int)whole) != 0;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
-    const int rg = lane >> 3;   // row group: token within a tile
-    const int j = lane & 7;     // element slice [8j, 8j+8) (+64 for D = 128)
-
-    int id = blockIdx.x;
-    const int h = id % a.num_kv_heads;
-    id /= a.num_kv_heads;
-    const int c = id % a.max_chunks;
-    const int b = id / a.max_chunks;
+    const int rg = lane >> 3;     // token within a tile
+    const int j = lane & 7;       // element slice [8j, 8j+8) (+64 for D = 128)
 
     const int p0 = a.indptr[b];
     const int npages = a.indptr[b + 1] - p0;
-    if (npages < 1)
-        return;
-    const int nchunks = (npages + a.chunk_pages - 1) / a.chunk_pages;
-    const int hq0 = h * G;
-    if (nchunks > a.max_chunks) {
-        // The entry is longer than the launch allows: poison its rows so the
-        // broken precondition is visible instead of silently truncated.
-        if (c == 0) {
-            const float nan = __builtin_nanf("");
-            for (int i = threadIdx.x; i < G * D; i += NW * 64)
-                a.out[((int64_t)b * a.num_qo_heads + hq0) * D + i] = 0x7FC0;
-            if (a.lse != nullptr && threadIdx.x < G)
-                a.lse[(int64_t)b * a.num_qo_heads + hq0 + threadIdx.x] = nan;
-        }
-        return;
-    }
-    if (c >= nchunks)
-        return;
     int last = a.last_len[b];
     last = last < 1 ? 1 : (last > a.page_size ? a.page_size : last);
     const int len = (npages - 1) * a.page_size + last;
-    const int tok0 = c * a.chunk_pages * a.page_size;
-    const int clen = min(a.chunk_pages * a.page_size, len - tok0);
-    const int cpages = min(a.chunk_pages, npages - c * a.chunk_pages);
-    const int ntiles = (clen + 7) >> 3;
-
-    // Page ids of this chunk, one per lane (chunk_pages <= 64).
-    int my_page = lane < cpages ? a.indices[p0 + c * a.chunk_pages + lane] : 0;
-    my_page = (my_page >= 0 && my_page < a.num_pages) ? my_page : 0;
+    const int last_tile = (len - 1) / kTileTokens;
+    const int hq0 = h * G;
+    const bool fused = a.k_new != nullptr;
+    const int64_t new_row = ((int64_t)b * a.num_kv_heads + h) * D + j * 8;
 
     // q rows of the G query heads that read KV head h, this lane's slice.
     uint32_t qv[G][NLD][4];
@@ -210,161 +208,190 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a) {
                 acc[g][i][e] = 0.f;
     }
 
-    // This wave's tiles are wave, wave + NW, ...; nt of them in nblk blocks.
-    const int nt = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
-    const int nblk = (nt + TB - 1) / TB;
-    const uint16_t *head_base = a.cache + h * D + j * 8;
-
     struct Block {
         uint4 k[TB][NLD];
         uint4 v[TB][NLD];
     };
 
-    // Issue the loads of block kb.  Tiles past the wave's last one reload the
-    // last tile (an L1/L2 hit) and are masked in compute.
-    auto load_block = [&](Block &blk, int kb) {
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            const int kt = min(kb * TB + tb, nt - 1);
-            const int t = wave + kt * NW;
-            const int tok = t * 8 + rg;
-            int page;
-            if (SMALL_PAGE)
-                page = __shfl(my_page, tok >> a.log2_page, 64);
-            else
-                page = __builtin_amdgcn_readlane(my_page, (t * 8) >> a.log2_page);
-            const int slot = tok & (a.page_size - 1);
-            const uint16_t *row = head_base + (int64_t)page * a.page_stride +
-                                  (int64_t)(slot * a.row_stride);
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                blk.k[tb][i] = load16(row + i * 64);
-                blk.v[tb][i] = load16(row + a.half_stride + i * 64);
-            }
-        }
-    };
+    // Windows of at most 64 pages: their ids sit one per lane.
+    for (int s0 = lt0; s0 < lt1;) {
+        const int fp = (s0 * kTileTokens) >> a.log2_page;    // first page of window
+        const int s1 = min(lt1, (int)((((int64_t)fp + 64) << a.log2_page) / kTileTokens));
+        int my_page = (fp + lane < npages) ? a.indices[p0 + fp + lane] : 0;
+        my_page = (my_page >= 0 && my_page < a.num_pages) ? my_page : 0;
+        const int nblk = (s1 - s0 + TB - 1) / TB;
 
-    auto compute_block = [&](const Block &blk, int kb) {
-        // Does this block hold a token at or past the chunk end?  (uniform)
-        const bool edge = (wave + ((kb + 1) * TB - 1) * NW + 1) * 8 > clen;
-        float s[TB][G];
+        // Issue the loads of block kb (tiles s0 + kb*TB + tb); tiles past s1
+        // reload tile s1 - 1.  The tile holding a fused append's new token
+        // takes that row from k_new / v_new: same number of loads either way.
+        auto load_block = [&](Block &blk, int kb) {
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float d = 0.f;
-#pragma unroll
-                for (int i = 0; i < NLD; ++i) {
-                    d = dot2_bf16(qv[g][i][0], blk.k[tb][i].x, d);
-                    d = dot2_bf16(qv[g][i][1], blk.k[tb][i].y, d);
-                    d = dot2_bf16(qv[g][i][2], blk.k[tb][i].z, d);
-                    d = dot2_bf16(qv[g][i][3], blk.k[tb][i].w, d);
+            for (int tb = 0; tb < TB; ++tb) {
+                const int t = min(s0 + kb * TB + tb, s1 - 1);
+                const int tok = t * kTileTokens + rg;
+                const int sl = tok & (a.page_size - 1);
+                const uint16_t *row;
+                if (SMALL_PAGE) {
+                    const int page = __shfl(my_page, (tok >> a.log2_page) - fp, 64);
+                    row = a.cache + (int64_t)page * a.page_stride + h * D +
+                          (uint32_t)(sl * a.row_stride + j * 8);
+                } else {
+                    const int page = __builtin_amdgcn_readlane(
+                        my_page, ((t * kTileTokens) >> a.log2_page) - fp);
+                    const uint16_t *base = a.cache + (int64_t)page * a.page_stride + h * D;
+                    row = base + (uint32_t)(sl * a.row_stride + j * 8);
                 }
-                s[tb][g] = sum_row8(d) * a.scale_log2;
-            }
-        bool ok[TB];
+                if (fused && t == last_tile) {
+                    const bool is_new = tok == len - 1;
+                    const uint16_t *kr = is_new ? a.k_new + new_row : row;
+                    const uint16_t *vr = is_new ? a.v_new + new_row : row + a.half_stride;
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            const int tok = (wave + (kb * TB + tb) * NW) * 8 + rg;
-            ok[tb] = tok < clen;
-        }
-        if (edge) {
+                    for (int i = 0; i < NLD; ++i) {
+                        blk.k[tb][i] = load16(kr + i * 64);
+                        blk.v[tb][i] = load16(vr + i * 64);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < NLD; ++i) {
+                        blk.k[tb][i] = load16(row + i * 64);
+                        blk.v[tb][i] = load16(row + a.half_stride + i * 64);
+                    }
+                }
+            }
+        };
+
+        auto compute_block = [&](const Block &blk, int kb) {
+            const int tfirst = s0 + kb * TB;
+            // Does this block hold a clamped tile or a token past the end?
+            const bool edge = (tfirst + TB > s1) || ((tfirst + TB) * kTileTokens > len);
+            float s[TB][G];
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-                for (int g = 0; g < G; ++g)
-                    s[tb][g] = ok[tb] ? s[tb][g] : -INFINITY;
-        }
-        // Lazy maximum: raise m only when a score passes it by more than kTau.
-        float mb[G];
-        bool raise_any = false;
+                for (int g = 0; g < G; ++g) {
+                    float d = 0.f;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            mb[g] = s[0][g];
+                    for (int i = 0; i < NLD; ++i) {
+                        d = dot2_bf16(qv[g][i][0], blk.k[tb][i].x, d);
+                        d = dot2_bf16(qv[g][i][1], blk.k[tb][i].y, d);
+                        d = dot2_bf16(qv[g][i][2], blk.k[tb][i].z, d);
+                        d = dot2_bf16(qv[g][i][3], blk.k[tb][i].w, d);
+                    }
+                    s[tb][g] = sum_row8(d) * a.scale_log2;
+                }
+            bool ok[TB];
 #pragma unroll
-            for (int tb = 1; tb < TB; ++tb)
-                mb[g] = fmaxf(mb[g], s[tb][g]);
-            raise_any |= mb[g] > m[g] + kTau;
-        }
-        if (raise_any) {
+            for (int tb = 0; tb < TB; ++tb) {
+                const int t = tfirst + tb;
+                ok[tb] = (t < s1) && (t * kTileTokens + rg < len);
+            }
+            if (edge) {
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        s[tb][g] = ok[tb] ? s[tb][g] : -INFINITY;
+            }
+            // Lazy maximum: raise m only when a score passes it by more than kTau.
+            float mb[G];
+            bool raise_any = false;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const bool up = mb[g] > m[g] + kTau;
-                const float mn = up ? mb[g] : m[g];
-                const float alpha = up ? exp2_fast(m[g] - mn) : 1.f;
-                m[g] = mn;
-                l[g] *= alpha;
+                mb[g] = s[0][g];
 #pragma unroll
-                for (int i = 0; i < NLD; ++i)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[g][i][e] *= alpha;
+                for (int tb = 1; tb < TB; ++tb)
+                    mb[g] = fmaxf(mb[g], s[tb][g]);
+                raise_any |= mb[g] > m[g] + kTau;
             }
-        }
+            if (raise_any) {
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            float vf[NLD][8];
+                for (int g = 0; g < G; ++g) {
+                    const bool up = mb[g] > m[g] + kTau;
+                    const float mn = up ? mb[g] : m[g];
+                    const float alpha = up ? exp2_fast(m[g] - mn) : 1.f;
+                    m[g] = mn;
+                    l[g] *= alpha;
 #pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                const uint4 w = blk.v[tb][i];
-                vf[i][0] = bf16_lo(w.x);
-                vf[i][1] = bf16_hi(w.x);
-                vf[i][2] = bf16_lo(w.y);
-                vf[i][3] = bf16_hi(w.y);
-                vf[i][4] = bf16_lo(w.z);
-                vf[i][5] = bf16_hi(w.z);
-                vf[i][6] = bf16_lo(w.w);
-                vf[i][7] = bf16_hi(w.w);
-            }
-            if (edge && !ok[tb]) {
-                // stale rows past the end may hold anything, NaN included
+                    for (int i = 0; i < NLD; ++i)
 #pragma unroll
-                for (int i = 0; i < NLD; ++i)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        vf[i][e] = 0.f;
+                        for (int e = 0; e < 8; ++e)
+                            acc[g][i][e] *= alpha;
+                }
             }
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float p = exp2_fast(s[tb][g] - m[g]);
-                if (edge)
-                    p = ok[tb] ? p : 0.f;   // also covers -inf - -inf
-                l[g] += p;
+            for (int tb = 0; tb < TB; ++tb) {
+                float vf[NLD][8];
 #pragma unroll
-                for (int i = 0; i < NLD; ++i)
+                for (int i = 0; i < NLD; ++i) {
+                    const uint4 w = blk.v[tb][i];
+                    vf[i][0] = bf16_lo(w.x);
+                    vf[i][1] = bf16_hi(w.x);
+                    vf[i][2] = bf16_lo(w.y);
+                    vf[i][3] = bf16_hi(w.y);
+                    vf[i][4] = bf16_lo(w.z);
+                    vf[i][5] = bf16_hi(w.z);
+                    vf[i][6] = bf16_lo(w.w);
+                    vf[i][7] = bf16_hi(w.w);
+                }
+                if (edge && !ok[tb]) {
+                    // stale rows past the end may hold anything, NaN included
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[g][i][e] = fmaf(p, vf[i][e], acc[g][i][e]);
+                    for (int i = 0; i < NLD; ++i)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            vf[i][e] = 0.f;
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    float p = exp2_fast(s[tb][g] - m[g]);
+                    if (edge)
+                        p = ok[tb] ? p : 0.f;   // also covers -inf - -inf
+                    l[g] += p;
+#pragma unroll
+                    for (int i = 0; i < NLD; ++i)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[g][i][e] = fmaf(p, vf[i][e], acc[g][i][e]);
+                }
             }
-        }
-    };
+        };
 
-    // Two-buffer pipeline written so that every compute is preceded, on every
-    // path, by exactly the loads of the other buffer: the compiler's wait then
-    // leaves that other buffer's loads in flight.
-    if (nblk > 0) {
-        Block A, B;
+        Block A, B, C;
         load_block(A, 0);
-        int kb = 0;
-        for (;;) {
-            if (kb + 1 >= nblk) {
-                compute_block(A, kb);
-                break;
-            }
-            load_block(B, kb + 1);
+        load_block(B, 1);
+        for (int kb = 0;;) {
+            load_block(C, kb + 2);
             compute_block(A, kb);
-            ++kb;
-            if (kb + 1 >= nblk) {
-                compute_block(B, kb);
+            if (++kb >= nblk)
                 break;
-            }
-            load_block(A, kb + 1);
+            load_block(A, kb + 2);
             compute_block(B, kb);
-            ++kb;
+            if (++kb >= nblk)
+                break;
+            load_block(B, kb + 2);
+            compute_block(C, kb);
+            if (++kb >= nblk)
+                break;
+        }
+        s0 = s1;
+    }
+
+    // Fused append: the row group holding token L-1 copies k_new / v_new of
+    // head h into the cache slot the standalone append would write.
+    if (fused && last_tile >= lt0 && last_tile < lt1 && rg == ((len - 1) & (kTileTokens - 1))) {
+        int page = a.indices[p0 + npages - 1];
+        page = (page >= 0 && page < a.num_pages) ? page : 0;
+        uint16_t *dst = a.cache_w + (int64_t)page * a.page_stride + h * D +
+                        (int64_t)(((len - 1) & (a.page_size - 1)) * a.row_stride) + j * 8;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            *reinterpret_cast<uint4 *>(dst + i * 64) = load16(a.k_new + new_row + i * 64);
+            *reinterpret_cast<uint4 *>(dst + a.half_stride + i * 64) =
+                load16(a.v_new + new_row + i * 64);
         }
     }
 
-    // Merge the 8 row groups of this wave.
+    // Merge the 8 row groups; every lane ends with the totals.
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const float mw = max_across_rows(m[g]);
@@ -377,153 +404,375 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a) {
                 acc[g][i][e] = sum_across_rows(acc[g][i][e] * f);
         m[g] = mw;
     }
-    if (rg == 0) {
+
+    // Row group g writes query head hq0 + g.
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < G; ++g) {
+        if (rg != g)
+            continue;
+        const int hq = hq0 + g;
+        const float inv = 1.f / l[g];
+        if (whole) {
+            uint16_t *o = a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8;
 #pragma unroll
-            for (int i = 0; i < NLD; ++i)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    sm_acc[wave][g][i * 64 + j * 8 + e] = acc[g][i][e];
-            if (j == 0) {
-                sm_m[wave][g] = m[g];
-                sm_l[wave][g] = l[g];
+            for (int i = 0; i < NLD; ++i) {
+                uint4 w;
+                w.x = pack_bf16x2(acc[g][i][0] * inv, acc[g][i][1] * inv);
+                w.y = pack_bf16x2(acc[g][i][2] * inv, acc[g][i][3] * inv);
+                w.z = pack_bf16x2(acc[g][i][4] * inv, acc[g][i][5] * inv);
+                w.w = pack_bf16x2(acc[g][i][6] * inv, acc[g][i][7] * inv);
+                *reinterpret_cast<uint4 *>(o + i * 64) = w;
             }
+            if (a.lse != nullptr && j == 0)
+                a.lse[(int64_t)b * a.num_qo_heads + hq] = (m[g] + log2_fast(l[g])) * kLn2;
+        } else {
+            const int64_t row = (int64_t)slot * a.num_qo_heads + hq;
+            float *o = a.part_o + row * D + j * 8;
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                *reinterpret_cast<float4 *>(o + i * 64) =
+                    make_float4(acc[g][i][0] * inv, acc[g][i][1] * inv, acc[g][i][2] * inv,
+                                acc[g][i][3] * inv);
+                *reinterpret_cast<float4 *>(o + i * 64 + 4) =
+                    make_float4(acc[g][i][4] * inv, acc[g][i][5] * inv, acc[g][i][6] * inv,
+                                acc[g][i][7] * inv);
+            }
+            if (j == 0)
+                a.part_lse[row] = m[g] + log2_fast(l[g]);
         }
     }
-    __syncthreads();
+}
 
-    // Merge the waves and write: one thread per pair of output elements.
-    for (int pi = threadIdx.x; pi < G * D / 2; pi += NW * 64) {
-        const int g = pi / (D / 2);
-        const int e2 = (pi % (D / 2)) * 2;
-        float mx = -INFINITY;
+// Exclusive scan of one int per thread over the workgroup (<= 16 waves).
+__device__ int block_exclusive_scan(int v, int *s_wave, int &total) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nwaves = (blockDim.x + 63) >> 6;
+    int x = v;
 #pragma unroll
-        for (int w = 0; w < NW; ++w)
-            mx = fmaxf(mx, sm_m[w][g]);
-        float sum = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d)
+            x += y;
+    }
+    if (lane == 63)
+        s_wave[wave] = x;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int w = lane < nwaves ? s_wave[lane] : 0;
+        int sc = w;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float mw = sm_m[w][g];
-            const float f = (mw == -INFINITY) ? 0.f : exp2_fast(mw - mx);
-            sum += sm_l[w][g] * f;
-            o0 += sm_acc[w][g][e2] * f;
-            o1 += sm_acc[w][g][e2 + 1] * f;
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(sc, d, 64);
+            if (lane >= d)
+                sc += y;
         }
-        const float inv = 1.f / sum;
-        const int hq = hq0 + g;
-        if (nchunks == 1) {
-            const int64_t o = ((int64_t)b * a.num_qo_heads + hq) * D + e2;
-            *reinterpret_cast<uint32_t *>(a.out + o) = pack_bf16x2(o0 * inv, o1 * inv);
-            if (a.lse != nullptr && e2 == 0)
-                a.lse[(int64_t)b * a.num_qo_heads + hq] = (mx + log2_fast(sum)) * kLn2;
-        } else {
-            const int64_t row = ((int64_t)b * a.max_chunks + c) * a.num_qo_heads + hq;
-            *reinterpret_cast<float2 *>(a.part_o + row * D + e2) =
-                make_float2(o0 * inv, o1 * inv);
-            if (e2 == 0)
-                a.part_lse[row] = mx + log2_fast(sum);
+        if (lane < nwaves)
+            s_wave[lane] = sc - w;     // exclusive prefix of wave totals
+        if (lane == nwaves - 1)
+            s_wave[16] = sc;           // grand total
+    }
+    __syncthreads();
+    total = s_wave[16];
+    return s_wave[wave] + x - v;
+}
+
+// ---------------------------------------------------------------------------
+// Decode pass.  Block: one wavefront per KV head.  Balanced mode: grid =
+// num_groups workgroups over the flattened tiles.  Fixed mode: grid =
+// batch * max_chunks, one workgroup per (entry, chunk).
+template <int D, int G, int TB, bool SMALL_PAGE>
+__global__ __launch_bounds__(kMaxWavesPerGroup * 64) void decode_kernel(DecodeArgs a) {
+    extern __shared__ int s_start[];   // [batch + 1] tile prefix sums (balanced)
+    __shared__ int s_wave[17];
+    // KV head of this wave: blockIdx.y picks a group of up to kMaxWavesPerGroup
+    // heads, one wave each (a grid dimension rather than a loop over heads)
+    const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * (blockDim.x >> 6) +
+                                                 (threadIdx.x >> 6));
+    // Waves past the last head (when Hkv is not a multiple of the group size)
+    // do no attention work but still take every barrier below.
+    const bool has_head = h < a.num_kv_heads;
+
+    if (a.chunk_tiles > 0) {
+        if (!has_head)
+            return;     // the fixed mode has no barrier
+        const int c = blockIdx.x % a.max_chunks;
+        const int b = blockIdx.x / a.max_chunks;
+        const int nt = entry_tiles(a, b);
+        const int nchunks = (nt + a.chunk_tiles - 1) / a.chunk_tiles;
+        if (nchunks > a.max_chunks) {
+            // Longer than the launch allows: poison the rows so the broken
+            // precondition shows instead of silently truncating.
+            if (c == 0) {
+                const int lane = threadIdx.x & 63;
+                for (int i = lane; i < G * D; i += 64)
+                    a.out[((int64_t)b * a.num_qo_heads + h * G) * D + i] = 0x7FC0;
+                if (a.lse != nullptr && lane < G)
+                    a.lse[(int64_t)b * a.num_qo_heads + h * G + lane] = __builtin_nanf("");
+            }
+            return;
         }
+        if (c >= nchunks)
+            return;
+        const int lt0 = c * a.chunk_tiles;
+        const int lt1 = min(nt, lt0 + a.chunk_tiles);
+        run_segment<D, G, TB, SMALL_PAGE>(a, b, h, lt0, lt1, nchunks == 1,
+                                          b * a.max_chunks + c);
+        return;
+    }
+
+    // Balanced: prefix sums of tiles per entry, in LDS.
+    const int nthreads = blockDim.x;
+    const int per = (a.batch + nthreads - 1) / nthreads;
+    const int e0 = min(a.batch, (int)threadIdx.x * per);
+    const int e1 = min(a.batch, e0 + per);
+    int local = 0;
+    for (int e = e0; e < e1; ++e) {
+        const int t = entry_tiles(a, e);
+        s_start[e] = t;
+        local += t;
+    }
+    int total = 0;
+    int run = block_exclusive_scan(local, s_wave, total);
+    for (int e = e0; e < e1; ++e) {
+        const int t = s_start[e];
+        s_start[e] = run;
+        run += t;
+    }
+    if (threadIdx.x == 0)
+        s_start[a.batch] = total;
+    __syncthreads();
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+        for (int e = threadIdx.x; e <= a.batch; e += nthreads)
+            a.tile_start[e] = s_start[e];
+
+    // W <= T workgroups take part, so each of them holds at least one tile
+    // (the merge recomputes the same W from T).
+    const int64_t T = total;
+    const int W = (int)(T < a.num_groups ? T : a.num_groups);
+    if ((int)blockIdx.x >= W)
+        return;
+    const int t_beg = (int)(T * blockIdx.x / W);
+    const int t_end = (int)(T * (blockIdx.x + 1) / W);
+    if (t_beg >= t_end)
+        return;
+    // entry holding tile t_beg: the largest b with s_start[b] <= t_beg
+    int lo = 0, hi = a.batch;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_start[mid] <= t_beg)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    int b = __builtin_amdgcn_readfirstlane(lo);
+    for (int t = t_beg; t < t_end; ++b) {
+        const int sb = s_start[b];
+        const int se = s_start[b + 1];
+        const int seg_end = min(t_end, se);
+        if (has_head && se > sb && seg_end > t)
+            run_segment<D, G, TB, SMALL_PAGE>(a, b, h, t - sb, seg_end - sb,
+                                              sb >= t_beg && se <= t_end,
+                                              (int)blockIdx.x + b);
+        t = seg_end > t ? seg_end : t;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the partials of split entries: one workgroup per (entry, KV head),
-// one thread per pair of output elements of the G query heads.
+// Merge of entries split over several workgroups or chunks: one workgroup per
+// (entry, KV head), one thread per 4 output elements of its G query heads.
 template <int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     const int h = blockIdx.x % a.num_kv_heads;
     const int b = blockIdx.x / a.num_kv_heads;
-    const int p0 = a.indptr[b];
-    const int npages = a.indptr[b + 1] - p0;
-    if (npages < 1)
-        return;
-    const int nchunks = (npages + a.chunk_pages - 1) / a.chunk_pages;
-    if (nchunks <= 1 || nchunks > a.max_chunks)
-        return;
-    for (int pi = threadIdx.x; pi < G * D / 2; pi += blockDim.x) {
-        const int g = pi / (D / 2);
-        const int e2 = (pi % (D / 2)) * 2;
+    int base, count;
+    if (a.chunk_tiles > 0) {
+        const int nt = entry_tiles(a, b);
+        const int nchunks = (nt + a.chunk_tiles - 1) / a.chunk_tiles;
+        if (nchunks <= 1 || nchunks > a.max_chunks)
+            return;
+        base = b * a.max_chunks;
+        count = nchunks;
+    } else {
+        const int sb = a.tile_start[b];
+        const int se = a.tile_start[b + 1];
+        const int64_t T = a.tile_start[a.batch];
+        if (se <= sb)
+            return;
+        const int64_t W = T < a.num_groups ? T : a.num_groups;
+        // workgroup w covers tiles [floor(T w / W), floor(T (w+1) / W)), and
+        // none of them is empty since W <= T
+        const int w_lo = (int)(((int64_t)(sb + 1) * W - 1) / T);
+        const int w_hi = (int)(((int64_t)se * W - 1) / T);
+        if (w_lo == w_hi)
+            return;
+        base = w_lo + b;
+        count = w_hi - w_lo + 1;
+    }
+    constexpr int Q4 = D / 4;
+    for (int it = threadIdx.x; it < G * Q4; it += blockDim.x) {
+        const int g = it / Q4;
+        const int e4 = (it % Q4) * 4;
         const int hq = h * G + g;
-        const int64_t row0 = (int64_t)b * a.max_chunks * a.num_qo_heads + hq;
+        const float *pl = a.part_lse + (int64_t)base * a.num_qo_heads + hq;
+        const float *po = a.part_o + ((int64_t)base * a.num_qo_heads + hq) * D + e4;
+        const int64_t stride_l = a.num_qo_heads;
+        const int64_t stride_o = (int64_t)a.num_qo_heads * D;
         float mx = -INFINITY;
-        for (int c = 0; c < nchunks; ++c)
-            mx = fmaxf(mx, a.part_lse[row0 + (int64_t)c * a.num_qo_heads]);
-        float sum = 0.f, o0 = 0.f, o1 = 0.f;
-        for (int c = 0; c < nchunks; ++c) {
-            const int64_t row = row0 + (int64_t)c * a.num_qo_heads;
-            const float w = exp2_fast(a.part_lse[row] - mx);
-            const float2 v = *reinterpret_cast<const float2 *>(a.part_o + row * D + e2);
+        for (int k = 0; k < count; ++k)
+            mx = fmaxf(mx, pl[k * stride_l]);
+        float sum = 0.f;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+        for (int k = 0; k < count; ++k) {
+            const float w = exp2_fast(pl[k * stride_l] - mx);
+            const float4 v = *reinterpret_cast<const float4 *>(po + k * stride_o);
             sum += w;
-            o0 = fmaf(w, v.x, o0);
-            o1 = fmaf(w, v.y, o1);
+            o.x = fmaf(w, v.x, o.x);
+            o.y = fmaf(w, v.y, o.y);
+            o.z = fmaf(w, v.z, o.z);
+            o.w = fmaf(w, v.w, o.w);
         }
         const float inv = 1.f / sum;
-        const int64_t o = ((int64_t)b * a.num_qo_heads + hq) * D + e2;
-        *reinterpret_cast<uint32_t *>(a.out + o) = pack_bf16x2(o0 * inv, o1 * inv);
-        if (a.lse != nullptr && e2 == 0)
+        uint2 packed;
+        packed.x = pack_bf16x2(o.x * inv, o.y * inv);
+        packed.y = pack_bf16x2(o.z * inv, o.w * inv);
+        *reinterpret_cast<uint2 *>(a.out + ((int64_t)b * a.num_qo_heads + hq) * D + e4) =
+            packed;
+        if (a.lse != nullptr && e4 == 0)
             a.lse[(int64_t)b * a.num_qo_heads + hq] = (mx + log2_fast(sum)) * kLn2;
     }
 }
 
-constexpr int kWaves = 4;       // waves per decode workgroup
-constexpr int kTilesPerBlock = 2;
+#ifndef PKV_TILES_PER_BLOCK
+#define PKV_TILES_PER_BLOCK 1
+#endif
+#ifndef PKV_WAVES_PER_CU
+#define PKV_WAVES_PER_CU 0   // 0: as many as the occupancy calculator allows
+#endif
+constexpr int kTilesPerBlock = PKV_TILES_PER_BLOCK;   // 8-token tiles per load block
 
 // Launch through hipLaunchKernel so the returned status belongs to this
 // launch alone (hipGetLastError could report an older, unrelated error).
 template <typename Args>
-hipError_t launch(const void *kernel, dim3 grid, dim3 block, const Args &args,
+hipError_t launch(const void *kernel, dim3 grid, dim3 block, size_t lds, const Args &args,
                   hipStream_t stream) {
     void *params[] = {const_cast<Args *>(&args)};
-    return hipLaunchKernel(kernel, grid, block, params, 0, stream);
+    return hipLaunchKernel(kernel, grid, block, params, lds, stream);
 }
 
 template <int D, int G>
-hipError_t launch_decode_dg(const DecodeArgs &a, int batch, hipStream_t stream) {
-    const dim3 grid((unsigned)a.num_kv_heads * (unsigned)a.max_chunks * (unsigned)batch);
-    const void *k = a.page_size < 8
-        ? reinterpret_cast<const void *>(
-              &decode_split_kernel<D, G, kWaves, kTilesPerBlock, true>)
-        : reinterpret_cast<const void *>(
-              &decode_split_kernel<D, G, kWaves, kTilesPerBlock, false>);
-    hipError_t err = launch(k, grid, dim3(kWaves * 64), a, stream);
-    if (err != hipSuccess || a.max_chunks <= 1)
-        return err;
-    constexpr int pairs = G * D / 2;
-    constexpr int threads = pairs >= 256 ? 256 : ((pairs + 63) / 64) * 64;
-    return launch(reinterpret_cast<const void *>(&merge_kernel<D, G>),
-                  dim3((unsigned)batch * a.num_kv_heads), dim3(threads), a, stream);
+const void *decode_kernel_for(int page_size) {
+    return page_size < kTileTokens
+               ? reinterpret_cast<const void *>(&decode_kernel<D, G, kTilesPerBlock, true>)
+               : reinterpret_cast<const void *>(&decode_kernel<D, G, kTilesPerBlock, false>);
 }
 
 template <int D>
-hipError_t launch_decode_d(const DecodeArgs &a, int group, int batch, hipStream_t s) {
+const void *decode_kernel_d(int group, int page_size) {
     switch (group) {
-    case 1: return launch_decode_dg<D, 1>(a, batch, s);
-    case 2: return launch_decode_dg<D, 2>(a, batch, s);
-    case 3: return launch_decode_dg<D, 3>(a, batch, s);
-    case 4: return launch_decode_dg<D, 4>(a, batch, s);
-    case 5: return launch_decode_dg<D, 5>(a, batch, s);
-    case 6: return launch_decode_dg<D, 6>(a, batch, s);
-    case 7: return launch_decode_dg<D, 7>(a, batch, s);
-    case 8: return launch_decode_dg<D, 8>(a, batch, s);
-    default: return hipErrorInvalidValue;
+    case 1: return decode_kernel_for<D, 1>(page_size);
+    case 2: return decode_kernel_for<D, 2>(page_size);
+    case 3: return decode_kernel_for<D, 3>(page_size);
+    case 4: return decode_kernel_for<D, 4>(page_size);
+    case 5: return decode_kernel_for<D, 5>(page_size);
+    case 6: return decode_kernel_for<D, 6>(page_size);
+    case 7: return decode_kernel_for<D, 7>(page_size);
+    case 8: return decode_kernel_for<D, 8>(page_size);
+    default: return nullptr;
     }
+}
+
+const void *decode_kernel_ptr(int head_dim, int group, int page_size) {
+    if (head_dim == 64)
+        return decode_kernel_d<64>(group, page_size);
+    if (head_dim == 128)
+        return decode_kernel_d<128>(group, page_size);
+    return nullptr;
+}
+
+template <int D>
+const void *merge_kernel_d(int group) {
+    switch (group) {
+    case 1: return reinterpret_cast<const void *>(&merge_kernel<D, 1>);
+    case 2: return reinterpret_cast<const void *>(&merge_kernel<D, 2>);
+    case 3: return reinterpret_cast<const void *>(&merge_kernel<D, 3>);
+    case 4: return reinterpret_cast<const void *>(&merge_kernel<D, 4>);
+    case 5: return reinterpret_cast<const void *>(&merge_kernel<D, 5>);
+    case 6: return reinterpret_cast<const void *>(&merge_kernel<D, 6>);
+    case 7: return reinterpret_cast<const void *>(&merge_kernel<D, 7>);
+    case 8: return reinterpret_cast<const void *>(&merge_kernel<D, 8>);
+    default: return nullptr;
+    }
+}
+
+size_t balanced_lds_bytes(int batch) { return sizeof(int) * ((size_t)batch + 1); }
+
+int group_waves(int num_kv_heads) {
+    return num_kv_heads < kMaxWavesPerGroup ? num_kv_heads : kMaxWavesPerGroup;
 }
 
 }  // namespace
 
 hipError_t launch_append(const AppendArgs &a, int batch, hipStream_t stream) {
     return launch(reinterpret_cast<const void *>(&append_kernel), dim3((unsigned)batch),
-                  dim3(256), a, stream);
+                  dim3(256), 0, a, stream);
 }
 
-hipError_t launch_decode(const DecodeArgs &a, int head_dim, int group, int batch,
-                         hipStream_t stream) {
-    if (head_dim == 64)
-        return launch_decode_d<64>(a, group, batch, stream);
-    if (head_dim == 128)
-        return launch_decode_d<128>(a, group, batch, stream);
-    return hipErrorInvalidValue;
+hipError_t balanced_groups(int head_dim, int group, int num_kv_heads, int page_size,
+                           int batch, int *groups) {
+    const void *k = decode_kernel_ptr(head_dim, group, page_size);
+    if (k == nullptr)
+        return hipErrorInvalidValue;
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess)
+        err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err == hipSuccess)
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, k, 64 * group_waves(num_kv_heads), balanced_lds_bytes(batch));
+    if (err != hipSuccess)
+        return err;
+    const int waves = group_waves(num_kv_heads);
+    const int head_groups = (num_kv_heads + waves - 1) / waves;
+    if (PKV_WAVES_PER_CU > 0)
+        per_cu = (PKV_WAVES_PER_CU + waves - 1) / waves;
+    if (per_cu < 1)
+        per_cu = 1;
+    if (cus > kMaxComputeUnits)
+        cus = kMaxComputeUnits;
+    // workgroups resident at once, shared by the head groups
+    int64_t w = ((int64_t)cus * per_cu + head_groups - 1) / head_groups;
+    const int64_t bound = balanced_groups_bound(num_kv_heads);
+    *groups = (int)(w < bound ? w : bound);
+    return hipSuccess;
+}
+
+hipError_t launch_decode(const DecodeArgs &a, int head_dim, int group, hipStream_t stream) {
+    const void *k = decode_kernel_ptr(head_dim, group, a.page_size);
+    const void *mk = head_dim == 64 ? merge_kernel_d<64>(group)
+                                    : (head_dim == 128 ? merge_kernel_d<128>(group) : nullptr);
+    if (k == nullptr || mk == nullptr)
+        return hipErrorInvalidValue;
+    const int waves = group_waves(a.num_kv_heads);
+    const dim3 block(64 * waves);
+    const unsigned head_groups = (unsigned)((a.num_kv_heads + waves - 1) / waves);
+    hipError_t err;
+    bool may_split;
+    if (a.chunk_tiles > 0) {
+        err = launch(k, dim3((unsigned)a.batch * (unsigned)a.max_chunks, head_groups), block,
+                     0, a, stream);
+        may_split = a.max_chunks > 1;
+    } else {
+        err = launch(k, dim3((unsigned)a.num_groups, head_groups), block,
+                     balanced_lds_bytes(a.batch), a, stream);
+        may_split = true;
+    }
+    if (err != hipSuccess || !may_split)
+        return err;
+    const int threads4 = group * head_dim / 4;
+    const int threads = threads4 >= 256 ? 256 : ((threads4 + 63) / 64) * 64;
+    return launch(mk, dim3((unsigned)a.batch * a.num_kv_heads), dim3(threads), 0, a, stream);
 }
 
 }  // namespace pkv

@@ -20,7 +20,7 @@ DESC = CacheDesc(2, 64, 16, 2, 64)
 def test_every_declared_symbol_is_exported():
     names = pkv.declared_functions()
     assert set(names) == {"pkv_append", "pkv_decode_workspace_size",
-                          "pkv_default_chunk_pages", "pkv_decode",
+                          "pkv_append_decode", "pkv_decode",
                           "pkv_validate_page_table", "pkv_status_string",
                           "pkv_last_hip_error"}
     for n in names:
@@ -38,13 +38,20 @@ def test_status_strings():
 
 
 def test_workspace_size():
-    k = pkv.default_chunk_pages()
-    assert 1 <= k <= 64
-    assert pkv.workspace_size(64, 32, 128, k, 0) == 0          # one chunk: no split
-    ws = pkv.workspace_size(8, 32, 128, 2048, 32)
+    d = CacheDesc(36, 8192, 16, 8, 128)
+    # fixed runs covering every entry in one run: no workspace
+    assert pkv.workspace_size(d, 32, 64, 16, 16) == 0
+    # fixed runs of 32 pages over 2048-page entries: 64 runs of partials
+    ws = pkv.workspace_size(d, 32, 8, 2048, 32)
     rows = 8 * 64 * 32
     assert ws >= rows * 128 * 4 + rows * 4 and ws % 256 == 0
-    assert pkv.workspace_size(0, 32, 128, 2048, 32) == 0
+    # balanced: partial slots for every workgroup plus every entry, and the
+    # tile prefix sums
+    wb = pkv.workspace_size(d, 32, 64, 256, 0)
+    assert wb >= (64 + 1) * 4 + 64 * 32 * 129 * 4
+    assert pkv.workspace_size(d, 32, 0, 256, 0) == 0
+    assert pkv.workspace_size(d, 30, 64, 256, 0) > 0        # sizes only
+    assert pkv.workspace_size(CacheDesc(36, 8192, 12, 8, 128), 32, 64, 256, 0) == 0
 
 
 def _decode(desc=DESC, layer=0, q=FAKE, hq=4, batch=3, scale=0.125, out=FAKE, lse=NULL,
@@ -77,7 +84,8 @@ def test_append_batch_zero_is_noop():
 @pytest.mark.parametrize("kw,code", [
     (dict(layer=5), -2), (dict(batch=-2), -2), (dict(hq=3), -2), (dict(hq=0), -2),
     (dict(scale=float("nan")), -2), (dict(scale=float("inf")), -2), (dict(maxp=0), -2),
-    (dict(chunk=-1), -2), (dict(chunk=65), -3), (dict(hq=18), -3),
+    (dict(chunk=-1), -2), (dict(chunk=65537), -3), (dict(hq=18), -3),
+    (dict(desc=CacheDesc(2, 64, 16, 17, 64), hq=17), -3),
     (dict(desc=CacheDesc(2, 64, 16, 2, 96)), -3), (dict(desc=CacheDesc(2, 64, 6, 2, 64)), -3),
     (dict(q=NULL), -1), (dict(out=NULL), -1), (dict(tables=(FAKE, FAKE, NULL)), -1),
     (dict(maxp=40, chunk=16), -4),
@@ -90,6 +98,24 @@ def test_decode_validation(kw, code):
 
 def test_decode_batch_zero_is_noop():
     assert _decode(batch=0, q=NULL, out=NULL, tables=(NULL, NULL, NULL)) == 0
+
+
+def _append_decode(k=FAKE, v=FAKE, layer=0, batch=3, chunk=0, hq=4, out=FAKE):
+    return lib.pkv_append_decode(FAKE, DESC, layer, k, v, FAKE, hq, FAKE, FAKE, FAKE, batch,
+                                 0.125, out, NULL, 4, chunk, NULL, 0, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=NULL), -1), (dict(v=NULL), -1), (dict(layer=9), -2), (dict(hq=3), -2),
+    (dict(out=NULL), -1), (dict(k=ctypes.c_void_p(0x100002)), -6),
+    (dict(), -4),                                  # balanced needs a workspace
+])
+def test_append_decode_validation(kw, code):
+    assert _append_decode(**kw) == code
+
+
+def test_append_decode_batch_zero_is_noop():
+    assert _append_decode(batch=0, k=NULL, v=NULL, out=NULL) == 0
 
 
 def test_validate_page_table():

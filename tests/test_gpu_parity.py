@@ -238,16 +238,19 @@ def test_decode_config4_sweep_sampled(batch):
 
 
 # ------------------------------------------------------------ invariances
-def test_batch_invariance_bit_exact():
-    """An entry's rows are bit-identical alone, in sub-batches and in the full
-    batch (cfg-4 shapes): the split depends only on the entry's own length."""
+@pytest.mark.parametrize("chunk", [1, 16])
+def test_batch_invariance_bit_exact(chunk):
+    """With fixed runs, an entry's rows are bit-identical alone, in
+    sub-batches and in the full batch (cfg-4 shapes): the split depends only
+    on the entry's own length."""
     spec = CONFIGS[4]
     table, cache, per_layer = _device_case(spec, 256)
     q, kn, vn = per_layer[0]
     tables = table_to_dev(table)
     pkv.append(cache, 0, kn, vn, *tables)
     full_out, full_lse = pkv.decode(cache, 0, q, *tables, spec.sm_scale,
-                                    max_pages_per_req=table.max_pages_per_req)
+                                    max_pages_per_req=table.max_pages_per_req,
+                                    kv_chunk_pages=chunk)
     rng = np.random.default_rng(3)
     act = np.flatnonzero(table.active)
     for size in (1, 2, 4, 16, 64):
@@ -259,7 +262,8 @@ def test_batch_invariance_bit_exact():
         sub = tuple(torch.from_numpy(x.astype(np.int32)).to(DEV)
                     for x in (ip, ix, table.last_len[sel]))
         o, l_ = pkv.decode(cache, 0, q[torch.from_numpy(sel).to(DEV)].contiguous(), *sub,
-                           spec.sm_scale, max_pages_per_req=int(n.max()) + 7)
+                           spec.sm_scale, max_pages_per_req=int(n.max()) + 7,
+                           kv_chunk_pages=chunk)
         sel_t = torch.from_numpy(sel).to(DEV)
         assert torch.equal(o.view(torch.int16), full_out[sel_t].view(torch.int16))
         assert torch.equal(l_, full_lse[sel_t])
@@ -303,8 +307,9 @@ def test_padding_isolation():
                      int(table.last_len[b]) - 1))
     assert {tuple(map(int, x)) for x in changed} <= allowed
     out0, lse0 = pkv.decode(cache, 0, dev[0], *tables, spec.sm_scale,
-                            max_pages_per_req=table.max_pages_per_req)
-    # the same active entries without any padding entry
+                            max_pages_per_req=table.max_pages_per_req, kv_chunk_pages=8)
+    # the same active entries without any padding entry (fixed runs, so the
+    # rows may not depend on the rest of the batch)
     act = np.flatnonzero(table.active)
     n = np.diff(table.indptr)[act]
     ip = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
@@ -313,7 +318,7 @@ def test_padding_isolation():
                 for x in (ip, ix, table.last_len[act]))
     act_t = torch.from_numpy(act).to(DEV)
     o1, l1 = pkv.decode(cache, 0, dev[0][act_t].contiguous(), *sub, spec.sm_scale,
-                        max_pages_per_req=table.max_pages_per_req)
+                        max_pages_per_req=table.max_pages_per_req, kv_chunk_pages=8)
     assert torch.equal(o1.view(torch.int16), out0[act_t].view(torch.int16))
     assert torch.equal(l1, lse0[act_t])
 
@@ -348,3 +353,87 @@ def test_closed_forms():
                         0.1)
     want = np.repeat(l1.v_new, 3, axis=1)
     np.testing.assert_array_equal(to_host_u16(out), want)
+
+
+# ------------------------------------------------------------ fused append
+@pytest.mark.parametrize("idx", range(len(SHAPES)))
+@pytest.mark.parametrize("chunk", [0, 2])
+def test_append_decode_fused(idx, chunk):
+    """pkv_append_decode leaves the cache bit-identical to pkv_append and gives
+    the rows of pkv_decode on it (bit-identical: same split, same values)."""
+    hq, hkv, d, ps, lengths, active = SHAPES[idx]
+    rng = np.random.default_rng(3000 + idx)
+    act = np.ones(len(lengths), bool) if active is None else np.asarray(active, bool)
+    table = table_from_lengths(lengths, act, ps, None, rng)
+    lds = [workloads.draw_layer(rng, table, hq, hkv, d, 1.0, stale="nan", unused="nan")
+           for _ in range(2)]
+    cache_host = np.stack([ld.cache for ld in lds])
+    fused_cache = to_dev_u16(cache_host)
+    sep_cache = to_dev_u16(cache_host)
+    tables = table_to_dev(table)
+    scale = 1.0 / math.sqrt(d)
+    layer = 1
+    ld = lds[layer]
+    q, kn, vn = to_dev_u16(ld.q), to_dev_u16(ld.k_new), to_dev_u16(ld.v_new)
+    mp = table.max_pages_per_req
+    fo, fl = pkv.append_decode(fused_cache, layer, kn, vn, q, *tables, scale,
+                               max_pages_per_req=mp, kv_chunk_pages=chunk)
+    pkv.append(sep_cache, layer, kn, vn, *tables)
+    so, sl = pkv.decode(sep_cache, layer, q, *tables, scale, max_pages_per_req=mp,
+                        kv_chunk_pages=chunk)
+    ro, rl = _oracle_full(cache_host, layer, ld, table, scale)
+    got = to_host_u16(fused_cache)
+    if (~act).any():
+        cands = [ld.k_new[b] for b in np.flatnonzero(~act)]
+        assert any(np.array_equal(got[layer, 0, 0, 0], c) for c in cands)
+        got[layer, 0] = cache_host[layer, 0]
+    np.testing.assert_array_equal(got, cache_host)
+    act_t = torch.from_numpy(np.flatnonzero(act)).to(DEV)
+    assert torch.equal(fo[act_t].view(torch.int16), so[act_t].view(torch.int16))
+    assert torch.equal(fl[act_t], sl[act_t])
+    compare(fo, fl, ro[act], rl[act], rows=act, what=f"fused shape {idx}")
+
+
+def test_append_decode_config3_layers():
+    spec = CONFIGS[3]
+    table = make_table(spec)
+    cache = torch.zeros((3, table.num_pages, 2, 16, 8, 128), dtype=torch.bfloat16,
+                        device=DEV)
+    tables = table_to_dev(table)
+    entries = _pick_entries(table, 5)
+    for layer in range(3):
+        dev = workloads.draw_layer_device(cache[layer], table, [3000 + layer, 64], 32, 1.0,
+                                          None)
+        host_rows = _HostRows(*dev)
+        ro, rl, (rb, rh) = oracle_rows_from_device(cache[layer], host_rows, table, entries,
+                                                   [0, 5, 31], spec.sm_scale)
+        out, lse = pkv.append_decode(cache, layer, dev[1], dev[2], dev[0], *tables,
+                                     spec.sm_scale, max_pages_per_req=table.max_pages_per_req)
+        og = out[torch.from_numpy(rb).to(DEV), torch.from_numpy(rh).to(DEV)]
+        lg = lse[torch.from_numpy(rb).to(DEV), torch.from_numpy(rh).to(DEV)]
+        compare(og, lg, ro, rl, what=f"fused cfg3 layer {layer}")
+
+
+def test_fixed_runs_poison_entries_over_the_bound():
+    """An entry longer than max_pages_per_req allows gets NaN rows in fixed
+    mode (a visible broken precondition); the other rows stay correct."""
+    spec = CONFIGS[2]
+    table = make_table(spec)
+    ld, dev = host_layer_case(spec, table, 0)
+    cache_host = ld.cache[None].copy()
+    cache = to_dev_u16(cache_host)
+    tables = table_to_dev(table)
+    n = np.diff(table.indptr)
+    bound = int(np.sort(n)[-3])          # the two longest entries exceed it
+    pkv.append(cache, 0, dev[1], dev[2], *tables)
+    out, lse = pkv.decode(cache, 0, dev[0], *tables, spec.sm_scale,
+                          max_pages_per_req=bound, kv_chunk_pages=4)
+    # runs of 4 pages = 8 tiles; the launch covers ceil(bound * 2 / 8) runs
+    tiles = (table.lengths + 7) // 8
+    over = (tiles + 7) // 8 > (bound * 2 + 7) // 8
+    assert over.any() and (table.active & ~over).any()
+    lse_h = lse.cpu().numpy()
+    assert np.all(np.isnan(lse_h[over]))
+    ro, rl = _oracle_full(cache_host, 0, ld, table, spec.sm_scale)
+    ok = table.active & ~over
+    compare(out, lse, ro[ok], rl[ok], rows=ok, what="rows under the bound")
