@@ -55,6 +55,22 @@ def parse():
     return ap.parse_args()
 
 
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when the kernel source changed since they were taken."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f)
+        with open(os.path.join(ROOT, rec["kernel_source"]), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    if not sha.startswith(rec["source_sha256_prefix"]):
+        return None
+    return rec["launch_read_bytes"] + rec["launch_write_bytes"]
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -247,7 +263,9 @@ def main():
         "ms_per_step_events": round(ms_step_ev, 5),
         "roofline": {"bound": "hbm", "kernel": f"{decode_name} (decode pass + LSE merge)",
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic() if args.config == 3 and not args.separate
+                     and args.chunk_pages == 0 else None,
                      "bytes_per_launch": launch_bytes, "avg_launch_us": round(dec_us, 3),
                      "launches": int(durs.size)},
     }

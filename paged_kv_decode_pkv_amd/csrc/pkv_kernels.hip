@@ -580,9 +580,19 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void decode_kernel(DecodeAr
 
 // ---------------------------------------------------------------------------
 // Merge of entries split over several workgroups or chunks: one workgroup per
-// (entry, KV head), one thread per 4 output elements of its G query heads.
+// (entry, KV head).  Thread (col, ks) owns float4 column `col` of the G query
+// heads' outputs and the partials k = ks, ks + KS, ...; it merges them online
+// (running maximum, rescaled sum) with the loads of four partials in flight,
+// and the KS per-thread states are then merged through LDS.
 template <int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+    constexpr int COLS = G * D / 4;                    // float4 columns
+    constexpr int KS = COLS >= 256 ? 1 : 256 / COLS;   // ways the partials are split
+    constexpr int U = 4;                               // partials in flight per thread
+    __shared__ float s_m[KS][COLS];
+    __shared__ float s_s[KS][COLS];
+    __shared__ float4 s_o[KS][COLS];
+
     const int h = blockIdx.x % a.num_kv_heads;
     const int b = blockIdx.x / a.num_kv_heads;
     int base, count;
@@ -609,39 +619,80 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
         base = w_lo + b;
         count = w_hi - w_lo + 1;
     }
-    constexpr int Q4 = D / 4;
-    for (int it = threadIdx.x; it < G * Q4; it += blockDim.x) {
-        const int g = it / Q4;
-        const int e4 = (it % Q4) * 4;
-        const int hq = h * G + g;
-        const float *pl = a.part_lse + (int64_t)base * a.num_qo_heads + hq;
-        const float *po = a.part_o + ((int64_t)base * a.num_qo_heads + hq) * D + e4;
-        const int64_t stride_l = a.num_qo_heads;
-        const int64_t stride_o = (int64_t)a.num_qo_heads * D;
-        float mx = -INFINITY;
-        for (int k = 0; k < count; ++k)
-            mx = fmaxf(mx, pl[k * stride_l]);
-        float sum = 0.f;
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-        for (int k = 0; k < count; ++k) {
-            const float w = exp2_fast(pl[k * stride_l] - mx);
-            const float4 v = *reinterpret_cast<const float4 *>(po + k * stride_o);
-            sum += w;
-            o.x = fmaf(w, v.x, o.x);
-            o.y = fmaf(w, v.y, o.y);
-            o.z = fmaf(w, v.z, o.z);
-            o.w = fmaf(w, v.w, o.w);
+    const int col = threadIdx.x % COLS;
+    const int ks = threadIdx.x / COLS;
+    const int g = col / (D / 4);
+    const int e4 = (col % (D / 4)) * 4;
+    const int hq = h * G + g;
+    const int64_t stride_l = a.num_qo_heads;
+    const int64_t stride_o = (int64_t)a.num_qo_heads * D;
+    const float *pl = a.part_lse + (int64_t)base * stride_l + hq;
+    const float *po = a.part_o + (int64_t)base * stride_o + (int64_t)hq * D + e4;
+
+    float m = -INFINITY, sum = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (ks < KS) {
+        for (int k0 = ks; k0 < count; k0 += KS * U) {
+            float lv[U];
+            float4 ov[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = min(k0 + u * KS, count - 1);
+                lv[u] = pl[k * stride_l];
+                ov[u] = *reinterpret_cast<const float4 *>(po + k * stride_o);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (k0 + u * KS >= count)
+                    break;
+                const float mn = fmaxf(m, lv[u]);
+                const float al = exp2_fast(m - mn);   // 0 while m is -inf
+                const float w = exp2_fast(lv[u] - mn);
+                sum = sum * al + w;
+                o.x = fmaf(w, ov[u].x, o.x * al);
+                o.y = fmaf(w, ov[u].y, o.y * al);
+                o.z = fmaf(w, ov[u].z, o.z * al);
+                o.w = fmaf(w, ov[u].w, o.w * al);
+                m = mn;
+            }
         }
-        const float inv = 1.f / sum;
-        uint2 packed;
-        packed.x = pack_bf16x2(o.x * inv, o.y * inv);
-        packed.y = pack_bf16x2(o.z * inv, o.w * inv);
-        *reinterpret_cast<uint2 *>(a.out + ((int64_t)b * a.num_qo_heads + hq) * D + e4) =
-            packed;
-        if (a.lse != nullptr && e4 == 0)
-            a.lse[(int64_t)b * a.num_qo_heads + hq] = (mx + log2_fast(sum)) * kLn2;
+        if (KS > 1) {
+            s_m[ks][col] = m;
+            s_s[ks][col] = sum;
+            s_o[ks][col] = o;
+        }
     }
+    if (KS > 1) {
+        __syncthreads();
+        if (ks != 0)
+            return;
+        m = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < KS; ++q)
+            m = fmaxf(m, s_m[q][col]);
+        sum = 0.f;
+        o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int q = 0; q < KS; ++q) {
+            const float mq = s_m[q][col];
+            const float f = mq == -INFINITY ? 0.f : exp2_fast(mq - m);
+            const float4 oq = s_o[q][col];
+            sum = fmaf(s_s[q][col], f, sum);
+            o.x = fmaf(oq.x, f, o.x);
+            o.y = fmaf(oq.y, f, o.y);
+            o.z = fmaf(oq.z, f, o.z);
+            o.w = fmaf(oq.w, f, o.w);
+        }
+    }
+    if (col >= COLS)
+        return;
+    const float inv = 1.f / sum;
+    uint2 packed;
+    packed.x = pack_bf16x2(o.x * inv, o.y * inv);
+    packed.y = pack_bf16x2(o.z * inv, o.w * inv);
+    *reinterpret_cast<uint2 *>(a.out + ((int64_t)b * a.num_qo_heads + hq) * D + e4) = packed;
+    if (a.lse != nullptr && e4 == 0)
+        a.lse[(int64_t)b * a.num_qo_heads + hq] = (m + log2_fast(sum)) * kLn2;
 }
 
 #ifndef PKV_TILES_PER_BLOCK
@@ -770,8 +821,10 @@ hipError_t launch_decode(const DecodeArgs &a, int head_dim, int group, hipStream
     }
     if (err != hipSuccess || !may_split)
         return err;
-    const int threads4 = group * head_dim / 4;
-    const int threads = threads4 >= 256 ? 256 : ((threads4 + 63) / 64) * 64;
+    // COLS float4 columns times KS ways: 256 threads for every built shape
+    // (COLS = group * head_dim / 4 divides 256 or exceeds it)
+    const int cols = group * head_dim / 4;
+    const int threads = cols >= 256 ? ((cols + 63) / 64) * 64 : (256 / cols) * cols;
     return launch(mk, dim3((unsigned)a.batch * a.num_kv_heads), dim3(threads), 0, a, stream);
 }
 
