@@ -121,7 +121,7 @@ size_t pkv_decode_workspace_size(pkv_cache_desc_t desc, int32_t num_qo_heads,
  *                        kv_chunk_pages pages (rounded up to whole 8-token
  *                        tiles); a row is bit-identical whatever else is in
  *                        the batch.  At most 65536.
- * Batches above 8192 entries use fixed runs of 16 pages.
+ * Batches above 4096 entries use fixed runs of 16 pages.
  *  kv_cache           bf16 cache described by `desc` (read only).
  *  q                  bf16 [batch, num_qo_heads, head_dim], RoPE applied.
  *  page_indptr/page_indices/last_page_len   as for pkv_append.

@@ -120,7 +120,7 @@ int decode_common(const void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
         (fused && (!aligned16(k_new) || !aligned16(v_new))))
         return PKV_ERR_ALIGNMENT;
     const Plan plan = make_plan(desc, num_qo_heads, batch, max_pages_per_req, kv_chunk_pages);
-    if (plan.chunk_tiles > 0 && (int64_t)batch * plan.max_chunks > 0x7fffffffLL)
+    if (plan.chunk_tiles > 0 && ((int64_t)batch + 7) / 8 * 8 * plan.max_chunks > 0x7fffffffLL)
         return PKV_ERR_BAD_SHAPE;
     if (plan.ws_bytes > 0 &&
         (workspace == nullptr || workspace_bytes < (size_t)plan.ws_bytes))

@@ -22,8 +22,9 @@
 //    The running maximum is raised only when a new score passes it by more
 //    than kTau (log2 units); between raises nothing is rescaled and exp2
 //    arguments stay <= kTau.  Row groups are merged once per segment.
-//  * Loads run two blocks of TB tiles ahead in registers (three rotating
-//    buffers; see run_segment).
+//  * Loads run two tiles ahead in registers (three rotating buffers), from
+//    an LDS table of the tiles' page ids built once per piece of work; see
+//    decode_kernel.
 //
 // Work split.  Balanced mode (default): the tiles of all entries are laid end
 // to end and each of W workgroups takes an equal run of them (W = what the
@@ -146,303 +147,6 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// Attention of KV head h's G query heads over tiles [lt0, lt1) of entry b,
-// run by one wavefront.  Writes the final rows when `whole`, else a partial
-// into `slot`.
-//
-// Pipeline: three rotating register buffers of TB tiles (A, B, C); while one
-// block is computed the next two are in flight.  Every load is issued
-// unconditionally -- a tile past the end of the segment reloads its last tile,
-// a cache hit, and is masked -- so at each compute the same two blocks are
-// outstanding on every path and the compiler's waits keep them in flight.
-template <int D, int G, int TB, bool SMALL_PAGE>
-__device__ __forceinline__ void run_segment(const DecodeArgs &a, int b, int h, int lt0,
-                                            int lt1, bool whole, int slot) {
-    constexpr int NLD = D / 64;   // 16-byte words per lane per token row
-    // segment bounds are uniform across the wave: keep them in SGPRs
-    b = __builtin_amdgcn_readfirstlane(b);
-    lt0 = __builtin_amdgcn_readfirstlane(lt0);
-    lt1 = __builtin_amdgcn_readfirstlane(lt1);
-    slot = __builtin_amdgcn_readfirstlane(slot);
-    whole = __builtin_amdgcn_readfirstlane((int)whole) != 0;
-    const int lane = threadIdx.x & 63;
-    const int rg = lane >> 3;     // token within a tile
-    const int j = lane & 7;       // element slice [8j, 8j+8) (+64 for D = 128)
-
-    const int p0 = a.indptr[b];
-    const int npages = a.indptr[b + 1] - p0;
-    int last = a.last_len[b];
-    last = last < 1 ? 1 : (last > a.page_size ? a.page_size : last);
-    const int len = (npages - 1) * a.page_size + last;
-    const int last_tile = (len - 1) / kTileTokens;
-    const int hq0 = h * G;
-    const bool fused = a.k_new != nullptr;
-    const int64_t new_row = ((int64_t)b * a.num_kv_heads + h) * D + j * 8;
-
-    // q rows of the G query heads that read KV head h, this lane's slice.
-    uint32_t qv[G][NLD][4];
-    {
-        const uint16_t *qb = a.q + ((int64_t)b * a.num_qo_heads + hq0) * D + j * 8;
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                const uint4 w = load16(qb + g * D + i * 64);
-                qv[g][i][0] = w.x;
-                qv[g][i][1] = w.y;
-                qv[g][i][2] = w.z;
-                qv[g][i][3] = w.w;
-            }
-    }
-
-    float m[G], l[G], acc[G][NLD][8];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m[g] = -INFINITY;
-        l[g] = 0.f;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                acc[g][i][e] = 0.f;
-    }
-
-    struct Block {
-        uint4 k[TB][NLD];
-        uint4 v[TB][NLD];
-    };
-
-    // Windows of at most 64 pages: their ids sit one per lane.
-    for (int s0 = lt0; s0 < lt1;) {
-        const int fp = (s0 * kTileTokens) >> a.log2_page;    // first page of window
-        const int s1 = min(lt1, (int)((((int64_t)fp + 64) << a.log2_page) / kTileTokens));
-        int my_page = (fp + lane < npages) ? a.indices[p0 + fp + lane] : 0;
-        my_page = (my_page >= 0 && my_page < a.num_pages) ? my_page : 0;
-        const int nblk = (s1 - s0 + TB - 1) / TB;
-
-        // Issue the loads of block kb (tiles s0 + kb*TB + tb); tiles past s1
-        // reload tile s1 - 1.  The tile holding a fused append's new token
-        // takes that row from k_new / v_new: same number of loads either way.
-        auto load_block = [&](Block &blk, int kb) {
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                const int t = min(s0 + kb * TB + tb, s1 - 1);
-                const int tok = t * kTileTokens + rg;
-                const int sl = tok & (a.page_size - 1);
-                const uint16_t *row;
-                if (SMALL_PAGE) {
-                    const int page = __shfl(my_page, (tok >> a.log2_page) - fp, 64);
-                    row = a.cache + (int64_t)page * a.page_stride + h * D +
-                          (uint32_t)(sl * a.row_stride + j * 8);
-                } else {
-                    const int page = __builtin_amdgcn_readlane(
-                        my_page, ((t * kTileTokens) >> a.log2_page) - fp);
-                    const uint16_t *base = a.cache + (int64_t)page * a.page_stride + h * D;
-                    row = base + (uint32_t)(sl * a.row_stride + j * 8);
-                }
-                if (fused && t == last_tile) {
-                    const bool is_new = tok == len - 1;
-                    const uint16_t *kr = is_new ? a.k_new + new_row : row;
-                    const uint16_t *vr = is_new ? a.v_new + new_row : row + a.half_stride;
-#pragma unroll
-                    for (int i = 0; i < NLD; ++i) {
-                        blk.k[tb][i] = load16(kr + i * 64);
-                        blk.v[tb][i] = load16(vr + i * 64);
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < NLD; ++i) {
-                        blk.k[tb][i] = load16(row + i * 64);
-                        blk.v[tb][i] = load16(row + a.half_stride + i * 64);
-                    }
-                }
-            }
-        };
-
-        auto compute_block = [&](const Block &blk, int kb) {
-            const int tfirst = s0 + kb * TB;
-            // Does this block hold a clamped tile or a token past the end?
-            const bool edge = (tfirst + TB > s1) || ((tfirst + TB) * kTileTokens > len);
-            float s[TB][G];
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    float d = 0.f;
-#pragma unroll
-                    for (int i = 0; i < NLD; ++i) {
-                        d = dot2_bf16(qv[g][i][0], blk.k[tb][i].x, d);
-                        d = dot2_bf16(qv[g][i][1], blk.k[tb][i].y, d);
-                        d = dot2_bf16(qv[g][i][2], blk.k[tb][i].z, d);
-                        d = dot2_bf16(qv[g][i][3], blk.k[tb][i].w, d);
-                    }
-                    s[tb][g] = sum_row8(d) * a.scale_log2;
-                }
-            bool ok[TB];
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                const int t = tfirst + tb;
-                ok[tb] = (t < s1) && (t * kTileTokens + rg < len);
-            }
-            if (edge) {
-#pragma unroll
-                for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-                    for (int g = 0; g < G; ++g)
-                        s[tb][g] = ok[tb] ? s[tb][g] : -INFINITY;
-            }
-            // Lazy maximum: raise m only when a score passes it by more than kTau.
-            float mb[G];
-            bool raise_any = false;
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                mb[g] = s[0][g];
-#pragma unroll
-                for (int tb = 1; tb < TB; ++tb)
-                    mb[g] = fmaxf(mb[g], s[tb][g]);
-                raise_any |= mb[g] > m[g] + kTau;
-            }
-            if (raise_any) {
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const bool up = mb[g] > m[g] + kTau;
-                    const float mn = up ? mb[g] : m[g];
-                    const float alpha = up ? exp2_fast(m[g] - mn) : 1.f;
-                    m[g] = mn;
-                    l[g] *= alpha;
-#pragma unroll
-                    for (int i = 0; i < NLD; ++i)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            acc[g][i][e] *= alpha;
-                }
-            }
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                float vf[NLD][8];
-#pragma unroll
-                for (int i = 0; i < NLD; ++i) {
-                    const uint4 w = blk.v[tb][i];
-                    vf[i][0] = bf16_lo(w.x);
-                    vf[i][1] = bf16_hi(w.x);
-                    vf[i][2] = bf16_lo(w.y);
-                    vf[i][3] = bf16_hi(w.y);
-                    vf[i][4] = bf16_lo(w.z);
-                    vf[i][5] = bf16_hi(w.z);
-                    vf[i][6] = bf16_lo(w.w);
-                    vf[i][7] = bf16_hi(w.w);
-                }
-                if (edge && !ok[tb]) {
-                    // stale rows past the end may hold anything, NaN included
-#pragma unroll
-                    for (int i = 0; i < NLD; ++i)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            vf[i][e] = 0.f;
-                }
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    float p = exp2_fast(s[tb][g] - m[g]);
-                    if (edge)
-                        p = ok[tb] ? p : 0.f;   // also covers -inf - -inf
-                    l[g] += p;
-#pragma unroll
-                    for (int i = 0; i < NLD; ++i)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            acc[g][i][e] = fmaf(p, vf[i][e], acc[g][i][e]);
-                }
-            }
-        };
-
-        Block A, B, C;
-        load_block(A, 0);
-        load_block(B, 1);
-        for (int kb = 0;;) {
-            load_block(C, kb + 2);
-            compute_block(A, kb);
-            if (++kb >= nblk)
-                break;
-            load_block(A, kb + 2);
-            compute_block(B, kb);
-            if (++kb >= nblk)
-                break;
-            load_block(B, kb + 2);
-            compute_block(C, kb);
-            if (++kb >= nblk)
-                break;
-        }
-        s0 = s1;
-    }
-
-    // Fused append: the row group holding token L-1 copies k_new / v_new of
-    // head h into the cache slot the standalone append would write.
-    if (fused && last_tile >= lt0 && last_tile < lt1 && rg == ((len - 1) & (kTileTokens - 1))) {
-        int page = a.indices[p0 + npages - 1];
-        page = (page >= 0 && page < a.num_pages) ? page : 0;
-        uint16_t *dst = a.cache_w + (int64_t)page * a.page_stride + h * D +
-                        (int64_t)(((len - 1) & (a.page_size - 1)) * a.row_stride) + j * 8;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            *reinterpret_cast<uint4 *>(dst + i * 64) = load16(a.k_new + new_row + i * 64);
-            *reinterpret_cast<uint4 *>(dst + a.half_stride + i * 64) =
-                load16(a.v_new + new_row + i * 64);
-        }
-    }
-
-    // Merge the 8 row groups; every lane ends with the totals.
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float mw = max_across_rows(m[g]);
-        const float f = (m[g] == -INFINITY) ? 0.f : exp2_fast(m[g] - mw);
-        l[g] = sum_across_rows(l[g] * f);
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                acc[g][i][e] = sum_across_rows(acc[g][i][e] * f);
-        m[g] = mw;
-    }
-
-    // Row group g writes query head hq0 + g.
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        if (rg != g)
-            continue;
-        const int hq = hq0 + g;
-        const float inv = 1.f / l[g];
-        if (whole) {
-            uint16_t *o = a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8;
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                uint4 w;
-                w.x = pack_bf16x2(acc[g][i][0] * inv, acc[g][i][1] * inv);
-                w.y = pack_bf16x2(acc[g][i][2] * inv, acc[g][i][3] * inv);
-                w.z = pack_bf16x2(acc[g][i][4] * inv, acc[g][i][5] * inv);
-                w.w = pack_bf16x2(acc[g][i][6] * inv, acc[g][i][7] * inv);
-                *reinterpret_cast<uint4 *>(o + i * 64) = w;
-            }
-            if (a.lse != nullptr && j == 0)
-                a.lse[(int64_t)b * a.num_qo_heads + hq] = (m[g] + log2_fast(l[g])) * kLn2;
-        } else {
-            const int64_t row = (int64_t)slot * a.num_qo_heads + hq;
-            float *o = a.part_o + row * D + j * 8;
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                *reinterpret_cast<float4 *>(o + i * 64) =
-                    make_float4(acc[g][i][0] * inv, acc[g][i][1] * inv, acc[g][i][2] * inv,
-                                acc[g][i][3] * inv);
-                *reinterpret_cast<float4 *>(o + i * 64 + 4) =
-                    make_float4(acc[g][i][4] * inv, acc[g][i][5] * inv, acc[g][i][6] * inv,
-                                acc[g][i][7] * inv);
-            }
-            if (j == 0)
-                a.part_lse[row] = m[g] + log2_fast(l[g]);
-        }
-    }
-}
-
 // Exclusive scan of one int per thread over the workgroup (<= 16 waves).
 __device__ int block_exclusive_scan(int v, int *s_wave, int &total) {
     const int lane = threadIdx.x & 63;
@@ -478,103 +182,461 @@ __device__ int block_exclusive_scan(int v, int *s_wave, int &total) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode pass.  Block: one wavefront per KV head.  Balanced mode: grid =
-// num_groups workgroups over the flattened tiles.  Fixed mode: grid =
-// batch * max_chunks, one workgroup per (entry, chunk).
-template <int D, int G, int TB, bool SMALL_PAGE>
-__global__ __launch_bounds__(kMaxWavesPerGroup * 64) void decode_kernel(DecodeArgs a) {
-    extern __shared__ int s_start[];   // [batch + 1] tile prefix sums (balanced)
-    __shared__ int s_wave[17];
-    // KV head of this wave: blockIdx.y picks a group of up to kMaxWavesPerGroup
-    // heads, one wave each (a grid dimension rather than a loop over heads)
-    const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * (blockDim.x >> 6) +
-                                                 (threadIdx.x >> 6));
-    // Waves past the last head (when Hkv is not a multiple of the group size)
-    // do no attention work but still take every barrier below.
-    const bool has_head = h < a.num_kv_heads;
+// Decode pass.
+//
+// A workgroup owns a run [g0, g1) of 8-token tiles in its entries' tiles laid
+// end to end, and has one wave per KV head (blockIdx.y picks the group of up to
+// kMaxWavesPerGroup heads).  Balanced mode (chunk_tiles == 0): W workgroups
+// take equal runs of all T tiles of the batch.  Fixed mode: a workgroup takes
+// run c of chunk_tiles tiles of one entry b alone.  Either way the entries
+// are described in LDS (tile prefix sums, first page-table slot, tokens), so
+// both modes run the same loop.
+//
+// The run is processed in pieces of at most kPiece tiles.  All threads first
+// resolve every tile's page id into an LDS table, with an info word per tile
+// (valid tokens, slot in the page, where entries start and end); then each
+// wave streams the piece through three rotating one-tile register buffers
+// (two tiles in flight while one is computed), switching entries where the
+// info word says so.  Loads never wait on the page table, and the q rows of
+// the piece's first entries are staged in LDS with the tables, so entry
+// switches cost no memory round trip.  Every load is issued unconditionally
+// (a tile past the piece reloads its last tile, a cache hit, and is never
+// computed), so at each compute the same two tiles are outstanding on every
+// path and the compiler's waits keep them in flight.
+constexpr int kPiece = 256;
+constexpr int kInfoNtok = 0xF;            // bits 0-3: valid tokens (1..8)
+constexpr int kInfoSlotShift = 4;         // bits 4-8: slot of the tile's first token / 8
+constexpr int kInfoSegFirst = 1 << 9;     // first tile of an entry within the run
+constexpr int kInfoSegLast = 1 << 10;     // last tile of an entry within the run
+constexpr int kInfoEntryLast = 1 << 11;   // the tile holding the entry's token L-1
+constexpr int kInfoNewRowShift = 12;      // bits 12-14: token L-1 within that tile
+constexpr int kInfoEntryShift = 16;       // bits 16-31: entry - first entry of piece
 
-    if (a.chunk_tiles > 0) {
-        if (!has_head)
-            return;     // the fixed mode has no barrier
-        const int c = blockIdx.x % a.max_chunks;
-        const int b = blockIdx.x / a.max_chunks;
-        const int nt = entry_tiles(a, b);
-        const int nchunks = (nt + a.chunk_tiles - 1) / a.chunk_tiles;
-        if (nchunks > a.max_chunks) {
-            // Longer than the launch allows: poison the rows so the broken
-            // precondition shows instead of silently truncating.
-            if (c == 0) {
-                const int lane = threadIdx.x & 63;
-                for (int i = lane; i < G * D; i += 64)
-                    a.out[((int64_t)b * a.num_qo_heads + h * G) * D + i] = 0x7FC0;
-                if (a.lse != nullptr && lane < G)
-                    a.lse[(int64_t)b * a.num_qo_heads + h * G + lane] = __builtin_nanf("");
-            }
-            return;
-        }
-        if (c >= nchunks)
-            return;
-        const int lt0 = c * a.chunk_tiles;
-        const int lt1 = min(nt, lt0 + a.chunk_tiles);
-        run_segment<D, G, TB, SMALL_PAGE>(a, b, h, lt0, lt1, nchunks == 1,
-                                          b * a.max_chunks + c);
-        return;
-    }
+// Tiles of entry b; also its first page-table slot and token count.
+__device__ __forceinline__ int entry_desc(const DecodeArgs &a, int b, int &p0, int &len) {
+    p0 = a.indptr[b];
+    const int n = a.indptr[b + 1] - p0;
+    int last = a.last_len[b];
+    last = last < 1 ? 1 : (last > a.page_size ? a.page_size : last);
+    len = n < 1 ? 0 : (n - 1) * a.page_size + last;
+    return (len + kTileTokens - 1) / kTileTokens;
+}
 
-    // Balanced: prefix sums of tiles per entry, in LDS.
-    const int nthreads = blockDim.x;
-    const int per = (a.batch + nthreads - 1) / nthreads;
-    const int e0 = min(a.batch, (int)threadIdx.x * per);
-    const int e1 = min(a.batch, e0 + per);
-    int local = 0;
-    for (int e = e0; e < e1; ++e) {
-        const int t = entry_tiles(a, e);
-        s_start[e] = t;
-        local += t;
-    }
-    int total = 0;
-    int run = block_exclusive_scan(local, s_wave, total);
-    for (int e = e0; e < e1; ++e) {
-        const int t = s_start[e];
-        s_start[e] = run;
-        run += t;
-    }
-    if (threadIdx.x == 0)
-        s_start[a.batch] = total;
-    __syncthreads();
-    if (blockIdx.x == 0 && blockIdx.y == 0)
-        for (int e = threadIdx.x; e <= a.batch; e += nthreads)
-            a.tile_start[e] = s_start[e];
+// Ints of padding after the entry descriptors so the staged q rows, which
+// follow the tile tables, start 16-byte aligned (the tables hold a multiple of
+// 4 ints).
+__host__ __device__ __forceinline__ int q_pad(int nb) { return (3 - (3 * nb) % 4) % 4; }
 
-    // W <= T workgroups take part, so each of them holds at least one tile
-    // (the merge recomputes the same W from T).
-    const int64_t T = total;
-    const int W = (int)(T < a.num_groups ? T : a.num_groups);
-    if ((int)blockIdx.x >= W)
-        return;
-    const int t_beg = (int)(T * blockIdx.x / W);
-    const int t_end = (int)(T * (blockIdx.x + 1) / W);
-    if (t_beg >= t_end)
-        return;
-    // entry holding tile t_beg: the largest b with s_start[b] <= t_beg
-    int lo = 0, hi = a.batch;
+// The largest e in [lo, hi] with start[e] <= t (start non-decreasing).
+__device__ __forceinline__ int entry_of(const int *start, int lo, int hi, int t) {
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (s_start[mid] <= t_beg)
+        if (start[mid] <= t)
             lo = mid;
         else
             hi = mid - 1;
     }
-    int b = __builtin_amdgcn_readfirstlane(lo);
-    for (int t = t_beg; t < t_end; ++b) {
-        const int sb = s_start[b];
-        const int se = s_start[b + 1];
-        const int seg_end = min(t_end, se);
-        if (has_head && se > sb && seg_end > t)
-            run_segment<D, G, TB, SMALL_PAGE>(a, b, h, t - sb, seg_end - sb,
-                                              sb >= t_beg && se <= t_end,
-                                              (int)blockIdx.x + b);
-        t = seg_end > t ? seg_end : t;
+    return lo;
+}
+
+template <int D, int G, bool SMALL_PAGE>
+__global__ __launch_bounds__(kMaxWavesPerGroup * 64) void decode_kernel(DecodeArgs a) {
+    constexpr int NLD = D / 64;                      // 16-byte words per lane per row
+    constexpr int PPT = SMALL_PAGE ? kTileTokens : 1;   // page ids per tile
+    extern __shared__ uint4 smem_words[];
+    int *smem = reinterpret_cast<int *>(smem_words);
+    __shared__ int s_wave[17];
+    const int lane = threadIdx.x & 63;
+    const int rg = lane >> 3;     // token within a tile
+    const int j = lane & 7;       // element slice [8j, 8j+8) (+64 for D = 128)
+    const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * (blockDim.x >> 6) +
+                                                 (threadIdx.x >> 6));
+    // Waves past the last head (when Hkv is not a multiple of the group size)
+    // do no attention work but still take every barrier.
+    const bool has_head = h < a.num_kv_heads;
+    const bool fixed = a.chunk_tiles > 0;
+    const bool fused = a.k_new != nullptr;
+    const int nb = fixed ? 1 : a.batch;
+    int *s_start = smem;              // [nb + 1] tile prefix sums
+    int *s_p0 = s_start + nb + 1;     // [nb] first page-table slot
+    int *s_len = s_p0 + nb;           // [nb] tokens
+    int *s_page = s_len + nb;         // [kPiece * PPT] page ids of the piece's tiles
+    int *s_info = s_page + kPiece * PPT;   // [kPiece] info words
+    // q rows of the piece's first q_slots entries, [q_slots][Hq][D] bf16
+    uint16_t *s_q = reinterpret_cast<uint16_t *>(s_info + kPiece + q_pad(nb));
+
+    int g0, g1, fixed_b = 0, fixed_c = 0;
+    if (fixed) {
+        // Chunk-major order over rows of batch8 = batch rounded up to 8
+        // workgroups, entries rotated by the chunk number.  Workgroups are
+        // dealt to the 8 XCDs round-robin, so chunk c of entry b lands on XCD
+        // (b - c) mod 8: consecutive chunks of an entry, and the first chunks
+        // of all entries, spread over every XCD.  Ids past the batch are empty.
+        const int batch8 = (a.batch + 7) & ~7;
+        fixed_c = blockIdx.x / batch8;
+        const int bp = blockIdx.x - fixed_c * batch8;
+        fixed_b = (bp + fixed_c) % batch8;
+        if (fixed_b >= a.batch)
+            return;
+        int p0, len;
+        const int nt = entry_desc(a, fixed_b, p0, len);
+        const int nchunks = (nt + a.chunk_tiles - 1) / a.chunk_tiles;
+        if (nchunks > a.max_chunks) {
+            // Longer than the launch allows: poison the rows so the broken
+            // precondition shows instead of silently truncating.
+            if (fixed_c == 0 && has_head) {
+                for (int i = lane; i < G * D; i += 64)
+                    a.out[((int64_t)fixed_b * a.num_qo_heads + h * G) * D + i] = 0x7FC0;
+                if (a.lse != nullptr && lane < G)
+                    a.lse[(int64_t)fixed_b * a.num_qo_heads + h * G + lane] = __builtin_nanf("");
+            }
+            return;
+        }
+        if (fixed_c >= nchunks)
+            return;
+        if (threadIdx.x == 0) {
+            s_start[0] = 0;
+            s_start[1] = nt;
+            s_p0[0] = p0;
+            s_len[0] = len;
+        }
+        g0 = fixed_c * a.chunk_tiles;
+        g1 = min(nt, g0 + a.chunk_tiles);
+        __syncthreads();
+    } else {
+        // Balanced: per-entry tiles, first slot and tokens, then prefix sums.
+        const int nthreads = blockDim.x;
+        const int per = (a.batch + nthreads - 1) / nthreads;
+        const int e0 = min(a.batch, (int)threadIdx.x * per);
+        const int e1 = min(a.batch, e0 + per);
+        int local = 0;
+        for (int e = e0; e < e1; ++e) {
+            int p0, len;
+            const int t = entry_desc(a, e, p0, len);
+            s_start[e] = t;
+            s_p0[e] = p0;
+            s_len[e] = len;
+            local += t;
+        }
+        int total = 0;
+        int run = block_exclusive_scan(local, s_wave, total);
+        for (int e = e0; e < e1; ++e) {
+            const int t = s_start[e];
+            s_start[e] = run;
+            run += t;
+        }
+        if (threadIdx.x == 0)
+            s_start[a.batch] = total;
+        __syncthreads();
+        if (blockIdx.x == 0 && blockIdx.y == 0)
+            for (int e = threadIdx.x; e <= a.batch; e += nthreads)
+                a.tile_start[e] = s_start[e];
+        // W <= T workgroups take part, so each holds at least one tile (the
+        // merge recomputes the same W from T)
+        const int64_t T = total;
+        const int W = (int)(T < a.num_groups ? T : a.num_groups);
+        if ((int)blockIdx.x >= W)
+            return;
+        g0 = (int)(T * blockIdx.x / W);
+        g1 = (int)(T * (blockIdx.x + 1) / W);
+    }
+
+    // ---- per-wave state, carried across pieces
+    uint32_t qv[G][NLD][4];   // q of the entry being computed
+    float m[G], l[G], acc[G][NLD][8];
+    const int row_elems_q = a.num_qo_heads * D;
+
+    for (int k0 = g0, k1; k0 < g1; k0 = k1) {
+        // A piece: at most kPiece tiles of at most q_slots entries (so every
+        // entry's q rows are staged).  Entry e_first holds tile k0, so
+        // s_start[e_first + 1] > k0 and the piece is never empty.
+        const int e_first = __builtin_amdgcn_readfirstlane(entry_of(s_start, 0, nb - 1, k0));
+        k1 = min(g1, k0 + kPiece);
+        if (e_first + a.q_slots < nb)
+            k1 = min(k1, s_start[e_first + a.q_slots]);
+        k1 = __builtin_amdgcn_readfirstlane(k1);
+        const int nk = k1 - k0;
+        __syncthreads();   // the previous piece's tables are no longer read
+        for (int t = threadIdx.x; t < nk * PPT; t += blockDim.x) {
+            const int kk = t / PPT;
+            const int r = t % PPT;
+            const int k = k0 + kk;
+            const int e = entry_of(s_start, e_first, nb - 1, k);
+            const int lt = k - s_start[e];
+            const int tok0 = lt * kTileTokens;
+            const int len = s_len[e];
+            const int tok = tok0 + r;
+            const int page_local = tok >> a.log2_page;
+            int page = (tok < len) ? a.indices[s_p0[e] + page_local] : 0;
+            page = (page >= 0 && page < a.num_pages) ? page : 0;
+            s_page[t] = page;
+            if (r == 0) {
+                const int ntok = min(kTileTokens, len - tok0);
+                const int slot8 = SMALL_PAGE ? 0 : ((tok0 & (a.page_size - 1)) >> 3);
+                int info = ntok | (slot8 << kInfoSlotShift) |
+                           (((len - 1) & (kTileTokens - 1)) << kInfoNewRowShift) |
+                           ((e - e_first) << kInfoEntryShift);
+                if (k == max(g0, s_start[e]))
+                    info |= kInfoSegFirst;
+                if (k == min(g1, s_start[e + 1]) - 1)
+                    info |= kInfoSegLast;
+                if (lt == (len - 1) / kTileTokens)
+                    info |= kInfoEntryLast;
+                s_info[kk] = info;
+            }
+        }
+        {
+            // q rows of the piece's entries, 16 bytes a thread
+            const int e_last = entry_of(s_start, e_first, nb - 1, k1 - 1);
+            const int nq = e_last - e_first + 1;   // <= q_slots
+            const int words = row_elems_q >> 3;
+            for (int t = threadIdx.x; t < nq * words; t += blockDim.x) {
+                const int qe = t / words;
+                const int w = t - qe * words;
+                const int b = fixed ? fixed_b : e_first + qe;
+                reinterpret_cast<uint4 *>(s_q + (int64_t)qe * row_elems_q)[w] =
+                    reinterpret_cast<const uint4 *>(a.q + (int64_t)b * row_elems_q)[w];
+            }
+        }
+        __syncthreads();
+        if (!has_head)
+            continue;
+
+        struct Tile {
+            uint4 k[NLD];
+            uint4 v[NLD];
+        };
+        const uint16_t *head_base = a.cache + h * D + j * 8;
+
+        auto load_tile = [&](Tile &x, int kk) {
+            kk = min(kk, nk - 1);
+            const int info = __builtin_amdgcn_readfirstlane(s_info[kk]);
+            const uint16_t *row;
+            if (SMALL_PAGE) {
+                const int page = s_page[kk * PPT + rg];
+                row = head_base + (int64_t)page * a.page_stride +
+                      (uint32_t)((rg & (a.page_size - 1)) * a.row_stride);
+            } else {
+                const int page = __builtin_amdgcn_readfirstlane(s_page[kk]);
+                const int sl = ((info >> kInfoSlotShift) & 31) * kTileTokens + rg;
+                row = head_base + (int64_t)page * a.page_stride + (uint32_t)(sl * a.row_stride);
+            }
+            // One load sequence on every path (only the addresses differ), so
+            // the compiler's waits keep two tiles in flight.
+            const uint16_t *kr = row;
+            const uint16_t *vr = row + a.half_stride;
+            if (fused && (info & kInfoEntryLast) && rg == ((info >> kInfoNewRowShift) & 7)) {
+                // the entry's new row comes from k_new / v_new
+                const int b = fixed ? fixed_b : e_first + (info >> kInfoEntryShift);
+                const int64_t nr = ((int64_t)b * a.num_kv_heads + h) * D + j * 8;
+                kr = a.k_new + nr;
+                vr = a.v_new + nr;
+            }
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                x.k[i] = load16(kr + i * 64);
+                x.v[i] = load16(vr + i * 64);
+            }
+        };
+
+        auto begin_entry = [&](int e) {
+            // q of the G query heads of KV head h, staged in LDS
+            const uint16_t *qb = s_q + (e - e_first) * row_elems_q + h * G * D + j * 8;
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int i = 0; i < NLD; ++i) {
+                    const uint4 w = *reinterpret_cast<const uint4 *>(qb + g * D + i * 64);
+                    qv[g][i][0] = w.x;
+                    qv[g][i][1] = w.y;
+                    qv[g][i][2] = w.z;
+                    qv[g][i][3] = w.w;
+                }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                m[g] = -INFINITY;
+                l[g] = 0.f;
+#pragma unroll
+                for (int i = 0; i < NLD; ++i)
+#pragma unroll
+                    for (int e8 = 0; e8 < 8; ++e8)
+                        acc[g][i][e8] = 0.f;
+            }
+        };
+
+        auto finish_entry = [&](int e, int info, int kk) {
+            const int b = fixed ? fixed_b : e;
+            if (fused && (info & kInfoEntryLast) && rg == ((info >> kInfoNewRowShift) & 7)) {
+                // append: copy the new row of head h into the cache slot
+                int page, sl;
+                if (SMALL_PAGE) {
+                    page = s_page[kk * PPT + rg];
+                    sl = rg & (a.page_size - 1);
+                } else {
+                    page = s_page[kk];
+                    sl = ((info >> kInfoSlotShift) & 31) * kTileTokens + rg;
+                }
+                const int64_t nr = ((int64_t)b * a.num_kv_heads + h) * D + j * 8;
+                uint16_t *dst = a.cache_w + h * D + j * 8 + (int64_t)page * a.page_stride +
+                                (int64_t)sl * a.row_stride;
+#pragma unroll
+                for (int i = 0; i < NLD; ++i) {
+                    *reinterpret_cast<uint4 *>(dst + i * 64) = load16(a.k_new + nr + i * 64);
+                    *reinterpret_cast<uint4 *>(dst + a.half_stride + i * 64) =
+                        load16(a.v_new + nr + i * 64);
+                }
+            }
+            // merge the 8 row groups; every lane ends with the totals
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float mw = max_across_rows(m[g]);
+                const float f = (m[g] == -INFINITY) ? 0.f : exp2_fast(m[g] - mw);
+                l[g] = sum_across_rows(l[g] * f);
+#pragma unroll
+                for (int i = 0; i < NLD; ++i)
+#pragma unroll
+                    for (int e8 = 0; e8 < 8; ++e8)
+                        acc[g][i][e8] = sum_across_rows(acc[g][i][e8] * f);
+                m[g] = mw;
+            }
+            const bool whole = s_start[e] >= g0 && s_start[e + 1] <= g1;
+            const int slot = fixed ? fixed_b * a.max_chunks + fixed_c : (int)blockIdx.x + e;
+            // row group g writes query head h * G + g
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (rg != g)
+                    continue;
+                const int hq = h * G + g;
+                const float inv = 1.f / l[g];
+                if (whole) {
+                    uint16_t *o = a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8;
+#pragma unroll
+                    for (int i = 0; i < NLD; ++i) {
+                        uint4 w;
+                        w.x = pack_bf16x2(acc[g][i][0] * inv, acc[g][i][1] * inv);
+                        w.y = pack_bf16x2(acc[g][i][2] * inv, acc[g][i][3] * inv);
+                        w.z = pack_bf16x2(acc[g][i][4] * inv, acc[g][i][5] * inv);
+                        w.w = pack_bf16x2(acc[g][i][6] * inv, acc[g][i][7] * inv);
+                        *reinterpret_cast<uint4 *>(o + i * 64) = w;
+                    }
+                    if (a.lse != nullptr && j == 0)
+                        a.lse[(int64_t)b * a.num_qo_heads + hq] =
+                            (m[g] + log2_fast(l[g])) * kLn2;
+                } else {
+                    const int64_t prow = (int64_t)slot * a.num_qo_heads + hq;
+                    float *o = a.part_o + prow * D + j * 8;
+#pragma unroll
+                    for (int i = 0; i < NLD; ++i) {
+                        *reinterpret_cast<float4 *>(o + i * 64) =
+                            make_float4(acc[g][i][0] * inv, acc[g][i][1] * inv,
+                                        acc[g][i][2] * inv, acc[g][i][3] * inv);
+                        *reinterpret_cast<float4 *>(o + i * 64 + 4) =
+                            make_float4(acc[g][i][4] * inv, acc[g][i][5] * inv,
+                                        acc[g][i][6] * inv, acc[g][i][7] * inv);
+                    }
+                    if (j == 0)
+                        a.part_lse[prow] = m[g] + log2_fast(l[g]);
+                }
+            }
+        };
+
+        auto compute_tile = [&](const Tile &x, int kk) {
+            const int info = __builtin_amdgcn_readfirstlane(s_info[kk]);
+            const int e = e_first + (info >> kInfoEntryShift);
+            if (info & kInfoSegFirst)
+                begin_entry(e);
+            const int ntok = info & kInfoNtok;
+            const bool edge = ntok < kTileTokens;
+            const bool ok = rg < ntok;
+            float s[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float d = 0.f;
+#pragma unroll
+                for (int i = 0; i < NLD; ++i) {
+                    d = dot2_bf16(qv[g][i][0], x.k[i].x, d);
+                    d = dot2_bf16(qv[g][i][1], x.k[i].y, d);
+                    d = dot2_bf16(qv[g][i][2], x.k[i].z, d);
+                    d = dot2_bf16(qv[g][i][3], x.k[i].w, d);
+                }
+                s[g] = sum_row8(d) * a.scale_log2;
+                if (edge)
+                    s[g] = ok ? s[g] : -INFINITY;
+            }
+            // Lazy maximum: raise m only when a score passes it by more than kTau.
+            bool raise_any = false;
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                raise_any |= s[g] > m[g] + kTau;
+            if (raise_any) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const bool up = s[g] > m[g] + kTau;
+                    const float mn = up ? s[g] : m[g];
+                    const float alpha = up ? exp2_fast(m[g] - mn) : 1.f;
+                    m[g] = mn;
+                    l[g] *= alpha;
+#pragma unroll
+                    for (int i = 0; i < NLD; ++i)
+#pragma unroll
+                        for (int e8 = 0; e8 < 8; ++e8)
+                            acc[g][i][e8] *= alpha;
+                }
+            }
+            float vf[NLD][8];
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const uint4 w = x.v[i];
+                vf[i][0] = bf16_lo(w.x);
+                vf[i][1] = bf16_hi(w.x);
+                vf[i][2] = bf16_lo(w.y);
+                vf[i][3] = bf16_hi(w.y);
+                vf[i][4] = bf16_lo(w.z);
+                vf[i][5] = bf16_hi(w.z);
+                vf[i][6] = bf16_lo(w.w);
+                vf[i][7] = bf16_hi(w.w);
+            }
+            if (edge && !ok) {
+                // stale rows past the end may hold anything, NaN included
+#pragma unroll
+                for (int i = 0; i < NLD; ++i)
+#pragma unroll
+                    for (int e8 = 0; e8 < 8; ++e8)
+                        vf[i][e8] = 0.f;
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float p = exp2_fast(s[g] - m[g]);
+                if (edge)
+                    p = ok ? p : 0.f;   // also covers -inf - -inf
+                l[g] += p;
+#pragma unroll
+                for (int i = 0; i < NLD; ++i)
+#pragma unroll
+                    for (int e8 = 0; e8 < 8; ++e8)
+                        acc[g][i][e8] = fmaf(p, vf[i][e8], acc[g][i][e8]);
+            }
+            if (info & kInfoSegLast)
+                finish_entry(e, info, kk);
+        };
+
+        Tile A, B, C;
+        load_tile(A, 0);
+        load_tile(B, 1);
+        for (int kk = 0;;) {
+            load_tile(C, kk + 2);
+            compute_tile(A, kk);
+            if (++kk >= nk)
+                break;
+            load_tile(A, kk + 2);
+            compute_tile(B, kk);
+            if (++kk >= nk)
+                break;
+            load_tile(B, kk + 2);
+            compute_tile(C, kk);
+            if (++kk >= nk)
+                break;
+        }
     }
 }
 
@@ -695,13 +757,9 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
         a.lse[(int64_t)b * a.num_qo_heads + hq] = (m + log2_fast(sum)) * kLn2;
 }
 
-#ifndef PKV_TILES_PER_BLOCK
-#define PKV_TILES_PER_BLOCK 1
-#endif
 #ifndef PKV_WAVES_PER_CU
 #define PKV_WAVES_PER_CU 0   // 0: as many as the occupancy calculator allows
 #endif
-constexpr int kTilesPerBlock = PKV_TILES_PER_BLOCK;   // 8-token tiles per load block
 
 // Launch through hipLaunchKernel so the returned status belongs to this
 // launch alone (hipGetLastError could report an older, unrelated error).
@@ -715,8 +773,8 @@ hipError_t launch(const void *kernel, dim3 grid, dim3 block, size_t lds, const A
 template <int D, int G>
 const void *decode_kernel_for(int page_size) {
     return page_size < kTileTokens
-               ? reinterpret_cast<const void *>(&decode_kernel<D, G, kTilesPerBlock, true>)
-               : reinterpret_cast<const void *>(&decode_kernel<D, G, kTilesPerBlock, false>);
+               ? reinterpret_cast<const void *>(&decode_kernel<D, G, true>)
+               : reinterpret_cast<const void *>(&decode_kernel<D, G, false>);
 }
 
 template <int D>
@@ -757,10 +815,33 @@ const void *merge_kernel_d(int group) {
     }
 }
 
-size_t balanced_lds_bytes(int batch) { return sizeof(int) * ((size_t)batch + 1); }
+// Dynamic LDS of the decode kernel: entry descriptors of nb entries, the
+// piece's tile tables, and q_slots staged q rows of q_row_bytes each.
+size_t decode_lds_bytes(int nb, int page_size, int q_slots, int q_row_bytes) {
+    const size_t ppt = page_size < kTileTokens ? kTileTokens : 1;
+    const size_t ints = (size_t)3 * nb + 1 + (size_t)kPiece * (ppt + 1) + q_pad(nb);
+    return sizeof(int) * ints + (size_t)q_slots * q_row_bytes;
+}
 
 int group_waves(int num_kv_heads) {
     return num_kv_heads < kMaxWavesPerGroup ? num_kv_heads : kMaxWavesPerGroup;
+}
+
+// q rows staged per piece: at most 8 and no more than the entries a
+// workgroup can see, within 32 KiB and a 64 KiB total for the workgroup's
+// LDS (0 when not even one fits: q is then read from memory).
+int decode_q_slots(int nb, int page_size, int q_row_bytes) {
+    const int64_t tables = (int64_t)decode_lds_bytes(nb, page_size, 0, q_row_bytes);
+    int64_t budget = (int64_t)(64 << 10) - tables;
+    budget = budget < (32 << 10) ? budget : (32 << 10);
+    int64_t n = budget > 0 ? budget / q_row_bytes : 0;
+    n = n > 8 ? 8 : n;
+    return (int)(n < nb ? n : nb);
+}
+
+size_t decode_lds_for(int nb, int page_size, int num_qo_heads, int head_dim) {
+    const int row = num_qo_heads * head_dim * 2;
+    return decode_lds_bytes(nb, page_size, decode_q_slots(nb, page_size, row), row);
 }
 
 }  // namespace
@@ -772,6 +853,7 @@ hipError_t launch_append(const AppendArgs &a, int batch, hipStream_t stream) {
 
 hipError_t balanced_groups(int head_dim, int group, int num_kv_heads, int page_size,
                            int batch, int *groups) {
+    const int num_qo_heads = group * num_kv_heads;
     const void *k = decode_kernel_ptr(head_dim, group, page_size);
     if (k == nullptr)
         return hipErrorInvalidValue;
@@ -781,7 +863,8 @@ hipError_t balanced_groups(int head_dim, int group, int num_kv_heads, int page_s
         err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err == hipSuccess)
         err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, k, 64 * group_waves(num_kv_heads), balanced_lds_bytes(batch));
+            &per_cu, k, 64 * group_waves(num_kv_heads),
+            decode_lds_for(batch, page_size, num_qo_heads, head_dim));
     if (err != hipSuccess)
         return err;
     const int waves = group_waves(num_kv_heads);
@@ -799,7 +882,12 @@ hipError_t balanced_groups(int head_dim, int group, int num_kv_heads, int page_s
     return hipSuccess;
 }
 
-hipError_t launch_decode(const DecodeArgs &a, int head_dim, int group, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs &args, int head_dim, int group, hipStream_t stream) {
+    DecodeArgs a = args;
+    const int nb = a.chunk_tiles > 0 ? 1 : a.batch;
+    const int q_row = a.num_qo_heads * head_dim * 2;
+    a.q_slots = decode_q_slots(nb, a.page_size, q_row);
+    const size_t lds = decode_lds_bytes(nb, a.page_size, a.q_slots, q_row);
     const void *k = decode_kernel_ptr(head_dim, group, a.page_size);
     const void *mk = head_dim == 64 ? merge_kernel_d<64>(group)
                                     : (head_dim == 128 ? merge_kernel_d<128>(group) : nullptr);
@@ -811,12 +899,13 @@ hipError_t launch_decode(const DecodeArgs &a, int head_dim, int group, hipStream
     hipError_t err;
     bool may_split;
     if (a.chunk_tiles > 0) {
-        err = launch(k, dim3((unsigned)a.batch * (unsigned)a.max_chunks, head_groups), block,
-                     0, a, stream);
+        const unsigned batch8 = ((unsigned)a.batch + 7u) & ~7u;
+        err = launch(k, dim3(batch8 * (unsigned)a.max_chunks, head_groups), block,
+                     lds, a, stream);
         may_split = a.max_chunks > 1;
     } else {
         err = launch(k, dim3((unsigned)a.num_groups, head_groups), block,
-                     balanced_lds_bytes(a.batch), a, stream);
+                     lds, a, stream);
         may_split = true;
     }
     if (err != hipSuccess || !may_split)

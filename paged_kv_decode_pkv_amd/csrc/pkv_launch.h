@@ -49,12 +49,13 @@ struct DecodeArgs {
     int32_t chunk_tiles;      // fixed mode: 8-token tiles per chunk; 0 = balanced
     int32_t max_chunks;       // fixed mode: chunks per entry the launch covers
     int32_t num_groups;       // balanced mode: workgroups sharing the tiles
+    int32_t q_slots;          // q rows a workgroup stages in LDS per piece (set at launch)
     float scale_log2;         // sm_scale * log2(e)
 };
 
 // Largest batch the balanced schedule keeps in LDS (its tile prefix sums);
 // larger batches use fixed chunks of kFallbackChunkPages pages.
-constexpr int kMaxBalancedBatch = 8192;
+constexpr int kMaxBalancedBatch = 4096;
 constexpr int kFallbackChunkPages = 16;
 constexpr int kMaxChunkPages = 1 << 16;
 // Upper bound on compute units, for sizing workspace without a device query.

@@ -437,3 +437,66 @@ def test_fixed_runs_poison_entries_over_the_bound():
     ro, rl = _oracle_full(cache_host, 0, ld, table, spec.sm_scale)
     ok = table.active & ~over
     compare(out, lse, ro[ok], rl[ok], rows=ok, what="rows under the bound")
+
+
+# ------------------------------------------------------------ workspace reuse
+def test_shared_workspace_across_calls():
+    """One workspace serves a sequence of balanced and fixed calls of
+    different shapes: whatever an earlier call left in it, every call's rows
+    equal those of a call given a fresh workspace (bit for bit) and the
+    oracle's."""
+    cases = []
+    for idx in (9, 5, 7):
+        hq, hkv, d, ps, lengths, active = SHAPES[idx]
+        rng = np.random.default_rng(4000 + idx)
+        act = np.ones(len(lengths), bool) if active is None else np.asarray(active, bool)
+        table = table_from_lengths(lengths, act, ps, None, rng)
+        ld = workloads.draw_layer(rng, table, hq, hkv, d, 1.0)
+        cases.append((idx, table, ld, act))
+    need = 0
+    for idx, table, ld, act in cases:
+        hq, hkv, d, ps = SHAPES[idx][:4]
+        desc = pkv.CacheDesc(1, table.num_pages, ps, hkv, d)
+        for chunk in (0, 1):
+            need = max(need, pkv.workspace_size(desc, hq, table.batch,
+                                                table.max_pages_per_req, chunk))
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)
+    for rep in range(2):
+        for idx, table, ld, act in cases:
+            hq, hkv, d, ps = SHAPES[idx][:4]
+            cache = to_dev_u16(ld.cache[None])
+            tables = table_to_dev(table)
+            q = to_dev_u16(ld.q)
+            scale = 1.0 / math.sqrt(d)
+            for chunk in (0, 1):
+                kw = dict(max_pages_per_req=table.max_pages_per_req, kv_chunk_pages=chunk)
+                out, lse = pkv.decode(cache, 0, q, *tables, scale, workspace=ws, **kw)
+                out2, lse2 = pkv.decode(cache, 0, q, *tables, scale, **kw)
+                assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+                assert torch.equal(lse, lse2)
+                ro = oracle.decode(ld.cache[None], 0, ld.q, table.indptr, table.indices,
+                                   table.last_len, scale)
+                compare(out, lse, ro[0][act], ro[1][act], rows=act,
+                        what=f"shape {idx} chunk {chunk} rep {rep}")
+
+
+@pytest.mark.parametrize("chunk", [0, 1])
+def test_batch_above_balanced_limit(chunk):
+    """4200 entries (above the 4096 the balanced schedule holds, so the
+    default falls back to fixed runs of 16 pages) x 16 KV heads, pages of one
+    token, 1 to 24 tokens each; with runs of one 8-token tile most entries
+    are split in 2 or 3 and merged."""
+    rng = np.random.default_rng(4242)
+    batch, hq, hkv, d, ps = 4200, 16, 16, 64, 1
+    lengths = rng.integers(1, 25, size=batch)
+    act = np.ones(batch, bool)
+    table = table_from_lengths(lengths.tolist(), act, ps, None, rng)
+    ld = workloads.draw_layer(rng, table, hq, hkv, d, 1.0)
+    cache = to_dev_u16(ld.cache[None])
+    tables = table_to_dev(table)
+    scale = 1.0 / math.sqrt(d)
+    out, lse = pkv.decode(cache, 0, to_dev_u16(ld.q), *tables, scale,
+                          max_pages_per_req=table.max_pages_per_req, kv_chunk_pages=chunk)
+    ro, rl = oracle.decode(ld.cache[None], 0, ld.q, table.indptr, table.indices,
+                           table.last_len, scale)
+    compare(out, lse, ro, rl, what=f"batch 4200 x 16 heads, chunk {chunk}")
