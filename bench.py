@@ -2,11 +2,11 @@
 """Benchmark of the paged-KV decode hot path on one MI355X.
 
 A step is one decode step of a Qwen3-4B-like model's attention over all 36
-layers: for each layer, ``pkv_append`` of the batch's new K/V rows and
-``pkv_decode`` of one query row per entry (batch 64, 32 query / 8 KV heads,
-head_dim 128, page_size 16, lengths log-uniform in [64, 4096]).  Inputs are
-seeded synthetic data resident in HBM before timing starts.  The step is
-captured once as a HIP graph and replayed.
+layers: ``pkv_plan`` walks the step's page table once, then for each layer
+``pkv_run`` appends the batch's new K/V rows and decodes one query row per
+entry (batch 64, 32 query / 8 KV heads, head_dim 128, page_size 16, lengths
+log-uniform in [64, 4096]).  Inputs are seeded synthetic data resident in HBM
+before timing starts.  The step is captured once as a HIP graph and replayed.
 
 Printed: ONE JSON line with the whole-step throughput (algorithmic bytes per
 second), the decode kernel's roofline figures measured live with HIP events on
@@ -49,7 +49,9 @@ def parse():
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--separate", action="store_true",
-                    help="call pkv_append then pkv_decode instead of pkv_append_decode")
+                    help="per layer pkv_append then a decode-only pkv_run")
+    ap.add_argument("--plan-per-layer", action="store_true",
+                    help="per layer pkv_append_decode (plans inside every call)")
     ap.add_argument("--probe-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter scale)")
     return ap.parse_args()
@@ -148,46 +150,67 @@ def main():
     desc = pkv.cache_desc(cache)
     vp = ctypes.c_void_p
     tab_ptrs = [vp(t.data_ptr()) for t in tabs]
+    null = vp(0)
+    ws_args = (vp(ws.data_ptr()), ws.numel())
 
     def calls_for(stream_handle):
+        """(plan call or None, per-layer [(fn, args, name), ...])"""
         s = vp(stream_handle)
-        app, dec = [], []
+        plan = None
+        if not args.plan_per_layer:
+            plan = (desc, hq, *tab_ptrs, b, maxp, chunk, *ws_args, s)
+        layers = []
         for layer in range(nl):
             kn, vn = vp(KN[layer].data_ptr()), vp(VN[layer].data_ptr())
-            tail = (b, ctypes.c_float(spec.sm_scale), vp(out[layer].data_ptr()),
-                    vp(lse[layer].data_ptr()), maxp, chunk, vp(ws.data_ptr()), ws.numel(), s)
+            qo = (vp(Q[layer].data_ptr()), hq)
+            res = (ctypes.c_float(spec.sm_scale), vp(out[layer].data_ptr()),
+                   vp(lse[layer].data_ptr()), maxp, chunk, *ws_args, s)
+            cl = []
             if args.separate:
-                app.append((vp(cache.data_ptr()), desc, layer, kn, vn, *tab_ptrs, b, s))
-                dec.append((vp(cache.data_ptr()), desc, layer, vp(Q[layer].data_ptr()), hq,
-                            *tab_ptrs, *tail))
+                cl.append((pkv.lib.pkv_append,
+                           (vp(cache.data_ptr()), desc, layer, kn, vn, *tab_ptrs, b, s),
+                           "pkv_append"))
+                cl.append((pkv.lib.pkv_run, (vp(cache.data_ptr()), desc, layer, null, null,
+                                             *qo, b, *res), "pkv_run"))
+            elif args.plan_per_layer:
+                cl.append((pkv.lib.pkv_append_decode,
+                           (vp(cache.data_ptr()), desc, layer, kn, vn, *qo, *tab_ptrs, b,
+                            *res), "pkv_append_decode"))
             else:
-                dec.append((vp(cache.data_ptr()), desc, layer, kn, vn,
-                            vp(Q[layer].data_ptr()), hq, *tab_ptrs, *tail))
-        return app, dec
+                cl.append((pkv.lib.pkv_run, (vp(cache.data_ptr()), desc, layer, kn, vn,
+                                             *qo, b, *res), "pkv_run"))
+            layers.append(cl)
+        return plan, layers
 
-    decode_fn = pkv.lib.pkv_decode if args.separate else pkv.lib.pkv_append_decode
-    decode_name = "pkv_decode" if args.separate else "pkv_append_decode"
+    if args.separate:
+        call_name = "pkv_append + pkv_run"
+    elif args.plan_per_layer:
+        call_name = "pkv_append_decode"
+    else:
+        call_name = "pkv_run (append + decode)"
 
-    def run_step(app, dec, events=None):
-        for layer in range(nl):
-            if app:
-                rc = pkv.lib.pkv_append(*app[layer])
-                if rc:
-                    raise pkv.PkvError(rc, "pkv_append")
-            if events is not None:
-                events[layer][0].record()
-            rc = decode_fn(*dec[layer])
+    def run_step(plan, layers, events=None):
+        if plan is not None:
+            rc = pkv.lib.pkv_plan(*plan)
             if rc:
-                raise pkv.PkvError(rc, decode_name)
-            if events is not None:
-                events[layer][1].record()
+                raise pkv.PkvError(rc, "pkv_plan")
+        for layer in range(nl):
+            for i, (fn, a, name) in enumerate(layers[layer]):
+                timed = events is not None and i == len(layers[layer]) - 1
+                if timed:
+                    events[layer][0].record()
+                rc = fn(*a)
+                if rc:
+                    raise pkv.PkvError(rc, name)
+                if timed:
+                    events[layer][1].record()
 
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
-        app, dec = calls_for(stream.cuda_stream)
+        plan_call, layer_calls = calls_for(stream.cuda_stream)
         for _ in range(2):
-            run_step(app, dec)
+            run_step(plan_call, layer_calls)
     torch.cuda.synchronize()
 
     # ---- the step as one HIP graph
@@ -196,15 +219,15 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             cap = torch.cuda.current_stream()
-            capp, cdec = calls_for(cap.cuda_stream)
-            run_step(capp, cdec)
+            cplan, clayers = calls_for(cap.cuda_stream)
+            run_step(cplan, clayers)
         torch.cuda.synchronize()
 
     def replay():
         if graph is not None:
             graph.replay()
         else:
-            run_step(app, dec)
+            run_step(plan_call, layer_calls)
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -233,7 +256,7 @@ def main():
         if hasattr(torch.cuda, "_sleep"):
             torch.cuda._sleep(20_000_000)   # let the host queue run ahead of the GPU
         for k in range(ksteps):
-            run_step(app, dec, events=evs[k])
+            run_step(plan_call, layer_calls, events=evs[k])
     torch.cuda.synchronize()
     durs = np.array([[a.elapsed_time(z) for a, z in row] for row in evs]) * 1e3   # us
     dec_us = float(durs.mean())
@@ -256,16 +279,16 @@ def main():
                    "layers": nl, "num_qo_heads": hq, "num_kv_heads": hkv, "head_dim": d,
                    "page_size": ps, "lengths": "log-uniform [64, 4096]",
                    "kv_chunk_pages": chunk, "hip_graph": graph is not None,
-                   "call": "pkv_append + pkv_decode" if args.separate else "pkv_append_decode",
+                   "call": call_name,
                    "step_bytes": step_bytes},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "decode_rows_per_s": round(rows_per_s, 1),
         "ms_per_step_events": round(ms_step_ev, 5),
-        "roofline": {"bound": "hbm", "kernel": f"{decode_name} (decode pass + LSE merge)",
+        "roofline": {"bound": "hbm", "kernel": f"{call_name}: run_kernel (decode + merge)",
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if args.config == 3 and not args.separate
-                     and args.chunk_pages == 0 else None,
+                     and not args.plan_per_layer and args.chunk_pages == 0 else None,
                      "bytes_per_launch": launch_bytes, "avg_launch_us": round(dec_us, 3),
                      "launches": int(durs.size)},
     }

@@ -89,14 +89,71 @@ int pkv_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
                const int32_t *last_page_len, int32_t batch, hipStream_t stream);
 
 /*
- * pkv_decode_workspace_size -- bytes of device workspace pkv_decode and
- * pkv_append_decode need for these arguments; 0 when none is needed (then
- * workspace may be NULL).  Host function; no device work.  Returns 0 for
- * arguments pkv_decode would reject.
+ * pkv_decode_workspace_size -- bytes of device workspace that pkv_plan,
+ * pkv_run, pkv_decode and pkv_append_decode need for these arguments.  Host
+ * function; no device work.  Returns 0 for arguments the calls would reject.
+ * The size grows with batch * max_pages_per_req (16 bytes per 8-token tile
+ * of that many pages, for the step's plan) plus fp32 partial rows for split
+ * entries.
  */
 size_t pkv_decode_workspace_size(pkv_cache_desc_t desc, int32_t num_qo_heads,
                                  int32_t batch, int32_t max_pages_per_req,
                                  int32_t kv_chunk_pages);
+
+/*
+ * pkv_plan -- walk a step's page table once and write the decode schedule
+ * into `workspace`, for any number of pkv_run calls (one per layer: the
+ * table is the same for every layer, because the layer is the outermost axis
+ * of the cache).  This is the page-table walk and work split of a decode
+ * step ("How a program runs": the KV page tables are written once per step).
+ *
+ * Work is split into runs of tokens whose partial (output, lse) pairs are
+ * merged by log-sum-exp, the way partial attentions are merged on the
+ * "Supported Models" page (LTX-2.5 notes):
+ *   kv_chunk_pages == 0  balanced: the tokens of the whole batch are shared
+ *                        evenly among the workgroups the GPU holds at once.
+ *                        Fastest; the split, so the last bits of a row, can
+ *                        change with the rest of the batch.
+ *   kv_chunk_pages  > 0  fixed: each entry is cut into runs of
+ *                        kv_chunk_pages pages; a row is bit-identical
+ *                        whatever else is in the batch.  At most 65536.
+ * Batches above 4096 entries use fixed runs of 16 pages.
+ *  page_indptr/page_indices/last_page_len   as for pkv_append.
+ *  max_pages_per_req  host upper bound on any entry's page count; it sizes
+ *                     the schedule.  An entry listing more pages gets NaN
+ *                     rows from pkv_run instead of a truncated result.
+ *  workspace          device memory, 256-byte aligned, of workspace_bytes >=
+ *                     pkv_decode_workspace_size(...).  Its contents need no
+ *                     initialisation; the plan overwrites what it uses.
+ * Errors as for pkv_decode.  Asynchronous like every call: the page table
+ * is read on the device when the plan runs, in stream order.
+ */
+int pkv_plan(pkv_cache_desc_t desc, int32_t num_qo_heads,
+             const int32_t *page_indptr, const int32_t *page_indices,
+             const int32_t *last_page_len, int32_t batch, int32_t max_pages_per_req,
+             int32_t kv_chunk_pages, void *workspace, size_t workspace_bytes,
+             hipStream_t stream);
+
+/*
+ * pkv_run -- the decode of one layer on a plan that pkv_plan wrote into
+ * `workspace`; with k_new and v_new also the append, in the same pass (see
+ * pkv_append_decode).  Computes exactly what pkv_decode computes.
+ *  kv_cache      bf16 cache described by `desc`; written only when k_new and
+ *                v_new are given (both or neither).
+ *  q, out, lse, sm_scale   as for pkv_decode.
+ *  batch, max_pages_per_req, kv_chunk_pages, desc.page_size,
+ *  desc.num_kv_heads, num_qo_heads   must equal those of the pkv_plan call
+ *                that wrote the workspace; the page table must be unchanged
+ *                since, and the plan must precede this call in stream order.
+ * Between the plan and its pkv_run calls the workspace may serve nothing
+ * else; pkv_run calls on one workspace must not overlap (each leaves the
+ * plan intact for the next).
+ */
+int pkv_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+            const void *k_new, const void *v_new, const void *q,
+            int32_t num_qo_heads, int32_t batch, float sm_scale, void *out,
+            float *lse, int32_t max_pages_per_req, int32_t kv_chunk_pages,
+            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * pkv_decode -- grouped-query attention of one query row per entry over its
@@ -110,30 +167,16 @@ size_t pkv_decode_workspace_size(pkv_cache_desc_t desc, int32_t num_qo_heads,
  *   lse[b, hq] = ln(sum_t exp(s_t))                         natural log
  *   out[b, hq, :] = sum_t exp(s_t - lse[b, hq]) * V_t[h, :]
  * Accumulation is fp32; out is rounded once to bf16 (nearest even).
- * Work is split into runs of tokens whose partial (output, lse) pairs are
- * merged by log-sum-exp, the way partial attentions are merged on the
- * "Supported Models" page (LTX-2.5 notes):
- *   kv_chunk_pages == 0  balanced: the tokens of the whole batch are shared
- *                        evenly among the workgroups the GPU holds at once.
- *                        Fastest; the split, so the last bits of a row, can
- *                        change with the rest of the batch.
- *   kv_chunk_pages  > 0  fixed: each entry is cut into runs of
- *                        kv_chunk_pages pages (rounded up to whole 8-token
- *                        tiles); a row is bit-identical whatever else is in
- *                        the batch.  At most 65536.
- * Batches above 4096 entries use fixed runs of 16 pages.
+ * The call is pkv_plan followed by pkv_run on the same workspace (two
+ * launches); a step that decodes several layers on one page table plans once
+ * and runs per layer instead.
  *  kv_cache           bf16 cache described by `desc` (read only).
  *  q                  bf16 [batch, num_qo_heads, head_dim], RoPE applied.
  *  page_indptr/page_indices/last_page_len   as for pkv_append.
  *  sm_scale           finite softmax scale, e.g. 1/sqrt(head_dim).
  *  out                bf16 [batch, num_qo_heads, head_dim], written.
  *  lse                fp32 [batch, num_qo_heads], written; may be NULL.
- *  max_pages_per_req  host upper bound on any entry's page count (sizes the
- *                     fixed-mode launch; in fixed mode an entry above it gets
- *                     NaN rows instead of a truncated result).
- *  workspace          device scratch, 256-byte aligned, of workspace_bytes >=
- *                     pkv_decode_workspace_size(...); may be NULL when that
- *                     size is 0.  Its contents need no initialisation.
+ *  max_pages_per_req, kv_chunk_pages, workspace   as for pkv_plan.
  * Supported: head_dim 64 or 128, num_kv_heads <= 16, num_qo_heads /
  * num_kv_heads in 1..8.  Rows of padding entries are computed over scratch
  * page 0 and are garbage by design; they never fault and never touch other

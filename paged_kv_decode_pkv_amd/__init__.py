@@ -10,7 +10,9 @@ to the library.  There is no fallback: importing this package fails if
 The calls follow the per-layer API on the vox-serve "Adding a Model" page
 (section 1): :func:`append` is ``set_kv_cache(kv_cache, k, v)`` and
 :func:`decode` is ``run(q, kv_cache)``, with the step's page table passed in
-CSR form (``page_indptr``, ``page_indices``, ``last_page_len``).
+CSR form (``page_indptr``, ``page_indices``, ``last_page_len``).  A step that
+decodes many layers on one page table calls :func:`plan` once and
+:func:`run` per layer.
 """
 from __future__ import annotations
 
@@ -90,6 +92,11 @@ def _load():
     lib.pkv_append_decode.argtypes = [p, CacheDesc, i32, p, p, p, i32, p, p, p, i32,
                                       ctypes.c_float, p, p, i32, i32, p, sz, p]
     lib.pkv_append_decode.restype = ctypes.c_int
+    lib.pkv_plan.argtypes = [CacheDesc, i32, p, p, p, i32, i32, i32, p, sz, p]
+    lib.pkv_plan.restype = ctypes.c_int
+    lib.pkv_run.argtypes = [p, CacheDesc, i32, p, p, p, i32, i32, ctypes.c_float, p, p,
+                            i32, i32, p, sz, p]
+    lib.pkv_run.restype = ctypes.c_int
     lib.pkv_validate_page_table.argtypes = [p, p, p, i32, i32, i32, i32,
                                             ctypes.POINTER(i32)]
     lib.pkv_validate_page_table.restype = ctypes.c_int
@@ -259,6 +266,74 @@ def append_decode(kv_cache, layer: int, k_new, v_new, q, page_indptr, page_indic
                                ws_bytes, _stream(stream))
     if rc != PKV_OK:
         raise PkvError(rc, "pkv_append_decode")
+    return out, lse
+
+
+class DecodePlan:
+    """A step's decode schedule (pkv_plan) in its workspace, with the shape
+    arguments every :func:`run` on it repeats."""
+
+    def __init__(self, workspace, batch, num_qo_heads, max_pages_per_req, kv_chunk_pages):
+        self.workspace = workspace
+        self.batch = batch
+        self.num_qo_heads = num_qo_heads
+        self.max_pages_per_req = max_pages_per_req
+        self.kv_chunk_pages = kv_chunk_pages
+
+
+def plan(kv_cache, num_qo_heads: int, page_indptr, page_indices, last_page_len,
+         max_pages_per_req: int, kv_chunk_pages: int = 0, workspace=None,
+         stream=None) -> DecodePlan:
+    """Walk the step's page table once (pkv_plan); returns the plan for :func:`run`."""
+    import torch
+    desc = cache_desc(kv_cache)
+    batch = int(last_page_len.shape[0])
+    dev = kv_cache.device
+    need = workspace_size(desc, num_qo_heads, batch, max_pages_per_req, kv_chunk_pages)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    rc = lib.pkv_plan(desc, int(num_qo_heads),
+                      *_tables(kv_cache, page_indptr, page_indices, last_page_len), batch,
+                      int(max_pages_per_req), int(kv_chunk_pages),
+                      _dev_ptr(workspace, "workspace", device=dev),
+                      workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != PKV_OK:
+        raise PkvError(rc, "pkv_plan")
+    return DecodePlan(workspace, batch, int(num_qo_heads), int(max_pages_per_req),
+                      int(kv_chunk_pages))
+
+
+def run(kv_cache, layer: int, q, plan_: DecodePlan, sm_scale: float, k_new=None,
+        v_new=None, out=None, lse=None, with_lse: bool = True, stream=None):
+    """Decode one layer on a plan (pkv_run); with k_new / v_new also the append."""
+    import torch
+    desc = cache_desc(kv_cache)
+    if q.dim() != 3 or q.shape[0] != plan_.batch or q.shape[1] != plan_.num_qo_heads:
+        raise ValueError("q must be [batch, Hq, D] of the plan")
+    batch, hq = plan_.batch, plan_.num_qo_heads
+    dev = kv_cache.device
+    if out is None:
+        out = torch.empty((batch, hq, desc.head_dim), dtype=torch.bfloat16, device=dev)
+    if lse is None and with_lse:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    fused = k_new is not None or v_new is not None
+    if fused:
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            if t is None or tuple(t.shape) != (batch, desc.num_kv_heads, desc.head_dim):
+                raise ValueError(f"{name} must be [batch, Hkv, D]")
+    null = ctypes.c_void_p(0)
+    ws = plan_.workspace
+    rc = lib.pkv_run(_dev_ptr(kv_cache, "kv_cache", torch.bfloat16), desc, int(layer),
+                     _dev_ptr(k_new, "k_new", torch.bfloat16, dev) if fused else null,
+                     _dev_ptr(v_new, "v_new", torch.bfloat16, dev) if fused else null,
+                     _dev_ptr(q, "q", torch.bfloat16, dev), hq, batch, float(sm_scale),
+                     _dev_ptr(out, "out", torch.bfloat16, dev),
+                     null if lse is None else _dev_ptr(lse, "lse", torch.float32, dev),
+                     plan_.max_pages_per_req, plan_.kv_chunk_pages,
+                     _dev_ptr(ws, "workspace", device=dev), ws.numel() * ws.element_size(),
+                     _stream(stream))
+    if rc != PKV_OK:
+        raise PkvError(rc, "pkv_run")
     return out, lse
 
 

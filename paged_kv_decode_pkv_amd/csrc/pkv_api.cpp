@@ -24,13 +24,6 @@ int hip_status(hipError_t err) {
 
 bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
-int log2_int(int32_t x) {
-    int r = 0;
-    while ((1 << r) < x)
-        ++r;
-    return r;
-}
-
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
@@ -47,37 +40,50 @@ int64_t page_elems(const pkv_cache_desc_t &d) {
     return 2 * (int64_t)d.page_size * d.num_kv_heads * d.head_dim;
 }
 
-// How one pkv_decode call splits its work, and the workspace that needs.
-struct Plan {
-    int32_t chunk_tiles = 0;   // 0: balanced
+// Workspace layout of a plan and how its work is split.  Every offset
+// depends on host arguments only (the balanced split's workgroup count W is a
+// device property, so regions are sized for its bound).
+struct Layout {
+    int32_t chunk_tiles = 0;    // 0: balanced
     int32_t max_chunks = 1;
-    int64_t slots = 0;         // partial rows per query head
+    int32_t tiles_per_page = 1;
+    int64_t max_tiles = 0;      // tiles of batch entries of max_pages_per_req pages
+    int64_t slots = 0;          // partial rows per query head
+    int64_t off_ent = 0, off_blocks = 0, off_part_o = 0, off_part_lse = 0;
     int64_t ws_bytes = 0;
-    int64_t off_lse = 0, off_start = 0;
 };
 
-Plan make_plan(const pkv_cache_desc_t &d, int32_t num_qo_heads, int32_t batch,
-               int32_t max_pages_per_req, int32_t kv_chunk_pages) {
-    Plan p;
+Layout make_layout(const pkv_cache_desc_t &d, int32_t num_qo_heads, int32_t batch,
+                   int32_t max_pages_per_req, int32_t kv_chunk_pages) {
+    Layout p;
+    const int64_t tt = pkv::kTileTokens;
+    p.tiles_per_page = (int32_t)((d.page_size + tt - 1) / tt);
+    const int64_t entry_tiles = (int64_t)max_pages_per_req * p.tiles_per_page;
+    p.max_tiles = (int64_t)batch * entry_tiles;
     int32_t chunk_pages = kv_chunk_pages;
     if (chunk_pages == 0 && batch > pkv::kMaxBalancedBatch)
         chunk_pages = pkv::kFallbackChunkPages;
+    int64_t block_ints4;   // int4 records of all blocks (headers included)
     if (chunk_pages > 0) {
-        const int64_t tt = pkv::kTileTokens;
-        p.chunk_tiles = (int32_t)(((int64_t)chunk_pages * d.page_size + tt - 1) / tt);
-        const int64_t max_tiles = ((int64_t)max_pages_per_req * d.page_size + tt - 1) / tt;
-        p.max_chunks = (int32_t)((max_tiles + p.chunk_tiles - 1) / p.chunk_tiles);
+        p.chunk_tiles = (int32_t)((int64_t)chunk_pages * p.tiles_per_page);
+        p.max_chunks = (int32_t)((entry_tiles + p.chunk_tiles - 1) / p.chunk_tiles);
         if (p.max_chunks < 1)
             p.max_chunks = 1;
-        p.slots = p.max_chunks > 1 ? (int64_t)batch * p.max_chunks : 0;
+        p.slots = (int64_t)batch * p.max_chunks;
+        const int64_t nblocks = ((int64_t)batch + 7) / 8 * 8 * p.max_chunks;
+        block_ints4 = nblocks * (1 + (int64_t)p.chunk_tiles);
     } else {
-        p.slots = pkv::balanced_groups_bound(d.num_kv_heads) + batch;
+        const int64_t wb = pkv::balanced_blocks_bound(d.num_kv_heads);
+        p.slots = wb + batch;
+        // W blocks of 1 + ceil(max_tiles / W) records each, for any W <= wb
+        block_ints4 = p.max_tiles + 2 * wb;
     }
+    p.off_ent = align256((int64_t)batch * d.num_kv_heads * 4);
+    p.off_blocks = p.off_ent + align256((int64_t)batch * 16);
+    p.off_part_o = p.off_blocks + align256(block_ints4 * 16);
     const int64_t rows = p.slots * num_qo_heads;
-    p.off_lse = align256(rows * d.head_dim * 4);
-    p.off_start = p.off_lse + align256(rows * 4);
-    const int64_t start_bytes = p.chunk_tiles > 0 ? 0 : align256(((int64_t)batch + 1) * 4);
-    p.ws_bytes = p.slots > 0 || start_bytes > 0 ? p.off_start + start_bytes : 0;
+    p.off_part_lse = p.off_part_o + align256(rows * d.head_dim * 4);
+    p.ws_bytes = p.off_part_lse + align256(rows * 4);
     return p;
 }
 
@@ -95,77 +101,173 @@ int check_decode_args(const pkv_cache_desc_t &desc, int32_t layer, int32_t num_q
         return PKV_ERR_UNSUPPORTED;
     const int group = num_qo_heads / desc.num_kv_heads;
     if ((desc.head_dim != 64 && desc.head_dim != 128) || group > 8 ||
-        desc.num_kv_heads > pkv::kMaxKvHeads)
+        desc.num_kv_heads > pkv::kMaxKvHeads || !pkv::run_supported(desc.head_dim, group))
         return PKV_ERR_UNSUPPORTED;
     return PKV_OK;
 }
 
-int decode_common(const void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
-                  const void *k_new, const void *v_new, const void *q, int32_t num_qo_heads,
-                  const int32_t *page_indptr, const int32_t *page_indices,
-                  const int32_t *last_page_len, int32_t batch, float sm_scale, void *out,
-                  float *lse, int32_t max_pages_per_req, int32_t kv_chunk_pages,
-                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+// Checks shared by pkv_plan and pkv_run; fills the layout and the number of
+// decode workgroups along x.
+int prepare(const pkv_cache_desc_t &desc, int32_t num_qo_heads, int32_t batch,
+            int32_t max_pages_per_req, int32_t kv_chunk_pages, const void *workspace,
+            size_t workspace_bytes, Layout &lay, int &num_blocks, int &block_stride) {
+    lay = make_layout(desc, num_qo_heads, batch, max_pages_per_req, kv_chunk_pages);
+    // tile and block indices, and byte offsets into the partial arrays, are
+    // 32-bit in the kernels
+    if (lay.max_tiles > 0x3fffffffLL || lay.ws_bytes - lay.off_part_o > 0x7fffffffLL)
+        return PKV_ERR_BAD_SHAPE;
+    if (workspace == nullptr || workspace_bytes < (size_t)lay.ws_bytes)
+        return PKV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return PKV_ERR_ALIGNMENT;
+    if (lay.chunk_tiles > 0) {
+        const int64_t nb = ((int64_t)batch + 7) / 8 * 8 * lay.max_chunks;
+        if (nb > 0x7fffffffLL || nb * (1 + (int64_t)lay.chunk_tiles) > 0x3fffffffLL)
+            return PKV_ERR_BAD_SHAPE;
+        num_blocks = (int)nb;
+        block_stride = 1 + lay.chunk_tiles;
+    } else {
+        const int group = num_qo_heads / desc.num_kv_heads;
+        hipError_t err = pkv::balanced_blocks(desc.head_dim, group, desc.num_kv_heads,
+                                              &num_blocks);
+        if (err != hipSuccess)
+            return hip_status(err);
+        block_stride = (int)(1 + (lay.max_tiles + num_blocks - 1) / num_blocks);
+    }
+    return PKV_OK;
+}
+
+// Host checks of a pkv_plan call; on success `args` is ready to launch.
+int prepare_plan(pkv_cache_desc_t desc, int32_t num_qo_heads, const int32_t *page_indptr,
+                 const int32_t *page_indices, const int32_t *last_page_len, int32_t batch,
+                 int32_t max_pages_per_req, int32_t kv_chunk_pages, void *workspace,
+                 size_t workspace_bytes, pkv::PlanArgs &a) {
+    int rc = check_decode_args(desc, 0, num_qo_heads, batch, 1.f, max_pages_per_req,
+                               kv_chunk_pages);
+    if (rc != PKV_OK)
+        return rc;
+    if (!page_indptr || !page_indices || !last_page_len)
+        return PKV_ERR_NULL_PTR;
+    Layout lay;
+    int num_blocks = 0, block_stride = 0;
+    rc = prepare(desc, num_qo_heads, batch, max_pages_per_req, kv_chunk_pages, workspace,
+                 workspace_bytes, lay, num_blocks, block_stride);
+    if (rc != PKV_OK)
+        return rc;
+    char *ws = static_cast<char *>(workspace);
+    a.indptr = page_indptr;
+    a.indices = page_indices;
+    a.last_len = last_page_len;
+    a.blocks = reinterpret_cast<int32_t *>(ws + lay.off_blocks);
+    a.ent = reinterpret_cast<int32_t *>(ws + lay.off_ent);
+    a.cnt = reinterpret_cast<int32_t *>(ws);
+    a.batch = batch;
+    a.num_pages = desc.num_pages;
+    a.page_size = desc.page_size;
+    a.tiles_per_page = lay.tiles_per_page;
+    a.num_kv_heads = desc.num_kv_heads;
+    a.num_blocks = num_blocks;
+    a.block_stride = block_stride;
+    a.chunk_tiles = lay.chunk_tiles;
+    a.max_chunks = lay.max_chunks;
+    a.max_pages = max_pages_per_req;
+    return PKV_OK;
+}
+
+// Host checks of a pkv_run call; on success `args` and the launch shape are set.
+struct RunLaunch {
+    pkv::RunArgs args;
+    const int32_t *blocks = nullptr;
+    const int32_t *ent = nullptr;
+    int num_blocks = 0;
+    int group = 0;
+};
+
+int prepare_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *k_new,
+                const void *v_new, const void *q, int32_t num_qo_heads, int32_t batch,
+                float sm_scale, void *out, float *lse, int32_t max_pages_per_req,
+                int32_t kv_chunk_pages, void *workspace, size_t workspace_bytes,
+                RunLaunch &r) {
     int rc = check_decode_args(desc, layer, num_qo_heads, batch, sm_scale, max_pages_per_req,
                                kv_chunk_pages);
     if (rc != PKV_OK)
         return rc;
     const bool fused = k_new != nullptr || v_new != nullptr;
-    if (batch == 0)
-        return PKV_OK;
-    if (!kv_cache || !q || !page_indptr || !page_indices || !last_page_len || !out ||
-        (fused && (!k_new || !v_new)))
+    if (!kv_cache || !q || !out || (fused && (!k_new || !v_new)))
         return PKV_ERR_NULL_PTR;
     if (!aligned16(kv_cache) || !aligned16(q) || !aligned16(out) ||
         (fused && (!aligned16(k_new) || !aligned16(v_new))))
         return PKV_ERR_ALIGNMENT;
-    const Plan plan = make_plan(desc, num_qo_heads, batch, max_pages_per_req, kv_chunk_pages);
-    if (plan.chunk_tiles > 0 && ((int64_t)batch + 7) / 8 * 8 * plan.max_chunks > 0x7fffffffLL)
-        return PKV_ERR_BAD_SHAPE;
-    if (plan.ws_bytes > 0 &&
-        (workspace == nullptr || workspace_bytes < (size_t)plan.ws_bytes))
-        return PKV_ERR_WORKSPACE;
-    if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return PKV_ERR_ALIGNMENT;
-
-    pkv::DecodeArgs a;
+    Layout lay;
+    int num_blocks = 0, block_stride = 0;
+    rc = prepare(desc, num_qo_heads, batch, max_pages_per_req, kv_chunk_pages, workspace,
+                 workspace_bytes, lay, num_blocks, block_stride);
+    if (rc != PKV_OK)
+        return rc;
+    char *ws = static_cast<char *>(workspace);
+    pkv::RunArgs &a = r.args;
     const int64_t layer_off = (int64_t)layer * desc.num_pages * page_elems(desc);
     a.cache = static_cast<const uint16_t *>(kv_cache) + layer_off;
-    a.cache_w = fused ? const_cast<uint16_t *>(a.cache) : nullptr;
+    a.cache_w = fused ? static_cast<uint16_t *>(kv_cache) + layer_off : nullptr;
     a.q = static_cast<const uint16_t *>(q);
     a.k_new = static_cast<const uint16_t *>(k_new);
     a.v_new = static_cast<const uint16_t *>(v_new);
-    a.indptr = page_indptr;
-    a.indices = page_indices;
-    a.last_len = last_page_len;
     a.out = static_cast<uint16_t *>(out);
     a.lse = lse;
-    char *ws = static_cast<char *>(workspace);
-    a.part_o = plan.slots ? reinterpret_cast<float *>(ws) : nullptr;
-    a.part_lse = plan.slots ? reinterpret_cast<float *>(ws + plan.off_lse) : nullptr;
-    a.tile_start = plan.chunk_tiles > 0 ? nullptr
-                                        : reinterpret_cast<int32_t *>(ws + plan.off_start);
+    a.part_o = reinterpret_cast<float *>(ws + lay.off_part_o);
+    a.part_lse = reinterpret_cast<float *>(ws + lay.off_part_lse);
+    a.part_o_bytes = lay.off_part_lse - lay.off_part_o;
+    a.part_lse_bytes = lay.ws_bytes - lay.off_part_lse;
+    a.cnt = reinterpret_cast<int32_t *>(ws);
     a.page_stride = page_elems(desc);
     a.half_stride = desc.page_size * desc.num_kv_heads * desc.head_dim;
     a.row_stride = desc.num_kv_heads * desc.head_dim;
     a.num_qo_heads = num_qo_heads;
     a.num_kv_heads = desc.num_kv_heads;
-    a.num_pages = desc.num_pages;
     a.batch = batch;
-    a.page_size = desc.page_size;
-    a.log2_page = log2_int(desc.page_size);
-    a.chunk_tiles = plan.chunk_tiles;
-    a.max_chunks = plan.max_chunks;
-    a.num_groups = 0;
+    a.block_stride = block_stride;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
-    const int group = num_qo_heads / desc.num_kv_heads;
-    if (plan.chunk_tiles == 0) {
-        hipError_t err = pkv::balanced_groups(desc.head_dim, group, desc.num_kv_heads,
-                                              desc.page_size, batch, &a.num_groups);
-        if (err != hipSuccess)
-            return hip_status(err);
-    }
-    return hip_status(pkv::launch_decode(a, desc.head_dim, group, stream));
+    r.blocks = reinterpret_cast<const int32_t *>(ws + lay.off_blocks);
+    r.ent = reinterpret_cast<const int32_t *>(ws + lay.off_ent);
+    r.num_blocks = num_blocks;
+    r.group = num_qo_heads / desc.num_kv_heads;
+    return PKV_OK;
+}
+
+int launch_run(const RunLaunch &r, const pkv_cache_desc_t &desc, hipStream_t stream) {
+    return hip_status(pkv::launch_run(r.args, r.blocks, r.ent, r.num_blocks, desc.head_dim,
+                                      r.group, stream));
+}
+
+// pkv_decode and pkv_append_decode: every host check of both halves first,
+// then the plan and the run.
+int plan_and_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *k_new,
+                 const void *v_new, const void *q, int32_t num_qo_heads,
+                 const int32_t *page_indptr, const int32_t *page_indices,
+                 const int32_t *last_page_len, int32_t batch, float sm_scale, void *out,
+                 float *lse, int32_t max_pages_per_req, int32_t kv_chunk_pages,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_decode_args(desc, layer, num_qo_heads, batch, sm_scale, max_pages_per_req,
+                               kv_chunk_pages);
+    if (rc != PKV_OK || batch == 0)
+        return rc;
+    if (!page_indptr || !page_indices || !last_page_len)
+        return PKV_ERR_NULL_PTR;
+    RunLaunch r;
+    rc = prepare_run(kv_cache, desc, layer, k_new, v_new, q, num_qo_heads, batch, sm_scale,
+                     out, lse, max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes,
+                     r);
+    if (rc != PKV_OK)
+        return rc;
+    pkv::PlanArgs pa;
+    rc = prepare_plan(desc, num_qo_heads, page_indptr, page_indices, last_page_len, batch,
+                      max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes, pa);
+    if (rc != PKV_OK)
+        return rc;
+    rc = hip_status(pkv::launch_plan(pa, stream));
+    if (rc != PKV_OK)
+        return rc;
+    return launch_run(r, desc, stream);
 }
 
 }  // namespace
@@ -225,8 +327,42 @@ size_t pkv_decode_workspace_size(pkv_cache_desc_t desc, int32_t num_qo_heads, in
     if (check_desc(desc) != PKV_OK || batch <= 0 || num_qo_heads <= 0 ||
         max_pages_per_req <= 0 || kv_chunk_pages < 0)
         return 0;
-    return (size_t)make_plan(desc, num_qo_heads, batch, max_pages_per_req, kv_chunk_pages)
+    return (size_t)make_layout(desc, num_qo_heads, batch, max_pages_per_req, kv_chunk_pages)
         .ws_bytes;
+}
+
+int pkv_plan(pkv_cache_desc_t desc, int32_t num_qo_heads, const int32_t *page_indptr,
+             const int32_t *page_indices, const int32_t *last_page_len, int32_t batch,
+             int32_t max_pages_per_req, int32_t kv_chunk_pages, void *workspace,
+             size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_decode_args(desc, 0, num_qo_heads, batch, 1.f, max_pages_per_req,
+                               kv_chunk_pages);
+    if (rc != PKV_OK || batch == 0)
+        return rc;
+    pkv::PlanArgs a;
+    rc = prepare_plan(desc, num_qo_heads, page_indptr, page_indices, last_page_len, batch,
+                      max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes, a);
+    if (rc != PKV_OK)
+        return rc;
+    return hip_status(pkv::launch_plan(a, stream));
+}
+
+int pkv_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *k_new,
+            const void *v_new, const void *q, int32_t num_qo_heads, int32_t batch,
+            float sm_scale, void *out, float *lse, int32_t max_pages_per_req,
+            int32_t kv_chunk_pages, void *workspace, size_t workspace_bytes,
+            hipStream_t stream) {
+    int rc = check_decode_args(desc, layer, num_qo_heads, batch, sm_scale, max_pages_per_req,
+                               kv_chunk_pages);
+    if (rc != PKV_OK || batch == 0)
+        return rc;
+    RunLaunch r;
+    rc = prepare_run(kv_cache, desc, layer, k_new, v_new, q, num_qo_heads, batch, sm_scale,
+                     out, lse, max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes,
+                     r);
+    if (rc != PKV_OK)
+        return rc;
+    return launch_run(r, desc, stream);
 }
 
 int pkv_decode(const void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *q,
@@ -234,10 +370,10 @@ int pkv_decode(const void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const
                const int32_t *last_page_len, int32_t batch, float sm_scale, void *out,
                float *lse, int32_t max_pages_per_req, int32_t kv_chunk_pages, void *workspace,
                size_t workspace_bytes, hipStream_t stream) {
-    return decode_common(kv_cache, desc, layer, nullptr, nullptr, q, num_qo_heads,
-                         page_indptr, page_indices, last_page_len, batch, sm_scale, out, lse,
-                         max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes,
-                         stream);
+    return plan_and_run(const_cast<void *>(kv_cache), desc, layer, nullptr, nullptr, q,
+                        num_qo_heads, page_indptr, page_indices, last_page_len, batch,
+                        sm_scale, out, lse, max_pages_per_req, kv_chunk_pages, workspace,
+                        workspace_bytes, stream);
 }
 
 int pkv_append_decode(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *k_new,
@@ -248,14 +384,13 @@ int pkv_append_decode(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, cons
                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
     const int rc = check_decode_args(desc, layer, num_qo_heads, batch, sm_scale,
                                      max_pages_per_req, kv_chunk_pages);
-    if (rc != PKV_OK)
+    if (rc != PKV_OK || batch == 0)
         return rc;
-    if (batch > 0 && (k_new == nullptr || v_new == nullptr))
+    if (k_new == nullptr || v_new == nullptr)
         return PKV_ERR_NULL_PTR;
-    return decode_common(kv_cache, desc, layer, k_new, v_new, q, num_qo_heads, page_indptr,
-                         page_indices, last_page_len, batch, sm_scale, out, lse,
-                         max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes,
-                         stream);
+    return plan_and_run(kv_cache, desc, layer, k_new, v_new, q, num_qo_heads, page_indptr,
+                        page_indices, last_page_len, batch, sm_scale, out, lse,
+                        max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes, stream);
 }
 
 int pkv_validate_page_table(const int32_t *page_indptr, const int32_t *page_indices,

@@ -10,38 +10,39 @@
 //    per byte for a GQA group of g query heads), so it uses the vector ALUs,
 //    not MFMA.  q.k runs on v_dot2_f32_bf16 straight from the bf16 words: no
 //    conversion of K, exact products, fp32 accumulation.
-//  * A workgroup has one wavefront per KV head.  In a wave, eight lanes cover
-//    one token row of its head (D/8 contiguous elements each) and the eight
-//    8-lane row groups cover 8 consecutive tokens: an 8-token "tile".  One
-//    16-byte load per lane reads 8 rows x 128 bytes, and the workgroup as a
-//    whole reads each tile's K rows and V rows of all heads, 16 KiB apiece
-//    for 8 heads of 128, as contiguous runs.
-//  * Partial dot products of a row are summed with three DPP steps
-//    (quad_perm, quad_perm, row_half_mirror): no LDS traffic.
-//  * Each row group keeps its own online-softmax state in the exp2 domain.
-//    The running maximum is raised only when a new score passes it by more
-//    than kTau (log2 units); between raises nothing is rescaled and exp2
-//    arguments stay <= kTau.  Row groups are merged once per segment.
-//  * Loads run two tiles ahead in registers (three rotating buffers), from
-//    an LDS table of the tiles' page ids built once per piece of work; see
-//    decode_kernel.
+//  * A workgroup has one wavefront per KV head.  Every lane owns 16 bytes
+//    (8 elements) of a token row: D/8 lanes cover one row of one head and the
+//    wave covers 64/(D/8) rows per load, so an 8-token tile is one or two
+//    16-byte loads per lane for K and as many for V, and the workgroup reads
+//    each tile's K rows and V rows of all heads as contiguous runs.
+//  * Partial dot products of a row are summed with DPP row operations (no
+//    LDS); the row groups of a wave keep separate online-softmax states in the
+//    exp2 domain and are merged only at the end of a segment, with the gfx950
+//    cross-row lane swaps (v_permlane16_swap, v_permlane32_swap).
+//  * The running maximum is raised only when a score passes it by more than
+//    kTau (log2 units); between raises nothing is rescaled.
+//  * Loads run two tiles ahead in registers (three rotating buffers); the
+//    tiles' page ids come from the step's plan through the scalar cache, one
+//    record ahead of the loads, so no load ever waits on the page table.
 //
-// Work split.  Balanced mode (default): the tiles of all entries are laid end
-// to end and each of W workgroups takes an equal run of them (W = what the
-// chip holds at once), so every compute unit streams the same number of
-// bytes.  A run may cover several entries and an entry may span several runs;
-// each (run, entry) segment writes either the final row (entry entirely in
-// the run) or a partial (output, lse) into slot run + entry, and the merge
-// kernel combines an entry's partials by log-sum-exp.  The split then depends
-// on the whole batch.  Fixed mode (chunk_tiles > 0): each entry is cut into
+// Work split.  The plan kernel walks the page table once per step (the table
+// is the same for every layer) and writes, per decode workgroup, the records
+// of its tiles.  Balanced mode (default): the tiles of all entries are laid
+// end to end and each of W workgroups (W = what the chip holds at once)
+// takes an equal run of them, so every compute unit streams the same number
+// of bytes; runs of neighbouring workgroup ids sit on different XCDs, so the
+// plan deals consecutive runs to one XCD.  Fixed mode: each entry is cut into
 // chunks of a fixed number of tiles, one workgroup each, so how an entry is
 // split depends only on its own length and its rows are bit-identical in any
-// batch.
+// batch.  An entry covered by several workgroups gets one partial (output,
+// lse) per segment; the wave that finishes last merges them by log-sum-exp
+// (an agent-scope counter per entry and head decides which), so no second
+// launch is needed.
 //
 // The fused append (k_new != null) treats the tile holding token L-1 of each
 // entry specially: that row is read from k_new/v_new and written into the
-// cache by the one workgroup that processes it, which is append followed by
-// decode without a second pass over memory.
+// cache by the one wave that processes it, which is append followed by decode
+// without a second pass over memory.
 //
 // All cache offsets are 64-bit.  Page ids outside [0, num_pages) are read as
 // scratch page 0, and an append with an out-of-range page or slot writes
@@ -59,7 +60,9 @@ namespace {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309f;
-constexpr float kTau = 8.0f;   // lazy-rescale threshold, log2 units
+constexpr float kTau = 8.0f;        // lazy-rescale threshold, log2 units
+constexpr float kMInit = -1.0e30f;  // running maximum before any score: finite, so
+                                    // exp2(-inf - kMInit) is 0, never NaN
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -84,43 +87,96 @@ __device__ __forceinline__ float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
-// Sum over the 8 lanes of an aligned row group; every lane gets the total.
-__device__ __forceinline__ float sum_row8(float x) {
+// Sum over the LPR (8 or 16) lanes of an aligned row; every lane gets the total.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
     x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
     x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
     x += dpp<0x141>(x);   // row_half_mirror: lane i <-> 7 - i within 8
+    if constexpr (LPR == 16)
+        x += dpp<0x140>(x);   // row_mirror: lane i <-> 15 - i within 16
     return x;
 }
 
-// Reductions across the 8 row groups of a wave (lanes with equal lane % 8).
-__device__ __forceinline__ float max_across_rows(float x) {
-    x = fmaxf(x, dpp<0x128>(x));        // row_ror:8 within 16 lanes = lane ^ 8
-    x = fmaxf(x, __shfl_xor(x, 16, 64));
-    x = fmaxf(x, __shfl_xor(x, 32, 64));
-    return x;
+// Both halves of a cross-row lane swap of x with itself.
+__device__ __forceinline__ void swap16(float x, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float sum_across_rows(float x) {
-    x += dpp<0x128>(x);
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
-    return x;
+__device__ __forceinline__ void swap32(float x, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
+// Max / sum over the RG row groups of a wave (lanes with equal lane % (64/RG));
+// every lane gets the result.
+template <int RG>
+__device__ __forceinline__ float group_max(float x) {
+    float a, b;
+    if constexpr (RG == 8)
+        x = fmaxf(x, dpp<0x128>(x));   // row_ror:8 = lane ^ 8 within 16
+    swap16(x, a, b);
+    x = fmaxf(a, b);
+    swap32(x, a, b);
+    return fmaxf(a, b);
+}
+template <int RG>
+__device__ __forceinline__ float group_sum(float x) {
+    float a, b;
+    if constexpr (RG == 8)
+        x += dpp<0x128>(x);
+    swap16(x, a, b);
+    x = a + b;
+    swap32(x, a, b);
+    return a + b;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
+// Partial rows cross workgroups (and XCDs, whose L2s are not coherent with
+// each other).  They are written and read through a buffer resource with the
+// device-scope cache policy (sc1): stores write through to the coherent
+// level and loads read from it, 16 bytes at a time, so no L2-wide writeback
+// or invalidate is needed around the arrival counter.  The resource's range
+// also bounds every access to the partial arrays.
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+constexpr int kPolicyDevice = 16;   // sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const float *base,
+                                                               int64_t bytes) {
+    const int range = bytes < 0x7fffffff ? (int)bytes : 0x7fffffff;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, range,
+                                             0x00020000);
+}
+__device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                float a, float b, float c, float d) {
+    const v4i_t v = {__float_as_int(a), __float_as_int(b), __float_as_int(c),
+                     __float_as_int(d)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kPolicyDevice);
+}
+__device__ __forceinline__ void store1_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                float a) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(a), r, (int)off, 0, kPolicyDevice);
+}
+__device__ __forceinline__ float4 load4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const v4i_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kPolicyDevice);
+    return make_float4(__int_as_float(v.x), __int_as_float(v.y), __int_as_float(v.z),
+                       __int_as_float(v.w));
+}
+__device__ __forceinline__ float load1_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kPolicyDevice));
+}
+
 __device__ __forceinline__ uint4 load16(const uint16_t *p) {
     return *reinterpret_cast<const uint4 *>(p);
 }
-
-// Tiles (8 tokens) of entry b; 0 for a malformed entry with no page.
-__device__ __forceinline__ int entry_tiles(const DecodeArgs &a, int b) {
-    const int n = a.indptr[b + 1] - a.indptr[b];
-    if (n < 1)
-        return 0;
-    int last = a.last_len[b];
-    last = last < 1 ? 1 : (last > a.page_size ? a.page_size : last);
-    return ((n - 1) * a.page_size + last + kTileTokens - 1) / kTileTokens;
+__device__ __forceinline__ void store16(uint16_t *p, uint4 v) {
+    *reinterpret_cast<uint4 *>(p) = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -146,6 +202,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         reinterpret_cast<uint4 *>(dst + (is_v ? a.half_stride : 0))[w] = val;
     }
 }
+
+// ---------------------------------------------------------------------------
+// Plan.
 
 // Exclusive scan of one int per thread over the workgroup (<= 16 waves).
 __device__ int block_exclusive_scan(int v, int *s_wave, int &total) {
@@ -181,54 +240,32 @@ __device__ int block_exclusive_scan(int v, int *s_wave, int &total) {
     return s_wave[wave] + x - v;
 }
 
-// ---------------------------------------------------------------------------
-// Decode pass.
-//
-// A workgroup owns a run [g0, g1) of 8-token tiles in its entries' tiles laid
-// end to end, and has one wave per KV head (blockIdx.y picks the group of up to
-// kMaxWavesPerGroup heads).  Balanced mode (chunk_tiles == 0): W workgroups
-// take equal runs of all T tiles of the batch.  Fixed mode: a workgroup takes
-// run c of chunk_tiles tiles of one entry b alone.  Either way the entries
-// are described in LDS (tile prefix sums, first page-table slot, tokens), so
-// both modes run the same loop.
-//
-// The run is processed in pieces of at most kPiece tiles.  All threads first
-// resolve every tile's page id into an LDS table, with an info word per tile
-// (valid tokens, slot in the page, where entries start and end); then each
-// wave streams the piece through three rotating one-tile register buffers
-// (two tiles in flight while one is computed), switching entries where the
-// info word says so.  Loads never wait on the page table, and the q rows of
-// the piece's first entries are staged in LDS with the tables, so entry
-// switches cost no memory round trip.  Every load is issued unconditionally
-// (a tile past the piece reloads its last tile, a cache hit, and is never
-// computed), so at each compute the same two tiles are outstanding on every
-// path and the compiler's waits keep them in flight.
-constexpr int kPiece = 256;
-constexpr int kInfoNtok = 0xF;            // bits 0-3: valid tokens (1..8)
-constexpr int kInfoSlotShift = 4;         // bits 4-8: slot of the tile's first token / 8
-constexpr int kInfoSegFirst = 1 << 9;     // first tile of an entry within the run
-constexpr int kInfoSegLast = 1 << 10;     // last tile of an entry within the run
-constexpr int kInfoEntryLast = 1 << 11;   // the tile holding the entry's token L-1
-constexpr int kInfoNewRowShift = 12;      // bits 12-14: token L-1 within that tile
-constexpr int kInfoEntryShift = 16;       // bits 16-31: entry - first entry of piece
+struct EntryShape {
+    int p0;     // first page-table slot
+    int n;      // pages listed
+    int last;   // rows in the last page, clamped to [1, page_size]
+    int tiles;  // tiles the decode covers (0: none, or over the page bound)
+};
 
-// Tiles of entry b; also its first page-table slot and token count.
-__device__ __forceinline__ int entry_desc(const DecodeArgs &a, int b, int &p0, int &len) {
-    p0 = a.indptr[b];
-    const int n = a.indptr[b + 1] - p0;
+__device__ __forceinline__ EntryShape entry_shape(const PlanArgs &a, int b) {
+    EntryShape e;
+    e.p0 = a.indptr[b];
+    e.n = a.indptr[b + 1] - e.p0;
     int last = a.last_len[b];
-    last = last < 1 ? 1 : (last > a.page_size ? a.page_size : last);
-    len = n < 1 ? 0 : (n - 1) * a.page_size + last;
-    return (len + kTileTokens - 1) / kTileTokens;
+    e.last = last < 1 ? 1 : (last > a.page_size ? a.page_size : last);
+    e.tiles = (e.n < 1 || e.n > a.max_pages)
+                  ? 0
+                  : (e.n - 1) * a.tiles_per_page + (e.last + kTileTokens - 1) / kTileTokens;
+    return e;
 }
 
-// Ints of padding after the entry descriptors so the staged q rows, which
-// follow the tile tables, start 16-byte aligned (the tables hold a multiple of
-// 4 ints).
-__host__ __device__ __forceinline__ int q_pad(int nb) { return (3 - (3 * nb) % 4) % 4; }
+__device__ __forceinline__ int valid_page(const PlanArgs &a, int page) {
+    return (page >= 0 && page < a.num_pages) ? page : 0;
+}
 
-// The largest e in [lo, hi] with start[e] <= t (start non-decreasing).
-__device__ __forceinline__ int entry_of(const int *start, int lo, int hi, int t) {
+// The largest e in [0, hi] with start[e] <= t (start non-decreasing).
+__device__ __forceinline__ int entry_of(const int *start, int hi, int64_t t) {
+    int lo = 0;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (start[mid] <= t)
@@ -239,83 +276,38 @@ __device__ __forceinline__ int entry_of(const int *start, int lo, int hi, int t)
     return lo;
 }
 
-template <int D, int G, bool SMALL_PAGE>
-__global__ __launch_bounds__(kMaxWavesPerGroup * 64) void decode_kernel(DecodeArgs a) {
-    constexpr int NLD = D / 64;                      // 16-byte words per lane per row
-    constexpr int PPT = SMALL_PAGE ? kTileTokens : 1;   // page ids per tile
-    extern __shared__ uint4 smem_words[];
-    int *smem = reinterpret_cast<int *>(smem_words);
-    __shared__ int s_wave[17];
-    const int lane = threadIdx.x & 63;
-    const int rg = lane >> 3;     // token within a tile
-    const int j = lane & 7;       // element slice [8j, 8j+8) (+64 for D = 128)
-    const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * (blockDim.x >> 6) +
-                                                 (threadIdx.x >> 6));
-    // Waves past the last head (when Hkv is not a multiple of the group size)
-    // do no attention work but still take every barrier.
-    const bool has_head = h < a.num_kv_heads;
-    const bool fixed = a.chunk_tiles > 0;
-    const bool fused = a.k_new != nullptr;
-    const int nb = fixed ? 1 : a.batch;
-    int *s_start = smem;              // [nb + 1] tile prefix sums
-    int *s_p0 = s_start + nb + 1;     // [nb] first page-table slot
-    int *s_len = s_p0 + nb;           // [nb] tokens
-    int *s_page = s_len + nb;         // [kPiece * PPT] page ids of the piece's tiles
-    int *s_info = s_page + kPiece * PPT;   // [kPiece] info words
-    // q rows of the piece's first q_slots entries, [q_slots][Hq][D] bf16
-    uint16_t *s_q = reinterpret_cast<uint16_t *>(s_info + kPiece + q_pad(nb));
+// Balanced mode: run index of workgroup id w.  Workgroups are dealt to the 8
+// XCDs round-robin, so ids w, w + 8, ... share an XCD; giving them
+// consecutive runs keeps an entry's pieces (and its q rows and partials)
+// within one XCD's L2 as far as possible.
+__device__ __forceinline__ int run_of_block(int w, int W) {
+    return (W % 8 == 0) ? (w % 8) * (W / 8) + w / 8 : w;
+}
 
-    int g0, g1, fixed_b = 0, fixed_c = 0;
-    if (fixed) {
-        // Chunk-major order over rows of batch8 = batch rounded up to 8
-        // workgroups, entries rotated by the chunk number.  Workgroups are
-        // dealt to the 8 XCDs round-robin, so chunk c of entry b lands on XCD
-        // (b - c) mod 8: consecutive chunks of an entry, and the first chunks
-        // of all entries, spread over every XCD.  Ids past the batch are empty.
-        const int batch8 = (a.batch + 7) & ~7;
-        fixed_c = blockIdx.x / batch8;
-        const int bp = blockIdx.x - fixed_c * batch8;
-        fixed_b = (bp + fixed_c) % batch8;
-        if (fixed_b >= a.batch)
-            return;
-        int p0, len;
-        const int nt = entry_desc(a, fixed_b, p0, len);
-        const int nchunks = (nt + a.chunk_tiles - 1) / a.chunk_tiles;
-        if (nchunks > a.max_chunks) {
-            // Longer than the launch allows: poison the rows so the broken
-            // precondition shows instead of silently truncating.
-            if (fixed_c == 0 && has_head) {
-                for (int i = lane; i < G * D; i += 64)
-                    a.out[((int64_t)fixed_b * a.num_qo_heads + h * G) * D + i] = 0x7FC0;
-                if (a.lse != nullptr && lane < G)
-                    a.lse[(int64_t)fixed_b * a.num_qo_heads + h * G + lane] = __builtin_nanf("");
-            }
-            return;
-        }
-        if (fixed_c >= nchunks)
-            return;
-        if (threadIdx.x == 0) {
-            s_start[0] = 0;
-            s_start[1] = nt;
-            s_p0[0] = p0;
-            s_len[0] = len;
-        }
-        g0 = fixed_c * a.chunk_tiles;
-        g1 = min(nt, g0 + a.chunk_tiles);
-        __syncthreads();
-    } else {
-        // Balanced: per-entry tiles, first slot and tokens, then prefix sums.
+// Number of runs among W_eff equal runs of T tiles that tile range [s, s + t)
+// touches, and the first of them (run r covers [T r / W_eff, T (r+1) / W_eff)).
+__device__ __forceinline__ void runs_of(int64_t s, int64_t t, int64_t T, int64_t weff,
+                                       int &first, int &count) {
+    const int lo = (int)(((s + 1) * weff - 1) / T);
+    const int hi = (int)(((s + t) * weff - 1) / T);
+    first = lo;
+    count = hi - lo + 1;
+}
+
+__global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
+    extern __shared__ int s_start[];   // balanced: [batch + 1] tile prefix sums
+    __shared__ int s_wave[17];
+    const bool fixed = a.chunk_tiles > 0;
+    int64_t T = 0;
+    if (!fixed) {
         const int nthreads = blockDim.x;
         const int per = (a.batch + nthreads - 1) / nthreads;
         const int e0 = min(a.batch, (int)threadIdx.x * per);
         const int e1 = min(a.batch, e0 + per);
         int local = 0;
         for (int e = e0; e < e1; ++e) {
-            int p0, len;
-            const int t = entry_desc(a, e, p0, len);
+            const int t = entry_shape(a, e).tiles;
             s_start[e] = t;
-            s_p0[e] = p0;
-            s_len[e] = len;
             local += t;
         }
         int total = 0;
@@ -328,593 +320,628 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void decode_kernel(DecodeAr
         if (threadIdx.x == 0)
             s_start[a.batch] = total;
         __syncthreads();
-        if (blockIdx.x == 0 && blockIdx.y == 0)
-            for (int e = threadIdx.x; e <= a.batch; e += nthreads)
-                a.tile_start[e] = s_start[e];
-        // W <= T workgroups take part, so each holds at least one tile (the
-        // merge recomputes the same W from T)
-        const int64_t T = total;
-        const int W = (int)(T < a.num_groups ? T : a.num_groups);
-        if ((int)blockIdx.x >= W)
-            return;
-        g0 = (int)(T * blockIdx.x / W);
-        g1 = (int)(T * (blockIdx.x + 1) / W);
+        T = total;
+    }
+    const int W = a.num_blocks;
+    const int64_t weff = fixed ? W : (T < W ? T : W);
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    int4 *blocks = reinterpret_cast<int4 *>(a.blocks);
+    int4 *ent = reinterpret_cast<int4 *>(a.ent);
+
+    for (int64_t i = tid; i < (int64_t)a.batch * a.num_kv_heads; i += nth)
+        a.cnt[i] = 0;
+
+    for (int64_t bb = tid; bb < a.batch; bb += nth) {
+        const int b = (int)bb;
+        const EntryShape e = entry_shape(a, b);
+        int4 d = make_int4(0, 0, 0, 0);
+        if (e.n > a.max_pages) {
+            // over the bound: no tiles; the decode writes NaN rows and, when
+            // fused, still appends the new row to its slot
+            d = make_int4(0, -1, valid_page(a, a.indices[e.p0 + e.n - 1]), e.last - 1);
+        } else if (e.tiles > 0) {
+            if (fixed) {
+                d.x = b * a.max_chunks;
+                d.y = (e.tiles + a.chunk_tiles - 1) / a.chunk_tiles;
+            } else {
+                int first, count;
+                runs_of(s_start[b], e.tiles, T, weff, first, count);
+                d.x = first + b;
+                d.y = count;
+            }
+        }
+        ent[b] = d;
     }
 
-    // ---- per-wave state, carried across pieces
-    uint32_t qv[G][NLD][4];   // q of the entry being computed
-    float m[G], l[G], acc[G][NLD][8];
-    const int row_elems_q = a.num_qo_heads * D;
-
-    for (int k0 = g0, k1; k0 < g1; k0 = k1) {
-        // A piece: at most kPiece tiles of at most q_slots entries (so every
-        // entry's q rows are staged).  Entry e_first holds tile k0, so
-        // s_start[e_first + 1] > k0 and the piece is never empty.
-        const int e_first = __builtin_amdgcn_readfirstlane(entry_of(s_start, 0, nb - 1, k0));
-        k1 = min(g1, k0 + kPiece);
-        if (e_first + a.q_slots < nb)
-            k1 = min(k1, s_start[e_first + a.q_slots]);
-        k1 = __builtin_amdgcn_readfirstlane(k1);
-        const int nk = k1 - k0;
-        __syncthreads();   // the previous piece's tables are no longer read
-        for (int t = threadIdx.x; t < nk * PPT; t += blockDim.x) {
-            const int kk = t / PPT;
-            const int r = t % PPT;
-            const int k = k0 + kk;
-            const int e = entry_of(s_start, e_first, nb - 1, k);
-            const int lt = k - s_start[e];
-            const int tok0 = lt * kTileTokens;
-            const int len = s_len[e];
-            const int tok = tok0 + r;
-            const int page_local = tok >> a.log2_page;
-            int page = (tok < len) ? a.indices[s_p0[e] + page_local] : 0;
-            page = (page >= 0 && page < a.num_pages) ? page : 0;
-            s_page[t] = page;
-            if (r == 0) {
-                const int ntok = min(kTileTokens, len - tok0);
-                const int slot8 = SMALL_PAGE ? 0 : ((tok0 & (a.page_size - 1)) >> 3);
-                int info = ntok | (slot8 << kInfoSlotShift) |
-                           (((len - 1) & (kTileTokens - 1)) << kInfoNewRowShift) |
-                           ((e - e_first) << kInfoEntryShift);
-                if (k == max(g0, s_start[e]))
-                    info |= kInfoSegFirst;
-                if (k == min(g1, s_start[e + 1]) - 1)
-                    info |= kInfoSegLast;
-                if (lt == (len - 1) / kTileTokens)
-                    info |= kInfoEntryLast;
-                s_info[kk] = info;
+    const int64_t items = (int64_t)W * a.block_stride;
+    for (int64_t i = tid; i < items; i += nth) {
+        const int w = (int)(i / a.block_stride);
+        const int jj = (int)(i - (int64_t)w * a.block_stride);
+        int b = 0, run = 0, ntiles = 0, lt0 = 0, nseg = 1, slot = 0;
+        int64_t g0 = 0, g1 = 0, s0 = 0;
+        EntryShape e{};
+        if (fixed) {
+            // chunk-major ids over rows of batch8 = batch rounded up to 8,
+            // entries rotated by the chunk number: chunk c of entry b runs on
+            // XCD (b - c) mod 8, so an entry's chunks spread over every XCD
+            const int batch8 = (a.batch + 7) & ~7;
+            const int c = w / batch8;
+            b = (w - c * batch8 + c) % batch8;
+            run = c;
+            if (b < a.batch) {
+                e = entry_shape(a, b);
+                lt0 = c * a.chunk_tiles;
+                ntiles = e.tiles > lt0 ? min(a.chunk_tiles, e.tiles - lt0) : 0;
+                nseg = (e.tiles + a.chunk_tiles - 1) / a.chunk_tiles;
+                slot = b * a.max_chunks + c;
+            }
+        } else {
+            run = run_of_block(w, W);
+            if (run < weff) {
+                g0 = T * run / weff;
+                g1 = T * (run + 1) / weff;
+                ntiles = (int)(g1 - g0);
             }
         }
-        {
-            // q rows of the piece's entries, 16 bytes a thread
-            const int e_last = entry_of(s_start, e_first, nb - 1, k1 - 1);
-            const int nq = e_last - e_first + 1;   // <= q_slots
-            const int words = row_elems_q >> 3;
-            for (int t = threadIdx.x; t < nq * words; t += blockDim.x) {
-                const int qe = t / words;
-                const int w = t - qe * words;
-                const int b = fixed ? fixed_b : e_first + qe;
-                reinterpret_cast<uint4 *>(s_q + (int64_t)qe * row_elems_q)[w] =
-                    reinterpret_cast<const uint4 *>(a.q + (int64_t)b * row_elems_q)[w];
-            }
-        }
-        __syncthreads();
-        if (!has_head)
+        if (jj == 0) {
+            blocks[i] = make_int4(ntiles, run, 0, 0);
             continue;
-
-        struct Tile {
-            uint4 k[NLD];
-            uint4 v[NLD];
-        };
-        const uint16_t *head_base = a.cache + h * D + j * 8;
-
-        auto load_tile = [&](Tile &x, int kk) {
-            kk = min(kk, nk - 1);
-            const int info = __builtin_amdgcn_readfirstlane(s_info[kk]);
-            const uint16_t *row;
-            if (SMALL_PAGE) {
-                const int page = s_page[kk * PPT + rg];
-                row = head_base + (int64_t)page * a.page_stride +
-                      (uint32_t)((rg & (a.page_size - 1)) * a.row_stride);
-            } else {
-                const int page = __builtin_amdgcn_readfirstlane(s_page[kk]);
-                const int sl = ((info >> kInfoSlotShift) & 31) * kTileTokens + rg;
-                row = head_base + (int64_t)page * a.page_stride + (uint32_t)(sl * a.row_stride);
-            }
-            // One load sequence on every path (only the addresses differ), so
-            // the compiler's waits keep two tiles in flight.
-            const uint16_t *kr = row;
-            const uint16_t *vr = row + a.half_stride;
-            if (fused && (info & kInfoEntryLast) && rg == ((info >> kInfoNewRowShift) & 7)) {
-                // the entry's new row comes from k_new / v_new
-                const int b = fixed ? fixed_b : e_first + (info >> kInfoEntryShift);
-                const int64_t nr = ((int64_t)b * a.num_kv_heads + h) * D + j * 8;
-                kr = a.k_new + nr;
-                vr = a.v_new + nr;
-            }
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                x.k[i] = load16(kr + i * 64);
-                x.v[i] = load16(vr + i * 64);
-            }
-        };
-
-        auto begin_entry = [&](int e) {
-            // q of the G query heads of KV head h, staged in LDS
-            const uint16_t *qb = s_q + (e - e_first) * row_elems_q + h * G * D + j * 8;
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int i = 0; i < NLD; ++i) {
-                    const uint4 w = *reinterpret_cast<const uint4 *>(qb + g * D + i * 64);
-                    qv[g][i][0] = w.x;
-                    qv[g][i][1] = w.y;
-                    qv[g][i][2] = w.z;
-                    qv[g][i][3] = w.w;
-                }
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                m[g] = -INFINITY;
-                l[g] = 0.f;
-#pragma unroll
-                for (int i = 0; i < NLD; ++i)
-#pragma unroll
-                    for (int e8 = 0; e8 < 8; ++e8)
-                        acc[g][i][e8] = 0.f;
-            }
-        };
-
-        auto finish_entry = [&](int e, int info, int kk) {
-            const int b = fixed ? fixed_b : e;
-            if (fused && (info & kInfoEntryLast) && rg == ((info >> kInfoNewRowShift) & 7)) {
-                // append: copy the new row of head h into the cache slot
-                int page, sl;
-                if (SMALL_PAGE) {
-                    page = s_page[kk * PPT + rg];
-                    sl = rg & (a.page_size - 1);
-                } else {
-                    page = s_page[kk];
-                    sl = ((info >> kInfoSlotShift) & 31) * kTileTokens + rg;
-                }
-                const int64_t nr = ((int64_t)b * a.num_kv_heads + h) * D + j * 8;
-                uint16_t *dst = a.cache_w + h * D + j * 8 + (int64_t)page * a.page_stride +
-                                (int64_t)sl * a.row_stride;
-#pragma unroll
-                for (int i = 0; i < NLD; ++i) {
-                    *reinterpret_cast<uint4 *>(dst + i * 64) = load16(a.k_new + nr + i * 64);
-                    *reinterpret_cast<uint4 *>(dst + a.half_stride + i * 64) =
-                        load16(a.v_new + nr + i * 64);
-                }
-            }
-            // merge the 8 row groups; every lane ends with the totals
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float mw = max_across_rows(m[g]);
-                const float f = (m[g] == -INFINITY) ? 0.f : exp2_fast(m[g] - mw);
-                l[g] = sum_across_rows(l[g] * f);
-#pragma unroll
-                for (int i = 0; i < NLD; ++i)
-#pragma unroll
-                    for (int e8 = 0; e8 < 8; ++e8)
-                        acc[g][i][e8] = sum_across_rows(acc[g][i][e8] * f);
-                m[g] = mw;
-            }
-            const bool whole = s_start[e] >= g0 && s_start[e + 1] <= g1;
-            const int slot = fixed ? fixed_b * a.max_chunks + fixed_c : (int)blockIdx.x + e;
-            // row group g writes query head h * G + g
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                if (rg != g)
-                    continue;
-                const int hq = h * G + g;
-                const float inv = 1.f / l[g];
-                if (whole) {
-                    uint16_t *o = a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8;
-#pragma unroll
-                    for (int i = 0; i < NLD; ++i) {
-                        uint4 w;
-                        w.x = pack_bf16x2(acc[g][i][0] * inv, acc[g][i][1] * inv);
-                        w.y = pack_bf16x2(acc[g][i][2] * inv, acc[g][i][3] * inv);
-                        w.z = pack_bf16x2(acc[g][i][4] * inv, acc[g][i][5] * inv);
-                        w.w = pack_bf16x2(acc[g][i][6] * inv, acc[g][i][7] * inv);
-                        *reinterpret_cast<uint4 *>(o + i * 64) = w;
-                    }
-                    if (a.lse != nullptr && j == 0)
-                        a.lse[(int64_t)b * a.num_qo_heads + hq] =
-                            (m[g] + log2_fast(l[g])) * kLn2;
-                } else {
-                    const int64_t prow = (int64_t)slot * a.num_qo_heads + hq;
-                    float *o = a.part_o + prow * D + j * 8;
-#pragma unroll
-                    for (int i = 0; i < NLD; ++i) {
-                        *reinterpret_cast<float4 *>(o + i * 64) =
-                            make_float4(acc[g][i][0] * inv, acc[g][i][1] * inv,
-                                        acc[g][i][2] * inv, acc[g][i][3] * inv);
-                        *reinterpret_cast<float4 *>(o + i * 64 + 4) =
-                            make_float4(acc[g][i][4] * inv, acc[g][i][5] * inv,
-                                        acc[g][i][6] * inv, acc[g][i][7] * inv);
-                    }
-                    if (j == 0)
-                        a.part_lse[prow] = m[g] + log2_fast(l[g]);
-                }
-            }
-        };
-
-        auto compute_tile = [&](const Tile &x, int kk) {
-            const int info = __builtin_amdgcn_readfirstlane(s_info[kk]);
-            const int e = e_first + (info >> kInfoEntryShift);
-            if (info & kInfoSegFirst)
-                begin_entry(e);
-            const int ntok = info & kInfoNtok;
-            const bool edge = ntok < kTileTokens;
-            const bool ok = rg < ntok;
-            float s[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float d = 0.f;
-#pragma unroll
-                for (int i = 0; i < NLD; ++i) {
-                    d = dot2_bf16(qv[g][i][0], x.k[i].x, d);
-                    d = dot2_bf16(qv[g][i][1], x.k[i].y, d);
-                    d = dot2_bf16(qv[g][i][2], x.k[i].z, d);
-                    d = dot2_bf16(qv[g][i][3], x.k[i].w, d);
-                }
-                s[g] = sum_row8(d) * a.scale_log2;
-                if (edge)
-                    s[g] = ok ? s[g] : -INFINITY;
-            }
-            // Lazy maximum: raise m only when a score passes it by more than kTau.
-            bool raise_any = false;
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-                raise_any |= s[g] > m[g] + kTau;
-            if (raise_any) {
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const bool up = s[g] > m[g] + kTau;
-                    const float mn = up ? s[g] : m[g];
-                    const float alpha = up ? exp2_fast(m[g] - mn) : 1.f;
-                    m[g] = mn;
-                    l[g] *= alpha;
-#pragma unroll
-                    for (int i = 0; i < NLD; ++i)
-#pragma unroll
-                        for (int e8 = 0; e8 < 8; ++e8)
-                            acc[g][i][e8] *= alpha;
-                }
-            }
-            float vf[NLD][8];
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                const uint4 w = x.v[i];
-                vf[i][0] = bf16_lo(w.x);
-                vf[i][1] = bf16_hi(w.x);
-                vf[i][2] = bf16_lo(w.y);
-                vf[i][3] = bf16_hi(w.y);
-                vf[i][4] = bf16_lo(w.z);
-                vf[i][5] = bf16_hi(w.z);
-                vf[i][6] = bf16_lo(w.w);
-                vf[i][7] = bf16_hi(w.w);
-            }
-            if (edge && !ok) {
-                // stale rows past the end may hold anything, NaN included
-#pragma unroll
-                for (int i = 0; i < NLD; ++i)
-#pragma unroll
-                    for (int e8 = 0; e8 < 8; ++e8)
-                        vf[i][e8] = 0.f;
-            }
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float p = exp2_fast(s[g] - m[g]);
-                if (edge)
-                    p = ok ? p : 0.f;   // also covers -inf - -inf
-                l[g] += p;
-#pragma unroll
-                for (int i = 0; i < NLD; ++i)
-#pragma unroll
-                    for (int e8 = 0; e8 < 8; ++e8)
-                        acc[g][i][e8] = fmaf(p, vf[i][e8], acc[g][i][e8]);
-            }
-            if (info & kInfoSegLast)
-                finish_entry(e, info, kk);
-        };
-
-        Tile A, B, C;
-        load_tile(A, 0);
-        load_tile(B, 1);
-        for (int kk = 0;;) {
-            load_tile(C, kk + 2);
-            compute_tile(A, kk);
-            if (++kk >= nk)
-                break;
-            load_tile(A, kk + 2);
-            compute_tile(B, kk);
-            if (++kk >= nk)
-                break;
-            load_tile(B, kk + 2);
-            compute_tile(C, kk);
-            if (++kk >= nk)
-                break;
         }
+        const int k = jj - 1;
+        if (k >= ntiles)
+            continue;   // capacity this block does not use; never read
+        int lt;
+        bool seg_first, seg_last;
+        if (fixed) {
+            lt = lt0 + k;
+            seg_first = k == 0;
+            seg_last = k == ntiles - 1;
+        } else {
+            const int64_t gk = g0 + k;
+            b = entry_of(s_start, a.batch - 1, gk);
+            e = entry_shape(a, b);
+            s0 = s_start[b];
+            lt = (int)(gk - s0);
+            seg_first = gk == (g0 > s0 ? g0 : s0);
+            const int64_t s1 = s0 + e.tiles;
+            seg_last = gk == (g1 < s1 ? g1 : s1) - 1;
+            int first;
+            runs_of(s0, e.tiles, T, weff, first, nseg);
+            slot = run + b;
+        }
+        const int pl = lt / a.tiles_per_page;
+        const int sub = lt - pl * a.tiles_per_page;
+        const int page = valid_page(a, a.indices[e.p0 + pl]);
+        const bool last_page = pl == e.n - 1;
+        const int rows = last_page ? e.last : a.page_size;
+        const int slot0 = sub * kTileTokens;
+        const int ntok = min(kTileTokens, rows - slot0);
+        int info = (ntok - 1) | (slot0 << kInfoSlotShift);
+        if (seg_first)
+            info |= kInfoSegFirst;
+        if (seg_last)
+            info |= kInfoSegLast;
+        if (nseg == 1)
+            info |= kInfoSegWhole;
+        if (last_page && sub == (e.last - 1) / kTileTokens)
+            info |= kInfoHasNew | (((e.last - 1) & (kTileTokens - 1)) << kInfoNewRowShift);
+        blocks[i] = make_int4(page, info, b, slot);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Merge of entries split over several workgroups or chunks: one workgroup per
-// (entry, KV head).  Thread (col, ks) owns float4 column `col` of the G query
-// heads' outputs and the partials k = ks, ks + KS, ...; it merges them online
-// (running maximum, rescaled sum) with the loads of four partials in flight,
-// and the KS per-thread states are then merged through LDS.
+// Decode.
+//
+// Each wave streams its workgroup's tiles for its KV head h through three
+// rotating register buffers: while tile kk is computed, tiles kk+1 and kk+2
+// are in flight, and the record of tile kk+3 is on its way through the
+// scalar cache.  Every load is issued unconditionally (past the last tile the
+// last one is loaded again, a cache hit, and never computed), so the
+// compiler's waits keep exactly two tiles outstanding.
+//
+// Lane layout: lane = rg * LPR + j owns elements [8j, 8j + 8) of rows
+// rg + RG * i (i < RPL) of each tile, for K and for V, and accumulates the G
+// query heads' outputs of those elements over its rows.
 template <int D, int G>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
-    constexpr int COLS = G * D / 4;                    // float4 columns
-    constexpr int KS = COLS >= 256 ? 1 : 256 / COLS;   // ways the partials are split
-    constexpr int U = 4;                               // partials in flight per thread
-    __shared__ float s_m[KS][COLS];
-    __shared__ float s_s[KS][COLS];
-    __shared__ float4 s_o[KS][COLS];
-
-    const int h = blockIdx.x % a.num_kv_heads;
-    const int b = blockIdx.x / a.num_kv_heads;
-    int base, count;
-    if (a.chunk_tiles > 0) {
-        const int nt = entry_tiles(a, b);
-        const int nchunks = (nt + a.chunk_tiles - 1) / a.chunk_tiles;
-        if (nchunks <= 1 || nchunks > a.max_chunks)
-            return;
-        base = b * a.max_chunks;
-        count = nchunks;
-    } else {
-        const int sb = a.tile_start[b];
-        const int se = a.tile_start[b + 1];
-        const int64_t T = a.tile_start[a.batch];
-        if (se <= sb)
-            return;
-        const int64_t W = T < a.num_groups ? T : a.num_groups;
-        // workgroup w covers tiles [floor(T w / W), floor(T (w+1) / W)), and
-        // none of them is empty since W <= T
-        const int w_lo = (int)(((int64_t)(sb + 1) * W - 1) / T);
-        const int w_hi = (int)(((int64_t)se * W - 1) / T);
-        if (w_lo == w_hi)
-            return;
-        base = w_lo + b;
-        count = w_hi - w_lo + 1;
-    }
-    const int col = threadIdx.x % COLS;
-    const int ks = threadIdx.x / COLS;
-    const int g = col / (D / 4);
-    const int e4 = (col % (D / 4)) * 4;
-    const int hq = h * G + g;
-    const int64_t stride_l = a.num_qo_heads;
-    const int64_t stride_o = (int64_t)a.num_qo_heads * D;
-    const float *pl = a.part_lse + (int64_t)base * stride_l + hq;
-    const float *po = a.part_o + (int64_t)base * stride_o + (int64_t)hq * D + e4;
-
-    float m = -INFINITY, sum = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (ks < KS) {
-        for (int k0 = ks; k0 < count; k0 += KS * U) {
-            float lv[U];
-            float4 ov[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int k = min(k0 + u * KS, count - 1);
-                lv[u] = pl[k * stride_l];
-                ov[u] = *reinterpret_cast<const float4 *>(po + k * stride_o);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (k0 + u * KS >= count)
-                    break;
-                const float mn = fmaxf(m, lv[u]);
-                const float al = exp2_fast(m - mn);   // 0 while m is -inf
-                const float w = exp2_fast(lv[u] - mn);
-                sum = sum * al + w;
-                o.x = fmaf(w, ov[u].x, o.x * al);
-                o.y = fmaf(w, ov[u].y, o.y * al);
-                o.z = fmaf(w, ov[u].z, o.z * al);
-                o.w = fmaf(w, ov[u].w, o.w * al);
-                m = mn;
-            }
-        }
-        if (KS > 1) {
-            s_m[ks][col] = m;
-            s_s[ks][col] = sum;
-            s_o[ks][col] = o;
-        }
-    }
-    if (KS > 1) {
-        __syncthreads();
-        if (ks != 0)
-            return;
-        m = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < KS; ++q)
-            m = fmaxf(m, s_m[q][col]);
-        sum = 0.f;
-        o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int q = 0; q < KS; ++q) {
-            const float mq = s_m[q][col];
-            const float f = mq == -INFINITY ? 0.f : exp2_fast(mq - m);
-            const float4 oq = s_o[q][col];
-            sum = fmaf(s_s[q][col], f, sum);
-            o.x = fmaf(oq.x, f, o.x);
-            o.y = fmaf(oq.y, f, o.y);
-            o.z = fmaf(oq.z, f, o.z);
-            o.w = fmaf(oq.w, f, o.w);
-        }
-    }
-    if (col >= COLS)
+__global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
+    RunArgs a, const int4 *__restrict__ blocks, const int4 *__restrict__ ent) {
+    constexpr int LPR = D / 8;                 // lanes per row
+    constexpr int RG = 64 / LPR;               // row groups
+    constexpr int RPL = kTileTokens / RG;      // rows per lane per tile
+    const int lane = threadIdx.x & 63;
+    const int rg = lane / LPR;
+    const int j = lane % LPR;
+    const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * (blockDim.x >> 6) +
+                                                 (threadIdx.x >> 6));
+    if (h >= a.num_kv_heads)
         return;
-    const float inv = 1.f / sum;
-    uint2 packed;
-    packed.x = pack_bf16x2(o.x * inv, o.y * inv);
-    packed.y = pack_bf16x2(o.z * inv, o.w * inv);
-    *reinterpret_cast<uint2 *>(a.out + ((int64_t)b * a.num_qo_heads + hq) * D + e4) = packed;
-    if (a.lse != nullptr && e4 == 0)
-        a.lse[(int64_t)b * a.num_qo_heads + hq] = (m + log2_fast(sum)) * kLn2;
-}
+    const bool fused = a.k_new != nullptr;
+    const int hq0 = h * G;
+    const int col = h * D + j * 8;   // element offset of this lane within a token row
 
-#ifndef PKV_WAVES_PER_CU
-#define PKV_WAVES_PER_CU 0   // 0: as many as the occupancy calculator allows
+    const int4 *blk = blocks + (int64_t)blockIdx.x * a.block_stride;
+    const int n = blk[0].x;
+
+    const __amdgpu_buffer_rsrc_t ro = partial_rsrc(a.part_o, a.part_o_bytes);
+    const __amdgpu_buffer_rsrc_t rl = partial_rsrc(a.part_lse, a.part_lse_bytes);
+    uint32_t qv[G][4];        // q of the entry being computed, 8 bf16 per head
+    float m[G], l[G], acc[G][8];
+    int pend0 = -1, pend1 = -1;   // entries whose partial this wave wrote
+
+    auto load_q = [&](int b) {
+        const uint16_t *qb = a.q + ((int64_t)b * a.num_qo_heads + hq0) * D + j * 8;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const uint4 w = load16(qb + g * D);
+            qv[g][0] = w.x;
+            qv[g][1] = w.y;
+            qv[g][2] = w.z;
+            qv[g][3] = w.w;
+        }
+    };
+
+    // Rows of heads hq0 + g for g = rg, rg + RG, ... are written by row group rg.
+    auto write_rows = [&](int b, int slot, bool whole) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (g % RG != rg)
+                continue;
+            const int hq = hq0 + g;
+            const float inv = 1.f / l[g];
+            if (whole) {
+                uint4 w;
+                w.x = pack_bf16x2(acc[g][0] * inv, acc[g][1] * inv);
+                w.y = pack_bf16x2(acc[g][2] * inv, acc[g][3] * inv);
+                w.z = pack_bf16x2(acc[g][4] * inv, acc[g][5] * inv);
+                w.w = pack_bf16x2(acc[g][6] * inv, acc[g][7] * inv);
+                store16(a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8, w);
+                if (a.lse != nullptr && j == 0)
+                    a.lse[(int64_t)b * a.num_qo_heads + hq] = (m[g] + log2_fast(l[g])) * kLn2;
+            } else {
+                const uint32_t prow = (uint32_t)slot * a.num_qo_heads + hq;
+                const uint32_t ob = (prow * D + j * 8) * 4;
+                store4_coherent(ro, ob, acc[g][0] * inv, acc[g][1] * inv, acc[g][2] * inv,
+                                acc[g][3] * inv);
+                store4_coherent(ro, ob + 16, acc[g][4] * inv, acc[g][5] * inv,
+                                acc[g][6] * inv, acc[g][7] * inv);
+                if (j == 0)
+                    store1_coherent(rl, prow * 4, m[g] + log2_fast(l[g]));
+            }
+        }
+    };
+
+    if (n > 0) {
+        struct Tile {
+            uint4 k[RPL];
+            uint4 v[RPL];
+            int4 rec;
+        };
+
+        auto rec_of = [&](int i) { return blk[1 + min(i, n - 1)]; };
+
+        // Byte offsets of this lane's rows within a tile (uniform base + 32-bit
+        // lane offset, so the loads take the scalar-base addressing form);
+        // rows past the tile's last token re-read its first row.
+        uint32_t voff[RPL];
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+            voff[i] = (uint32_t)(((rg + RG * i) * a.row_stride + col) * 2);
+        const uint32_t voff0 = (uint32_t)(col * 2);
+        const int64_t half_bytes = (int64_t)a.half_stride * 2;
+
+        auto load_tile = [&](Tile &x, const int4 rec) {
+            x.rec = rec;
+            const int info = rec.y;
+            const int ntok = (info & kInfoNtokMask) + 1;
+            const int slot0 = (info >> kInfoSlotShift) & kInfoSlotMask;
+            const char *kb = reinterpret_cast<const char *>(a.cache) +
+                             ((int64_t)rec.x * a.page_stride + (int64_t)slot0 * a.row_stride) * 2;
+            const char *vb = kb + half_bytes;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                const uint32_t vo = (rg + RG * i) < ntok ? voff[i] : voff0;
+                x.k[i] = *reinterpret_cast<const uint4 *>(kb + vo);
+                x.v[i] = *reinterpret_cast<const uint4 *>(vb + vo);
+            }
+        };
+
+        bool q_ready = true;   // the first segment's q is loaded before the loop
+
+#ifndef PKV_PRIO
+#define PKV_PRIO 2
 #endif
+        // Two waves of the workgroup share each SIMD (wave w and w ^ 4), and
+        // with equal priority the older one wins issue, so the younger one
+        // would finish its (identical) work far later and the compute unit
+        // would stream with half its waves at the end.  The wave that is
+        // behind its partner takes the higher priority.
+        __shared__ int s_prog[kMaxWavesPerGroup];
+        const int wslot = threadIdx.x >> 6;
+        const int partner = wslot ^ 4;
+        const bool has_partner = partner < (int)(blockDim.x >> 6);
+        auto balance = [&](int done) {
+            if (PKV_PRIO == 1) {
+                if (((done & 1) != 0) == (wslot >= 4))
+                    __builtin_amdgcn_s_setprio(1);
+                else
+                    __builtin_amdgcn_s_setprio(0);
+            } else if (PKV_PRIO == 2 && has_partner) {
+                if (lane == 0)
+                    s_prog[wslot] = done;
+                const int other = s_prog[partner];
+                if (done <= other)
+                    __builtin_amdgcn_s_setprio(1);
+                else
+                    __builtin_amdgcn_s_setprio(0);
+            }
+        };
+
+        auto compute_tile = [&](const Tile &x) {
+            const int info = x.rec.y;
+            if (info & kInfoSegFirst) {
+                if (!q_ready) {
+                    load_q(x.rec.z);
+                    // Wait here, on this rare path: q must not be left in
+                    // flight across the join, or every later tile would wait
+                    // for the youngest loads before its first dot product.
+                    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+                }
+                q_ready = false;
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    m[g] = kMInit;
+                    l[g] = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[g][e] = 0.f;
+                }
+            }
+            const int ntok = (info & kInfoNtokMask) + 1;
+            // Fused append: the entry's new row is not in the cache yet; the
+            // lanes holding it take it from k_new / v_new (once per entry, so
+            // this rare path waits for its own loads right here).
+            uint4 kx[RPL], vx[RPL];
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                kx[i] = x.k[i];
+                vx[i] = x.v[i];
+            }
+            const int nr = (info >> kInfoNewRowShift) & (kTileTokens - 1);
+            if (fused && (info & kInfoHasNew)) {
+                const int64_t src = ((int64_t)x.rec.z * a.num_kv_heads + h) * D + j * 8;
+#pragma unroll
+                for (int i = 0; i < RPL; ++i)
+                    if (rg + RG * i == nr) {
+                        kx[i] = load16(a.k_new + src);
+                        vx[i] = load16(a.v_new + src);
+                    }
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            }
+            float s[RPL][G];
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    float d = 0.f;
+                    d = dot2_bf16(qv[g][0], kx[i].x, d);
+                    d = dot2_bf16(qv[g][1], kx[i].y, d);
+                    d = dot2_bf16(qv[g][2], kx[i].z, d);
+                    d = dot2_bf16(qv[g][3], kx[i].w, d);
+                    s[i][g] = row_sum<LPR>(d) * a.scale_log2;
+                }
+            if (ntok < kTileTokens) {
+                // rows past the tile's last token (they re-read its first row,
+                // which for a fused append is the stale slot of the new row):
+                // weight 0 and value 0, so nothing they hold reaches the sums
+#pragma unroll
+                for (int i = 0; i < RPL; ++i)
+                    if (rg + RG * i >= ntok) {
+#pragma unroll
+                        for (int g = 0; g < G; ++g)
+                            s[i][g] = -INFINITY;
+                        vx[i] = make_uint4(0u, 0u, 0u, 0u);
+                    }
+            }
+            // Lazy maximum: raise m only when a score passes it by more than kTau.
+            float smax[G];
+            bool raise = false;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                smax[g] = s[0][g];
+#pragma unroll
+                for (int i = 1; i < RPL; ++i)
+                    smax[g] = fmaxf(smax[g], s[i][g]);
+                raise |= smax[g] > m[g] + kTau;
+            }
+            if (raise) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const bool up = smax[g] > m[g] + kTau;
+                    const float mn = up ? smax[g] : m[g];
+                    const float alpha = up ? exp2_fast(m[g] - mn) : 1.f;
+                    m[g] = mn;
+                    l[g] *= alpha;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[g][e] *= alpha;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                const uint4 w = vx[i];
+                const float vf[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                                     bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float p = exp2_fast(s[i][g] - m[g]);   // 0 for masked rows
+                    l[g] += p;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+                }
+            }
+            if (fused && (info & kInfoHasNew)) {
+                // append: the lanes holding the new row store it into its slot
+                const int slot0 = (info >> kInfoSlotShift) & kInfoSlotMask;
+                uint16_t *dst = a.cache_w + (int64_t)x.rec.x * a.page_stride +
+                                (int64_t)(slot0 + nr) * a.row_stride + col;
+#pragma unroll
+                for (int i = 0; i < RPL; ++i)
+                    if (rg + RG * i == nr) {
+                        store16(dst, kx[i]);
+                        store16(dst + a.half_stride, vx[i]);
+                    }
+            }
+            if (info & kInfoSegLast) {
+                // merge the row groups; every lane ends with the totals
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float mw = group_max<RG>(m[g]);
+                    const float f = exp2_fast(m[g] - mw);
+                    l[g] = group_sum<RG>(l[g] * f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[g][e] = group_sum<RG>(acc[g][e] * f);
+                    m[g] = mw;
+                }
+                const bool whole = (info & kInfoSegWhole) != 0;
+                write_rows(x.rec.z, x.rec.w, whole);
+                if (!whole) {
+                    if (pend0 < 0)
+                        pend0 = x.rec.z;
+                    else
+                        pend1 = x.rec.z;
+                }
+            }
+        };
+
+        // Full cycles of three tiles in a single-exit loop (so the compiler
+        // sees one simple loop and keeps its waits exact), then at most two
+        // tiles, already loaded, outside it.
+        const int4 r0 = rec_of(0);
+        const int4 r1 = rec_of(1);
+        int4 rn = rec_of(2);
+        load_q(r0.z);
+        Tile A, B, C;
+        load_tile(A, r0);
+        load_tile(B, r1);
+        int kk = 0;
+        for (; kk + 3 <= n; kk += 3) {
+            load_tile(C, rn);
+            rn = rec_of(kk + 3);
+            compute_tile(A);
+            balance(kk + 1);
+            load_tile(A, rn);
+            rn = rec_of(kk + 4);
+            compute_tile(B);
+            balance(kk + 2);
+            load_tile(B, rn);
+            rn = rec_of(kk + 5);
+            compute_tile(C);
+            balance(kk + 3);
+        }
+        if (kk < n)
+            compute_tile(A);
+        if (kk + 1 < n)
+            compute_tile(B);
+    }
+
+    // Split entries: count this wave's partial in; the last of an entry's
+    // segments to arrive merges them all and resets the counter.
+    if (pend0 >= 0) {
+        // this wave's partial stores are complete (written through) before
+        // its arrival is counted; the compiler may not move them past here
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int b = p == 0 ? pend0 : pend1;
+            if (b < 0)
+                break;
+            int32_t *counter = a.cnt + (int64_t)b * a.num_kv_heads + h;
+            int old = 0;
+            if (lane == 0)
+                old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+            old = __builtin_amdgcn_readfirstlane(old);
+            const int4 e = ent[b];
+            if (old != e.y - 1)
+                continue;
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            // row group rg merges query heads hq0 + rg, hq0 + rg + RG, ...: all
+            // lanes load at once, one round of loads per RG heads
+#pragma unroll
+            for (int g0 = 0; g0 < G; g0 += RG) {
+                const int g = g0 + rg;
+                if (g >= G)
+                    break;
+                const int hq = hq0 + g;
+                const uint32_t pl = ((uint32_t)e.x * a.num_qo_heads + hq) * 4;
+                const uint32_t po = (((uint32_t)e.x * a.num_qo_heads + hq) * D + j * 8) * 4;
+                const uint32_t sl = (uint32_t)a.num_qo_heads * 4;
+                const uint32_t so = (uint32_t)a.num_qo_heads * D * 4;
+                float mm = kMInit, sum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                for (int s0 = 0; s0 < e.y; s0 += 4) {
+                    float lv[4];
+                    float4 ov[4][2];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t s = (uint32_t)min(s0 + u, e.y - 1);
+                        lv[u] = load1_coherent(rl, pl + s * sl);
+                        ov[u][0] = load4_coherent(ro, po + s * so);
+                        ov[u][1] = load4_coherent(ro, po + s * so + 16);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        if (s0 + u >= e.y)
+                            break;
+                        const float mn = fmaxf(mm, lv[u]);
+                        const float al = exp2_fast(mm - mn);
+                        const float w = exp2_fast(lv[u] - mn);
+                        sum = fmaf(sum, al, w);
+                        const float ou[8] = {ov[u][0].x, ov[u][0].y, ov[u][0].z, ov[u][0].w,
+                                             ov[u][1].x, ov[u][1].y, ov[u][1].z, ov[u][1].w};
+#pragma unroll
+                        for (int t = 0; t < 8; ++t)
+                            o[t] = fmaf(w, ou[t], o[t] * al);
+                        mm = mn;
+                    }
+                }
+                const float inv = 1.f / sum;
+                uint4 w;
+                w.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+                w.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+                w.z = pack_bf16x2(o[4] * inv, o[5] * inv);
+                w.w = pack_bf16x2(o[6] * inv, o[7] * inv);
+                store16(a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8, w);
+                if (a.lse != nullptr && j == 0)
+                    a.lse[(int64_t)b * a.num_qo_heads + hq] = (mm + log2_fast(sum)) * kLn2;
+            }
+            if (lane == 0)
+                __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    // Entries over the page bound: NaN rows (the broken precondition shows
+    // instead of a truncated result) and, when fused, the append all the same.
+    for (int b = blockIdx.x; b < a.batch; b += gridDim.x) {
+        const int4 e = ent[b];
+        if (e.y >= 0)
+            continue;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (g % RG != rg)
+                continue;
+            const int hq = hq0 + g;
+            store16(a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8,
+                    make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u));
+            if (a.lse != nullptr && j == 0)
+                a.lse[(int64_t)b * a.num_qo_heads + hq] = __builtin_nanf("");
+        }
+        if (fused && rg == 0) {
+            const int64_t src = ((int64_t)b * a.num_kv_heads + h) * D + j * 8;
+            uint16_t *dst = a.cache_w + (int64_t)e.z * a.page_stride +
+                            (int64_t)e.w * a.row_stride + col;
+            store16(dst, load16(a.k_new + src));
+            store16(dst + a.half_stride, load16(a.v_new + src));
+        }
+    }
+}
 
 // Launch through hipLaunchKernel so the returned status belongs to this
 // launch alone (hipGetLastError could report an older, unrelated error).
-template <typename Args>
-hipError_t launch(const void *kernel, dim3 grid, dim3 block, size_t lds, const Args &args,
-                  hipStream_t stream) {
-    void *params[] = {const_cast<Args *>(&args)};
+hipError_t launch_raw(const void *kernel, dim3 grid, dim3 block, size_t lds, void **params,
+                      hipStream_t stream) {
     return hipLaunchKernel(kernel, grid, block, params, lds, stream);
 }
 
-template <int D, int G>
-const void *decode_kernel_for(int page_size) {
-    return page_size < kTileTokens
-               ? reinterpret_cast<const void *>(&decode_kernel<D, G, true>)
-               : reinterpret_cast<const void *>(&decode_kernel<D, G, false>);
-}
-
 template <int D>
-const void *decode_kernel_d(int group, int page_size) {
+const void *run_kernel_d(int group) {
     switch (group) {
-    case 1: return decode_kernel_for<D, 1>(page_size);
-    case 2: return decode_kernel_for<D, 2>(page_size);
-    case 3: return decode_kernel_for<D, 3>(page_size);
-    case 4: return decode_kernel_for<D, 4>(page_size);
-    case 5: return decode_kernel_for<D, 5>(page_size);
-    case 6: return decode_kernel_for<D, 6>(page_size);
-    case 7: return decode_kernel_for<D, 7>(page_size);
-    case 8: return decode_kernel_for<D, 8>(page_size);
+    case 1: return reinterpret_cast<const void *>(&run_kernel<D, 1>);
+    case 2: return reinterpret_cast<const void *>(&run_kernel<D, 2>);
+    case 3: return reinterpret_cast<const void *>(&run_kernel<D, 3>);
+    case 4: return reinterpret_cast<const void *>(&run_kernel<D, 4>);
+    case 5: return reinterpret_cast<const void *>(&run_kernel<D, 5>);
+    case 6: return reinterpret_cast<const void *>(&run_kernel<D, 6>);
+    case 7: return reinterpret_cast<const void *>(&run_kernel<D, 7>);
+    case 8: return reinterpret_cast<const void *>(&run_kernel<D, 8>);
     default: return nullptr;
     }
 }
 
-const void *decode_kernel_ptr(int head_dim, int group, int page_size) {
+const void *run_kernel_ptr(int head_dim, int group) {
     if (head_dim == 64)
-        return decode_kernel_d<64>(group, page_size);
+        return run_kernel_d<64>(group);
     if (head_dim == 128)
-        return decode_kernel_d<128>(group, page_size);
+        return run_kernel_d<128>(group);
     return nullptr;
-}
-
-template <int D>
-const void *merge_kernel_d(int group) {
-    switch (group) {
-    case 1: return reinterpret_cast<const void *>(&merge_kernel<D, 1>);
-    case 2: return reinterpret_cast<const void *>(&merge_kernel<D, 2>);
-    case 3: return reinterpret_cast<const void *>(&merge_kernel<D, 3>);
-    case 4: return reinterpret_cast<const void *>(&merge_kernel<D, 4>);
-    case 5: return reinterpret_cast<const void *>(&merge_kernel<D, 5>);
-    case 6: return reinterpret_cast<const void *>(&merge_kernel<D, 6>);
-    case 7: return reinterpret_cast<const void *>(&merge_kernel<D, 7>);
-    case 8: return reinterpret_cast<const void *>(&merge_kernel<D, 8>);
-    default: return nullptr;
-    }
-}
-
-// Dynamic LDS of the decode kernel: entry descriptors of nb entries, the
-// piece's tile tables, and q_slots staged q rows of q_row_bytes each.
-size_t decode_lds_bytes(int nb, int page_size, int q_slots, int q_row_bytes) {
-    const size_t ppt = page_size < kTileTokens ? kTileTokens : 1;
-    const size_t ints = (size_t)3 * nb + 1 + (size_t)kPiece * (ppt + 1) + q_pad(nb);
-    return sizeof(int) * ints + (size_t)q_slots * q_row_bytes;
-}
-
-int group_waves(int num_kv_heads) {
-    return num_kv_heads < kMaxWavesPerGroup ? num_kv_heads : kMaxWavesPerGroup;
-}
-
-// q rows staged per piece: at most 8 and no more than the entries a
-// workgroup can see, within 32 KiB and a 64 KiB total for the workgroup's
-// LDS (0 when not even one fits: q is then read from memory).
-int decode_q_slots(int nb, int page_size, int q_row_bytes) {
-    const int64_t tables = (int64_t)decode_lds_bytes(nb, page_size, 0, q_row_bytes);
-    int64_t budget = (int64_t)(64 << 10) - tables;
-    budget = budget < (32 << 10) ? budget : (32 << 10);
-    int64_t n = budget > 0 ? budget / q_row_bytes : 0;
-    n = n > 8 ? 8 : n;
-    return (int)(n < nb ? n : nb);
-}
-
-size_t decode_lds_for(int nb, int page_size, int num_qo_heads, int head_dim) {
-    const int row = num_qo_heads * head_dim * 2;
-    return decode_lds_bytes(nb, page_size, decode_q_slots(nb, page_size, row), row);
 }
 
 }  // namespace
 
 hipError_t launch_append(const AppendArgs &a, int batch, hipStream_t stream) {
-    return launch(reinterpret_cast<const void *>(&append_kernel), dim3((unsigned)batch),
-                  dim3(256), 0, a, stream);
+    AppendArgs args = a;
+    void *params[] = {&args};
+    return launch_raw(reinterpret_cast<const void *>(&append_kernel), dim3((unsigned)batch),
+                      dim3(256), 0, params, stream);
 }
 
-hipError_t balanced_groups(int head_dim, int group, int num_kv_heads, int page_size,
-                           int batch, int *groups) {
-    const int num_qo_heads = group * num_kv_heads;
-    const void *k = decode_kernel_ptr(head_dim, group, page_size);
+bool run_supported(int head_dim, int group) { return run_kernel_ptr(head_dim, group) != nullptr; }
+
+hipError_t balanced_blocks(int head_dim, int group, int num_kv_heads, int *blocks) {
+    const void *k = run_kernel_ptr(head_dim, group);
     if (k == nullptr)
         return hipErrorInvalidValue;
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err == hipSuccess)
         err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int waves = group_waves(num_kv_heads);
     if (err == hipSuccess)
-        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, k, 64 * group_waves(num_kv_heads),
-            decode_lds_for(batch, page_size, num_qo_heads, head_dim));
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64 * waves, 0);
     if (err != hipSuccess)
         return err;
-    const int waves = group_waves(num_kv_heads);
     const int head_groups = (num_kv_heads + waves - 1) / waves;
-    if (PKV_WAVES_PER_CU > 0)
-        per_cu = (PKV_WAVES_PER_CU + waves - 1) / waves;
     if (per_cu < 1)
         per_cu = 1;
     if (cus > kMaxComputeUnits)
         cus = kMaxComputeUnits;
     // workgroups resident at once, shared by the head groups
     int64_t w = ((int64_t)cus * per_cu + head_groups - 1) / head_groups;
-    const int64_t bound = balanced_groups_bound(num_kv_heads);
-    *groups = (int)(w < bound ? w : bound);
+    const int64_t bound = balanced_blocks_bound(num_kv_heads);
+    *blocks = (int)(w < bound ? w : bound);
     return hipSuccess;
 }
 
-hipError_t launch_decode(const DecodeArgs &args, int head_dim, int group, hipStream_t stream) {
-    DecodeArgs a = args;
-    const int nb = a.chunk_tiles > 0 ? 1 : a.batch;
-    const int q_row = a.num_qo_heads * head_dim * 2;
-    a.q_slots = decode_q_slots(nb, a.page_size, q_row);
-    const size_t lds = decode_lds_bytes(nb, a.page_size, a.q_slots, q_row);
-    const void *k = decode_kernel_ptr(head_dim, group, a.page_size);
-    const void *mk = head_dim == 64 ? merge_kernel_d<64>(group)
-                                    : (head_dim == 128 ? merge_kernel_d<128>(group) : nullptr);
-    if (k == nullptr || mk == nullptr)
+hipError_t launch_plan(const PlanArgs &a, hipStream_t stream) {
+    PlanArgs args = a;
+    void *params[] = {&args};
+    const int64_t items = (int64_t)a.num_blocks * a.block_stride;
+    const int64_t other = (int64_t)a.batch * a.num_kv_heads;
+    const int64_t work = items > other ? items : other;
+    int64_t grid = (work + 255) / 256;
+    grid = grid < 1 ? 1 : (grid > 1024 ? 1024 : grid);
+    const size_t lds = a.chunk_tiles > 0 ? 0 : sizeof(int) * ((size_t)a.batch + 1);
+    return launch_raw(reinterpret_cast<const void *>(&plan_kernel), dim3((unsigned)grid),
+                      dim3(256), lds, params, stream);
+}
+
+hipError_t launch_run(const RunArgs &a, const int32_t *blocks, const int32_t *ent,
+                      int num_blocks, int head_dim, int group, hipStream_t stream) {
+    const void *k = run_kernel_ptr(head_dim, group);
+    if (k == nullptr)
         return hipErrorInvalidValue;
+    RunArgs args = a;
+    const int4 *bp = reinterpret_cast<const int4 *>(blocks);
+    const int4 *ep = reinterpret_cast<const int4 *>(ent);
+    void *params[] = {&args, &bp, &ep};
     const int waves = group_waves(a.num_kv_heads);
-    const dim3 block(64 * waves);
     const unsigned head_groups = (unsigned)((a.num_kv_heads + waves - 1) / waves);
-    hipError_t err;
-    bool may_split;
-    if (a.chunk_tiles > 0) {
-        const unsigned batch8 = ((unsigned)a.batch + 7u) & ~7u;
-        err = launch(k, dim3(batch8 * (unsigned)a.max_chunks, head_groups), block,
-                     lds, a, stream);
-        may_split = a.max_chunks > 1;
-    } else {
-        err = launch(k, dim3((unsigned)a.num_groups, head_groups), block,
-                     lds, a, stream);
-        may_split = true;
-    }
-    if (err != hipSuccess || !may_split)
-        return err;
-    // COLS float4 columns times KS ways: 256 threads for every built shape
-    // (COLS = group * head_dim / 4 divides 256 or exceeds it)
-    const int cols = group * head_dim / 4;
-    const int threads = cols >= 256 ? ((cols + 63) / 64) * 64 : (256 / cols) * cols;
-    return launch(mk, dim3((unsigned)a.batch * a.num_kv_heads), dim3(threads), 0, a, stream);
+    return launch_raw(k, dim3((unsigned)num_blocks, head_groups), dim3(64 * waves), 0, params,
+                      stream);
 }
 
 }  // namespace pkv

@@ -22,67 +22,111 @@ struct AppendArgs {
     int32_t page_size;
 };
 
-// Arguments of the decode and merge kernels.
-struct DecodeArgs {
+// Tiles are up to 8 consecutive tokens of one page: page_size / 8 tiles per
+// page (one tile when page_size < 8), the last page of an entry cut at its
+// last row.
+constexpr int kTileTokens = 8;
+
+// The plan of a decode step (pkv_plan) lives in the workspace:
+//   cnt     int32 [batch * Hkv]   arrival counters of split entries; zero
+//                                 between launches (the plan zeroes them, the
+//                                 merging wave resets its own)
+//   ent     int4  [batch]         per entry: first partial slot, number of
+//                                 segments (0: no tiles, -1: over the page
+//                                 bound), and the append target page / slot
+//   blocks  int4  [num_blocks][block_stride]
+//                                 per decode workgroup: a header {tiles, run,
+//                                 0, 0} and then one record per tile
+//                                 {page, info, entry, partial slot}
+//   part_o  fp32  [slots, Hq, D]  partial outputs of split entries
+//   part_lse fp32 [slots, Hq]     their log-sum-exp, base 2
+// Bits of a record's info word:
+constexpr int kInfoNtokMask = 0x7;        // tokens in the tile - 1
+constexpr int kInfoSlotShift = 3;         // bits 3-11: page slot of the first token
+constexpr int kInfoSlotMask = 0x1FF;
+constexpr int kInfoSegFirst = 1 << 12;    // first tile of its segment
+constexpr int kInfoSegLast = 1 << 13;     // last tile of its segment
+constexpr int kInfoSegWhole = 1 << 14;    // the segment is the whole entry
+constexpr int kInfoHasNew = 1 << 15;      // the tile holds the entry's token L-1
+constexpr int kInfoNewRowShift = 16;      // bits 16-18: that token's row in the tile
+
+struct PlanArgs {
+    const int32_t *indptr;
+    const int32_t *indices;
+    const int32_t *last_len;
+    int32_t *blocks;          // int4 records, see above
+    int32_t *ent;             // int4 per entry
+    int32_t *cnt;
+    int32_t batch;
+    int32_t num_pages;
+    int32_t page_size;
+    int32_t tiles_per_page;
+    int32_t num_kv_heads;
+    int32_t num_blocks;       // decode workgroups along x
+    int32_t block_stride;     // int4 records per block: 1 + capacity
+    int32_t chunk_tiles;      // fixed mode: tiles per chunk; 0 = balanced
+    int32_t max_chunks;       // fixed mode: chunks per entry
+    int32_t max_pages;        // entries listing more pages are poisoned
+};
+
+struct RunArgs {
     const uint16_t *cache;    // first element of this layer's slab
     uint16_t *cache_w;        // same slab, written by the fused append, or null
     const uint16_t *q;        // [batch, Hq, D]
     const uint16_t *k_new;    // fused append rows [batch, Hkv, D], or null
     const uint16_t *v_new;
-    const int32_t *indptr;
-    const int32_t *indices;
-    const int32_t *last_len;
     uint16_t *out;            // [batch, Hq, D] bf16
     float *lse;               // [batch, Hq] or null
-    float *part_o;            // [slots, Hq, D] fp32 partial outputs
-    float *part_lse;          // [slots, Hq] fp32 partial lse, log2 domain
-    int32_t *tile_start;      // [batch + 1] tile prefix sums (balanced mode)
-    int64_t page_stride;
-    int32_t half_stride;
+    float *part_o;
+    float *part_lse;
+    int64_t part_o_bytes;     // sizes of the two partial arrays
+    int64_t part_lse_bytes;
+    int32_t *cnt;
+    int64_t page_stride;      // 2 * page_size * Hkv * D
+    int32_t half_stride;      // page_size * Hkv * D
     int32_t row_stride;       // Hkv * D
     int32_t num_qo_heads;
     int32_t num_kv_heads;
-    int32_t num_pages;
     int32_t batch;
-    int32_t page_size;
-    int32_t log2_page;
-    int32_t chunk_tiles;      // fixed mode: 8-token tiles per chunk; 0 = balanced
-    int32_t max_chunks;       // fixed mode: chunks per entry the launch covers
-    int32_t num_groups;       // balanced mode: workgroups sharing the tiles
-    int32_t q_slots;          // q rows a workgroup stages in LDS per piece (set at launch)
+    int32_t block_stride;
     float scale_log2;         // sm_scale * log2(e)
 };
 
-// Largest batch the balanced schedule keeps in LDS (its tile prefix sums);
+// Largest batch the balanced plan handles (its tile prefix sums sit in LDS);
 // larger batches use fixed chunks of kFallbackChunkPages pages.
 constexpr int kMaxBalancedBatch = 4096;
 constexpr int kFallbackChunkPages = 16;
 constexpr int kMaxChunkPages = 1 << 16;
-// Upper bound on compute units, for sizing workspace without a device query.
+// Upper bounds for sizing workspace without a device query.
 constexpr int kMaxComputeUnits = 320;
 constexpr int kMaxWavesPerCU = 32;
 constexpr int kMaxKvHeads = 16;
 // A decode workgroup has one wave per KV head, at most 8; more heads use more
-// workgroups along the grid's y axis.  The kernel keeps to 256 registers a
-// wave (two waves per SIMD), the most VALU instructions can address.
+// workgroups along the grid's y axis.
 constexpr int kMaxWavesPerGroup = 8;
 
-// Tiles are 8 tokens: one token row per 8-lane group of a 64-wide wavefront.
-constexpr int kTileTokens = 8;
+inline int group_waves(int num_kv_heads) {
+    return num_kv_heads < kMaxWavesPerGroup ? num_kv_heads : kMaxWavesPerGroup;
+}
 
-inline int64_t balanced_groups_bound(int num_kv_heads) {
-    const int waves = num_kv_heads < kMaxWavesPerGroup ? num_kv_heads : kMaxWavesPerGroup;
+inline int64_t balanced_blocks_bound(int num_kv_heads) {
+    const int waves = group_waves(num_kv_heads);
     return ((int64_t)kMaxComputeUnits * kMaxWavesPerCU + waves - 1) / waves;
 }
 
 hipError_t launch_append(const AppendArgs &a, int batch, hipStream_t stream);
 
-// Number of workgroups the balanced schedule uses on the current device.
-hipError_t balanced_groups(int head_dim, int group, int num_kv_heads, int page_size,
-                           int batch, int *groups);
+// Workgroups per head group the balanced plan uses on the current device
+// (what the device holds at once).
+hipError_t balanced_blocks(int head_dim, int group, int num_kv_heads, int *blocks);
 
-// Enqueues the decode pass, then the merge of entries split over several
-// workgroups.  hipErrorInvalidValue for a (head_dim, group) that is not built.
-hipError_t launch_decode(const DecodeArgs &a, int head_dim, int group, hipStream_t stream);
+// True when the decode kernel is built for (head_dim, group).
+bool run_supported(int head_dim, int group);
+
+hipError_t launch_plan(const PlanArgs &a, hipStream_t stream);
+
+// Enqueues the decode kernel: num_blocks x head-group workgroups.
+hipError_t launch_run(const RunArgs &a, const int32_t *blocks, const int32_t *ent,
+                      int num_blocks, int head_dim, int group, hipStream_t stream);
 
 }  // namespace pkv

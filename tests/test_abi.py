@@ -20,7 +20,7 @@ DESC = CacheDesc(2, 64, 16, 2, 64)
 def test_every_declared_symbol_is_exported():
     names = pkv.declared_functions()
     assert set(names) == {"pkv_append", "pkv_decode_workspace_size",
-                          "pkv_append_decode", "pkv_decode",
+                          "pkv_append_decode", "pkv_decode", "pkv_plan", "pkv_run",
                           "pkv_validate_page_table", "pkv_status_string",
                           "pkv_last_hip_error"}
     for n in names:
@@ -39,19 +39,24 @@ def test_status_strings():
 
 def test_workspace_size():
     d = CacheDesc(36, 8192, 16, 8, 128)
-    # fixed runs covering every entry in one run: no workspace
-    assert pkv.workspace_size(d, 32, 64, 16, 16) == 0
+    # fixed runs of 16 pages over entries of at most 16 pages: one run each;
+    # the plan holds 8 x (1 + 32) records per block row of 8 entries
+    ws = pkv.workspace_size(d, 32, 64, 16, 16)
+    assert ws >= 64 * (1 + 32) * 16 and ws % 256 == 0
     # fixed runs of 32 pages over 2048-page entries: 64 runs of partials
     ws = pkv.workspace_size(d, 32, 8, 2048, 32)
     rows = 8 * 64 * 32
-    assert ws >= rows * 128 * 4 + rows * 4 and ws % 256 == 0
-    # balanced: partial slots for every workgroup plus every entry, and the
-    # tile prefix sums
+    assert ws >= rows * 128 * 4 + rows * 4 + 8 * 4096 * 16 and ws % 256 == 0
+    # balanced: a record per tile of batch x max_pages pages, partial slots for
+    # every workgroup plus every entry, counters and entry descriptors
     wb = pkv.workspace_size(d, 32, 64, 256, 0)
-    assert wb >= (64 + 1) * 4 + 64 * 32 * 129 * 4
+    assert wb >= 64 * 256 * 2 * 16 + 64 * 32 * 129 * 4 + 64 * 8 * 4 + 64 * 16
     assert pkv.workspace_size(d, 32, 0, 256, 0) == 0
     assert pkv.workspace_size(d, 30, 64, 256, 0) > 0        # sizes only
     assert pkv.workspace_size(CacheDesc(36, 8192, 12, 8, 128), 32, 64, 256, 0) == 0
+    # pages of fewer than 8 tokens are one tile each
+    assert (pkv.workspace_size(CacheDesc(1, 64, 2, 8, 128), 32, 64, 256, 16)
+            > pkv.workspace_size(CacheDesc(1, 64, 2, 8, 128), 32, 64, 128, 16))
 
 
 def _decode(desc=DESC, layer=0, q=FAKE, hq=4, batch=3, scale=0.125, out=FAKE, lse=NULL,
@@ -116,6 +121,44 @@ def test_append_decode_validation(kw, code):
 
 def test_append_decode_batch_zero_is_noop():
     assert _append_decode(batch=0, k=NULL, v=NULL, out=NULL) == 0
+
+
+def _plan(desc=DESC, hq=4, batch=3, maxp=4, chunk=0, ws=NULL, wsb=0,
+          tables=(FAKE, FAKE, FAKE)):
+    return lib.pkv_plan(desc, hq, *tables, batch, maxp, chunk, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(hq=3), -2), (dict(maxp=0), -2), (dict(chunk=-1), -2),
+    (dict(chunk=65537), -3), (dict(desc=CacheDesc(2, 64, 16, 2, 96)), -3),
+    (dict(tables=(FAKE, NULL, FAKE)), -1), (dict(), -4), (dict(chunk=2), -4),
+    (dict(ws=FAKE, wsb=16), -4),
+    (dict(ws=ctypes.c_void_p(0x100010), wsb=1 << 30), -6),
+])
+def test_plan_validation(kw, code):
+    assert _plan(**kw) == code
+
+
+def _run(k=NULL, v=NULL, layer=0, batch=3, hq=4, q=FAKE, out=FAKE, chunk=0, ws=NULL,
+         wsb=0, scale=0.125):
+    return lib.pkv_run(FAKE, DESC, layer, k, v, q, hq, batch, scale, out, NULL, 4, chunk,
+                       ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layer=2), -2), (dict(hq=3), -2), (dict(scale=float("nan")), -2),
+    (dict(q=NULL), -1), (dict(out=NULL), -1), (dict(k=FAKE), -1), (dict(v=FAKE), -1),
+    (dict(out=ctypes.c_void_p(0x100004)), -6),
+    (dict(k=FAKE, v=ctypes.c_void_p(0x100002)), -6),
+    (dict(), -4), (dict(chunk=1, ws=FAKE, wsb=64), -4),
+])
+def test_run_validation(kw, code):
+    assert _run(**kw) == code
+
+
+def test_plan_and_run_batch_zero_are_noops():
+    assert _plan(batch=0, tables=(NULL, NULL, NULL)) == 0
+    assert _run(batch=0, q=NULL, out=NULL) == 0
 
 
 def test_validate_page_table():

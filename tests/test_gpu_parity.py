@@ -414,9 +414,11 @@ def test_append_decode_config3_layers():
         compare(og, lg, ro, rl, what=f"fused cfg3 layer {layer}")
 
 
-def test_fixed_runs_poison_entries_over_the_bound():
-    """An entry longer than max_pages_per_req allows gets NaN rows in fixed
-    mode (a visible broken precondition); the other rows stay correct."""
+@pytest.mark.parametrize("chunk", [4, 0])
+def test_entries_over_the_page_bound_get_nan_rows(chunk):
+    """An entry listing more pages than max_pages_per_req gets NaN rows (a
+    visible broken precondition, in both split modes); the other rows stay
+    correct."""
     spec = CONFIGS[2]
     table = make_table(spec)
     ld, dev = host_layer_case(spec, table, 0)
@@ -427,16 +429,62 @@ def test_fixed_runs_poison_entries_over_the_bound():
     bound = int(np.sort(n)[-3])          # the two longest entries exceed it
     pkv.append(cache, 0, dev[1], dev[2], *tables)
     out, lse = pkv.decode(cache, 0, dev[0], *tables, spec.sm_scale,
-                          max_pages_per_req=bound, kv_chunk_pages=4)
-    # runs of 4 pages = 8 tiles; the launch covers ceil(bound * 2 / 8) runs
-    tiles = (table.lengths + 7) // 8
-    over = (tiles + 7) // 8 > (bound * 2 + 7) // 8
+                          max_pages_per_req=bound, kv_chunk_pages=chunk)
+    over = n > bound
     assert over.any() and (table.active & ~over).any()
     lse_h = lse.cpu().numpy()
     assert np.all(np.isnan(lse_h[over]))
+    assert np.all(np.isnan(bf16_to_f32(to_host_u16(out))[over]))
     ro, rl = _oracle_full(cache_host, 0, ld, table, spec.sm_scale)
     ok = table.active & ~over
     compare(out, lse, ro[ok], rl[ok], rows=ok, what="rows under the bound")
+
+
+# ------------------------------------------------------------ plan once, run per layer
+@pytest.mark.parametrize("idx", [1, 3, 9])
+@pytest.mark.parametrize("chunk", [0, 2])
+def test_plan_once_run_every_layer(idx, chunk):
+    """One pkv_plan serves pkv_run on every layer, decode-only and fused: each
+    layer's rows are bit-identical to a standalone pkv_decode /
+    pkv_append_decode on the same inputs, and within tolerance of the oracle;
+    the cache after the fused runs equals the oracle's appends."""
+    hq, hkv, d, ps, lengths, active = SHAPES[idx]
+    rng = np.random.default_rng(5000 + idx)
+    act = np.ones(len(lengths), bool) if active is None else np.asarray(active, bool)
+    table = table_from_lengths(lengths, act, ps, None, rng)
+    nl = 3
+    lds = [workloads.draw_layer(rng, table, hq, hkv, d, 1.0, stale="nan", unused="nan")
+           for _ in range(nl)]
+    cache_host = np.stack([ld.cache for ld in lds])
+    cache_a = to_dev_u16(cache_host)
+    cache_b = to_dev_u16(cache_host)
+    tables = table_to_dev(table)
+    scale = 1.0 / math.sqrt(d)
+    mp = table.max_pages_per_req
+    plan = pkv.plan(cache_a, hq, *tables, mp, chunk)
+    for rep in range(2):
+        for layer in (2, 0, 1):
+            ld = lds[layer]
+            q, kn, vn = to_dev_u16(ld.q), to_dev_u16(ld.k_new), to_dev_u16(ld.v_new)
+            if rep == 0:
+                out, lse = pkv.run(cache_a, layer, q, plan, scale, k_new=kn, v_new=vn)
+                out2, lse2 = pkv.append_decode(cache_b, layer, kn, vn, q, *tables, scale,
+                                               max_pages_per_req=mp, kv_chunk_pages=chunk)
+                ro, rl = _oracle_full(cache_host, layer, ld, table, scale)
+            else:
+                out, lse = pkv.run(cache_a, layer, q, plan, scale)
+                out2, lse2 = pkv.decode(cache_b, layer, q, *tables, scale,
+                                        max_pages_per_req=mp, kv_chunk_pages=chunk)
+                ro, rl = oracle.decode(cache_host, layer, ld.q, table.indptr,
+                                       table.indices, table.last_len, scale)
+            assert torch.equal(out[act].view(torch.int16), out2[act].view(torch.int16))
+            assert torch.equal(lse[act], lse2[act])
+            compare(out, lse, ro[act], rl[act], rows=act,
+                    what=f"shape {idx} layer {layer} rep {rep}")
+    got = to_host_u16(cache_a)
+    want = cache_host.copy()
+    pages = np.unique(table.indices[table.indices > 0])
+    np.testing.assert_array_equal(got[:, pages], want[:, pages])
 
 
 # ------------------------------------------------------------ workspace reuse
