@@ -433,53 +433,80 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
 // ---------------------------------------------------------------------------
 // Decode.
 //
-// Each wave streams its workgroup's tiles for its KV head h through three
-// rotating register buffers: while tile kk is computed, tiles kk+1 and kk+2
-// are in flight, and the record of tile kk+3 is on its way through the
-// scalar cache.  Every load is issued unconditionally (past the last tile the
-// last one is loaded again, a cache hit, and never computed), so the
-// compiler's waits keep exactly two tiles outstanding.
+// Tiles are staged through LDS.  For each 8-token tile the workgroup (one
+// wave per KV head of its head group) copies the K rows and the V rows of all
+// its heads from HBM into an LDS buffer with direct-to-LDS loads
+// (global_load_lds_dwordx4): every instruction moves 1 KiB of one contiguous
+// row run, so each page is read in long contiguous runs, and no registers
+// hold data in flight.  A ring of NBUF buffers keeps NBUF - 1 tiles in
+// flight; one barrier per tile makes a tile visible to every wave (each
+// wave first waits for its own copies) and frees the buffer that the copy of
+// tile k + NBUF - 1 then refills.  The waves then read their own head's rows
+// from LDS.  The q rows of a segment's entry travel the same way, in a slot
+// of the tile where the segment starts.
 //
-// Lane layout: lane = rg * LPR + j owns elements [8j, 8j + 8) of rows
-// rg + RG * i (i < RPL) of each tile, for K and for V, and accumulates the G
-// query heads' outputs of those elements over its rows.
-template <int D, int G>
+// The copies are written as inline assembly, so the compiler does not track
+// them; the kernel waits for them itself (s_waitcnt vmcnt with the number of
+// copies issued after the tile's, a lower bound, so the wait is never short).
+//
+// Lane layout in compute: lane = rg * LPR + j owns elements [8j, 8j + 8) of
+// rows rg + RG * i (i < RPL) of each tile, for K and for V, and accumulates
+// the G query heads' outputs of those elements over its rows.
+
+// s_waitcnt immediate for "at most n vector memory operations outstanding"
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at
+// their maximum, i.e. not waited for).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// One direct-to-LDS copy: 16 bytes from each lane's global address to LDS at
+// lds + 16 * lane (lds is wave-uniform and goes through M0).
+__device__ __forceinline__ void copy_to_lds(const void *src, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+// The same from a wave-uniform base plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void copy_to_lds(const void *base, uint32_t off, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds)
+                 : "memory");
+}
+
+template <int D, int G, int NBUF>
 __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     RunArgs a, const int4 *__restrict__ blocks, const int4 *__restrict__ ent) {
     constexpr int LPR = D / 8;                 // lanes per row
     constexpr int RG = 64 / LPR;               // row groups
     constexpr int RPL = kTileTokens / RG;      // rows per lane per tile
+    constexpr int IPW = D / 64;                // copies per wave per tile half (K or V)
+    constexpr int IPT = 2 * IPW;               // copies per wave per tile
+    constexpr int QB = G * D * 2;              // q bytes of one KV head's query heads
+    constexpr int QI = (QB + 1023) / 1024;     // copies for them
+    extern __shared__ uint4 smem[];
     const int lane = threadIdx.x & 63;
     const int rg = lane / LPR;
     const int j = lane % LPR;
-    const int h = __builtin_amdgcn_readfirstlane(blockIdx.y * (blockDim.x >> 6) +
-                                                 (threadIdx.x >> 6));
-    if (h >= a.num_kv_heads)
-        return;
+    const int nw = blockDim.x >> 6;            // waves = KV heads of the group
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h0 = blockIdx.y * nw;
+    const int h = h0 + w;
     const bool fused = a.k_new != nullptr;
     const int hq0 = h * G;
-    const int col = h * D + j * 8;   // element offset of this lane within a token row
+    const int col = h * D + j * 8;             // element offset of this lane within a token row
 
-    const int4 *blk = blocks + (int64_t)blockIdx.x * a.block_stride;
-    const int n = blk[0].x;
+    // LDS buffer b: K rows [8][nw][D], V rows [8][nw][D], then per wave QI KiB of q
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    const uint32_t part_bytes = (uint32_t)(kTileTokens * nw * D * 2);
+    const uint32_t buf_bytes = 2 * part_bytes + (uint32_t)(nw * QI * 1024);
+    const int upr = nw * D / 8;                // 16-byte units per row of the group
+    const int64_t half_bytes = (int64_t)a.half_stride * 2;
+    const int64_t row_bytes = (int64_t)a.row_stride * 2;
 
     const __amdgpu_buffer_rsrc_t ro = partial_rsrc(a.part_o, a.part_o_bytes);
     const __amdgpu_buffer_rsrc_t rl = partial_rsrc(a.part_lse, a.part_lse_bytes);
+    const int4 *blk = blocks + (int64_t)blockIdx.x * a.block_stride;
+    const int n = blk[0].x;
+
     uint32_t qv[G][4];        // q of the entry being computed, 8 bf16 per head
     float m[G], l[G], acc[G][8];
     int pend0 = -1, pend1 = -1;   // entries whose partial this wave wrote
-
-    auto load_q = [&](int b) {
-        const uint16_t *qb = a.q + ((int64_t)b * a.num_qo_heads + hq0) * D + j * 8;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const uint4 w = load16(qb + g * D);
-            qv[g][0] = w.x;
-            qv[g][1] = w.y;
-            qv[g][2] = w.z;
-            qv[g][3] = w.w;
-        }
-    };
 
     // Rows of heads hq0 + g for g = rg, rg + RG, ... are written by row group rg.
     auto write_rows = [&](int b, int slot, bool whole) {
@@ -490,12 +517,12 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             const int hq = hq0 + g;
             const float inv = 1.f / l[g];
             if (whole) {
-                uint4 w;
-                w.x = pack_bf16x2(acc[g][0] * inv, acc[g][1] * inv);
-                w.y = pack_bf16x2(acc[g][2] * inv, acc[g][3] * inv);
-                w.z = pack_bf16x2(acc[g][4] * inv, acc[g][5] * inv);
-                w.w = pack_bf16x2(acc[g][6] * inv, acc[g][7] * inv);
-                store16(a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8, w);
+                uint4 v;
+                v.x = pack_bf16x2(acc[g][0] * inv, acc[g][1] * inv);
+                v.y = pack_bf16x2(acc[g][2] * inv, acc[g][3] * inv);
+                v.z = pack_bf16x2(acc[g][4] * inv, acc[g][5] * inv);
+                v.w = pack_bf16x2(acc[g][6] * inv, acc[g][7] * inv);
+                store16(a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8, v);
                 if (a.lse != nullptr && j == 0)
                     a.lse[(int64_t)b * a.num_qo_heads + hq] = (m[g] + log2_fast(l[g])) * kLn2;
             } else {
@@ -512,82 +539,110 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     };
 
     if (n > 0) {
-        struct Tile {
-            uint4 k[RPL];
-            uint4 v[RPL];
-            int4 rec;
-        };
-
         auto rec_of = [&](int i) { return blk[1 + min(i, n - 1)]; };
 
-        // Byte offsets of this lane's rows within a tile (uniform base + 32-bit
-        // lane offset, so the loads take the scalar-base addressing form);
-        // rows past the tile's last token re-read its first row.
-        uint32_t voff[RPL];
+        // Per-lane byte offsets of this wave's copies: copy i (of IPW per
+        // half) moves 16-byte unit u = (w * IPW + i) * 64 + lane of the K (or
+        // V) rows, row u / upr, unit u % upr of that row's head-group run.
+        // Rows past the tile's last token re-read its first row (off0).
+        int crow[IPW];
+        uint32_t coff[IPW], coff0[IPW];
 #pragma unroll
-        for (int i = 0; i < RPL; ++i)
-            voff[i] = (uint32_t)(((rg + RG * i) * a.row_stride + col) * 2);
-        const uint32_t voff0 = (uint32_t)(col * 2);
-        const int64_t half_bytes = (int64_t)a.half_stride * 2;
+        for (int i = 0; i < IPW; ++i) {
+            const int u = (w * IPW + i) * 64 + lane;
+            crow[i] = u / upr;
+            const int c = u - crow[i] * upr;
+            coff0[i] = (uint32_t)(c * 16);
+            coff[i] = (uint32_t)(crow[i] * row_bytes) + coff0[i];
+        }
+        const char *cache_b = reinterpret_cast<const char *>(a.cache) + (int64_t)h0 * D * 2;
+        const int64_t page_bytes = a.page_stride * 2;
 
-        auto load_tile = [&](Tile &x, const int4 rec) {
-            x.rec = rec;
+        // The records of the tiles in the ring: record of buffer b in lane b
+        // of four registers.
+        int ring_x = 0, ring_y = 0, ring_z = 0, ring_w = 0;
+
+        // This wave's share of the copies of tile `rec` into LDS buffer `buf`:
+        // the q rows first (when a segment starts there), then IPW 1-KiB runs
+        // of K rows and as many of V rows; the fused append's new row comes
+        // from k_new / v_new.
+        auto issue = [&](const int4 rec, int buf) {
+            if (lane == buf) {
+                ring_x = rec.x;
+                ring_y = rec.y;
+                ring_z = rec.z;
+                ring_w = rec.w;
+            }
             const int info = rec.y;
             const int ntok = (info & kInfoNtokMask) + 1;
             const int slot0 = (info >> kInfoSlotShift) & kInfoSlotMask;
-            const char *kb = reinterpret_cast<const char *>(a.cache) +
-                             ((int64_t)rec.x * a.page_stride + (int64_t)slot0 * a.row_stride) * 2;
-            const char *vb = kb + half_bytes;
-#pragma unroll
-            for (int i = 0; i < RPL; ++i) {
-                const uint32_t vo = (rg + RG * i) < ntok ? voff[i] : voff0;
-                x.k[i] = *reinterpret_cast<const uint4 *>(kb + vo);
-                x.v[i] = *reinterpret_cast<const uint4 *>(vb + vo);
-            }
-        };
-
-        bool q_ready = true;   // the first segment's q is loaded before the loop
-
-#ifndef PKV_PRIO
-#define PKV_PRIO 2
-#endif
-        // Two waves of the workgroup share each SIMD (wave w and w ^ 4), and
-        // with equal priority the older one wins issue, so the younger one
-        // would finish its (identical) work far later and the compute unit
-        // would stream with half its waves at the end.  The wave that is
-        // behind its partner takes the higher priority.
-        __shared__ int s_prog[kMaxWavesPerGroup];
-        const int wslot = threadIdx.x >> 6;
-        const int partner = wslot ^ 4;
-        const bool has_partner = partner < (int)(blockDim.x >> 6);
-        auto balance = [&](int done) {
-            if (PKV_PRIO == 1) {
-                if (((done & 1) != 0) == (wslot >= 4))
-                    __builtin_amdgcn_s_setprio(1);
-                else
-                    __builtin_amdgcn_s_setprio(0);
-            } else if (PKV_PRIO == 2 && has_partner) {
-                if (lane == 0)
-                    s_prog[wslot] = done;
-                const int other = s_prog[partner];
-                if (done <= other)
-                    __builtin_amdgcn_s_setprio(1);
-                else
-                    __builtin_amdgcn_s_setprio(0);
-            }
-        };
-
-        auto compute_tile = [&](const Tile &x) {
-            const int info = x.rec.y;
+            const uint32_t bb = lds0 + (uint32_t)buf * buf_bytes;
             if (info & kInfoSegFirst) {
-                if (!q_ready) {
-                    load_q(x.rec.z);
-                    // Wait here, on this rare path: q must not be left in
-                    // flight across the join, or every later tile would wait
-                    // for the youngest loads before its first dot product.
-                    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+                const char *qs = reinterpret_cast<const char *>(a.q) +
+                                 ((int64_t)rec.z * a.num_qo_heads + hq0) * D * 2;
+#pragma unroll
+                for (int i = 0; i < QI; ++i) {
+                    const int off = min((i * 64 + lane) * 16, QB - 16);
+                    copy_to_lds(qs + off, bb + 2 * part_bytes + (uint32_t)(w * QI + i) * 1024);
                 }
-                q_ready = false;
+            }
+            const char *kb = cache_b + (int64_t)rec.x * page_bytes + (int64_t)slot0 * row_bytes;
+            const char *vb = kb + half_bytes;
+            if (fused && (info & kInfoHasNew)) {
+                const int nr = (info >> kInfoNewRowShift) & (kTileTokens - 1);
+                const int64_t nsrc = ((int64_t)rec.z * a.num_kv_heads + h0) * D * 2;
+#pragma unroll
+                for (int i = 0; i < IPW; ++i) {
+                    const uint32_t o = crow[i] < ntok ? coff[i] : coff0[i];
+                    const bool is_new = crow[i] == nr;
+                    const char *ks = is_new ? reinterpret_cast<const char *>(a.k_new) + nsrc +
+                                                  coff0[i]
+                                            : kb + o;
+                    const char *vs = is_new ? reinterpret_cast<const char *>(a.v_new) + nsrc +
+                                                  coff0[i]
+                                            : vb + o;
+                    copy_to_lds(ks, bb + (uint32_t)(w * IPW + i) * 1024);
+                    copy_to_lds(vs, bb + part_bytes + (uint32_t)(w * IPW + i) * 1024);
+                }
+            } else if (ntok == kTileTokens) {
+#pragma unroll
+                for (int i = 0; i < IPW; ++i) {
+                    copy_to_lds(kb, coff[i], bb + (uint32_t)(w * IPW + i) * 1024);
+                    copy_to_lds(vb, coff[i], bb + part_bytes + (uint32_t)(w * IPW + i) * 1024);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < IPW; ++i) {
+                    const uint32_t o = crow[i] < ntok ? coff[i] : coff0[i];
+                    copy_to_lds(kb, o, bb + (uint32_t)(w * IPW + i) * 1024);
+                    copy_to_lds(vb, o, bb + part_bytes + (uint32_t)(w * IPW + i) * 1024);
+                }
+            }
+        };
+
+        // LDS in 16-byte units: this lane's K row i of a buffer, its q rows
+        const int kunit = (rg * nw + w) * (D / 8) + j;       // row rg, head w, unit j
+        const int rstep = RG * nw * (D / 8);                  // next row of the lane
+        const int part_units = (int)(part_bytes / 16);
+        const int buf_units = (int)(buf_bytes / 16);
+        const int qunit = (2 * part_bytes + w * QI * 1024) / 16 + j;
+
+        auto compute_tile = [&](int buf) {
+            const int4 rec = make_int4(__builtin_amdgcn_readlane(ring_x, buf),
+                                       __builtin_amdgcn_readlane(ring_y, buf),
+                                       __builtin_amdgcn_readlane(ring_z, buf),
+                                       __builtin_amdgcn_readlane(ring_w, buf));
+            const int info = rec.y;
+            const uint4 *sb = smem + buf * buf_units;
+            if (info & kInfoSegFirst) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const uint4 v = sb[qunit + g * (D / 8)];
+                    qv[g][0] = v.x;
+                    qv[g][1] = v.y;
+                    qv[g][2] = v.z;
+                    qv[g][3] = v.w;
+                }
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     m[g] = kMInit;
@@ -598,38 +653,58 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                 }
             }
             const int ntok = (info & kInfoNtokMask) + 1;
-            // Fused append: the entry's new row is not in the cache yet; the
-            // lanes holding it take it from k_new / v_new (once per entry, so
-            // this rare path waits for its own loads right here).
+            const int nr = (info >> kInfoNewRowShift) & (kTileTokens - 1);
             uint4 kx[RPL], vx[RPL];
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
-                kx[i] = x.k[i];
-                vx[i] = x.v[i];
+                kx[i] = sb[kunit + i * rstep];
+                vx[i] = sb[part_units + kunit + i * rstep];
             }
-            const int nr = (info >> kInfoNewRowShift) & (kTileTokens - 1);
-            if (fused && (info & kInfoHasNew)) {
-                const int64_t src = ((int64_t)x.rec.z * a.num_kv_heads + h) * D + j * 8;
-#pragma unroll
-                for (int i = 0; i < RPL; ++i)
-                    if (rg + RG * i == nr) {
-                        kx[i] = load16(a.k_new + src);
-                        vx[i] = load16(a.v_new + src);
-                    }
-                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-            }
-            float s[RPL][G];
+            // q.k: RPL x G independent dot products, then their row sums
+            // step by step across all of them
+            float d[RPL][G];
 #pragma unroll
             for (int i = 0; i < RPL; ++i)
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    float d = 0.f;
-                    d = dot2_bf16(qv[g][0], kx[i].x, d);
-                    d = dot2_bf16(qv[g][1], kx[i].y, d);
-                    d = dot2_bf16(qv[g][2], kx[i].z, d);
-                    d = dot2_bf16(qv[g][3], kx[i].w, d);
-                    s[i][g] = row_sum<LPR>(d) * a.scale_log2;
-                }
+                for (int g = 0; g < G; ++g)
+                    d[i][g] = dot2_bf16(qv[g][0], kx[i].x, 0.f);
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    d[i][g] = dot2_bf16(qv[g][1], kx[i].y, d[i][g]);
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    d[i][g] = dot2_bf16(qv[g][2], kx[i].z, d[i][g]);
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    d[i][g] = dot2_bf16(qv[g][3], kx[i].w, d[i][g]);
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    d[i][g] += dpp<0xB1>(d[i][g]);
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    d[i][g] += dpp<0x4E>(d[i][g]);
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    d[i][g] += dpp<0x141>(d[i][g]);
+            if constexpr (LPR == 16) {
+#pragma unroll
+                for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        d[i][g] += dpp<0x140>(d[i][g]);
+            }
             if (ntok < kTileTokens) {
                 // rows past the tile's last token (they re-read its first row,
                 // which for a fused append is the stale slot of the new row):
@@ -639,26 +714,29 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                     if (rg + RG * i >= ntok) {
 #pragma unroll
                         for (int g = 0; g < G; ++g)
-                            s[i][g] = -INFINITY;
+                            d[i][g] = -INFINITY;
                         vx[i] = make_uint4(0u, 0u, 0u, 0u);
                     }
             }
-            // Lazy maximum: raise m only when a score passes it by more than kTau.
-            float smax[G];
+            // Lazy maximum (log2 units, scores d * scale_log2): raise m only
+            // when a score passes it by more than kTau.
+            const float c2 = a.scale_log2;
+            float dmax[G];
             bool raise = false;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                smax[g] = s[0][g];
+                dmax[g] = d[0][g];
 #pragma unroll
                 for (int i = 1; i < RPL; ++i)
-                    smax[g] = fmaxf(smax[g], s[i][g]);
-                raise |= smax[g] > m[g] + kTau;
+                    dmax[g] = fmaxf(dmax[g], d[i][g]);
+                raise |= fmaf(dmax[g], c2, -m[g]) > kTau;
             }
             if (raise) {
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const bool up = smax[g] > m[g] + kTau;
-                    const float mn = up ? smax[g] : m[g];
+                    const float sm = dmax[g] * c2;
+                    const bool up = sm - m[g] > kTau;
+                    const float mn = up ? sm : m[g];
                     const float alpha = up ? exp2_fast(m[g] - mn) : 1.f;
                     m[g] = mn;
                     l[g] *= alpha;
@@ -669,12 +747,12 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             }
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
-                const uint4 w = vx[i];
-                const float vf[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                                     bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+                const uint4 v = vx[i];
+                const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                                     bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const float p = exp2_fast(s[i][g] - m[g]);   // 0 for masked rows
+                    const float p = exp2_fast(fmaf(d[i][g], c2, -m[g]));   // 0 for masked rows
                     l[g] += p;
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
@@ -684,7 +762,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             if (fused && (info & kInfoHasNew)) {
                 // append: the lanes holding the new row store it into its slot
                 const int slot0 = (info >> kInfoSlotShift) & kInfoSlotMask;
-                uint16_t *dst = a.cache_w + (int64_t)x.rec.x * a.page_stride +
+                uint16_t *dst = a.cache_w + (int64_t)rec.x * a.page_stride +
                                 (int64_t)(slot0 + nr) * a.row_stride + col;
 #pragma unroll
                 for (int i = 0; i < RPL; ++i)
@@ -706,45 +784,33 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                     m[g] = mw;
                 }
                 const bool whole = (info & kInfoSegWhole) != 0;
-                write_rows(x.rec.z, x.rec.w, whole);
+                write_rows(rec.z, rec.w, whole);
                 if (!whole) {
                     if (pend0 < 0)
-                        pend0 = x.rec.z;
+                        pend0 = rec.z;
                     else
-                        pend1 = x.rec.z;
+                        pend1 = rec.z;
                 }
             }
         };
 
-        // Full cycles of three tiles in a single-exit loop (so the compiler
-        // sees one simple loop and keeps its waits exact), then at most two
-        // tiles, already loaded, outside it.
-        const int4 r0 = rec_of(0);
-        const int4 r1 = rec_of(1);
-        int4 rn = rec_of(2);
-        load_q(r0.z);
-        Tile A, B, C;
-        load_tile(A, r0);
-        load_tile(B, r1);
-        int kk = 0;
-        for (; kk + 3 <= n; kk += 3) {
-            load_tile(C, rn);
-            rn = rec_of(kk + 3);
-            compute_tile(A);
-            balance(kk + 1);
-            load_tile(A, rn);
-            rn = rec_of(kk + 4);
-            compute_tile(B);
-            balance(kk + 2);
-            load_tile(B, rn);
-            rn = rec_of(kk + 5);
-            compute_tile(C);
-            balance(kk + 3);
+        // Tiles 0 .. NBUF-2 in flight before the loop; every iteration waits
+        // for its tile, passes the barrier, refills the freed buffer with the
+        // tile NBUF - 1 ahead (past the end, the last tile again: never
+        // computed, and the wait count stays exact) and computes.
+#pragma unroll
+        for (int t = 0; t < NBUF - 1; ++t)
+            issue(rec_of(t), t);
+        int4 rn = rec_of(NBUF - 1);
+        for (int k = 0; k < n; ++k) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPT * (NBUF - 2)));
+            __builtin_amdgcn_s_barrier();
+            issue(rn, (k + NBUF - 1) % NBUF);
+            rn = rec_of(k + NBUF);
+            compute_tile(k % NBUF);
         }
-        if (kk < n)
-            compute_tile(A);
-        if (kk + 1 < n)
-            compute_tile(B);
+        // the copies issued past the last tile land before the wave moves on
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
 
     // Split entries: count this wave's partial in; the last of an entry's
@@ -857,27 +923,63 @@ hipError_t launch_raw(const void *kernel, dim3 grid, dim3 block, size_t lds, voi
     return hipLaunchKernel(kernel, grid, block, params, lds, stream);
 }
 
-template <int D>
-const void *run_kernel_d(int group) {
+template <int D, int NBUF>
+const void *run_kernel_dn(int group) {
     switch (group) {
-    case 1: return reinterpret_cast<const void *>(&run_kernel<D, 1>);
-    case 2: return reinterpret_cast<const void *>(&run_kernel<D, 2>);
-    case 3: return reinterpret_cast<const void *>(&run_kernel<D, 3>);
-    case 4: return reinterpret_cast<const void *>(&run_kernel<D, 4>);
-    case 5: return reinterpret_cast<const void *>(&run_kernel<D, 5>);
-    case 6: return reinterpret_cast<const void *>(&run_kernel<D, 6>);
-    case 7: return reinterpret_cast<const void *>(&run_kernel<D, 7>);
-    case 8: return reinterpret_cast<const void *>(&run_kernel<D, 8>);
+    case 1: return reinterpret_cast<const void *>(&run_kernel<D, 1, NBUF>);
+    case 2: return reinterpret_cast<const void *>(&run_kernel<D, 2, NBUF>);
+    case 3: return reinterpret_cast<const void *>(&run_kernel<D, 3, NBUF>);
+    case 4: return reinterpret_cast<const void *>(&run_kernel<D, 4, NBUF>);
+    case 5: return reinterpret_cast<const void *>(&run_kernel<D, 5, NBUF>);
+    case 6: return reinterpret_cast<const void *>(&run_kernel<D, 6, NBUF>);
+    case 7: return reinterpret_cast<const void *>(&run_kernel<D, 7, NBUF>);
+    case 8: return reinterpret_cast<const void *>(&run_kernel<D, 8, NBUF>);
     default: return nullptr;
     }
 }
 
-const void *run_kernel_ptr(int head_dim, int group) {
+template <int D>
+const void *run_kernel_d(int group, int nbuf) {
+    switch (nbuf) {
+    case 2: return run_kernel_dn<D, 2>(group);
+    case 3: return run_kernel_dn<D, 3>(group);
+    case 4: return run_kernel_dn<D, 4>(group);
+    default: return nullptr;
+    }
+}
+
+const void *run_kernel_ptr(int head_dim, int group, int nbuf) {
     if (head_dim == 64)
-        return run_kernel_d<64>(group);
+        return run_kernel_d<64>(group, nbuf);
     if (head_dim == 128)
-        return run_kernel_d<128>(group);
+        return run_kernel_d<128>(group, nbuf);
     return nullptr;
+}
+
+// LDS bytes of one staging buffer: K and V rows of a tile for nw heads, and
+// the q rows of their query heads.
+size_t stage_buffer_bytes(int nw, int head_dim, int group) {
+    const size_t qi = ((size_t)group * head_dim * 2 + 1023) / 1024;
+    return (size_t)2 * kTileTokens * nw * head_dim * 2 + (size_t)nw * qi * 1024;
+}
+
+// Staging depth (buffers) and LDS bytes of the decode kernel on the current
+// device: as deep as LDS allows, up to 4.
+hipError_t stage_shape(int head_dim, int group, int num_kv_heads, int *nbuf, size_t *lds) {
+    int dev = 0, max_lds = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess)
+        err = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (err != hipSuccess)
+        return err;
+    const size_t buf = stage_buffer_bytes(group_waves(num_kv_heads), head_dim, group);
+    int n = (int)((size_t)max_lds / buf);
+    n = n > 4 ? 4 : n;
+    if (n < 2)
+        return hipErrorInvalidValue;
+    *nbuf = n;
+    *lds = buf * (size_t)n;
+    return hipSuccess;
 }
 
 }  // namespace
@@ -889,22 +991,31 @@ hipError_t launch_append(const AppendArgs &a, int batch, hipStream_t stream) {
                       dim3(256), 0, params, stream);
 }
 
-bool run_supported(int head_dim, int group) { return run_kernel_ptr(head_dim, group) != nullptr; }
+bool run_supported(int head_dim, int group) {
+    return run_kernel_ptr(head_dim, group, 2) != nullptr;
+}
 
 hipError_t balanced_blocks(int head_dim, int group, int num_kv_heads, int *blocks) {
-    const void *k = run_kernel_ptr(head_dim, group);
+    int nbuf = 0;
+    size_t lds = 0;
+    hipError_t err = stage_shape(head_dim, group, num_kv_heads, &nbuf, &lds);
+    if (err != hipSuccess)
+        return err;
+    const void *k = run_kernel_ptr(head_dim, group, nbuf);
     if (k == nullptr)
         return hipErrorInvalidValue;
     int dev = 0, cus = 0, per_cu = 0;
-    hipError_t err = hipGetDevice(&dev);
+    err = hipGetDevice(&dev);
     if (err == hipSuccess)
         err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int waves = group_waves(num_kv_heads);
     if (err == hipSuccess)
-        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64 * waves, 0);
+        err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err == hipSuccess)
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64 * waves, lds);
     if (err != hipSuccess)
         return err;
-    const int head_groups = (num_kv_heads + waves - 1) / waves;
+    const int head_groups = num_kv_heads / waves;
     if (per_cu < 1)
         per_cu = 1;
     if (cus > kMaxComputeUnits)
@@ -931,16 +1042,24 @@ hipError_t launch_plan(const PlanArgs &a, hipStream_t stream) {
 
 hipError_t launch_run(const RunArgs &a, const int32_t *blocks, const int32_t *ent,
                       int num_blocks, int head_dim, int group, hipStream_t stream) {
-    const void *k = run_kernel_ptr(head_dim, group);
+    int nbuf = 0;
+    size_t lds = 0;
+    hipError_t err = stage_shape(head_dim, group, a.num_kv_heads, &nbuf, &lds);
+    if (err != hipSuccess)
+        return err;
+    const void *k = run_kernel_ptr(head_dim, group, nbuf);
     if (k == nullptr)
         return hipErrorInvalidValue;
+    err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess)
+        return err;
     RunArgs args = a;
     const int4 *bp = reinterpret_cast<const int4 *>(blocks);
     const int4 *ep = reinterpret_cast<const int4 *>(ent);
     void *params[] = {&args, &bp, &ep};
     const int waves = group_waves(a.num_kv_heads);
-    const unsigned head_groups = (unsigned)((a.num_kv_heads + waves - 1) / waves);
-    return launch_raw(k, dim3((unsigned)num_blocks, head_groups), dim3(64 * waves), 0, params,
+    const unsigned head_groups = (unsigned)(a.num_kv_heads / waves);
+    return launch_raw(k, dim3((unsigned)num_blocks, head_groups), dim3(64 * waves), lds, params,
                       stream);
 }
 

@@ -101,12 +101,18 @@ constexpr int kMaxChunkPages = 1 << 16;
 constexpr int kMaxComputeUnits = 320;
 constexpr int kMaxWavesPerCU = 32;
 constexpr int kMaxKvHeads = 16;
-// A decode workgroup has one wave per KV head, at most 8; more heads use more
+// A decode workgroup has one wave per KV head of its head group; groups are
+// the largest divisor of the head count up to 8 heads, so every group is full
+// (the workgroup's waves all take the same barriers), and more heads use more
 // workgroups along the grid's y axis.
 constexpr int kMaxWavesPerGroup = 8;
 
 inline int group_waves(int num_kv_heads) {
-    return num_kv_heads < kMaxWavesPerGroup ? num_kv_heads : kMaxWavesPerGroup;
+    for (int w = num_kv_heads < kMaxWavesPerGroup ? num_kv_heads : kMaxWavesPerGroup; w > 1;
+         --w)
+        if (num_kv_heads % w == 0)
+            return w;
+    return 1;
 }
 
 inline int64_t balanced_blocks_bound(int num_kv_heads) {
