@@ -80,6 +80,7 @@ Layout make_layout(const pkv_cache_desc_t &d, int32_t num_qo_heads, int32_t batc
     }
     p.off_ent = align256((int64_t)batch * d.num_kv_heads * 4);
     p.off_blocks = p.off_ent + align256((int64_t)batch * 16);
+    block_ints4 += pkv::kMaxStageBuffers;   // records read ahead past the last block
     p.off_part_o = p.off_blocks + align256(block_ints4 * 16);
     const int64_t rows = p.slots * num_qo_heads;
     p.off_part_lse = p.off_part_o + align256(rows * d.head_dim * 4);

@@ -52,6 +52,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -449,9 +451,21 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
 // them; the kernel waits for them itself (s_waitcnt vmcnt with the number of
 // copies issued after the tile's, a lower bound, so the wait is never short).
 //
-// Lane layout in compute: lane = rg * LPR + j owns elements [8j, 8j + 8) of
-// rows rg + RG * i (i < RPL) of each tile, for K and for V, and accumulates
-// the G query heads' outputs of those elements over its rows.
+// Lane layout in compute.  A row of the tile (one token of one head, D
+// elements) is spread over LPR lanes, 8 for G <= 4 query heads per KV head
+// and 16 for more (D = 128), so the wave holds RG = 64 / LPR rows at a time
+// and each lane RPL = 8 / RG rows of a tile.  Lane = r * LPR + j holds rows
+// r + RG i and, of each, the 8-element chunks j + LPR c (c < NC =
+// D / (8 LPR)) of K and of V: the LPR lanes of a row read 16 * LPR
+// contiguous bytes, so the LDS reads are conflict-free.  A row's score is
+// summed over its lanes in DPP steps.  The lane accumulates the G query
+// heads' outputs of its elements over its rows.  The running maximum of a
+// query head is the same in all row groups (when a raise is due it is taken
+// over the whole tile), so at the end of a segment the row groups' sums are
+// simply added, by a reduce-scatter that leaves each lane a distinct share of
+// the G x D outputs to write.  Eight lanes per row halve the DPP steps and
+// the exponentials of sixteen; sixteen keep the accumulators of G > 4 heads
+// within the registers of two waves per SIMD.
 
 // s_waitcnt immediate for "at most n vector memory operations outstanding"
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at
@@ -469,19 +483,85 @@ __device__ __forceinline__ void copy_to_lds(const void *base, uint32_t off, uint
                  : "memory");
 }
 
+// v[i] of a wave-uniform array for a lane-varying i < N.  The candidates go
+// through scalar registers first: a selection among plain loads of v would be
+// folded into one load from a computed address, which would force v (and the
+// caller's array) out of registers into scratch memory.
+template <int N>
+__device__ __forceinline__ float pick_uniform(const float (&v)[N], int i) {
+    float r = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v[0])));
+#pragma unroll
+    for (int t = 1; t < N; ++t) {
+        const float c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v[t])));
+        r = i == t ? c : r;
+    }
+    return r;
+}
+
+// x of lane ^ DIST (DIST = 8, 16 or 32) for every lane.
+template <int DIST>
+__device__ __forceinline__ float partner_lane(float x, int lane) {
+    if constexpr (DIST == 8) {
+        return dpp<0x128>(x);   // row_ror:8 = lane ^ 8 within 16
+    } else if constexpr (DIST == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        return __uint_as_float((lane & 16) ? r[0] : r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        return __uint_as_float((lane & 32) ? r[0] : r[1]);
+    }
+}
+
+// Stores n (8, 4, 2 or 1) consecutive outputs as bf16.
+template <int N>
+__device__ __forceinline__ void store_bf16(uint16_t *p, const float *v, float s) {
+    if constexpr (N == 8) {
+        store16(p, make_uint4(pack_bf16x2(v[0] * s, v[1] * s), pack_bf16x2(v[2] * s, v[3] * s),
+                              pack_bf16x2(v[4] * s, v[5] * s), pack_bf16x2(v[6] * s, v[7] * s)));
+    } else if constexpr (N == 4) {
+        *reinterpret_cast<uint2 *>(p) =
+            make_uint2(pack_bf16x2(v[0] * s, v[1] * s), pack_bf16x2(v[2] * s, v[3] * s));
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(v[0] * s, v[1] * s);
+    } else {
+        *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[0] * s));
+    }
+}
+
+// Stores n (8, 4, 2 or 1) consecutive fp32 partial outputs at byte offset off.
+template <int N>
+__device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                              const float *v, float s) {
+    if constexpr (N >= 4) {
+#pragma unroll
+        for (int q = 0; q < N; q += 4)
+            store4_coherent(r, off + 4 * q, v[q] * s, v[q + 1] * s, v[q + 2] * s, v[q + 3] * s);
+    } else {
+#pragma unroll
+        for (int q = 0; q < N; ++q)
+            store1_coherent(r, off + 4 * q, v[q] * s);
+    }
+}
+
 template <int D, int G, int NBUF>
 __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     RunArgs a, const int4 *__restrict__ blocks, const int4 *__restrict__ ent) {
-    constexpr int LPR = D / 8;                 // lanes per row
-    constexpr int RG = 64 / LPR;               // row groups
+    constexpr int LPR = (D == 128 && G > 4) ? 16 : 8;   // lanes per row
+    constexpr int RG = 64 / LPR;               // row groups: rows the wave holds at once
     constexpr int RPL = kTileTokens / RG;      // rows per lane per tile
+    constexpr int NC = D / (8 * LPR);          // 8-element chunks per lane and row
+    constexpr int V = G * NC * 8 / RG;         // outputs per lane after the reduce-scatter
+    constexpr int HPR = (G + RG - 1) / RG;     // heads per row group in merges and lse
     constexpr int IPW = D / 64;                // copies per wave per tile half (K or V)
     constexpr int IPT = 2 * IPW;               // copies per wave per tile
     constexpr int QB = G * D * 2;              // q bytes of one KV head's query heads
     constexpr int QI = (QB + 1023) / 1024;     // copies for them
+    static_assert(NC >= 1 && RPL >= 1 && V >= 1, "unsupported head_dim");
     extern __shared__ uint4 smem[];
     const int lane = threadIdx.x & 63;
-    const int rg = lane / LPR;
+    const int rg = lane / LPR;                 // row group of this lane
     const int j = lane % LPR;
     const int nw = blockDim.x >> 6;            // waves = KV heads of the group
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -489,9 +569,9 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     const int h = h0 + w;
     const bool fused = a.k_new != nullptr;
     const int hq0 = h * G;
-    const int col = h * D + j * 8;             // element offset of this lane within a token row
+    const int col = h * D + j * 8;             // element of this lane's chunk 0 in a token row
 
-    // LDS buffer b: K rows [8][nw][D], V rows [8][nw][D], then per wave QI KiB of q
+    // LDS buffer b: K rows [8][nw][D], V rows, then per wave QI KiB of q
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
     const uint32_t part_bytes = (uint32_t)(kTileTokens * nw * D * 2);
     const uint32_t buf_bytes = 2 * part_bytes + (uint32_t)(nw * QI * 1024);
@@ -502,38 +582,66 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     const __amdgpu_buffer_rsrc_t ro = partial_rsrc(a.part_o, a.part_o_bytes);
     const __amdgpu_buffer_rsrc_t rl = partial_rsrc(a.part_lse, a.part_lse_bytes);
     const int4 *blk = blocks + (int64_t)blockIdx.x * a.block_stride;
+    // the header and the first NBUF records load together (the block region
+    // is padded, so they are in bounds even past a short block's records)
     const int n = blk[0].x;
+    int4 rec0[NBUF];
+#pragma unroll
+    for (int t = 0; t < NBUF; ++t)
+        rec0[t] = blk[1 + t];
 
-    uint32_t qv[G][4];        // q of the entry being computed, 8 bf16 per head
-    float m[G], l[G], acc[G][8];
+    uint32_t qv[G][NC][4];    // q of the entry being computed
+    float m[G], l[G], acc[G][NC][8];
     int pend0 = -1, pend1 = -1;   // entries whose partial this wave wrote
 
-    // Rows of heads hq0 + g for g = rg, rg + RG, ... are written by row group rg.
-    auto write_rows = [&](int b, int slot, bool whole) {
+    // Writes this lane's share of a finished segment: the outputs (whole
+    // entry) or the partial outputs and base-2 lse of slot `slot`.  u[t] is
+    // the total of value r * V + t of the lane's flattened [G][NC][8]
+    // accumulators; lt[g] is head g's sum of weights.
+    auto write_rows = [&](int b, int slot, bool whole, const float (&u)[V],
+                          const float (&lt)[G]) {
+        float inv[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (g % RG != rg)
-                continue;
-            const int hq = hq0 + g;
-            const float inv = 1.f / l[g];
-            if (whole) {
-                uint4 v;
-                v.x = pack_bf16x2(acc[g][0] * inv, acc[g][1] * inv);
-                v.y = pack_bf16x2(acc[g][2] * inv, acc[g][3] * inv);
-                v.z = pack_bf16x2(acc[g][4] * inv, acc[g][5] * inv);
-                v.w = pack_bf16x2(acc[g][6] * inv, acc[g][7] * inv);
-                store16(a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8, v);
-                if (a.lse != nullptr && j == 0)
-                    a.lse[(int64_t)b * a.num_qo_heads + hq] = (m[g] + log2_fast(l[g])) * kLn2;
-            } else {
-                const uint32_t prow = (uint32_t)slot * a.num_qo_heads + hq;
-                const uint32_t ob = (prow * D + j * 8) * 4;
-                store4_coherent(ro, ob, acc[g][0] * inv, acc[g][1] * inv, acc[g][2] * inv,
-                                acc[g][3] * inv);
-                store4_coherent(ro, ob + 16, acc[g][4] * inv, acc[g][5] * inv,
-                                acc[g][6] * inv, acc[g][7] * inv);
-                if (j == 0)
-                    store1_coherent(rl, prow * 4, m[g] + log2_fast(l[g]));
+        for (int g = 0; g < G; ++g)
+            inv[g] = 1.f / lt[g];
+        const int64_t orow = (int64_t)b * a.num_qo_heads + hq0;    // output row of head 0
+        const uint32_t prow = (uint32_t)slot * a.num_qo_heads + hq0;
+        // one run of N values starting at flattened value f
+        auto put = [&](auto nv, int f, const float *v) {
+            constexpr int N = decltype(nv)::value;
+            const int k = f >> 3;
+            const int g = k / NC;
+            const int e = ((j + LPR * (k % NC)) << 3) + (f & 7);   // element within the head
+            const float s = pick_uniform<G>(inv, g);
+            if (whole)
+                store_bf16<N>(a.out + (orow + g) * D + e, v, s);
+            else
+                store_partial<N>(ro, ((prow + g) * D + e) * 4, v, s);
+        };
+        if constexpr (V % 8 == 0) {
+#pragma unroll
+            for (int q = 0; q < V; q += 8)
+                put(std::integral_constant<int, 8>{}, rg * V + q, u + q);
+        } else if constexpr (8 % V == 0) {
+            put(std::integral_constant<int, V>{}, rg * V, u);
+        } else {
+#pragma unroll
+            for (int t = 0; t < V; ++t)
+                put(std::integral_constant<int, 1>{}, rg * V + t, u + t);
+        }
+        if (j == 0) {
+#pragma unroll
+            for (int t = 0; t < HPR; ++t) {
+                const int g = rg + RG * t;
+                if (g >= G)
+                    break;
+                const float lse2 = pick_uniform<G>(m, g) + log2_fast(pick_uniform<G>(lt, g));
+                if (whole) {
+                    if (a.lse != nullptr)
+                        a.lse[orow + g] = lse2 * kLn2;
+                } else {
+                    store1_coherent(rl, (prow + g) * 4, lse2);
+                }
             }
         }
     };
@@ -620,9 +728,10 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             }
         };
 
-        // LDS in 16-byte units: this lane's K row i of a buffer, its q rows
-        const int kunit = (rg * nw + w) * (D / 8) + j;       // row rg, head w, unit j
-        const int rstep = RG * nw * (D / 8);                  // next row of the lane
+        // LDS in 16-byte units: this lane's chunk 0 of its first K row (row
+        // rg, head w, unit j), the step to its next row, its q chunk 0
+        const int kunit = (rg * nw + w) * (D / 8) + j;
+        const int rstep = RG * nw * (D / 8);
         const int part_units = (int)(part_bytes / 16);
         const int buf_units = (int)(buf_bytes / 16);
         const int qunit = (2 * part_bytes + w * QI * 1024) / 16 + j;
@@ -636,74 +745,83 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             const uint4 *sb = smem + buf * buf_units;
             if (info & kInfoSegFirst) {
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const uint4 v = sb[qunit + g * (D / 8)];
-                    qv[g][0] = v.x;
-                    qv[g][1] = v.y;
-                    qv[g][2] = v.z;
-                    qv[g][3] = v.w;
-                }
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) {
+                        const uint4 v = sb[qunit + g * (D / 8) + LPR * c];
+                        qv[g][c][0] = v.x;
+                        qv[g][c][1] = v.y;
+                        qv[g][c][2] = v.z;
+                        qv[g][c][3] = v.w;
+                    }
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     m[g] = kMInit;
                     l[g] = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[g][e] = 0.f;
+                    for (int c = 0; c < NC; ++c)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[g][c][e] = 0.f;
                 }
             }
             const int ntok = (info & kInfoNtokMask) + 1;
             const int nr = (info >> kInfoNewRowShift) & (kTileTokens - 1);
-            uint4 kx[RPL], vx[RPL];
+            uint4 kx[RPL][NC], vx[RPL][NC];
 #pragma unroll
-            for (int i = 0; i < RPL; ++i) {
-                kx[i] = sb[kunit + i * rstep];
-                vx[i] = sb[part_units + kunit + i * rstep];
-            }
-            // q.k: RPL x G independent dot products, then their row sums
-            // step by step across all of them
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    kx[i][c] = sb[kunit + i * rstep + LPR * c];
+                    vx[i][c] = sb[part_units + kunit + i * rstep + LPR * c];
+                }
+            // q.k: RPL x G independent dot products over the lane's chunks,
+            // then their row sums step by step across all of them
             float d[RPL][G];
 #pragma unroll
-            for (int i = 0; i < RPL; ++i)
+            for (int c = 0; c < NC; ++c) {
 #pragma unroll
-                for (int g = 0; g < G; ++g)
-                    d[i][g] = dot2_bf16(qv[g][0], kx[i].x, 0.f);
+                for (int i = 0; i < RPL; ++i)
 #pragma unroll
-            for (int i = 0; i < RPL; ++i)
+                    for (int g = 0; g < G; ++g)
+                        d[i][g] = dot2_bf16(qv[g][c][0], kx[i][c].x, c == 0 ? 0.f : d[i][g]);
 #pragma unroll
-                for (int g = 0; g < G; ++g)
-                    d[i][g] = dot2_bf16(qv[g][1], kx[i].y, d[i][g]);
+                for (int i = 0; i < RPL; ++i)
 #pragma unroll
-            for (int i = 0; i < RPL; ++i)
+                    for (int g = 0; g < G; ++g)
+                        d[i][g] = dot2_bf16(qv[g][c][1], kx[i][c].y, d[i][g]);
 #pragma unroll
-                for (int g = 0; g < G; ++g)
-                    d[i][g] = dot2_bf16(qv[g][2], kx[i].z, d[i][g]);
+                for (int i = 0; i < RPL; ++i)
 #pragma unroll
-            for (int i = 0; i < RPL; ++i)
+                    for (int g = 0; g < G; ++g)
+                        d[i][g] = dot2_bf16(qv[g][c][2], kx[i][c].z, d[i][g]);
 #pragma unroll
-                for (int g = 0; g < G; ++g)
-                    d[i][g] = dot2_bf16(qv[g][3], kx[i].w, d[i][g]);
+                for (int i = 0; i < RPL; ++i)
 #pragma unroll
-            for (int i = 0; i < RPL; ++i)
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-                    d[i][g] += dpp<0xB1>(d[i][g]);
+                    for (int g = 0; g < G; ++g)
+                        d[i][g] = dot2_bf16(qv[g][c][3], kx[i][c].w, d[i][g]);
+            }
 #pragma unroll
             for (int i = 0; i < RPL; ++i)
 #pragma unroll
                 for (int g = 0; g < G; ++g)
-                    d[i][g] += dpp<0x4E>(d[i][g]);
+                    d[i][g] += dpp<0xB1>(d[i][g]);    // quad_perm [1,0,3,2]: lane ^ 1
 #pragma unroll
             for (int i = 0; i < RPL; ++i)
 #pragma unroll
                 for (int g = 0; g < G; ++g)
-                    d[i][g] += dpp<0x141>(d[i][g]);
+                    d[i][g] += dpp<0x4E>(d[i][g]);    // quad_perm [2,3,0,1]: lane ^ 2
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    d[i][g] += dpp<0x141>(d[i][g]);   // row_half_mirror: 7 - lane within 8
             if constexpr (LPR == 16) {
 #pragma unroll
                 for (int i = 0; i < RPL; ++i)
 #pragma unroll
                     for (int g = 0; g < G; ++g)
-                        d[i][g] += dpp<0x140>(d[i][g]);
+                        d[i][g] += dpp<0x140>(d[i][g]);   // row_mirror: 15 - lane within 16
             }
             if (ntok < kTileTokens) {
                 // rows past the tile's last token (they re-read its first row,
@@ -715,48 +833,60 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
 #pragma unroll
                         for (int g = 0; g < G; ++g)
                             d[i][g] = -INFINITY;
-                        vx[i] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+                        for (int c = 0; c < NC; ++c)
+                            vx[i][c] = make_uint4(0u, 0u, 0u, 0u);
                     }
             }
-            // Lazy maximum (log2 units, scores d * scale_log2): raise m only
-            // when a score passes it by more than kTau.
+            // Lazy maximum (log2 units, scores d * scale_log2): raised only
+            // when some row's score passes it by more than kTau, then to the
+            // maximum over the tile's rows, in every row group alike.
             const float c2 = a.scale_log2;
-            float dmax[G];
             bool raise = false;
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                dmax[g] = d[0][g];
+            for (int i = 0; i < RPL; ++i)
 #pragma unroll
-                for (int i = 1; i < RPL; ++i)
-                    dmax[g] = fmaxf(dmax[g], d[i][g]);
-                raise |= fmaf(dmax[g], c2, -m[g]) > kTau;
-            }
-            if (raise) {
+                for (int g = 0; g < G; ++g)
+                    raise |= fmaf(d[i][g], c2, -m[g]) > kTau;
+            if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const float sm = dmax[g] * c2;
-                    const bool up = sm - m[g] > kTau;
-                    const float mn = up ? sm : m[g];
-                    const float alpha = up ? exp2_fast(m[g] - mn) : 1.f;
-                    m[g] = mn;
-                    l[g] *= alpha;
+                    float dm = d[0][g];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[g][e] *= alpha;
+                    for (int i = 1; i < RPL; ++i)
+                        dm = fmaxf(dm, d[i][g]);
+                    const float sm = group_max<RG>(dm) * c2;
+                    if (sm - m[g] > kTau) {
+                        const float alpha = exp2_fast(m[g] - sm);
+                        m[g] = sm;
+                        l[g] *= alpha;
+#pragma unroll
+                        for (int c = 0; c < NC; ++c)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                acc[g][c][e] *= alpha;
+                    }
                 }
             }
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
-                const uint4 v = vx[i];
-                const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                                     bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+                float p[G];
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const float p = exp2_fast(fmaf(d[i][g], c2, -m[g]));   // 0 for masked rows
-                    l[g] += p;
+                    p[g] = exp2_fast(fmaf(d[i][g], c2, -m[g]));   // 0 for masked rows
+                    l[g] += p[g];
+                }
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+                for (int c = 0; c < NC; ++c) {
+                    const uint4 v = vx[i][c];
+                    const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y),
+                                         bf16_hi(v.y), bf16_lo(v.z), bf16_hi(v.z),
+                                         bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[g][c][e] = fmaf(p[g], vf[e], acc[g][c][e]);
                 }
             }
             if (fused && (info & kInfoHasNew)) {
@@ -767,24 +897,60 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
 #pragma unroll
                 for (int i = 0; i < RPL; ++i)
                     if (rg + RG * i == nr) {
-                        store16(dst, kx[i]);
-                        store16(dst + a.half_stride, vx[i]);
+#pragma unroll
+                        for (int c = 0; c < NC; ++c) {
+                            store16(dst + 8 * LPR * c, kx[i][c]);
+                            store16(dst + 8 * LPR * c + a.half_stride, vx[i][c]);
+                        }
                     }
             }
             if (info & kInfoSegLast) {
-                // merge the row groups; every lane ends with the totals
+                // Add the row groups: the weight sums in every lane, the
+                // accumulators by halving steps across lanes 32, 16 and (for
+                // 8 row groups) 8 apart: at each step a lane keeps the lower
+                // half of its values when its lane bit is 0 and the upper half
+                // when it is 1, and adds the partner's same half.  Lane (r, j)
+                // ends with the totals of values r * V .. r * V + V - 1.
+                float lt[G];
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const float mw = group_max<RG>(m[g]);
-                    const float f = exp2_fast(m[g] - mw);
-                    l[g] = group_sum<RG>(l[g] * f);
+                for (int g = 0; g < G; ++g)
+                    lt[g] = group_sum<RG>(l[g]);
+                constexpr int T = G * NC * 8;
+                float x4[T / 2];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[g][e] = group_sum<RG>(acc[g][e] * f);
-                    m[g] = mw;
+                for (int i = 0; i < T / 2; ++i) {
+                    constexpr int S = 8 * NC;
+                    const int i2 = i + T / 2;
+                    // permlane32_swap(a, b): lanes 0-31 get a of lanes 32-63 in
+                    // b's place, lanes 32-63 get b of lanes 0-31 in a's place
+                    const auto r = __builtin_amdgcn_permlane32_swap(
+                        __float_as_uint(acc[i / S][(i % S) / 8][i % 8]),
+                        __float_as_uint(acc[i2 / S][(i2 % S) / 8][i2 % 8]), false, false);
+                    x4[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+                }
+                float x2[T / 4];
+#pragma unroll
+                for (int i = 0; i < T / 4; ++i) {
+                    const auto r = __builtin_amdgcn_permlane16_swap(
+                        __float_as_uint(x4[i]), __float_as_uint(x4[i + T / 4]), false, false);
+                    x2[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+                }
+                float u[V];
+                if constexpr (RG == 8) {
+                    const bool odd = (rg & 1) != 0;
+#pragma unroll
+                    for (int i = 0; i < V; ++i) {
+                        const float keep = odd ? x2[i + V] : x2[i];
+                        const float send = odd ? x2[i] : x2[i + V];
+                        u[i] = keep + dpp<0x128>(send);   // row_ror:8 = lane ^ 8 within 16
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < V; ++i)
+                        u[i] = x2[i];
                 }
                 const bool whole = (info & kInfoSegWhole) != 0;
-                write_rows(rec.z, rec.w, whole);
+                write_rows(rec.z, rec.w, whole, u, lt);
                 if (!whole) {
                     if (pend0 < 0)
                         pend0 = rec.z;
@@ -798,10 +964,14 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
         // for its tile, passes the barrier, refills the freed buffer with the
         // tile NBUF - 1 ahead (past the end, the last tile again: never
         // computed, and the wait count stays exact) and computes.
+        int4 rt = rec0[0];
 #pragma unroll
-        for (int t = 0; t < NBUF - 1; ++t)
-            issue(rec_of(t), t);
-        int4 rn = rec_of(NBUF - 1);
+        for (int t = 0; t < NBUF - 1; ++t) {
+            if (t > 0 && t < n)
+                rt = rec0[t];
+            issue(rt, t);
+        }
+        int4 rn = NBUF - 1 < n ? rec0[NBUF - 1] : rt;
         for (int k = 0; k < n; ++k) {
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPT * (NBUF - 2)));
             __builtin_amdgcn_s_barrier();
@@ -813,80 +983,126 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
 
-    // Split entries: count this wave's partial in; the last of an entry's
-    // segments to arrive merges them all and resets the counter.
+    // Split entries: count this wave's partials in (both at once); the last
+    // of an entry's segments to arrive merges them all and resets the counter.
     if (pend0 >= 0) {
         // this wave's partial stores are complete (written through) before
-        // its arrival is counted; the compiler may not move them past here
+        // its arrivals are counted; the compiler may not move them past here
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        int32_t *cnt0 = a.cnt + (int64_t)pend0 * a.num_kv_heads + h;
+        int32_t *cnt1 = a.cnt + (int64_t)(pend1 >= 0 ? pend1 : pend0) * a.num_kv_heads + h;
+        int old = 0;
+        if (lane == 0 || (lane == 1 && pend1 >= 0))
+            old = __hip_atomic_fetch_add(lane == 0 ? cnt0 : cnt1, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+        const int old0 = __builtin_amdgcn_readlane(old, 0);
+        const int old1 = __builtin_amdgcn_readlane(old, 1);
+        // Merge layout: with one head per row group, heads are rounded up to
+        // GP (a power of two) and the RG / GP groups of GP row groups (parts)
+        // take every P-th segment, eight segments' loads in flight per part;
+        // the parts' states are then combined across lanes.
+        constexpr int GP = G == 1 ? 1 : G == 2 ? 2 : G <= 4 ? 4 : 8;
+        constexpr int P = HPR == 1 ? RG / GP : 1;
+        constexpr int SPR = 8;                        // segments per round and part
+        const int part = HPR == 1 ? rg / GP : 0;
+        const int gb = HPR == 1 ? rg % GP : rg;
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int b = p == 0 ? pend0 : pend1;
+        for (int pp = 0; pp < 2; ++pp) {
+            const int b = pp == 0 ? pend0 : pend1;
             if (b < 0)
                 break;
-            int32_t *counter = a.cnt + (int64_t)b * a.num_kv_heads + h;
-            int old = 0;
-            if (lane == 0)
-                old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-            old = __builtin_amdgcn_readfirstlane(old);
             const int4 e = ent[b];
-            if (old != e.y - 1)
+            if ((pp == 0 ? old0 : old1) != e.y - 1)
                 continue;
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            // row group rg merges query heads hq0 + rg, hq0 + rg + RG, ...: all
-            // lanes load at once, one round of loads per RG heads
 #pragma unroll
-            for (int g0 = 0; g0 < G; g0 += RG) {
-                const int g = g0 + rg;
-                if (g >= G)
-                    break;
-                const int hq = hq0 + g;
+            for (int t = 0; t < HPR; ++t) {
+                const int g = gb + RG * t;
+                const bool act = g < G;
+                const int hq = hq0 + (act ? g : 0);
                 const uint32_t pl = ((uint32_t)e.x * a.num_qo_heads + hq) * 4;
                 const uint32_t po = (((uint32_t)e.x * a.num_qo_heads + hq) * D + j * 8) * 4;
                 const uint32_t sl = (uint32_t)a.num_qo_heads * 4;
                 const uint32_t so = (uint32_t)a.num_qo_heads * D * 4;
-                float mm = kMInit, sum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                for (int s0 = 0; s0 < e.y; s0 += 4) {
-                    float lv[4];
-                    float4 ov[4][2];
+                float mm = kMInit, sum = 0.f, o[NC][8];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const uint32_t s = (uint32_t)min(s0 + u, e.y - 1);
+                for (int c = 0; c < NC; ++c)
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        o[c][q] = 0.f;
+                const int ns = act ? e.y : 0;
+                for (int s0 = part; s0 < ns; s0 += SPR * P) {
+                    float lv[SPR];
+                    float4 ov[SPR][NC][2];
+#pragma unroll
+                    for (int u = 0; u < SPR; ++u) {
+                        const uint32_t s = (uint32_t)min(s0 + u * P, ns - 1);
                         lv[u] = load1_coherent(rl, pl + s * sl);
-                        ov[u][0] = load4_coherent(ro, po + s * so);
-                        ov[u][1] = load4_coherent(ro, po + s * so + 16);
+#pragma unroll
+                        for (int c = 0; c < NC; ++c) {
+                            const uint32_t oc = po + s * so + 32 * LPR * c;
+                            ov[u][c][0] = load4_coherent(ro, oc);
+                            ov[u][c][1] = load4_coherent(ro, oc + 16);
+                        }
                     }
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        if (s0 + u >= e.y)
+                    for (int u = 0; u < SPR; ++u) {
+                        if (s0 + u * P >= ns)
                             break;
                         const float mn = fmaxf(mm, lv[u]);
                         const float al = exp2_fast(mm - mn);
-                        const float w = exp2_fast(lv[u] - mn);
-                        sum = fmaf(sum, al, w);
-                        const float ou[8] = {ov[u][0].x, ov[u][0].y, ov[u][0].z, ov[u][0].w,
-                                             ov[u][1].x, ov[u][1].y, ov[u][1].z, ov[u][1].w};
+                        const float wt = exp2_fast(lv[u] - mn);
+                        sum = fmaf(sum, al, wt);
 #pragma unroll
-                        for (int t = 0; t < 8; ++t)
-                            o[t] = fmaf(w, ou[t], o[t] * al);
+                        for (int c = 0; c < NC; ++c) {
+                            const float ou[8] = {ov[u][c][0].x, ov[u][c][0].y, ov[u][c][0].z,
+                                                 ov[u][c][0].w, ov[u][c][1].x, ov[u][c][1].y,
+                                                 ov[u][c][1].z, ov[u][c][1].w};
+#pragma unroll
+                            for (int q = 0; q < 8; ++q)
+                                o[c][q] = fmaf(wt, ou[q], o[c][q] * al);
+                        }
                         mm = mn;
                     }
                 }
-                const float inv = 1.f / sum;
-                uint4 w;
-                w.x = pack_bf16x2(o[0] * inv, o[1] * inv);
-                w.y = pack_bf16x2(o[2] * inv, o[3] * inv);
-                w.z = pack_bf16x2(o[4] * inv, o[5] * inv);
-                w.w = pack_bf16x2(o[6] * inv, o[7] * inv);
-                store16(a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8, w);
-                if (a.lse != nullptr && j == 0)
-                    a.lse[(int64_t)b * a.num_qo_heads + hq] = (mm + log2_fast(sum)) * kLn2;
+                // combine the parts: butterfly over the lane bits that select
+                // the part (all lanes take part; idle ones hold empty states)
+                auto combine = [&](auto dist_c) {
+                    constexpr int DIST = decltype(dist_c)::value;
+                    const float m2 = partner_lane<DIST>(mm, lane);
+                    const float s2 = partner_lane<DIST>(sum, lane);
+                    const float mn = fmaxf(mm, m2);
+                    const float a1 = exp2_fast(mm - mn);
+                    const float a2 = exp2_fast(m2 - mn);
+                    sum = sum * a1 + s2 * a2;
+#pragma unroll
+                    for (int c = 0; c < NC; ++c)
+#pragma unroll
+                        for (int q = 0; q < 8; ++q)
+                            o[c][q] = o[c][q] * a1 + partner_lane<DIST>(o[c][q], lane) * a2;
+                    mm = mn;
+                };
+                if constexpr (P > 1)
+                    combine(std::integral_constant<int, LPR * GP>{});
+                if constexpr (P > 2)
+                    combine(std::integral_constant<int, 2 * LPR * GP>{});
+                if constexpr (P > 4)
+                    combine(std::integral_constant<int, 4 * LPR * GP>{});
+                if (act && part == 0) {
+                    const float inv = 1.f / sum;
+                    uint16_t *orow = a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8;
+#pragma unroll
+                    for (int c = 0; c < NC; ++c)
+                        store_bf16<8>(orow + 8 * LPR * c, o[c], inv);
+                    if (a.lse != nullptr && j == 0)
+                        a.lse[(int64_t)b * a.num_qo_heads + hq] = (mm + log2_fast(sum)) * kLn2;
+                }
             }
             if (lane == 0)
-                __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(pp == 0 ? cnt0 : cnt1, 0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
@@ -897,12 +1113,16 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
         if (e.y >= 0)
             continue;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (g % RG != rg)
-                continue;
+        for (int t = 0; t < HPR; ++t) {
+            const int g = rg + RG * t;
+            if (g >= G)
+                break;
             const int hq = hq0 + g;
-            store16(a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8,
-                    make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u));
+            uint16_t *orow = a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                store16(orow + 8 * LPR * c,
+                        make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u));
             if (a.lse != nullptr && j == 0)
                 a.lse[(int64_t)b * a.num_qo_heads + hq] = __builtin_nanf("");
         }
@@ -910,8 +1130,12 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             const int64_t src = ((int64_t)b * a.num_kv_heads + h) * D + j * 8;
             uint16_t *dst = a.cache_w + (int64_t)e.z * a.page_stride +
                             (int64_t)e.w * a.row_stride + col;
-            store16(dst, load16(a.k_new + src));
-            store16(dst + a.half_stride, load16(a.v_new + src));
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                store16(dst + 8 * LPR * c, load16(a.k_new + src + 8 * LPR * c));
+                store16(dst + 8 * LPR * c + a.half_stride,
+                        load16(a.v_new + src + 8 * LPR * c));
+            }
         }
     }
 }
@@ -974,7 +1198,7 @@ hipError_t stage_shape(int head_dim, int group, int num_kv_heads, int *nbuf, siz
         return err;
     const size_t buf = stage_buffer_bytes(group_waves(num_kv_heads), head_dim, group);
     int n = (int)((size_t)max_lds / buf);
-    n = n > 4 ? 4 : n;
+    n = n > kMaxStageBuffers ? kMaxStageBuffers : n;
     if (n < 2)
         return hipErrorInvalidValue;
     *nbuf = n;

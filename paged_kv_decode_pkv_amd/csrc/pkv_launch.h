@@ -106,6 +106,10 @@ constexpr int kMaxKvHeads = 16;
 // (the workgroup's waves all take the same barriers), and more heads use more
 // workgroups along the grid's y axis.
 constexpr int kMaxWavesPerGroup = 8;
+// The decode kernel stages tiles through a ring of at most this many LDS
+// buffers and reads that many records of its block at once, before it knows
+// how many the block has: the block region is padded by as many records.
+constexpr int kMaxStageBuffers = 4;
 
 inline int group_waves(int num_kv_heads) {
     for (int w = num_kv_heads < kMaxWavesPerGroup ? num_kv_heads : kMaxWavesPerGroup; w > 1;
