@@ -75,8 +75,9 @@ Layout make_layout(const pkv_cache_desc_t &d, int32_t num_qo_heads, int32_t batc
     } else {
         const int64_t wb = pkv::balanced_blocks_bound(d.num_kv_heads);
         p.slots = wb + batch;
-        // W blocks of 1 + ceil(max_tiles / W) records each, for any W <= wb
-        block_ints4 = p.max_tiles + 2 * wb;
+        // W blocks of 1 + balanced_capacity records each, for any W <= wb:
+        // at most W (1 + max_tiles / W + 1 + 2 batch / W + 1 + 2) in total
+        block_ints4 = p.max_tiles + 2 * (int64_t)batch + 5 * wb;
     }
     p.off_ent = align256((int64_t)batch * d.num_kv_heads * 4);
     p.off_blocks = p.off_ent + align256((int64_t)batch * 16);
@@ -133,7 +134,7 @@ int prepare(const pkv_cache_desc_t &desc, int32_t num_qo_heads, int32_t batch,
                                               &num_blocks);
         if (err != hipSuccess)
             return hip_status(err);
-        block_stride = (int)(1 + (lay.max_tiles + num_blocks - 1) / num_blocks);
+        block_stride = (int)(1 + pkv::balanced_capacity(lay.max_tiles, batch, num_blocks));
     }
     return PKV_OK;
 }

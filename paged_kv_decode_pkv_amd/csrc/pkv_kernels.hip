@@ -286,46 +286,94 @@ __device__ __forceinline__ int run_of_block(int w, int W) {
     return (W % 8 == 0) ? (w % 8) * (W / 8) + w / 8 : w;
 }
 
-// Number of runs among W_eff equal runs of T tiles that tile range [s, s + t)
-// touches, and the first of them (run r covers [T r / W_eff, T (r+1) / W_eff)).
-__device__ __forceinline__ void runs_of(int64_t s, int64_t t, int64_t T, int64_t weff,
-                                       int &first, int &count) {
-    const int lo = (int)(((s + 1) * weff - 1) / T);
-    const int hi = (int)(((s + t) * weff - 1) / T);
-    first = lo;
-    count = hi - lo + 1;
-}
+// Balanced mode splits cost, not tiles.  Every entry's tiles are laid end to
+// end on a cost axis: the entry first takes kEntryCost units for the work of
+// starting and ending a segment (q rows, the first tile's rescale, the merge
+// of row groups and the stores), then kTileCost units per tile; the axis of
+// total length C is cut into W_eff runs [C r / W_eff, C (r+1) / W_eff), and a
+// tile belongs to the run holding its start.  Short entries thus count for
+// more than their tiles, and a run of several entries gets fewer tiles.
+
+struct CostAxis {
+    const int *start;   // [batch + 1] tile prefix sums
+    const int *nz;      // [batch + 1] prefix counts of entries with tiles
+    int batch;
+    int64_t T, C, weff;
+    // cost position where entry b begins
+    __device__ int64_t entry_pos(int b) const {
+        return kTileCost * (int64_t)start[b] + kEntryCost * (int64_t)nz[b];
+    }
+    // start position of tile i of entry b
+    __device__ int64_t tile_pos(int b, int64_t i) const {
+        return entry_pos(b) + kEntryCost + kTileCost * i;
+    }
+    // run holding position p: the largest r with floor(C r / W_eff) <= p
+    __device__ int run_of(int64_t p) const { return (int)(((p + 1) * weff - 1) / C); }
+    // number of tiles (of all entries) that start before position x
+    __device__ int64_t tiles_before(int64_t x) const {
+        if (x >= C)
+            return T;
+        int lo = 0, hi = batch - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (entry_pos(mid) <= x)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        const int64_t in = x - entry_pos(lo) - kEntryCost;
+        const int64_t i = in <= 0 ? 0 : (in + kTileCost - 1) / kTileCost;
+        const int64_t nt = start[lo + 1] - start[lo];
+        return start[lo] + (i < nt ? i : nt);
+    }
+};
 
 __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
-    extern __shared__ int s_start[];   // balanced: [batch + 1] tile prefix sums
+    // balanced: [batch + 1] tile prefix sums, then [batch + 1] prefix counts
+    // of entries with tiles
+    extern __shared__ int s_start[];
     __shared__ int s_wave[17];
     const bool fixed = a.chunk_tiles > 0;
+    int *s_nz = s_start + a.batch + 1;
     int64_t T = 0;
+    const int W = a.num_blocks;
+    CostAxis ax{s_start, s_nz, a.batch, 0, 0, 1};
     if (!fixed) {
         const int nthreads = blockDim.x;
         const int per = (a.batch + nthreads - 1) / nthreads;
         const int e0 = min(a.batch, (int)threadIdx.x * per);
         const int e1 = min(a.batch, e0 + per);
-        int local = 0;
+        int local = 0, localz = 0;
         for (int e = e0; e < e1; ++e) {
             const int t = entry_shape(a, e).tiles;
             s_start[e] = t;
             local += t;
+            localz += t > 0;
         }
-        int total = 0;
+        int total = 0, totalz = 0;
         int run = block_exclusive_scan(local, s_wave, total);
+        __syncthreads();   // s_wave is reused
+        int runz = block_exclusive_scan(localz, s_wave, totalz);
         for (int e = e0; e < e1; ++e) {
             const int t = s_start[e];
             s_start[e] = run;
+            s_nz[e] = runz;
             run += t;
+            runz += t > 0;
         }
-        if (threadIdx.x == 0)
+        if (threadIdx.x == 0) {
             s_start[a.batch] = total;
+            s_nz[a.batch] = totalz;
+        }
         __syncthreads();
         T = total;
+        ax.T = T;
+        ax.C = kTileCost * (int64_t)total + kEntryCost * (int64_t)totalz;
+        // runs no shorter than a tile, so no run inside an entry's tiles is empty
+        const int64_t cap = ax.C / kTileCost;
+        ax.weff = cap < 1 ? 1 : (cap < W ? cap : W);
     }
-    const int W = a.num_blocks;
-    const int64_t weff = fixed ? W : (T < W ? T : W);
+    const int64_t weff = fixed ? W : ax.weff;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
     int4 *blocks = reinterpret_cast<int4 *>(a.blocks);
@@ -347,10 +395,9 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
                 d.x = b * a.max_chunks;
                 d.y = (e.tiles + a.chunk_tiles - 1) / a.chunk_tiles;
             } else {
-                int first, count;
-                runs_of(s_start[b], e.tiles, T, weff, first, count);
+                const int first = ax.run_of(ax.tile_pos(b, 0));
                 d.x = first + b;
-                d.y = count;
+                d.y = ax.run_of(ax.tile_pos(b, e.tiles - 1)) - first + 1;
             }
         }
         ent[b] = d;
@@ -381,8 +428,8 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
         } else {
             run = run_of_block(w, W);
             if (run < weff) {
-                g0 = T * run / weff;
-                g1 = T * (run + 1) / weff;
+                g0 = ax.tiles_before(ax.C * run / weff);
+                g1 = ax.tiles_before(ax.C * (run + 1) / weff);
                 ntiles = (int)(g1 - g0);
             }
         }
@@ -408,8 +455,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
             seg_first = gk == (g0 > s0 ? g0 : s0);
             const int64_t s1 = s0 + e.tiles;
             seg_last = gk == (g1 < s1 ? g1 : s1) - 1;
-            int first;
-            runs_of(s0, e.tiles, T, weff, first, nseg);
+            nseg = ax.run_of(ax.tile_pos(b, e.tiles - 1)) - ax.run_of(ax.tile_pos(b, 0)) + 1;
             slot = run + b;
         }
         const int pl = lt / a.tiles_per_page;
@@ -448,8 +494,12 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
 // of the tile where the segment starts.
 //
 // The copies are written as inline assembly, so the compiler does not track
-// them; the kernel waits for them itself (s_waitcnt vmcnt with the number of
-// copies issued after the tile's, a lower bound, so the wait is never short).
+// them; the kernel waits for them itself.  Vector memory operations of a wave
+// complete in issue order, so a tile has landed once no more are outstanding
+// than were issued after its copies: the copies of later tiles and their q
+// rows, and the output, partial and append stores of the tiles computed
+// since.  The kernel counts all of them (stores as a lower bound: a count too
+// low only waits longer) and waits for exactly that many.
 //
 // Lane layout in compute.  A row of the tile (one token of one head, D
 // elements) is spread over LPR lanes, 8 for G <= 4 query heads per KV head
@@ -471,6 +521,21 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at
 // their maximum, i.e. not waited for).
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kMaxVmWait = 24;   // largest wait count the decode loop uses
+
+// s_waitcnt vmcnt(min(n, N)) for a wave-uniform n >= 0 (the immediate must be
+// a constant: a chain of scalar compares picks it).
+template <int N>
+__device__ __forceinline__ void wait_vm_at_most(int n) {
+    if constexpr (N == 0) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    } else {
+        if (n >= N)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+        else
+            wait_vm_at_most<N - 1>(n);
+    }
+}
 
 // One direct-to-LDS copy: 16 bytes from each lane's global address to LDS at
 // lds + 16 * lane (lds is wave-uniform and goes through M0).
@@ -559,6 +624,10 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     constexpr int QB = G * D * 2;              // q bytes of one KV head's query heads
     constexpr int QI = (QB + 1023) / 1024;     // copies for them
     static_assert(NC >= 1 && RPL >= 1 && V >= 1, "unsupported head_dim");
+    // Vector memory stores a segment end issues (outputs and lse): they count
+    // in vmcnt like the copies, so the waits below include them.
+    constexpr int kOutStores = V % 8 == 0 ? V / 8 : (8 % V == 0 ? 1 : V);
+    constexpr int kPartStores = V % 8 == 0 ? V / 4 : (8 % V == 0 ? (V >= 4 ? V / 4 : V) : V);
     extern __shared__ uint4 smem[];
     const int lane = threadIdx.x & 63;
     const int rg = lane / LPR;                 // row group of this lane
@@ -669,19 +738,26 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
         // The records of the tiles in the ring: record of buffer b in lane b
         // of four registers.
         int ring_x = 0, ring_y = 0, ring_z = 0, ring_w = 0;
+        // Vector memory operations issued so far (modulo 2^32), and in lane b
+        // of ring_ops their number right after the copies of buffer b's tile:
+        // a tile has landed once at most ops - ring_ops[b] are outstanding.
+        uint32_t ops = 0;
+        int ring_ops = 0;
 
         // This wave's share of the copies of tile `rec` into LDS buffer `buf`:
         // the q rows first (when a segment starts there), then IPW 1-KiB runs
         // of K rows and as many of V rows; the fused append's new row comes
         // from k_new / v_new.
         auto issue = [&](const int4 rec, int buf) {
+            const int info = rec.y;
+            ops += ((info & kInfoSegFirst) ? QI : 0) + IPT;
             if (lane == buf) {
                 ring_x = rec.x;
                 ring_y = rec.y;
                 ring_z = rec.z;
                 ring_w = rec.w;
+                ring_ops = (int)ops;
             }
-            const int info = rec.y;
             const int ntok = (info & kInfoNtokMask) + 1;
             const int slot0 = (info >> kInfoSlotShift) & kInfoSlotMask;
             const uint32_t bb = lds0 + (uint32_t)buf * buf_bytes;
@@ -903,6 +979,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                             store16(dst + 8 * LPR * c + a.half_stride, vx[i][c]);
                         }
                     }
+                ops += 2 * NC;   // one row of the tile holds the new token
             }
             if (info & kInfoSegLast) {
                 // Add the row groups: the weight sums in every lane, the
@@ -951,6 +1028,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                 }
                 const bool whole = (info & kInfoSegWhole) != 0;
                 write_rows(rec.z, rec.w, whole, u, lt);
+                ops += whole ? kOutStores + (a.lse != nullptr ? HPR : 0) : kPartStores + HPR;
                 if (!whole) {
                     if (pend0 < 0)
                         pend0 = rec.z;
@@ -973,7 +1051,13 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
         }
         int4 rn = NBUF - 1 < n ? rec0[NBUF - 1] : rt;
         for (int k = 0; k < n; ++k) {
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPT * (NBUF - 2)));
+            // tile k has landed: at most the operations issued after its
+            // copies (NBUF - 2 tiles, their q rows, the stores since) remain
+            const int after = (int)(ops - (uint32_t)__builtin_amdgcn_readlane(ring_ops, k % NBUF));
+            if (after == IPT * (NBUF - 2))
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPT * (NBUF - 2)));
+            else
+                wait_vm_at_most<kMaxVmWait>(after);
             __builtin_amdgcn_s_barrier();
             issue(rn, (k + NBUF - 1) % NBUF);
             rn = rec_of(k + NBUF);
@@ -1259,7 +1343,7 @@ hipError_t launch_plan(const PlanArgs &a, hipStream_t stream) {
     const int64_t work = items > other ? items : other;
     int64_t grid = (work + 255) / 256;
     grid = grid < 1 ? 1 : (grid > 1024 ? 1024 : grid);
-    const size_t lds = a.chunk_tiles > 0 ? 0 : sizeof(int) * ((size_t)a.batch + 1);
+    const size_t lds = a.chunk_tiles > 0 ? 0 : 2 * sizeof(int) * ((size_t)a.batch + 1);
     return launch_raw(reinterpret_cast<const void *>(&plan_kernel), dim3((unsigned)grid),
                       dim3(256), lds, params, stream);
 }

@@ -119,6 +119,19 @@ inline int group_waves(int num_kv_heads) {
     return 1;
 }
 
+// Cost units of the balanced split: a tile, and the extra work of an entry
+// (starting and ending a segment: about one and a half tiles of decode time).
+constexpr int kTileCost = 4;
+constexpr int kEntryCost = 6;
+
+// Records one balanced block may receive: a run of the cost axis holds at most
+// (kTileCost T + kEntryCost Z) / (kTileCost W) + 1 tiles for T tiles in Z
+// entries and W >= 1 runs, and the last two terms round that up.
+inline int64_t balanced_capacity(int64_t max_tiles, int64_t batch, int64_t blocks) {
+    return (max_tiles + blocks - 1) / blocks +
+           (kEntryCost * batch + kTileCost * blocks - 1) / (kTileCost * blocks) + 2;
+}
+
 inline int64_t balanced_blocks_bound(int num_kv_heads) {
     const int waves = group_waves(num_kv_heads);
     return ((int64_t)kMaxComputeUnits * kMaxWavesPerCU + waves - 1) / waves;
