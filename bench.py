@@ -44,8 +44,8 @@ def parse():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--chunk-pages", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="approximate CPU work of the oracle baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="approximate CPU time (summed over threads) of the oracle sample")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--separate", action="store_true",
@@ -358,48 +358,40 @@ def check_sample(spec, table, cache, Q, KN, VN, out, lse, torch):
 def cpu_baseline(spec, table, cache, Q, KN, VN, torch, seconds):
     """The fp64 oracle (as it stands) on a bounded sample of the workload.
 
-    Sample: layer 0, every query head of a seeded random subset of active
-    entries sized to roughly ``seconds`` of single-thread work; the entries run
-    concurrently on a thread pool (the oracle releases the GIL).  The rate uses
-    the same algorithmic-byte formula as the GPU figure."""
+    Sample: whole layers of the step, in order, every query head of every
+    active entry, until about ``seconds`` of CPU time (summed over the worker
+    threads) have been spent or the step's layers run out; the entries of a
+    layer run concurrently on a thread pool (the oracle releases the GIL).
+    Only the oracle calls are timed, not the copies of the pages to the host.
+    The rate uses the same algorithmic-byte formula as the GPU figure."""
     import oracle
     hq, hkv, d = spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
-    rng = np.random.default_rng(11)
-    act = rng.permutation(np.flatnonzero(table.active))
-    # calibrate: one short entry, all heads
-    e0 = int(act[0])
-    mini, ip, ix, ll = _host_entries(table, cache[0], [e0], torch)
-    q0 = _u16(Q[0])[[e0]]
-    t = time.perf_counter()
-    oracle.decode(mini, 0, q0, ip, ix, ll, spec.sm_scale)
-    per_token = (time.perf_counter() - t) / float(table.lengths[e0])
     threads = max(1, min(16, os.cpu_count() or 1))
-    budget_tokens = seconds * threads / max(per_token, 1e-9)
-    chosen, tot = [], 0
-    for e in act:
-        if tot >= budget_tokens and chosen:
-            break
-        chosen.append(int(e))
-        tot += int(table.lengths[e])
-    qh = _u16(Q[0])
-    kn, vn = _u16(KN[0]), _u16(VN[0])
-    jobs = []
-    for e in chosen:
-        mini, ip, ix, ll = _host_entries(table, cache[0], [e], torch)
-        jobs.append((mini, ip, ix, ll, qh[[e]], kn[[e]], vn[[e]]))
+    act = [int(e) for e in np.flatnonzero(table.active)]
 
     def run(job):
         mini, ip, ix, ll, q, k, v = job
         oracle.append(mini, 0, k, v, ip, ix, ll)
         oracle.decode(mini, 0, q, ip, ix, ll, spec.sm_scale)
 
-    t = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(run, jobs))
-    dt = time.perf_counter() - t
-    lens = table.lengths[chosen]
-    nbytes = (int(lens.sum()) * 2 * hkv * d * 2 + len(chosen) * hq * d * 2 * 2
-              + len(chosen) * hq * 4 + len(chosen) * 2 * 2 * hkv * d * 2)
+    dt, layers, nbytes = 0.0, 0, 0
+    lens = table.lengths[act]
+    per_layer = (int(lens.sum()) * 2 * hkv * d * 2 + len(act) * hq * d * 2 * 2
+                 + len(act) * hq * 4 + len(act) * 2 * 2 * hkv * d * 2)
+    for layer in range(spec.num_layers):
+        if dt * threads >= seconds:
+            break
+        qh, kn, vn = _u16(Q[layer]), _u16(KN[layer]), _u16(VN[layer])
+        jobs = []
+        for e in act:
+            mini, ip, ix, ll = _host_entries(table, cache[layer], [e], torch)
+            jobs.append((mini, ip, ix, ll, qh[[e]], kn[[e]], vn[[e]]))
+        t = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(run, jobs))
+        dt += time.perf_counter() - t
+        layers += 1
+        nbytes += per_layer
     cpu_model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -410,10 +402,10 @@ def cpu_baseline(spec, table, cache, Q, KN, VN, torch, seconds):
         pass
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"layer 0, all {hq} query heads of {len(chosen)} of "
-                      f"{int(table.active.sum())} active entries ({int(lens.sum())} "
-                      f"tokens), append + fp64 decode, {dt:.1f} s on {threads} threads",
-            "decode_rows_per_s_equiv": round(len(chosen) / dt / spec.num_layers, 3),
+            "sample": f"layers 0-{layers - 1} of {spec.num_layers}, all {hq} query heads of "
+                      f"all {len(act)} active entries ({int(lens.sum())} tokens per layer), "
+                      f"append + fp64 decode, {dt:.2f} s on {threads} threads",
+            "decode_rows_per_s_equiv": round(len(act) * layers / dt / spec.num_layers, 3),
             "cpu_model": cpu_model}
 
 

@@ -93,8 +93,8 @@ int pkv_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
  * pkv_run, pkv_decode and pkv_append_decode need for these arguments.  Host
  * function; no device work.  Returns 0 for arguments the calls would reject.
  * The size grows with batch * max_pages_per_req (16 bytes per 8-token tile
- * of that many pages, for the step's plan) plus fp32 partial rows for split
- * entries.
+ * of that many pages, for the step's plan, plus a few records per entry and
+ * per workgroup) plus fp32 partial rows for split entries.
  */
 size_t pkv_decode_workspace_size(pkv_cache_desc_t desc, int32_t num_qo_heads,
                                  int32_t batch, int32_t max_pages_per_req,
@@ -110,10 +110,11 @@ size_t pkv_decode_workspace_size(pkv_cache_desc_t desc, int32_t num_qo_heads,
  * Work is split into runs of tokens whose partial (output, lse) pairs are
  * merged by log-sum-exp, the way partial attentions are merged on the
  * "Supported Models" page (LTX-2.5 notes):
- *   kv_chunk_pages == 0  balanced: the tokens of the whole batch are shared
- *                        evenly among the workgroups the GPU holds at once.
- *                        Fastest; the split, so the last bits of a row, can
- *                        change with the rest of the batch.
+ *   kv_chunk_pages == 0  balanced: the work of the whole batch (its tokens,
+ *                        plus a fixed cost per entry) is shared evenly among
+ *                        the workgroups the GPU holds at once.  Fastest; the
+ *                        split, so the last bits of a row, can change with
+ *                        the rest of the batch.
  *   kv_chunk_pages  > 0  fixed: each entry is cut into runs of
  *                        kv_chunk_pages pages; a row is bit-identical
  *                        whatever else is in the batch.  At most 65536.

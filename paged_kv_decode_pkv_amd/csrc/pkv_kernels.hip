@@ -10,27 +10,23 @@
 //    per byte for a GQA group of g query heads), so it uses the vector ALUs,
 //    not MFMA.  q.k runs on v_dot2_f32_bf16 straight from the bf16 words: no
 //    conversion of K, exact products, fp32 accumulation.
-//  * A workgroup has one wavefront per KV head.  Every lane owns 16 bytes
-//    (8 elements) of a token row: D/8 lanes cover one row of one head and the
-//    wave covers 64/(D/8) rows per load, so an 8-token tile is one or two
-//    16-byte loads per lane for K and as many for V, and the workgroup reads
-//    each tile's K rows and V rows of all heads as contiguous runs.
-//  * Partial dot products of a row are summed with DPP row operations (no
-//    LDS); the row groups of a wave keep separate online-softmax states in the
-//    exp2 domain and are merged only at the end of a segment, with the gfx950
-//    cross-row lane swaps (v_permlane16_swap, v_permlane32_swap).
+//  * A workgroup has one wavefront per KV head of its head group.  Each 8-token
+//    tile's K rows and V rows of all those heads are copied from HBM into LDS
+//    with direct-to-LDS loads, 1 KiB of one contiguous run per instruction,
+//    through a ring of buffers a few tiles deep; every wave then reads its own
+//    head's rows.
+//  * A token row of a head is spread over 8 (or 16) lanes; row sums are DPP
+//    row operations, row groups are combined with the gfx950 cross-row lane
+//    swaps (v_permlane16_swap, v_permlane32_swap).
 //  * The running maximum is raised only when a score passes it by more than
 //    kTau (log2 units); between raises nothing is rescaled.
-//  * Loads run two tiles ahead in registers (three rotating buffers); the
-//    tiles' page ids come from the step's plan through the scalar cache, one
-//    record ahead of the loads, so no load ever waits on the page table.
 //
 // Work split.  The plan kernel walks the page table once per step (the table
 // is the same for every layer) and writes, per decode workgroup, the records
-// of its tiles.  Balanced mode (default): the tiles of all entries are laid
-// end to end and each of W workgroups (W = what the chip holds at once)
-// takes an equal run of them, so every compute unit streams the same number
-// of bytes; runs of neighbouring workgroup ids sit on different XCDs, so the
+// of its tiles.  Balanced mode (default): the work of all entries is laid end
+// to end (tiles, plus a fixed cost per entry for starting and ending it) and
+// each of W workgroups (W = what the chip holds at once) takes an equal run
+// of it; runs of neighbouring workgroup ids sit on different XCDs, so the
 // plan deals consecutive runs to one XCD.  Fixed mode: each entry is cut into
 // chunks of a fixed number of tiles, one workgroup each, so how an entry is
 // split depends only on its own length and its rows are bit-identical in any
