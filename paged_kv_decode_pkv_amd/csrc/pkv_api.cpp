@@ -84,8 +84,8 @@ Layout make_layout(const pkv_cache_desc_t &d, int32_t num_qo_heads, int32_t batc
     block_ints4 += pkv::kMaxStageBuffers;   // records read ahead past the last block
     p.off_part_o = p.off_blocks + align256(block_ints4 * 16);
     const int64_t rows = p.slots * num_qo_heads;
-    p.off_part_lse = p.off_part_o + align256(rows * d.head_dim * 4);
-    p.ws_bytes = p.off_part_lse + align256(rows * 4);
+    p.off_part_lse = p.off_part_o + align256(rows * d.head_dim * 2);
+    p.ws_bytes = p.off_part_lse + align256(rows * 8);
     return p;
 }
 
@@ -216,7 +216,7 @@ int prepare_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void
     a.v_new = static_cast<const uint16_t *>(v_new);
     a.out = static_cast<uint16_t *>(out);
     a.lse = lse;
-    a.part_o = reinterpret_cast<float *>(ws + lay.off_part_o);
+    a.part_o = reinterpret_cast<uint16_t *>(ws + lay.off_part_o);
     a.part_lse = reinterpret_cast<float *>(ws + lay.off_part_lse);
     a.part_o_bytes = lay.off_part_lse - lay.off_part_o;
     a.part_lse_bytes = lay.ws_bytes - lay.off_part_lse;

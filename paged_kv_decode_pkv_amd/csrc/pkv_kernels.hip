@@ -139,35 +139,70 @@ __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_lo
 // Partial rows cross workgroups (and XCDs, whose L2s are not coherent with
 // each other).  They are written and read through a buffer resource with the
 // device-scope cache policy (sc1): stores write through to the coherent
-// level and loads read from it, 16 bytes at a time, so no L2-wide writeback
-// or invalidate is needed around the arrival counter.  The resource's range
-// also bounds every access to the partial arrays.
+// level and loads read from it, so no L2-wide writeback or invalidate is
+// needed around the arrival counter.  The resource's range also bounds every
+// access to the partial arrays.
+//
+// A partial is stored compactly: its normalized outputs in fp16, scaled by a
+// power of two 2^-s chosen per (segment, KV head) so that the largest
+// magnitude is below 1 (no overflow for any finite input, 11 significant
+// bits), and per query head the pair {lse (base 2), s}.
 typedef int v4i_t __attribute__((ext_vector_type(4)));
+typedef int v2i_t __attribute__((ext_vector_type(2)));
 constexpr int kPolicyDevice = 16;   // sc1
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const float *base,
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const void *base,
                                                                int64_t bytes) {
     const int range = bytes < 0x7fffffff ? (int)bytes : 0x7fffffff;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, range,
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, range,
                                              0x00020000);
 }
-__device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off,
-                                                float a, float b, float c, float d) {
-    const v4i_t v = {__float_as_int(a), __float_as_int(b), __float_as_int(c),
-                     __float_as_int(d)};
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kPolicyDevice);
+__device__ __forceinline__ void store_b128_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                    uint4 v) {
+    const v4i_t x = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)off, 0, kPolicyDevice);
 }
-__device__ __forceinline__ void store1_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off,
-                                                float a) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(a), r, (int)off, 0, kPolicyDevice);
+__device__ __forceinline__ void store_b64_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                   uint32_t a, uint32_t b) {
+    const v2i_t x = {(int)a, (int)b};
+    __builtin_amdgcn_raw_buffer_store_b64(x, r, (int)off, 0, kPolicyDevice);
 }
-__device__ __forceinline__ float4 load4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+__device__ __forceinline__ void store_b32_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                   uint32_t a) {
+    __builtin_amdgcn_raw_buffer_store_b32((int)a, r, (int)off, 0, kPolicyDevice);
+}
+__device__ __forceinline__ void store_b16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                   uint16_t a) {
+    __builtin_amdgcn_raw_buffer_store_b16((short)a, r, (int)off, 0, kPolicyDevice);
+}
+__device__ __forceinline__ uint4 load_b128_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     const v4i_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kPolicyDevice);
-    return make_float4(__int_as_float(v.x), __int_as_float(v.y), __int_as_float(v.z),
-                       __int_as_float(v.w));
+    return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
 }
-__device__ __forceinline__ float load1_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kPolicyDevice));
+__device__ __forceinline__ float2 load_f2_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const v2i_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kPolicyDevice);
+    return make_float2(__int_as_float(v.x), __int_as_float(v.y));
+}
+
+// Adds 1 to *p at device scope and returns the old value in `old`, without the
+// compiler tracking it: the caller reads `old` only after its own wait for all
+// vector memory operations (a compiler-visible atomic whose result is used
+// later would make the compiler wait for every outstanding copy right away).
+__device__ __forceinline__ void atomic_inc_untracked(int32_t *p, int &old) {
+    asm volatile("global_atomic_add %0, %1, %2, off sc0" : "+v"(old) : "v"(p), "v"(1)
+                 : "memory");
+}
+
+// fp32 -> fp16 (round to nearest even), two values packed low-first, and back.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
 __device__ __forceinline__ uint4 load16(const uint16_t *p) {
@@ -591,19 +626,33 @@ __device__ __forceinline__ void store_bf16(uint16_t *p, const float *v, float s)
     }
 }
 
-// Stores n (8, 4, 2 or 1) consecutive fp32 partial outputs at byte offset off.
+// Stores n (8, 4, 2 or 1) consecutive partial outputs v[i] * s in fp16 at byte
+// offset off.
 template <int N>
 __device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                               const float *v, float s) {
-    if constexpr (N >= 4) {
-#pragma unroll
-        for (int q = 0; q < N; q += 4)
-            store4_coherent(r, off + 4 * q, v[q] * s, v[q + 1] * s, v[q + 2] * s, v[q + 3] * s);
+    if constexpr (N == 8) {
+        store_b128_coherent(r, off, make_uint4(pack_f16x2(v[0] * s, v[1] * s),
+                                               pack_f16x2(v[2] * s, v[3] * s),
+                                               pack_f16x2(v[4] * s, v[5] * s),
+                                               pack_f16x2(v[6] * s, v[7] * s)));
+    } else if constexpr (N == 4) {
+        store_b64_coherent(r, off, pack_f16x2(v[0] * s, v[1] * s), pack_f16x2(v[2] * s, v[3] * s));
+    } else if constexpr (N == 2) {
+        store_b32_coherent(r, off, pack_f16x2(v[0] * s, v[1] * s));
     } else {
-#pragma unroll
-        for (int q = 0; q < N; ++q)
-            store1_coherent(r, off + 4 * q, v[q] * s);
+        store_b16_coherent(r, off, __builtin_bit_cast(uint16_t, (_Float16)(v[0] * s)));
     }
+}
+
+// Maximum over all 64 lanes of a wave; every lane gets it.
+__device__ __forceinline__ float wave_max(float x, int lane) {
+    x = fmaxf(x, dpp<0xB1>(x));    // lane ^ 1
+    x = fmaxf(x, dpp<0x4E>(x));    // lane ^ 2
+    x = fmaxf(x, dpp<0x141>(x));   // row_half_mirror
+    x = fmaxf(x, dpp<0x140>(x));   // row_mirror
+    x = fmaxf(x, partner_lane<16>(x, lane));
+    return fmaxf(x, partner_lane<32>(x, lane));
 }
 
 template <int D, int G, int NBUF>
@@ -622,8 +671,9 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     static_assert(NC >= 1 && RPL >= 1 && V >= 1, "unsupported head_dim");
     // Vector memory stores a segment end issues (outputs and lse): they count
     // in vmcnt like the copies, so the waits below include them.
+    // (fp16 partial outputs take as many stores as bf16 outputs)
     constexpr int kOutStores = V % 8 == 0 ? V / 8 : (8 % V == 0 ? 1 : V);
-    constexpr int kPartStores = V % 8 == 0 ? V / 4 : (8 % V == 0 ? (V >= 4 ? V / 4 : V) : V);
+    constexpr int kPartStores = kOutStores;
     extern __shared__ uint4 smem[];
     const int lane = threadIdx.x & 63;
     const int rg = lane / LPR;                 // row group of this lane
@@ -658,11 +708,17 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     uint32_t qv[G][NC][4];    // q of the entry being computed
     float m[G], l[G], acc[G][NC][8];
     int pend0 = -1, pend1 = -1;   // entries whose partial this wave wrote
+    // The first partial of a block usually ends before the block's last tile;
+    // it signals its arrival at loop iteration sig_at, when its stores are
+    // known to be complete, and old0 keeps what its counter held then.
+    int sig_at = -1, old0 = 0;
+    bool signaled0 = false;
 
     // Writes this lane's share of a finished segment: the outputs (whole
-    // entry) or the partial outputs and base-2 lse of slot `slot`.  u[t] is
-    // the total of value r * V + t of the lane's flattened [G][NC][8]
-    // accumulators; lt[g] is head g's sum of weights.
+    // entry) or the partial of slot `slot` (fp16 outputs scaled by 2^-s, and
+    // per query head {base-2 lse, s}).  u[t] is the total of value r * V + t
+    // of the lane's flattened [G][NC][8] accumulators; lt[g] is head g's sum
+    // of weights.
     auto write_rows = [&](int b, int slot, bool whole, const float (&u)[V],
                           const float (&lt)[G]) {
         float inv[G];
@@ -671,28 +727,41 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             inv[g] = 1.f / lt[g];
         const int64_t orow = (int64_t)b * a.num_qo_heads + hq0;    // output row of head 0
         const uint32_t prow = (uint32_t)slot * a.num_qo_heads + hq0;
+        float nv[V];   // normalized outputs
+#pragma unroll
+        for (int t = 0; t < V; ++t)
+            nv[t] = u[t] * pick_uniform<G>(inv, ((rg * V + t) >> 3) / NC);
+        float sc = 1.f, sexp = 0.f;
+        if (!whole) {
+            float amax = 0.f;
+#pragma unroll
+            for (int t = 0; t < V; ++t)
+                amax = fmaxf(amax, fabsf(nv[t]));
+            const int e = __builtin_amdgcn_frexp_expf(wave_max(amax, lane));   // amax < 2^e
+            sc = __builtin_amdgcn_ldexpf(1.f, -e);
+            sexp = (float)e;
+        }
         // one run of N values starting at flattened value f
-        auto put = [&](auto nv, int f, const float *v) {
-            constexpr int N = decltype(nv)::value;
+        auto put = [&](auto nvc, int f, const float *v) {
+            constexpr int N = decltype(nvc)::value;
             const int k = f >> 3;
             const int g = k / NC;
             const int e = ((j + LPR * (k % NC)) << 3) + (f & 7);   // element within the head
-            const float s = pick_uniform<G>(inv, g);
             if (whole)
-                store_bf16<N>(a.out + (orow + g) * D + e, v, s);
+                store_bf16<N>(a.out + (orow + g) * D + e, v, 1.f);
             else
-                store_partial<N>(ro, ((prow + g) * D + e) * 4, v, s);
+                store_partial<N>(ro, ((prow + g) * D + e) * 2, v, sc);
         };
         if constexpr (V % 8 == 0) {
 #pragma unroll
             for (int q = 0; q < V; q += 8)
-                put(std::integral_constant<int, 8>{}, rg * V + q, u + q);
+                put(std::integral_constant<int, 8>{}, rg * V + q, nv + q);
         } else if constexpr (8 % V == 0) {
-            put(std::integral_constant<int, V>{}, rg * V, u);
+            put(std::integral_constant<int, V>{}, rg * V, nv);
         } else {
 #pragma unroll
             for (int t = 0; t < V; ++t)
-                put(std::integral_constant<int, 1>{}, rg * V + t, u + t);
+                put(std::integral_constant<int, 1>{}, rg * V + t, nv + t);
         }
         if (j == 0) {
 #pragma unroll
@@ -705,7 +774,8 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                     if (a.lse != nullptr)
                         a.lse[orow + g] = lse2 * kLn2;
                 } else {
-                    store1_coherent(rl, (prow + g) * 4, lse2);
+                    store_b64_coherent(rl, (prow + g) * 8, __float_as_uint(lse2),
+                                       __float_as_uint(sexp));
                 }
             }
         }
@@ -808,7 +878,8 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
         const int buf_units = (int)(buf_bytes / 16);
         const int qunit = (2 * part_bytes + w * QI * 1024) / 16 + j;
 
-        auto compute_tile = [&](int buf) {
+        auto compute_tile = [&](int k) {
+            const int buf = k % NBUF;
             const int4 rec = make_int4(__builtin_amdgcn_readlane(ring_x, buf),
                                        __builtin_amdgcn_readlane(ring_y, buf),
                                        __builtin_amdgcn_readlane(ring_z, buf),
@@ -1026,10 +1097,15 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                 write_rows(rec.z, rec.w, whole, u, lt);
                 ops += whole ? kOutStores + (a.lse != nullptr ? HPR : 0) : kPartStores + HPR;
                 if (!whole) {
-                    if (pend0 < 0)
+                    if (pend0 < 0) {
                         pend0 = rec.z;
-                    else
+                        // the copies of tile k + NBUF are issued after these
+                        // stores, so once that tile has landed they are done
+                        if (k + NBUF < n)
+                            sig_at = k + NBUF;
+                    } else {
                         pend1 = rec.z;
+                    }
                 }
             }
         };
@@ -1055,16 +1131,25 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             else
                 wait_vm_at_most<kMaxVmWait>(after);
             __builtin_amdgcn_s_barrier();
+            if (k == sig_at) {
+                // the first partial's stores are complete (tile k landed)
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                if (lane == 0)
+                    atomic_inc_untracked(a.cnt + (int64_t)pend0 * a.num_kv_heads + h, old0);
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                signaled0 = true;
+                ops += 1;
+            }
             issue(rn, (k + NBUF - 1) % NBUF);
             rn = rec_of(k + NBUF);
-            compute_tile(k % NBUF);
+            compute_tile(k);
         }
         // the copies issued past the last tile land before the wave moves on
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
 
-    // Split entries: count this wave's partials in (both at once); the last
-    // of an entry's segments to arrive merges them all and resets the counter.
+    // Split entries: count this wave's remaining partials in; the last of an
+    // entry's segments to arrive merges them all and resets the counter.
     if (pend0 >= 0) {
         // this wave's partial stores are complete (written through) before
         // its arrivals are counted; the compiler may not move them past here
@@ -1074,110 +1159,93 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
         int32_t *cnt0 = a.cnt + (int64_t)pend0 * a.num_kv_heads + h;
         int32_t *cnt1 = a.cnt + (int64_t)(pend1 >= 0 ? pend1 : pend0) * a.num_kv_heads + h;
         int old = 0;
-        if (lane == 0 || (lane == 1 && pend1 >= 0))
+        if ((lane == 0 && !signaled0) || (lane == 1 && pend1 >= 0))
             old = __hip_atomic_fetch_add(lane == 0 ? cnt0 : cnt1, 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
-        const int old0 = __builtin_amdgcn_readlane(old, 0);
-        const int old1 = __builtin_amdgcn_readlane(old, 1);
-        // Merge layout: with one head per row group, heads are rounded up to
-        // GP (a power of two) and the RG / GP groups of GP row groups (parts)
-        // take every P-th segment, eight segments' loads in flight per part;
-        // the parts' states are then combined across lanes.
-        constexpr int GP = G == 1 ? 1 : G == 2 ? 2 : G <= 4 ? 4 : 8;
-        constexpr int P = HPR == 1 ? RG / GP : 1;
-        constexpr int SPR = 8;                        // segments per round and part
-        const int part = HPR == 1 ? rg / GP : 0;
-        const int gb = HPR == 1 ? rg % GP : rg;
+        const int arr0 = __builtin_amdgcn_readlane(signaled0 ? old0 : old, 0);
+        const int arr1 = __builtin_amdgcn_readlane(old, 1);
+        // Merge: lane handles UPL units of 8 consecutive outputs of the KV
+        // head's G x D; all of a round's SR segments are loaded at once.
+        constexpr int DU = D / 8;                   // units per query head
+        constexpr int NU = G * DU;
+        constexpr int UPL = (NU + 63) / 64;
+        constexpr int SR = 24 / UPL;
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
             const int b = pp == 0 ? pend0 : pend1;
             if (b < 0)
                 break;
             const int4 e = ent[b];
-            if ((pp == 0 ? old0 : old1) != e.y - 1)
+            if ((pp == 0 ? arr0 : arr1) != e.y - 1)
                 continue;
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            const int ns = e.y;
+            uint32_t lo[UPL], oo[UPL];   // byte offsets in slot e.x: lse pair, outputs
+            float mm[UPL], zs[UPL], o[UPL][8];
 #pragma unroll
-            for (int t = 0; t < HPR; ++t) {
-                const int g = gb + RG * t;
-                const bool act = g < G;
-                const int hq = hq0 + (act ? g : 0);
-                const uint32_t pl = ((uint32_t)e.x * a.num_qo_heads + hq) * 4;
-                const uint32_t po = (((uint32_t)e.x * a.num_qo_heads + hq) * D + j * 8) * 4;
-                const uint32_t sl = (uint32_t)a.num_qo_heads * 4;
-                const uint32_t so = (uint32_t)a.num_qo_heads * D * 4;
-                float mm = kMInit, sum = 0.f, o[NC][8];
+            for (int i = 0; i < UPL; ++i) {
+                const int unit = min(lane + 64 * i, NU - 1);
+                const uint32_t row = (uint32_t)e.x * a.num_qo_heads + hq0 + unit / DU;
+                lo[i] = row * 8;
+                oo[i] = (row * D + (unit % DU) * 8) * 2;
+                mm[i] = kMInit;
+                zs[i] = 0.f;
 #pragma unroll
-                for (int c = 0; c < NC; ++c)
+                for (int q = 0; q < 8; ++q)
+                    o[i][q] = 0.f;
+            }
+            const uint32_t sl = (uint32_t)a.num_qo_heads * 8;       // slot stride, lse pairs
+            const uint32_t so = (uint32_t)a.num_qo_heads * D * 2;   // slot stride, outputs
+            for (int s0 = 0; s0 < ns; s0 += SR) {
+                float2 lv[SR][UPL];
+                uint4 ov[SR][UPL];
+                // only the segments that exist: device-scope loads of the
+                // same address are not merged, each one costs a full access
 #pragma unroll
-                    for (int q = 0; q < 8; ++q)
-                        o[c][q] = 0.f;
-                const int ns = act ? e.y : 0;
-                for (int s0 = part; s0 < ns; s0 += SPR * P) {
-                    float lv[SPR];
-                    float4 ov[SPR][NC][2];
+                for (int u = 0; u < SR; ++u) {
+                    const uint32_t s = (uint32_t)(s0 + u);
 #pragma unroll
-                    for (int u = 0; u < SPR; ++u) {
-                        const uint32_t s = (uint32_t)min(s0 + u * P, ns - 1);
-                        lv[u] = load1_coherent(rl, pl + s * sl);
-#pragma unroll
-                        for (int c = 0; c < NC; ++c) {
-                            const uint32_t oc = po + s * so + 32 * LPR * c;
-                            ov[u][c][0] = load4_coherent(ro, oc);
-                            ov[u][c][1] = load4_coherent(ro, oc + 16);
+                    for (int i = 0; i < UPL; ++i) {
+                        if (s0 + u < ns) {
+                            lv[u][i] = load_f2_coherent(rl, lo[i] + s * sl);
+                            ov[u][i] = load_b128_coherent(ro, oo[i] + s * so);
                         }
-                    }
-#pragma unroll
-                    for (int u = 0; u < SPR; ++u) {
-                        if (s0 + u * P >= ns)
-                            break;
-                        const float mn = fmaxf(mm, lv[u]);
-                        const float al = exp2_fast(mm - mn);
-                        const float wt = exp2_fast(lv[u] - mn);
-                        sum = fmaf(sum, al, wt);
-#pragma unroll
-                        for (int c = 0; c < NC; ++c) {
-                            const float ou[8] = {ov[u][c][0].x, ov[u][c][0].y, ov[u][c][0].z,
-                                                 ov[u][c][0].w, ov[u][c][1].x, ov[u][c][1].y,
-                                                 ov[u][c][1].z, ov[u][c][1].w};
-#pragma unroll
-                            for (int q = 0; q < 8; ++q)
-                                o[c][q] = fmaf(wt, ou[q], o[c][q] * al);
-                        }
-                        mm = mn;
                     }
                 }
-                // combine the parts: butterfly over the lane bits that select
-                // the part (all lanes take part; idle ones hold empty states)
-                auto combine = [&](auto dist_c) {
-                    constexpr int DIST = decltype(dist_c)::value;
-                    const float m2 = partner_lane<DIST>(mm, lane);
-                    const float s2 = partner_lane<DIST>(sum, lane);
-                    const float mn = fmaxf(mm, m2);
-                    const float a1 = exp2_fast(mm - mn);
-                    const float a2 = exp2_fast(m2 - mn);
-                    sum = sum * a1 + s2 * a2;
 #pragma unroll
-                    for (int c = 0; c < NC; ++c)
+                for (int u = 0; u < SR; ++u) {
+                    if (s0 + u >= ns)   // wave-uniform: absent segments cost nothing
+                        continue;
+#pragma unroll
+                    for (int i = 0; i < UPL; ++i) {
+                        // weight of the segment: 2^(lse - m); its stored
+                        // outputs carry a further factor 2^-s
+                        const float l2 = lv[u][i].x;
+                        const float mn = fmaxf(mm[i], l2);
+                        const float al = exp2_fast(mm[i] - mn);
+                        const float wz = exp2_fast(l2 - mn);
+                        const float wo = exp2_fast(l2 + lv[u][i].y - mn);
+                        zs[i] = fmaf(zs[i], al, wz);
+                        const uint4 v = ov[u][i];
+                        const float x[8] = {f16_lo(v.x), f16_hi(v.x), f16_lo(v.y), f16_hi(v.y),
+                                            f16_lo(v.z), f16_hi(v.z), f16_lo(v.w), f16_hi(v.w)};
 #pragma unroll
                         for (int q = 0; q < 8; ++q)
-                            o[c][q] = o[c][q] * a1 + partner_lane<DIST>(o[c][q], lane) * a2;
-                    mm = mn;
-                };
-                if constexpr (P > 1)
-                    combine(std::integral_constant<int, LPR * GP>{});
-                if constexpr (P > 2)
-                    combine(std::integral_constant<int, 2 * LPR * GP>{});
-                if constexpr (P > 4)
-                    combine(std::integral_constant<int, 4 * LPR * GP>{});
-                if (act && part == 0) {
-                    const float inv = 1.f / sum;
-                    uint16_t *orow = a.out + ((int64_t)b * a.num_qo_heads + hq) * D + j * 8;
+                            o[i][q] = fmaf(wo, x[q], o[i][q] * al);
+                        mm[i] = mn;
+                    }
+                }
+            }
 #pragma unroll
-                    for (int c = 0; c < NC; ++c)
-                        store_bf16<8>(orow + 8 * LPR * c, o[c], inv);
-                    if (a.lse != nullptr && j == 0)
-                        a.lse[(int64_t)b * a.num_qo_heads + hq] = (mm + log2_fast(sum)) * kLn2;
+            for (int i = 0; i < UPL; ++i) {
+                const int unit = lane + 64 * i;
+                if (unit < NU) {
+                    const int hq = hq0 + unit / DU;
+                    const float inv = 1.f / zs[i];
+                    store_bf16<8>(a.out + ((int64_t)b * a.num_qo_heads + hq) * D + (unit % DU) * 8,
+                                  o[i], inv);
+                    if (a.lse != nullptr && unit % DU == 0)
+                        a.lse[(int64_t)b * a.num_qo_heads + hq] = (mm[i] + log2_fast(zs[i])) * kLn2;
                 }
             }
             if (lane == 0)
@@ -1247,7 +1315,6 @@ const void *run_kernel_d(int group, int nbuf) {
     switch (nbuf) {
     case 2: return run_kernel_dn<D, 2>(group);
     case 3: return run_kernel_dn<D, 3>(group);
-    case 4: return run_kernel_dn<D, 4>(group);
     default: return nullptr;
     }
 }

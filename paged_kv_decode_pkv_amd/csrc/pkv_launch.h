@@ -38,8 +38,10 @@ constexpr int kTileTokens = 8;
 //                                 per decode workgroup: a header {tiles, run,
 //                                 0, 0} and then one record per tile
 //                                 {page, info, entry, partial slot}
-//   part_o  fp32  [slots, Hq, D]  partial outputs of split entries
-//   part_lse fp32 [slots, Hq]     their log-sum-exp, base 2
+//   part_o  fp16  [slots, Hq, D]  partial outputs of split entries, each
+//                                 (slot, KV head) scaled by a power of two
+//                                 2^-s that keeps them below 1 in magnitude
+//   part_lse fp32 [slots, Hq, 2]  their log-sum-exp (base 2) and s
 // Bits of a record's info word:
 constexpr int kInfoNtokMask = 0x7;        // tokens in the tile - 1
 constexpr int kInfoSlotShift = 3;         // bits 3-11: page slot of the first token
@@ -77,8 +79,8 @@ struct RunArgs {
     const uint16_t *v_new;
     uint16_t *out;            // [batch, Hq, D] bf16
     float *lse;               // [batch, Hq] or null
-    float *part_o;
-    float *part_lse;
+    uint16_t *part_o;         // fp16 [slots, Hq, D], scaled by 2^-s
+    float *part_lse;          // [slots, Hq] pairs {base-2 lse, s}
     int64_t part_o_bytes;     // sizes of the two partial arrays
     int64_t part_lse_bytes;
     int32_t *cnt;
@@ -109,7 +111,7 @@ constexpr int kMaxWavesPerGroup = 8;
 // The decode kernel stages tiles through a ring of at most this many LDS
 // buffers and reads that many records of its block at once, before it knows
 // how many the block has: the block region is padded by as many records.
-constexpr int kMaxStageBuffers = 4;
+constexpr int kMaxStageBuffers = 3;
 
 inline int group_waves(int num_kv_heads) {
     for (int w = num_kv_heads < kMaxWavesPerGroup ? num_kv_heads : kMaxWavesPerGroup; w > 1;

@@ -44,13 +44,14 @@ def test_workspace_size():
     ws = pkv.workspace_size(d, 32, 64, 16, 16)
     assert ws >= 64 * (1 + 32) * 16 and ws % 256 == 0
     # fixed runs of 32 pages over 2048-page entries: 64 runs of partials
+    # (fp16 outputs and an fp32 {lse, scale} pair per row)
     ws = pkv.workspace_size(d, 32, 8, 2048, 32)
     rows = 8 * 64 * 32
-    assert ws >= rows * 128 * 4 + rows * 4 + 8 * 4096 * 16 and ws % 256 == 0
+    assert ws >= rows * 128 * 2 + rows * 8 + 8 * 4096 * 16 and ws % 256 == 0
     # balanced: a record per tile of batch x max_pages pages, partial slots for
     # every workgroup plus every entry, counters and entry descriptors
     wb = pkv.workspace_size(d, 32, 64, 256, 0)
-    assert wb >= 64 * 256 * 2 * 16 + 64 * 32 * 129 * 4 + 64 * 8 * 4 + 64 * 16
+    assert wb >= 64 * 256 * 2 * 16 + 64 * 32 * (128 * 2 + 8) + 64 * 8 * 4 + 64 * 16
     assert pkv.workspace_size(d, 32, 0, 256, 0) == 0
     assert pkv.workspace_size(d, 30, 64, 256, 0) > 0        # sizes only
     assert pkv.workspace_size(CacheDesc(36, 8192, 12, 8, 128), 32, 64, 256, 0) == 0
