@@ -512,17 +512,23 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
 // ---------------------------------------------------------------------------
 // Decode.
 //
-// Tiles are staged through LDS.  For each 8-token tile the workgroup (one
-// wave per KV head of its head group) copies the K rows and the V rows of all
-// its heads from HBM into an LDS buffer with direct-to-LDS loads
-// (global_load_lds_dwordx4): every instruction moves 1 KiB of one contiguous
-// row run, so each page is read in long contiguous runs, and no registers
-// hold data in flight.  A ring of NBUF buffers keeps NBUF - 1 tiles in
-// flight; one barrier per tile makes a tile visible to every wave (each
-// wave first waits for its own copies) and frees the buffer that the copy of
-// tile k + NBUF - 1 then refills.  The waves then read their own head's rows
-// from LDS.  The q rows of a segment's entry travel the same way, in a slot
-// of the tile where the segment starts.
+// Tiles are staged through LDS.  A workgroup has one wave per KV head of its
+// head group, and all its waves walk the same tiles.  For each 8-token tile a
+// wave copies its own head's K rows and V rows from HBM into its own region
+// of an LDS buffer with direct-to-LDS loads (global_load_lds_dwordx4, 1 KiB
+// per instruction: 4 rows of 256 B at D = 128), so no registers hold data in
+// flight; together the waves read every 16 KiB run of a tile's K (and V)
+// rows at about the same time.  A ring of NBUF buffers keeps NBUF - 1 tiles
+// in flight per wave.  No LDS data is shared between waves, so there is no
+// barrier: each wave waits for its own copies only, refills the buffer it has
+// just finished with the tile NBUF - 1 ahead, before anything waits for a
+// slower wave (a barrier per tile ahead of the copies made every wave's next
+// copies wait for the slowest wave's compute, which cost about a tenth of the
+// streaming rate; the waves now meet only every kSyncTiles tiles, after
+// their copies are out).
+// The loads are non-temporal: the stream is read once, and it leaves the
+// L2 to what is reused.  The q rows of a segment's entry travel the same
+// way, in the wave's slot of the tile where the segment starts.
 //
 // The copies are written as inline assembly, so the compiler does not track
 // them; the kernel waits for them itself.  Vector memory operations of a wave
@@ -553,6 +559,12 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
 // their maximum, i.e. not waited for).
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 constexpr int kMaxVmWait = 24;   // largest wait count the decode loop uses
+// Two waves of a workgroup share each SIMD, and the older one wins the issue
+// arbitration: left alone, the younger waves fall about an eighth behind and
+// the workgroup ends with its slowest wave.  A barrier every kSyncTiles tiles,
+// placed after the wave has issued its next copies (so no copy waits for it),
+// keeps the waves within a few tiles of each other.
+constexpr int kSyncTiles = 4;
 
 // s_waitcnt vmcnt(min(n, N)) for a wave-uniform n >= 0 (the immediate must be
 // a constant: a chain of scalar compares picks it).
@@ -571,11 +583,11 @@ __device__ __forceinline__ void wait_vm_at_most(int n) {
 // One direct-to-LDS copy: 16 bytes from each lane's global address to LDS at
 // lds + 16 * lane (lds is wave-uniform and goes through M0).
 __device__ __forceinline__ void copy_to_lds(const void *src, uint32_t lds) {
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+    asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(lds) : "memory");
 }
 // The same from a wave-uniform base plus a 32-bit per-lane byte offset.
 __device__ __forceinline__ void copy_to_lds(const void *base, uint32_t off, uint32_t lds) {
-    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds)
+    asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(base), "{m0}"(lds)
                  : "memory");
 }
 
@@ -690,7 +702,8 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
     const uint32_t part_bytes = (uint32_t)(kTileTokens * nw * D * 2);
     const uint32_t buf_bytes = 2 * part_bytes + (uint32_t)(nw * QI * 1024);
-    const int upr = nw * D / 8;                // 16-byte units per row of the group
+    constexpr int RPI = 512 / D;               // rows of one head per 1 KiB copy
+    constexpr int HB = kTileTokens * D * 2;    // bytes of a wave's K (or V) rows of a tile
     const int64_t half_bytes = (int64_t)a.half_stride * 2;
     const int64_t row_bytes = (int64_t)a.row_stride * 2;
 
@@ -785,17 +798,16 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
         auto rec_of = [&](int i) { return blk[1 + min(i, n - 1)]; };
 
         // Per-lane byte offsets of this wave's copies: copy i (of IPW per
-        // half) moves 16-byte unit u = (w * IPW + i) * 64 + lane of the K (or
-        // V) rows, row u / upr, unit u % upr of that row's head-group run.
-        // Rows past the tile's last token re-read its first row (off0).
+        // half) moves rows RPI i .. RPI i + RPI - 1 of head w, lane = row
+        // within the copy * D / 8 + 16-byte unit of the row, into LDS rows of
+        // D * 2 bytes.  Rows past the tile's last token re-read its first row
+        // (off0).
         int crow[IPW];
         uint32_t coff[IPW], coff0[IPW];
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
-            const int u = (w * IPW + i) * 64 + lane;
-            crow[i] = u / upr;
-            const int c = u - crow[i] * upr;
-            coff0[i] = (uint32_t)(c * 16);
+            crow[i] = RPI * i + lane / (D / 8);
+            coff0[i] = (uint32_t)(w * D * 2 + (lane % (D / 8)) * 16);
             coff[i] = (uint32_t)(crow[i] * row_bytes) + coff0[i];
         }
         const char *cache_b = reinterpret_cast<const char *>(a.cache) + (int64_t)h0 * D * 2;
@@ -851,29 +863,29 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                     const char *vs = is_new ? reinterpret_cast<const char *>(a.v_new) + nsrc +
                                                   coff0[i]
                                             : vb + o;
-                    copy_to_lds(ks, bb + (uint32_t)(w * IPW + i) * 1024);
-                    copy_to_lds(vs, bb + part_bytes + (uint32_t)(w * IPW + i) * 1024);
+                    copy_to_lds(ks, bb + (uint32_t)(w * HB + i * 1024));
+                    copy_to_lds(vs, bb + part_bytes + (uint32_t)(w * HB + i * 1024));
                 }
             } else if (ntok == kTileTokens) {
 #pragma unroll
                 for (int i = 0; i < IPW; ++i) {
-                    copy_to_lds(kb, coff[i], bb + (uint32_t)(w * IPW + i) * 1024);
-                    copy_to_lds(vb, coff[i], bb + part_bytes + (uint32_t)(w * IPW + i) * 1024);
+                    copy_to_lds(kb, coff[i], bb + (uint32_t)(w * HB + i * 1024));
+                    copy_to_lds(vb, coff[i], bb + part_bytes + (uint32_t)(w * HB + i * 1024));
                 }
             } else {
 #pragma unroll
                 for (int i = 0; i < IPW; ++i) {
                     const uint32_t o = crow[i] < ntok ? coff[i] : coff0[i];
-                    copy_to_lds(kb, o, bb + (uint32_t)(w * IPW + i) * 1024);
-                    copy_to_lds(vb, o, bb + part_bytes + (uint32_t)(w * IPW + i) * 1024);
+                    copy_to_lds(kb, o, bb + (uint32_t)(w * HB + i * 1024));
+                    copy_to_lds(vb, o, bb + part_bytes + (uint32_t)(w * HB + i * 1024));
                 }
             }
         };
 
-        // LDS in 16-byte units: this lane's chunk 0 of its first K row (row
-        // rg, head w, unit j), the step to its next row, its q chunk 0
-        const int kunit = (rg * nw + w) * (D / 8) + j;
-        const int rstep = RG * nw * (D / 8);
+        // LDS in 16-byte units: this lane's chunk 0 of its first K row (head
+        // w's region, row rg, unit j), the step to its next row, its q chunk 0
+        const int kunit = (w * kTileTokens + rg) * (D / 8) + j;
+        const int rstep = RG * (D / 8);
         const int part_units = (int)(part_bytes / 16);
         const int buf_units = (int)(buf_bytes / 16);
         const int qunit = (2 * part_bytes + w * QI * 1024) / 16 + j;
@@ -1111,7 +1123,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
         };
 
         // Tiles 0 .. NBUF-2 in flight before the loop; every iteration waits
-        // for its tile, passes the barrier, refills the freed buffer with the
+        // for its tile, refills the buffer the wave has just finished with the
         // tile NBUF - 1 ahead (past the end, the last tile again: never
         // computed, and the wait count stays exact) and computes.
         int4 rt = rec0[0];
@@ -1130,7 +1142,6 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPT * (NBUF - 2)));
             else
                 wait_vm_at_most<kMaxVmWait>(after);
-            __builtin_amdgcn_s_barrier();
             if (k == sig_at) {
                 // the first partial's stores are complete (tile k landed)
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1142,6 +1153,9 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             }
             issue(rn, (k + NBUF - 1) % NBUF);
             rn = rec_of(k + NBUF);
+            // keep the waves together: see kSyncTiles
+            if (k % kSyncTiles == kSyncTiles - 1)
+                __builtin_amdgcn_s_barrier();
             compute_tile(k);
         }
         // the copies issued past the last tile land before the wave moves on
@@ -1315,6 +1329,7 @@ const void *run_kernel_d(int group, int nbuf) {
     switch (nbuf) {
     case 2: return run_kernel_dn<D, 2>(group);
     case 3: return run_kernel_dn<D, 3>(group);
+    case 4: return run_kernel_dn<D, 4>(group);
     default: return nullptr;
     }
 }
