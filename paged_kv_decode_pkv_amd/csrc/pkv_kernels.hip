@@ -1124,14 +1124,15 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
 
         // Tiles 0 .. NBUF-2 in flight before the loop; every iteration waits
         // for its tile, refills the buffer the wave has just finished with the
-        // tile NBUF - 1 ahead (past the end, the last tile again: never
-        // computed, and the wait count stays exact) and computes.
+        // tile NBUF - 1 ahead (none past the end: the waits count only what
+        // was issued, so they stay exact) and computes.
         int4 rt = rec0[0];
 #pragma unroll
         for (int t = 0; t < NBUF - 1; ++t) {
             if (t > 0 && t < n)
                 rt = rec0[t];
-            issue(rt, t);
+            if (t < n)
+                issue(rt, t);
         }
         int4 rn = NBUF - 1 < n ? rec0[NBUF - 1] : rt;
         for (int k = 0; k < n; ++k) {
@@ -1151,20 +1152,24 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                 signaled0 = true;
                 ops += 1;
             }
-            issue(rn, (k + NBUF - 1) % NBUF);
+            if (k + NBUF - 1 < n)
+                issue(rn, (k + NBUF - 1) % NBUF);
             rn = rec_of(k + NBUF);
             // keep the waves together: see kSyncTiles
             if (k % kSyncTiles == kSyncTiles - 1)
                 __builtin_amdgcn_s_barrier();
             compute_tile(k);
         }
-        // the copies issued past the last tile land before the wave moves on
+        // the last stores complete before the wave moves on
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
 
     // Split entries: count this wave's remaining partials in; the last of an
     // entry's segments to arrive merges them all and resets the counter.
     if (pend0 >= 0) {
+        // the entries' descriptors load while the stores complete
+        const int4 ent0 = ent[pend0];
+        const int4 ent1 = ent[pend1 >= 0 ? pend1 : pend0];
         // this wave's partial stores are complete (written through) before
         // its arrivals are counted; the compiler may not move them past here
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1189,7 +1194,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             const int b = pp == 0 ? pend0 : pend1;
             if (b < 0)
                 break;
-            const int4 e = ent[b];
+            const int4 e = pp == 0 ? ent0 : ent1;
             if ((pp == 0 ? arr0 : arr1) != e.y - 1)
                 continue;
             __atomic_signal_fence(__ATOMIC_SEQ_CST);

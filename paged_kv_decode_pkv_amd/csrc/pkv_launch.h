@@ -122,9 +122,11 @@ inline int group_waves(int num_kv_heads) {
 }
 
 // Cost units of the balanced split: a tile, and the extra work of an entry
-// (starting and ending a segment: about one and a half tiles of decode time).
+// (starting and ending a segment: its q rows, a partly filled last tile, the
+// first tile's rescale, the merge of row groups and the stores; measured at
+// about two and a half tiles of decode time).
 constexpr int kTileCost = 4;
-constexpr int kEntryCost = 6;
+constexpr int kEntryCost = 10;
 
 // Records one balanced block may receive: a run of the cost axis holds at most
 // (kTileCost T + kEntryCost Z) / (kTileCost W) + 1 tiles for T tiles in Z
