@@ -94,7 +94,8 @@ int pkv_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
  * function; no device work.  Returns 0 for arguments the calls would reject.
  * The size grows with batch * max_pages_per_req (16 bytes per 8-token tile
  * of that many pages, for the step's plan, plus a few records per entry and
- * per workgroup) plus fp32 partial rows for split entries.
+ * per workgroup) plus partial rows for split entries (fp16 outputs and an
+ * fp32 {lse, scale} pair per query head).
  */
 size_t pkv_decode_workspace_size(pkv_cache_desc_t desc, int32_t num_qo_heads,
                                  int32_t batch, int32_t max_pages_per_req,
