@@ -703,6 +703,12 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     const uint32_t part_bytes = (uint32_t)(kTileTokens * nw * D * 2);
     const uint32_t buf_bytes = 2 * part_bytes + (uint32_t)(nw * QI * 1024);
     constexpr int RPI = 512 / D;               // rows of one head per 1 KiB copy
+    // LDS reads of 16 lanes meet in one pass: with 8 lanes per 256-byte row
+    // those are two rows, on the same banks, so odd rows hold their two
+    // 128-byte halves swapped (the copies place them so: every lane picks its
+    // own source)
+    constexpr bool SWZ = D == 128 && LPR == 8;
+    static_assert(!SWZ || RPL == 1, "the swap is keyed to a lane's one row");
     constexpr int HB = kTileTokens * D * 2;    // bytes of a wave's K (or V) rows of a tile
     const int64_t half_bytes = (int64_t)a.half_stride * 2;
     const int64_t row_bytes = (int64_t)a.row_stride * 2;
@@ -807,7 +813,8 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             crow[i] = RPI * i + lane / (D / 8);
-            coff0[i] = (uint32_t)(w * D * 2 + (lane % (D / 8)) * 16);
+            const int unit = (lane % (D / 8)) ^ (SWZ ? ((crow[i] & 1) << 3) : 0);
+            coff0[i] = (uint32_t)(w * D * 2 + unit * 16);
             coff[i] = (uint32_t)(crow[i] * row_bytes) + coff0[i];
         }
         const char *cache_b = reinterpret_cast<const char *>(a.cache) + (int64_t)h0 * D * 2;
@@ -884,7 +891,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
 
         // LDS in 16-byte units: this lane's chunk 0 of its first K row (head
         // w's region, row rg, unit j), the step to its next row, its q chunk 0
-        const int kunit = (w * kTileTokens + rg) * (D / 8) + j;
+        const int kunit = (w * kTileTokens + rg) * (D / 8) + j;   // SWZ: chunk at j + 8 (c ^ rg&1)
         const int rstep = RG * (D / 8);
         const int part_units = (int)(part_bytes / 16);
         const int buf_units = (int)(buf_bytes / 16);
@@ -927,8 +934,9 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             for (int i = 0; i < RPL; ++i)
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    kx[i][c] = sb[kunit + i * rstep + LPR * c];
-                    vx[i][c] = sb[part_units + kunit + i * rstep + LPR * c];
+                    const int cu = SWZ ? 8 * (c ^ (rg & 1)) : LPR * c;
+                    kx[i][c] = sb[kunit + i * rstep + cu];
+                    vx[i][c] = sb[part_units + kunit + i * rstep + cu];
                 }
             // q.k: RPL x G independent dot products over the lane's chunks,
             // then their row sums step by step across all of them
