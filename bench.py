@@ -13,8 +13,11 @@ second), the decode kernel's roofline figures measured live with HIP events on
 its own stream, and the fp64 oracle timed on the host cores on a bounded
 sample of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--chunk-pages P] [--no-cpu-baseline]
-                  [--no-check] [--probe-copy]
+  python bench.py [--steps K] [--warmup W] [--config C] [--batch B]
+                  [--chunk-pages P] [--no-cpu-baseline] [--no-check] [--probe-copy]
+
+The other workloads (--config 1, 2, 4, 5; --batch for the batch sweep of the
+Qwen3-0.6B-like one) print the same line for that workload.
 """
 from __future__ import annotations
 
@@ -42,6 +45,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--batch", type=int, default=0,
+                    help="batch size (with its padding share) instead of the workload's own")
     ap.add_argument("--chunk-pages", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
@@ -77,8 +82,9 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def probe_copy(torch):
-    """Plain device-to-device copy of a known size, for counter calibration."""
+def probe_copy(torch, quiet=False):
+    """Plain device-to-device copy of a known size: the counter calibration,
+    and the copy rate the chip reaches (an informational ceiling)."""
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -93,8 +99,13 @@ def probe_copy(torch):
         dst.copy_(src)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / reps
-    print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n,
-                      "ms": dt * 1e3, "GBs": 2 * n / dt / 1e9}), flush=True)
+    rec = {"probe": "copy", "bytes_read": n, "bytes_written": n, "ms": dt * 1e3,
+           "GBs": 2 * n / dt / 1e9}
+    del src, dst
+    torch.cuda.empty_cache()
+    if not quiet:
+        print(json.dumps(rec), flush=True)
+    return rec
 
 
 def main():
@@ -115,7 +126,7 @@ def main():
     import workloads
 
     spec = workloads.CONFIGS[args.config]
-    table = workloads.make_table(spec)
+    table = workloads.make_table(spec, args.batch or None)
     nl, b = spec.num_layers, table.batch
     hq, hkv, d, ps = spec.num_qo_heads, spec.num_kv_heads, spec.head_dim, spec.page_size
     dev = torch.device("cuda:0")
@@ -235,18 +246,22 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
     with torch.cuda.stream(stream):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # an event between consecutive steps: per-step durations as well
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        e0.record()
-        for _ in range(args.steps):
+        ev[0].record()
+        for i in range(args.steps):
             replay()
-        e1.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    ms_step_ev = e0.elapsed_time(e1) / args.steps
-    log(f"step: {ms_step:.4f} ms wall, {ms_step_ev:.4f} ms events")
+    ms_step_ev = ev[0].elapsed_time(ev[-1]) / args.steps
+    step_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    p10, p50, p90 = (float(x) for x in np.percentile(step_ms, [10, 50, 90]))
+    log(f"step: {ms_step:.4f} ms wall, {ms_step_ev:.4f} ms events "
+        f"(p10 {p10:.4f}, median {p50:.4f}, p90 {p90:.4f})")
 
     # ---- live per-launch timing of the decode kernel: a HIP graph of the
     # step's per-layer launches alone (no plan), replayed between two events
@@ -285,6 +300,9 @@ def main():
     durs = np.array([[a.elapsed_time(z) for a, z in row] for row in evs]) * 1e3   # us
     eager_us = float(durs.mean())
 
+    copy = probe_copy(torch, quiet=True)
+    log(f"plain 1 GiB device copy: {copy['GBs']:.0f} GB/s (read + write)")
+
     by = workloads.algorithmic_bytes(table, hq, hkv, d)
     step_bytes = nl * by["total"]
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
@@ -301,13 +319,18 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": spec.name, "batch": b, "active": int(table.active.sum()),
                    "layers": nl, "num_qo_heads": hq, "num_kv_heads": hkv, "head_dim": d,
-                   "page_size": ps, "lengths": "log-uniform [64, 4096]",
+                   "page_size": ps,
+                   "lengths": ("log-uniform" if spec.length_dist == "loguniform" else "uniform")
+                   + f" [{spec.length_lo}, {spec.length_hi}]",
                    "kv_chunk_pages": chunk, "hip_graph": graph is not None,
                    "call": call_name,
                    "step_bytes": step_bytes},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "decode_rows_per_s": round(rows_per_s, 1),
         "ms_per_step_events": round(ms_step_ev, 5),
+        "ms_per_step_p10_median_p90": [round(p10, 5), round(p50, 5), round(p90, 5)],
+        "gbs_at_median_step": round(step_bytes / (p50 * 1e-3) / 1e9, 1),
+        "copy_probe_gbs": round(copy["GBs"], 1),
         "roofline": {"bound": "hbm", "kernel": f"{call_name}: run_kernel (decode + merge)",
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
@@ -390,7 +413,8 @@ def cpu_baseline(spec, table, cache, Q, KN, VN, torch, seconds):
     threads) have been spent or the step's layers run out; the entries of a
     layer run concurrently on a thread pool (the oracle releases the GIL).
     Only the oracle calls are timed, not the copies of the pages to the host.
-    The rate uses the same algorithmic-byte formula as the GPU figure."""
+    The rate uses the same algorithmic-byte formula as the GPU figure.  The
+    first layer is then run again on one thread for the single-core rate."""
     import oracle
     hq, hkv, d = spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -405,20 +429,29 @@ def cpu_baseline(spec, table, cache, Q, KN, VN, torch, seconds):
     lens = table.lengths[act]
     per_layer = (int(lens.sum()) * 2 * hkv * d * 2 + len(act) * hq * d * 2 * 2
                  + len(act) * hq * 4 + len(act) * 2 * 2 * hkv * d * 2)
-    for layer in range(spec.num_layers):
-        if dt * threads >= seconds:
-            break
+    def layer_jobs(layer):
         qh, kn, vn = _u16(Q[layer]), _u16(KN[layer]), _u16(VN[layer])
         jobs = []
         for e in act:
             mini, ip, ix, ll = _host_entries(table, cache[layer], [e], torch)
             jobs.append((mini, ip, ix, ll, qh[[e]], kn[[e]], vn[[e]]))
+        return jobs
+
+    for layer in range(spec.num_layers):
+        if dt * threads >= seconds:
+            break
+        jobs = layer_jobs(layer)
         t = time.perf_counter()
         with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(run, jobs))
         dt += time.perf_counter() - t
         layers += 1
         nbytes += per_layer
+    jobs = layer_jobs(0)
+    t = time.perf_counter()
+    for job in jobs:
+        run(job)
+    dt1 = time.perf_counter() - t
     cpu_model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -433,6 +466,8 @@ def cpu_baseline(spec, table, cache, Q, KN, VN, torch, seconds):
                       f"all {len(act)} active entries ({int(lens.sum())} tokens per layer), "
                       f"append + fp64 decode, {dt:.2f} s on {threads} threads",
             "decode_rows_per_s_equiv": round(len(act) * layers / dt / spec.num_layers, 3),
+            "value_1thread": round(per_layer / dt1 / 1e9, 4),
+            "sample_1thread": f"layer 0 on one thread, {dt1:.2f} s",
             "cpu_model": cpu_model}
 
 
