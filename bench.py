@@ -267,16 +267,21 @@ def main():
     # step's per-layer launches alone (no plan), replayed between two events
     # recorded on the stream the kernels run on; a launch's duration is the
     # elapsed time over the launches, so it includes the dispatch gap to the
-    # next launch (rocprofv3's kernel time leaves that gap out).
+    # next launch (rocprofv3's kernel time leaves that gap out).  Workloads of
+    # few layers repeat their layers in the graph (at least 32 launches), so
+    # the host's graph submissions do not leave the GPU idle between them;
+    # a repeated launch recomputes the same outputs.
     ksteps = max(1, min(args.steps, 20))
+    reps = -(-32 // nl)
     run_graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(run_graph):
         _, rlayers = calls_for(torch.cuda.current_stream().cuda_stream)
         # the decode launches only (with --separate, not the appends)
         rlayers = [[c for c in cl if c[2] != "pkv_append"] for cl in rlayers]
-        run_step(None, rlayers)
+        for _ in range(reps):
+            run_step(None, rlayers)
     torch.cuda.synchronize()
-    launches_per_step = sum(len(c) for c in rlayers)
+    launches_per_step = reps * sum(len(c) for c in rlayers)
     with torch.cuda.stream(stream):
         for _ in range(2):
             run_graph.replay()
@@ -338,7 +343,8 @@ def main():
                      and not args.plan_per_layer and args.chunk_pages == 0 else None,
                      "bytes_per_launch": launch_bytes, "avg_launch_us": round(dec_us, 3),
                      "launches": int(ksteps * launches_per_step),
-                     "timing": "HIP events around graph replays of the step's run launches "
+                     "timing": "HIP events around graph replays of the step's run launches, layers "
+                               "repeated to at least 32 launches "
                                "(no plan); per launch = elapsed / launches",
                      "avg_launch_us_eager_events": round(eager_us, 3)},
     }

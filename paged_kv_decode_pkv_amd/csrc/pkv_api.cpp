@@ -76,8 +76,14 @@ Layout make_layout(const pkv_cache_desc_t &d, int32_t num_qo_heads, int32_t batc
         const int64_t wb = pkv::balanced_blocks_bound(d.num_kv_heads);
         p.slots = wb + batch;
         // W blocks of 1 + balanced_capacity records each, for any W <= wb:
-        // at most W (1 + max_tiles / W + 1 + 2 batch / W + 1 + 2) in total
-        block_ints4 = p.max_tiles + 2 * (int64_t)batch + 5 * wb;
+        // at most W (1 + max_tiles / W + 1 + E batch / W + 1 + 2) with E =
+        // kEntryCost / kTileCost, or W (1 + 2 kMinRunTiles + 2), in total
+        const int64_t full = p.max_tiles +
+                             (pkv::kEntryCost * (int64_t)batch + pkv::kTileCost - 1) /
+                                 pkv::kTileCost +
+                             5 * wb;
+        const int64_t shortest = wb * (3 + 2 * (int64_t)pkv::kMinRunTiles);
+        block_ints4 = full > shortest ? full : shortest;
     }
     p.off_ent = align256((int64_t)batch * d.num_kv_heads * 4);
     p.off_blocks = p.off_ent + align256((int64_t)batch * 16);

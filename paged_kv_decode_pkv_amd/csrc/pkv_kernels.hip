@@ -309,12 +309,18 @@ __device__ __forceinline__ int entry_of(const int *start, int hi, int64_t t) {
     return lo;
 }
 
-// Balanced mode: run index of workgroup id w.  Workgroups are dealt to the 8
-// XCDs round-robin, so ids w, w + 8, ... share an XCD; giving them
-// consecutive runs keeps an entry's pieces (and its q rows and partials)
-// within one XCD's L2 as far as possible.
-__device__ __forceinline__ int run_of_block(int w, int W) {
-    return (W % 8 == 0) ? (w % 8) * (W / 8) + w / 8 : w;
+// Balanced mode: run index of workgroup id w of W for R <= W runs (R when
+// it has none).  Workgroups are dealt to the 8 XCDs round-robin, so ids w,
+// w + 8, ... share an XCD; XCD x takes runs [R x / 8, R (x + 1) / 8) on
+// consecutive ids, which keeps an entry's pieces (and its q rows and
+// partials) within one XCD's L2 as far as possible, and spreads fewer runs
+// than workgroups over all XCDs and their CUs.
+__device__ __forceinline__ int run_of_block(int w, int W, int R) {
+    if (W % 8 != 0)
+        return w < R ? w : R;
+    const int x = w % 8, i = w / 8;
+    const int r0 = (int)((int64_t)R * x / 8), r1 = (int)((int64_t)R * (x + 1) / 8);
+    return r0 + i < r1 ? r0 + i : R;
 }
 
 // Balanced mode splits cost, not tiles.  Every entry's tiles are laid end to
@@ -400,8 +406,10 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
         T = total;
         ax.T = T;
         ax.C = kTileCost * (int64_t)total + kEntryCost * (int64_t)totalz;
-        // runs no shorter than a tile, so no run inside an entry's tiles is empty
-        const int64_t cap = ax.C / kTileCost;
+        // runs no shorter than kMinRunTiles tiles: a shorter run costs more
+        // in its start, its partial and the merge than its tiles take (and
+        // no run inside an entry's tiles is empty)
+        const int64_t cap = ax.C / (kTileCost * kMinRunTiles);
         ax.weff = cap < 1 ? 1 : (cap < W ? cap : W);
     }
     const int64_t weff = fixed ? W : ax.weff;
@@ -457,7 +465,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
                 slot = b * a.max_chunks + c;
             }
         } else {
-            run = run_of_block(w, W);
+            run = run_of_block(w, W, (int)weff);
             if (run < weff) {
                 g0 = ax.tiles_before(ax.C * run / weff);
                 g1 = ax.tiles_before(ax.C * (run + 1) / weff);

@@ -128,12 +128,21 @@ inline int group_waves(int num_kv_heads) {
 constexpr int kTileCost = 4;
 constexpr int kEntryCost = 10;
 
-// Records one balanced block may receive: a run of the cost axis holds at most
-// (kTileCost T + kEntryCost Z) / (kTileCost W) + 1 tiles for T tiles in Z
-// entries and W >= 1 runs, and the last two terms round that up.
+// Shortest run of the balanced split, in tiles: a small workload takes fewer
+// runs than there are workgroups rather than runs of a tile or two, whose
+// start, partial and share of the merge cost more than their tiles.
+constexpr int kMinRunTiles = 4;
+
+// Records one balanced block may receive.  The cost axis (kTileCost T +
+// kEntryCost Z for T tiles in Z entries) is cut into R runs, R = W when the
+// axis holds W runs of kMinRunTiles tiles, else fewer (at least 1): a run
+// then holds at most (kTileCost T + kEntryCost Z) / (kTileCost W) + 1 tiles
+// (the first term's two rounded-up parts and the last term bound it), or
+// less than 2 kMinRunTiles + 1.
 inline int64_t balanced_capacity(int64_t max_tiles, int64_t batch, int64_t blocks) {
-    return (max_tiles + blocks - 1) / blocks +
-           (kEntryCost * batch + kTileCost * blocks - 1) / (kTileCost * blocks) + 2;
+    const int64_t full = (max_tiles + blocks - 1) / blocks +
+                         (kEntryCost * batch + kTileCost * blocks - 1) / (kTileCost * blocks) + 2;
+    return full > 2 * kMinRunTiles + 2 ? full : 2 * kMinRunTiles + 2;
 }
 
 inline int64_t balanced_blocks_bound(int num_kv_heads) {
