@@ -526,10 +526,11 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
 // of an LDS buffer with direct-to-LDS loads (global_load_lds_dwordx4, 1 KiB
 // per instruction: 4 rows of 256 B at D = 128), so no registers hold data in
 // flight; together the waves read every 16 KiB run of a tile's K (and V)
-// rows at about the same time.  A ring of NBUF buffers keeps NBUF - 1 tiles
-// in flight per wave.  No LDS data is shared between waves, so there is no
-// barrier: each wave waits for its own copies only, refills the buffer it has
-// just finished with the tile NBUF - 1 ahead, before anything waits for a
+// rows at about the same time.  A ring of NBUF buffers keeps NBUF tiles in
+// flight per wave while it waits: the buffer a wave has just computed is
+// refilled at once with the tile NBUF ahead.  No LDS data is shared between
+// waves, so there is no barrier: each wave waits for its own copies only and
+// issues its next copies before anything waits for a
 // slower wave (a barrier per tile ahead of the copies made every wave's next
 // copies wait for the slowest wave's compute, which cost about a tenth of the
 // streaming rate; the waves now meet only every kSyncTiles tiles, after
@@ -1138,25 +1139,23 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             }
         };
 
-        // Tiles 0 .. NBUF-2 in flight before the loop; every iteration waits
-        // for its tile, refills the buffer the wave has just finished with the
-        // tile NBUF - 1 ahead (none past the end: the waits count only what
-        // was issued, so they stay exact) and computes.
-        int4 rt = rec0[0];
+        // Tiles 0 .. NBUF-1 in flight before the loop; every iteration waits
+        // for its tile, computes it and refills the buffer it has just
+        // finished with the tile NBUF ahead (none past the end: the waits
+        // count only what was issued, so they stay exact), so NBUF tiles are
+        // in flight while a wave waits.
 #pragma unroll
-        for (int t = 0; t < NBUF - 1; ++t) {
-            if (t > 0 && t < n)
-                rt = rec0[t];
+        for (int t = 0; t < NBUF; ++t) {
             if (t < n)
-                issue(rt, t);
+                issue(rec0[t], t);
         }
-        int4 rn = NBUF - 1 < n ? rec0[NBUF - 1] : rt;
+        int4 rn = rec_of(NBUF);
         for (int k = 0; k < n; ++k) {
             // tile k has landed: at most the operations issued after its
-            // copies (NBUF - 2 tiles, their q rows, the stores since) remain
+            // copies (NBUF - 1 tiles, their q rows, the stores since) remain
             const int after = (int)(ops - (uint32_t)__builtin_amdgcn_readlane(ring_ops, k % NBUF));
-            if (after == IPT * (NBUF - 2))
-                __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPT * (NBUF - 2)));
+            if (after == IPT * (NBUF - 1))
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPT * (NBUF - 1)));
             else
                 wait_vm_at_most<kMaxVmWait>(after);
             if (k == sig_at) {
@@ -1168,13 +1167,16 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                 signaled0 = true;
                 ops += 1;
             }
-            if (k + NBUF - 1 < n)
-                issue(rn, (k + NBUF - 1) % NBUF);
-            rn = rec_of(k + NBUF);
-            // keep the waves together: see kSyncTiles
-            if (k % kSyncTiles == kSyncTiles - 1)
-                __builtin_amdgcn_s_barrier();
             compute_tile(k);
+            const bool more = k + NBUF < n;   // uniform: the waves share the block
+            if (more)
+                issue(rn, k % NBUF);
+            rn = rec_of(k + NBUF + 1);
+            // keep the waves together while they still issue copies: see
+            // kSyncTiles (past the last copies a barrier would only hold the
+            // faster waves' stores and arrival counts back)
+            if (more && k % kSyncTiles == kSyncTiles - 1)
+                __builtin_amdgcn_s_barrier();
         }
         // the last stores complete before the wave moves on
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -1371,7 +1373,7 @@ size_t stage_buffer_bytes(int nw, int head_dim, int group) {
 }
 
 // Staging depth (buffers) and LDS bytes of the decode kernel on the current
-// device: as deep as LDS allows, up to 4.
+// device: as deep as LDS allows, up to kMaxStageBuffers.
 hipError_t stage_shape(int head_dim, int group, int num_kv_heads, int *nbuf, size_t *lds) {
     int dev = 0, max_lds = 0;
     hipError_t err = hipGetDevice(&dev);
