@@ -15,6 +15,11 @@ compiles that file with gcc into ``liboracle.so`` and wraps its three calls:
   merged by log-sum-exp ("Adding a Model", section 1: ``run``; "Supported
   Models", LTX-2.5 notes, for merging partial attentions).
 * :func:`decode_rows` -- the same for a chosen list of rows.
+* :func:`qk_norm_rope_append` -- per-head RMSNorm of q and k, rotary
+  embedding at each entry's position, and the KV write of the rotated k and
+  the v rows ("Supported Models", M* docs, Qwen3-Omni and Qwen3-TTS notes:
+  q/k norm, RoPE and KV write as one fused step).
+* :func:`bf16_round` -- fp64 to bf16, round to nearest even.
 
 Every function here is pinned by ``tests/test_oracle_pins.py``.
 """
@@ -58,6 +63,12 @@ def load(path: str = _LIB_PATH):
     lib.oracle_decode_rows.argtypes = ([p] + [i64] * 6 + [p, i64, p, p, p, i64,
                                        ctypes.c_double, i64, p, p, i64, p, p])
     lib.oracle_decode_rows.restype = ctypes.c_int
+    d64 = ctypes.c_double
+    lib.oracle_qk_norm_rope_append.argtypes = ([p] + [i64] * 6 + [p, i64, p, p, p, p, d64,
+                                               d64, p, p, p, p, i64, p, p])
+    lib.oracle_qk_norm_rope_append.restype = ctypes.c_int
+    lib.oracle_bf16_round.argtypes = [d64]
+    lib.oracle_bf16_round.restype = ctypes.c_uint16
     if path == _LIB_PATH:
         _lib = lib
     return lib
@@ -141,3 +152,42 @@ def decode_rows(cache, layer, q, indptr, indices, last_len, sm_scale, rows_b,
     if rc:
         raise ValueError(f"oracle_decode_rows failed (code {rc})")
     return out, lse
+
+
+def qk_norm_rope_append(cache, layer, q, k_new, v_new, q_norm_w, k_norm_w, eps, theta,
+                        positions, indptr, indices, last_len, lib=None):
+    """Return (q_out fp64 [batch, Hq, D], k_out fp64 [batch, Hkv, D]); write
+    bf16(k_out) and v_new into each entry's append slot of ``cache``."""
+    lib = lib or load()
+    _check_cache(cache)
+    nl, npg, _, ps, hkv, d = cache.shape
+    indptr, indices, last_len = _tables(indptr, indices, last_len)
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k_new = np.ascontiguousarray(k_new, dtype=np.uint16)
+    v_new = np.ascontiguousarray(v_new, dtype=np.uint16)
+    q_norm_w = np.ascontiguousarray(q_norm_w, dtype=np.uint16)
+    k_norm_w = np.ascontiguousarray(k_norm_w, dtype=np.uint16)
+    positions = np.ascontiguousarray(positions, dtype=np.int32)
+    batch, hq, dq = q.shape
+    if (dq != d or batch != len(last_len) or k_new.shape != (batch, hkv, d)
+            or v_new.shape != (batch, hkv, d) or q_norm_w.shape != (d,)
+            or k_norm_w.shape != (d,) or positions.shape != (batch,)):
+        raise ValueError("shapes: q [batch, Hq, D], k_new/v_new [batch, Hkv, D], "
+                         "weights [D], positions [batch]")
+    q_out = np.zeros((batch, hq, d), dtype=np.float64)
+    k_out = np.zeros((batch, hkv, d), dtype=np.float64)
+    rc = lib.oracle_qk_norm_rope_append(
+        _ptr(cache), nl, npg, ps, hkv, d, layer, _ptr(q), hq, _ptr(k_new), _ptr(v_new),
+        _ptr(q_norm_w), _ptr(k_norm_w), float(eps), float(theta), _ptr(positions),
+        _ptr(indptr), _ptr(indices), _ptr(last_len), batch, _ptr(q_out), _ptr(k_out))
+    if rc:
+        raise ValueError(f"oracle_qk_norm_rope_append failed (code {rc})")
+    return q_out, k_out
+
+
+def bf16_round(x, lib=None) -> np.ndarray:
+    """fp64 values rounded to bf16 bits (nearest, ties to even), one by one."""
+    lib = lib or load()
+    flat = np.asarray(x, dtype=np.float64).ravel()
+    out = np.array([lib.oracle_bf16_round(float(v)) for v in flat], dtype=np.uint16)
+    return out.reshape(np.shape(x))

@@ -32,6 +32,21 @@
  *    attentions ("Supported Models", M* docs, LTX-2.5 notes: queries merge
  *    the ranks' partial attentions).
  *
+ *  - Fused q/k norm, rotary embedding and KV write ("Supported Models", M*
+ *    docs, Qwen3-Omni and Qwen3-TTS notes: each layer's q/k RMSNorm, RoPE and
+ *    KV write run as one kernel, in fp32 throughout and rounded once, with
+ *    the RoPE theta taken from the position resource).  Per head of D values
+ *    x: y = x / sqrt(mean(x^2) + eps) * w (RMSNorm over the head, weight w of
+ *    D values, one for q heads and one for k heads); then the rotary
+ *    embedding at the entry's position p in the rotate-half pairing of
+ *    Qwen3-style attention: for i < D/2, with angle a_i = p * theta^(-2i/D),
+ *      z_i       = y_i cos a_i - y_{i+D/2} sin a_i
+ *      z_{i+D/2} = y_{i+D/2} cos a_i + y_i sin a_i.
+ *    The rotated q rows are returned; the rotated k rows (rounded to bf16)
+ *    and the v rows (bit copies) go to the slot the append fills.  The
+ *    pages name the fusion but not its formulas: the RMSNorm and the
+ *    rotate-half pairing are the readings this oracle takes.
+ *
  * All arithmetic is fp64; every bf16 input is widened exactly.
  * Functions return 0 on success and a negative value on a malformed table.
  */
@@ -47,6 +62,26 @@ static double widen_bf16(uint16_t bits)
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+}
+
+/*
+ * Round an fp64 value to the nearest bf16 (ties to even), directly: a bf16 is
+ * the top 16 bits of an fp32, so first round to fp32, then to bf16, and where
+ * the fp32 lands exactly halfway between two bf16 values although the fp64
+ * value did not, round toward the fp64 value instead of to even.  Finite
+ * inputs only.
+ */
+uint16_t oracle_bf16_round(double x)
+{
+    float f = (float)x;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0xFFFFu) == 0x8000u && (double)f != x) {
+        uint32_t hi = u >> 16;   /* the bf16 below f in magnitude */
+        return (uint16_t)(fabs(x) > fabs((double)f) ? hi + 1 : hi);
+    }
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
 }
 
 /* Element index of cache[layer][page][kv][slot][head][0]. */
@@ -264,6 +299,83 @@ int oracle_decode_rows(const uint16_t *cache, int64_t num_layers, int64_t num_pa
                             out + i * head_dim, lse + i);
         if (rc)
             return rc;
+    }
+    return 0;
+}
+
+/* RMSNorm of one head row: y = x / sqrt(mean(x^2) + eps) * w. */
+static void rms_norm_row(const uint16_t *x, const uint16_t *w, int64_t head_dim,
+                         double eps, double *y)
+{
+    double ss = 0.0;
+    for (int64_t d = 0; d < head_dim; ++d) {
+        double v = widen_bf16(x[d]);
+        ss += v * v;
+    }
+    double inv = 1.0 / sqrt(ss / (double)head_dim + eps);
+    for (int64_t d = 0; d < head_dim; ++d)
+        y[d] = widen_bf16(x[d]) * inv * widen_bf16(w[d]);
+}
+
+/* Rotary embedding of one head row in place, rotate-half pairing: element i
+ * and element i + D/2 turn by the angle pos * theta^(-2i/D). */
+static void rope_row(double *y, int64_t head_dim, double pos, double theta)
+{
+    int64_t half = head_dim / 2;
+    for (int64_t i = 0; i < half; ++i) {
+        double angle = pos * pow(theta, -2.0 * (double)i / (double)head_dim);
+        double c = cos(angle), s = sin(angle);
+        double lo = y[i], hi = y[i + half];
+        y[i] = lo * c - hi * s;
+        y[i + half] = hi * c + lo * s;
+    }
+}
+
+/*
+ * q_out[b, hq, :] = rope(rmsnorm(q[b, hq, :], q_w), positions[b]) (fp64), and
+ * k_out[b, h, :] = rope(rmsnorm(k_new[b, h, :], k_w), positions[b]) (fp64),
+ * whose bf16 rounding goes to the K slot the append fills, with v_new[b, h, :]
+ * copied bit for bit to the V slot (same page and slot as oracle_append).
+ * head_dim must be even.
+ */
+int oracle_qk_norm_rope_append(uint16_t *cache, int64_t num_layers, int64_t num_pages,
+                               int64_t page_size, int64_t num_kv_heads, int64_t head_dim,
+                               int64_t layer, const uint16_t *q, int64_t num_qo_heads,
+                               const uint16_t *k_new, const uint16_t *v_new,
+                               const uint16_t *q_w, const uint16_t *k_w, double eps,
+                               double theta, const int32_t *positions,
+                               const int32_t *page_indptr, const int32_t *page_indices,
+                               const int32_t *last_page_len, int64_t batch,
+                               double *q_out, double *k_out)
+{
+    if (layer < 0 || layer >= num_layers || head_dim % 2 != 0)
+        return -1;
+    for (int64_t b = 0; b < batch; ++b) {
+        if (entry_len(page_indptr, last_page_len, page_size, b) < 0)
+            return -2;
+        int64_t page = page_indices[page_indptr[b + 1] - 1];
+        int64_t slot = last_page_len[b] - 1;
+        if (page < 0 || page >= num_pages)
+            return -3;
+        double pos = (double)positions[b];
+        for (int64_t hq = 0; hq < num_qo_heads; ++hq) {
+            int64_t row = (b * num_qo_heads + hq) * head_dim;
+            rms_norm_row(q + row, q_w, head_dim, eps, q_out + row);
+            rope_row(q_out + row, head_dim, pos, theta);
+        }
+        for (int64_t h = 0; h < num_kv_heads; ++h) {
+            int64_t row = (b * num_kv_heads + h) * head_dim;
+            rms_norm_row(k_new + row, k_w, head_dim, eps, k_out + row);
+            rope_row(k_out + row, head_dim, pos, theta);
+            int64_t dk = cache_row(num_pages, page_size, num_kv_heads, head_dim,
+                                   layer, page, 0, slot, h);
+            int64_t dv = cache_row(num_pages, page_size, num_kv_heads, head_dim,
+                                   layer, page, 1, slot, h);
+            for (int64_t d = 0; d < head_dim; ++d) {
+                cache[dk + d] = oracle_bf16_round(k_out[row + d]);
+                cache[dv + d] = v_new[row + d];
+            }
+        }
     }
     return 0;
 }

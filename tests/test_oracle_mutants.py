@@ -18,6 +18,42 @@ from test_oracle_pins import PINS
 SRC = os.path.join(os.path.dirname(oracle.__file__), "pkv_oracle.c")
 
 MUTANTS = {
+    "rope_sin_sign": (
+        "y[i] = lo * c - hi * s;",
+        "y[i] = lo * c + hi * s;"),
+    "rope_second_half_sign": (
+        "y[i + half] = hi * c + lo * s;",
+        "y[i + half] = hi * c - lo * s;"),
+    "rope_frequency_exponent": (
+        "pow(theta, -2.0 * (double)i / (double)head_dim)",
+        "pow(theta, -1.0 * (double)i / (double)head_dim)"),
+    "rope_interleaved_pairs": (
+        "double lo = y[i], hi = y[i + half];",
+        "double lo = y[(2 * i) % head_dim], hi = y[(2 * i + 1) % head_dim];"),
+    "rope_position_off_by_one": (
+        "double pos = (double)positions[b];",
+        "double pos = (double)positions[b] + 1.0;"),
+    "rmsnorm_eps_dropped": (
+        "sqrt(ss / (double)head_dim + eps)",
+        "sqrt(ss / (double)head_dim + 0.0 * eps)"),
+    "rmsnorm_sum_not_mean": (
+        "sqrt(ss / (double)head_dim + eps)",
+        "sqrt(ss + eps)"),
+    "rmsnorm_weight_dropped": (
+        "y[d] = widen_bf16(x[d]) * inv * widen_bf16(w[d]);",
+        "y[d] = widen_bf16(x[d]) * inv * (w[d] != 0 ? 1.0 : 1.0);"),
+    "k_norm_uses_q_weight": (
+        "rms_norm_row(k_new + row, k_w, head_dim, eps, k_out + row);",
+        "rms_norm_row(k_new + row, q_w, head_dim, eps, k_out + row);"),
+    "norm_rope_v_from_k": (
+        "cache[dv + d] = v_new[row + d];",
+        "cache[dv + d] = k_new[row + d];"),
+    "bf16_round_ties_away": (
+        "u += 0x7FFFu + ((u >> 16) & 1u);",
+        "u += 0x8000u;"),
+    "bf16_round_double_rounding": (
+        "if ((u & 0xFFFFu) == 0x8000u && (double)f != x) {",
+        "if ((u & 0xFFFFu) == 0x8000u && (double)f != x && 0) {"),
     "append_slot_off_by_one": (
         "int64_t slot = last_page_len[b] - 1;",
         "int64_t slot = last_page_len[b] % page_size;"),

@@ -12,7 +12,11 @@ serving pages fix:
   one-hot V, equal keys, huge scores against scipy's softmax);
 * invariants (shift of keys, page relabelling, split runs vs unsplit);
 * the append's bit copy, checked through a contiguous view of the pages and a
-  byte diff of the whole cache.
+  byte diff of the whole cache;
+* for the fused q/k RMSNorm + rotary embedding + KV write: hand-derived bf16
+  roundings, the RMSNorm of a constant head in closed form, rotations of unit
+  vectors worked by hand, the relative-position and length invariants of the
+  rotation, and its KV write checked against the pinned append.
 
 ``tests/test_oracle_mutants.py`` re-runs all of them on deliberately broken
 copies of the oracle and requires each copy to fail at least one.
@@ -315,10 +319,130 @@ def pin_append_then_single_token_decode(lib):
         np.testing.assert_array_equal(out, bf16_to_f32(vn).astype(np.float64))
 
 
+# ---- fused q/k RMSNorm + rotary embedding + KV write
+
+def _bf16(x):
+    return bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def _norm_rope(lib, q, k, v, qw, kw, eps, theta, positions, lengths, ps=4, hkv=None,
+               cache=None, seed=0):
+    """One layer of a 2-layer cache; returns (q_out, k_out, cache before, cache after)."""
+    rng = np.random.default_rng(seed)
+    b, hq, d = q.shape
+    hkv = k.shape[1]
+    table = table_from_lengths(np.asarray(lengths), np.ones(b, bool), ps, None, rng)
+    if cache is None:
+        cache = bf16_bits(rng.normal(size=(2, table.num_pages, 2, ps, hkv, d)))
+    before = cache.copy()
+    q_out, k_out = oracle.qk_norm_rope_append(cache, 1, q, k, v, qw, kw, eps, theta,
+                                              positions, table.indptr, table.indices,
+                                              table.last_len, lib=lib)
+    return q_out, k_out, before, cache, table
+
+
+def pin_bf16_round(lib):
+    # Hand-derived roundings: 1 + 2^-8 is halfway between bf16 1.0 and the next
+    # value (1 + 2^-7): ties go to the even one; a hair above (below) the
+    # midpoint rounds up (down) even though fp32 alone would land on the
+    # midpoint; negative values mirror.
+    cases = [(1.0, 0x3F80), (3.0, 0x4040), (-2.5, 0xC020),
+             (1 + 2.0 ** -8, 0x3F80), (1 + 3 * 2.0 ** -8, 0x3F82),
+             (1 + 2.0 ** -8 + 2.0 ** -40, 0x3F81), (1 + 2.0 ** -8 - 2.0 ** -40, 0x3F80),
+             (-(1 + 2.0 ** -8 + 2.0 ** -40), 0xBF81), (1 + 2.0 ** -9, 0x3F80),
+             (1 + 2.0 ** -7 - 2.0 ** -12, 0x3F81), (0.0, 0x0000)]
+    for x, bits in cases:
+        got = int(lib.oracle_bf16_round(float(x)))
+        assert got == bits, f"bf16({x!r}) = {got:#06x}, want {bits:#06x}"
+
+
+def pin_rms_norm_closed_form(lib):
+    # A head of D equal values c normalises to c / sqrt(c^2 + eps) per element
+    # (times the weight); at position 0 the rotation is the identity.
+    d, eps = 8, 1e-6
+    rng = np.random.default_rng(20)
+    cs = bf16_to_f32(_bf16([1e-3, -1e-3, 0.75, -40.0, 3e-4])).astype(np.float64)
+    q = np.repeat(_bf16(cs)[None, :, None], d, axis=2)              # [1, 5, D]
+    qw = _bf16(rng.uniform(0.5, 2.0, size=d))
+    kw = _bf16(rng.uniform(0.5, 2.0, size=d))
+    k = q[:, :1]
+    q_out, k_out, _, _, _ = _norm_rope(lib, q, k, k, qw, kw, eps, 1e6, [0], [3])
+    w_q = bf16_to_f32(qw).astype(np.float64)
+    w_k = bf16_to_f32(kw).astype(np.float64)
+    want = (cs / np.sqrt(cs * cs + eps))[:, None] * w_q[None, :]
+    np.testing.assert_allclose(q_out[0], want, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(k_out[0, 0], cs[0] / math.sqrt(cs[0] ** 2 + eps) * w_k,
+                               rtol=1e-14, atol=0)
+
+
+def pin_rope_worked_example(lib):
+    # D = 4, eps = 0, unit weights: the unit vector e_j normalises to 2 e_j;
+    # then element i pairs with i + 2 and turns by pos * theta^(-i/2).
+    d = 4
+    q = _bf16(np.eye(d))[None]                                         # [1, 4, 4]
+    ones = _bf16(np.ones(d))
+    for pos, theta in [(1, 10000.0), (3, 100.0), (-2, 10000.0)]:
+        q_out, _, _, _, _ = _norm_rope(lib, q, q[:, :1], q[:, :1], ones, ones, 0.0,
+                                       theta, [pos], [2])
+        a0, a1 = pos * 1.0, pos * theta ** -0.5
+        want = 2 * np.array([[math.cos(a0), 0, math.sin(a0), 0],
+                             [0, math.cos(a1), 0, math.sin(a1)],
+                             [-math.sin(a0), 0, math.cos(a0), 0],
+                             [0, -math.sin(a1), 0, math.cos(a1)]])
+        np.testing.assert_allclose(q_out[0], want, rtol=0, atol=1e-14,
+                                   err_msg=f"pos {pos} theta {theta}")
+
+
+def pin_rope_relative_position(lib):
+    # <rope(q, m), rope(k, n)> depends on m - n only, and the rotation keeps
+    # each pair's length.
+    rng = np.random.default_rng(21)
+    d, eps, theta = 128, 1e-6, 1e6
+    qrow = _bf16(rng.normal(size=(1, 1, d)))
+    krow = _bf16(rng.normal(size=(1, 1, d)))
+    w = _bf16(rng.uniform(0.5, 1.5, size=d))
+    q = np.concatenate([qrow, qrow])
+    k = np.concatenate([krow, krow])
+    dots = []
+    for m, n in [(5000, 1234), (3766, 0), (40000, 36234)]:
+        q_out, k_out, _, _, _ = _norm_rope(lib, q, k, k, w, w, eps, theta, [m, n], [3, 7])
+        dots.append(float(q_out[0, 0] @ k_out[1, 0]))
+        for row, src in [(q_out[0, 0], qrow[0, 0]), (k_out[1, 0], krow[0, 0])]:
+            x = bf16_to_f32(src).astype(np.float64)
+            y = x / math.sqrt(np.mean(x * x) + eps) * bf16_to_f32(w)
+            np.testing.assert_allclose(row[:d // 2] ** 2 + row[d // 2:] ** 2,
+                                       y[:d // 2] ** 2 + y[d // 2:] ** 2, rtol=1e-12)
+    np.testing.assert_allclose(dots[1:], dots[0], rtol=1e-10)
+
+
+def pin_norm_rope_write_is_append(lib):
+    # The KV write lands where the pinned append puts rows: bf16(k_out) in the
+    # K slot, v bit for bit in the V slot, nothing else touched.  The k path
+    # is the q path with the k weight.
+    rng = np.random.default_rng(22)
+    b, hq, hkv, d = 3, 4, 2, 16
+    q = _bf16(rng.normal(size=(b, hq, d)))
+    k = _bf16(rng.normal(size=(b, hkv, d)))
+    v = _bf16(rng.normal(size=(b, hkv, d)))
+    qw = _bf16(rng.uniform(0.5, 1.5, size=d))
+    kw = _bf16(rng.uniform(0.5, 1.5, size=d))
+    pos = [7, 0, 123]
+    q_out, k_out, before, after, table = _norm_rope(lib, q, k, v, qw, kw, 1e-6, 1e4, pos,
+                                                    [5, 9, 13])
+    expect = before.copy()
+    oracle.append(expect, 1, oracle.bf16_round(k_out, lib=lib), v, table.indptr,
+                  table.indices, table.last_len, lib=lib)
+    np.testing.assert_array_equal(after, expect)
+    q2, _, _, _, _ = _norm_rope(lib, k, k, v, kw, kw, 1e-6, 1e4, pos, [5, 9, 13])
+    np.testing.assert_array_equal(q2, k_out)
+
+
 PINS = [pin_golden, pin_dense_sdpa, pin_single_token, pin_zero_query,
         pin_constant_values, pin_one_hot_values_are_softmax, pin_huge_scores,
         pin_key_shift, pin_split_matches_unsplit, pin_page_relabel,
-        pin_append_is_last_token, pin_append_then_single_token_decode]
+        pin_append_is_last_token, pin_append_then_single_token_decode,
+        pin_bf16_round, pin_rms_norm_closed_form, pin_rope_worked_example,
+        pin_rope_relative_position, pin_norm_rope_write_is_append]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
