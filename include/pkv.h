@@ -89,6 +89,44 @@ int pkv_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
                const int32_t *last_page_len, int32_t batch, hipStream_t stream);
 
 /*
+ * pkv_qk_norm_rope_append -- the fused step that feeds decode on Qwen3-style
+ * attention: per-head RMSNorm of q and k, rotary embedding at each entry's
+ * position, and the KV write ("Supported Models", M* docs, Qwen3-Omni and
+ * Qwen3-TTS notes: q/k norm, RoPE and KV write as one kernel, in fp32
+ * throughout and rounded once; the RoPE theta comes with the positions).
+ *
+ * For each entry b and head row x (D values) at position p = positions[b]:
+ *   y = x / sqrt(mean(x^2) + eps) * w            (w: q_norm_weight for q
+ *                                                 heads, k_norm_weight for k)
+ *   z_i       = y_i cos a_i - y_{i+D/2} sin a_i,  a_i = p * rope_theta^(-2i/D)
+ *   z_{i+D/2} = y_{i+D/2} cos a_i + y_i sin a_i   (rotate-half pairing, i < D/2)
+ * computed in fp32 (the angle in fp64) and rounded once to bf16.  The q rows
+ * go to q_out; the k rows to cache[layer, p_b, 0, s_b, h, :] and v_new's rows,
+ * bit for bit, to cache[layer, p_b, 1, s_b, h, :], with page p_b and slot s_b
+ * chosen as pkv_append chooses them (entries whose table row is malformed
+ * get no KV write, as in pkv_append).  It replaces pkv_append in a layer
+ * whose decode then runs with pkv_run(k_new = v_new = NULL) on q_out.
+ *  kv_cache       bf16 cache described by `desc`, modified in place.
+ *  q              bf16 [batch, num_qo_heads, head_dim], contiguous.
+ *  k_new, v_new   bf16 [batch, num_kv_heads, head_dim], contiguous.
+ *  q_norm_weight, k_norm_weight   bf16 [head_dim].
+ *  eps            >= 0, finite (Qwen3: 1e-6).
+ *  rope_theta     > 0, finite (Qwen3: 1e6).
+ *  positions      int32 [batch]: the position of the entry's new token.
+ *  page_indptr, page_indices, last_page_len   as for pkv_append.
+ *  q_out          bf16 [batch, num_qo_heads, head_dim]; may be q itself.
+ * head_dim 64 or 128 (else PKV_ERR_UNSUPPORTED).  Padding entries write page 0
+ * slot 0 as in pkv_append; their q_out rows are computed all the same.
+ */
+int pkv_qk_norm_rope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+                            const void *q, int32_t num_qo_heads, const void *k_new,
+                            const void *v_new, const void *q_norm_weight,
+                            const void *k_norm_weight, float eps, float rope_theta,
+                            const int32_t *positions, const int32_t *page_indptr,
+                            const int32_t *page_indices, const int32_t *last_page_len,
+                            int32_t batch, void *q_out, hipStream_t stream);
+
+/*
  * pkv_decode_workspace_size -- bytes of device workspace that pkv_plan,
  * pkv_run, pkv_decode and pkv_append_decode need for these arguments.  Host
  * function; no device work.  Returns 0 for arguments the calls would reject.

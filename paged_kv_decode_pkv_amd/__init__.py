@@ -84,6 +84,10 @@ def _load():
     p, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.pkv_append.argtypes = [p, CacheDesc, i32, p, p, p, p, p, i32, p]
     lib.pkv_append.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    lib.pkv_qk_norm_rope_append.argtypes = [p, CacheDesc, i32, p, i32, p, p, p, p, f32, f32,
+                                            p, p, p, p, i32, p, p]
+    lib.pkv_qk_norm_rope_append.restype = ctypes.c_int
     lib.pkv_decode_workspace_size.argtypes = [CacheDesc, i32, i32, i32, i32]
     lib.pkv_decode_workspace_size.restype = sz
     lib.pkv_decode.argtypes = [p, CacheDesc, i32, p, i32, p, p, p, i32, ctypes.c_float,
@@ -185,6 +189,45 @@ def append(kv_cache, layer: int, k_new, v_new, page_indptr, page_indices, last_p
                         batch, _stream(stream))
     if rc != PKV_OK:
         raise PkvError(rc, "pkv_append")
+
+
+def qk_norm_rope_append(kv_cache, layer: int, q, k_new, v_new, q_norm_weight,
+                        k_norm_weight, positions, page_indptr, page_indices, last_page_len,
+                        eps: float = 1e-6, rope_theta: float = 1e6, q_out=None,
+                        stream=None):
+    """Fused per-head RMSNorm of q and k, rotary embedding at ``positions`` and
+    the KV write of the rotated k and of v; returns q_out [batch, Hq, D] (bf16,
+    allocated when not given; may be ``q`` itself)."""
+    import torch
+    desc = cache_desc(kv_cache)
+    batch = int(last_page_len.shape[0])
+    d = desc.head_dim
+    if q.dim() != 3 or q.shape[0] != batch or q.shape[2] != d:
+        raise ValueError(f"q must be [batch, Hq, {d}], got {tuple(q.shape)}")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (batch, desc.num_kv_heads, d):
+            raise ValueError(f"{name} must be [batch, Hkv, D], got {tuple(t.shape)}")
+    for name, t in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        if tuple(t.shape) != (d,):
+            raise ValueError(f"{name} must be [{d}], got {tuple(t.shape)}")
+    if tuple(positions.shape) != (batch,):
+        raise ValueError(f"positions must be [batch], got {tuple(positions.shape)}")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    dev = kv_cache.device
+    rc = lib.pkv_qk_norm_rope_append(
+        _dev_ptr(kv_cache, "kv_cache", torch.bfloat16), desc, int(layer),
+        _dev_ptr(q, "q", torch.bfloat16, dev), int(q.shape[1]),
+        _dev_ptr(k_new, "k_new", torch.bfloat16, dev),
+        _dev_ptr(v_new, "v_new", torch.bfloat16, dev),
+        _dev_ptr(q_norm_weight, "q_norm_weight", torch.bfloat16, dev),
+        _dev_ptr(k_norm_weight, "k_norm_weight", torch.bfloat16, dev),
+        float(eps), float(rope_theta), _dev_ptr(positions, "positions", torch.int32, dev),
+        *_tables(kv_cache, page_indptr, page_indices, last_page_len), batch,
+        _dev_ptr(q_out, "q_out", torch.bfloat16, dev), _stream(stream))
+    if rc != PKV_OK:
+        raise PkvError(rc, "pkv_qk_norm_rope_append")
+    return q_out
 
 
 def _decode_outputs(kv_cache, q, out, lse, with_lse, workspace, max_pages_per_req,

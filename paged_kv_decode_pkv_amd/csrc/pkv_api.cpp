@@ -330,6 +330,57 @@ int pkv_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void 
     return hip_status(pkv::launch_append(a, batch, stream));
 }
 
+int pkv_qk_norm_rope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+                            const void *q, int32_t num_qo_heads, const void *k_new,
+                            const void *v_new, const void *q_norm_weight,
+                            const void *k_norm_weight, float eps, float rope_theta,
+                            const int32_t *positions, const int32_t *page_indptr,
+                            const int32_t *page_indices, const int32_t *last_page_len,
+                            int32_t batch, void *q_out, hipStream_t stream) {
+    int rc = check_desc(desc);
+    if (rc != PKV_OK)
+        return rc;
+    if (layer < 0 || layer >= desc.num_layers || batch < 0 || num_qo_heads < 1 ||
+        !(eps >= 0.0f) || !isfinite(eps) || !(rope_theta > 0.0f) || !isfinite(rope_theta))
+        return PKV_ERR_BAD_SHAPE;
+    if (!pkv::norm_rope_supported(desc.head_dim))
+        return PKV_ERR_UNSUPPORTED;
+    if (batch == 0)
+        return PKV_OK;
+    if (!kv_cache || !q || !k_new || !v_new || !q_norm_weight || !k_norm_weight ||
+        !positions || !page_indptr || !page_indices || !last_page_len || !q_out)
+        return PKV_ERR_NULL_PTR;
+    if (!aligned16(kv_cache) || !aligned16(q) || !aligned16(k_new) || !aligned16(v_new) ||
+        !aligned16(q_norm_weight) || !aligned16(k_norm_weight) || !aligned16(q_out))
+        return PKV_ERR_ALIGNMENT;
+    if ((int64_t)batch * (num_qo_heads + desc.num_kv_heads) > 0x7fffffffLL * 4)
+        return PKV_ERR_BAD_SHAPE;
+    pkv::NormRopeArgs a;
+    a.cache = static_cast<uint16_t *>(kv_cache) + (int64_t)layer * desc.num_pages * page_elems(desc);
+    a.q = static_cast<const uint16_t *>(q);
+    a.k_new = static_cast<const uint16_t *>(k_new);
+    a.v_new = static_cast<const uint16_t *>(v_new);
+    a.q_w = static_cast<const uint16_t *>(q_norm_weight);
+    a.k_w = static_cast<const uint16_t *>(k_norm_weight);
+    a.q_out = static_cast<uint16_t *>(q_out);
+    a.positions = positions;
+    a.indptr = page_indptr;
+    a.indices = page_indices;
+    a.last_len = last_page_len;
+    a.page_stride = page_elems(desc);
+    a.half_stride = desc.page_size * desc.num_kv_heads * desc.head_dim;
+    a.row_elems = desc.num_kv_heads * desc.head_dim;
+    a.num_pages = desc.num_pages;
+    a.page_size = desc.page_size;
+    a.num_qo_heads = num_qo_heads;
+    a.num_kv_heads = desc.num_kv_heads;
+    a.head_dim = desc.head_dim;
+    a.batch = batch;
+    a.eps = eps;
+    a.log2_theta = log2((double)rope_theta);
+    return hip_status(pkv::launch_norm_rope(a, stream));
+}
+
 size_t pkv_decode_workspace_size(pkv_cache_desc_t desc, int32_t num_qo_heads, int32_t batch,
                                  int32_t max_pages_per_req, int32_t kv_chunk_pages) {
     if (check_desc(desc) != PKV_OK || batch <= 0 || num_qo_heads <= 0 ||

@@ -154,6 +154,38 @@ inline int64_t balanced_blocks_bound(int num_kv_heads) {
 
 hipError_t launch_append(const AppendArgs &a, int batch, hipStream_t stream);
 
+// Arguments of the fused q/k RMSNorm + rotary embedding + KV write kernel
+// (offsets in bf16 elements).
+struct NormRopeArgs {
+    uint16_t *cache;          // first element of this layer's slab
+    const uint16_t *q;        // [batch, Hq, D]
+    const uint16_t *k_new;    // [batch, Hkv, D]
+    const uint16_t *v_new;
+    const uint16_t *q_w;      // [D] RMSNorm weights of the q heads
+    const uint16_t *k_w;      // [D] of the k heads
+    uint16_t *q_out;          // [batch, Hq, D], may be q
+    const int32_t *positions; // [batch]
+    const int32_t *indptr;
+    const int32_t *indices;
+    const int32_t *last_len;
+    int64_t page_stride;      // 2 * page_size * Hkv * D
+    int32_t half_stride;      // page_size * Hkv * D
+    int32_t row_elems;        // Hkv * D
+    int32_t num_pages;
+    int32_t page_size;
+    int32_t num_qo_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t batch;
+    float eps;
+    double log2_theta;        // log2 of the rotary base
+};
+
+// True when the fused norm/rope/write kernel is built for head_dim.
+bool norm_rope_supported(int head_dim);
+
+hipError_t launch_norm_rope(const NormRopeArgs &a, hipStream_t stream);
+
 // Workgroups per head group the balanced plan uses on the current device
 // (what the device holds at once).
 hipError_t balanced_blocks(int head_dim, int group, int num_kv_heads, int *blocks);

@@ -19,7 +19,7 @@ DESC = CacheDesc(2, 64, 16, 2, 64)
 
 def test_every_declared_symbol_is_exported():
     names = pkv.declared_functions()
-    assert set(names) == {"pkv_append", "pkv_decode_workspace_size",
+    assert set(names) == {"pkv_append", "pkv_qk_norm_rope_append", "pkv_decode_workspace_size",
                           "pkv_append_decode", "pkv_decode", "pkv_plan", "pkv_run",
                           "pkv_validate_page_table", "pkv_status_string",
                           "pkv_last_hip_error"}
@@ -104,6 +104,31 @@ def test_decode_validation(kw, code):
 
 def test_decode_batch_zero_is_noop():
     assert _decode(batch=0, q=NULL, out=NULL, tables=(NULL, NULL, NULL)) == 0
+
+
+def _norm_rope(desc=DESC, layer=0, q=FAKE, hq=4, k=FAKE, v=FAKE, qw=FAKE, kw=FAKE, eps=1e-6,
+               theta=1e6, pos=FAKE, batch=3, q_out=FAKE, cache=FAKE,
+               tables=(FAKE, FAKE, FAKE)):
+    return lib.pkv_qk_norm_rope_append(cache, desc, layer, q, hq, k, v, qw, kw, eps, theta,
+                                       pos, *tables, batch, q_out, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layer=2), -2), (dict(batch=-1), -2), (dict(hq=0), -2),
+    (dict(eps=-1.0), -2), (dict(eps=float("nan")), -2), (dict(theta=0.0), -2),
+    (dict(theta=float("inf")), -2), (dict(desc=CacheDesc(2, 64, 16, 2, 32)), -3),
+    (dict(desc=CacheDesc(2, 64, 12, 2, 64)), -3),
+    (dict(q=NULL), -1), (dict(kw=NULL), -1), (dict(pos=NULL), -1), (dict(q_out=NULL), -1),
+    (dict(tables=(FAKE, FAKE, NULL)), -1), (dict(cache=NULL), -1),
+    (dict(qw=ctypes.c_void_p(0x100008)), -6), (dict(q_out=ctypes.c_void_p(0x100004)), -6),
+])
+def test_norm_rope_validation(kw, code):
+    assert _norm_rope(**kw) == code
+
+
+def test_norm_rope_batch_zero_is_noop():
+    assert _norm_rope(batch=0, q=NULL, k=NULL, v=NULL, qw=NULL, kw=NULL, pos=NULL,
+                      q_out=NULL, cache=NULL, tables=(NULL, NULL, NULL)) == 0
 
 
 def _append_decode(k=FAKE, v=FAKE, layer=0, batch=3, chunk=0, hq=4, out=FAKE):
