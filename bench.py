@@ -57,6 +57,9 @@ def parse():
                     help="per layer pkv_append then a decode-only pkv_run")
     ap.add_argument("--plan-per-layer", action="store_true",
                     help="per layer pkv_append_decode (plans inside every call)")
+    ap.add_argument("--qk-norm-rope", action="store_true",
+                    help="per layer the fused q/k RMSNorm + rotary + KV write, then a "
+                         "decode-only pkv_run on its q")
     ap.add_argument("--probe-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter scale)")
     return ap.parse_args()
@@ -149,6 +152,14 @@ def main():
             for x in (table.indptr, table.indices, table.last_len)]
     out = torch.empty((nl, b, hq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((nl, b, hq), dtype=torch.float32, device=dev)
+    nr = None
+    if args.qk_norm_rope:
+        # per-layer RMSNorm weights, the new tokens' positions, the rotated q
+        gen = torch.Generator(device=dev).manual_seed(1000 * spec.cfg + 997)
+        nr = {"qw": (torch.rand((nl, d), generator=gen, device=dev) + 0.5).to(torch.bfloat16),
+              "kw": (torch.rand((nl, d), generator=gen, device=dev) + 0.5).to(torch.bfloat16),
+              "pos": torch.from_numpy((table.lengths - 1).astype(np.int32)).to(dev),
+              "qo": torch.empty_like(Q), "eps": 1e-6, "theta": 1e6}
     maxp = table.max_pages_per_req
     chunk = args.chunk_pages
     ws_bytes = pkv.workspace_size(pkv.cache_desc(cache), hq, b, maxp, chunk)
@@ -177,7 +188,18 @@ def main():
             res = (ctypes.c_float(spec.sm_scale), vp(out[layer].data_ptr()),
                    vp(lse[layer].data_ptr()), maxp, chunk, *ws_args, s)
             cl = []
-            if args.separate:
+            if args.qk_norm_rope:
+                qo = (vp(nr["qo"][layer].data_ptr()), hq)
+                cl.append((pkv.lib.pkv_qk_norm_rope_append,
+                           (vp(cache.data_ptr()), desc, layer, vp(Q[layer].data_ptr()), hq, kn,
+                            vn, vp(nr["qw"][layer].data_ptr()), vp(nr["kw"][layer].data_ptr()),
+                            ctypes.c_float(nr["eps"]), ctypes.c_float(nr["theta"]),
+                            vp(nr["pos"].data_ptr()), *tab_ptrs, b,
+                            vp(nr["qo"][layer].data_ptr()), s),
+                           "pkv_qk_norm_rope_append"))
+                cl.append((pkv.lib.pkv_run, (vp(cache.data_ptr()), desc, layer, null, null,
+                                             *qo, b, *res), "pkv_run"))
+            elif args.separate:
                 cl.append((pkv.lib.pkv_append,
                            (vp(cache.data_ptr()), desc, layer, kn, vn, *tab_ptrs, b, s),
                            "pkv_append"))
@@ -193,7 +215,9 @@ def main():
             layers.append(cl)
         return plan, layers
 
-    if args.separate:
+    if args.qk_norm_rope:
+        call_name = "pkv_qk_norm_rope_append + pkv_run"
+    elif args.separate:
         call_name = "pkv_append + pkv_run"
     elif args.plan_per_layer:
         call_name = "pkv_append_decode"
@@ -277,7 +301,8 @@ def main():
     with torch.cuda.graph(run_graph):
         _, rlayers = calls_for(torch.cuda.current_stream().cuda_stream)
         # the decode launches only (with --separate, not the appends)
-        rlayers = [[c for c in cl if c[2] != "pkv_append"] for cl in rlayers]
+        rlayers = [[c for c in cl if c[2] not in ("pkv_append", "pkv_qk_norm_rope_append")]
+                   for cl in rlayers]
         for _ in range(reps):
             run_step(None, rlayers)
     torch.cuda.synchronize()
@@ -308,11 +333,32 @@ def main():
     copy = probe_copy(torch, quiet=True)
     log(f"plain 1 GiB device copy: {copy['GBs']:.0f} GB/s (read + write)")
 
+    nr_us = None
+    if args.qk_norm_rope:
+        # the fused norm/rotary/KV-write launches alone, timed the same way
+        nr_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(nr_graph):
+            _, nlayers = calls_for(torch.cuda.current_stream().cuda_stream)
+            nlayers = [[c for c in cl if c[2] == "pkv_qk_norm_rope_append"] for cl in nlayers]
+            for _ in range(reps):
+                run_step(None, nlayers)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                nr_graph.replay()
+            n0, n1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n0.record()
+            for _ in range(ksteps):
+                nr_graph.replay()
+            n1.record()
+        torch.cuda.synchronize()
+        nr_us = n0.elapsed_time(n1) * 1e3 / (ksteps * reps * nl)
+
     by = workloads.algorithmic_bytes(table, hq, hkv, d)
-    step_bytes = nl * by["total"]
+    step_bytes = nl * (by["decode"] + by["norm_rope"] if args.qk_norm_rope else by["total"])
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     rows_per_s = int(table.active.sum()) / (ms_step * 1e-3)
-    launch_bytes = by["decode"] if args.separate else by["total"]
+    launch_bytes = by["decode"] if (args.separate or args.qk_norm_rope) else by["total"]
     dec_gbs = launch_bytes / (dec_us * 1e-6) / 1e9
     log(f"decode launch avg {dec_us:.2f} us (graph; eager with events {eager_us:.2f} us) "
         f"-> {dec_gbs:.0f} GB/s algorithmic; step {gbs:.0f} GB/s")
@@ -340,7 +386,8 @@ def main():
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if args.config == 3 and not args.separate
-                     and not args.plan_per_layer and args.chunk_pages == 0 else None,
+                     and not args.plan_per_layer and not args.qk_norm_rope
+                     and args.chunk_pages == 0 else None,
                      "bytes_per_launch": launch_bytes, "avg_launch_us": round(dec_us, 3),
                      "launches": int(ksteps * launches_per_step),
                      "timing": "HIP events around graph replays of the step's run launches, layers "
@@ -349,8 +396,16 @@ def main():
                      "avg_launch_us_eager_events": round(eager_us, 3)},
     }
 
+    if nr_us is not None:
+        result["norm_rope"] = {
+            "kernel": "pkv_qk_norm_rope_append: norm_rope_kernel",
+            "avg_launch_us": round(nr_us, 3), "bytes_per_launch": by["norm_rope"],
+            "achieved_gbs": round(by["norm_rope"] / (nr_us * 1e-6) / 1e9, 1),
+            "bound": "latency",
+            "note": "a few bytes per entry and head: the launch is bound by latency"}
+        log(f"norm_rope launch avg {nr_us:.2f} us")
     if not args.no_check:
-        result["parity"] = check_sample(spec, table, cache, Q, KN, VN, out, lse, torch)
+        result["parity"] = check_sample(spec, table, cache, Q, KN, VN, out, lse, torch, nr)
         log(f"parity on sampled rows: {result['parity']}")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(spec, table, cache, Q, KN, VN, torch,
@@ -377,12 +432,14 @@ def _u16(t):
     return t.contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
 
 
-def check_sample(spec, table, cache, Q, KN, VN, out, lse, torch):
+def check_sample(spec, table, cache, Q, KN, VN, out, lse, torch, nr=None):
     """Sampled rows of the benchmarked step against the oracle (layers 0, mid, last).
 
     The timed steps re-append the same rows, so the cache now holds the
     post-append state; the oracle appends again (a no-op on those bytes) from
-    the same k_new / v_new."""
+    the same k_new / v_new.  With the fused q/k norm + rotary step (``nr``)
+    the oracle runs that step on the sampled entries instead and decodes its
+    own bf16-rounded q."""
     import oracle
     from workloads import bf16_to_f32
     act = np.flatnonzero(table.active)
@@ -392,12 +449,19 @@ def check_sample(spec, table, cache, Q, KN, VN, out, lse, torch):
     worst = {"out_max": 0.0, "out_mean": 0.0, "lse_max": 0.0, "rows": 0}
     for layer in sorted({0, spec.num_layers // 2, spec.num_layers - 1}):
         mini, ip, ix, ll = _host_entries(table, cache[layer], entries, torch)
-        oracle.append(mini, 0, _u16(KN[layer])[entries], _u16(VN[layer])[entries], ip, ix,
-                      ll)
+        q_rows = _u16(Q[layer])[entries]
+        if nr is None:
+            oracle.append(mini, 0, _u16(KN[layer])[entries], _u16(VN[layer])[entries], ip,
+                          ix, ll)
+        else:
+            q_ref, _ = oracle.qk_norm_rope_append(
+                mini, 0, q_rows, _u16(KN[layer])[entries], _u16(VN[layer])[entries],
+                _u16(nr["qw"][layer]), _u16(nr["kw"][layer]), nr["eps"], nr["theta"],
+                nr["pos"].cpu().numpy()[entries], ip, ix, ll)
+            q_rows = oracle.bf16_round(q_ref)
         rb = np.repeat(np.arange(len(entries)), len(heads))
         rh = np.tile(heads, len(entries))
-        ro, rl = oracle.decode_rows(mini, 0, _u16(Q[layer])[entries], ip, ix, ll,
-                                    spec.sm_scale, rb, rh)
+        ro, rl = oracle.decode_rows(mini, 0, q_rows, ip, ix, ll, spec.sm_scale, rb, rh)
         eb = np.asarray(entries)[rb]
         og = bf16_to_f32(_u16(out[layer])[eb, rh]).astype(np.float64)
         lg = lse[layer].cpu().numpy()[eb, rh].astype(np.float64)

@@ -377,7 +377,10 @@ int pkv_qk_norm_rope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer
     a.head_dim = desc.head_dim;
     a.batch = batch;
     a.eps = eps;
-    a.log2_theta = log2((double)rope_theta);
+    for (int i = 0; i < 64; ++i)
+        a.turns[i] = i < desc.head_dim / 2
+                         ? pow((double)rope_theta, -2.0 * i / desc.head_dim) / (2.0 * M_PI)
+                         : 0.0;
     return hip_status(pkv::launch_norm_rope(a, stream));
 }
 

@@ -178,7 +178,8 @@ struct NormRopeArgs {
     int32_t head_dim;
     int32_t batch;
     float eps;
-    double log2_theta;        // log2 of the rotary base
+    // rotation rate of pair i in turns per position: theta^(-2i/D) / (2 pi)
+    double turns[64];
 };
 
 // True when the fused norm/rope/write kernel is built for head_dim.

@@ -15,10 +15,13 @@
 // heads of every entry.  Lane l holds elements 2l and 2l + 1 of the row (one
 // 4-byte word, so a row is one coalesced 256-byte access at D = 128); the
 // element D/2 away sits in lane l ^ (D/4), and one lane swap brings it over.
-// The angle is formed and reduced modulo 2 pi in fp64 (positions reach tens
-// of thousands, where an fp32 product would already be off by a few
-// thousandths of a radian), then the rotation runs in fp32.  The work is a
-// few KiB per entry: the launch is bound by latency, not by HBM.
+// The angle is formed in turns and reduced to [-1/2, 1/2] of a turn in fp64
+// (positions reach tens of thousands, where an fp32 product would already be
+// off by a few thousandths of a radian; the fp64 product is off by about
+// 1e-12 of a turn, and taking the nearest whole turn off is exact), then the
+// sine and cosine and the rotation run in fp32.  The rates per pair come with the arguments,
+// computed on the host.  The work is a few KiB per entry: the launch is bound
+// by latency, not by HBM.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -79,11 +82,10 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int i = (2 * lane + j) % (D / 2);   // pair index of the element
-        const double angle = pos * exp2(-2.0 * (double)i / (double)D * a.log2_theta);
-        const double r = angle - 6.283185307179586 * rint(angle * 0.15915494309189535);
-        double sd, cd;
-        sincos(r, &sd, &cd);
-        const float c = (float)cd, s = (float)sd;
+        const double turns = pos * a.turns[i];
+        const float ang = (float)(turns - rint(turns)) * 6.2831853071795865f;
+        float s, c;
+        sincosf(ang, &s, &c);
         const float y = j == 0 ? y0 : y1;
         const float p = j == 0 ? p0 : p1;
         z[j] = upper ? y * c + p * s : y * c - p * s;

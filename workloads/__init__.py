@@ -327,5 +327,10 @@ def algorithmic_bytes(table: PageTable, num_qo_heads: int, num_kv_heads: int,
     lse = b * num_qo_heads * 4
     ptab = 4 * (b + 1) + 4 * int(table.indptr[-1]) + 4 * b
     app = 2 * (2 * b * num_kv_heads * head_dim * 2)
+    # the fused q/k norm + rotary + KV write: q in and out, k and v in and into
+    # the cache, the two norm weights, positions and each entry's last-page
+    # lookup (two indptr words, one page id, one last-page length)
+    norm_rope = 2 * q + app + 2 * head_dim * 2 + 4 * b + 16 * b
     return {"kv": kv, "q": q, "out": out, "lse": lse, "ptab": ptab, "append": app,
-            "decode": kv + q + out + lse + ptab, "total": kv + q + out + lse + ptab + app}
+            "decode": kv + q + out + lse + ptab, "total": kv + q + out + lse + ptab + app,
+            "norm_rope": norm_rope}
