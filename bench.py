@@ -410,6 +410,9 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(spec, table, cache, Q, KN, VN, torch,
                                               args.cpu_seconds)
+        if nr is not None:
+            result["norm_rope"]["cpu_oracle"] = norm_rope_oracle_time(table, Q, KN, VN, nr,
+                                                                      by["norm_rope"])
     print(json.dumps(result), flush=True)
     return 0
 
@@ -473,6 +476,34 @@ def check_sample(spec, table, cache, Q, KN, VN, out, lse, torch, nr=None):
     worst["pass"] = bool(worst["out_max"] <= 1e-2 and worst["out_mean"] <= 1e-3
                          and worst["lse_max"] <= 1e-3)
     return worst
+
+
+def norm_rope_oracle_time(table, Q, KN, VN, nr, nbytes):
+    """The oracle's fused q/k norm + rotary + KV write on layer 0's whole batch
+    (one thread), into a host copy of just the pages it writes."""
+    import oracle
+    b = table.batch
+    last = table.indices[table.indptr[1:] - 1]
+    pages, inv = np.unique(last, return_inverse=True)
+    hkv, d = KN.shape[2], KN.shape[3]
+    mini = np.zeros((1, len(pages), 2, table.page_size, hkv, d), dtype=np.uint16)
+    ip = np.arange(b + 1, dtype=np.int32)
+    ix = inv.astype(np.int32)
+    q, kn, vn = _u16(Q[0]), _u16(KN[0]), _u16(VN[0])
+    qw, kw = _u16(nr["qw"][0]), _u16(nr["kw"][0])
+    pos = nr["pos"].cpu().numpy()
+    t = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.qk_norm_rope_append(mini, 0, q, kn, vn, qw, kw, nr["eps"], nr["theta"], pos,
+                                   ip, ix, table.last_len)
+        reps += 1
+        dt = time.perf_counter() - t
+        if dt > 1.0:
+            break
+    return {"us_per_launch": round(dt / reps * 1e6, 1), "cores": 1, "kind": "oracle",
+            "gbs": round(nbytes / (dt / reps) / 1e9, 3),
+            "sample": f"layer 0, all {b} entries, {reps} calls"}
 
 
 def cpu_baseline(spec, table, cache, Q, KN, VN, torch, seconds):
