@@ -80,7 +80,8 @@ typedef struct {
  *  page_indices   int32 [page_indptr[batch]].
  *  last_page_len  int32 [batch], rows used in the last page after the append.
  * Padding entries list page 0 with last_page_len 1 and write only its slot 0;
- * when several do, any one of their rows may remain there.  Two real entries
+ * when several do, their writes race and that slot ends up holding, element
+ * by element, the value of one or another of their rows.  Two real entries
  * must not share a last page slot.
  */
 int pkv_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,

@@ -106,12 +106,13 @@ def _check_all(table, cache_dev, q_got, host, q_ref, k_ref, v_new, what, layer=1
     mask = np.ones(got_cache.shape, bool)
     mask[layer, pages[act], 0, slots[act]] = False
     if (~act).any():
-        # padding entries all write page 0 slot 0: any one of their V rows
-        # may remain there (and the K row next to it is not compared)
+        # padding entries all write page 0 slot 0 and race there: each V
+        # element holds the value of one or another of their rows (the K row
+        # next to it is not compared)
         mask[layer, 0, :, 0] = False
         v_pad = got_cache[layer, 0, 1, 0]
-        assert any(np.array_equal(v_pad, v_new[b]) for b in np.flatnonzero(~act)), \
-            f"{what}: padding slot holds no padding entry's V row"
+        assert np.all(np.any(v_pad[None] == v_new[~act], axis=0)), \
+            f"{what}: padding slot holds values of no padding entry"
     np.testing.assert_array_equal(got_cache[mask], host[mask], err_msg=f"{what} cache")
 
 

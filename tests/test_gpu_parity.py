@@ -117,9 +117,10 @@ def test_append_bit_exact(idx):
                       table.last_len)
         got = to_host_u16(cache)
         pad = np.flatnonzero(~act)
-        if len(pad):   # padding entries race on page 0 slot 0: any of theirs may win
-            cands = [ld.k_new[b] for b in pad]
-            assert any(np.array_equal(got[layer, 0, 0, 0], c) for c in cands)
+        if len(pad):   # padding entries race on page 0 slot 0: element by element,
+            # one or another of their rows wins
+            for kv, rows in ((0, ld.k_new), (1, ld.v_new)):
+                assert np.all(np.any(got[layer, 0, kv, 0][None] == rows[pad], axis=0))
             got[layer, 0] = cache_host[layer, 0]
         np.testing.assert_array_equal(got, cache_host, err_msg=f"shape {idx} layer {layer}")
 
