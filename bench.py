@@ -146,7 +146,8 @@ def main():
     for layer in range(nl):
         q, kn, vn = workloads.draw_layer_device(cache[layer], table,
                                                 [1000 * spec.cfg + layer, b], hq,
-                                                spec.sigma, offs)
+                                                spec.sigma, offs,
+                                                real_head_dim=spec.real_head_dim)
         Q[layer], KN[layer], VN[layer] = q, kn, vn
     tabs = [torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
             for x in (table.indptr, table.indices, table.last_len)]
@@ -373,6 +374,8 @@ def main():
                    "page_size": ps,
                    "lengths": ("log-uniform" if spec.length_dist == "loguniform" else "uniform")
                    + f" [{spec.length_lo}, {spec.length_hi}]",
+                   "head_dim_real": spec.real_head_dim or d,
+                   "paired_streams": spec.paired,
                    "kv_chunk_pages": chunk, "hip_graph": graph is not None,
                    "call": call_name,
                    "step_bytes": step_bytes},

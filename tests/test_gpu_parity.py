@@ -167,7 +167,8 @@ def _device_case(spec, batch=None, layers=(0,), extra_layers=0):
     for layer in layers:
         q, kn, vn = workloads.draw_layer_device(
             cache[layer], table, [1000 * spec.cfg + layer, table.batch],
-            spec.num_qo_heads, spec.sigma, workloads.k_offsets(spec))
+            spec.num_qo_heads, spec.sigma, workloads.k_offsets(spec),
+            real_head_dim=spec.real_head_dim)
         per_layer[layer] = (q, kn, vn)
     return table, cache, per_layer
 
@@ -195,6 +196,43 @@ def test_decode_config5_long_context(chunk):
     table, cache, per_layer = _device_case(spec)
     _sampled_check(spec, table, cache, 0, per_layer[0], range(spec.batch),
                    [0, 3, 4, 17, 31], chunk=chunk, what=f"cfg5 chunk{chunk}")
+
+
+@pytest.mark.parametrize("chunk", [0, 4])
+def test_decode_config6_cfg_pairs_zero_padded_heads(chunk):
+    """CFG talker-like layer: each session's conditional and unconditional
+    streams ride one plan as two entries; 128-token pages from a pool of 1025
+    with sink page 0; heads of 72 values zero-padded to 128, scale 1/sqrt(72).
+    Zero-padding is exact: the padded output columns are exactly zero, and the
+    first 72 match the oracle run on the unpadded 72-value heads."""
+    spec = CONFIGS[6]
+    real = spec.real_head_dim
+    table, cache, per_layer = _device_case(spec)
+    q, kn, vn = per_layer[0]
+    entries = list(range(0, 12))          # six sessions, both streams
+    heads = [0, 5, 11, 15]
+    # the unpadded oracle case: the entries' pages sliced to 72 values
+    pages = [table.indices[table.indptr[b]:table.indptr[b + 1]] for b in entries]
+    flat = np.concatenate(pages).astype(np.int64)
+    host_pages = to_host_u16(cache[0][torch.from_numpy(flat).to(DEV)])
+    assert not host_pages[..., real:].any()
+    mini = np.zeros((1, 1 + len(flat)) + host_pages.shape[1:-1] + (real,), dtype=np.uint16)
+    mini[0, 1:] = host_pages[..., :real]
+    indptr = np.zeros(len(entries) + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum([len(p) for p in pages])
+    indices = np.arange(1, 1 + len(flat), dtype=np.int32)
+    last = table.last_len[entries].astype(np.int32)
+    qh, kh, vh = (to_host_u16(t)[entries][..., :real] for t in (q, kn, vn))
+    oracle.append(mini, 0, kh, vh, indptr, indices, last)
+    rb = np.repeat(np.arange(len(entries)), len(heads))
+    rh = np.tile(np.asarray(heads), len(entries))
+    ro, rl = oracle.decode_rows(mini, 0, qh, indptr, indices, last, spec.sm_scale, rb, rh)
+    out, lse = gpu_step(cache, 0, per_layer[0], table_to_dev(table), table, spec.sm_scale,
+                        chunk)
+    eb = torch.from_numpy(np.asarray(entries)[rb]).to(DEV)
+    eh = torch.from_numpy(rh).to(DEV)
+    assert not to_host_u16(out[..., real:]).any(), "padded output columns are not zero"
+    compare(out[eb, eh][..., :real], lse[eb, eh], ro, rl, what=f"cfg6 chunk {chunk}")
 
 
 def _pick_entries(table, n):

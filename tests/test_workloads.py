@@ -27,7 +27,7 @@ def test_config_tables(cfg):
     assert t.batch == spec.batch
     act = t.lengths[t.active]
     assert act.min() >= spec.length_lo and act.max() <= spec.length_hi
-    npad = {1: 1, 2: 4, 3: 0, 4: 26, 5: 0}[cfg]
+    npad = {1: 1, 2: 4, 3: 0, 4: 26, 5: 0, 6: 0}[cfg]
     assert int((~t.active).sum()) == npad
     if spec.num_pages is not None:
         assert t.num_pages == spec.num_pages
@@ -41,6 +41,23 @@ def test_config_tables(cfg):
     t2 = make_table(spec)
     np.testing.assert_array_equal(t.indices, t2.indices)
     np.testing.assert_array_equal(t.lengths, t2.lengths)
+
+
+def test_cfg6_pairs_and_padded_heads():
+    # a session's conditional and unconditional streams have equal lengths;
+    # the pool has the sink page plus 1024 pages; drawn heads carry 72 values
+    spec = CONFIGS[6]
+    t = make_table(spec)
+    np.testing.assert_array_equal(t.lengths[0::2], t.lengths[1::2])
+    assert t.num_pages == 1025 and t.max_pages_per_req <= 16
+    assert abs(spec.sm_scale - 1 / np.sqrt(72)) < 1e-15
+    small = workloads.table_from_lengths(t.lengths[:4], np.ones(4, bool), 128, 64,
+                                         np.random.default_rng(0))
+    ld = workloads.draw_layer(np.random.default_rng(1), small, 16, 16, 128,
+                              real_head_dim=72)
+    for a in (ld.q, ld.k_new, ld.v_new, ld.cache):
+        assert not a[..., 72:].any()
+        assert a[..., :72].any()
 
 
 def test_cfg4_sweep_padding():

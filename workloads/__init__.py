@@ -75,10 +75,12 @@ class ConfigSpec:
     k_offset_sigma: float = 0.0    # per-KV-head K offset (long-context stress)
     chunk_pages: tuple = ()        # split sizes its parity tests exercise
     description: str = ""
+    real_head_dim: int = 0         # > 0: q/k/v carry this many values, zero-padded
+    paired: bool = False           # entries come in pairs of equal length
 
     @property
     def sm_scale(self) -> float:
-        return 1.0 / math.sqrt(self.head_dim)
+        return 1.0 / math.sqrt(self.real_head_dim or self.head_dim)
 
     @property
     def group(self) -> int:
@@ -112,6 +114,12 @@ CONFIGS = {
                   32768, 1.0, None, k_offset_sigma=2.0, chunk_pages=(32, 64),
                   description="long-context Qwen3-4B-like layer, batch 8, lengths "
                               "U[16384, 32768], per-head K offsets N(0, 2)"),
+    6: ConfigSpec(6, "talker_cfg_pairs_ps128_d72", 1, 16, 16, 128, 128, 64, 0, "uniform",
+                  38, 2000, 1.0, 1025, real_head_dim=72, paired=True,
+                  description="CFG talker-like layer: 32 sessions x (conditional, "
+                              "unconditional) streams of equal length U[38, 2000], 16/16 "
+                              "heads of 72 values zero-padded to 128, 128-token pages, "
+                              "pool of 1025 pages with sink page 0"),
 }
 
 CFG4_SWEEP = (1, 2, 4, 8, 16, 32, 64, 128, 256)
@@ -176,13 +184,16 @@ def make_table(spec: ConfigSpec, batch: int | None = None) -> PageTable:
     """Lengths, padding positions and page permutation of a config (seeded)."""
     batch = spec.batch if batch is None else batch
     rng = np.random.default_rng([1000 * spec.cfg + 999, batch])
+    n = (batch + 1) // 2 if spec.paired else batch
     if spec.length_dist == "uniform":
-        lengths = rng.integers(spec.length_lo, spec.length_hi + 1, size=batch)
+        lengths = rng.integers(spec.length_lo, spec.length_hi + 1, size=n)
     elif spec.length_dist == "loguniform":
-        u = rng.uniform(math.log(spec.length_lo), math.log(spec.length_hi), size=batch)
+        u = rng.uniform(math.log(spec.length_lo), math.log(spec.length_hi), size=n)
         lengths = np.clip(np.rint(np.exp(u)), spec.length_lo, spec.length_hi)
     else:
         raise ValueError(spec.length_dist)
+    if spec.paired:   # a session's two streams advance together
+        lengths = np.repeat(lengths, 2)[:batch]
     active = np.ones(batch, dtype=bool)
     npad = spec.padding_for(batch)
     if npad:
@@ -211,10 +222,12 @@ class LayerData:
 def draw_layer(rng: np.random.Generator, table: PageTable, num_qo_heads: int,
                num_kv_heads: int, head_dim: int, sigma: float = 1.0,
                k_offset: np.ndarray | None = None, stale: str = "random",
-               unused: str = "zero") -> LayerData:
+               unused: str = "zero", real_head_dim: int = 0) -> LayerData:
     """Draw one layer of a batch described by ``table``.
 
     Draw order: q, k_new, v_new, then the active entries' pages in table order.
+    With ``real_head_dim`` > 0 the values past it in every row (q, k_new,
+    v_new, the drawn pages) are zero: heads of that size zero-padded.
     """
     b, ps = table.batch, table.page_size
     sig = np.float32(sigma)
@@ -252,6 +265,11 @@ def draw_layer(rng: np.random.Generator, table: PageTable, num_qo_heads: int,
             cache[last, :, table.last_len[i] - 1:] = BF16_NAN
     elif stale != "random":
         raise ValueError(stale)
+    if real_head_dim:
+        for a in (q, k_new, v_new):
+            a[..., real_head_dim:] = 0
+        if len(pages):
+            cache[pages, ..., real_head_dim:] = 0
     return LayerData(cache, q, k_new, v_new)
 
 
@@ -259,7 +277,7 @@ def layer_data(spec: ConfigSpec, table: PageTable, layer: int, **kw) -> LayerDat
     """Seeded data of ``layer`` for config ``spec`` and its page table."""
     rng = np.random.default_rng([1000 * spec.cfg + layer, table.batch])
     return draw_layer(rng, table, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim,
-                      spec.sigma, k_offsets(spec), **kw)
+                      spec.sigma, k_offsets(spec), real_head_dim=spec.real_head_dim, **kw)
 
 
 def active_pages(table: PageTable) -> np.ndarray:
@@ -270,7 +288,8 @@ def active_pages(table: PageTable) -> np.ndarray:
 
 
 def draw_layer_device(cache_layer, table: PageTable, seed, num_qo_heads: int,
-                      sigma: float = 1.0, k_offset: np.ndarray | None = None):
+                      sigma: float = 1.0, k_offset: np.ndarray | None = None,
+                      real_head_dim: int = 0):
     """Fill one layer of a device cache and return device (q, k_new, v_new).
 
     The big configurations hold gigabytes of K/V, so their bulk values are
@@ -279,7 +298,8 @@ def draw_layer_device(cache_layer, table: PageTable, seed, num_qo_heads: int,
     rounds to nearest even), optional per-KV-head K offset, real pages of the
     active entries filled, other pages left as they are.  ``cache_layer`` is a
     bf16 tensor [num_pages, 2, page_size, Hkv, D]; ``seed`` is an int or a
-    list of ints (folded into one 63-bit seed).
+    list of ints (folded into one 63-bit seed).  ``real_head_dim`` > 0 zeroes
+    the values past it, as in :func:`draw_layer`.
     """
     import torch
     dev = cache_layer.device
@@ -309,7 +329,12 @@ def draw_layer_device(cache_layer, table: PageTable, seed, num_qo_heads: int,
         vals = normal((len(idx), 2, ps, hkv, d))
         if off is not None:
             vals[:, 0] += off[None, None]
+        if real_head_dim:
+            vals[..., real_head_dim:] = 0
         cache_layer[idx] = vals.to(torch.bfloat16)
+    if real_head_dim:
+        for t in (q, k_new, v_new):
+            t[..., real_head_dim:] = 0
     return q, k_new, v_new
 
 
