@@ -20,6 +20,9 @@ compiles that file with gcc into ``liboracle.so`` and wraps its three calls:
   the v rows ("Supported Models", M* docs, Qwen3-Omni and Qwen3-TTS notes:
   q/k norm, RoPE and KV write as one fused step).
 * :func:`bf16_round` -- fp64 to bf16, round to nearest even.
+* :func:`append_rows` / :func:`prefill` -- several new rows per entry: their
+  append at the entry's last positions, and the causal attention of each row
+  over the tokens up to its own position (paged prefill and mixed steps).
 
 Every function here is pinned by ``tests/test_oracle_pins.py``.
 """
@@ -67,6 +70,10 @@ def load(path: str = _LIB_PATH):
     lib.oracle_qk_norm_rope_append.argtypes = ([p] + [i64] * 6 + [p, i64, p, p, p, p, d64,
                                                d64, p, p, p, p, i64, p, p])
     lib.oracle_qk_norm_rope_append.restype = ctypes.c_int
+    lib.oracle_append_rows.argtypes = [p] + [i64] * 6 + [p, p, p, p, p, p, i64]
+    lib.oracle_append_rows.restype = ctypes.c_int
+    lib.oracle_prefill.argtypes = [p] + [i64] * 6 + [p, i64, p, p, p, p, i64, d64, p, p]
+    lib.oracle_prefill.restype = ctypes.c_int
     lib.oracle_bf16_round.argtypes = [d64]
     lib.oracle_bf16_round.restype = ctypes.c_uint16
     if path == _LIB_PATH:
@@ -191,3 +198,46 @@ def bf16_round(x, lib=None) -> np.ndarray:
     flat = np.asarray(x, dtype=np.float64).ravel()
     out = np.array([lib.oracle_bf16_round(float(v)) for v in flat], dtype=np.uint16)
     return out.reshape(np.shape(x))
+
+
+def append_rows(cache, layer, k_new, v_new, qo_indptr, indptr, indices, last_len,
+                lib=None):
+    """In-place bit copy of each entry's new rows k_new/v_new [rows, Hkv, D]
+    into its last positions."""
+    lib = lib or load()
+    _check_cache(cache)
+    nl, npg, _, ps, hkv, d = cache.shape
+    indptr, indices, last_len = _tables(indptr, indices, last_len)
+    qo_indptr = np.ascontiguousarray(qo_indptr, dtype=np.int32)
+    k_new = np.ascontiguousarray(k_new, dtype=np.uint16)
+    v_new = np.ascontiguousarray(v_new, dtype=np.uint16)
+    rows = int(qo_indptr[-1])
+    if k_new.shape != (rows, hkv, d) or v_new.shape != (rows, hkv, d):
+        raise ValueError("k_new/v_new must be [rows, Hkv, D]")
+    rc = lib.oracle_append_rows(_ptr(cache), nl, npg, ps, hkv, d, layer, _ptr(k_new),
+                                _ptr(v_new), _ptr(qo_indptr), _ptr(indptr), _ptr(indices),
+                                _ptr(last_len), len(last_len))
+    if rc:
+        raise ValueError(f"oracle_append_rows rejected the tables (code {rc})")
+
+
+def prefill(cache, layer, q, qo_indptr, indptr, indices, last_len, sm_scale, lib=None):
+    """Return (out fp64 [rows, Hq, D], lse fp64 [rows, Hq]): causal attention
+    of each new row over its entry's tokens up to its own position."""
+    lib = lib or load()
+    _check_cache(cache)
+    nl, npg, _, ps, hkv, d = cache.shape
+    indptr, indices, last_len = _tables(indptr, indices, last_len)
+    qo_indptr = np.ascontiguousarray(qo_indptr, dtype=np.int32)
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    rows, hq, dq = q.shape
+    if dq != d or rows != int(qo_indptr[-1]) or len(qo_indptr) != len(last_len) + 1:
+        raise ValueError("q must be [rows, Hq, D] with rows = qo_indptr[-1]")
+    out = np.zeros((rows, hq, d), dtype=np.float64)
+    lse = np.zeros((rows, hq), dtype=np.float64)
+    rc = lib.oracle_prefill(_ptr(cache), nl, npg, ps, hkv, d, layer, _ptr(q), hq,
+                            _ptr(qo_indptr), _ptr(indptr), _ptr(indices), _ptr(last_len),
+                            len(last_len), float(sm_scale), _ptr(out), _ptr(lse))
+    if rc:
+        raise ValueError(f"oracle_prefill failed (code {rc})")
+    return out, lse

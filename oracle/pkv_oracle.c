@@ -32,6 +32,14 @@
  *    attentions ("Supported Models", M* docs, LTX-2.5 notes: queries merge
  *    the ranks' partial attentions).
  *
+ *  - Paged prefill and mixed steps ("Adding a Model", "How a program runs":
+ *    prefill runs several rows per request over the same paged cache;
+ *    "Supported Models", Qwen3-Omni / Qwen3-TTS notes: new prompts ride a
+ *    decode step as a mixed step).  Entry b brings n_b = qo_indptr[b+1] -
+ *    qo_indptr[b] new rows (n_b = 1 is a decode row); after they are
+ *    appended its L tokens end with them, at positions L - n_b .. L - 1.
+ *    Row j of entry b sits at position p = L - n_b + j and attends tokens
+ *    0 .. p (causal), with the decode formula above.
  *  - Fused q/k norm, rotary embedding and KV write ("Supported Models", M*
  *    docs, Qwen3-Omni and Qwen3-TTS notes: each layer's q/k RMSNorm, RoPE and
  *    KV write run as one kernel, in fp32 throughout and rounded once, with
@@ -376,6 +384,90 @@ int oracle_qk_norm_rope_append(uint16_t *cache, int64_t num_layers, int64_t num_
                 cache[dv + d] = v_new[row + d];
             }
         }
+    }
+    return 0;
+}
+
+/*
+ * Append of several rows per entry: row j of entry b (global row
+ * qo_indptr[b] + j) goes to token position L - n_b + j, i.e. page
+ * page_indices[page_indptr[b] + t / page_size], slot t % page_size.
+ * k_new, v_new: [total rows, num_kv_heads, head_dim].
+ */
+int oracle_append_rows(uint16_t *cache, int64_t num_layers, int64_t num_pages,
+                       int64_t page_size, int64_t num_kv_heads, int64_t head_dim,
+                       int64_t layer, const uint16_t *k_new, const uint16_t *v_new,
+                       const int32_t *qo_indptr, const int32_t *page_indptr,
+                       const int32_t *page_indices, const int32_t *last_page_len,
+                       int64_t batch)
+{
+    if (layer < 0 || layer >= num_layers)
+        return -1;
+    for (int64_t b = 0; b < batch; ++b) {
+        int64_t len = entry_len(page_indptr, last_page_len, page_size, b);
+        int64_t n = (int64_t)qo_indptr[b + 1] - (int64_t)qo_indptr[b];
+        if (len < 0 || n < 0 || n > len)
+            return -2;
+        for (int64_t j = 0; j < n; ++j) {
+            int64_t t = len - n + j;
+            int64_t page = page_indices[page_indptr[b] + t / page_size];
+            if (page < 0 || page >= num_pages)
+                return -3;
+            for (int64_t h = 0; h < num_kv_heads; ++h) {
+                int64_t src = ((qo_indptr[b] + j) * num_kv_heads + h) * head_dim;
+                int64_t dk = cache_row(num_pages, page_size, num_kv_heads, head_dim,
+                                       layer, page, 0, t % page_size, h);
+                int64_t dv = cache_row(num_pages, page_size, num_kv_heads, head_dim,
+                                       layer, page, 1, t % page_size, h);
+                for (int64_t d = 0; d < head_dim; ++d) {
+                    cache[dk + d] = k_new[src + d];
+                    cache[dv + d] = v_new[src + d];
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Causal attention of every new row: row j of entry b at position
+ * p = L - n_b + j over tokens 0 .. p of its pages.  q, out: [total rows,
+ * num_qo_heads, head_dim] (out fp64); lse: fp64 [total rows, num_qo_heads].
+ */
+int oracle_prefill(const uint16_t *cache, int64_t num_layers, int64_t num_pages,
+                   int64_t page_size, int64_t num_kv_heads, int64_t head_dim,
+                   int64_t layer, const uint16_t *q, int64_t num_qo_heads,
+                   const int32_t *qo_indptr, const int32_t *page_indptr,
+                   const int32_t *page_indices, const int32_t *last_page_len,
+                   int64_t batch, double sm_scale, double *out, double *lse)
+{
+    if (layer < 0 || layer >= num_layers || num_qo_heads % num_kv_heads != 0)
+        return -1;
+    int64_t group = num_qo_heads / num_kv_heads;
+    for (int64_t b = 0; b < batch; ++b) {
+        int64_t len = entry_len(page_indptr, last_page_len, page_size, b);
+        int64_t n = (int64_t)qo_indptr[b + 1] - (int64_t)qo_indptr[b];
+        if (len < 0 || n < 0 || n > len)
+            return -2;
+        const int32_t *pages = page_indices + page_indptr[b];
+        for (int64_t i = 0; i < page_indptr[b + 1] - page_indptr[b]; ++i)
+            if (pages[i] < 0 || pages[i] >= num_pages)
+                return -3;
+        double *scores = malloc(sizeof(double) * (size_t)len);
+        if (!scores)
+            return -4;
+        for (int64_t j = 0; j < n; ++j) {
+            int64_t row = qo_indptr[b] + j;
+            int64_t pos = len - n + j;
+            for (int64_t hq = 0; hq < num_qo_heads; ++hq) {
+                const uint16_t *qrow = q + (row * num_qo_heads + hq) * head_dim;
+                attend_range(cache, num_pages, page_size, num_kv_heads, head_dim, layer,
+                             qrow, hq / group, pages, 0, pos + 1, sm_scale, scores,
+                             out + (row * num_qo_heads + hq) * head_dim,
+                             lse + row * num_qo_heads + hq);
+            }
+        }
+        free(scores);
     }
     return 0;
 }

@@ -18,6 +18,24 @@ from test_oracle_pins import PINS
 SRC = os.path.join(os.path.dirname(oracle.__file__), "pkv_oracle.c")
 
 MUTANTS = {
+    "prefill_not_causal": (
+        "qrow, hq / group, pages, 0, pos + 1, sm_scale, scores,",
+        "qrow, hq / group, pages, 0, len, sm_scale, scores,"),
+    "prefill_causal_excludes_self": (
+        "qrow, hq / group, pages, 0, pos + 1, sm_scale, scores,",
+        "qrow, hq / group, pages, 0, pos + (pos == 0), sm_scale, scores,"),
+    "prefill_position_from_start": (
+        "int64_t pos = len - n + j;",
+        "int64_t pos = j;"),
+    "prefill_gqa_modulo": (
+        "qrow, hq / group, pages, 0, pos + 1, sm_scale, scores,",
+        "qrow, hq % num_kv_heads, pages, 0, pos + 1, sm_scale, scores,"),
+    "append_rows_shifted": (
+        "int64_t t = len - n + j;",
+        "int64_t t = (len - n + j + 1) % len;"),
+    "append_rows_v_into_k": (
+        "cache[dk + d] = k_new[src + d];\n                    cache[dv + d] = v_new[src + d];",
+        "cache[dk + d] = v_new[src + d];\n                    cache[dv + d] = v_new[src + d];"),
     "rope_sin_sign": (
         "y[i] = lo * c - hi * s;",
         "y[i] = lo * c + hi * s;"),

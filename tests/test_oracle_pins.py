@@ -437,12 +437,108 @@ def pin_norm_rope_write_is_append(lib):
     np.testing.assert_array_equal(q2, k_out)
 
 
+# ---- several new rows per entry: append at the last positions, causal attention
+
+def _rows_case(seed, hq, hkv, d, ps, lengths, nrows):
+    rng = np.random.default_rng(seed)
+    table = table_from_lengths(np.asarray(lengths), np.ones(len(lengths), bool), ps, None,
+                               rng)
+    cache = bf16_bits(rng.normal(size=(NUM_LAYERS, table.num_pages, 2, ps, hkv, d)))
+    qo = np.concatenate([[0], np.cumsum(nrows)]).astype(np.int32)
+    rows = int(qo[-1])
+    q = bf16_bits(rng.normal(size=(rows, hq, d)))
+    kn = bf16_bits(rng.normal(size=(rows, hkv, d)))
+    vn = bf16_bits(rng.normal(size=(rows, hkv, d)))
+    return table, cache, qo, q, kn, vn
+
+
+def _gather(cache, layer, table, b, kv):
+    """Contiguous [L, Hkv, D] K (kv 0) or V (kv 1) rows of entry b, in token order."""
+    pages = table.indices[table.indptr[b]:table.indptr[b + 1]]
+    rows = cache[layer, pages, kv].reshape(-1, cache.shape[4], cache.shape[5])
+    return rows[:int(table.lengths[b])]
+
+
+def pin_append_rows_positions(lib):
+    # Entry b's new rows land at token positions L - n .. L - 1 of its page
+    # list (read back through a contiguous gather); nothing else changes.
+    table, cache, qo, q, kn, vn = _rows_case(30, 4, 2, 8, 4, [9, 5, 12, 3], [4, 1, 0, 3])
+    before = cache.copy()
+    oracle.append_rows(cache, LAYER, kn, vn, qo, table.indptr, table.indices,
+                       table.last_len, lib=lib)
+    expect = before.copy()
+    for b in range(table.batch):
+        n, L = int(qo[b + 1] - qo[b]), int(table.lengths[b])
+        pages = table.indices[table.indptr[b]:table.indptr[b + 1]]
+        for j in range(n):
+            t = L - n + j
+            expect[LAYER, pages[t // 4], 0, t % 4] = kn[qo[b] + j]
+            expect[LAYER, pages[t // 4], 1, t % 4] = vn[qo[b] + j]
+        np.testing.assert_array_equal(_gather(cache, LAYER, table, b, 0)[L - n:],
+                                      kn[qo[b]:qo[b + 1]])
+    np.testing.assert_array_equal(cache, expect)
+
+
+def pin_prefill_causal_sdpa(lib):
+    # Brute force: each entry's K/V gathered contiguous, torch's fp64
+    # scaled_dot_product_attention with a bottom-right causal mask (row j
+    # sees tokens 0 .. L - n + j) and its own GQA grouping; lse by logsumexp.
+    for seed, (hq, hkv, d, ps, lengths, nrows) in enumerate([
+            (4, 2, 8, 4, [9, 5, 12, 7], [4, 1, 12, 2]),
+            (6, 3, 16, 8, [20, 1, 33], [20, 1, 5]),
+            (8, 8, 8, 1, [3, 6], [2, 6])]):
+        table, cache, qo, q, kn, vn = _rows_case(31 + seed, hq, hkv, d, ps, lengths, nrows)
+        oracle.append_rows(cache, LAYER, kn, vn, qo, table.indptr, table.indices,
+                           table.last_len, lib=lib)
+        scale = 0.37
+        out, lse = oracle.prefill(cache, LAYER, q, qo, table.indptr, table.indices,
+                                  table.last_len, scale, lib=lib)
+        for b in range(table.batch):
+            n, L = int(qo[b + 1] - qo[b]), int(table.lengths[b])
+            if n == 0:
+                continue
+            K = torch.from_numpy(bf16_to_f32(_gather(cache, LAYER, table, b, 0))).double()
+            V = torch.from_numpy(bf16_to_f32(_gather(cache, LAYER, table, b, 1))).double()
+            Q = torch.from_numpy(bf16_to_f32(q[qo[b]:qo[b + 1]])).double()
+            qh, kh, vh = Q.permute(1, 0, 2), K.permute(1, 0, 2), V.permute(1, 0, 2)
+            pos = torch.arange(n)[:, None] + (L - n)
+            mask = torch.arange(L)[None, :] <= pos                      # [n, L]
+            o = F.scaled_dot_product_attention(qh[None], kh[None], vh[None],
+                                               attn_mask=mask[None, None], scale=scale,
+                                               enable_gqa=True)[0]
+            grp = hq // hkv
+            s_ = torch.einsum("hnd,hld->hnl", qh, kh.repeat_interleave(grp, 0)) * scale
+            s_ = s_.masked_fill(~mask[None], float("-inf"))
+            ls = torch.logsumexp(s_, dim=-1)                            # [hq, n]
+            np.testing.assert_allclose(out[qo[b]:qo[b + 1]], o.permute(1, 0, 2).numpy(),
+                                       rtol=0, atol=1e-12, err_msg=f"case {seed} entry {b}")
+            np.testing.assert_allclose(lse[qo[b]:qo[b + 1]], ls.T.numpy(), rtol=0,
+                                       atol=1e-12)
+
+
+def pin_prefill_one_row_is_decode(lib):
+    # One new row per entry is a decode step: same cache after the append,
+    # same rows as the (separately pinned) decode.
+    table, cache, qo, q, kn, vn = _rows_case(35, 6, 2, 8, 4, [9, 5, 12, 1], [1, 1, 1, 1])
+    c2 = cache.copy()
+    oracle.append_rows(cache, LAYER, kn, vn, qo, table.indptr, table.indices,
+                       table.last_len, lib=lib)
+    _append(lib, c2, kn, vn, table)
+    np.testing.assert_array_equal(cache, c2)
+    out, lse = oracle.prefill(cache, LAYER, q, qo, table.indptr, table.indices,
+                              table.last_len, 0.5, lib=lib)
+    o2, l2 = _decode(lib, cache, q, table, 0.5)
+    np.testing.assert_array_equal(out, o2)
+    np.testing.assert_array_equal(lse, l2)
+
+
 PINS = [pin_golden, pin_dense_sdpa, pin_single_token, pin_zero_query,
         pin_constant_values, pin_one_hot_values_are_softmax, pin_huge_scores,
         pin_key_shift, pin_split_matches_unsplit, pin_page_relabel,
         pin_append_is_last_token, pin_append_then_single_token_decode,
         pin_bf16_round, pin_rms_norm_closed_form, pin_rope_worked_example,
-        pin_rope_relative_position, pin_norm_rope_write_is_append]
+        pin_rope_relative_position, pin_norm_rope_write_is_append,
+        pin_append_rows_positions, pin_prefill_causal_sdpa, pin_prefill_one_row_is_decode]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
