@@ -90,6 +90,39 @@ int pkv_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
                const int32_t *last_page_len, int32_t batch, hipStream_t stream);
 
 /*
+ * pkv_prefill -- paged prefill and mixed prefill + decode steps: several new
+ * rows per entry, appended and attended causally ("Adding a Model", "How a
+ * program runs": prefill runs several rows per request over the paged cache;
+ * "Supported Models", Qwen3-Omni / Qwen3-TTS notes: new prompts ride a decode
+ * step as one mixed step).
+ *
+ * Entry b brings n_b = qo_indptr[b+1] - qo_indptr[b] >= 0 rows (n_b = 1 is a
+ * decode row); the page table already counts them, so the entry holds
+ * L = (pages - 1) * page_size + last_page_len[b] tokens ending with them.
+ * Row j (global row r = qo_indptr[b] + j) sits at position p = L - n_b + j:
+ *   with k_new / v_new:  cache[layer, page(p), 0/1, slot(p), :, :] = k_new[r] / v_new[r]
+ *   out[r, hq, :] = sum_{t <= p} softmax_t(sm_scale * q[r, hq, :] . K_t) V_t
+ *   lse[r, hq]    = ln sum_{t <= p} exp(sm_scale * q[r, hq, :] . K_t)
+ * with KV head hq / (Hq / Hkv), as in pkv_decode.  The append runs before the
+ * attention (two launches in stream order), so rows see each other's keys.
+ *  q, out        bf16 [total rows, num_qo_heads, head_dim]; total rows =
+ *                qo_indptr[batch].
+ *  qo_indptr     int32 [batch + 1], non-decreasing, qo_indptr[0] == 0.
+ *  k_new, v_new  bf16 [total rows, num_kv_heads, head_dim], or both NULL when
+ *                the rows are already in the cache.
+ *  lse           fp32 [total rows, num_qo_heads], natural log, or NULL.
+ *  max_q_rows    host upper bound on any n_b (>= 1); it sizes the grid.
+ * Preconditions as for pkv_decode, plus n_b <= L and n_b <= max_q_rows; rows
+ * past max_q_rows are not computed.  head_dim 128 only (else
+ * PKV_ERR_UNSUPPORTED); batch <= 65535.  Uses matrix-core (MFMA) products.
+ */
+int pkv_prefill(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *q,
+                int32_t num_qo_heads, const int32_t *qo_indptr, const void *k_new,
+                const void *v_new, const int32_t *page_indptr, const int32_t *page_indices,
+                const int32_t *last_page_len, int32_t batch, int32_t max_q_rows,
+                float sm_scale, void *out, float *lse, hipStream_t stream);
+
+/*
  * pkv_qk_norm_rope_append -- the fused step that feeds decode on Qwen3-style
  * attention: per-head RMSNorm of q and k, rotary embedding at each entry's
  * position, and the KV write ("Supported Models", M* docs, Qwen3-Omni and

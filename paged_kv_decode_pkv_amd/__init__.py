@@ -88,6 +88,9 @@ def _load():
     lib.pkv_qk_norm_rope_append.argtypes = [p, CacheDesc, i32, p, i32, p, p, p, p, f32, f32,
                                             p, p, p, p, i32, p, p]
     lib.pkv_qk_norm_rope_append.restype = ctypes.c_int
+    lib.pkv_prefill.argtypes = [p, CacheDesc, i32, p, i32, p, p, p, p, p, p, i32, i32, f32,
+                                p, p, p]
+    lib.pkv_prefill.restype = ctypes.c_int
     lib.pkv_decode_workspace_size.argtypes = [CacheDesc, i32, i32, i32, i32]
     lib.pkv_decode_workspace_size.restype = sz
     lib.pkv_decode.argtypes = [p, CacheDesc, i32, p, i32, p, p, p, i32, ctypes.c_float,
@@ -228,6 +231,46 @@ def qk_norm_rope_append(kv_cache, layer: int, q, k_new, v_new, q_norm_weight,
     if rc != PKV_OK:
         raise PkvError(rc, "pkv_qk_norm_rope_append")
     return q_out
+
+
+def prefill(kv_cache, layer: int, q, qo_indptr, page_indptr, page_indices, last_page_len,
+            sm_scale: float, max_q_rows: int, k_new=None, v_new=None, out=None, lse=None,
+            with_lse: bool = True, stream=None):
+    """Several new rows per entry (qo_indptr): optional append of k_new/v_new
+    [rows, Hkv, D] at each entry's last positions, then the causal attention
+    of every row; returns (out [rows, Hq, D] bf16, lse [rows, Hq] fp32 or None)."""
+    import torch
+    desc = cache_desc(kv_cache)
+    batch = int(last_page_len.shape[0])
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError(f"q must be [rows, Hq, {desc.head_dim}], got {tuple(q.shape)}")
+    rows, hq = int(q.shape[0]), int(q.shape[1])
+    if tuple(qo_indptr.shape) != (batch + 1,):
+        raise ValueError("qo_indptr must be [batch + 1]")
+    append = k_new is not None or v_new is not None
+    if append:
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            if t is None or tuple(t.shape) != (rows, desc.num_kv_heads, desc.head_dim):
+                raise ValueError(f"{name} must be [rows, Hkv, D]")
+    dev = kv_cache.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((rows, hq), dtype=torch.float32, device=dev)
+    null = ctypes.c_void_p(0)
+    rc = lib.pkv_prefill(_dev_ptr(kv_cache, "kv_cache", torch.bfloat16), desc, int(layer),
+                         _dev_ptr(q, "q", torch.bfloat16, dev), hq,
+                         _dev_ptr(qo_indptr, "qo_indptr", torch.int32, dev),
+                         _dev_ptr(k_new, "k_new", torch.bfloat16, dev) if append else null,
+                         _dev_ptr(v_new, "v_new", torch.bfloat16, dev) if append else null,
+                         *_tables(kv_cache, page_indptr, page_indices, last_page_len), batch,
+                         int(max_q_rows), float(sm_scale),
+                         _dev_ptr(out, "out", torch.bfloat16, dev),
+                         null if lse is None else _dev_ptr(lse, "lse", torch.float32, dev),
+                         _stream(stream))
+    if rc != PKV_OK:
+        raise PkvError(rc, "pkv_prefill")
+    return out, lse
 
 
 def _decode_outputs(kv_cache, q, out, lse, with_lse, workspace, max_pages_per_req,

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
 SOURCES = [os.path.join(CSRC, "pkv_kernels.hip"), os.path.join(CSRC, "pkv_norm_rope.hip"),
-           os.path.join(CSRC, "pkv_api.cpp")]
+           os.path.join(CSRC, "pkv_prefill.hip"), os.path.join(CSRC, "pkv_api.cpp")]
 
 # Packed-fp32 VALU forms stay disabled in all device code.
 HIPCC_FLAGS = [

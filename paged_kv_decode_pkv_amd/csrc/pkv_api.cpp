@@ -330,6 +330,55 @@ int pkv_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void 
     return hip_status(pkv::launch_append(a, batch, stream));
 }
 
+int pkv_prefill(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *q,
+                int32_t num_qo_heads, const int32_t *qo_indptr, const void *k_new,
+                const void *v_new, const int32_t *page_indptr, const int32_t *page_indices,
+                const int32_t *last_page_len, int32_t batch, int32_t max_q_rows,
+                float sm_scale, void *out, float *lse, hipStream_t stream) {
+    int rc = check_desc(desc);
+    if (rc != PKV_OK)
+        return rc;
+    if (layer < 0 || layer >= desc.num_layers || batch < 0 || num_qo_heads < 1 ||
+        num_qo_heads % desc.num_kv_heads != 0 || max_q_rows < 1 || !isfinite(sm_scale))
+        return PKV_ERR_BAD_SHAPE;
+    if (!pkv::prefill_supported(desc.head_dim) || batch > 65535)
+        return PKV_ERR_UNSUPPORTED;
+    if (batch == 0)
+        return PKV_OK;
+    const bool append = k_new != nullptr || v_new != nullptr;
+    if (!kv_cache || !q || !qo_indptr || !page_indptr || !page_indices || !last_page_len ||
+        !out || (append && (!k_new || !v_new)))
+        return PKV_ERR_NULL_PTR;
+    if (!aligned16(kv_cache) || !aligned16(q) || !aligned16(out) ||
+        (append && (!aligned16(k_new) || !aligned16(v_new))))
+        return PKV_ERR_ALIGNMENT;
+    pkv::PrefillArgs a;
+    uint16_t *slab = static_cast<uint16_t *>(kv_cache) + (int64_t)layer * desc.num_pages * page_elems(desc);
+    a.cache = slab;
+    a.cache_w = append ? slab : nullptr;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k_new = static_cast<const uint16_t *>(k_new);
+    a.v_new = static_cast<const uint16_t *>(v_new);
+    a.out = static_cast<uint16_t *>(out);
+    a.lse = lse;
+    a.qo_indptr = qo_indptr;
+    a.indptr = page_indptr;
+    a.indices = page_indices;
+    a.last_len = last_page_len;
+    a.page_stride = page_elems(desc);
+    a.half_stride = desc.page_size * desc.num_kv_heads * desc.head_dim;
+    a.row_stride = desc.num_kv_heads * desc.head_dim;
+    a.num_pages = desc.num_pages;
+    a.page_size = desc.page_size;
+    a.num_qo_heads = num_qo_heads;
+    a.num_kv_heads = desc.num_kv_heads;
+    a.head_dim = desc.head_dim;
+    a.batch = batch;
+    a.max_rows = max_q_rows;
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    return hip_status(pkv::launch_prefill(a, append, stream));
+}
+
 int pkv_qk_norm_rope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
                             const void *q, int32_t num_qo_heads, const void *k_new,
                             const void *v_new, const void *q_norm_weight,

@@ -182,6 +182,39 @@ struct NormRopeArgs {
     double turns[64];
 };
 
+// Arguments of the paged prefill (several new rows per entry) kernels; offsets
+// in bf16 elements.
+struct PrefillArgs {
+    const uint16_t *cache;    // first element of this layer's slab
+    uint16_t *cache_w;        // same slab, written by the append, or null
+    const uint16_t *q;        // [rows, Hq, D]
+    const uint16_t *k_new;    // [rows, Hkv, D] or null
+    const uint16_t *v_new;
+    uint16_t *out;            // [rows, Hq, D]
+    float *lse;               // [rows, Hq] or null
+    const int32_t *qo_indptr; // [batch + 1] rows per entry
+    const int32_t *indptr;
+    const int32_t *indices;
+    const int32_t *last_len;
+    int64_t page_stride;      // 2 * page_size * Hkv * D
+    int32_t half_stride;      // page_size * Hkv * D
+    int32_t row_stride;       // Hkv * D
+    int32_t num_pages;
+    int32_t page_size;
+    int32_t num_qo_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t batch;
+    int32_t max_rows;         // host bound on any entry's new rows
+    float scale_log2;         // sm_scale * log2(e)
+};
+
+// True when the prefill kernels are built for head_dim.
+bool prefill_supported(int head_dim);
+
+// Enqueues the append of the new rows (when `append`), then the attention.
+hipError_t launch_prefill(const PrefillArgs &a, bool append, hipStream_t stream);
+
 // True when the fused norm/rope/write kernel is built for head_dim.
 bool norm_rope_supported(int head_dim);
 

@@ -1,0 +1,269 @@
+// pkv_prefill.hip -- paged prefill and mixed prefill + decode steps on gfx950
+// (MI355X): several new query rows per entry, appended to the paged cache and
+// attended causally over it.
+//
+// Entry b brings n_b = qo_indptr[b+1] - qo_indptr[b] new rows (a decode row
+// is n_b = 1); after the append its L tokens end with them, so row j sits at
+// position p = L - n_b + j and attends tokens 0 .. p ("Adding a Model",
+// "How a program runs": prefill runs several rows per request over the same
+// paged cache; "Supported Models", Qwen3-Omni / Qwen3-TTS notes: new prompts
+// ride a decode step as one mixed step).
+//
+// Several rows against the same keys make a dense contraction, so the
+// products run on the matrix cores (v_mfma_f32_16x16x16_bf16).  One wave
+// takes 16 columns: (row, query head) pairs of one entry and KV head, the G
+// heads of a row side by side.  Per 16-token tile of the entry's pages:
+//   S^T[t][c] = sum_d K[t][d] Q[c][d]      8 MFMAs (K = 16 values of d each)
+//   O^T[d][c] += sum_t V[t][d] P[c][t]     8 MFMAs per half of P (see below)
+// With lane l = 16 q + c (c = column, q = lane group), the MFMA gives lane l
+// the scores of column c for tokens 4q .. 4q + 3 of the tile, exactly the
+// B-operand slots of P^T in the second product, and it holds column c of
+// O^T: the online softmax of a column (its running maximum and sum, the
+// rescale of its outputs) stays within the lane and the three other lanes of
+// its column.  Within a 16-value group of d the order of the sum is free, so
+// lane group q takes d = 32 q + 4 m + r (m = MFMA index, r = element): each
+// lane reads 64 contiguous bytes of a K row (and of its q row), and 64 lanes
+// read a whole 16-token K tile.  The V tile goes through LDS (rows padded to
+// 272 bytes, so the four lane groups' transposed reads hit distinct banks):
+// the A operand of the second product wants four tokens at one d.
+// P is split into a bf16 high part and a bf16 remainder, two MFMAs each, so
+// the weights keep about 16 significant bits (a single bf16 P costs a few
+// thousandths of the output, too much for the parity bar).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kMaskedScore = -1e30f;   // log2-domain score of a masked token
+constexpr int kRowPad = 272;             // LDS bytes per staged V row (256 + 16)
+
+__device__ __forceinline__ short bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (short)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ float bf16_val(short s) {
+    return __uint_as_float((uint32_t)(uint16_t)s << 16);
+}
+
+// ---------------------------------------------------------------------------
+// Append of several rows per entry: workgroup (j, b) copies row j of entry b,
+// if it exists, into token position L - n_b + j.
+__global__ __launch_bounds__(256) void append_rows_kernel(PrefillArgs a) {
+    const int j = blockIdx.x, b = blockIdx.y;
+    const int r0 = a.qo_indptr[b];
+    const int n = a.qo_indptr[b + 1] - r0;
+    if (j >= n)
+        return;
+    const int p0 = a.indptr[b];
+    const int np = a.indptr[b + 1] - p0;
+    const int last = a.last_len[b];
+    if (np < 1 || last < 1 || last > a.page_size)
+        return;
+    const int len = (np - 1) * a.page_size + last;
+    if (n > len)
+        return;
+    const int t = len - n + j;
+    const int page = a.indices[p0 + t / a.page_size];
+    if (page < 0 || page >= a.num_pages)
+        return;
+    uint16_t *dst = a.cache_w + (int64_t)page * a.page_stride +
+                    (int64_t)(t % a.page_size) * a.row_stride;
+    const uint16_t *ks = a.k_new + (int64_t)(r0 + j) * a.row_stride;
+    const uint16_t *vs = a.v_new + (int64_t)(r0 + j) * a.row_stride;
+    const int words = a.row_stride >> 3;   // 16-byte words per row
+    for (int i = threadIdx.x; i < 2 * words; i += blockDim.x) {
+        const bool is_v = i >= words;
+        const int w = is_v ? i - words : i;
+        const uint4 val = reinterpret_cast<const uint4 *>(is_v ? vs : ks)[w];
+        reinterpret_cast<uint4 *>(dst + (is_v ? a.half_stride : 0))[w] = val;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Causal attention of the new rows: one wave per (16-column block, KV head,
+// entry).  D = 128.
+__global__ __launch_bounds__(64) void prefill_kernel(PrefillArgs a) {
+    constexpr int D = 128;
+    __shared__ __attribute__((aligned(16))) char vt[16 * kRowPad];
+    const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int l = threadIdx.x;
+    const int c = l & 15, q = l >> 4;
+    const int G = a.num_qo_heads / a.num_kv_heads;
+
+    const int r0 = a.qo_indptr[b];
+    const int n = a.qo_indptr[b + 1] - r0;
+    const int ncols = n * G;
+    if (cb * 16 >= ncols)
+        return;   // whole wave
+    const int p0 = a.indptr[b];
+    const int np = a.indptr[b + 1] - p0;
+    const int last = a.last_len[b];
+    if (np < 1 || last < 1 || last > a.page_size)
+        return;
+    const int len = (np - 1) * a.page_size + last;
+    if (n > len)
+        return;
+    const int32_t *pages = a.indices + p0;
+
+    // this lane's column: row j, head g of the KV head's group
+    const int col = cb * 16 + c;
+    const bool valid = col < ncols;
+    const int j = valid ? col / G : 0;
+    const int g = valid ? col % G : 0;
+    const int pos = valid ? len - n + j : -1;
+    const int last_col = min(ncols, cb * 16 + 16) - 1;
+    const int pmax = len - n + last_col / G;   // largest position of the block
+
+    // q: this lane's 32 values of d (lane group q takes d = 32 q .. 32 q + 31)
+    bf16x4_t qb[8];
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            a.q + ((int64_t)(r0 + j) * a.num_qo_heads + h * G + g) * D + 32 * q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = valid ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+            qb[2 * i] = bf16x4_t{(short)(v.x & 0xFFFF), (short)(v.x >> 16),
+                                 (short)(v.y & 0xFFFF), (short)(v.y >> 16)};
+            qb[2 * i + 1] = bf16x4_t{(short)(v.z & 0xFFFF), (short)(v.z >> 16),
+                                     (short)(v.w & 0xFFFF), (short)(v.w >> 16)};
+        }
+    }
+
+    f32x4_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = kMaskedScore;   // running maximum of column c (log2 domain)
+    float lsum = 0.f;         // this lane's share of the column's weight sum
+    const float c2 = a.scale_log2;
+    const uint16_t *kbase = a.cache + (int64_t)h * D + 32 * q;
+
+    for (int t0 = 0; t0 <= pmax; t0 += 16) {
+        // K rows and V rows of token t0 + c (this lane's 64 bytes of each)
+        const int tl = t0 + c;
+        uint4 kr[4], vr[4];
+        if (tl < len) {
+            int page = pages[tl / a.page_size];
+            page = (page >= 0 && page < a.num_pages) ? page : 0;   // bad table: no fault
+            const uint16_t *row = kbase + (int64_t)page * a.page_stride +
+                                  (int64_t)(tl % a.page_size) * a.row_stride;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kr[i] = reinterpret_cast<const uint4 *>(row)[i];
+                vr[i] = reinterpret_cast<const uint4 *>(row + a.half_stride)[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                kr[i] = vr[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        // stage V: row c of the tile, bytes 64 q .. 64 q + 63
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4 *>(vt + c * kRowPad + 64 * q + 16 * i) = vr[i];
+
+        // S^T tile
+        f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = kr[i];
+            const bf16x4_t k0 = {(short)(v.x & 0xFFFF), (short)(v.x >> 16),
+                                 (short)(v.y & 0xFFFF), (short)(v.y >> 16)};
+            const bf16x4_t k1 = {(short)(v.z & 0xFFFF), (short)(v.z >> 16),
+                                 (short)(v.w & 0xFFFF), (short)(v.w >> 16)};
+            s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(k0, qb[2 * i], s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(k1, qb[2 * i + 1], s, 0, 0, 0);
+        }
+        // scores of column c, tokens t0 + 4 q + r; causal and length mask
+        float sc[4];
+        float tmax = kMaskedScore;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 4 * q + r;
+            sc[r] = (t <= pos && t < len) ? s[r] * c2 : kMaskedScore;
+            tmax = fmaxf(tmax, sc[r]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float mn = fmaxf(m, tmax);
+        const float alpha = exp2f(m - mn);
+        m = mn;
+        lsum *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            o[i] *= alpha;
+        bf16x4_t phi, plo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float p = exp2f(sc[r] - mn);
+            lsum += p;
+            phi[r] = bf16_rne(p);
+            plo[r] = bf16_rne(p - bf16_val(phi[r]));
+        }
+        // O^T += V^T P^T: A operand = V[t0 + 4 q + r][16 blk + c]
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+            bf16x4_t va;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                va[r] = *reinterpret_cast<const short *>(vt + (4 * q + r) * kRowPad +
+                                                         2 * (16 * blk + c));
+            o[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, o[blk], 0, 0, 0);
+            o[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, o[blk], 0, 0, 0);
+        }
+    }
+
+    // the column's weight sum over its four lanes, then the outputs
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (!valid)
+        return;
+    const float inv = 1.f / lsum;
+    uint16_t *orow = a.out + ((int64_t)(r0 + j) * a.num_qo_heads + h * G + g) * D;
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+        // lane holds O^T[16 blk + 4 q + r][c]
+        const uint32_t w0 = (uint32_t)(uint16_t)bf16_rne(o[blk][0] * inv) |
+                            ((uint32_t)(uint16_t)bf16_rne(o[blk][1] * inv) << 16);
+        const uint32_t w1 = (uint32_t)(uint16_t)bf16_rne(o[blk][2] * inv) |
+                            ((uint32_t)(uint16_t)bf16_rne(o[blk][3] * inv) << 16);
+        *reinterpret_cast<uint2 *>(orow + 16 * blk + 4 * q) = make_uint2(w0, w1);
+    }
+    if (a.lse != nullptr && q == 0)
+        a.lse[(int64_t)(r0 + j) * a.num_qo_heads + h * G + g] =
+            (m + __log2f(lsum)) * 0.6931471805599453f;
+}
+
+}  // namespace
+
+bool prefill_supported(int head_dim) { return head_dim == 128; }
+
+hipError_t launch_prefill(const PrefillArgs &a, bool append, hipStream_t stream) {
+    PrefillArgs args = a;
+    void *params[] = {&args};
+    if (a.head_dim != 128 || a.batch > 65535 || a.num_kv_heads > 65535)
+        return hipErrorInvalidValue;
+    hipError_t err = hipSuccess;
+    if (append) {
+        err = hipLaunchKernel(reinterpret_cast<const void *>(&append_rows_kernel),
+                              dim3((unsigned)a.max_rows, (unsigned)a.batch), dim3(256), params,
+                              0, stream);
+        if (err != hipSuccess)
+            return err;
+    }
+    const int G = a.num_qo_heads / a.num_kv_heads;
+    const int64_t blocks = ((int64_t)a.max_rows * G + 15) / 16;
+    if (blocks > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_kernel),
+                           dim3((unsigned)blocks, (unsigned)a.num_kv_heads, (unsigned)a.batch),
+                           dim3(64), params, 0, stream);
+}
+
+}  // namespace pkv

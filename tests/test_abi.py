@@ -19,7 +19,8 @@ DESC = CacheDesc(2, 64, 16, 2, 64)
 
 def test_every_declared_symbol_is_exported():
     names = pkv.declared_functions()
-    assert set(names) == {"pkv_append", "pkv_qk_norm_rope_append", "pkv_decode_workspace_size",
+    assert set(names) == {"pkv_append", "pkv_qk_norm_rope_append", "pkv_prefill",
+                          "pkv_decode_workspace_size",
                           "pkv_append_decode", "pkv_decode", "pkv_plan", "pkv_run",
                           "pkv_validate_page_table", "pkv_status_string",
                           "pkv_last_hip_error"}
@@ -129,6 +130,28 @@ def test_norm_rope_validation(kw, code):
 def test_norm_rope_batch_zero_is_noop():
     assert _norm_rope(batch=0, q=NULL, k=NULL, v=NULL, qw=NULL, kw=NULL, pos=NULL,
                       q_out=NULL, cache=NULL, tables=(NULL, NULL, NULL)) == 0
+
+
+def _prefill(desc=CacheDesc(2, 64, 16, 2, 128), layer=0, q=FAKE, hq=4, qo=FAKE, k=FAKE,
+             v=FAKE, batch=3, maxr=8, scale=0.1, out=FAKE, tables=(FAKE, FAKE, FAKE)):
+    return lib.pkv_prefill(FAKE, desc, layer, q, hq, qo, k, v, *tables, batch, maxr, scale,
+                           out, NULL, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layer=2), -2), (dict(batch=-1), -2), (dict(hq=3), -2), (dict(maxr=0), -2),
+    (dict(scale=float("nan")), -2), (dict(desc=CacheDesc(2, 64, 16, 2, 64)), -3),
+    (dict(batch=70000), -3), (dict(q=NULL), -1), (dict(qo=NULL), -1), (dict(out=NULL), -1),
+    (dict(k=NULL), -1), (dict(tables=(FAKE, NULL, FAKE)), -1),
+    (dict(out=ctypes.c_void_p(0x100004)), -6),
+])
+def test_prefill_validation(kw, code):
+    assert _prefill(**kw) == code
+
+
+def test_prefill_batch_zero_is_noop():
+    assert _prefill(batch=0, q=NULL, qo=NULL, k=NULL, v=NULL, out=NULL,
+                    tables=(NULL, NULL, NULL)) == 0
 
 
 def _append_decode(k=FAKE, v=FAKE, layer=0, batch=3, chunk=0, hq=4, out=FAKE):

@@ -1,0 +1,137 @@
+"""Parity of the paged prefill / mixed step (several new rows per entry) with
+the fp64 oracle (GPU, through the C ABI).
+
+Bars: the multi-row append bit for bit (the whole cache compared).  Each
+output element within half a bf16 step of the fp64 value plus 1e-3 (the
+kernel rounds its fp32 result to bf16 once; a row that attends a few tokens
+returns values of single V rows, up to about 4.5 at unit variance, whose
+rounding alone passes the decode's absolute 1e-2), mean |err| within 2^-8 of
+the mean |output| plus 1e-4, lse within 1e-3.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_decode_pkv_amd as pkv
+from gpu_util import DEV, compare, table_to_dev, to_dev_u16, to_host_u16
+from workloads import bf16_bits, bf16_to_f32, table_from_lengths
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def check_rows(out, lse, ref_out, ref_lse, what):
+    got = bf16_to_f32(to_host_u16(out)).astype(np.float64)
+    lg = lse.detach().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(lg)), f"{what}: non-finite"
+    err = np.abs(got - ref_out)
+    bound = 2.0 ** -8 * np.abs(ref_out) + 1e-3
+    steps = err / np.maximum(2.0 ** -7 * np.abs(ref_out), 1e-30)   # in bf16 steps
+    stats = {"out_max": float(err.max()), "out_mean": float(err.mean()),
+             "worst_in_bf16_steps": float(steps[err > 1e-3].max(initial=0.0)),
+             "lse_max": float(np.abs(lg - ref_lse).max())}
+    assert np.all(err <= bound), f"{what}: {stats}"
+    # the mean scales with the outputs' size, as rounding errors do
+    assert stats["out_mean"] <= 2.0 ** -8 * float(np.abs(ref_out).mean()) + 1e-4, \
+        f"{what}: {stats}"
+    assert stats["lse_max"] <= 1e-3, f"{what}: {stats}"
+    return stats
+
+
+def _case(seed, hq, hkv, ps, lengths, nrows, sigma=1.0):
+    rng = np.random.default_rng(seed)
+    lengths = np.asarray(lengths)
+    table = table_from_lengths(lengths, np.ones(len(lengths), bool), ps, None, rng)
+    cache = bf16_bits((rng.standard_normal((2, table.num_pages, 2, ps, hkv, D),
+                                           dtype=np.float32) * sigma))
+    qo = np.concatenate([[0], np.cumsum(nrows)]).astype(np.int32)
+    rows = int(qo[-1])
+    q = bf16_bits(rng.standard_normal((rows, hq, D), dtype=np.float32) * sigma)
+    kn = bf16_bits(rng.standard_normal((rows, hkv, D), dtype=np.float32) * sigma)
+    vn = bf16_bits(rng.standard_normal((rows, hkv, D), dtype=np.float32) * sigma)
+    return table, cache, qo, q, kn, vn
+
+
+def _run(table, cache, qo, q, kn, vn, scale, append=True, layer=1):
+    cache_dev = to_dev_u16(cache)
+    tabs = table_to_dev(table)
+    qo_dev = torch.from_numpy(qo).to(DEV)
+    maxr = int(np.max(np.diff(qo))) if len(qo) > 1 else 1
+    out, lse = pkv.prefill(cache_dev, layer, to_dev_u16(q), qo_dev, *tabs, scale,
+                           max(maxr, 1), k_new=to_dev_u16(kn) if append else None,
+                           v_new=to_dev_u16(vn) if append else None)
+    torch.cuda.synchronize()
+    host = cache.copy()
+    if append:
+        oracle.append_rows(host, layer, kn, vn, qo, table.indptr, table.indices,
+                           table.last_len)
+    ro, rl = oracle.prefill(host, layer, q, qo, table.indptr, table.indices,
+                            table.last_len, scale)
+    return cache_dev, out, lse, host, ro, rl
+
+
+CASES = [
+    # seed, hq, hkv, ps, lengths, rows per entry
+    (1, 32, 8, 16, [300, 40, 17, 1, 64, 129], [300, 1, 5, 1, 16, 0]),     # mixed step
+    (2, 8, 8, 16, [50, 33], [50, 33]),                                      # pure prefill, G 1
+    (3, 16, 8, 1, [20, 9, 31], [7, 1, 31]),                                 # one-token pages
+    (4, 16, 2, 128, [700, 129, 1000], [45, 2, 1]),                          # G 8, 128-token pages
+    (5, 24, 8, 16, [17, 16, 15, 33], [17, 1, 15, 32]),                      # G 3, ragged tiles
+    (6, 32, 8, 16, [1, 1, 1, 1, 1], [1, 1, 1, 1, 1]),                       # one token each
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"c{c[0]}" for c in CASES])
+def test_prefill_matches_oracle(case):
+    seed, hq, hkv, ps, lengths, nrows = case
+    print(f"prefill case {case}", flush=True)
+    table, cache, qo, q, kn, vn = _case(seed, hq, hkv, ps, lengths, nrows)
+    scale = 1.0 / np.sqrt(D)
+    cache_dev, out, lse, host, ro, rl = _run(table, cache, qo, q, kn, vn, scale)
+    np.testing.assert_array_equal(to_host_u16(cache_dev), host, err_msg="append")
+    if qo[-1]:
+        check_rows(out, lse, ro, rl, what=f"prefill case {seed}")
+
+
+def test_prefill_rows_already_in_cache():
+    # no k_new / v_new: the rows were appended before (here by the oracle)
+    table, cache, qo, q, kn, vn = _case(11, 32, 8, 16, [90, 260, 3], [12, 64, 3])
+    oracle.append_rows(cache, 1, kn, vn, qo, table.indptr, table.indices, table.last_len)
+    cache_dev, out, lse, host, ro, rl = _run(table, cache, qo, q, kn, vn, 0.09, append=False)
+    np.testing.assert_array_equal(to_host_u16(cache_dev), cache)
+    check_rows(out, lse, ro, rl, what="no append")
+
+
+def test_prefill_decode_rows_match_decode():
+    # one row per entry is a decode step: the prefill path and the decode path
+    # agree within the decode bars on the same cache
+    table, cache, qo, q, kn, vn = _case(12, 32, 8, 16, [500, 77, 1024, 9], [1, 1, 1, 1])
+    scale = 1.0 / np.sqrt(D)
+    cache_dev, out, lse, host, ro, rl = _run(table, cache, qo, q, kn, vn, scale)
+    tabs = table_to_dev(table)
+    o2, l2 = pkv.decode(cache_dev, 1, to_dev_u16(q), *tabs, scale,
+                        max_pages_per_req=table.max_pages_per_req)
+    torch.cuda.synchronize()
+    compare(out, lse, ro, rl, what="prefill path")
+    compare(o2, l2, ro, rl, what="decode path")
+
+
+def test_prefill_large_scores():
+    # sigma 4: scores spread over hundreds of log2 units; the running maximum
+    # and the split weights keep every row finite and on the oracle
+    table, cache, qo, q, kn, vn = _case(13, 16, 4, 16, [200, 48], [80, 48], sigma=4.0)
+    cache_dev, out, lse, host, ro, rl = _run(table, cache, qo, q, kn, vn, 1.0 / np.sqrt(D))
+    check_rows(out, lse, ro, rl, what="large scores")
