@@ -60,6 +60,17 @@ def parse():
     ap.add_argument("--qk-norm-rope", action="store_true",
                     help="per layer the fused q/k RMSNorm + rotary + KV write, then a "
                          "decode-only pkv_run on its q")
+    ap.add_argument("--prefill", action="store_true",
+                    help="a mixed step instead: decode rows plus whole new prompts, per "
+                         "layer pkv_prefill (append + causal attention)")
+    ap.add_argument("--prompt-rows", type=int, default=512,
+                    help="rows of each new prompt in the mixed step")
+    ap.add_argument("--decode-rows", type=int, default=60,
+                    help="decode entries (one row each) in the mixed step")
+    ap.add_argument("--one-call", action="store_true",
+                    help="mixed step as one pkv_prefill over all entries (default: the "
+                         "decode entries through pkv_plan + pkv_run, the prompts through "
+                         "pkv_prefill)")
     ap.add_argument("--probe-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter scale)")
     return ap.parse_args()
@@ -124,6 +135,8 @@ def main():
     if args.probe_copy:
         probe_copy(torch)
         return 0
+    if args.prefill:
+        return bench_prefill(args, torch)
 
     import paged_kv_decode_pkv_amd as pkv
     import workloads
@@ -416,6 +429,184 @@ def main():
         if nr is not None:
             result["norm_rope"]["cpu_oracle"] = norm_rope_oracle_time(table, Q, KN, VN, nr,
                                                                       by["norm_rope"])
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_prefill(args, torch):
+    """Mixed step on the Qwen3-4B-like shape: 60 decode rows (the first 60
+    entries of the batch-64 workload, one row each) plus 4 new prompts of
+    ``--prompt-rows`` rows that fill their entries; per layer one pkv_prefill
+    (append of every new row, causal attention of every row), 36 layers,
+    captured as one HIP graph."""
+    import paged_kv_decode_pkv_amd as pkv
+    import workloads
+    spec = workloads.CONFIGS[3]
+    base = workloads.make_table(spec)
+    nd, npr, pr = int(args.decode_rows), 4, int(args.prompt_rows)
+    lengths = np.concatenate([base.lengths[:nd], np.full(npr, pr)])
+    nrows = np.concatenate([np.ones(nd, np.int64), np.full(npr, pr)])
+    rng = np.random.default_rng([1000 * spec.cfg + 996, pr])
+    table = workloads.table_from_lengths(lengths, np.ones(len(lengths), bool),
+                                         spec.page_size, None, rng)
+    nl, hq, hkv, d, ps = (spec.num_layers, spec.num_qo_heads, spec.num_kv_heads,
+                          spec.head_dim, spec.page_size)
+    b = table.batch
+    qo_h = np.concatenate([[0], np.cumsum(nrows)]).astype(np.int32)
+    rows = int(qo_h[-1])
+    dev = torch.device("cuda:0")
+    log(f"mixed step: {nd} decode rows + {npr} prompts of {pr} rows = {rows} rows, "
+        f"{nl} layers, pool {table.num_pages} pages")
+    cache = torch.zeros((nl, table.num_pages, 2, ps, hkv, d), dtype=torch.bfloat16,
+                        device=dev)
+    gen = torch.Generator(device=dev).manual_seed(1000 * spec.cfg + 995)
+    Q = torch.randn((nl, rows, hq, d), generator=gen, device=dev).to(torch.bfloat16)
+    KN = torch.randn((nl, rows, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+    VN = torch.randn((nl, rows, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+    for layer in range(nl):
+        workloads.draw_layer_device(cache[layer], table, [1000 * spec.cfg + 900 + layer, b],
+                                    hq, spec.sigma)
+    tabs = [torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
+            for x in (table.indptr, table.indices, table.last_len)]
+    qo = torch.from_numpy(qo_h).to(dev)
+    out = torch.empty((nl, rows, hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((nl, rows, hq), dtype=torch.float32, device=dev)
+    maxr = int(nrows.max())
+    split = nd > 0 and not args.one_call
+    if split:
+        # the decode entries as a decode batch (plan once, fused append + decode
+        # per layer), the prompt entries as a prefill batch: two tables over the
+        # same pages
+        def sub_table(entries):
+            ptr = np.concatenate([[0], np.cumsum([table.indptr[e + 1] - table.indptr[e]
+                                                  for e in entries])]).astype(np.int32)
+            idx = np.concatenate([table.indices[table.indptr[e]:table.indptr[e + 1]]
+                                  for e in entries]).astype(np.int32)
+            ll = table.last_len[entries].astype(np.int32)
+            return [torch.from_numpy(x).to(dev) for x in (ptr, idx, ll)]
+        dec_e, pr_e = list(range(nd)), list(range(nd, b))
+        dtab, ptab = sub_table(dec_e), sub_table(pr_e)
+        dmaxp = int(max(table.indptr[e + 1] - table.indptr[e] for e in dec_e))
+        pqo = torch.from_numpy((np.concatenate([[0], np.cumsum(nrows[nd:])]) ).astype(
+            np.int32)).to(dev)
+        ws = torch.empty(max(pkv.workspace_size(pkv.cache_desc(cache), hq, nd, dmaxp, 0), 256),
+                         dtype=torch.uint8, device=dev)
+
+    def step():
+        if split:
+            plan = pkv.plan(cache, hq, *dtab, dmaxp, workspace=ws)
+            for layer in range(nl):
+                pkv.run(cache, layer, Q[layer][:nd], plan, spec.sm_scale,
+                        k_new=KN[layer][:nd], v_new=VN[layer][:nd], out=out[layer][:nd],
+                        lse=lse[layer][:nd])
+                pkv.prefill(cache, layer, Q[layer][nd:], pqo, *ptab, spec.sm_scale, pr,
+                            k_new=KN[layer][nd:], v_new=VN[layer][nd:], out=out[layer][nd:],
+                            lse=lse[layer][nd:])
+            return
+        for layer in range(nl):
+            pkv.prefill(cache, layer, Q[layer], qo, *tabs, spec.sm_scale, maxr,
+                        k_new=KN[layer], v_new=VN[layer], out=out[layer], lse=lse[layer])
+
+    stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            graph.replay()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record()
+        for i in range(args.steps):
+            graph.replay()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    step_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    p10, p50, p90 = (float(x) for x in np.percentile(step_ms, [10, 50, 90]))
+
+    # algorithmic work per layer: every row's q.k and p.v over the tokens up to
+    # its position; bytes: each entry's K/V once, q and out, the new rows'
+    # read and their write into the cache
+    pos_count = 0
+    for i in range(b):
+        n, L = int(nrows[i]), int(lengths[i])
+        pos_count += n * (L - n) + n * (n + 1) // 2      # sum over rows of (p + 1)
+    flops = 4 * d * hq * pos_count
+    kv = int(lengths.sum()) * 2 * hkv * d * 2
+    by = kv + 2 * rows * hq * d * 2 + rows * hq * 4 + 4 * rows * hkv * d * 2
+    launch_us = step_ms.mean() * 1e3 / nl
+    gbs = by / (launch_us * 1e-6) / 1e9
+    tflops = flops / (launch_us * 1e-6) / 1e12
+    log(f"per layer {launch_us:.2f} us: {gbs:.0f} GB/s algorithmic, {tflops:.1f} TFLOP/s")
+
+    result = {
+        "metric": "paged prefill / mixed step: achieved HBM GB/s and TFLOP/s",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"qwen3_4b_like_mixed_{nd}dec_{npr}x{pr}prompt_36l",
+                   "entries": b, "rows": rows, "layers": nl, "num_qo_heads": hq,
+                   "num_kv_heads": hkv, "head_dim": d, "page_size": ps,
+                   "call": ("pkv_plan + per layer pkv_run (decode entries) and pkv_prefill "
+                            "(prompt entries)") if split else
+                           "pkv_prefill (append + causal attention) over all entries",
+                   "hip_graph": True},
+        "ms_per_step_p10_median_p90": [round(p10, 5), round(p50, 5), round(p90, 5)],
+        "roofline": {"bound": "hbm",
+                     "kernel": ("run_kernel + prefill_kernel (+ append_rows_kernel)" if split
+                                else "prefill_kernel (+ append_rows_kernel)"),
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": by,
+                     "avg_launch_us": round(launch_us, 3),
+                     "flops_per_launch": flops, "tflops": round(tflops, 2),
+                     "mfma_bf16_peak_tflops": 2500.0,
+                     "timing": "HIP events between graph replays of the 36-layer step; "
+                               "per layer = step / 36 (all launches of the layer)"},
+    }
+    if not args.no_check:
+        # sampled rows of layer 0 against the oracle: two decode rows, the
+        # first, middle and last rows of one prompt
+        import oracle
+        ent = [0, 1, nd] if nd > 1 else [nd]
+        picks = ([(0, 0), (1, 0)] if nd > 1 else []) + [(nd, 0), (nd, pr // 2), (nd, pr - 1)]
+        mini, ip, ix, ll = _host_entries(table, cache[0], ent, torch)
+        qsub = np.concatenate([[0], np.cumsum([nrows[e] for e in ent])]).astype(np.int32)
+        qh = np.concatenate([_u16(Q[0])[qo_h[e]:qo_h[e + 1]] for e in ent])
+        ro, rl = oracle.prefill(mini, 0, qh, qsub, ip, ix, ll, spec.sm_scale)
+        worst = {"out_max": 0.0, "lse_max": 0.0, "rows": len(picks) * hq}
+        for e, j in picks:
+            k = ent.index(e)
+            r_g, r_s = qo_h[e] + j, qsub[k] + j
+            og = workloads.bf16_to_f32(_u16(out[0, r_g])).astype(np.float64)
+            err = np.abs(og - ro[r_s])
+            worst["out_max"] = max(worst["out_max"], float(err.max()))
+            worst["lse_max"] = max(worst["lse_max"], float(np.abs(
+                lse[0, r_g].cpu().numpy() - rl[r_s]).max()))
+        worst["pass"] = bool(worst["out_max"] <= 2e-2 and worst["lse_max"] <= 1e-3)
+        result["parity"] = worst
+        log(f"parity on sampled rows: {worst}")
+    if not args.no_cpu_baseline:
+        import oracle
+        ent = [0, nd] if nd > 0 else [0]
+        mini, ip, ix, ll = _host_entries(table, cache[0], ent, torch)
+        qsub = np.concatenate([[0], np.cumsum([nrows[e] for e in ent])]).astype(np.int32)
+        qh = np.concatenate([_u16(Q[0])[qo_h[e]:qo_h[e + 1]] for e in ent])
+        t = time.perf_counter()
+        oracle.prefill(mini, 0, qh, qsub, ip, ix, ll, spec.sm_scale)
+        dt = time.perf_counter() - t
+        f_s = 4 * d * hq * sum(int(nrows[e]) * (int(lengths[e]) - int(nrows[e]))
+                               + int(nrows[e]) * (int(nrows[e]) + 1) // 2 for e in ent)
+        result["cpu_baseline"] = {"value": round(f_s / dt / 1e12, 6), "unit": "TFLOP/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"layer 0, one decode row and one {pr}-row "
+                                            f"prompt, {dt:.2f} s"}
     print(json.dumps(result), flush=True)
     return 0
 

@@ -85,6 +85,88 @@ __global__ __launch_bounds__(256) void append_rows_kernel(PrefillArgs a) {
     }
 }
 
+// This lane's 64 bytes of the K row and of the V row of token tl; past the
+// entry's last token the last token's rows are read again (their weight is
+// zero, and a real token's values are finite).  kbase points at the lane's
+// bytes of the KV head's row in a page.
+__device__ __forceinline__ void load_tile(const PrefillArgs &a, const int32_t *pages,
+                                          const uint16_t *kbase, int len, int tl, uint4 *kr,
+                                          uint4 *vr) {
+    const int t = min(tl, len - 1);
+    int page = pages[t / a.page_size];
+    page = (page >= 0 && page < a.num_pages) ? page : 0;   // bad table: no fault
+    const uint16_t *row = kbase + (int64_t)page * a.page_stride +
+                          (int64_t)(t % a.page_size) * a.row_stride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        kr[i] = reinterpret_cast<const uint4 *>(row)[i];
+        vr[i] = reinterpret_cast<const uint4 *>(row + a.half_stride)[i];
+    }
+}
+
+// One 16-token tile of a wave's columns: S^T, the causal mask, the online
+// softmax update of each column and O^T += V^T P^T.  kr / vr hold this lane's
+// 64 bytes of the K and V rows of token t0 + c.
+__device__ __forceinline__ void attend_tile(const uint4 *kr, const uint4 *vr, int t0, int c,
+                                            int q, int pos, int len, float c2,
+                                            const bf16x4_t *qb, char *vt, f32x4_t *o,
+                                            float &m, float &lsum) {
+    // stage V: row c of the tile, bytes 64 q .. 64 q + 63
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4 *>(vt + c * kRowPad + 64 * q + 16 * i) = vr[i];
+
+    // S^T tile
+    f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 v = kr[i];
+        const bf16x4_t k0 = {(short)(v.x & 0xFFFF), (short)(v.x >> 16),
+                             (short)(v.y & 0xFFFF), (short)(v.y >> 16)};
+        const bf16x4_t k1 = {(short)(v.z & 0xFFFF), (short)(v.z >> 16),
+                             (short)(v.w & 0xFFFF), (short)(v.w >> 16)};
+        s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(k0, qb[2 * i], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(k1, qb[2 * i + 1], s, 0, 0, 0);
+    }
+    // scores of column c, tokens t0 + 4 q + r; causal and length mask
+    float sc[4];
+    float tmax = kMaskedScore;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 4 * q + r;
+        sc[r] = (t <= pos && t < len) ? s[r] * c2 : kMaskedScore;
+        tmax = fmaxf(tmax, sc[r]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mn = fmaxf(m, tmax);
+    const float alpha = exp2f(m - mn);
+    m = mn;
+    lsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        o[i] *= alpha;
+    bf16x4_t phi, plo;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float p = exp2f(sc[r] - mn);
+        lsum += p;
+        phi[r] = bf16_rne(p);
+        plo[r] = bf16_rne(p - bf16_val(phi[r]));
+    }
+    // O^T += V^T P^T: A operand = V[t0 + 4 q + r][16 blk + c]
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+        bf16x4_t va;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            va[r] = *reinterpret_cast<const short *>(vt + (4 * q + r) * kRowPad +
+                                                     2 * (16 * blk + c));
+        o[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, o[blk], 0, 0, 0);
+        o[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, o[blk], 0, 0, 0);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Causal attention of the new rows: one wave per (16-column block, KV head,
 // entry).  D = 128.
@@ -144,79 +226,20 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillArgs a) {
     const float c2 = a.scale_log2;
     const uint16_t *kbase = a.cache + (int64_t)h * D + 32 * q;
 
-    for (int t0 = 0; t0 <= pmax; t0 += 16) {
-        // K rows and V rows of token t0 + c (this lane's 64 bytes of each)
-        const int tl = t0 + c;
-        uint4 kr[4], vr[4];
-        if (tl < len) {
-            int page = pages[tl / a.page_size];
-            page = (page >= 0 && page < a.num_pages) ? page : 0;   // bad table: no fault
-            const uint16_t *row = kbase + (int64_t)page * a.page_stride +
-                                  (int64_t)(tl % a.page_size) * a.row_stride;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                kr[i] = reinterpret_cast<const uint4 *>(row)[i];
-                vr[i] = reinterpret_cast<const uint4 *>(row + a.half_stride)[i];
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                kr[i] = vr[i] = make_uint4(0u, 0u, 0u, 0u);
-        }
-        // stage V: row c of the tile, bytes 64 q .. 64 q + 63
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4 *>(vt + c * kRowPad + 64 * q + 16 * i) = vr[i];
-
-        // S^T tile
-        f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint4 v = kr[i];
-            const bf16x4_t k0 = {(short)(v.x & 0xFFFF), (short)(v.x >> 16),
-                                 (short)(v.y & 0xFFFF), (short)(v.y >> 16)};
-            const bf16x4_t k1 = {(short)(v.z & 0xFFFF), (short)(v.z >> 16),
-                                 (short)(v.w & 0xFFFF), (short)(v.w >> 16)};
-            s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(k0, qb[2 * i], s, 0, 0, 0);
-            s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(k1, qb[2 * i + 1], s, 0, 0, 0);
-        }
-        // scores of column c, tokens t0 + 4 q + r; causal and length mask
-        float sc[4];
-        float tmax = kMaskedScore;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = t0 + 4 * q + r;
-            sc[r] = (t <= pos && t < len) ? s[r] * c2 : kMaskedScore;
-            tmax = fmaxf(tmax, sc[r]);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mn = fmaxf(m, tmax);
-        const float alpha = exp2f(m - mn);
-        m = mn;
-        lsum *= alpha;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            o[i] *= alpha;
-        bf16x4_t phi, plo;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float p = exp2f(sc[r] - mn);
-            lsum += p;
-            phi[r] = bf16_rne(p);
-            plo[r] = bf16_rne(p - bf16_val(phi[r]));
-        }
-        // O^T += V^T P^T: A operand = V[t0 + 4 q + r][16 blk + c]
-#pragma unroll
-        for (int blk = 0; blk < 8; ++blk) {
-            bf16x4_t va;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                va[r] = *reinterpret_cast<const short *>(vt + (4 * q + r) * kRowPad +
-                                                         2 * (16 * blk + c));
-            o[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, o[blk], 0, 0, 0);
-            o[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, o[blk], 0, 0, 0);
-        }
+    // K rows and V rows of token t0 + c of a tile (this lane's 64 bytes of
+    // each), in two register sets: the next tile's loads are issued before
+    // the current tile is computed
+    uint4 ka[4], va[4], kb[4], vb[4];
+    load_tile(a, pages, kbase, len, c, ka, va);
+    // (the loads are unconditional, of a clamped token past the end, so the
+    // compiler can wait for exactly the older set)
+    for (int t0 = 0; t0 <= pmax; t0 += 32) {
+        load_tile(a, pages, kbase, len, t0 + 16 + c, kb, vb);
+        attend_tile(ka, va, t0, c, q, pos, len, c2, qb, vt, o, m, lsum);
+        if (t0 + 16 > pmax)
+            break;
+        load_tile(a, pages, kbase, len, t0 + 32 + c, ka, va);
+        attend_tile(kb, vb, t0 + 16, c, q, pos, len, c2, qb, vt, o, m, lsum);
     }
 
     // the column's weight sum over its four lanes, then the outputs
