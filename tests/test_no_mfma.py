@@ -1,12 +1,16 @@
-"""The decode path is bandwidth-bound and runs on the vector ALUs: the built
-library's gfx950 code holds no matrix-core (MFMA) instruction.
+"""Which kernels of the built library use the matrix cores (CPU only).
 
 Decode streams 4 D bytes of K/V per token and KV head against 4 g D flops, g =
 2..7 flops per byte, below the fp32 vector ridge of MI355X; one query row per
-entry is not a dense contraction, so matrix cores have nothing to do.  This
-reads the code object of the library built here (the clang offload bundle in
-its .hip_fatbin section) and disassembles it with the ROCm llvm-objdump."""
+entry is not a dense contraction, so the decode kernels (and the append, the
+plan and the fused norm/rotary step) hold no matrix-core (MFMA) instruction.
+The paged prefill, several rows against the same keys, is a dense contraction
+and does use them.  This reads every gfx950 code object of the library built
+here (one clang offload bundle per source file, in its .hip_fatbin section),
+disassembles them with the ROCm llvm-objdump and sorts the MFMA instructions
+by the kernel they sit in."""
 import os
+import re
 import struct
 import subprocess
 
@@ -18,30 +22,54 @@ OBJDUMP = "/opt/rocm/llvm/bin/llvm-objdump"
 MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 
 
-def _gfx950_code_object(blob: bytes) -> bytes:
-    """The gfx950 entry of the library's (uncompressed) clang offload bundle:
-    magic, entry count, then per entry {offset, size, triple length, triple}."""
+def _gfx950_code_objects(blob: bytes):
+    """The gfx950 entries of every (uncompressed) clang offload bundle in the
+    library: magic, entry count, then per entry {offset, size, triple length,
+    triple}."""
+    found = []
     base = blob.find(MAGIC)
-    assert base >= 0, "no offload bundle in the library"
-    (count,) = struct.unpack_from("<Q", blob, base + len(MAGIC))
-    pos = base + len(MAGIC) + 8
-    for _ in range(count):
-        off, size, tlen = struct.unpack_from("<QQQ", blob, pos)
-        pos += 24
-        triple = blob[pos:pos + tlen].decode()
-        pos += tlen
-        if triple.endswith("gfx950"):
-            return blob[base + off:base + off + size]
-    raise AssertionError("no gfx950 code object in the bundle")
+    while base >= 0:
+        (count,) = struct.unpack_from("<Q", blob, base + len(MAGIC))
+        pos = base + len(MAGIC) + 8
+        for _ in range(count):
+            off, size, tlen = struct.unpack_from("<QQQ", blob, pos)
+            pos += 24
+            triple = blob[pos:pos + tlen].decode()
+            pos += tlen
+            if triple.endswith("gfx950"):
+                found.append(blob[base + off:base + off + size])
+        base = blob.find(MAGIC, base + len(MAGIC))
+    assert found, "no gfx950 code object in the library"
+    return found
+
+
+def _mfma_by_kernel(asm: str) -> dict:
+    counts, current = {}, None
+    for line in asm.splitlines():
+        m = re.match(r"^[0-9a-f]+ <(.+)>:$", line)
+        if m:
+            current = m.group(1)
+            counts.setdefault(current, 0)
+        elif current is not None and ("v_mfma" in line or "v_smfmac" in line):
+            counts[current] += 1
+    return counts
 
 
 @pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
 @pytest.mark.skipif(not os.path.exists(OBJDUMP), reason="ROCm llvm-objdump missing")
-def test_no_mfma_in_decode_library(tmp_path):
-    co = tmp_path / "pkv_gfx950.co"
-    co.write_bytes(_gfx950_code_object(open(LIB, "rb").read()))
-    asm = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", str(co)], capture_output=True,
-                         text=True, check=True).stdout
-    assert "v_dot2" in asm, "disassembly holds none of the kernels' bf16 dot products"
-    assert "global_load_lds_dwordx4" in asm
-    assert "v_mfma" not in asm and "v_smfmac" not in asm
+def test_matrix_cores_only_in_prefill(tmp_path):
+    counts, asm_all = {}, ""
+    for i, code in enumerate(_gfx950_code_objects(open(LIB, "rb").read())):
+        co = tmp_path / f"pkv_gfx950_{i}.co"
+        co.write_bytes(code)
+        asm = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", str(co)], capture_output=True,
+                             text=True, check=True).stdout
+        asm_all += asm
+        for k, v in _mfma_by_kernel(asm).items():
+            counts[k] = counts.get(k, 0) + v
+    assert "v_dot2" in asm_all and "global_load_lds_dwordx4" in asm_all
+    names = list(counts)
+    for kernel in ("run_kernel", "plan_kernel", "append_kernel", "norm_rope_kernel"):
+        assert any(kernel in n for n in names), f"{kernel} not found"
+    with_mfma = {n: c for n, c in counts.items() if c}
+    assert with_mfma and all("prefill_kernel" in n for n in with_mfma), with_mfma
