@@ -42,6 +42,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kMaskedScore = -1e30f;   // log2-domain score of a masked token
 constexpr int kRowPad = 272;             // LDS bytes per staged V row (256 + 16)
+constexpr int kColumnGroups = 2;         // groups of 16 columns per wave
 
 __device__ __forceinline__ short bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -104,55 +105,61 @@ __device__ __forceinline__ void load_tile(const PrefillArgs &a, const int32_t *p
     }
 }
 
-// One 16-token tile of a wave's columns: S^T, the causal mask, the online
-// softmax update of each column and O^T += V^T P^T.  kr / vr hold this lane's
-// 64 bytes of the K and V rows of token t0 + c.
+// One 16-token tile of a wave's NG groups of 16 columns: S^T of each group,
+// the causal mask, the online softmax update of each column and O^T += V^T
+// P^T.  The groups share the tile's K/V loads, the V staging and the V^T
+// reads.  kr / vr hold this lane's 64 bytes of the K and V rows of token
+// t0 + c.
+template <int NG>
 __device__ __forceinline__ void attend_tile(const uint4 *kr, const uint4 *vr, int t0, int c,
-                                            int q, int pos, int len, float c2,
-                                            const bf16x4_t *qb, char *vt, f32x4_t *o,
-                                            float &m, float &lsum) {
+                                            int q, const int *pos, int len, float c2,
+                                            const bf16x4_t (*qb)[8], char *vt,
+                                            f32x4_t (*o)[8], float *m, float *lsum) {
     // stage V: row c of the tile, bytes 64 q .. 64 q + 63
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         *reinterpret_cast<uint4 *>(vt + c * kRowPad + 64 * q + 16 * i) = vr[i];
 
-    // S^T tile
-    f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x4_t phi[NG], plo[NG];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint4 v = kr[i];
-        const bf16x4_t k0 = {(short)(v.x & 0xFFFF), (short)(v.x >> 16),
-                             (short)(v.y & 0xFFFF), (short)(v.y >> 16)};
-        const bf16x4_t k1 = {(short)(v.z & 0xFFFF), (short)(v.z >> 16),
-                             (short)(v.w & 0xFFFF), (short)(v.w >> 16)};
-        s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(k0, qb[2 * i], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(k1, qb[2 * i + 1], s, 0, 0, 0);
-    }
-    // scores of column c, tokens t0 + 4 q + r; causal and length mask
-    float sc[4];
-    float tmax = kMaskedScore;
+    for (int gi = 0; gi < NG; ++gi) {
+        // S^T tile of the group
+        f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int t = t0 + 4 * q + r;
-        sc[r] = (t <= pos && t < len) ? s[r] * c2 : kMaskedScore;
-        tmax = fmaxf(tmax, sc[r]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mn = fmaxf(m, tmax);
-    const float alpha = exp2f(m - mn);
-    m = mn;
-    lsum *= alpha;
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = kr[i];
+            const bf16x4_t k0 = {(short)(v.x & 0xFFFF), (short)(v.x >> 16),
+                                 (short)(v.y & 0xFFFF), (short)(v.y >> 16)};
+            const bf16x4_t k1 = {(short)(v.z & 0xFFFF), (short)(v.z >> 16),
+                                 (short)(v.w & 0xFFFF), (short)(v.w >> 16)};
+            s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(k0, qb[gi][2 * i], s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(k1, qb[gi][2 * i + 1], s, 0, 0, 0);
+        }
+        // scores of column c, tokens t0 + 4 q + r; causal and length mask
+        float sc[4];
+        float tmax = kMaskedScore;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        o[i] *= alpha;
-    bf16x4_t phi, plo;
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 4 * q + r;
+            sc[r] = (t <= pos[gi] && t < len) ? s[r] * c2 : kMaskedScore;
+            tmax = fmaxf(tmax, sc[r]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float mn = fmaxf(m[gi], tmax);
+        const float alpha = exp2f(m[gi] - mn);
+        m[gi] = mn;
+        lsum[gi] *= alpha;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(sc[r] - mn);
-        lsum += p;
-        phi[r] = bf16_rne(p);
-        plo[r] = bf16_rne(p - bf16_val(phi[r]));
+        for (int i = 0; i < 8; ++i)
+            o[gi][i] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float p = exp2f(sc[r] - mn);
+            lsum[gi] += p;
+            phi[gi][r] = bf16_rne(p);
+            plo[gi][r] = bf16_rne(p - bf16_val(phi[gi][r]));
+        }
     }
     // O^T += V^T P^T: A operand = V[t0 + 4 q + r][16 blk + c]
 #pragma unroll
@@ -162,16 +169,23 @@ __device__ __forceinline__ void attend_tile(const uint4 *kr, const uint4 *vr, in
         for (int r = 0; r < 4; ++r)
             va[r] = *reinterpret_cast<const short *>(vt + (4 * q + r) * kRowPad +
                                                      2 * (16 * blk + c));
-        o[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, o[blk], 0, 0, 0);
-        o[blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, o[blk], 0, 0, 0);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            o[gi][blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi[gi], o[gi][blk], 0,
+                                                                   0, 0);
+            o[gi][blk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo[gi], o[gi][blk], 0,
+                                                                   0, 0);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Causal attention of the new rows: one wave per (16-column block, KV head,
 // entry).  D = 128.
+template <int NG>
 __global__ __launch_bounds__(64) void prefill_kernel(PrefillArgs a) {
     constexpr int D = 128;
+    constexpr int W = 16 * NG;   // columns per wave
     __shared__ __attribute__((aligned(16))) char vt[16 * kRowPad];
     const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int l = threadIdx.x;
@@ -181,7 +195,7 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillArgs a) {
     const int r0 = a.qo_indptr[b];
     const int n = a.qo_indptr[b + 1] - r0;
     const int ncols = n * G;
-    if (cb * 16 >= ncols)
+    if (cb * W >= ncols)
         return;   // whole wave
     const int p0 = a.indptr[b];
     const int np = a.indptr[b + 1] - p0;
@@ -192,75 +206,81 @@ __global__ __launch_bounds__(64) void prefill_kernel(PrefillArgs a) {
     if (n > len)
         return;
     const int32_t *pages = a.indices + p0;
-
-    // this lane's column: row j, head g of the KV head's group
-    const int col = cb * 16 + c;
-    const bool valid = col < ncols;
-    const int j = valid ? col / G : 0;
-    const int g = valid ? col % G : 0;
-    const int pos = valid ? len - n + j : -1;
-    const int last_col = min(ncols, cb * 16 + 16) - 1;
+    const int last_col = min(ncols, cb * W + W) - 1;
     const int pmax = len - n + last_col / G;   // largest position of the block
 
-    // q: this lane's 32 values of d (lane group q takes d = 32 q .. 32 q + 31)
-    bf16x4_t qb[8];
-    {
+    // this lane's columns (one per group): row j, head g of the KV head's group
+    int jj[NG], gg[NG], pos[NG];
+    bool valid[NG];
+    bf16x4_t qb[NG][8];
+    f32x4_t o[NG][8];
+    float m[NG], lsum[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        const int col = cb * W + 16 * gi + c;
+        valid[gi] = col < ncols;
+        jj[gi] = valid[gi] ? col / G : 0;
+        gg[gi] = valid[gi] ? col % G : 0;
+        pos[gi] = valid[gi] ? len - n + jj[gi] : -1;
+        // q: this lane's 32 values of d (lane group q takes d = 32 q .. 32 q + 31)
         const uint4 *src = reinterpret_cast<const uint4 *>(
-            a.q + ((int64_t)(r0 + j) * a.num_qo_heads + h * G + g) * D + 32 * q);
+            a.q + ((int64_t)(r0 + jj[gi]) * a.num_qo_heads + h * G + gg[gi]) * D + 32 * q);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint4 v = valid ? src[i] : make_uint4(0u, 0u, 0u, 0u);
-            qb[2 * i] = bf16x4_t{(short)(v.x & 0xFFFF), (short)(v.x >> 16),
-                                 (short)(v.y & 0xFFFF), (short)(v.y >> 16)};
-            qb[2 * i + 1] = bf16x4_t{(short)(v.z & 0xFFFF), (short)(v.z >> 16),
-                                     (short)(v.w & 0xFFFF), (short)(v.w >> 16)};
+            const uint4 v = valid[gi] ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+            qb[gi][2 * i] = bf16x4_t{(short)(v.x & 0xFFFF), (short)(v.x >> 16),
+                                     (short)(v.y & 0xFFFF), (short)(v.y >> 16)};
+            qb[gi][2 * i + 1] = bf16x4_t{(short)(v.z & 0xFFFF), (short)(v.z >> 16),
+                                         (short)(v.w & 0xFFFF), (short)(v.w >> 16)};
         }
-    }
-
-    f32x4_t o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m = kMaskedScore;   // running maximum of column c (log2 domain)
-    float lsum = 0.f;         // this lane's share of the column's weight sum
+        for (int i = 0; i < 8; ++i)
+            o[gi][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m[gi] = kMaskedScore;   // running maximum of the column (log2 domain)
+        lsum[gi] = 0.f;         // this lane's share of the column's weight sum
+    }
     const float c2 = a.scale_log2;
     const uint16_t *kbase = a.cache + (int64_t)h * D + 32 * q;
 
     // K rows and V rows of token t0 + c of a tile (this lane's 64 bytes of
     // each), in two register sets: the next tile's loads are issued before
-    // the current tile is computed
+    // the current tile is computed (unconditional loads of a clamped token
+    // past the end, so the compiler can wait for exactly the older set)
     uint4 ka[4], va[4], kb[4], vb[4];
     load_tile(a, pages, kbase, len, c, ka, va);
-    // (the loads are unconditional, of a clamped token past the end, so the
-    // compiler can wait for exactly the older set)
     for (int t0 = 0; t0 <= pmax; t0 += 32) {
         load_tile(a, pages, kbase, len, t0 + 16 + c, kb, vb);
-        attend_tile(ka, va, t0, c, q, pos, len, c2, qb, vt, o, m, lsum);
+        attend_tile<NG>(ka, va, t0, c, q, pos, len, c2, qb, vt, o, m, lsum);
         if (t0 + 16 > pmax)
             break;
         load_tile(a, pages, kbase, len, t0 + 32 + c, ka, va);
-        attend_tile(kb, vb, t0 + 16, c, q, pos, len, c2, qb, vt, o, m, lsum);
+        attend_tile<NG>(kb, vb, t0 + 16, c, q, pos, len, c2, qb, vt, o, m, lsum);
     }
 
-    // the column's weight sum over its four lanes, then the outputs
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
-    if (!valid)
-        return;
-    const float inv = 1.f / lsum;
-    uint16_t *orow = a.out + ((int64_t)(r0 + j) * a.num_qo_heads + h * G + g) * D;
 #pragma unroll
-    for (int blk = 0; blk < 8; ++blk) {
-        // lane holds O^T[16 blk + 4 q + r][c]
-        const uint32_t w0 = (uint32_t)(uint16_t)bf16_rne(o[blk][0] * inv) |
-                            ((uint32_t)(uint16_t)bf16_rne(o[blk][1] * inv) << 16);
-        const uint32_t w1 = (uint32_t)(uint16_t)bf16_rne(o[blk][2] * inv) |
-                            ((uint32_t)(uint16_t)bf16_rne(o[blk][3] * inv) << 16);
-        *reinterpret_cast<uint2 *>(orow + 16 * blk + 4 * q) = make_uint2(w0, w1);
+    for (int gi = 0; gi < NG; ++gi) {
+        // the column's weight sum over its four lanes, then the outputs
+        float ls = lsum[gi];
+        ls += __shfl_xor(ls, 16, 64);
+        ls += __shfl_xor(ls, 32, 64);
+        if (!valid[gi])
+            continue;
+        const float inv = 1.f / ls;
+        uint16_t *orow =
+            a.out + ((int64_t)(r0 + jj[gi]) * a.num_qo_heads + h * G + gg[gi]) * D;
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+            // lane holds O^T[16 blk + 4 q + r][c]
+            const uint32_t w0 = (uint32_t)(uint16_t)bf16_rne(o[gi][blk][0] * inv) |
+                                ((uint32_t)(uint16_t)bf16_rne(o[gi][blk][1] * inv) << 16);
+            const uint32_t w1 = (uint32_t)(uint16_t)bf16_rne(o[gi][blk][2] * inv) |
+                                ((uint32_t)(uint16_t)bf16_rne(o[gi][blk][3] * inv) << 16);
+            *reinterpret_cast<uint2 *>(orow + 16 * blk + 4 * q) = make_uint2(w0, w1);
+        }
+        if (a.lse != nullptr && q == 0)
+            a.lse[(int64_t)(r0 + jj[gi]) * a.num_qo_heads + h * G + gg[gi]] =
+                (m[gi] + __log2f(ls)) * 0.6931471805599453f;
     }
-    if (a.lse != nullptr && q == 0)
-        a.lse[(int64_t)(r0 + j) * a.num_qo_heads + h * G + g] =
-            (m + __log2f(lsum)) * 0.6931471805599453f;
 }
 
 }  // namespace
@@ -281,10 +301,11 @@ hipError_t launch_prefill(const PrefillArgs &a, bool append, hipStream_t stream)
             return err;
     }
     const int G = a.num_qo_heads / a.num_kv_heads;
-    const int64_t blocks = ((int64_t)a.max_rows * G + 15) / 16;
+    const int64_t blocks = ((int64_t)a.max_rows * G + 16 * kColumnGroups - 1) /
+                           (16 * kColumnGroups);
     if (blocks > 0x7fffffffLL)
         return hipErrorInvalidValue;
-    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_kernel),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_kernel<kColumnGroups>),
                            dim3((unsigned)blocks, (unsigned)a.num_kv_heads, (unsigned)a.batch),
                            dim3(64), params, 0, stream);
 }
