@@ -11,8 +11,10 @@
 //
 // Several rows against the same keys make a dense contraction, so the
 // products run on the matrix cores (v_mfma_f32_16x16x16_bf16).  One wave
-// takes 16 columns: (row, query head) pairs of one entry and KV head, the G
-// heads of a row side by side.  Per 16-token tile of the entry's pages:
+// takes two groups of 16 columns: (row, query head) pairs of one entry and
+// KV head, the G heads of a row side by side; the groups share each tile's
+// K/V loads, its V staging and its V^T reads.  Per 16-token tile of the
+// entry's pages and per group:
 //   S^T[t][c] = sum_d K[t][d] Q[c][d]      8 MFMAs (K = 16 values of d each)
 //   O^T[d][c] += sum_t V[t][d] P[c][t]     8 MFMAs per half of P (see below)
 // With lane l = 16 q + c (c = column, q = lane group), the MFMA gives lane l
