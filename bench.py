@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--qk-norm-rope", action="store_true",
                     help="per layer the fused q/k RMSNorm + rotary + KV write, then a "
                          "decode-only pkv_run on its q")
+    ap.add_argument("--fused-norm-rope", action="store_true",
+                    help="per layer one pkv_run_qk_norm_rope: the decode with the append "
+                         "and the q/k RMSNorm + rotary folded in")
     ap.add_argument("--prefill", action="store_true",
                     help="a mixed step instead: decode rows plus whole new prompts, per "
                          "layer pkv_prefill (append + causal attention)")
@@ -167,7 +170,7 @@ def main():
     out = torch.empty((nl, b, hq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((nl, b, hq), dtype=torch.float32, device=dev)
     nr = None
-    if args.qk_norm_rope:
+    if args.qk_norm_rope or args.fused_norm_rope:
         # per-layer RMSNorm weights, the new tokens' positions, the rotated q
         gen = torch.Generator(device=dev).manual_seed(1000 * spec.cfg + 997)
         nr = {"qw": (torch.rand((nl, d), generator=gen, device=dev) + 0.5).to(torch.bfloat16),
@@ -202,7 +205,13 @@ def main():
             res = (ctypes.c_float(spec.sm_scale), vp(out[layer].data_ptr()),
                    vp(lse[layer].data_ptr()), maxp, chunk, *ws_args, s)
             cl = []
-            if args.qk_norm_rope:
+            if args.fused_norm_rope:
+                cl.append((pkv.lib.pkv_run_qk_norm_rope,
+                           (vp(cache.data_ptr()), desc, layer, kn, vn, *qo, b,
+                            vp(nr["qw"][layer].data_ptr()), vp(nr["kw"][layer].data_ptr()),
+                            ctypes.c_float(nr["eps"]), ctypes.c_float(nr["theta"]),
+                            vp(nr["pos"].data_ptr()), *res), "pkv_run_qk_norm_rope"))
+            elif args.qk_norm_rope:
                 qo = (vp(nr["qo"][layer].data_ptr()), hq)
                 cl.append((pkv.lib.pkv_qk_norm_rope_append,
                            (vp(cache.data_ptr()), desc, layer, vp(Q[layer].data_ptr()), hq, kn,
@@ -229,7 +238,9 @@ def main():
             layers.append(cl)
         return plan, layers
 
-    if args.qk_norm_rope:
+    if args.fused_norm_rope:
+        call_name = "pkv_run_qk_norm_rope (norm + rotary + append + decode)"
+    elif args.qk_norm_rope:
         call_name = "pkv_qk_norm_rope_append + pkv_run"
     elif args.separate:
         call_name = "pkv_append + pkv_run"
@@ -369,10 +380,15 @@ def main():
         nr_us = n0.elapsed_time(n1) * 1e3 / (ksteps * reps * nl)
 
     by = workloads.algorithmic_bytes(table, hq, hkv, d)
-    step_bytes = nl * (by["decode"] + by["norm_rope"] if args.qk_norm_rope else by["total"])
+    if args.fused_norm_rope:
+        step_bytes = nl * by["fused_norm_rope"]
+    else:
+        step_bytes = nl * (by["decode"] + by["norm_rope"] if args.qk_norm_rope else by["total"])
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     rows_per_s = int(table.active.sum()) / (ms_step * 1e-3)
     launch_bytes = by["decode"] if (args.separate or args.qk_norm_rope) else by["total"]
+    if args.fused_norm_rope:
+        launch_bytes = by["fused_norm_rope"]
     dec_gbs = launch_bytes / (dec_us * 1e-6) / 1e9
     log(f"decode launch avg {dec_us:.2f} us (graph; eager with events {eager_us:.2f} us) "
         f"-> {dec_gbs:.0f} GB/s algorithmic; step {gbs:.0f} GB/s")
@@ -403,6 +419,7 @@ def main():
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic() if args.config == 3 and not args.separate
                      and not args.plan_per_layer and not args.qk_norm_rope
+                     and not args.fused_norm_rope
                      and args.chunk_pages == 0 else None,
                      "bytes_per_launch": launch_bytes, "avg_launch_us": round(dec_us, 3),
                      "launches": int(ksteps * launches_per_step),
@@ -426,7 +443,7 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(spec, table, cache, Q, KN, VN, torch,
                                               args.cpu_seconds)
-        if nr is not None:
+        if nr_us is not None:
             result["norm_rope"]["cpu_oracle"] = norm_rope_oracle_time(table, Q, KN, VN, nr,
                                                                       by["norm_rope"])
     print(json.dumps(result), flush=True)

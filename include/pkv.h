@@ -230,6 +230,37 @@ int pkv_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pkv_run_qk_norm_rope -- pkv_run with the append (k_new, v_new required) and
+ * the q/k RMSNorm and rotary embedding of pkv_qk_norm_rope_append folded into
+ * the same pass: one launch per layer instead of two for Qwen3-style
+ * attention ("Supported Models", M* docs, Qwen3-Omni and Qwen3-TTS notes: q/k
+ * norm, RoPE and KV write fused).  q is the raw projection; every workgroup
+ * that computes a run of an entry normalizes and rotates that entry's q rows
+ * itself, and the workgroup whose run holds the new token does the same to
+ * its k row before it uses and stores it.  The q rows are transformed with
+ * the same formulas as pkv_qk_norm_rope_append (fp32, angle reduced in fp64,
+ * rounded once to bf16) but are not written out; the cache receives the
+ * transformed k row and v_new's row, bit for bit, in the append's slot.
+ * Results match pkv_qk_norm_rope_append followed by pkv_run within rounding
+ * (the sum of squares adds in another order, so a q or k element can differ
+ * by one bf16 step).
+ *  q_norm_weight, k_norm_weight, eps, rope_theta, positions
+ *                 as for pkv_qk_norm_rope_append (16-byte aligned weights).
+ *  every other argument as for pkv_run.
+ * Supported: head_dim 128 with num_qo_heads / num_kv_heads in 1..4 (else
+ * PKV_ERR_UNSUPPORTED).  Padding entries write page 0 slot 0 as in pkv_append.
+ */
+int pkv_run_qk_norm_rope(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+                         const void *k_new, const void *v_new, const void *q,
+                         int32_t num_qo_heads, int32_t batch,
+                         const void *q_norm_weight, const void *k_norm_weight,
+                         float eps, float rope_theta, const int32_t *positions,
+                         float sm_scale, void *out, float *lse,
+                         int32_t max_pages_per_req, int32_t kv_chunk_pages,
+                         void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
  * pkv_decode -- grouped-query attention of one query row per entry over its
  * pages ("Adding a Model", section 1: run(q, kv_cache); "How a program
  * runs": lm_decode is one row per request).

@@ -104,6 +104,9 @@ def _load():
     lib.pkv_run.argtypes = [p, CacheDesc, i32, p, p, p, i32, i32, ctypes.c_float, p, p,
                             i32, i32, p, sz, p]
     lib.pkv_run.restype = ctypes.c_int
+    lib.pkv_run_qk_norm_rope.argtypes = [p, CacheDesc, i32, p, p, p, i32, i32, p, p, f32, f32,
+                                         p, f32, p, p, i32, i32, p, sz, p]
+    lib.pkv_run_qk_norm_rope.restype = ctypes.c_int
     lib.pkv_validate_page_table.argtypes = [p, p, p, i32, i32, i32, i32,
                                             ctypes.POINTER(i32)]
     lib.pkv_validate_page_table.restype = ctypes.c_int
@@ -420,6 +423,51 @@ def run(kv_cache, layer: int, q, plan_: DecodePlan, sm_scale: float, k_new=None,
                      _stream(stream))
     if rc != PKV_OK:
         raise PkvError(rc, "pkv_run")
+    return out, lse
+
+
+def run_qk_norm_rope(kv_cache, layer: int, q, plan_: DecodePlan, sm_scale: float, k_new,
+                     v_new, q_norm_weight, k_norm_weight, positions, eps: float = 1e-6,
+                     rope_theta: float = 1e6, out=None, lse=None, with_lse: bool = True,
+                     stream=None):
+    """Decode one layer on a plan with the append and the q/k RMSNorm + rotary
+    embedding folded in (pkv_run_qk_norm_rope): q, k_new are the raw
+    projections; returns (out, lse)."""
+    import torch
+    desc = cache_desc(kv_cache)
+    batch, hq, d = plan_.batch, plan_.num_qo_heads, desc.head_dim
+    if q.dim() != 3 or q.shape[0] != batch or q.shape[1] != hq:
+        raise ValueError("q must be [batch, Hq, D] of the plan")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t is None or tuple(t.shape) != (batch, desc.num_kv_heads, d):
+            raise ValueError(f"{name} must be [batch, Hkv, D]")
+    for name, t in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        if tuple(t.shape) != (d,):
+            raise ValueError(f"{name} must be [{d}], got {tuple(t.shape)}")
+    if tuple(positions.shape) != (batch,):
+        raise ValueError(f"positions must be [batch], got {tuple(positions.shape)}")
+    dev = kv_cache.device
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=torch.bfloat16, device=dev)
+    if lse is None and with_lse:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    null = ctypes.c_void_p(0)
+    ws = plan_.workspace
+    rc = lib.pkv_run_qk_norm_rope(
+        _dev_ptr(kv_cache, "kv_cache", torch.bfloat16), desc, int(layer),
+        _dev_ptr(k_new, "k_new", torch.bfloat16, dev),
+        _dev_ptr(v_new, "v_new", torch.bfloat16, dev),
+        _dev_ptr(q, "q", torch.bfloat16, dev), hq, batch,
+        _dev_ptr(q_norm_weight, "q_norm_weight", torch.bfloat16, dev),
+        _dev_ptr(k_norm_weight, "k_norm_weight", torch.bfloat16, dev),
+        float(eps), float(rope_theta), _dev_ptr(positions, "positions", torch.int32, dev),
+        float(sm_scale), _dev_ptr(out, "out", torch.bfloat16, dev),
+        null if lse is None else _dev_ptr(lse, "lse", torch.float32, dev),
+        plan_.max_pages_per_req, plan_.kv_chunk_pages,
+        _dev_ptr(ws, "workspace", device=dev), ws.numel() * ws.element_size(),
+        _stream(stream))
+    if rc != PKV_OK:
+        raise PkvError(rc, "pkv_run_qk_norm_rope")
     return out, lse
 
 

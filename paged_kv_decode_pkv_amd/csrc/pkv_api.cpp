@@ -235,6 +235,11 @@ int prepare_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void
     a.batch = batch;
     a.block_stride = block_stride;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
+    a.q_w = nullptr;
+    a.k_w = nullptr;
+    a.positions = nullptr;
+    a.eps = 0.f;
+    a.log2_theta = 0.0;
     r.blocks = reinterpret_cast<const int32_t *>(ws + lay.off_blocks);
     r.ent = reinterpret_cast<const int32_t *>(ws + lay.off_ent);
     r.num_blocks = num_blocks;
@@ -431,6 +436,42 @@ int pkv_qk_norm_rope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer
                          ? pow((double)rope_theta, -2.0 * i / desc.head_dim) / (2.0 * M_PI)
                          : 0.0;
     return hip_status(pkv::launch_norm_rope(a, stream));
+}
+
+int pkv_run_qk_norm_rope(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+                         const void *k_new, const void *v_new, const void *q,
+                         int32_t num_qo_heads, int32_t batch, const void *q_norm_weight,
+                         const void *k_norm_weight, float eps, float rope_theta,
+                         const int32_t *positions, float sm_scale, void *out, float *lse,
+                         int32_t max_pages_per_req, int32_t kv_chunk_pages, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_decode_args(desc, layer, num_qo_heads, batch, sm_scale, max_pages_per_req,
+                               kv_chunk_pages);
+    if (rc != PKV_OK)
+        return rc;
+    if (!(eps >= 0.0f) || !isfinite(eps) || !(rope_theta > 0.0f) || !isfinite(rope_theta))
+        return PKV_ERR_BAD_SHAPE;
+    if (!pkv::run_norm_rope_supported(desc.head_dim, num_qo_heads / desc.num_kv_heads))
+        return PKV_ERR_UNSUPPORTED;
+    if (batch == 0)
+        return PKV_OK;
+    if (!k_new || !v_new || !q_norm_weight || !k_norm_weight || !positions)
+        return PKV_ERR_NULL_PTR;
+    if (!aligned16(q_norm_weight) || !aligned16(k_norm_weight))
+        return PKV_ERR_ALIGNMENT;
+    RunLaunch r;
+    rc = prepare_run(kv_cache, desc, layer, k_new, v_new, q, num_qo_heads, batch, sm_scale,
+                     out, lse, max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes,
+                     r);
+    if (rc != PKV_OK)
+        return rc;
+    pkv::RunArgs &a = r.args;
+    a.q_w = static_cast<const uint16_t *>(q_norm_weight);
+    a.k_w = static_cast<const uint16_t *>(k_norm_weight);
+    a.positions = positions;
+    a.eps = eps;
+    a.log2_theta = log2((double)rope_theta);
+    return launch_run(r, desc, stream);
 }
 
 size_t pkv_decode_workspace_size(pkv_cache_desc_t desc, int32_t num_qo_heads, int32_t batch,

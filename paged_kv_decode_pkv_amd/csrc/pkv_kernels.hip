@@ -594,6 +594,10 @@ __device__ __forceinline__ void wait_vm_at_most(int n) {
 __device__ __forceinline__ void copy_to_lds(const void *src, uint32_t lds) {
     asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(lds) : "memory");
 }
+// 4 bytes per lane from src into LDS at byte address lds + 4 * lane.
+__device__ __forceinline__ void copy_dword_to_lds(const void *src, uint32_t lds) {
+    asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
 // The same from a wave-uniform base plus a 32-bit per-lane byte offset.
 __device__ __forceinline__ void copy_to_lds(const void *base, uint32_t off, uint32_t lds) {
     asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(base), "{m0}"(lds)
@@ -676,9 +680,101 @@ __device__ __forceinline__ float wave_max(float x, int lane) {
     return fmaxf(x, partner_lane<32>(x, lane));
 }
 
-template <int D, int G, int NBUF>
+// Fused q/k RMSNorm + rotary embedding of head rows held as 8 lanes x two
+// 8-element chunks (D = 128, 8 lanes per row: lane j holds elements 8 j .. 8 j
+// + 7 and 64 + 8 j .. 64 + 8 j + 7 as packed bf16 pairs, so each element's
+// rotate-half partner, D/2 away, is in the same lane).  y = x / sqrt(mean(x^2)
+// + eps) * w, then pair i = 8 j + t turns by pos * turns[i] (in turns, reduced
+// in fp64, sine and cosine in fp32); fp32 throughout, rounded to bf16 once.
+// The weights and the rates come from LDS: a vector memory load in the tile
+// loop would count in vmcnt behind the tile copies in flight, and waiting for
+// it would drain them.
+//
+// Per-wave LDS block of the fused step: q weight [128] bf16, k weight [128]
+// bf16, rates [64] fp64.
+constexpr int kNormRopeLds = 1024;
+
+// sin and cos of 2 pi x for |x| <= 1/2 (x in turns): the nearest quarter turn
+// q comes off exactly, the rest r (|r| <= 1/8 turn, |2 pi r| <= pi/4) goes
+// through the Taylor series of sin to degree 9 and of cos to degree 10
+// (truncation below 2e-9), then the result turns by q quarter turns.
+__device__ __forceinline__ void sincos_turns(float x, float &s, float &c) {
+    const float q = rintf(4.f * x);
+    const float t = fmaf(q, -0.25f, x) * 6.2831853071795865f;
+    const float t2 = t * t;
+    float ps = fmaf(t2, 2.7557319e-6f, -1.9841270e-4f);
+    ps = fmaf(t2, ps, 8.3333333e-3f);
+    ps = fmaf(t2, ps, -1.6666667e-1f);
+    const float sv = fmaf(t * t2, ps, t);
+    float pc = fmaf(t2, -2.7557319e-7f, 2.4801587e-5f);
+    pc = fmaf(t2, pc, -1.3888889e-3f);
+    pc = fmaf(t2, pc, 4.1666667e-2f);
+    pc = fmaf(t2, pc, -0.5f);
+    const float cv = fmaf(t2, pc, 1.0f);
+    const int qi = (int)q & 3;   // quarter turns, modulo a whole turn
+    const float s1 = (qi & 1) ? cv : sv;
+    const float c1 = (qi & 1) ? sv : cv;
+    s = (qi & 2) ? -s1 : s1;                    // q = 2, 3: sin negated
+    c = (qi == 1 || qi == 2) ? -c1 : c1;        // q = 1, 2: cos negated
+}
+
+// cos and sin of the lane's eight angles at position pos.
+__device__ __forceinline__ void rope_angles(const char *nrl, int j, double pos, float (&cs)[8],
+                                            float (&sn)[8]) {
+    const double *turns = reinterpret_cast<const double *>(nrl + 512) + 8 * j;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const double tn = pos * turns[t];
+        sincos_turns((float)(tn - rint(tn)), sn[t], cs[t]);
+    }
+}
+
+// One row: RMSNorm with weight row wsel (0: q, 1: k) and the rotation by the
+// lane's angles.  Every lane of the wave runs it (the sum of squares takes DPP
+// steps within each 8-lane row group).
+__device__ __forceinline__ void norm_rope_row(uint32_t (&x)[2][4], const char *nrl, int wsel,
+                                              int j, float eps, const float (&cs)[8],
+                                              const float (&sn)[8]) {
+    float f[2][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            f[c][2 * k] = bf16_lo(x[c][k]);
+            f[c][2 * k + 1] = bf16_hi(x[c][k]);
+            ss += f[c][2 * k] * f[c][2 * k] + f[c][2 * k + 1] * f[c][2 * k + 1];
+        }
+    ss = row_sum<8>(ss);
+    const float inv = 1.0f / sqrtf(ss / 128.0f + eps);
+    const uint4 *wrow = reinterpret_cast<const uint4 *>(nrl + 256 * wsel);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const uint4 wv = wrow[j + 8 * c];
+        const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            f[c][2 * k] = f[c][2 * k] * inv * bf16_lo(ww[k]);
+            f[c][2 * k + 1] = f[c][2 * k + 1] * inv * bf16_hi(ww[k]);
+        }
+    }
+    float z[2][8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        z[0][t] = f[0][t] * cs[t] - f[1][t] * sn[t];
+        z[1][t] = f[1][t] * cs[t] + f[0][t] * sn[t];
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            x[c][k] = pack_bf16x2(z[c][2 * k], z[c][2 * k + 1]);
+}
+
+template <int D, int G, int NBUF, bool NR = false>
 __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
-    RunArgs a, const int4 *__restrict__ blocks, const int4 *__restrict__ ent) {
+    RunArgs a, const int4 *__restrict__ blocks, const int4 *__restrict__ ent,
+    const int32_t *__restrict__ positions) {
     constexpr int LPR = (D == 128 && G > 4) ? 16 : 8;   // lanes per row
     constexpr int RG = 64 / LPR;               // row groups: rows the wave holds at once
     constexpr int RPL = kTileTokens / RG;      // rows per lane per tile
@@ -690,6 +786,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     constexpr int QB = G * D * 2;              // q bytes of one KV head's query heads
     constexpr int QI = (QB + 1023) / 1024;     // copies for them
     static_assert(NC >= 1 && RPL >= 1 && V >= 1, "unsupported head_dim");
+    static_assert(!NR || (D == 128 && LPR == 8), "the fused norm/rotary needs 8 lanes per row");
     // Vector memory stores a segment end issues (outputs and lse): they count
     // in vmcnt like the copies, so the waits below include them.
     // (fp16 partial outputs take as many stores as bf16 outputs)
@@ -722,6 +819,19 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     const int64_t half_bytes = (int64_t)a.half_stride * 2;
     const int64_t row_bytes = (int64_t)a.row_stride * 2;
 
+    // The fused step's weights and rates, in this wave's own LDS block: the
+    // weights by two copies issued ahead of every tile copy (so a tile that
+    // has landed implies they have), the rate of pair `lane`, theta^(-lane/64)
+    // / (2 pi), computed here in fp64.
+    const char *nrl = reinterpret_cast<const char *>(smem) + NBUF * buf_bytes +
+                      w * kNormRopeLds;
+    if constexpr (NR) {
+        const uint32_t nb = lds0 + NBUF * buf_bytes + (uint32_t)(w * kNormRopeLds);
+        copy_dword_to_lds(a.q_w + 2 * lane, nb);
+        copy_dword_to_lds(a.k_w + 2 * lane, nb + 256);
+        reinterpret_cast<double *>(const_cast<char *>(nrl) + 512)[lane] =
+            exp2(-(double)lane * (a.log2_theta / 64.0)) * 0.15915494309189535;
+    }
     const __amdgpu_buffer_rsrc_t ro = partial_rsrc(a.part_o, a.part_o_bytes);
     const __amdgpu_buffer_rsrc_t rl = partial_rsrc(a.part_lse, a.part_lse_bytes);
     const int4 *blk = blocks + (int64_t)blockIdx.x * a.block_stride;
@@ -915,6 +1025,22 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             const int info = rec.y;
             const uint4 *sb = smem + buf * buf_units;
             if (info & kInfoSegFirst) {
+                if constexpr (NR) {
+                    // row group rg normalizes and rotates query head rg in
+                    // place (the other groups compute a copy and keep it);
+                    // the loads below then give every group all G heads
+                    float cs[8], sn[8];
+                    rope_angles(nrl, j, (double)positions[rec.z], cs, sn);
+                    uint4 *qrow = smem + buf * buf_units + qunit + (rg < G ? rg : 0) * (D / 8);
+                    const uint4 v0 = qrow[0], v1 = qrow[8];
+                    uint32_t x[2][4] = {{v0.x, v0.y, v0.z, v0.w}, {v1.x, v1.y, v1.z, v1.w}};
+                    norm_rope_row(x, nrl, 0, j, a.eps, cs, sn);
+                    if (rg < G) {
+                        qrow[0] = make_uint4(x[0][0], x[0][1], x[0][2], x[0][3]);
+                        qrow[8] = make_uint4(x[1][0], x[1][1], x[1][2], x[1][3]);
+                    }
+                    asm volatile("" ::: "memory");
+                }
 #pragma unroll
                 for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -947,6 +1073,24 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                     kx[i][c] = sb[kunit + i * rstep + cu];
                     vx[i][c] = sb[part_units + kunit + i * rstep + cu];
                 }
+            if constexpr (NR) {
+                if (info & kInfoHasNew) {
+                    // the new row arrives raw from k_new: normalize and rotate
+                    // it here, in the row group holding it (every lane runs
+                    // the arithmetic; the others keep their rows), so the
+                    // dot product and the cache store below both see the
+                    // transformed row
+                    uint32_t kk[2][4] = {{kx[0][0].x, kx[0][0].y, kx[0][0].z, kx[0][0].w},
+                                         {kx[0][1].x, kx[0][1].y, kx[0][1].z, kx[0][1].w}};
+                    float cs[8], sn[8];
+                    rope_angles(nrl, j, (double)positions[rec.z], cs, sn);
+                    norm_rope_row(kk, nrl, 1, j, a.eps, cs, sn);
+                    if (rg == nr) {
+                        kx[0][0] = make_uint4(kk[0][0], kk[0][1], kk[0][2], kk[0][3]);
+                        kx[0][1] = make_uint4(kk[1][0], kk[1][1], kk[1][2], kk[1][3]);
+                    }
+                }
+            }
             // q.k: RPL x G independent dot products over the lane's chunks,
             // then their row sums step by step across all of them
             float d[RPL][G];
@@ -1311,15 +1455,34 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             if (a.lse != nullptr && j == 0)
                 a.lse[(int64_t)b * a.num_qo_heads + hq] = __builtin_nanf("");
         }
-        if (fused && rg == 0) {
+        if (fused) {
             const int64_t src = ((int64_t)b * a.num_kv_heads + h) * D + j * 8;
             uint16_t *dst = a.cache_w + (int64_t)e.z * a.page_stride +
                             (int64_t)e.w * a.row_stride + col;
+            uint4 kr[NC];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                store16(dst + 8 * LPR * c, load16(a.k_new + src + 8 * LPR * c));
-                store16(dst + 8 * LPR * c + a.half_stride,
-                        load16(a.v_new + src + 8 * LPR * c));
+            for (int c = 0; c < NC; ++c)
+                kr[c] = load16(a.k_new + src + 8 * LPR * c);
+            if constexpr (NR) {
+                // every row group transforms the row (the sums run on whole
+                // 8-lane groups); the first stores it.  The staged weights
+                // have landed once nothing is outstanding.
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                uint32_t kk[2][4] = {{kr[0].x, kr[0].y, kr[0].z, kr[0].w},
+                                     {kr[1].x, kr[1].y, kr[1].z, kr[1].w}};
+                float cs[8], sn[8];
+                rope_angles(nrl, j, (double)positions[b], cs, sn);
+                norm_rope_row(kk, nrl, 1, j, a.eps, cs, sn);
+                kr[0] = make_uint4(kk[0][0], kk[0][1], kk[0][2], kk[0][3]);
+                kr[1] = make_uint4(kk[1][0], kk[1][1], kk[1][2], kk[1][3]);
+            }
+            if (rg == 0) {
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    store16(dst + 8 * LPR * c, kr[c]);
+                    store16(dst + 8 * LPR * c + a.half_stride,
+                            load16(a.v_new + src + 8 * LPR * c));
+                }
             }
         }
     }
@@ -1353,6 +1516,20 @@ const void *run_kernel_d(int group, int nbuf) {
     case 2: return run_kernel_dn<D, 2>(group);
     case 3: return run_kernel_dn<D, 3>(group);
     case 4: return run_kernel_dn<D, 4>(group);
+    default: return nullptr;
+    }
+}
+
+// The decode with the fused q/k norm + rotary embedding: head_dim 128, groups
+// up to 4, two staging buffers.
+const void *run_kernel_nr_ptr(int head_dim, int group, int nbuf) {
+    if (head_dim != 128 || nbuf != 2)
+        return nullptr;
+    switch (group) {
+    case 1: return reinterpret_cast<const void *>(&run_kernel<128, 1, 2, true>);
+    case 2: return reinterpret_cast<const void *>(&run_kernel<128, 2, 2, true>);
+    case 3: return reinterpret_cast<const void *>(&run_kernel<128, 3, 2, true>);
+    case 4: return reinterpret_cast<const void *>(&run_kernel<128, 4, 2, true>);
     default: return nullptr;
     }
 }
@@ -1402,6 +1579,10 @@ hipError_t launch_append(const AppendArgs &a, int batch, hipStream_t stream) {
 
 bool run_supported(int head_dim, int group) {
     return run_kernel_ptr(head_dim, group, 2) != nullptr;
+}
+
+bool run_norm_rope_supported(int head_dim, int group) {
+    return run_kernel_nr_ptr(head_dim, group, kMaxStageBuffers) != nullptr;
 }
 
 hipError_t balanced_blocks(int head_dim, int group, int num_kv_heads, int *blocks) {
@@ -1456,16 +1637,20 @@ hipError_t launch_run(const RunArgs &a, const int32_t *blocks, const int32_t *en
     hipError_t err = stage_shape(head_dim, group, a.num_kv_heads, &nbuf, &lds);
     if (err != hipSuccess)
         return err;
-    const void *k = run_kernel_ptr(head_dim, group, nbuf);
+    const void *k = a.q_w != nullptr ? run_kernel_nr_ptr(head_dim, group, nbuf)
+                                     : run_kernel_ptr(head_dim, group, nbuf);
     if (k == nullptr)
         return hipErrorInvalidValue;
+    if (a.q_w != nullptr)
+        lds += (size_t)group_waves(a.num_kv_heads) * kNormRopeLds;
     err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess)
         return err;
     RunArgs args = a;
     const int4 *bp = reinterpret_cast<const int4 *>(blocks);
     const int4 *ep = reinterpret_cast<const int4 *>(ent);
-    void *params[] = {&args, &bp, &ep};
+    const int32_t *pp = a.positions;
+    void *params[] = {&args, &bp, &ep, &pp};
     const int waves = group_waves(a.num_kv_heads);
     const unsigned head_groups = (unsigned)(a.num_kv_heads / waves);
     return launch_raw(k, dim3((unsigned)num_blocks, head_groups), dim3(64 * waves), lds, params,

@@ -92,6 +92,13 @@ struct RunArgs {
     int32_t batch;
     int32_t block_stride;
     float scale_log2;         // sm_scale * log2(e)
+    // Fused q/k RMSNorm + rotary embedding of the segment's q rows and of the
+    // appended k row (q_w null: off); see NormRopeArgs for the formulas.
+    const uint16_t *q_w;      // [D]
+    const uint16_t *k_w;      // [D]
+    const int32_t *positions; // [batch]
+    float eps;
+    double log2_theta;        // log2 of the rotary base
 };
 
 // Largest batch the balanced plan handles (its tile prefix sums sit in LDS);
@@ -226,6 +233,10 @@ hipError_t balanced_blocks(int head_dim, int group, int num_kv_heads, int *block
 
 // True when the decode kernel is built for (head_dim, group).
 bool run_supported(int head_dim, int group);
+
+// True when the decode kernel with the fused q/k norm + rotary embedding is
+// built for (head_dim, group).
+bool run_norm_rope_supported(int head_dim, int group);
 
 hipError_t launch_plan(const PlanArgs &a, hipStream_t stream);
 

@@ -22,6 +22,7 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"pkv_append", "pkv_qk_norm_rope_append", "pkv_prefill",
                           "pkv_decode_workspace_size",
                           "pkv_append_decode", "pkv_decode", "pkv_plan", "pkv_run",
+                          "pkv_run_qk_norm_rope",
                           "pkv_validate_page_table", "pkv_status_string",
                           "pkv_last_hip_error"}
     for n in names:
@@ -239,3 +240,32 @@ def test_single_hip_runtime_shared_with_torch():
     assert len(rts) == 1
     assert os.path.dirname(next(iter(rts))) == os.path.realpath(
         os.path.join(os.path.dirname(torch.__file__), "lib"))
+
+
+DESC128 = CacheDesc(2, 64, 16, 2, 128)
+
+
+def _run_nr(desc=DESC128, layer=0, k=FAKE, v=FAKE, q=FAKE, hq=8, batch=3, qw=FAKE, kw=FAKE,
+            eps=1e-6, theta=1e6, pos=FAKE, scale=0.125, out=FAKE, chunk=0, ws=NULL, wsb=0):
+    return lib.pkv_run_qk_norm_rope(FAKE, desc, layer, k, v, q, hq, batch, qw, kw, eps, theta,
+                                    pos, scale, out, NULL, 4, chunk, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layer=2), -2), (dict(hq=3), -2), (dict(scale=float("nan")), -2),
+    (dict(eps=-1.0), -2), (dict(eps=float("inf")), -2), (dict(theta=0.0), -2),
+    (dict(theta=float("nan")), -2),
+    (dict(desc=CacheDesc(2, 64, 16, 2, 64)), -3),      # head_dim 128 only
+    (dict(hq=10), -3),                                  # groups up to 4
+    (dict(k=NULL), -1), (dict(v=NULL), -1), (dict(qw=NULL), -1), (dict(kw=NULL), -1),
+    (dict(pos=NULL), -1), (dict(q=NULL), -1), (dict(out=NULL), -1),
+    (dict(kw=ctypes.c_void_p(0x100008)), -6), (dict(out=ctypes.c_void_p(0x100004)), -6),
+    (dict(), -4), (dict(chunk=1, ws=FAKE, wsb=64), -4),
+])
+def test_run_norm_rope_validation(kw, code):
+    assert _run_nr(**kw) == code
+
+
+def test_run_norm_rope_batch_zero_is_noop():
+    assert _run_nr(batch=0, k=NULL, v=NULL, q=NULL, qw=NULL, kw=NULL, pos=NULL,
+                   out=NULL) == 0

@@ -2,8 +2,9 @@
 eager calls (GPU).
 
 The step is the one the benchmark captures: one ``pkv_plan``, then per layer
-either the fused append + decode ``pkv_run`` or the fused q/k norm + rotary +
-KV write followed by a decode-only ``pkv_run``.  The graph is replayed several
+the fused append + decode ``pkv_run``, the fused q/k norm + rotary + KV write
+followed by a decode-only ``pkv_run``, or the one ``pkv_run_qk_norm_rope``
+that does all of it.  The graph is replayed several
 times with eager work in between (the cache and the outputs are reset by
 ordinary copies and fills), and every replay must reproduce the eager outputs,
 LSEs and cache exactly; the eager step itself is checked against the oracle
@@ -47,10 +48,11 @@ def _inputs(seed, batch=24, npad=3):
     return table, lds, cache, qw, kw
 
 
-@pytest.mark.parametrize("mode", ["fused_append", "norm_rope"])
+@pytest.mark.parametrize("mode", ["fused_append", "norm_rope", "run_norm_rope"])
 def test_graph_replays_match_eager(mode):
     print(f"graph mode {mode}", flush=True)
-    table, lds, cache_host, qw_h, kw_h = _inputs(41 if mode == "fused_append" else 42)
+    table, lds, cache_host, qw_h, kw_h = _inputs({"fused_append": 41, "norm_rope": 42,
+                                                  "run_norm_rope": 43}[mode])
     batch, scale = table.batch, 1.0 / np.sqrt(D)
     maxp = table.max_pages_per_req
     tabs = table_to_dev(table)
@@ -75,6 +77,9 @@ def test_graph_replays_match_eager(mode):
             if mode == "fused_append":
                 pkv.run(cache, layer, Q[layer], p, scale, k_new=KN[layer], v_new=VN[layer],
                         out=out[layer], lse=lse[layer])
+            elif mode == "run_norm_rope":
+                pkv.run_qk_norm_rope(cache, layer, Q[layer], p, scale, KN[layer], VN[layer],
+                                     QW[layer], KW[layer], pos, out=out[layer], lse=lse[layer])
             else:
                 pkv.qk_norm_rope_append(cache, layer, Q[layer], KN[layer], VN[layer],
                                         QW[layer], KW[layer], pos, *tabs, q_out=qo[layer])

@@ -358,4 +358,7 @@ def algorithmic_bytes(table: PageTable, num_qo_heads: int, num_kv_heads: int,
     norm_rope = 2 * q + app + 2 * head_dim * 2 + 4 * b + 16 * b
     return {"kv": kv, "q": q, "out": out, "lse": lse, "ptab": ptab, "append": app,
             "decode": kv + q + out + lse + ptab, "total": kv + q + out + lse + ptab + app,
-            "norm_rope": norm_rope}
+            "norm_rope": norm_rope,
+            # the decode with the append and the norm/rotary folded in: the
+            # fused append's bytes plus the two norm weights and the positions
+            "fused_norm_rope": kv + q + out + lse + ptab + app + 2 * head_dim * 2 + 4 * b}
