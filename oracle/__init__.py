@@ -19,6 +19,9 @@ compiles that file with gcc into ``liboracle.so`` and wraps its three calls:
   embedding at each entry's position, and the KV write of the rotated k and
   the v rows ("Supported Models", M* docs, Qwen3-Omni and Qwen3-TTS notes:
   q/k norm, RoPE and KV write as one fused step).
+* :func:`qk_norm_mrope_append` -- the same with multimodal RoPE: a (t, h, w)
+  position per entry, each rotary pair following one named component (the
+  Qwen3-Omni Thinker's q/k norm + multimodal RoPE + KV write, same notes).
 * :func:`bf16_round` -- fp64 to bf16, round to nearest even.
 * :func:`append_rows` / :func:`prefill` -- several new rows per entry: their
   append at the entry's last positions, and the causal attention of each row
@@ -70,6 +73,9 @@ def load(path: str = _LIB_PATH):
     lib.oracle_qk_norm_rope_append.argtypes = ([p] + [i64] * 6 + [p, i64, p, p, p, p, d64,
                                                d64, p, p, p, p, i64, p, p])
     lib.oracle_qk_norm_rope_append.restype = ctypes.c_int
+    lib.oracle_qk_norm_mrope_append.argtypes = ([p] + [i64] * 6 + [p, i64, p, p, p, p, d64,
+                                                d64, p, p, p, p, p, i64, p, p])
+    lib.oracle_qk_norm_mrope_append.restype = ctypes.c_int
     lib.oracle_append_rows.argtypes = [p] + [i64] * 6 + [p, p, p, p, p, p, i64]
     lib.oracle_append_rows.restype = ctypes.c_int
     lib.oracle_prefill.argtypes = [p] + [i64] * 6 + [p, i64, p, p, p, p, i64, d64, p, p]
@@ -198,6 +204,41 @@ def bf16_round(x, lib=None) -> np.ndarray:
     flat = np.asarray(x, dtype=np.float64).ravel()
     out = np.array([lib.oracle_bf16_round(float(v)) for v in flat], dtype=np.uint16)
     return out.reshape(np.shape(x))
+
+
+def qk_norm_mrope_append(cache, layer, q, k_new, v_new, q_norm_w, k_norm_w, eps, theta,
+                         positions, pair_axis, indptr, indices, last_len, lib=None):
+    """Multimodal RoPE: positions [batch, 3] (t, h, w), pair_axis [D/2] (each 0,
+    1 or 2); returns (q_out, k_out) fp64 and writes the cache as
+    :func:`qk_norm_rope_append` does."""
+    lib = lib or load()
+    _check_cache(cache)
+    nl, npg, _, ps, hkv, d = cache.shape
+    indptr, indices, last_len = _tables(indptr, indices, last_len)
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k_new = np.ascontiguousarray(k_new, dtype=np.uint16)
+    v_new = np.ascontiguousarray(v_new, dtype=np.uint16)
+    q_norm_w = np.ascontiguousarray(q_norm_w, dtype=np.uint16)
+    k_norm_w = np.ascontiguousarray(k_norm_w, dtype=np.uint16)
+    positions = np.ascontiguousarray(positions, dtype=np.int32)
+    pair_axis = np.ascontiguousarray(pair_axis, dtype=np.uint8)
+    batch, hq, dq = q.shape
+    if (dq != d or batch != len(last_len) or k_new.shape != (batch, hkv, d)
+            or v_new.shape != (batch, hkv, d) or q_norm_w.shape != (d,)
+            or k_norm_w.shape != (d,) or positions.shape != (batch, 3)
+            or pair_axis.shape != (d // 2,)):
+        raise ValueError("shapes: q [batch, Hq, D], k_new/v_new [batch, Hkv, D], "
+                         "weights [D], positions [batch, 3], pair_axis [D/2]")
+    q_out = np.zeros((batch, hq, d), dtype=np.float64)
+    k_out = np.zeros((batch, hkv, d), dtype=np.float64)
+    rc = lib.oracle_qk_norm_mrope_append(
+        _ptr(cache), nl, npg, ps, hkv, d, layer, _ptr(q), hq, _ptr(k_new), _ptr(v_new),
+        _ptr(q_norm_w), _ptr(k_norm_w), float(eps), float(theta), _ptr(positions),
+        _ptr(pair_axis), _ptr(indptr), _ptr(indices), _ptr(last_len), batch, _ptr(q_out),
+        _ptr(k_out))
+    if rc:
+        raise ValueError(f"oracle_qk_norm_mrope_append failed (code {rc})")
+    return q_out, k_out
 
 
 def append_rows(cache, layer, k_new, v_new, qo_indptr, indptr, indices, last_len,

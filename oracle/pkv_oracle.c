@@ -326,17 +326,74 @@ static void rms_norm_row(const uint16_t *x, const uint16_t *w, int64_t head_dim,
 }
 
 /* Rotary embedding of one head row in place, rotate-half pairing: element i
- * and element i + D/2 turn by the angle pos * theta^(-2i/D). */
-static void rope_row(double *y, int64_t head_dim, double pos, double theta)
+ * and element i + D/2 turn by the angle pair_pos[i] * theta^(-2i/D), where
+ * pair_pos[i] is the position pair i follows (the entry's position for plain
+ * RoPE; for multimodal RoPE the component of the entry's (t, h, w) position
+ * named for that pair). */
+static void rope_row(double *y, int64_t head_dim, const double *pair_pos, double theta)
 {
     int64_t half = head_dim / 2;
     for (int64_t i = 0; i < half; ++i) {
-        double angle = pos * pow(theta, -2.0 * (double)i / (double)head_dim);
+        double angle = pair_pos[i] * pow(theta, -2.0 * (double)i / (double)head_dim);
         double c = cos(angle), s = sin(angle);
         double lo = y[i], hi = y[i + half];
         y[i] = lo * c - hi * s;
         y[i + half] = hi * c + lo * s;
     }
+}
+
+/*
+ * The q/k norm, rotary embedding and KV write of one layer, for plain RoPE
+ * (pos_stride 1, pair_axis NULL: every pair follows positions[b]) and for
+ * multimodal RoPE (pos_stride 3: positions[b] is the entry's (t, h, w)
+ * position, and pair i follows component pair_axis[i]).
+ */
+static int norm_rope_append(uint16_t *cache, int64_t num_layers, int64_t num_pages,
+                            int64_t page_size, int64_t num_kv_heads, int64_t head_dim,
+                            int64_t layer, const uint16_t *q, int64_t num_qo_heads,
+                            const uint16_t *k_new, const uint16_t *v_new,
+                            const uint16_t *q_w, const uint16_t *k_w, double eps,
+                            double theta, const int32_t *positions, int64_t pos_stride,
+                            const uint8_t *pair_axis, const int32_t *page_indptr,
+                            const int32_t *page_indices, const int32_t *last_page_len,
+                            int64_t batch, double *q_out, double *k_out)
+{
+    if (layer < 0 || layer >= num_layers || head_dim % 2 != 0 || head_dim > 512)
+        return -1;
+    double pair_pos[256];
+    for (int64_t b = 0; b < batch; ++b) {
+        if (entry_len(page_indptr, last_page_len, page_size, b) < 0)
+            return -2;
+        int64_t page = page_indices[page_indptr[b + 1] - 1];
+        int64_t slot = last_page_len[b] - 1;
+        if (page < 0 || page >= num_pages)
+            return -3;
+        for (int64_t i = 0; i < head_dim / 2; ++i) {
+            int64_t axis = pair_axis ? pair_axis[i] : 0;
+            if (axis < 0 || axis >= pos_stride)
+                return -4;
+            pair_pos[i] = (double)positions[b * pos_stride + axis];
+        }
+        for (int64_t hq = 0; hq < num_qo_heads; ++hq) {
+            int64_t row = (b * num_qo_heads + hq) * head_dim;
+            rms_norm_row(q + row, q_w, head_dim, eps, q_out + row);
+            rope_row(q_out + row, head_dim, pair_pos, theta);
+        }
+        for (int64_t h = 0; h < num_kv_heads; ++h) {
+            int64_t row = (b * num_kv_heads + h) * head_dim;
+            rms_norm_row(k_new + row, k_w, head_dim, eps, k_out + row);
+            rope_row(k_out + row, head_dim, pair_pos, theta);
+            int64_t dk = cache_row(num_pages, page_size, num_kv_heads, head_dim,
+                                   layer, page, 0, slot, h);
+            int64_t dv = cache_row(num_pages, page_size, num_kv_heads, head_dim,
+                                   layer, page, 1, slot, h);
+            for (int64_t d = 0; d < head_dim; ++d) {
+                cache[dk + d] = oracle_bf16_round(k_out[row + d]);
+                cache[dv + d] = v_new[row + d];
+            }
+        }
+    }
+    return 0;
 }
 
 /*
@@ -356,36 +413,33 @@ int oracle_qk_norm_rope_append(uint16_t *cache, int64_t num_layers, int64_t num_
                                const int32_t *last_page_len, int64_t batch,
                                double *q_out, double *k_out)
 {
-    if (layer < 0 || layer >= num_layers || head_dim % 2 != 0)
-        return -1;
-    for (int64_t b = 0; b < batch; ++b) {
-        if (entry_len(page_indptr, last_page_len, page_size, b) < 0)
-            return -2;
-        int64_t page = page_indices[page_indptr[b + 1] - 1];
-        int64_t slot = last_page_len[b] - 1;
-        if (page < 0 || page >= num_pages)
-            return -3;
-        double pos = (double)positions[b];
-        for (int64_t hq = 0; hq < num_qo_heads; ++hq) {
-            int64_t row = (b * num_qo_heads + hq) * head_dim;
-            rms_norm_row(q + row, q_w, head_dim, eps, q_out + row);
-            rope_row(q_out + row, head_dim, pos, theta);
-        }
-        for (int64_t h = 0; h < num_kv_heads; ++h) {
-            int64_t row = (b * num_kv_heads + h) * head_dim;
-            rms_norm_row(k_new + row, k_w, head_dim, eps, k_out + row);
-            rope_row(k_out + row, head_dim, pos, theta);
-            int64_t dk = cache_row(num_pages, page_size, num_kv_heads, head_dim,
-                                   layer, page, 0, slot, h);
-            int64_t dv = cache_row(num_pages, page_size, num_kv_heads, head_dim,
-                                   layer, page, 1, slot, h);
-            for (int64_t d = 0; d < head_dim; ++d) {
-                cache[dk + d] = oracle_bf16_round(k_out[row + d]);
-                cache[dv + d] = v_new[row + d];
-            }
-        }
-    }
-    return 0;
+    return norm_rope_append(cache, num_layers, num_pages, page_size, num_kv_heads, head_dim,
+                            layer, q, num_qo_heads, k_new, v_new, q_w, k_w, eps, theta,
+                            positions, 1, NULL, page_indptr, page_indices, last_page_len,
+                            batch, q_out, k_out);
+}
+
+/*
+ * The same with multimodal RoPE: positions is [batch, 3], the (t, h, w)
+ * position of each entry's new token, and rotary pair i (elements i and
+ * i + D/2) turns by positions[b, pair_axis[i]] * theta^(-2i/D); pair_axis
+ * holds D/2 entries, each 0, 1 or 2.  With equal components it is the plain
+ * RoPE above.
+ */
+int oracle_qk_norm_mrope_append(uint16_t *cache, int64_t num_layers, int64_t num_pages,
+                                int64_t page_size, int64_t num_kv_heads, int64_t head_dim,
+                                int64_t layer, const uint16_t *q, int64_t num_qo_heads,
+                                const uint16_t *k_new, const uint16_t *v_new,
+                                const uint16_t *q_w, const uint16_t *k_w, double eps,
+                                double theta, const int32_t *positions,
+                                const uint8_t *pair_axis, const int32_t *page_indptr,
+                                const int32_t *page_indices, const int32_t *last_page_len,
+                                int64_t batch, double *q_out, double *k_out)
+{
+    return norm_rope_append(cache, num_layers, num_pages, page_size, num_kv_heads, head_dim,
+                            layer, q, num_qo_heads, k_new, v_new, q_w, k_w, eps, theta,
+                            positions, 3, pair_axis, page_indptr, page_indices,
+                            last_page_len, batch, q_out, k_out);
 }
 
 /*

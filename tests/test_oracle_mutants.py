@@ -49,8 +49,17 @@ MUTANTS = {
         "double lo = y[i], hi = y[i + half];",
         "double lo = y[(2 * i) % head_dim], hi = y[(2 * i + 1) % head_dim];"),
     "rope_position_off_by_one": (
-        "double pos = (double)positions[b];",
-        "double pos = (double)positions[b] + 1.0;"),
+        "pair_pos[i] = (double)positions[b * pos_stride + axis];",
+        "pair_pos[i] = (double)positions[b * pos_stride + axis] + 1.0;"),
+    "mrope_axis_ignored": (
+        "int64_t axis = pair_axis ? pair_axis[i] : 0;",
+        "int64_t axis = 0;"),
+    "mrope_axis_shifted": (
+        "int64_t axis = pair_axis ? pair_axis[i] : 0;",
+        "int64_t axis = pair_axis ? pair_axis[(i + 1) % (head_dim / 2)] : 0;"),
+    "mrope_position_stride_dropped": (
+        "pair_pos[i] = (double)positions[b * pos_stride + axis];",
+        "pair_pos[i] = (double)positions[b + axis];"),
     "rmsnorm_eps_dropped": (
         "sqrt(ss / (double)head_dim + eps)",
         "sqrt(ss / (double)head_dim + 0.0 * eps)"),

@@ -437,6 +437,78 @@ def pin_norm_rope_write_is_append(lib):
     np.testing.assert_array_equal(q2, k_out)
 
 
+def _norm_mrope(lib, q, k, v, qw, kw, eps, theta, positions, axis, lengths, ps=4, seed=0):
+    rng = np.random.default_rng(seed)
+    b, hq, d = q.shape
+    hkv = k.shape[1]
+    table = table_from_lengths(np.asarray(lengths), np.ones(b, bool), ps, None, rng)
+    cache = bf16_bits(rng.normal(size=(2, table.num_pages, 2, ps, hkv, d)))
+    before = cache.copy()
+    q_out, k_out = oracle.qk_norm_mrope_append(cache, 1, q, k, v, qw, kw, eps, theta,
+                                               np.asarray(positions, np.int32),
+                                               np.asarray(axis, np.uint8), table.indptr,
+                                               table.indices, table.last_len, lib=lib)
+    return q_out, k_out, before, cache, table
+
+
+def pin_mrope_worked_example(lib):
+    # D = 8, eps = 0, unit weights, base 16: the rates 16^(-2i/8) are 1, 1/2,
+    # 1/4, 1/8, and e_j normalises to sqrt(8) e_j.  Pair i (elements i, i + 4)
+    # turns by the component of (t, h, w) its axis names.
+    d = 8
+    q = _bf16(np.eye(d))[None]                                         # [1, 8, 8]
+    ones = _bf16(np.ones(d))
+    for pos, axis in [((3, -2, 5), (0, 1, 2, 0)), ((7, 1, 0), (0, 0, 1, 2)),
+                      ((0, 4, 9), (2, 2, 1, 1))]:
+        q_out, _, _, _, _ = _norm_mrope(lib, q, q[:, :1], q[:, :1], ones, ones, 0.0, 16.0,
+                                        [pos], axis, [2])
+        want = np.zeros((d, d))
+        for i in range(4):
+            a = pos[axis[i]] * 2.0 ** -i
+            c, s = math.cos(a), math.sin(a)
+            want[i, i], want[i, i + 4] = c, s               # row e_i
+            want[i + 4, i], want[i + 4, i + 4] = -s, c      # row e_{i+4}
+        np.testing.assert_allclose(q_out[0], math.sqrt(8) * want, rtol=0, atol=1e-14,
+                                   err_msg=f"positions {pos} axes {axis}")
+
+
+def pin_mrope_equal_components_is_rope(lib):
+    # with t = h = w the multimodal rotation is the plain one, for any axes
+    rng = np.random.default_rng(23)
+    b, hq, hkv, d = 3, 4, 2, 64
+    q = _bf16(rng.normal(size=(b, hq, d)))
+    k = _bf16(rng.normal(size=(b, hkv, d)))
+    v = _bf16(rng.normal(size=(b, hkv, d)))
+    qw = _bf16(rng.uniform(0.5, 1.5, size=d))
+    kw = _bf16(rng.uniform(0.5, 1.5, size=d))
+    pos = [11, 0, 4000]
+    axis = rng.integers(0, 3, size=d // 2)
+    q1, k1, _, c1, _ = _norm_rope(lib, q, k, v, qw, kw, 1e-6, 1e6, pos, [5, 9, 13])
+    q3, k3, _, c3, _ = _norm_mrope(lib, q, k, v, qw, kw, 1e-6, 1e6,
+                                   [[p, p, p] for p in pos], axis, [5, 9, 13])
+    np.testing.assert_array_equal(q3, q1)
+    np.testing.assert_array_equal(k3, k1)
+    np.testing.assert_array_equal(c3, c1)
+
+
+def pin_mrope_components_act_on_their_pairs(lib):
+    # moving one component changes exactly the pairs that follow it
+    rng = np.random.default_rng(24)
+    d = 32
+    q = _bf16(rng.normal(size=(1, 2, d)))
+    k = _bf16(rng.normal(size=(1, 1, d)))
+    w = _bf16(rng.uniform(0.5, 1.5, size=d))
+    axis = np.array([0] * 6 + [1] * 5 + [2] * 5)
+    base, _, _, _, _ = _norm_mrope(lib, q, k, k, w, w, 1e-6, 1e4, [[9, 4, 2]], axis, [3])
+    for comp in range(3):
+        pos = [9, 4, 2]
+        pos[comp] += 3
+        moved, _, _, _, _ = _norm_mrope(lib, q, k, k, w, w, 1e-6, 1e4, [pos], axis, [3])
+        pairs = np.concatenate([axis, axis]) == comp       # element i and i + D/2
+        np.testing.assert_array_equal(moved[..., ~pairs], base[..., ~pairs])
+        assert np.all(np.abs(moved[..., pairs] - base[..., pairs]).max(axis=-1) > 1e-3)
+
+
 # ---- several new rows per entry: append at the last positions, causal attention
 
 def _rows_case(seed, hq, hkv, d, ps, lengths, nrows):
@@ -538,6 +610,8 @@ PINS = [pin_golden, pin_dense_sdpa, pin_single_token, pin_zero_query,
         pin_append_is_last_token, pin_append_then_single_token_decode,
         pin_bf16_round, pin_rms_norm_closed_form, pin_rope_worked_example,
         pin_rope_relative_position, pin_norm_rope_write_is_append,
+        pin_mrope_worked_example, pin_mrope_equal_components_is_rope,
+        pin_mrope_components_act_on_their_pairs,
         pin_append_rows_positions, pin_prefill_causal_sdpa, pin_prefill_one_row_is_decode]
 
 
