@@ -161,6 +161,30 @@ int pkv_qk_norm_rope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer
                             int32_t batch, void *q_out, hipStream_t stream);
 
 /*
+ * pkv_qk_norm_mrope_append -- pkv_qk_norm_rope_append with multimodal RoPE,
+ * the Qwen3-Omni Thinker's variant ("Supported Models", M* docs, Qwen3-Omni
+ * notes: q/k RMSNorm and multimodal RoPE with the KV write in one kernel,
+ * fp32 throughout, rounded once).  Each entry has a (t, h, w) position and
+ * each rotary pair i (elements i and i + D/2) follows one component:
+ *   a_i = positions[b, pair_axis[i]] * rope_theta^(-2i/D)
+ * everything else as in pkv_qk_norm_rope_append.  With t = h = w it gives
+ * exactly pkv_qk_norm_rope_append's result.
+ *  positions   int32 [batch, 3], device, row-major (t, h, w).
+ *  pair_axis   uint8 [head_dim / 2], HOST, each 0, 1 or 2 (else
+ *              PKV_ERR_BAD_SHAPE): contiguous sections (t for the first
+ *              pairs, then h, then w) and interleaved layouts are both a
+ *              choice of this map.  Read during the call only.
+ */
+int pkv_qk_norm_mrope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+                             const void *q, int32_t num_qo_heads, const void *k_new,
+                             const void *v_new, const void *q_norm_weight,
+                             const void *k_norm_weight, float eps, float rope_theta,
+                             const int32_t *positions, const uint8_t *pair_axis,
+                             const int32_t *page_indptr, const int32_t *page_indices,
+                             const int32_t *last_page_len, int32_t batch, void *q_out,
+                             hipStream_t stream);
+
+/*
  * pkv_decode_workspace_size -- bytes of device workspace that pkv_plan,
  * pkv_run, pkv_decode and pkv_append_decode need for these arguments.  Host
  * function; no device work.  Returns 0 for arguments the calls would reject.

@@ -88,6 +88,9 @@ def _load():
     lib.pkv_qk_norm_rope_append.argtypes = [p, CacheDesc, i32, p, i32, p, p, p, p, f32, f32,
                                             p, p, p, p, i32, p, p]
     lib.pkv_qk_norm_rope_append.restype = ctypes.c_int
+    lib.pkv_qk_norm_mrope_append.argtypes = [p, CacheDesc, i32, p, i32, p, p, p, p, f32, f32,
+                                             p, p, p, p, p, i32, p, p]
+    lib.pkv_qk_norm_mrope_append.restype = ctypes.c_int
     lib.pkv_prefill.argtypes = [p, CacheDesc, i32, p, i32, p, p, p, p, p, p, i32, i32, f32,
                                 p, p, p]
     lib.pkv_prefill.restype = ctypes.c_int
@@ -233,6 +236,49 @@ def qk_norm_rope_append(kv_cache, layer: int, q, k_new, v_new, q_norm_weight,
         _dev_ptr(q_out, "q_out", torch.bfloat16, dev), _stream(stream))
     if rc != PKV_OK:
         raise PkvError(rc, "pkv_qk_norm_rope_append")
+    return q_out
+
+
+def qk_norm_mrope_append(kv_cache, layer: int, q, k_new, v_new, q_norm_weight,
+                         k_norm_weight, positions, pair_axis, page_indptr, page_indices,
+                         last_page_len, eps: float = 1e-6, rope_theta: float = 1e6,
+                         q_out=None, stream=None):
+    """:func:`qk_norm_rope_append` with multimodal RoPE: positions [batch, 3]
+    int32 on the device, pair_axis a host sequence of head_dim/2 values in
+    {0, 1, 2} (the position component each rotary pair follows)."""
+    import torch
+    desc = cache_desc(kv_cache)
+    batch = int(last_page_len.shape[0])
+    d = desc.head_dim
+    if q.dim() != 3 or q.shape[0] != batch or q.shape[2] != d:
+        raise ValueError(f"q must be [batch, Hq, {d}], got {tuple(q.shape)}")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (batch, desc.num_kv_heads, d):
+            raise ValueError(f"{name} must be [batch, Hkv, D], got {tuple(t.shape)}")
+    for name, t in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        if tuple(t.shape) != (d,):
+            raise ValueError(f"{name} must be [{d}], got {tuple(t.shape)}")
+    if tuple(positions.shape) != (batch, 3) or not positions.is_contiguous():
+        raise ValueError(f"positions must be contiguous [batch, 3], got {tuple(positions.shape)}")
+    axis = np.ascontiguousarray(pair_axis, dtype=np.uint8)
+    if axis.shape != (d // 2,):
+        raise ValueError(f"pair_axis must hold {d // 2} values")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    dev = kv_cache.device
+    rc = lib.pkv_qk_norm_mrope_append(
+        _dev_ptr(kv_cache, "kv_cache", torch.bfloat16), desc, int(layer),
+        _dev_ptr(q, "q", torch.bfloat16, dev), int(q.shape[1]),
+        _dev_ptr(k_new, "k_new", torch.bfloat16, dev),
+        _dev_ptr(v_new, "v_new", torch.bfloat16, dev),
+        _dev_ptr(q_norm_weight, "q_norm_weight", torch.bfloat16, dev),
+        _dev_ptr(k_norm_weight, "k_norm_weight", torch.bfloat16, dev),
+        float(eps), float(rope_theta), _dev_ptr(positions, "positions", torch.int32, dev),
+        axis.ctypes.data_as(ctypes.c_void_p),
+        *_tables(kv_cache, page_indptr, page_indices, last_page_len), batch,
+        _dev_ptr(q_out, "q_out", torch.bfloat16, dev), _stream(stream))
+    if rc != PKV_OK:
+        raise PkvError(rc, "pkv_qk_norm_mrope_append")
     return q_out
 
 

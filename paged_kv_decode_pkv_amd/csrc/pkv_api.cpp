@@ -384,13 +384,19 @@ int pkv_prefill(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void
     return hip_status(pkv::launch_prefill(a, append, stream));
 }
 
-int pkv_qk_norm_rope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
-                            const void *q, int32_t num_qo_heads, const void *k_new,
-                            const void *v_new, const void *q_norm_weight,
-                            const void *k_norm_weight, float eps, float rope_theta,
-                            const int32_t *positions, const int32_t *page_indptr,
-                            const int32_t *page_indices, const int32_t *last_page_len,
-                            int32_t batch, void *q_out, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// pkv_qk_norm_rope_append and its multimodal variant (pair_axis non-null:
+// positions [batch, 3], pair i following component pair_axis[i]).
+int norm_rope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *q,
+                     int32_t num_qo_heads, const void *k_new, const void *v_new,
+                     const void *q_norm_weight, const void *k_norm_weight, float eps,
+                     float rope_theta, const int32_t *positions, const uint8_t *pair_axis,
+                     bool multimodal, const int32_t *page_indptr, const int32_t *page_indices,
+                     const int32_t *last_page_len, int32_t batch, void *q_out,
+                     hipStream_t stream) {
     int rc = check_desc(desc);
     if (rc != PKV_OK)
         return rc;
@@ -399,6 +405,16 @@ int pkv_qk_norm_rope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer
         return PKV_ERR_BAD_SHAPE;
     if (!pkv::norm_rope_supported(desc.head_dim))
         return PKV_ERR_UNSUPPORTED;
+    uint32_t axis_bits[4] = {0, 0, 0, 0};
+    if (multimodal) {
+        if (!pair_axis)
+            return PKV_ERR_NULL_PTR;
+        for (int i = 0; i < desc.head_dim / 2; ++i) {
+            if (pair_axis[i] > 2)
+                return PKV_ERR_BAD_SHAPE;
+            axis_bits[i / 16] |= (uint32_t)pair_axis[i] << (2 * (i % 16));
+        }
+    }
     if (batch == 0)
         return PKV_OK;
     if (!kv_cache || !q || !k_new || !v_new || !q_norm_weight || !k_norm_weight ||
@@ -431,11 +447,45 @@ int pkv_qk_norm_rope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer
     a.head_dim = desc.head_dim;
     a.batch = batch;
     a.eps = eps;
+    a.pos_stride = multimodal ? 3 : 1;
+    for (int i = 0; i < 4; ++i)
+        a.axis_bits[i] = axis_bits[i];
     for (int i = 0; i < 64; ++i)
         a.turns[i] = i < desc.head_dim / 2
                          ? pow((double)rope_theta, -2.0 * i / desc.head_dim) / (2.0 * M_PI)
                          : 0.0;
     return hip_status(pkv::launch_norm_rope(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_qk_norm_rope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+                            const void *q, int32_t num_qo_heads, const void *k_new,
+                            const void *v_new, const void *q_norm_weight,
+                            const void *k_norm_weight, float eps, float rope_theta,
+                            const int32_t *positions, const int32_t *page_indptr,
+                            const int32_t *page_indices, const int32_t *last_page_len,
+                            int32_t batch, void *q_out, hipStream_t stream) {
+    return norm_rope_append(kv_cache, desc, layer, q, num_qo_heads, k_new, v_new,
+                            q_norm_weight, k_norm_weight, eps, rope_theta, positions, nullptr,
+                            false, page_indptr, page_indices, last_page_len, batch, q_out,
+                            stream);
+}
+
+int pkv_qk_norm_mrope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+                             const void *q, int32_t num_qo_heads, const void *k_new,
+                             const void *v_new, const void *q_norm_weight,
+                             const void *k_norm_weight, float eps, float rope_theta,
+                             const int32_t *positions, const uint8_t *pair_axis,
+                             const int32_t *page_indptr, const int32_t *page_indices,
+                             const int32_t *last_page_len, int32_t batch, void *q_out,
+                             hipStream_t stream) {
+    return norm_rope_append(kv_cache, desc, layer, q, num_qo_heads, k_new, v_new,
+                            q_norm_weight, k_norm_weight, eps, rope_theta, positions, pair_axis,
+                            true, page_indptr, page_indices, last_page_len, batch, q_out,
+                            stream);
 }
 
 int pkv_run_qk_norm_rope(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,

@@ -171,7 +171,7 @@ struct NormRopeArgs {
     const uint16_t *q_w;      // [D] RMSNorm weights of the q heads
     const uint16_t *k_w;      // [D] of the k heads
     uint16_t *q_out;          // [batch, Hq, D], may be q
-    const int32_t *positions; // [batch]
+    const int32_t *positions; // [batch], or [batch, 3] (t, h, w) for multimodal RoPE
     const int32_t *indptr;
     const int32_t *indices;
     const int32_t *last_len;
@@ -185,6 +185,10 @@ struct NormRopeArgs {
     int32_t head_dim;
     int32_t batch;
     float eps;
+    int32_t pos_stride;       // 1, or 3 for multimodal RoPE
+    // multimodal RoPE: the position component (0, 1, 2) pair i follows, two
+    // bits per pair, pair i at bits 2 (i % 16) of word i / 16
+    uint32_t axis_bits[4];
     // rotation rate of pair i in turns per position: theta^(-2i/D) / (2 pi)
     double turns[64];
 };

@@ -20,7 +20,9 @@
 // off by a few thousandths of a radian; the fp64 product is off by about
 // 1e-12 of a turn, and taking the nearest whole turn off is exact), then the
 // sine and cosine and the rotation run in fp32.  The rates per pair come with the arguments,
-// computed on the host.  The work is a few KiB per entry: the launch is bound
+// computed on the host.  Multimodal RoPE (the Qwen3-Omni Thinker's variant) gives
+// each entry a (t, h, w) position and each pair the component it follows; the
+// rest is the same.  The work is a few KiB per entry: the launch is bound
 // by latency, not by HBM.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -42,7 +44,7 @@ __device__ __forceinline__ uint32_t float_to_bf16(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int D>
+template <int D, bool MR>
 __global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a) {
     constexpr int kLanes = D / 2;   // lanes holding a word of the row
     const int lane = threadIdx.x & 63;
@@ -77,12 +79,22 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a) {
     const float p0 = __shfl_xor(y0, D / 4, 64);
     const float p1 = __shfl_xor(y1, D / 4, 64);
     const bool upper = lane >= D / 4;   // holds elements of the second half
-    const double pos = (double)a.positions[b];
+    const double pos = (double)a.positions[(int64_t)b * a.pos_stride];
     float z[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int i = (2 * lane + j) % (D / 2);   // pair index of the element
-        const double turns = pos * a.turns[i];
+        double pp = pos;   // the position this pair follows
+        if constexpr (MR) {
+            const int q4 = i >> 4;
+            const uint32_t word = q4 == 0   ? a.axis_bits[0]
+                                  : q4 == 1 ? a.axis_bits[1]
+                                  : q4 == 2 ? a.axis_bits[2]
+                                            : a.axis_bits[3];
+            const int ax = (int)((word >> (2 * (i & 15))) & 3u);
+            pp = (double)a.positions[(int64_t)b * 3 + ax];
+        }
+        const double turns = pp * a.turns[i];
         const float ang = (float)(turns - rint(turns)) * 6.2831853071795865f;
         float s, c;
         sincosf(ang, &s, &c);
@@ -129,10 +141,13 @@ hipError_t launch_norm_rope(const NormRopeArgs &a, hipStream_t stream) {
     if (blocks > 0x7fffffffLL)
         return hipErrorInvalidValue;
     const void *k = nullptr;
+    const bool mr = a.pos_stride == 3;
     if (a.head_dim == 128)
-        k = reinterpret_cast<const void *>(&norm_rope_kernel<128>);
+        k = mr ? reinterpret_cast<const void *>(&norm_rope_kernel<128, true>)
+               : reinterpret_cast<const void *>(&norm_rope_kernel<128, false>);
     else if (a.head_dim == 64)
-        k = reinterpret_cast<const void *>(&norm_rope_kernel<64>);
+        k = mr ? reinterpret_cast<const void *>(&norm_rope_kernel<64, true>)
+               : reinterpret_cast<const void *>(&norm_rope_kernel<64, false>);
     else
         return hipErrorInvalidValue;
     return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(256), params, 0, stream);

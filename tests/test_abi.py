@@ -20,6 +20,7 @@ DESC = CacheDesc(2, 64, 16, 2, 64)
 def test_every_declared_symbol_is_exported():
     names = pkv.declared_functions()
     assert set(names) == {"pkv_append", "pkv_qk_norm_rope_append", "pkv_prefill",
+                          "pkv_qk_norm_mrope_append",
                           "pkv_decode_workspace_size",
                           "pkv_append_decode", "pkv_decode", "pkv_plan", "pkv_run",
                           "pkv_run_qk_norm_rope",
@@ -269,3 +270,24 @@ def test_run_norm_rope_validation(kw, code):
 def test_run_norm_rope_batch_zero_is_noop():
     assert _run_nr(batch=0, k=NULL, v=NULL, q=NULL, qw=NULL, kw=NULL, pos=NULL,
                    out=NULL) == 0
+
+
+AXIS = (ctypes.c_uint8 * 32)(*([0] * 11 + [1] * 11 + [2] * 10))
+
+
+def _norm_mrope(axis=AXIS, desc=DESC, batch=3, q=FAKE, pos=FAKE, eps=1e-6):
+    return lib.pkv_qk_norm_mrope_append(FAKE, desc, 0, q, 4, FAKE, FAKE, FAKE, FAKE, eps, 1e6,
+                                        pos, axis, FAKE, FAKE, FAKE, batch, FAKE, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(axis=None), -1), (dict(axis=(ctypes.c_uint8 * 32)(*([0] * 31 + [3]))), -2),
+    (dict(eps=-1.0), -2), (dict(desc=CacheDesc(2, 64, 16, 2, 32)), -3),
+    (dict(q=NULL), -1), (dict(pos=NULL), -1),
+])
+def test_norm_mrope_validation(kw, code):
+    assert _norm_mrope(**kw) == code
+
+
+def test_norm_mrope_batch_zero_is_noop():
+    assert _norm_mrope(batch=0) == 0

@@ -177,3 +177,61 @@ def test_norm_rope_then_decode_config3_shape():
     og = out[torch.from_numpy(rb).to(DEV), torch.from_numpy(rh).to(DEV)]
     lg = lse[torch.from_numpy(rb).to(DEV), torch.from_numpy(rh).to(DEV)]
     compare(og, lg, o_ref, l_ref, what="decode after norm_rope")
+
+
+# ---- multimodal RoPE: a (t, h, w) position per entry, a component per pair
+
+def _axis(kind, d, rng):
+    h = d // 2
+    if kind == "sections":        # contiguous t / h / w bands, 24 : 20 : 20
+        t, hh = h * 24 // 64, h * 20 // 64
+        return np.array([0] * t + [1] * hh + [2] * (h - t - hh), np.uint8)
+    if kind == "interleaved":
+        return (np.arange(h) % 3).astype(np.uint8)
+    return rng.integers(0, 3, size=h).astype(np.uint8)
+
+
+MR_SHAPES = [
+    # seed, batch, hq, hkv, d, ps, lo, hi, axes, pos_max, npad
+    (31, 5, 16, 4, 128, 16, 1, 200, "sections", 40000, 1),
+    (32, 6, 14, 2, 64, 8, 1, 90, "interleaved", 100000, 0),
+    (33, 3, 8, 8, 128, 1, 1, 40, "random", 7, 0),
+]
+
+
+@pytest.mark.parametrize("shape", MR_SHAPES, ids=[f"m{s[0]}" for s in MR_SHAPES])
+def test_norm_mrope_matches_oracle(shape):
+    seed, batch, hq, hkv, d, ps, lo, hi, kind, pos_max, npad = shape
+    print(f"norm_mrope shape {shape}", flush=True)
+    table, cache, ld, qw, kw, _ = _case(seed, batch, hq, hkv, d, ps, lo, hi, 1e6, 1e-6, npad)
+    rng = np.random.default_rng(seed + 100)
+    pos3 = rng.integers(0, pos_max + 1, size=(batch, 3)).astype(np.int32)
+    axis = _axis(kind, d, rng)
+    cache_dev = to_dev_u16(cache)
+    tabs = table_to_dev(table)
+    q_out = pkv.qk_norm_mrope_append(cache_dev, 1, to_dev_u16(ld.q), to_dev_u16(ld.k_new),
+                                     to_dev_u16(ld.v_new), to_dev_u16(qw), to_dev_u16(kw),
+                                     torch.from_numpy(pos3).to(DEV), axis, *tabs)
+    torch.cuda.synchronize()
+    host = cache.copy()
+    q_ref, k_ref = oracle.qk_norm_mrope_append(host, 1, ld.q, ld.k_new, ld.v_new, qw, kw,
+                                               1e-6, 1e6, pos3, axis, table.indptr,
+                                               table.indices, table.last_len)
+    _check_all(table, cache_dev, to_host_u16(q_out), host, q_ref, k_ref, ld.v_new,
+               f"mrope {seed}")
+
+
+def test_norm_mrope_equal_components_is_plain_rope():
+    # t = h = w: the same angles as the plain kernel, so the same bits
+    table, cache, ld, qw, kw, positions = _case(34, 7, 32, 8, 128, 16, 1, 500, 1e6, 1e-6)
+    tabs = table_to_dev(table)
+    pos3 = np.repeat(positions[:, None], 3, axis=1).astype(np.int32)
+    axis = _axis("random", 128, np.random.default_rng(5))
+    c1, c2 = to_dev_u16(cache), to_dev_u16(cache)
+    args = (to_dev_u16(ld.q), to_dev_u16(ld.k_new), to_dev_u16(ld.v_new), to_dev_u16(qw),
+            to_dev_u16(kw))
+    q1 = pkv.qk_norm_rope_append(c1, 1, *args, torch.from_numpy(positions).to(DEV), *tabs)
+    q2 = pkv.qk_norm_mrope_append(c2, 1, *args, torch.from_numpy(pos3).to(DEV), axis, *tabs)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2)
+    assert torch.equal(c1, c2)
