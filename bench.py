@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--qk-norm-rope", action="store_true",
                     help="per layer the fused q/k RMSNorm + rotary + KV write, then a "
                          "decode-only pkv_run on its q")
+    ap.add_argument("--mrope", action="store_true",
+                    help="with --qk-norm-rope: multimodal RoPE (positions (L-1, (L-1)/2, "
+                         "(L-1)/3), contiguous 24:20:20 bands of pairs)")
     ap.add_argument("--fused-norm-rope", action="store_true",
                     help="per layer one pkv_run_qk_norm_rope: the decode with the append "
                          "and the q/k RMSNorm + rotary folded in")
@@ -177,6 +180,15 @@ def main():
               "kw": (torch.rand((nl, d), generator=gen, device=dev) + 0.5).to(torch.bfloat16),
               "pos": torch.from_numpy((table.lengths - 1).astype(np.int32)).to(dev),
               "qo": torch.empty_like(Q), "eps": 1e-6, "theta": 1e6}
+        if args.mrope:
+            if not args.qk_norm_rope:
+                raise SystemExit("--mrope goes with --qk-norm-rope")
+            last = (table.lengths - 1).astype(np.int32)
+            nr["pos3"] = torch.from_numpy(
+                np.stack([last, last // 2, last // 3], axis=1).astype(np.int32)).to(dev)
+            h = d // 2
+            t3, h3 = h * 24 // 64, h * 20 // 64
+            nr["axis"] = np.array([0] * t3 + [1] * h3 + [2] * (h - t3 - h3), np.uint8)
     maxp = table.max_pages_per_req
     chunk = args.chunk_pages
     ws_bytes = pkv.workspace_size(pkv.cache_desc(cache), hq, b, maxp, chunk)
@@ -213,13 +225,19 @@ def main():
                             vp(nr["pos"].data_ptr()), *res), "pkv_run_qk_norm_rope"))
             elif args.qk_norm_rope:
                 qo = (vp(nr["qo"][layer].data_ptr()), hq)
-                cl.append((pkv.lib.pkv_qk_norm_rope_append,
-                           (vp(cache.data_ptr()), desc, layer, vp(Q[layer].data_ptr()), hq, kn,
-                            vn, vp(nr["qw"][layer].data_ptr()), vp(nr["kw"][layer].data_ptr()),
-                            ctypes.c_float(nr["eps"]), ctypes.c_float(nr["theta"]),
-                            vp(nr["pos"].data_ptr()), *tab_ptrs, b,
-                            vp(nr["qo"][layer].data_ptr()), s),
-                           "pkv_qk_norm_rope_append"))
+                head = (vp(cache.data_ptr()), desc, layer, vp(Q[layer].data_ptr()), hq, kn,
+                        vn, vp(nr["qw"][layer].data_ptr()), vp(nr["kw"][layer].data_ptr()),
+                        ctypes.c_float(nr["eps"]), ctypes.c_float(nr["theta"]))
+                tail = (*tab_ptrs, b, vp(nr["qo"][layer].data_ptr()), s)
+                if "axis" in nr:
+                    cl.append((pkv.lib.pkv_qk_norm_mrope_append,
+                               (*head, vp(nr["pos3"].data_ptr()),
+                                nr["axis"].ctypes.data_as(vp), *tail),
+                               "pkv_qk_norm_rope_append"))
+                else:
+                    cl.append((pkv.lib.pkv_qk_norm_rope_append,
+                               (*head, vp(nr["pos"].data_ptr()), *tail),
+                               "pkv_qk_norm_rope_append"))
                 cl.append((pkv.lib.pkv_run, (vp(cache.data_ptr()), desc, layer, null, null,
                                              *qo, b, *res), "pkv_run"))
             elif args.separate:
@@ -240,6 +258,8 @@ def main():
 
     if args.fused_norm_rope:
         call_name = "pkv_run_qk_norm_rope (norm + rotary + append + decode)"
+    elif args.qk_norm_rope and args.mrope:
+        call_name = "pkv_qk_norm_mrope_append + pkv_run"
     elif args.qk_norm_rope:
         call_name = "pkv_qk_norm_rope_append + pkv_run"
     elif args.separate:
@@ -431,7 +451,8 @@ def main():
 
     if nr_us is not None:
         result["norm_rope"] = {
-            "kernel": "pkv_qk_norm_rope_append: norm_rope_kernel",
+            "kernel": ("pkv_qk_norm_mrope_append: norm_rope_kernel<D, true>" if "axis" in nr
+                       else "pkv_qk_norm_rope_append: norm_rope_kernel"),
             "avg_launch_us": round(nr_us, 3), "bytes_per_launch": by["norm_rope"],
             "achieved_gbs": round(by["norm_rope"] / (nr_us * 1e-6) / 1e9, 1),
             "bound": "latency",
@@ -667,6 +688,12 @@ def check_sample(spec, table, cache, Q, KN, VN, out, lse, torch, nr=None):
         if nr is None:
             oracle.append(mini, 0, _u16(KN[layer])[entries], _u16(VN[layer])[entries], ip,
                           ix, ll)
+        elif "axis" in nr:
+            q_ref, _ = oracle.qk_norm_mrope_append(
+                mini, 0, q_rows, _u16(KN[layer])[entries], _u16(VN[layer])[entries],
+                _u16(nr["qw"][layer]), _u16(nr["kw"][layer]), nr["eps"], nr["theta"],
+                nr["pos3"].cpu().numpy()[entries], nr["axis"], ip, ix, ll)
+            q_rows = oracle.bf16_round(q_ref)
         else:
             q_ref, _ = oracle.qk_norm_rope_append(
                 mini, 0, q_rows, _u16(KN[layer])[entries], _u16(VN[layer])[entries],
@@ -706,8 +733,13 @@ def norm_rope_oracle_time(table, Q, KN, VN, nr, nbytes):
     t = time.perf_counter()
     reps = 0
     while True:
-        oracle.qk_norm_rope_append(mini, 0, q, kn, vn, qw, kw, nr["eps"], nr["theta"], pos,
-                                   ip, ix, table.last_len)
+        if "axis" in nr:
+            oracle.qk_norm_mrope_append(mini, 0, q, kn, vn, qw, kw, nr["eps"], nr["theta"],
+                                        nr["pos3"].cpu().numpy(), nr["axis"], ip, ix,
+                                        table.last_len)
+        else:
+            oracle.qk_norm_rope_append(mini, 0, q, kn, vn, qw, kw, nr["eps"], nr["theta"],
+                                       pos, ip, ix, table.last_len)
         reps += 1
         dt = time.perf_counter() - t
         if dt > 1.0:
