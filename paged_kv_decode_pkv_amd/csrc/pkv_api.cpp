@@ -28,6 +28,10 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
+// Largest head count any call accepts (query or key/value heads): head
+// indices and their sums stay far inside 32 bits.
+constexpr int32_t kMaxHeads = 65535;
+
 int check_desc(const pkv_cache_desc_t &d) {
     if (d.num_layers < 1 || d.num_pages < 1 || d.num_kv_heads < 1 || d.head_dim < 1)
         return PKV_ERR_BAD_SHAPE;
@@ -145,6 +149,26 @@ int prepare(const pkv_cache_desc_t &desc, int32_t num_qo_heads, int32_t batch,
     return PKV_OK;
 }
 
+// The signature of a plan: a nonzero hash (FNV-1a) of the arguments it is
+// made for.  pkv_plan writes it into every block header and each pkv_run
+// compares it with the hash of its own arguments, so a run on a plan made for
+// other arguments (or on a workspace that holds no plan) is caught before it
+// uses a record.
+int32_t plan_signature(const pkv_cache_desc_t &desc, int32_t num_qo_heads, int32_t batch,
+                       int32_t max_pages_per_req, int32_t kv_chunk_pages, const Layout &lay,
+                       int num_blocks, int block_stride) {
+    const int32_t v[] = {batch, num_qo_heads, desc.num_kv_heads, desc.page_size,
+                         desc.head_dim, max_pages_per_req, kv_chunk_pages, desc.num_pages,
+                         num_blocks, block_stride, lay.tiles_per_page};
+    uint32_t h = 2166136261u;
+    for (int32_t x : v)
+        for (int k = 0; k < 4; ++k) {
+            h ^= ((uint32_t)x >> (8 * k)) & 0xFFu;
+            h *= 16777619u;
+        }
+    return (int32_t)(h | 1u);
+}
+
 // Host checks of a pkv_plan call; on success `args` is ready to launch.
 int prepare_plan(pkv_cache_desc_t desc, int32_t num_qo_heads, const int32_t *page_indptr,
                  const int32_t *page_indices, const int32_t *last_page_len, int32_t batch,
@@ -169,6 +193,8 @@ int prepare_plan(pkv_cache_desc_t desc, int32_t num_qo_heads, const int32_t *pag
     a.blocks = reinterpret_cast<int32_t *>(ws + lay.off_blocks);
     a.ent = reinterpret_cast<int32_t *>(ws + lay.off_ent);
     a.cnt = reinterpret_cast<int32_t *>(ws);
+    a.plan_sig = plan_signature(desc, num_qo_heads, batch, max_pages_per_req, kv_chunk_pages,
+                                lay, num_blocks, block_stride);
     a.batch = batch;
     a.num_pages = desc.num_pages;
     a.page_size = desc.page_size;
@@ -227,6 +253,10 @@ int prepare_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void
     a.part_o_bytes = lay.off_part_lse - lay.off_part_o;
     a.part_lse_bytes = lay.ws_bytes - lay.off_part_lse;
     a.cnt = reinterpret_cast<int32_t *>(ws);
+    a.plan_sig = plan_signature(desc, num_qo_heads, batch, max_pages_per_req, kv_chunk_pages,
+                                lay, num_blocks, block_stride);
+    a.num_pages = desc.num_pages;
+    a.page_size = desc.page_size;
     a.page_stride = page_elems(desc);
     a.half_stride = desc.page_size * desc.num_kv_heads * desc.head_dim;
     a.row_stride = desc.num_kv_heads * desc.head_dim;
@@ -344,6 +374,7 @@ int pkv_prefill(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void
     if (rc != PKV_OK)
         return rc;
     if (layer < 0 || layer >= desc.num_layers || batch < 0 || num_qo_heads < 1 ||
+        num_qo_heads > kMaxHeads || desc.num_kv_heads > kMaxHeads ||
         num_qo_heads % desc.num_kv_heads != 0 || max_q_rows < 1 || !isfinite(sm_scale))
         return PKV_ERR_BAD_SHAPE;
     if (!pkv::prefill_supported(desc.head_dim) || batch > 65535)
@@ -401,7 +432,11 @@ int norm_rope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const
     if (rc != PKV_OK)
         return rc;
     if (layer < 0 || layer >= desc.num_layers || batch < 0 || num_qo_heads < 1 ||
+        num_qo_heads > kMaxHeads || desc.num_kv_heads > kMaxHeads ||
         !(eps >= 0.0f) || !isfinite(eps) || !(rope_theta > 0.0f) || !isfinite(rope_theta))
+        return PKV_ERR_BAD_SHAPE;
+    // one wave per (entry, head): the wave count is formed in 64 bits
+    if ((int64_t)batch * ((int64_t)num_qo_heads + desc.num_kv_heads) > 0x7fffffffLL * 4)
         return PKV_ERR_BAD_SHAPE;
     if (!pkv::norm_rope_supported(desc.head_dim))
         return PKV_ERR_UNSUPPORTED;
@@ -423,8 +458,6 @@ int norm_rope_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const
     if (!aligned16(kv_cache) || !aligned16(q) || !aligned16(k_new) || !aligned16(v_new) ||
         !aligned16(q_norm_weight) || !aligned16(k_norm_weight) || !aligned16(q_out))
         return PKV_ERR_ALIGNMENT;
-    if ((int64_t)batch * (num_qo_heads + desc.num_kv_heads) > 0x7fffffffLL * 4)
-        return PKV_ERR_BAD_SHAPE;
     pkv::NormRopeArgs a;
     a.cache = static_cast<uint16_t *>(kv_cache) + (int64_t)layer * desc.num_pages * page_elems(desc);
     a.q = static_cast<const uint16_t *>(q);

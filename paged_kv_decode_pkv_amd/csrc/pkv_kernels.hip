@@ -48,6 +48,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "pkv_launch.h"
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
             }
         }
         if (jj == 0) {
-            blocks[i] = make_int4(ntiles, run, 0, 0);
+            blocks[i] = make_int4(ntiles, run, a.plan_sig, 0);
             continue;
         }
         const int k = jj - 1;
@@ -837,11 +838,17 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     const int4 *blk = blocks + (int64_t)blockIdx.x * a.block_stride;
     // the header and the first NBUF records load together (the block region
     // is padded, so they are in bounds even past a short block's records)
-    const int n = blk[0].x;
+    const int4 hdr = blk[0];
     int4 rec0[NBUF];
 #pragma unroll
     for (int t = 0; t < NBUF; ++t)
         rec0[t] = blk[1 + t];
+    // The plan must be the one made for this launch's arguments: the
+    // signature in the block header is compared before any record is used.
+    // A workspace holding another plan (or none) gives NaN rows and writes no
+    // cache byte.
+    const bool plan_ok = hdr.z == a.plan_sig;
+    const int n = plan_ok ? hdr.x : 0;
 
     uint32_t qv[G][NC][4];    // q of the entry being computed
     float m[G], l[G], acc[G][NC][8];
@@ -974,7 +981,8 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                     copy_to_lds(qs + off, bb + 2 * part_bytes + (uint32_t)(w * QI + i) * 1024);
                 }
             }
-            const char *kb = cache_b + (int64_t)rec.x * page_bytes + (int64_t)slot0 * row_bytes;
+            const int page = (unsigned)rec.x < (unsigned)a.num_pages ? rec.x : 0;
+            const char *kb = cache_b + (int64_t)page * page_bytes + (int64_t)slot0 * row_bytes;
             const char *vb = kb + half_bytes;
             if (fused && (info & kInfoHasNew)) {
                 const int nr = (info >> kInfoNewRowShift) & (kTileTokens - 1);
@@ -1208,18 +1216,25 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             if (fused && (info & kInfoHasNew)) {
                 // append: the lanes holding the new row store it into its slot
                 const int slot0 = (info >> kInfoSlotShift) & kInfoSlotMask;
+                // a page or slot outside the pool (only a corrupted plan has
+                // one) writes nothing
+                const bool in_pool = (unsigned)rec.x < (unsigned)a.num_pages &&
+                                     slot0 + nr < a.page_size;
                 uint16_t *dst = a.cache_w + (int64_t)rec.x * a.page_stride +
                                 (int64_t)(slot0 + nr) * a.row_stride + col;
 #pragma unroll
                 for (int i = 0; i < RPL; ++i)
-                    if (rg + RG * i == nr) {
+                    if (rg + RG * i == nr && in_pool) {
 #pragma unroll
                         for (int c = 0; c < NC; ++c) {
                             store16(dst + 8 * LPR * c, kx[i][c]);
                             store16(dst + 8 * LPR * c + a.half_stride, vx[i][c]);
                         }
                     }
-                ops += 2 * NC;   // one row of the tile holds the new token
+                // one row of the tile holds the new token; in_pool is the same
+                // in every lane, so the stores were issued exactly when it holds
+                if (in_pool)
+                    ops += 2 * NC;
             }
             if (info & kInfoSegLast) {
                 // Add the row groups: the weight sums in every lane, the
@@ -1438,7 +1453,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     // Entries over the page bound: NaN rows (the broken precondition shows
     // instead of a truncated result) and, when fused, the append all the same.
     for (int b = blockIdx.x; b < a.batch; b += gridDim.x) {
-        const int4 e = ent[b];
+        const int4 e = plan_ok ? ent[b] : make_int4(0, -1, -1, -1);
         if (e.y >= 0)
             continue;
 #pragma unroll
@@ -1455,7 +1470,10 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             if (a.lse != nullptr && j == 0)
                 a.lse[(int64_t)b * a.num_qo_heads + hq] = __builtin_nanf("");
         }
-        if (fused) {
+        // with a plan of other arguments, no append; otherwise the target must
+        // lie in the pool
+        if (fused && plan_ok && (unsigned)e.z < (unsigned)a.num_pages &&
+            (unsigned)e.w < (unsigned)a.page_size) {
             const int64_t src = ((int64_t)b * a.num_kv_heads + h) * D + j * 8;
             uint16_t *dst = a.cache_w + (int64_t)e.z * a.page_stride +
                             (int64_t)e.w * a.row_stride + col;
@@ -1512,12 +1530,8 @@ const void *run_kernel_dn(int group) {
 
 template <int D>
 const void *run_kernel_d(int group, int nbuf) {
-    switch (nbuf) {
-    case 2: return run_kernel_dn<D, 2>(group);
-    case 3: return run_kernel_dn<D, 3>(group);
-    case 4: return run_kernel_dn<D, 4>(group);
-    default: return nullptr;
-    }
+    static_assert(kMaxStageBuffers == 2, "only the two-buffer ring is instantiated");
+    return nbuf == 2 ? run_kernel_dn<D, 2>(group) : nullptr;
 }
 
 // The decode with the fused q/k norm + rotary embedding: head_dim 128, groups
@@ -1549,22 +1563,112 @@ size_t stage_buffer_bytes(int nw, int head_dim, int group) {
     return (size_t)2 * kTileTokens * nw * head_dim * 2 + (size_t)nw * qi * 1024;
 }
 
+// Per-device facts the launches need, queried once per device and kept for
+// the life of the process: the LDS a workgroup may use, the compute units,
+// and for each decode kernel the dynamic LDS it has been allowed and how many
+// of its workgroups one compute unit holds.  Guarded by a mutex, so the
+// calls stay thread-safe.
+constexpr int kMaxDevices = 64;
+struct DeviceFacts {
+    bool known = false;
+    int max_lds = 0;
+    int cus = 0;
+};
+struct KernelFacts {
+    int dev;
+    const void *kernel;
+    size_t lds;       // dynamic LDS the kernel has been allowed on dev
+    int threads;
+    int per_cu;       // workgroups of `threads` threads with `lds` bytes per CU
+};
+std::mutex g_facts_mu;
+DeviceFacts g_dev_facts[kMaxDevices];
+constexpr int kMaxKernelFacts = 256;
+KernelFacts g_kernel_facts[kMaxKernelFacts];
+int g_num_kernel_facts = 0;
+
+hipError_t device_facts(int *dev, DeviceFacts *out) {
+    hipError_t err = hipGetDevice(dev);
+    if (err != hipSuccess)
+        return err;
+    if (*dev < 0 || *dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_facts_mu);
+    DeviceFacts &f = g_dev_facts[*dev];
+    if (!f.known) {
+        int lds = 0, cus = 0;
+        err = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, *dev);
+        if (err == hipSuccess)
+            err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, *dev);
+        if (err != hipSuccess)
+            return err;
+        f.max_lds = lds;
+        f.cus = cus;
+        f.known = true;
+    }
+    *out = f;
+    return hipSuccess;
+}
+
+// Allows `kernel` `lds` bytes of dynamic LDS on device dev (once; again only
+// when a call needs more) and returns how many of its workgroups of
+// `threads` threads a compute unit holds with that much LDS.
+hipError_t kernel_facts(int dev, const void *kernel, size_t lds, int threads, int *per_cu) {
+    std::lock_guard<std::mutex> lock(g_facts_mu);
+    KernelFacts *f = nullptr;
+    for (int i = 0; i < g_num_kernel_facts; ++i)
+        if (g_kernel_facts[i].dev == dev && g_kernel_facts[i].kernel == kernel) {
+            f = &g_kernel_facts[i];
+            break;
+        }
+    if (f != nullptr && f->lds >= lds && f->threads == threads) {
+        if (per_cu != nullptr)
+            *per_cu = f->per_cu;
+        return hipSuccess;
+    }
+    const size_t allow = f != nullptr && f->lds > lds ? f->lds : lds;
+    hipError_t err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)allow);
+    int pc = 0;
+    if (err == hipSuccess)
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&pc, kernel, threads, lds);
+    if (err != hipSuccess)
+        return err;
+    if (f == nullptr) {
+        if (g_num_kernel_facts == kMaxKernelFacts) {
+            // full (far more kernels than exist): answer without keeping it
+            if (per_cu != nullptr)
+                *per_cu = pc;
+            return hipSuccess;
+        }
+        f = &g_kernel_facts[g_num_kernel_facts++];
+        f->dev = dev;
+        f->kernel = kernel;
+    }
+    f->lds = allow;
+    f->threads = threads;
+    f->per_cu = pc;
+    if (per_cu != nullptr)
+        *per_cu = pc;
+    return hipSuccess;
+}
+
 // Staging depth (buffers) and LDS bytes of the decode kernel on the current
 // device: as deep as LDS allows, up to kMaxStageBuffers.
-hipError_t stage_shape(int head_dim, int group, int num_kv_heads, int *nbuf, size_t *lds) {
-    int dev = 0, max_lds = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err == hipSuccess)
-        err = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+hipError_t stage_shape(int head_dim, int group, int num_kv_heads, int *dev, int *cus,
+                       int *nbuf, size_t *lds) {
+    DeviceFacts f;
+    hipError_t err = device_facts(dev, &f);
     if (err != hipSuccess)
         return err;
     const size_t buf = stage_buffer_bytes(group_waves(num_kv_heads), head_dim, group);
-    int n = (int)((size_t)max_lds / buf);
+    int n = (int)((size_t)f.max_lds / buf);
     n = n > kMaxStageBuffers ? kMaxStageBuffers : n;
     if (n < 2)
         return hipErrorInvalidValue;
     *nbuf = n;
     *lds = buf * (size_t)n;
+    *cus = f.cus;
     return hipSuccess;
 }
 
@@ -1586,23 +1690,16 @@ bool run_norm_rope_supported(int head_dim, int group) {
 }
 
 hipError_t balanced_blocks(int head_dim, int group, int num_kv_heads, int *blocks) {
-    int nbuf = 0;
+    int dev = 0, cus = 0, nbuf = 0, per_cu = 0;
     size_t lds = 0;
-    hipError_t err = stage_shape(head_dim, group, num_kv_heads, &nbuf, &lds);
+    hipError_t err = stage_shape(head_dim, group, num_kv_heads, &dev, &cus, &nbuf, &lds);
     if (err != hipSuccess)
         return err;
     const void *k = run_kernel_ptr(head_dim, group, nbuf);
     if (k == nullptr)
         return hipErrorInvalidValue;
-    int dev = 0, cus = 0, per_cu = 0;
-    err = hipGetDevice(&dev);
-    if (err == hipSuccess)
-        err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int waves = group_waves(num_kv_heads);
-    if (err == hipSuccess)
-        err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err == hipSuccess)
-        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 64 * waves, lds);
+    err = kernel_facts(dev, k, lds, 64 * waves, &per_cu);
     if (err != hipSuccess)
         return err;
     const int head_groups = num_kv_heads / waves;
@@ -1632,9 +1729,9 @@ hipError_t launch_plan(const PlanArgs &a, hipStream_t stream) {
 
 hipError_t launch_run(const RunArgs &a, const int32_t *blocks, const int32_t *ent,
                       int num_blocks, int head_dim, int group, hipStream_t stream) {
-    int nbuf = 0;
+    int dev = 0, cus = 0, nbuf = 0;
     size_t lds = 0;
-    hipError_t err = stage_shape(head_dim, group, a.num_kv_heads, &nbuf, &lds);
+    hipError_t err = stage_shape(head_dim, group, a.num_kv_heads, &dev, &cus, &nbuf, &lds);
     if (err != hipSuccess)
         return err;
     const void *k = a.q_w != nullptr ? run_kernel_nr_ptr(head_dim, group, nbuf)
@@ -1643,7 +1740,7 @@ hipError_t launch_run(const RunArgs &a, const int32_t *blocks, const int32_t *en
         return hipErrorInvalidValue;
     if (a.q_w != nullptr)
         lds += (size_t)group_waves(a.num_kv_heads) * kNormRopeLds;
-    err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    err = kernel_facts(dev, k, lds, 64 * group_waves(a.num_kv_heads), nullptr);
     if (err != hipSuccess)
         return err;
     RunArgs args = a;

@@ -36,8 +36,12 @@ constexpr int kTileTokens = 8;
 //                                 bound), and the append target page / slot
 //   blocks  int4  [num_blocks][block_stride]
 //                                 per decode workgroup: a header {tiles, run,
-//                                 0, 0} and then one record per tile
-//                                 {page, info, entry, partial slot}
+//                                 plan signature, 0} and then one record per
+//                                 tile {page, info, entry, partial slot}
+// The plan signature is a nonzero 32-bit hash of the arguments the plan was
+// made for (batch, heads, page size, head_dim, page bound, chunk, pool pages,
+// workgroups, record stride, tiles per page); a decode launch compares it
+// with the hash of its own arguments before it uses any record.
 //   part_o  fp16  [slots, Hq, D]  partial outputs of split entries, each
 //                                 (slot, KV head) scaled by a power of two
 //                                 2^-s that keeps them below 1 in magnitude
@@ -53,6 +57,7 @@ constexpr int kInfoHasNew = 1 << 15;      // the tile holds the entry's token L-
 constexpr int kInfoNewRowShift = 16;      // bits 16-18: that token's row in the tile
 
 struct PlanArgs {
+    int32_t plan_sig;         // signature written into every block header
     const int32_t *indptr;
     const int32_t *indices;
     const int32_t *last_len;
@@ -72,6 +77,9 @@ struct PlanArgs {
 };
 
 struct RunArgs {
+    int32_t plan_sig;         // the signature this launch's arguments give
+    int32_t num_pages;        // pool pages: page ids past it are read as page 0
+    int32_t page_size;
     const uint16_t *cache;    // first element of this layer's slab
     uint16_t *cache_w;        // same slab, written by the fused append, or null
     const uint16_t *q;        // [batch, Hq, D]

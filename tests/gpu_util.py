@@ -2,6 +2,9 @@
 through the C ABI, and compare with the fp64 oracle on the same inputs."""
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -92,3 +95,50 @@ def oracle_rows_from_device(cache_dev_layer, ld_host, table, entries, heads, sm_
     out, lse = oracle.decode_rows(mini, 0, ld_host.q[entries], indptr, indices, last,
                                   sm_scale, rb, rh, chunk_pages=chunk)
     return out, lse, (np.asarray(entries)[rb], rh)
+
+
+def oracle_threads() -> int:
+    """Host threads the oracle may use in a test: every CPU of the process's
+    affinity set, at most 16 (the oracle releases the GIL)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_all_rows_from_device(cache_dev_layer, ld_host, table, sm_scale):
+    """Oracle rows for EVERY active entry and EVERY query head of a layer whose
+    cache lives on the GPU (pre-append pages, as for oracle_rows_from_device).
+
+    The active entries' pages are copied to the host once; the oracle appends
+    the new rows there and then computes the rows on a pool of host threads,
+    each taking its own share of the (entry, head) rows.  Returns (out fp64
+    [A, Hq, D], lse fp64 [A, Hq], active entry ids)."""
+    entries = np.flatnonzero(table.active)
+    pages = [table.indices[table.indptr[b]:table.indptr[b + 1]] for b in entries]
+    flat = np.concatenate(pages).astype(np.int64)
+    host_pages = to_host_u16(cache_dev_layer[torch.from_numpy(flat).to(DEV)])
+    mini = np.zeros((1, 1 + len(flat)) + host_pages.shape[1:], dtype=np.uint16)
+    mini[0, 1:] = host_pages
+    del host_pages
+    indptr = np.zeros(len(entries) + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum([len(p) for p in pages])
+    indices = np.arange(1, 1 + len(flat), dtype=np.int32)
+    last = np.asarray(table.last_len)[entries].astype(np.int32)
+    q = np.ascontiguousarray(ld_host.q[entries])
+    oracle.append(mini, 0, ld_host.k_new[entries], ld_host.v_new[entries], indptr,
+                  indices, last)
+    hq = q.shape[1]
+    rb = np.repeat(np.arange(len(entries)), hq)
+    rh = np.tile(np.arange(hq), len(entries))
+    # interleaved shares: long and short entries spread over the threads
+    nt = oracle_threads()
+    shares = [np.arange(i, len(rb), nt) for i in range(nt)]
+
+    def job(idx):
+        return oracle.decode_rows(mini, 0, q, indptr, indices, last, sm_scale, rb[idx],
+                                  rh[idx])
+
+    out = np.zeros((len(rb), q.shape[2]))
+    lse = np.zeros(len(rb))
+    with ThreadPoolExecutor(max_workers=nt) as ex:
+        for idx, (o, l) in zip(shares, ex.map(job, shares)):
+            out[idx], lse[idx] = o, l
+    return out.reshape(len(entries), hq, -1), lse.reshape(len(entries), hq), entries

@@ -124,6 +124,9 @@ def _norm_rope(desc=DESC, layer=0, q=FAKE, hq=4, k=FAKE, v=FAKE, qw=FAKE, kw=FAK
     (dict(q=NULL), -1), (dict(kw=NULL), -1), (dict(pos=NULL), -1), (dict(q_out=NULL), -1),
     (dict(tables=(FAKE, FAKE, NULL)), -1), (dict(cache=NULL), -1),
     (dict(qw=ctypes.c_void_p(0x100008)), -6), (dict(q_out=ctypes.c_void_p(0x100004)), -6),
+    # head counts whose 32-bit sum would overflow are rejected before any sum
+    (dict(hq=0x7fffffff), -2), (dict(hq=65536), -2),
+    (dict(desc=CacheDesc(2, 64, 16, 70000, 64)), -2),
 ])
 def test_norm_rope_validation(kw, code):
     assert _norm_rope(**kw) == code
@@ -145,7 +148,7 @@ def _prefill(desc=CacheDesc(2, 64, 16, 2, 128), layer=0, q=FAKE, hq=4, qo=FAKE, 
     (dict(scale=float("nan")), -2), (dict(desc=CacheDesc(2, 64, 16, 2, 64)), -3),
     (dict(batch=70000), -3), (dict(q=NULL), -1), (dict(qo=NULL), -1), (dict(out=NULL), -1),
     (dict(k=NULL), -1), (dict(tables=(FAKE, NULL, FAKE)), -1),
-    (dict(out=ctypes.c_void_p(0x100004)), -6),
+    (dict(out=ctypes.c_void_p(0x100004)), -6), (dict(hq=0x7fffffff), -2),
 ])
 def test_prefill_validation(kw, code):
     assert _prefill(**kw) == code

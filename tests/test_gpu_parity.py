@@ -17,8 +17,8 @@ import oracle
 import paged_kv_decode_pkv_amd as pkv
 import workloads
 from golden_cases import build_case, load_cases
-from gpu_util import (DEV, compare, gpu_step, host_layer_case, oracle_rows_from_device,
-                      table_to_dev, to_dev_u16, to_host_u16)
+from gpu_util import (DEV, compare, gpu_step, host_layer_case, oracle_all_rows_from_device,
+                      oracle_rows_from_device, table_to_dev, to_dev_u16, to_host_u16)
 from workloads import CONFIGS, bf16_to_f32, make_table, table_from_lengths
 
 pytestmark = pytest.mark.gpu
@@ -233,6 +233,58 @@ def test_decode_config6_cfg_pairs_zero_padded_heads(chunk):
     eh = torch.from_numpy(rh).to(DEV)
     assert not to_host_u16(out[..., real:]).any(), "padded output columns are not zero"
     compare(out[eb, eh][..., :real], lse[eb, eh], ro, rl, what=f"cfg6 chunk {chunk}")
+
+
+def _full_check(spec, table, cache, layer, dev, chunk=0, what="", fused=False):
+    """Append + decode of one layer in the benchmark's launch shape; EVERY
+    active entry x EVERY query head compared with the oracle, element by
+    element, at the decode bars."""
+    host_rows = _HostRows(*dev)
+    ro, rl, ent = oracle_all_rows_from_device(cache[layer], host_rows, table, spec.sm_scale)
+    tables = table_to_dev(table)
+    if fused:
+        q, kn, vn = dev
+        out, lse = pkv.append_decode(cache, layer, kn, vn, q, *tables, spec.sm_scale,
+                                     max_pages_per_req=table.max_pages_per_req,
+                                     kv_chunk_pages=chunk)
+    else:
+        out, lse = gpu_step(cache, layer, dev, tables, table, spec.sm_scale, chunk)
+    sel = torch.from_numpy(ent).to(DEV)
+    stats = compare(out[sel], lse[sel], ro, rl, what=what)
+    print(f"{what}: {len(ent)} entries x {ro.shape[1]} heads: {stats}", flush=True)
+    return stats
+
+
+@pytest.mark.parametrize("chunk", [0, 32, 64])
+def test_decode_config5_all_rows(chunk):
+    """Long-context layer (batch 8, 16k-32k tokens, per-head K offsets): every
+    query head of every entry, for the balanced split and 32- and 64-page
+    runs (16-64 runs merged per entry)."""
+    spec = CONFIGS[5]
+    table, cache, per_layer = _device_case(spec)
+    _full_check(spec, table, cache, 0, per_layer[0], chunk=chunk, what=f"cfg5 chunk{chunk}")
+
+
+def test_decode_config3_all_rows():
+    """Qwen3-4B-like step in the benchmark's launch shape (balanced split,
+    fused append + decode): layers 0, 17 and 35, every query head of all 64
+    entries."""
+    spec = CONFIGS[3]
+    table, cache, per_layer = _device_case(spec, layers=(0, 17, 35))
+    for layer in (0, 17, 35):
+        _full_check(spec, table, cache, layer, per_layer[layer], fused=True,
+                    what=f"cfg3 layer {layer}")
+
+
+@pytest.mark.parametrize("chunk", [0, 16])
+def test_decode_config4_all_rows(chunk):
+    """Qwen3-0.6B-like layers at batch 256 (26 padding entries): layers 0 and
+    27, every query head of every active entry."""
+    spec = CONFIGS[4]
+    table, cache, per_layer = _device_case(spec, 256, layers=(0, 27))
+    for layer in (0, 27):
+        _full_check(spec, table, cache, layer, per_layer[layer], chunk=chunk,
+                    what=f"cfg4 B=256 layer {layer} chunk {chunk}")
 
 
 def _pick_entries(table, n):
@@ -477,6 +529,64 @@ def test_entries_over_the_page_bound_get_nan_rows(chunk):
     ro, rl = _oracle_full(cache_host, 0, ld, table, spec.sm_scale)
     ok = table.active & ~over
     compare(out, lse, ro[ok], rl[ok], rows=ok, what="rows under the bound")
+
+
+def test_run_on_a_mismatched_plan_gives_nan_rows_and_no_cache_writes():
+    """pkv_run compares the plan's signature with its own arguments before it
+    uses the plan: on a workspace holding no plan (zeroed, or filled with a
+    byte pattern) or a plan made for other arguments it writes NaN rows and
+    leaves every cache byte as it was, fused append included; a matching plan
+    then gives the oracle's rows."""
+    spec = CONFIGS[2]
+    table = make_table(spec)
+    ld, dev = host_layer_case(spec, table, 0)
+    cache_host = ld.cache[None].copy()
+    cache = to_dev_u16(cache_host)
+    tables = table_to_dev(table)
+    mp = table.max_pages_per_req
+    hq, b = spec.num_qo_heads, table.batch
+    desc = pkv.cache_desc(cache)
+    need = max(pkv.workspace_size(desc, hq, b, mp, c) for c in (0, 4))
+    need = max(need, pkv.workspace_size(desc, hq, b, 2 * mp, 0))
+
+    def expect_nan_untouched(ws, chunk, maxp, what):
+        plan = pkv.DecodePlan(ws, b, hq, maxp, chunk)
+        out, lse = pkv.run(cache, 0, dev[0], plan, spec.sm_scale, k_new=dev[1], v_new=dev[2])
+        torch.cuda.synchronize()
+        assert np.all(np.isnan(lse.cpu().numpy())), what
+        assert np.all(np.isnan(bf16_to_f32(to_host_u16(out)))), what
+        np.testing.assert_array_equal(to_host_u16(cache), cache_host, err_msg=what)
+
+    expect_nan_untouched(torch.zeros(need, dtype=torch.uint8, device=DEV), 0, mp,
+                         "zeroed workspace")
+    expect_nan_untouched(torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV), 0, mp,
+                         "byte-pattern workspace")
+    # plans made for other arguments, each in a workspace of its own (a
+    # workspace still holding an earlier plan for these very arguments is a
+    # valid plan for them: the page table is the caller's to keep unchanged)
+    def other_plan(*plan_args):
+        ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+        pkv.plan(cache, hq, *plan_args, workspace=ws)
+        return ws
+
+    expect_nan_untouched(other_plan(*tables, mp, 0), 4, mp,
+                         "planned balanced, run as 4-page runs")
+    expect_nan_untouched(other_plan(*tables, mp, 4), 0, mp,
+                         "planned as 4-page runs, run balanced")
+    expect_nan_untouched(other_plan(*tables, mp, 0), 0, 2 * mp,
+                         "planned for another page bound")
+    half = (tables[0][: b // 2 + 1], tables[1], tables[2][: b // 2])
+    expect_nan_untouched(other_plan(*half, mp, 0), 0, mp, "planned for half the batch")
+    # the matching plan: the oracle's rows and appends
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    plan = pkv.plan(cache, hq, *tables, mp, 0, workspace=ws)
+    out, lse = pkv.run(cache, 0, dev[0], plan, spec.sm_scale, k_new=dev[1], v_new=dev[2])
+    ro, rl = _oracle_full(cache_host, 0, ld, table, spec.sm_scale)
+    act = table.active
+    compare(out, lse, ro[act], rl[act], rows=act, what="matching plan")
+    got = to_host_u16(cache)
+    got[0, 0] = cache_host[0, 0]
+    np.testing.assert_array_equal(got, cache_host)
 
 
 # ------------------------------------------------------------ plan once, run per layer
