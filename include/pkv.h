@@ -339,6 +339,32 @@ int pkv_append_decode(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pkv_decode_static -- pkv_decode with no workspace argument and no
+ * allocation, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Computes exactly what pkv_decode computes (same plan and kernels, so the
+ * same bits), with the plan and partial rows in a 16 MiB (16 << 20 bytes)
+ * device array inside the library instead of a caller's workspace.  Each GPU
+ * the library runs on holds its own array from the first call on that device
+ * until the process ends; the first call on a device looks its address up
+ * (no allocation, then or later).  Every call on a GPU shares that GPU's
+ * array and leaves its plan there: calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller, as they
+ * would be on one shared workspace.
+ *  Arguments as for pkv_decode, without workspace / workspace_bytes.
+ * Returns PKV_ERR_WORKSPACE, before touching the device, when the call needs
+ * more than 16 MiB (pkv_decode_workspace_size gives the need); other errors
+ * as for pkv_decode.
+ */
+int pkv_decode_static(const void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+                      const void *q, int32_t num_qo_heads,
+                      const int32_t *page_indptr, const int32_t *page_indices,
+                      const int32_t *last_page_len, int32_t batch, float sm_scale,
+                      void *out, float *lse, int32_t max_pages_per_req,
+                      int32_t kv_chunk_pages, hipStream_t stream);
+
+/*
  * pkv_validate_page_table -- debug check of HOST copies of a page table
  * against the device-side preconditions above.  Returns PKV_OK or
  * PKV_ERR_BAD_TABLE (with *bad_entry set to the first offending entry, or -1

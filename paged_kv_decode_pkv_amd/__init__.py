@@ -99,6 +99,9 @@ def _load():
     lib.pkv_decode.argtypes = [p, CacheDesc, i32, p, i32, p, p, p, i32, ctypes.c_float,
                                p, p, i32, i32, p, sz, p]
     lib.pkv_decode.restype = ctypes.c_int
+    lib.pkv_decode_static.argtypes = [p, CacheDesc, i32, p, i32, p, p, p, i32,
+                                      ctypes.c_float, p, p, i32, i32, p]
+    lib.pkv_decode_static.restype = ctypes.c_int
     lib.pkv_append_decode.argtypes = [p, CacheDesc, i32, p, p, p, i32, p, p, p, i32,
                                       ctypes.c_float, p, p, i32, i32, p, sz, p]
     lib.pkv_append_decode.restype = ctypes.c_int
@@ -375,6 +378,34 @@ def decode(kv_cache, layer: int, q, page_indptr, page_indices, last_page_len,
                         _stream(stream))
     if rc != PKV_OK:
         raise PkvError(rc, "pkv_decode")
+    return out, lse
+
+
+def decode_static(kv_cache, layer: int, q, page_indptr, page_indices, last_page_len,
+                  sm_scale: float, max_pages_per_req: int, kv_chunk_pages: int = 0,
+                  out=None, lse=None, with_lse: bool = True, stream=None):
+    """:func:`decode` through pkv_decode_static: no workspace, the plan and
+    partial rows in the library's own 16 MiB device array (callers that
+    cannot allocate; ``out`` and ``lse`` must then be passed in)."""
+    import torch
+    desc = cache_desc(kv_cache)
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError(f"q must be [batch, Hq, {desc.head_dim}], got {tuple(q.shape)}")
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    dev = kv_cache.device
+    if out is None:
+        out = torch.empty((batch, hq, desc.head_dim), dtype=torch.bfloat16, device=dev)
+    if lse is None and with_lse:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    lse_ptr = ctypes.c_void_p(0) if lse is None else _dev_ptr(lse, "lse", torch.float32, dev)
+    rc = lib.pkv_decode_static(_dev_ptr(kv_cache, "kv_cache", torch.bfloat16), desc,
+                               int(layer), _dev_ptr(q, "q", torch.bfloat16, dev), hq,
+                               *_tables(kv_cache, page_indptr, page_indices, last_page_len),
+                               batch, float(sm_scale),
+                               _dev_ptr(out, "out", torch.bfloat16, dev), lse_ptr,
+                               int(max_pages_per_req), int(kv_chunk_pages), _stream(stream))
+    if rc != PKV_OK:
+        raise PkvError(rc, "pkv_decode_static")
     return out, lse
 
 

@@ -628,6 +628,31 @@ int pkv_append_decode(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, cons
                         max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes, stream);
 }
 
+int pkv_decode_static(const void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+                      const void *q, int32_t num_qo_heads, const int32_t *page_indptr,
+                      const int32_t *page_indices, const int32_t *last_page_len,
+                      int32_t batch, float sm_scale, void *out, float *lse,
+                      int32_t max_pages_per_req, int32_t kv_chunk_pages, hipStream_t stream) {
+    const int rc = check_decode_args(desc, layer, num_qo_heads, batch, sm_scale,
+                                     max_pages_per_req, kv_chunk_pages);
+    if (rc != PKV_OK || batch == 0)
+        return rc;
+    // the size check is host arithmetic only: nothing reaches the device for
+    // a call the array cannot hold
+    const Layout lay = make_layout(desc, num_qo_heads, batch, max_pages_per_req,
+                                   kv_chunk_pages);
+    if ((uint64_t)lay.ws_bytes > (uint64_t)pkv::kStaticScratchBytes)
+        return PKV_ERR_WORKSPACE;
+    void *scratch = nullptr;
+    const int hrc = hip_status(pkv::static_scratch(&scratch));
+    if (hrc != PKV_OK)
+        return hrc;
+    return plan_and_run(const_cast<void *>(kv_cache), desc, layer, nullptr, nullptr, q,
+                        num_qo_heads, page_indptr, page_indices, last_page_len, batch,
+                        sm_scale, out, lse, max_pages_per_req, kv_chunk_pages, scratch,
+                        pkv::kStaticScratchBytes, stream);
+}
+
 int pkv_validate_page_table(const int32_t *page_indptr, const int32_t *page_indices,
                             const int32_t *last_page_len, int32_t batch, int32_t num_pages,
                             int32_t page_size, int32_t max_pages_per_req, int32_t *bad_entry) {

@@ -1672,7 +1672,38 @@ hipError_t stage_shape(int head_dim, int group, int num_kv_heads, int *dev, int 
     return hipSuccess;
 }
 
+// Device memory of pkv_decode_static: the plan and partial rows of one call
+// live in this file-scope array instead of a caller's workspace.  Each GPU
+// the library runs on holds its own copy for the life of the process.  Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device, and is kept in g_scratch_ptr.
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
 }  // namespace
+
+hipError_t static_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return err;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess)
+            return err;
+        if (p == nullptr)
+            return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_append(const AppendArgs &a, int batch, hipStream_t stream) {
     AppendArgs args = a;

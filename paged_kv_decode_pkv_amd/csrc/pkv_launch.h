@@ -252,6 +252,13 @@ bool run_norm_rope_supported(int head_dim, int group);
 
 hipError_t launch_plan(const PlanArgs &a, hipStream_t stream);
 
+// Bytes of the file-scope device array behind pkv_decode_static.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+
+// Device address of that array on the current device (looked up once per
+// device with hipGetSymbolAddress and kept).  No allocation.
+hipError_t static_scratch(void **ptr);
+
 // Enqueues the decode kernel: num_blocks x head-group workgroups.
 hipError_t launch_run(const RunArgs &a, const int32_t *blocks, const int32_t *ent,
                       int num_blocks, int head_dim, int group, hipStream_t stream);

@@ -23,7 +23,7 @@ def test_every_declared_symbol_is_exported():
                           "pkv_qk_norm_mrope_append",
                           "pkv_decode_workspace_size",
                           "pkv_append_decode", "pkv_decode", "pkv_plan", "pkv_run",
-                          "pkv_run_qk_norm_rope",
+                          "pkv_run_qk_norm_rope", "pkv_decode_static",
                           "pkv_validate_page_table", "pkv_status_string",
                           "pkv_last_hip_error"}
     for n in names:
@@ -294,3 +294,19 @@ def test_norm_mrope_validation(kw, code):
 
 def test_norm_mrope_batch_zero_is_noop():
     assert _norm_mrope(batch=0) == 0
+
+
+def test_decode_static_rejects_what_its_array_cannot_hold():
+    # 16 MiB of device memory behind pkv_decode_static: a call needing more is
+    # refused before anything reaches the device (no GPU here), argument
+    # errors as for pkv_decode, batch 0 a no-op
+    d = CacheDesc(1, 1 << 20, 16, 8, 128)
+    assert pkv.workspace_size(d, 32, 4096, 4096, 0) > 16 << 20
+    assert lib.pkv_decode_static(FAKE, d, 0, FAKE, 32, FAKE, FAKE, FAKE, 4096, 0.1, FAKE,
+                                 NULL, 4096, 0, NULL) == -4
+    assert lib.pkv_decode_static(FAKE, d, 1, FAKE, 32, FAKE, FAKE, FAKE, 4, 0.1, FAKE, NULL,
+                                 16, 0, NULL) == -2
+    assert lib.pkv_decode_static(FAKE, d, 0, FAKE, 30, FAKE, FAKE, FAKE, 4, 0.1, FAKE, NULL,
+                                 16, 0, NULL) == -2
+    assert lib.pkv_decode_static(NULL, d, 0, NULL, 32, NULL, NULL, NULL, 0, 0.1, NULL, NULL,
+                                 16, 0, NULL) == 0
