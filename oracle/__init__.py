@@ -39,7 +39,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pkv_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# PKV_ORACLE_LIB: another build of pkv_oracle.c to load instead (the
+# sanitizer test runs every pin against an AddressSanitizer build)
+_LIB_PATH = os.environ.get("PKV_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
@@ -57,7 +59,8 @@ def load(path: str = _LIB_PATH):
     if _lib is not None and path == _LIB_PATH:
         return _lib
     if not os.path.exists(path) or (
-            path == _LIB_PATH and os.path.getmtime(path) < os.path.getmtime(_SRC)):
+            path == _LIB_PATH and not os.environ.get("PKV_ORACLE_LIB")
+            and os.path.getmtime(path) < os.path.getmtime(_SRC)):
         build(out=path)
     lib = ctypes.CDLL(path)
     i64, p = ctypes.c_int64, ctypes.c_void_p
