@@ -74,8 +74,12 @@ Layout make_layout(const pkv_cache_desc_t &d, int32_t num_qo_heads, int32_t batc
         if (p.max_chunks < 1)
             p.max_chunks = 1;
         p.slots = (int64_t)batch * p.max_chunks;
-        const int64_t nblocks = ((int64_t)batch + 7) / 8 * 8 * p.max_chunks;
-        block_ints4 = nblocks * (1 + (int64_t)p.chunk_tiles);
+        // the chunks are dealt to W <= wb workgroups, each holding at most
+        // fixed_capacity records: W (1 + capacity) <= wb (1 + c) + T c for
+        // T = batch * max_chunks chunks of at most c tiles
+        const int64_t wb = pkv::balanced_blocks_bound(d.num_kv_heads);
+        const int64_t c = p.chunk_tiles < entry_tiles ? p.chunk_tiles : entry_tiles;
+        block_ints4 = wb * (1 + c) + p.slots * c;
     } else {
         const int64_t wb = pkv::balanced_blocks_bound(d.num_kv_heads);
         p.slots = wb + batch;
@@ -109,7 +113,7 @@ int check_decode_args(const pkv_cache_desc_t &desc, int32_t layer, int32_t num_q
         num_qo_heads % desc.num_kv_heads != 0 || !isfinite(sm_scale) ||
         max_pages_per_req < 1 || kv_chunk_pages < 0)
         return PKV_ERR_BAD_SHAPE;
-    if (kv_chunk_pages > pkv::kMaxChunkPages)
+    if (kv_chunk_pages > pkv::kMaxChunkPages || batch > pkv::kMaxPlanBatch)
         return PKV_ERR_UNSUPPORTED;
     const int group = num_qo_heads / desc.num_kv_heads;
     if ((desc.head_dim != 64 && desc.head_dim != 128) || group > 8 ||
@@ -132,18 +136,19 @@ int prepare(const pkv_cache_desc_t &desc, int32_t num_qo_heads, int32_t batch,
         return PKV_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return PKV_ERR_ALIGNMENT;
+    // both modes keep the workgroups the GPU holds at once busy
+    const int group = num_qo_heads / desc.num_kv_heads;
+    hipError_t err = pkv::balanced_blocks(desc.head_dim, group, desc.num_kv_heads, &num_blocks);
+    if (err != hipSuccess)
+        return hip_status(err);
     if (lay.chunk_tiles > 0) {
-        const int64_t nb = ((int64_t)batch + 7) / 8 * 8 * lay.max_chunks;
-        if (nb > 0x7fffffffLL || nb * (1 + (int64_t)lay.chunk_tiles) > 0x3fffffffLL)
+        const int64_t cap = pkv::fixed_capacity(lay.slots, lay.chunk_tiles,
+                                                lay.max_tiles / (batch > 0 ? batch : 1),
+                                                num_blocks);
+        if ((int64_t)num_blocks * (1 + cap) > 0x3fffffffLL)
             return PKV_ERR_BAD_SHAPE;
-        num_blocks = (int)nb;
-        block_stride = 1 + lay.chunk_tiles;
+        block_stride = (int)(1 + cap);
     } else {
-        const int group = num_qo_heads / desc.num_kv_heads;
-        hipError_t err = pkv::balanced_blocks(desc.head_dim, group, desc.num_kv_heads,
-                                              &num_blocks);
-        if (err != hipSuccess)
-            return hip_status(err);
         block_stride = (int)(1 + pkv::balanced_capacity(lay.max_tiles, batch, num_blocks));
     }
     return PKV_OK;

@@ -366,6 +366,40 @@ struct CostAxis {
     }
 };
 
+// Fixed mode deals whole chunks (runs of chunk_tiles tiles of one entry; an
+// entry's last chunk may be shorter) to the W resident workgroups.  Chunks
+// are ranked largest first: the F full chunks in entry order, then the P
+// shorter last chunks by decreasing size (ties, and every partial chunk of a
+// batch above kRankedBatch, in entry order).  Rank r goes to workgroup
+// r mod W in round r / W, the rounds alternating direction (a snake), so
+// workgroup w holds ranks k W + w for even k and k W + W - 1 - w for odd k:
+// with the larger chunks dealt first, the workgroups that drew smaller ones
+// draw next, close to a longest-first assignment.  Which workgroup computes a
+// chunk never changes its bits: a chunk's partial, and the merge of an
+// entry's chunks (in chunk order), depend only on the entry.
+struct FixedChunks {
+    const int *full;    // [batch + 1] prefix sums of full chunks per entry
+    const int *pent;    // [P] entry of the partial chunk of each rank
+    const int *psz;     // [P] its tiles
+    int batch, ct, W;
+    int F, P;
+    __device__ int rank_of(int w, int k) const {
+        return k * W + ((k & 1) ? W - 1 - w : w);
+    }
+    // entry b, chunk index c and tiles of the chunk of rank r (< F + P)
+    __device__ void chunk(int r, int &b, int &c, int &tiles) const {
+        if (r < F) {
+            b = entry_of(full, batch - 1, r);
+            c = r - full[b];
+            tiles = ct;
+        } else {
+            b = pent[r - F];
+            c = full[b + 1] - full[b];
+            tiles = psz[r - F];
+        }
+    }
+};
+
 __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     // balanced: [batch + 1] tile prefix sums, then [batch + 1] prefix counts
     // of entries with tiles
@@ -413,6 +447,60 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
         const int64_t cap = ax.C / (kTileCost * kMinRunTiles);
         ax.weff = cap < 1 ? 1 : (cap < W ? cap : W);
     }
+    FixedChunks fc{s_start, s_nz, s_nz + a.batch, a.batch, a.chunk_tiles, W, 0, 0};
+    if (fixed) {
+        // [batch + 1] full-chunk prefix sums, then [batch] entries and
+        // [batch] sizes of the partial chunks by rank; for ranking, the
+        // partial size of every entry (or 0) in a further [batch] array
+        int *s_pent = s_nz, *s_psz = s_nz + a.batch, *s_pse = s_nz + 2 * a.batch;
+        const int ranked = a.batch <= kRankedBatch;
+        const int nthreads = blockDim.x;
+        const int per = (a.batch + nthreads - 1) / nthreads;
+        const int e0 = min(a.batch, (int)threadIdx.x * per);
+        const int e1 = min(a.batch, e0 + per);
+        int local = 0, localp = 0;
+        for (int e = e0; e < e1; ++e) {
+            const int t = entry_shape(a, e).tiles;
+            const int fl = t / a.chunk_tiles, ps = t - fl * a.chunk_tiles;
+            s_start[e] = fl;
+            if (ranked)
+                s_pse[e] = ps;
+            local += fl;
+            localp += ps > 0;
+        }
+        int totf = 0, totp = 0;
+        int run = block_exclusive_scan(local, s_wave, totf);
+        __syncthreads();   // s_wave is reused
+        int runp = block_exclusive_scan(localp, s_wave, totp);
+        for (int e = e0; e < e1; ++e) {
+            const int fl = s_start[e];
+            s_start[e] = run;
+            run += fl;
+        }
+        if (threadIdx.x == 0)
+            s_start[a.batch] = totf;
+        __syncthreads();
+        for (int e = e0; e < e1; ++e) {
+            const int t = entry_shape(a, e).tiles;
+            const int ps = t - (s_start[e + 1] - s_start[e]) * a.chunk_tiles;
+            if (ps <= 0)
+                continue;
+            int q = runp++;   // entry order
+            if (ranked) {
+                // larger partial chunks first, ties in entry order
+                q = 0;
+                for (int f = 0; f < a.batch; ++f) {
+                    const int pf = s_pse[f];
+                    q += pf > ps || (pf == ps && f < e);
+                }
+            }
+            s_pent[q] = e;
+            s_psz[q] = ps;
+        }
+        __syncthreads();
+        fc.F = totf;
+        fc.P = totp;
+    }
     const int64_t weff = fixed ? W : ax.weff;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
@@ -447,24 +535,33 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     for (int64_t i = tid; i < items; i += nth) {
         const int w = (int)(i / a.block_stride);
         const int jj = (int)(i - (int64_t)w * a.block_stride);
-        int b = 0, run = 0, ntiles = 0, lt0 = 0, nseg = 1, slot = 0;
+        int b = 0, run = 0, ntiles = 0, nseg = 1, slot = 0;
         int64_t g0 = 0, g1 = 0, s0 = 0;
         EntryShape e{};
+        int kc = 0, ct0 = 0, ctiles = 0;   // fixed: the chunk holding record jj - 1
         if (fixed) {
-            // chunk-major ids over rows of batch8 = batch rounded up to 8,
-            // entries rotated by the chunk number: chunk c of entry b runs on
-            // XCD (b - c) mod 8, so an entry's chunks spread over every XCD
-            const int batch8 = (a.batch + 7) & ~7;
-            const int c = w / batch8;
-            b = (w - c * batch8 + c) % batch8;
-            run = c;
-            if (b < a.batch) {
-                e = entry_shape(a, b);
-                lt0 = c * a.chunk_tiles;
-                ntiles = e.tiles > lt0 ? min(a.chunk_tiles, e.tiles - lt0) : 0;
-                nseg = (e.tiles + a.chunk_tiles - 1) / a.chunk_tiles;
-                slot = b * a.max_chunks + c;
+            // walk this workgroup's chunks (ranks in dealing order) to the one
+            // holding record jj - 1 (the header, jj 0, sums them all)
+            run = w;
+            const int T = fc.F + fc.P;
+            for (int k = 0;; ++k) {
+                const int r = fc.rank_of(w, k);
+                if (r >= T)
+                    break;
+                int cb, cc, csz;
+                fc.chunk(r, cb, cc, csz);
+                if (jj > 0 && jj - 1 < ntiles + csz) {
+                    b = cb;
+                    kc = cc;
+                    ct0 = ntiles;
+                    ctiles = csz;
+                    ntiles += csz;
+                    break;
+                }
+                ntiles += csz;
             }
+            if (jj > 0 && ctiles == 0)
+                continue;   // capacity this block does not use; never read
         } else {
             run = run_of_block(w, W, (int)weff);
             if (run < weff) {
@@ -483,9 +580,13 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
         int lt;
         bool seg_first, seg_last;
         if (fixed) {
-            lt = lt0 + k;
-            seg_first = k == 0;
-            seg_last = k == ntiles - 1;
+            const int t = k - ct0;   // tile within the chunk
+            e = entry_shape(a, b);
+            lt = kc * a.chunk_tiles + t;
+            seg_first = t == 0;
+            seg_last = t == ctiles - 1;
+            nseg = (e.tiles + a.chunk_tiles - 1) / a.chunk_tiles;
+            slot = b * a.max_chunks + kc;
         } else {
             const int64_t gk = g0 + k;
             b = entry_of(s_start, a.batch - 1, gk);
@@ -852,7 +953,8 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
 
     uint32_t qv[G][NC][4];    // q of the entry being computed
     float m[G], l[G], acc[G][NC][8];
-    int pend0 = -1, pend1 = -1;   // entries whose partial this wave wrote
+    int pend0 = -1, pend1 = -1;   // entries of this wave's first and last partials
+    int nsplit = 0;               // partials this wave wrote (split segment ends)
     // The first partial of a block usually ends before the block's last tile;
     // it signals its arrival at loop iteration sig_at, when its stores are
     // known to be complete, and old0 keeps what its counter held then.
@@ -1285,6 +1387,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                 write_rows(rec.z, rec.w, whole, u, lt);
                 ops += whole ? kOutStores + (a.lse != nullptr ? HPR : 0) : kPartStores + HPR;
                 if (!whole) {
+                    ++nsplit;
                     if (pend0 < 0) {
                         pend0 = rec.z;
                         // the copies of tile k + NBUF are issued after these
@@ -1366,14 +1469,65 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
         constexpr int NU = G * DU;
         constexpr int UPL = (NU + 63) / 64;
         constexpr int SR = 24 / UPL;
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-            const int b = pp == 0 ? pend0 : pend1;
-            if (b < 0)
-                break;
-            const int4 e = pp == 0 ? ent0 : ent1;
-            if ((pp == 0 ? arr0 : arr1) != e.y - 1)
-                continue;
+        // The entries this wave arrived last for are merged one after the
+        // other: pend0, pend1, then, in a block that ended more than two
+        // split segments (fixed runs dealt several to a workgroup), the ones
+        // between, found from the block's records one lane per record, 64
+        // at a time, their arrivals counted together.
+        int stage = 0;             // 0: pend0, 1: pend1, 2: the segments between
+        int k0 = 0, idx_base = 0;  // next record round, split ends before it
+        uint64_t todo = 0;         // lanes of the round whose entry to merge
+        int rz = 0;                // per lane: the record's entry
+        int4 rem = make_int4(0, 0, 0, 0);   // and its descriptor
+        for (;;) {
+            int b;
+            int4 e;
+            int32_t *cp;
+            if (stage == 0) {
+                stage = 1;
+                if (arr0 != ent0.y - 1)
+                    continue;
+                b = pend0;
+                e = ent0;
+                cp = cnt0;
+            } else if (stage == 1) {
+                stage = 2;
+                if (pend1 < 0 || arr1 != ent1.y - 1)
+                    continue;
+                b = pend1;
+                e = ent1;
+                cp = cnt1;
+            } else {
+                while (todo == 0 && nsplit > 2 && k0 < n) {
+                    const int k = k0 + lane;
+                    k0 += 64;
+                    const int4 rec = k < n ? blk[1 + k] : make_int4(0, 0, 0, 0);
+                    const bool split_end =
+                        k < n && (rec.y & kInfoSegLast) != 0 && (rec.y & kInfoSegWhole) == 0;
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(split_end);
+                    const int idx =
+                        idx_base + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+                    idx_base += __builtin_popcountll(m);
+                    const bool mine = split_end && idx >= 1 && idx <= nsplit - 2;
+                    int oldm = -1;
+                    rz = rec.z;
+                    if (mine) {
+                        rem = ent[rec.z];
+                        oldm = __hip_atomic_fetch_add(a.cnt + (int64_t)rec.z * a.num_kv_heads + h,
+                                                      1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    todo = __builtin_amdgcn_ballot_w64(mine && oldm == rem.y - 1);
+                }
+                if (todo == 0)
+                    break;
+                const int l = __builtin_ctzll(todo);
+                todo &= todo - 1;
+                b = __builtin_amdgcn_readlane(rz, l);
+                e = make_int4(__builtin_amdgcn_readlane(rem.x, l),
+                              __builtin_amdgcn_readlane(rem.y, l), 0, 0);
+                cp = a.cnt + (int64_t)b * a.num_kv_heads + h;
+            }
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             const int ns = e.y;
             uint32_t lo[UPL], oo[UPL];   // byte offsets in slot e.x: lse pair, outputs
@@ -1445,8 +1599,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                 }
             }
             if (lane == 0)
-                __hip_atomic_store(pp == 0 ? cnt0 : cnt1, 0, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(cp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
@@ -1753,7 +1906,16 @@ hipError_t launch_plan(const PlanArgs &a, hipStream_t stream) {
     const int64_t work = items > other ? items : other;
     int64_t grid = (work + 255) / 256;
     grid = grid < 1 ? 1 : (grid > 1024 ? 1024 : grid);
-    const size_t lds = a.chunk_tiles > 0 ? 0 : 2 * sizeof(int) * ((size_t)a.batch + 1);
+    const size_t lds = plan_lds_bytes(a.batch, a.chunk_tiles > 0);
+    int dev = 0;
+    DeviceFacts f;
+    hipError_t err = device_facts(&dev, &f);
+    if (err == hipSuccess && lds > (size_t)f.max_lds)
+        err = hipErrorInvalidValue;
+    if (err == hipSuccess)
+        err = kernel_facts(dev, reinterpret_cast<const void *>(&plan_kernel), lds, 256, nullptr);
+    if (err != hipSuccess)
+        return err;
     return launch_raw(reinterpret_cast<const void *>(&plan_kernel), dim3((unsigned)grid),
                       dim3(256), lds, params, stream);
 }

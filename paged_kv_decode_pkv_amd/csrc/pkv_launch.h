@@ -113,6 +113,20 @@ struct RunArgs {
 // larger batches use fixed chunks of kFallbackChunkPages pages.
 constexpr int kMaxBalancedBatch = 4096;
 constexpr int kFallbackChunkPages = 16;
+// Largest batch of any plan (fixed chunks keep three int arrays per entry in
+// the plan kernel's LDS), and the largest for which fixed mode ranks the
+// entries' last chunks by size (an all-pairs count in LDS; above it they are
+// dealt in entry order).
+constexpr int kMaxPlanBatch = 8192;
+constexpr int kRankedBatch = 256;
+
+// Dynamic LDS bytes of the plan kernel.
+inline size_t plan_lds_bytes(int batch, bool fixed) {
+    const size_t b = (size_t)batch;
+    if (!fixed)
+        return 2 * sizeof(int) * (b + 1);
+    return sizeof(int) * ((b + 1) + 2 * b + (batch <= kRankedBatch ? b : 0));
+}
 constexpr int kMaxChunkPages = 1 << 16;
 // Upper bounds for sizing workspace without a device query.
 constexpr int kMaxComputeUnits = 320;
@@ -160,6 +174,15 @@ inline int64_t balanced_capacity(int64_t max_tiles, int64_t batch, int64_t block
     const int64_t full = (max_tiles + blocks - 1) / blocks +
                          (kEntryCost * batch + kTileCost * blocks - 1) / (kTileCost * blocks) + 2;
     return full > 2 * kMinRunTiles + 2 ? full : 2 * kMinRunTiles + 2;
+}
+
+// Records one fixed-mode block may receive: the snake deals each of W
+// workgroups at most ceil(T / W) of the T chunks, each of at most
+// min(chunk_tiles, entry_tiles) tiles.
+inline int64_t fixed_capacity(int64_t chunks, int64_t chunk_tiles, int64_t entry_tiles,
+                              int64_t blocks) {
+    const int64_t c = chunk_tiles < entry_tiles ? chunk_tiles : entry_tiles;
+    return (chunks + blocks - 1) / blocks * (c > 0 ? c : 1);
 }
 
 inline int64_t balanced_blocks_bound(int num_kv_heads) {

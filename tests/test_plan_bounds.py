@@ -118,3 +118,79 @@ def test_workspace_holds_every_block_region(waves):
         bound = block_region_bound(max_tiles, batch, wb)
         for W in {1, 8, 100, wb // 2, wb - 1, wb}:
             assert W * (1 + capacity(max_tiles, batch, W)) <= bound
+
+
+# ------------------------------------------------------------- fixed runs
+RANKED = const("kRankedBatch")
+
+
+def fixed_deal(tiles, ct, W):
+    """Workgroup of every (entry, chunk), from the fixed-mode definition: the
+    full chunks in entry order, then the shorter last chunks largest first
+    (ties, and all of them above the ranked batch size, in entry order),
+    dealt in snake order over W workgroups."""
+    tiles = [int(t) for t in tiles]
+    full = [(b, c, ct) for b, t in enumerate(tiles) for c in range(t // ct)]
+    part = [(b, t // ct, t % ct) for b, t in enumerate(tiles) if t % ct]
+    if len(tiles) <= RANKED:
+        part.sort(key=lambda x: (-x[2], x[0]))
+    order = full + part
+    deal = {}
+    for r, (b, c, n) in enumerate(order):
+        k, i = divmod(r, W)
+        deal[(b, c)] = (i if k % 2 == 0 else W - 1 - i, n)
+    return deal
+
+
+def fixed_capacity(chunks, ct, entry_tiles, W):
+    return -(-chunks // W) * max(1, min(ct, entry_tiles))
+
+
+@pytest.mark.parametrize("ct", [1, 2, 8, 32, 128])
+def test_fixed_deal_covers_every_chunk_once_within_capacity(ct):
+    rng = np.random.default_rng(11 + ct)
+    for _ in range(60):
+        batch = int(rng.integers(1, 300))
+        maxt = int(rng.integers(1, 40 * ct + 1 if ct < 8 else 600))
+        tiles = rng.integers(0, maxt + 1, size=batch)
+        W = int(rng.choice([1, 8, 250, 256, 512]))
+        deal = fixed_deal(tiles, ct, W)
+        # each entry's chunks are exactly those of its own length: the split
+        # does not depend on the rest of the batch
+        for b, t in enumerate(tiles):
+            assert sorted(c for (bb, c) in deal if bb == b) == list(range(-(-int(t) // ct)))
+        load = np.zeros(W, np.int64)
+        for (b, c), (w, n) in deal.items():
+            assert 0 <= w < W and 0 < n <= ct
+            load[w] += n
+        assert load.sum() == tiles.sum()
+        max_chunks = max(1, -(-maxt // ct))
+        assert load.max() <= fixed_capacity(batch * max_chunks, ct, maxt, W)
+
+
+def test_fixed_deal_balances_the_qwen3_4b_like_step():
+    """16-page runs of the Qwen3-4B-like batch (lengths log-uniform in
+    [64, 4096], 8-token tiles) over 256 workgroups: the busiest workgroup
+    holds at most one run more than the mean share."""
+    import workloads
+    spec = workloads.CONFIGS[3]
+    table = workloads.make_table(spec)
+    tiles = -(-np.asarray(table.lengths) // 8)
+    ct, W = 32, 256
+    deal = fixed_deal(tiles, ct, W)
+    load = np.zeros(W, np.int64)
+    for (w, n) in deal.values():
+        load[w] += n
+    assert load.max() <= tiles.sum() / W + ct
+
+
+@pytest.mark.parametrize("waves", [1, 8])
+def test_workspace_holds_every_fixed_block_region(waves):
+    wb = (MAX_CUS * MAX_WAVES_CU + waves - 1) // waves
+    for batch, entry_tiles, ct in [(1, 2, 2), (64, 438, 32), (8, 4096, 2), (4200, 48, 32),
+                                   (256, 64, 131072)]:
+        chunks = batch * -(-entry_tiles // ct)
+        c = min(ct, entry_tiles)
+        bound = wb * (1 + c) + chunks * c
+        for W in {1, 8, 100, wb // 2, wb}:
+            assert W * (1 + fixed_capacity(chunks, ct, entry_tiles, W)) <= bound
