@@ -248,6 +248,8 @@ struct PrefillArgs {
     int32_t head_dim;
     int32_t batch;
     int32_t max_rows;         // host bound on any entry's new rows
+    int32_t skip_single;      // 1: entries with one new row are left to the decode
+    int32_t page_shift;       // log2(page_size)
     float scale_log2;         // sm_scale * log2(e)
 };
 

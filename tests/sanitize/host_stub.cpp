@@ -26,7 +26,7 @@ hipError_t launch_append(const AppendArgs &a, int batch, hipStream_t) {
     return hipSuccess;
 }
 
-bool prefill_supported(int head_dim) { return head_dim == 128; }
+bool prefill_supported(int head_dim) { return head_dim == 64 || head_dim == 128; }
 
 hipError_t launch_prefill(const PrefillArgs &a, bool append, hipStream_t) {
     if (!a.q || !a.out || (append != (a.cache_w != nullptr)) || a.max_rows < 1 ||

@@ -145,7 +145,7 @@ def _prefill(desc=CacheDesc(2, 64, 16, 2, 128), layer=0, q=FAKE, hq=4, qo=FAKE, 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(layer=2), -2), (dict(batch=-1), -2), (dict(hq=3), -2), (dict(maxr=0), -2),
-    (dict(scale=float("nan")), -2), (dict(desc=CacheDesc(2, 64, 16, 2, 64)), -3),
+    (dict(scale=float("nan")), -2), (dict(desc=CacheDesc(2, 64, 16, 2, 32)), -3),
     (dict(batch=70000), -3), (dict(q=NULL), -1), (dict(qo=NULL), -1), (dict(out=NULL), -1),
     (dict(k=NULL), -1), (dict(tables=(FAKE, NULL, FAKE)), -1),
     (dict(out=ctypes.c_void_p(0x100004)), -6), (dict(hq=0x7fffffff), -2),
