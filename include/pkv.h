@@ -103,8 +103,9 @@ int pkv_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
  *   with k_new / v_new:  cache[layer, page(p), 0/1, slot(p), :, :] = k_new[r] / v_new[r]
  *   out[r, hq, :] = sum_{t <= p} softmax_t(sm_scale * q[r, hq, :] . K_t) V_t
  *   lse[r, hq]    = ln sum_{t <= p} exp(sm_scale * q[r, hq, :] . K_t)
- * with KV head hq / (Hq / Hkv), as in pkv_decode.  The append runs before the
- * attention (two launches in stream order), so rows see each other's keys.
+ * with KV head hq / (Hq / Hkv), as in pkv_decode.  Rows see each other's keys
+ * (the attention reads the new rows from k_new / v_new and writes them into
+ * the cache in the same launch).
  *  q, out        bf16 [total rows, num_qo_heads, head_dim]; total rows =
  *                qo_indptr[batch].
  *  qo_indptr     int32 [batch + 1], non-decreasing, qo_indptr[0] == 0.
@@ -113,8 +114,9 @@ int pkv_append(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
  *  lse           fp32 [total rows, num_qo_heads], natural log, or NULL.
  *  max_q_rows    host upper bound on any n_b (>= 1); it sizes the grid.
  * Preconditions as for pkv_decode, plus n_b <= L and n_b <= max_q_rows; rows
- * past max_q_rows are not computed.  head_dim 128 only (else
- * PKV_ERR_UNSUPPORTED); batch <= 65535.  Uses matrix-core (MFMA) products.
+ * past max_q_rows are neither appended nor computed.  head_dim 64 or 128
+ * (else PKV_ERR_UNSUPPORTED); batch <= 65535.  Uses matrix-core (MFMA)
+ * products.
  */
 int pkv_prefill(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *q,
                 int32_t num_qo_heads, const int32_t *qo_indptr, const void *k_new,

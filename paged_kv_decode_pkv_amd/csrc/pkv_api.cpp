@@ -416,12 +416,14 @@ int pkv_prefill(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void
     a.head_dim = desc.head_dim;
     a.batch = batch;
     a.max_rows = max_q_rows;
+    const int64_t col_tiles = ((int64_t)max_q_rows * (num_qo_heads / desc.num_kv_heads) + 127) / 128;
+    a.pair_tiles = (int32_t)((col_tiles + 1) / 2);
     a.skip_single = 0;
     a.page_shift = 0;
     while ((1 << a.page_shift) < desc.page_size)
         ++a.page_shift;
     a.scale_log2 = sm_scale * 1.4426950408889634f;
-    return hip_status(pkv::launch_prefill(a, append, stream));
+    return hip_status(pkv::launch_prefill(a, stream));
 }
 
 }  // extern "C"

@@ -248,6 +248,8 @@ struct PrefillArgs {
     int32_t head_dim;
     int32_t batch;
     int32_t max_rows;         // host bound on any entry's new rows
+    int32_t pair_tiles;       // workgroups per (entry, KV head): ceil(T / 2) for the
+                              // T = ceil(max_rows * G / 128) column tiles
     int32_t skip_single;      // 1: entries with one new row are left to the decode
     int32_t page_shift;       // log2(page_size)
     float scale_log2;         // sm_scale * log2(e)
@@ -256,8 +258,9 @@ struct PrefillArgs {
 // True when the prefill kernels are built for head_dim.
 bool prefill_supported(int head_dim);
 
-// Enqueues the append of the new rows (when `append`), then the attention.
-hipError_t launch_prefill(const PrefillArgs &a, bool append, hipStream_t stream);
+// Enqueues the attention of the new rows, with their append when
+// a.cache_w is set.
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 // True when the fused norm/rope/write kernel is built for head_dim.
 bool norm_rope_supported(int head_dim);

@@ -13,31 +13,48 @@
 // products run on the matrix cores (v_mfma_f32_16x16x32_bf16).  The query
 // columns of an entry and KV head are its (row, query head) pairs, column
 // j G + g for row j and head g of the head group (the G heads of a row share
-// the keys and values).  A workgroup of four waves takes 128 consecutive
-// columns, 32 per wave in two blocks of 16, and walks the entry's tokens up
-// to its last column's position in tiles of 32:
-//   S^T[t][c] = sum_d K[t][d] Q[c][d]     K tile as the A operand (from LDS),
+// the keys and values), cut into column tiles of 128.  Four waves take the
+// 128 columns of a tile, 32 per wave in two blocks of 16, and walk the
+// entry's tokens up to the tile's last position in token tiles of 32:
+//   S^T[t][c] = sum_d K[t][d] Q[c][d]     K rows as the A operand (LDS),
 //                                         Q^T as the B operand (registers)
-//   O^T[d][c] += sum_t V^T[d][t] P^T[t][c] V^T from LDS, P^T from the scores
+//   O^T[d][c] += sum_t V^T[d][t] P^T[t][c] V^T as the A operand, read
+//                                         transposed from V rows in LDS
 // The MFMA gives lane l the scores of column l % 16 at tokens 4 (l / 16) + r
 // of each 16-token half of the tile, which is exactly a B operand of the
 // second product when its contraction index k = 8 (l / 16) + e names token
 // 4 (l / 16) + e (e < 4) or 16 + 4 (l / 16) + e - 4 (e >= 4) (the order of a
-// sum is free); V^T is read in the same token order.  The online softmax of
-// a column stays within its four lanes.  P goes in as a bf16 high part and a
-// bf16 remainder (two products): a single bf16 P is off by up to half a
-// bf16 step of the output, the whole parity bar.
+// sum is free).  V^T in that token order is what ds_read_b64_tr_b16 returns
+// from V rows: within each 16 lanes it hands lane i element i % 4 of the
+// 8 bytes that lane 4 e + i / 4 addressed, so four lanes addressing four
+// consecutive d of one token row give lane i four tokens of one d.  The
+// online softmax of a column stays within its four lanes.  P goes in as a
+// bf16 high part and a bf16 remainder (two products): a single bf16 P is off
+// by up to half a bf16 step of the output, the whole parity bar.
 //
-// The four waves share each tile's K rows and its V rows, transposed, in
-// LDS (two buffers: the next tile's loads are in flight while one is
-// computed).  Rows are padded so that the operand reads meet distinct banks.
-// The grid lists (entry, KV head) pairs fastest, so the heaviest tiles (the
-// last columns, the longest prefixes) of every pair start first and, with
-// 8 | batch x Hkv, all tiles of a pair run on one XCD and share its L2.
+// Balance.  Column tile j of an entry needs about j + 1 token tiles (its
+// rows' prefixes grow with j), so a workgroup of eight waves takes the pair
+// of column tiles (k, T-1-k) as two chains of four waves that walk about the
+// same number of token tiles: chain A all of tile k and then the first
+// token tiles of tile T-1-k, chain B the rest of tile T-1-k.  Chain A's wave
+// w and chain B's wave w hold the same columns of tile T-1-k, and at the end
+// B merges A's partial (running maximum, weight sum, outputs) from LDS.  The
+// middle tile of an odd T is split the same way.  Each SIMD holds one wave of
+// each chain.
+//
+// Each chain stages its token tiles through a ring of three LDS slots with
+// direct-to-LDS copies (global_load_lds_dwordx4, 1 KiB a copy), so no
+// registers hold tiles in flight; the page ids of a tile go ahead of it into
+// a slot of their own the same way.  Rows sit unpadded in LDS with their
+// 16-byte chunks permuted by an XOR of the row index, chosen so that the
+// operand reads of a wave (K rows, and the transposed V reads) meet distinct
+// banks.  New rows are read from k_new / v_new, and the workgroups of an
+// entry and KV head share writing them into the cache.
+//
+// The grid lists (entry, KV head, pair) with the pairs of one (entry, KV
+// head) adjacent, dealt so that they run on one XCD and share its L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-
-#include <type_traits>
 
 #include "pkv_launch.h"
 
@@ -45,18 +62,69 @@ namespace pkv {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr float kMaskedScore = -1e30f;   // log2-domain score of a masked token
-constexpr float kTau = 8.0f;             // lazy-rescale threshold, log2 units
-constexpr int kTileTok = 32;             // tokens per tile
-constexpr int kCols = 128;               // query columns per workgroup
-constexpr int kThreads = 256;            // four waves
-constexpr int kStagePages = 1024;        // page ids of an entry held in LDS
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr float kInitMax = -1e30f;       // running maximum before any token (log2 domain)
+constexpr float kTau = 8.0f;             // lazy-rescale threshold, log2 units
+constexpr int kTileTok = 32;             // tokens per token tile
+constexpr int kCols = 128;               // query columns per column tile
+constexpr int kWaves = 8;                // two chains of four waves
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRing = 3;                 // LDS slots per chain
+constexpr int kPageSlot = 64;            // page ids staged per token tile
+
+// LDS layout of one chain: kRing tile slots (K rows, then V rows, 2 D bytes
+// a row), then kRing page slots; the two chains side by side.  After the
+// walk the same memory holds chain A's partials.
+template <int D>
+struct Geo {
+    static constexpr int CPR = D / 8;               // 16-byte chunks per row
+    static constexpr int RPC = 64 / CPR;            // rows per 1 KiB copy
+    static constexpr int CPW = kTileTok / RPC / 4;  // copies per wave, per tensor and tile
+    static constexpr int TILE = kTileTok * 2 * D;   // bytes of K (or V) in a tile
+    static constexpr int SLOT = 2 * TILE;
+    static constexpr int PAGES = kRing * SLOT;      // first page slot
+    static constexpr int RING = PAGES + kRing * kPageSlot * 4;
+    static constexpr int LDS = 2 * RING;
+    static constexpr int DC = D / 32;               // 32-value chunks of d (first product)
+    static constexpr int DB = D / 16;               // 16-row blocks of d (second product)
+    static constexpr int MQ = 2 * DB + 1;           // 16-byte words of a lane's partial
+    static_assert(CPW >= 1 && 4 * CPW * RPC == kTileTok, "unsupported head_dim");
+    static_assert(4 * MQ * 64 * 16 <= LDS, "partials do not fit");
+};
+
+// Chunk permutations (XOR of the chunk index) of K and V rows in LDS.  K is
+// read as 16 rows x one 16-byte chunk per 16 lanes, V (transposed) as 4
+// consecutive rows x two chunks per 16 lanes and 8 rows per 32 lanes; both
+// land on 16 distinct 4-bank groups.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+    return D == 128 ? ((r << 1) & 14) : (r & 6);
+}
+
+// s_waitcnt immediate for "at most n vector memory operations outstanding"
+// (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Direct-to-LDS copies: 16 (or 4) bytes from each lane's global address to
+// LDS at lds + 16 * lane (4 * lane); lds is wave-uniform and goes through M0.
+// They are inline assembly, so the compiler does not track them: the kernel
+// waits for them itself.
+__device__ __forceinline__ void copy16_to_lds(const void *src, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void copy4_to_lds(const void *src, uint32_t lds) {
+    asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
 
 // two fp32 -> two bf16 (round to nearest even), packed low-first: one
 // v_cvt_pk_bf16_f32 on gfx950
@@ -66,7 +134,7 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo_up(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_up(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one column's
+// Maximum (sum) over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one column's
 // lanes), with the gfx950 cross-row lane swaps.
 __device__ __forceinline__ float column_max(float x) {
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -88,58 +156,21 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
 }
 
 // ---------------------------------------------------------------------------
-// Append of several rows per entry: workgroup (j, b) copies row j of entry b,
-// if it exists, into token position L - n_b + j.
-__global__ __launch_bounds__(256) void append_rows_kernel(PrefillArgs a) {
-    const int j = blockIdx.x, b = blockIdx.y;
-    const int r0 = a.qo_indptr[b];
-    const int n = a.qo_indptr[b + 1] - r0;
-    if (j >= n)
-        return;
-    const int p0 = a.indptr[b];
-    const int np = a.indptr[b + 1] - p0;
-    const int last = a.last_len[b];
-    if (np < 1 || last < 1 || last > a.page_size)
-        return;
-    const int len = (np - 1) * a.page_size + last;
-    if (n > len)
-        return;
-    const int t = len - n + j;
-    const int page = a.indices[p0 + t / a.page_size];
-    if (page < 0 || page >= a.num_pages)
-        return;
-    uint16_t *dst = a.cache_w + (int64_t)page * a.page_stride +
-                    (int64_t)(t % a.page_size) * a.row_stride;
-    const uint16_t *ks = a.k_new + (int64_t)(r0 + j) * a.row_stride;
-    const uint16_t *vs = a.v_new + (int64_t)(r0 + j) * a.row_stride;
-    const int words = a.row_stride >> 3;   // 16-byte words per row
-    for (int i = threadIdx.x; i < 2 * words; i += blockDim.x) {
-        const bool is_v = i >= words;
-        const int w = is_v ? i - words : i;
-        const uint4 val = reinterpret_cast<const uint4 *>(is_v ? vs : ks)[w];
-        reinterpret_cast<uint4 *>(dst + (is_v ? a.half_stride : 0))[w] = val;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Causal attention of the new rows; see the file comment.
+// Causal attention of the new rows (and their append); see the file comment.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
-    constexpr int DC = D / 32;                 // 32-value chunks of d (first product)
-    constexpr int DB = D / 16;                 // 16-row blocks of d (second product)
-    constexpr int KP = 2 * D + 16;             // LDS bytes per K row (padded)
-    constexpr int VP = 2 * kTileTok + 16;      // LDS bytes per V^T row (padded)
-    constexpr int CR = D / 8;                  // 16-byte chunks per K (or V) row
-    constexpr int KPT = kTileTok * CR / kThreads;   // K chunks per thread per tile
-    constexpr int VJOBS = (kTileTok / 2) * CR;       // V jobs: (token pair, chunk)
-    static_assert(KPT >= 1 && VJOBS <= kThreads, "unsupported head_dim");
-    __shared__ __attribute__((aligned(16))) char sk[2][kTileTok * KP];
-    __shared__ __attribute__((aligned(16))) char sv[2][D * VP];
-    __shared__ int s_pages[kStagePages];   // the entry's page list, when it fits
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
+    using Gm = Geo<D>;
+    constexpr int DC = Gm::DC, DB = Gm::DB, CPR = Gm::CPR, RPC = Gm::RPC, CPW = Gm::CPW;
+    constexpr int RB = 2 * D;   // bytes per row in LDS
+    __shared__ __attribute__((aligned(1024))) char smem[Gm::LDS];
 
-    const int pairs = a.batch * a.num_kv_heads;
-    const int pair = blockIdx.x % pairs;
-    const int trev = blockIdx.x / pairs;       // 0: the entry's last (heaviest) tile
+    // workgroup -> (entry, KV head, pair k): blocks congruent mod 8 share an
+    // XCD, and each XCD takes a contiguous run of the linear order
+    const int nb = gridDim.x;
+    const int xcd = blockIdx.x & 7;
+    const int lin = xcd * (nb >> 3) + min(xcd, nb & 7) + (blockIdx.x >> 3);
+    const int pair = lin / a.pair_tiles;
+    const int kk = lin - pair * a.pair_tiles;
     const int b = pair / a.num_kv_heads, h = pair - b * a.num_kv_heads;
     const int G = a.num_qo_heads / a.num_kv_heads;
 
@@ -147,179 +178,208 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int n = a.qo_indptr[b + 1] - r0;
     if (n < 1 || (n == 1 && a.skip_single))
         return;
-    const int ncols = n * G;
-    const int ntile = (ncols + kCols - 1) / kCols;
-    if (trev >= ntile)
+    const int nc = min(n, a.max_rows);   // rows computed (and appended)
+    const int ncols = nc * G;
+    const int T = (ncols + kCols - 1) / kCols;
+    if (kk >= (T + 1) / 2)
         return;
     const int p0 = a.indptr[b];
     const int np = a.indptr[b + 1] - p0;
     const int last = a.last_len[b];
-    if (np < 1 || last < 1 || last > a.page_size)
+    if (np < 1 || last < 1 || last > a.page_size ||
+        (int64_t)(np - 1) * a.page_size + last > 0x7fffff00LL)
         return;
     const int len = (np - 1) * a.page_size + last;
     if (n > len)
         return;
-    const int col0 = (ntile - 1 - trev) * kCols;
-    const int pmax = len - n + (min(ncols, col0 + kCols) - 1) / G;   // last position
+    const int base_pos = len - n;   // position of the entry's first new row
     const int32_t *pages = a.indices + p0;
 
-    const int tid = threadIdx.x;
-    const int wv = tid >> 6, l = tid & 63;
-    const int q = l >> 4, c = l & 15;
+    // the two chains: A = column tile jl over token tiles [0, nA1), then
+    // column tile jh over [0, nA2); B = column tile jh over [xB, xB + nB)
+    auto tiles_of = [&](int j) {   // token tiles column tile j walks
+        return (base_pos + (min(ncols, kCols * (j + 1)) - 1) / G) / kTileTok + 1;
+    };
+    const int jl = kk, jh = T - 1 - kk;
+    int nA1, nA2, xB, nB;
+    if (jl < jh) {
+        const int w1 = tiles_of(jl), w2 = tiles_of(jh);
+        const int x = max(0, (w1 + w2) / 2 - w1);
+        nA1 = w1; nA2 = x; xB = x; nB = w2 - x;
+    } else {   // the middle tile, halved
+        const int w = tiles_of(jl);
+        nA1 = w / 2; nA2 = 0; xB = w / 2; nB = w - w / 2;
+    }
+    // B merges A's partial when A walked part of B's column tile
+    const bool merge = jl < jh ? nA2 > 0 : nA1 > 0;
+    const int lenA = nA1 + nA2;
+    const int steps = max(lenA, nB);
 
-    // this lane's two columns (blocks cb = 0, 1 of the wave's 32)
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6, lane = tid & 63;
+    const int chain = wv >> 2, w4 = wv & 3;
+    const int q = lane >> 4, c = lane & 15;
+    const int my_len = chain ? nB : lenA;
+    char *ring = smem + chain * Gm::RING;
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+    auto tok_tile = [&](int s) { return chain ? xB + s : (s < nA1 ? s : s - nA1); };
+
+    // fold a negative scale into q (exact: a sign flip of bf16)
+    const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+    const float c2 = fabsf(a.scale_log2);
+
+    // ---- the wave's columns and running state
     int crow[2], chead[2], cpos[2];
     bool cok[2];
     bf16x8_t qb[2][DC];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        const int col = col0 + 32 * wv + 16 * cb + c;
-        cok[cb] = col < ncols;
-        crow[cb] = cok[cb] ? col / G : 0;
-        chead[cb] = cok[cb] ? h * G + col % G : 0;
-        cpos[cb] = cok[cb] ? len - n + crow[cb] : -1;
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            a.q + ((int64_t)(r0 + crow[cb]) * a.num_qo_heads + chead[cb]) * D + 8 * q);
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc)
-            qb[cb][dc] = as_bf16x8(cok[cb] ? src[4 * dc] : make_uint4(0u, 0u, 0u, 0u));
-    }
-    // smallest position among the wave's valid columns (the first column's:
-    // positions grow with the column)
-    const int wave_min_pos = len - n + min(col0 + 32 * wv, ncols - 1) / G;
     f32x4_t o[2][DB];
     float m[2], lsum[2];
+    int wmin = 0, wmax = -1;   // first and last position among the wave's valid columns
+    auto set_columns = [&](int j) {
+        const int colw = kCols * j + 32 * w4;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+        for (int cb = 0; cb < 2; ++cb) {
+            const int col = colw + 16 * cb + c;
+            cok[cb] = col < ncols;
+            crow[cb] = cok[cb] ? col / G : 0;
+            chead[cb] = cok[cb] ? h * G + col % G : 0;
+            cpos[cb] = cok[cb] ? base_pos + crow[cb] : -1;
+            const uint4 *src = reinterpret_cast<const uint4 *>(
+                a.q + ((int64_t)(r0 + crow[cb]) * a.num_qo_heads + chead[cb]) * D + 8 * q);
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc) {
+                uint4 v = cok[cb] ? src[4 * dc] : make_uint4(0u, 0u, 0u, 0u);
+                v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
+                qb[cb][dc] = as_bf16x8(v);
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                o[cb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            m[cb] = kInitMax;   // running maximum of the column (log2 domain)
+            lsum[cb] = 0.f;     // this lane's share of the column's weight sum
+        }
+        wmin = base_pos + min(colw, ncols - 1) / G;
+        wmax = colw < ncols ? base_pos + (min(ncols, colw + 32) - 1) / G : -1;
+    };
+    auto finalize = [&]() {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            // the column's weight sum over its four lanes, then the outputs
+            const float ls = column_sum(lsum[cb]);
+            if (!cok[cb])
+                continue;
+            const float inv = 1.f / ls;
+            uint16_t *orow =
+                a.out + ((int64_t)(r0 + crow[cb]) * a.num_qo_heads + chead[cb]) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                // lane holds O^T[16 db + 4 q + r][c]
+                const uint32_t w0 = bf16x2_rne(o[cb][db][0] * inv, o[cb][db][1] * inv);
+                const uint32_t w1 = bf16x2_rne(o[cb][db][2] * inv, o[cb][db][3] * inv);
+                *reinterpret_cast<uint2 *>(orow + 16 * db + 4 * q) = make_uint2(w0, w1);
+            }
+            if (a.lse != nullptr && q == 0)
+                a.lse[(int64_t)(r0 + crow[cb]) * a.num_qo_heads + chead[cb]] =
+                    (m[cb] + __log2f(ls)) * 0.6931471805599453f;
+        }
+    };
+    set_columns(chain ? jh : jl);
+
+    // ---- copies of one step's page ids and K / V rows into the ring
+    const int pmask = a.page_size - 1;   // page sizes are powers of two
+    const bool fresh = a.k_new != nullptr;
+    auto issue_pages = [&](int s) {   // wave 0 of the chain
+        if (w4 != 0)
+            return;
+        const int t0 = tok_tile(s) * kTileTok;
+        const int pi = min((t0 >> a.page_shift) + lane, np - 1);
+        copy4_to_lds(pages + pi, ring_lds + Gm::PAGES + (s % kRing) * (kPageSlot * 4));
+    };
+    auto issue_kv = [&](int s) {
+        const int t0 = tok_tile(s) * kTileTok;
+        const int slot = s % kRing;
+        const int *ps = reinterpret_cast<const int *>(ring + Gm::PAGES + slot * (kPageSlot * 4));
+        const uint32_t kdst = ring_lds + slot * Gm::SLOT;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int ci = w4 + 4 * i;                      // copy within the tile
+            const int r = RPC * ci + lane / CPR;            // row within the tile
+            const int ch = lane % CPR;                      // chunk slot in LDS
+            const int tok = min(t0 + r, len - 1);           // past the end: the last token (masked)
+            const uint16_t *kr, *vr;
+            if (fresh && tok >= base_pos) {
+                kr = a.k_new + (int64_t)(r0 + tok - base_pos) * a.row_stride + h * D;
+                vr = a.v_new + (int64_t)(r0 + tok - base_pos) * a.row_stride + h * D;
+            } else {
+                int page = ps[(tok - t0) >> a.page_shift];
+                page = (page >= 0 && page < a.num_pages) ? page : 0;   // bad table: no fault
+                kr = a.cache + (int64_t)page * a.page_stride + (int64_t)(tok & pmask) * a.row_stride +
+                     h * D;
+                vr = kr + a.half_stride;
+            }
+            copy16_to_lds(kr + 8 * (ch ^ swz_k<D>(r)), kdst + ci * 1024);
+            copy16_to_lds(vr + 8 * (ch ^ swz_v<D>(r)), kdst + Gm::TILE + ci * 1024);
+        }
+    };
+
+    // ---- lane-constant LDS read offsets
+    // K: row 16 tb + c, logical chunk 4 dc + q
+    int koff[DC];
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+        koff[dc] = c * RB + 16 * ((4 * dc + q) ^ swz_k<D>(c));
+    // V (transposed reads): row 4 q + c / 4 (+16), d = 16 db + 4 (c % 4)
+    int voff[DB];
+    {
+        const int r = 4 * q + (c >> 2);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-            o[cb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        m[cb] = kMaskedScore;   // running maximum of the column (log2 domain)
-        lsum[cb] = 0.f;         // this lane's share of the column's weight sum
+            voff[db] = r * RB + 16 * ((2 * db + ((c & 3) >> 1)) ^ swz_v<D>(r)) + 8 * (c & 1);
     }
-    const float c2 = a.scale_log2;
 
-    // Global -> register loads of one tile: K chunks tid + 256 i (row = id /
-    // CR), and V as (token pair, chunk) jobs for the transposed store.  Tokens
-    // past the entry's end read its last token again (finite; masked).
-    const uint16_t *kbase = a.cache + (int64_t)h * D;
-    // the page ids the walk needs, staged once (a tile's loads then wait for
-    // no page-table read)
-    const bool staged = np <= kStagePages;
-    if (staged)
-        for (int i = tid; i < np; i += kThreads) {
-            const int page = pages[i];
-            s_pages[i] = (page >= 0 && page < a.num_pages) ? page : 0;   // bad table: no fault
-        }
-    __syncthreads();
-    const int pmask = a.page_size - 1;   // page sizes are powers of two
-    auto row_ptr = [&](int t) {
-        t = min(t, len - 1);
-        int page;
-        if (staged) {
-            page = s_pages[t >> a.page_shift];
-        } else {
-            page = pages[t >> a.page_shift];
-            page = (page >= 0 && page < a.num_pages) ? page : 0;
-        }
-        return kbase + (int64_t)page * a.page_stride + (int64_t)(t & pmask) * a.row_stride;
-    };
-    // Two register sets of tile loads in flight: the loads of tile t are
-    // issued while tile t - 3 is computed and stored to LDS while tile t - 1
-    // is; past the last tile they read its last tokens again (unconditional,
-    // so the waits for the older set stay exact).
-    uint4 kr[2][KPT], vr[2][2];
-    auto load_tile = [&](auto setc, int t0) {
-        constexpr int S = decltype(setc)::value;
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int id = tid + kThreads * i;
-            kr[S][i] = reinterpret_cast<const uint4 *>(row_ptr(t0 + id / CR))[id % CR];
-        }
-        if (tid < VJOBS) {
-            const int tp = tid % (kTileTok / 2), ch = tid / (kTileTok / 2);
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-                vr[S][u] = reinterpret_cast<const uint4 *>(row_ptr(t0 + 2 * tp + u) +
-                                                           a.half_stride)[ch];
-        }
-    };
-    // Registers -> LDS buffer: K rows as they are; V transposed, V^T[d][t]
-    // with the token pair (2 tp, 2 tp + 1) as one 4-byte word per d.
-    auto store_tile = [&](auto setc, int buf) {
-        constexpr int S = decltype(setc)::value;
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int id = tid + kThreads * i;
-            *reinterpret_cast<uint4 *>(sk[buf] + (id / CR) * KP + (id % CR) * 16) = kr[S][i];
-        }
-        if (tid < VJOBS) {
-            const int tp = tid % (kTileTok / 2), ch = tid / (kTileTok / 2);
-            const uint32_t a0[4] = {vr[S][0].x, vr[S][0].y, vr[S][0].z, vr[S][0].w};
-            const uint32_t a1[4] = {vr[S][1].x, vr[S][1].y, vr[S][1].z, vr[S][1].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // d = 8 ch + 2 e (low halves) and 8 ch + 2 e + 1 (high halves)
-                const uint32_t lo = (a0[e] & 0xFFFFu) | (a1[e] << 16);
-                const uint32_t hi = (a0[e] >> 16) | (a1[e] & 0xFFFF0000u);
-                char *dst = sv[buf] + (8 * ch + 2 * e) * VP + 4 * tp;
-                *reinterpret_cast<uint32_t *>(dst) = lo;
-                *reinterpret_cast<uint32_t *>(dst + VP) = hi;
-            }
-        }
-    };
-
-    const int ntiles = pmax / kTileTok + 1;
-    auto tile_t0 = [&](int i) { return min(i, ntiles - 1) * kTileTok; };
-    using Set0 = std::integral_constant<int, 0>;
-    using Set1 = std::integral_constant<int, 1>;
-    auto compute_tile = [&](int it, int buf) {
-        const int t0 = it * kTileTok;
-        const char *kb = sk[buf];
-        const char *vb = sv[buf];
+    auto compute = [&](int s) {
+        const int t0 = tok_tile(s) * kTileTok;
+        if (t0 > wmax)   // no token of the tile is visible to the wave's columns
+            return;
+        const char *kb = ring + (s % kRing) * Gm::SLOT;
+        const char *vb = kb + Gm::TILE;
         // S^T blocks: tokens 16 tb + (rows of the MFMA), columns of block cb
-        f32x4_t s[2][2];
+        f32x4_t sc[2][2];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             bf16x8_t ka[DC];
 #pragma unroll
             for (int dc = 0; dc < DC; ++dc)
-                ka[dc] = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                    kb + (16 * tb + c) * KP + (32 * dc + 8 * q) * 2));
+                ka[dc] = as_bf16x8(*reinterpret_cast<const uint4 *>(kb + 16 * tb * RB + koff[dc]));
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
                 f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int dc = 0; dc < DC; ++dc)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[dc], qb[cb][dc], acc, 0, 0, 0);
-                s[tb][cb] = acc;
+                sc[tb][cb] = acc;
             }
         }
         // online softmax per column; P^T operands in the token order above.
         // Tiles wholly below every position of the wave need no mask.
-        const bool masked = t0 + kTileTok - 1 > wave_min_pos;
+        const bool masked = t0 + kTileTok - 1 > wmin;
         bf16x8_t phi[2], plo[2];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-            float x[8];
-            float tmax = kMaskedScore;
+            bool vis[8];
+            float tmax = -__builtin_inff();
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = t0 + 16 * tb + 4 * q + r;
-                    float v = s[tb][cb][r] * c2;
-                    if (masked)
-                        v = (t <= cpos[cb]) ? v : kMaskedScore;
-                    x[4 * tb + r] = v;
-                    tmax = fmaxf(tmax, v);
-                }
+            for (int e = 0; e < 8; ++e) {
+                const int t = t0 + 16 * (e >> 2) + 4 * q + (e & 3);
+                vis[e] = !masked || t <= cpos[cb];
+                tmax = fmaxf(tmax, vis[e] ? sc[e >> 2][cb][e & 3] : -__builtin_inff());
+            }
             // lazy maximum: raised (to the tile's column maximum) only when a
             // score passes it by more than kTau, so weights stay below
             // 2^kTau and most tiles rescale nothing
-            if (__builtin_amdgcn_ballot_w64(tmax > m[cb] + kTau) != 0) {
-                tmax = column_max(tmax);
-                const float mn = fmaxf(m[cb], tmax);
+            const float ts = tmax * c2;
+            if (__builtin_amdgcn_ballot_w64(ts > m[cb] + kTau) != 0) {
+                const float mn = fmaxf(m[cb], column_max(ts));
                 const float alpha = __builtin_amdgcn_exp2f(m[cb] - mn);
                 m[cb] = mn;
                 lsum[cb] *= alpha;
@@ -327,11 +387,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
                 for (int db = 0; db < DB; ++db)
                     o[cb][db] *= alpha;
             }
-            const float mn = m[cb];
+            const float nm = -m[cb];
             float pv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                pv[e] = __builtin_amdgcn_exp2f(x[e] - mn);
+                const float p = __builtin_amdgcn_exp2f(fmaf(sc[e >> 2][cb][e & 3], c2, nm));
+                pv[e] = vis[e] ? p : 0.f;
                 lsum[cb] += pv[e];
             }
             uint32_t hw[4], lw[4];
@@ -344,14 +405,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
             phi[cb] = __builtin_bit_cast(bf16x8_t, u32x4_t{hw[0], hw[1], hw[2], hw[3]});
             plo[cb] = __builtin_bit_cast(bf16x8_t, u32x4_t{lw[0], lw[1], lw[2], lw[3]});
         }
-        // O^T += V^T P^T: lane reads V^T[16 db + c] at tokens 4 q .. 4 q + 3
-        // and 16 + 4 q .. 16 + 4 q + 3
+        // O^T += V^T P^T: lane gets V^T[16 db + c] at tokens 4 q .. 4 q + 3 and
+        // 16 + 4 q .. 16 + 4 q + 3
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const char *row = vb + (16 * db + c) * VP + 8 * q;
-            const uint2 v0 = *reinterpret_cast<const uint2 *>(row);
-            const uint2 v1 = *reinterpret_cast<const uint2 *>(row + 32);
-            const bf16x8_t va = __builtin_bit_cast(bf16x8_t, u32x4_t{v0.x, v0.y, v1.x, v1.y});
+            const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t *)(vb + voff[db]));
+            const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t *)(vb + voff[db] + 16 * RB));
+            const bf16x8_t va = __builtin_bit_cast(
+                bf16x8_t, u32x4_t{__builtin_bit_cast(uint2, v0).x, __builtin_bit_cast(uint2, v0).y,
+                                  __builtin_bit_cast(uint2, v1).x, __builtin_bit_cast(uint2, v1).y});
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
                 o[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[cb], o[cb][db], 0, 0, 0);
@@ -359,73 +423,133 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
             }
         }
     };
-    load_tile(Set0{}, 0);
-    store_tile(Set0{}, 0);
+
+    // ---- the walk.  Per step s, in this order: wait for the step's rows (and
+    // the page ids two steps ahead), barrier, issue the page ids of step s + 3
+    // and the rows of step s + 2, compute step s.  Waves of both chains meet
+    // at every barrier.
+    if (0 < my_len)
+        issue_pages(0);
+    if (1 < my_len)
+        issue_pages(1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    load_tile(Set1{}, tile_t0(1));
-    load_tile(Set0{}, tile_t0(2));
-    for (int it = 0; it < ntiles; it += 2) {
-        // even tile from buffer 0; tile it + 1 (set 1) to buffer 1, then set 1
-        // fetches tile it + 3
-        compute_tile(it, 0);
-        if (it + 1 >= ntiles)
-            break;
-        store_tile(Set1{}, 1);
-        __syncthreads();
-        load_tile(Set1{}, tile_t0(it + 3));
-        // odd tile from buffer 1; tile it + 2 (set 0) to buffer 0, set 0
-        // fetches tile it + 4
-        compute_tile(it + 1, 1);
-        if (it + 2 >= ntiles)
-            break;
-        store_tile(Set0{}, 0);
-        __syncthreads();
-        load_tile(Set0{}, tile_t0(it + 4));
+    if (0 < my_len)
+        issue_kv(0);
+    if (2 < my_len)
+        issue_pages(2);
+    if (1 < my_len)
+        issue_kv(1);
+
+    // the append: this workgroup's share of the (entry, KV head)'s new rows,
+    // four 16-byte chunks per thread in flight
+    if (a.cache_w != nullptr) {
+        const int share = (T + 1) / 2;
+        const int j0 = (int)((int64_t)nc * kk / share), j1 = (int)((int64_t)nc * (kk + 1) / share);
+        const int jobs = (j1 - j0) * 2 * CPR;
+        // job -> source and destination (null: no job, or a bad page id);
+        // past the last job the source is the last job's (a plain load)
+        auto job_ptrs = [&](int job, const uint4 *&src, uint4 *&dst) {
+            const bool live = job < jobs;
+            job = min(job, jobs - 1);
+            const int row = j0 + job / (2 * CPR);
+            const int is_v = (job / CPR) & 1, ch = job % CPR;
+            const int tok = base_pos + row;
+            const int page = pages[tok >> a.page_shift];
+            src = reinterpret_cast<const uint4 *>((is_v ? a.v_new : a.k_new) +
+                                                  (int64_t)(r0 + row) * a.row_stride + h * D) + ch;
+            dst = nullptr;
+            if (live && page >= 0 && page < a.num_pages)
+                dst = reinterpret_cast<uint4 *>(a.cache_w + (int64_t)page * a.page_stride +
+                                                (is_v ? a.half_stride : 0) +
+                                                (int64_t)(tok & pmask) * a.row_stride + h * D) + ch;
+        };
+        for (int i0 = tid; i0 < jobs; i0 += 4 * kThreads) {
+            const uint4 *s0, *s1, *s2, *s3;
+            uint4 *d0, *d1, *d2, *d3;
+            job_ptrs(i0, s0, d0);
+            job_ptrs(i0 + kThreads, s1, d1);
+            job_ptrs(i0 + 2 * kThreads, s2, d2);
+            job_ptrs(i0 + 3 * kThreads, s3, d3);
+            const uint4 v0 = *s0, v1 = *s1, v2 = *s2, v3 = *s3;
+            if (d0)
+                *d0 = v0;
+            if (d1)
+                *d1 = v1;
+            if (d2)
+                *d2 = v2;
+            if (d3)
+                *d3 = v3;
+        }
     }
 
+    for (int s = 0; s < steps; ++s) {
+        if (s + 1 < my_len)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CPW));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        if (s >= my_len)
+            continue;
+        if (s + 3 < my_len)
+            issue_pages(s + 3);
+        if (s + 2 < my_len)
+            issue_kv(s + 2);
+        if (chain == 0 && s == nA1 && nA2 > 0) {
+            // chain A moves from its own column tile to the pair's other one
+            finalize();
+            set_columns(jh);
+        }
+        compute(s);
+    }
+    __syncthreads();
+
+    if (!merge) {
+        if (my_len > 0)
+            finalize();
+        return;
+    }
+    // chain A's partials through LDS, lane for lane: o, then (m, lsum)
+    f32x4_t *part = reinterpret_cast<f32x4_t *>(smem) + w4 * Gm::MQ * 64 + lane;
+    if (chain == 0) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                part[(cb * DB + db) * 64] = o[cb][db];
+        part[2 * DB * 64] = f32x4_t{m[0], m[1], lsum[0], lsum[1]};
+    }
+    __syncthreads();
+    if (chain == 0)
+        return;
+    const f32x4_t ml = part[2 * DB * 64];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-        // the column's weight sum over its four lanes, then the outputs
-        const float ls = column_sum(lsum[cb]);
-        if (!cok[cb])
-            continue;
-        const float inv = 1.f / ls;
-        uint16_t *orow = a.out + ((int64_t)(r0 + crow[cb]) * a.num_qo_heads + chead[cb]) * D;
+        const float ma = ml[cb], la = ml[2 + cb];
+        const float mn = fmaxf(ma, m[cb]);
+        const float sa = __builtin_amdgcn_exp2f(ma - mn), sb = __builtin_amdgcn_exp2f(m[cb] - mn);
+        m[cb] = mn;
+        lsum[cb] = la * sa + lsum[cb] * sb;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            // lane holds O^T[16 db + 4 q + r][c]
-            const uint32_t w0 = bf16x2_rne(o[cb][db][0] * inv, o[cb][db][1] * inv);
-            const uint32_t w1 = bf16x2_rne(o[cb][db][2] * inv, o[cb][db][3] * inv);
-            *reinterpret_cast<uint2 *>(orow + 16 * db + 4 * q) = make_uint2(w0, w1);
-        }
-        if (a.lse != nullptr && q == 0)
-            a.lse[(int64_t)(r0 + crow[cb]) * a.num_qo_heads + chead[cb]] =
-                (m[cb] + __log2f(ls)) * 0.6931471805599453f;
+        for (int db = 0; db < DB; ++db)
+            o[cb][db] = part[(cb * DB + db) * 64] * sa + o[cb][db] * sb;
     }
+    finalize();
 }
 
 }  // namespace
 
 bool prefill_supported(int head_dim) { return head_dim == 64 || head_dim == 128; }
 
-hipError_t launch_prefill(const PrefillArgs &a, bool append, hipStream_t stream) {
-    PrefillArgs args = a;
-    void *params[] = {&args};
-    if (!prefill_supported(a.head_dim) || a.batch > 65535 || a.num_kv_heads > 65535)
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
+    if (!prefill_supported(a.head_dim) || a.batch > 65535 || a.num_kv_heads > 65535 ||
+        a.pair_tiles < 1)
         return hipErrorInvalidValue;
-    hipError_t err = hipSuccess;
-    if (append) {
-        err = hipLaunchKernel(reinterpret_cast<const void *>(&append_rows_kernel),
-                              dim3((unsigned)a.max_rows, (unsigned)a.batch), dim3(256), params,
-                              0, stream);
-        if (err != hipSuccess)
-            return err;
-    }
-    const int G = a.num_qo_heads / a.num_kv_heads;
-    const int64_t tiles = ((int64_t)a.max_rows * G + kCols - 1) / kCols;
-    const int64_t blocks = tiles * a.batch * a.num_kv_heads;
+    const int64_t blocks = (int64_t)a.pair_tiles * a.batch * a.num_kv_heads;
     if (blocks > 0x7fffffffLL)
         return hipErrorInvalidValue;
+    PrefillArgs args = a;
+    void *params[] = {&args};
     const void *k = a.head_dim == 128 ? reinterpret_cast<const void *>(&prefill_kernel<128>)
                                       : reinterpret_cast<const void *>(&prefill_kernel<64>);
     return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(kThreads), params, 0, stream);

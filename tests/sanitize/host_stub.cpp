@@ -28,9 +28,10 @@ hipError_t launch_append(const AppendArgs &a, int batch, hipStream_t) {
 
 bool prefill_supported(int head_dim) { return head_dim == 64 || head_dim == 128; }
 
-hipError_t launch_prefill(const PrefillArgs &a, bool append, hipStream_t) {
-    if (!a.q || !a.out || (append != (a.cache_w != nullptr)) || a.max_rows < 1 ||
-        a.num_qo_heads % a.num_kv_heads != 0 || a.row_stride != a.num_kv_heads * a.head_dim)
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t) {
+    if (!a.q || !a.out || ((a.k_new != nullptr) != (a.cache_w != nullptr)) || a.max_rows < 1 ||
+        a.pair_tiles < 1 || a.num_qo_heads % a.num_kv_heads != 0 ||
+        a.row_stride != a.num_kv_heads * a.head_dim)
         return hipErrorInvalidValue;
     return hipSuccess;
 }

@@ -48,25 +48,26 @@ def check_rows(out, lse, ref_out, ref_lse, what):
     return stats
 
 
-def _case(seed, hq, hkv, ps, lengths, nrows, sigma=1.0):
+def _case(seed, hq, hkv, ps, lengths, nrows, sigma=1.0, d=D):
     rng = np.random.default_rng(seed)
     lengths = np.asarray(lengths)
     table = table_from_lengths(lengths, np.ones(len(lengths), bool), ps, None, rng)
-    cache = bf16_bits((rng.standard_normal((2, table.num_pages, 2, ps, hkv, D),
+    cache = bf16_bits((rng.standard_normal((2, table.num_pages, 2, ps, hkv, d),
                                            dtype=np.float32) * sigma))
     qo = np.concatenate([[0], np.cumsum(nrows)]).astype(np.int32)
     rows = int(qo[-1])
-    q = bf16_bits(rng.standard_normal((rows, hq, D), dtype=np.float32) * sigma)
-    kn = bf16_bits(rng.standard_normal((rows, hkv, D), dtype=np.float32) * sigma)
-    vn = bf16_bits(rng.standard_normal((rows, hkv, D), dtype=np.float32) * sigma)
+    q = bf16_bits(rng.standard_normal((rows, hq, d), dtype=np.float32) * sigma)
+    kn = bf16_bits(rng.standard_normal((rows, hkv, d), dtype=np.float32) * sigma)
+    vn = bf16_bits(rng.standard_normal((rows, hkv, d), dtype=np.float32) * sigma)
     return table, cache, qo, q, kn, vn
 
 
-def _run(table, cache, qo, q, kn, vn, scale, append=True, layer=1):
+def _run(table, cache, qo, q, kn, vn, scale, append=True, layer=1, maxr=None):
     cache_dev = to_dev_u16(cache)
     tabs = table_to_dev(table)
     qo_dev = torch.from_numpy(qo).to(DEV)
-    maxr = int(np.max(np.diff(qo))) if len(qo) > 1 else 1
+    if maxr is None:
+        maxr = int(np.max(np.diff(qo))) if len(qo) > 1 else 1
     out, lse = pkv.prefill(cache_dev, layer, to_dev_u16(q), qo_dev, *tabs, scale,
                            max(maxr, 1), k_new=to_dev_u16(kn) if append else None,
                            v_new=to_dev_u16(vn) if append else None)
@@ -88,15 +89,25 @@ CASES = [
     (4, 16, 2, 128, [700, 129, 1000], [45, 2, 1]),                          # G 8, 128-token pages
     (5, 24, 8, 16, [17, 16, 15, 33], [17, 1, 15, 32]),                      # G 3, ragged tiles
     (6, 32, 8, 16, [1, 1, 1, 1, 1], [1, 1, 1, 1, 1]),                       # one token each
+    # column tiles of 128 (row, head) pairs, taken in pairs (k, T-1-k) by two
+    # chains of waves that split the longer tile's tokens and merge
+    (7, 16, 4, 16, [512, 200], [512, 150]),                                 # T 16 and 5
+    (8, 4, 4, 16, [400, 390], [300, 129]),                                  # G 1: T 3 (middle
+                                                                            # tile halved), 2
+    (9, 64, 8, 16, [2100, 40], [100, 40]),                                  # G 8, long prefix
+    (10, 8, 2, 1, [2500, 70], [96, 70]),                                    # one-token pages,
+                                                                            # 80 pages a walk
+    (11, 32, 8, 64, [1100, 5, 333], [700, 5, 1]),                           # 64-token pages
 ]
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("case", CASES, ids=[f"c{c[0]}" for c in CASES])
-def test_prefill_matches_oracle(case):
+def test_prefill_matches_oracle(case, d):
     seed, hq, hkv, ps, lengths, nrows = case
-    print(f"prefill case {case}", flush=True)
-    table, cache, qo, q, kn, vn = _case(seed, hq, hkv, ps, lengths, nrows)
-    scale = 1.0 / np.sqrt(D)
+    print(f"prefill case {case} head_dim {d}", flush=True)
+    table, cache, qo, q, kn, vn = _case(seed, hq, hkv, ps, lengths, nrows, d=d)
+    scale = 1.0 / np.sqrt(d)
     cache_dev, out, lse, host, ro, rl = _run(table, cache, qo, q, kn, vn, scale)
     np.testing.assert_array_equal(to_host_u16(cache_dev), host, err_msg="append")
     if qo[-1]:
@@ -132,3 +143,34 @@ def test_prefill_large_scores():
     table, cache, qo, q, kn, vn = _case(13, 16, 4, 16, [200, 48], [80, 48], sigma=4.0)
     cache_dev, out, lse, host, ro, rl = _run(table, cache, qo, q, kn, vn, 1.0 / np.sqrt(D))
     check_rows(out, lse, ro, rl, what="large scores")
+
+
+def test_prefill_negative_and_zero_scale():
+    # a negative scale flips every score (folded into q as a sign flip); a
+    # zero scale weighs every visible token alike
+    for scale in (-0.07, 0.0):
+        table, cache, qo, q, kn, vn = _case(14, 16, 4, 16, [260, 37], [200, 30])
+        cache_dev, out, lse, host, ro, rl = _run(table, cache, qo, q, kn, vn, scale)
+        check_rows(out, lse, ro, rl, what=f"scale {scale}")
+
+
+def test_prefill_rows_past_max_rows():
+    # rows past max_q_rows are neither appended nor computed: the cache holds
+    # the appended rows of the first 130 rows of each entry and the old
+    # values at the positions of the others
+    maxr = 130
+    table, cache, qo, q, kn, vn = _case(15, 16, 4, 16, [300, 90], [260, 90])
+    cache_dev, out, lse, full, ro, rl = _run(table, cache, qo, q, kn, vn, 0.1, maxr=maxr)
+    keep = np.concatenate([np.arange(0, maxr), np.arange(260, 350)])
+    got_out = bf16_to_f32(to_host_u16(out)).astype(np.float64)[keep]
+    got_lse = lse.detach().cpu().numpy().astype(np.float64)[keep]
+    stats = prefill_parity(got_out, ro[keep], got_lse, rl[keep])
+    assert stats["pass"], stats
+    want = cache.copy()
+    lengths = np.array([300, 90])
+    for e, n in enumerate([260, 90]):
+        for j in range(min(n, maxr)):
+            pos = lengths[e] - n + j
+            page = table.indices[table.indptr[e] + pos // 16]
+            want[1, page, :, pos % 16] = full[1, page, :, pos % 16]
+    np.testing.assert_array_equal(to_host_u16(cache_dev), want)
