@@ -56,6 +56,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -76,11 +78,10 @@ constexpr int kCols = 128;               // query columns per column tile
 constexpr int kWaves = 8;                // two chains of four waves
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRing = 3;                 // LDS slots per chain
-constexpr int kPageSlot = 64;            // page ids staged per token tile
 
-// LDS layout of one chain: kRing tile slots (K rows, then V rows, 2 D bytes
-// a row), then kRing page slots; the two chains side by side.  After the
-// walk the same memory holds chain A's partials.
+// LDS layout: per chain kRing tile slots (K rows, then V rows, 2 D bytes a
+// row), the two chains side by side, then the q rows of chain A's second
+// column tile.  After the walk the same memory holds chain A's partials.
 template <int D>
 struct Geo {
     static constexpr int CPR = D / 8;               // 16-byte chunks per row
@@ -88,9 +89,9 @@ struct Geo {
     static constexpr int CPW = kTileTok / RPC / 4;  // copies per wave, per tensor and tile
     static constexpr int TILE = kTileTok * 2 * D;   // bytes of K (or V) in a tile
     static constexpr int SLOT = 2 * TILE;
-    static constexpr int PAGES = kRing * SLOT;      // first page slot
-    static constexpr int RING = PAGES + kRing * kPageSlot * 4;
-    static constexpr int LDS = 2 * RING;
+    static constexpr int RING = kRing * SLOT;
+    static constexpr int QA = 4 * 32 * 2 * D;        // chain A's second q tile
+    static constexpr int LDS = 2 * RING + QA;
     static constexpr int DC = D / 32;               // 32-value chunks of d (first product)
     static constexpr int DB = D / 16;               // 16-row blocks of d (second product)
     static constexpr int MQ = 2 * DB + 1;           // 16-byte words of a lane's partial
@@ -122,8 +123,28 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4
 __device__ __forceinline__ void copy16_to_lds(const void *src, uint32_t lds) {
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
-__device__ __forceinline__ void copy4_to_lds(const void *src, uint32_t lds) {
-    asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+// The same from a wave-uniform base plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void copy16_to_lds_s(const void *base, uint32_t off, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+// A 16-byte store to a wave-uniform base plus a per-lane byte offset.
+__device__ __forceinline__ void store16_s(void *base, uint32_t off, uint4 v) {
+    const u32x4_t d = {v.x, v.y, v.z, v.w};
+    asm volatile("global_store_dwordx4 %0, %1, %2" ::"v"(off), "v"(d), "s"(base) : "memory");
+}
+
+// s_waitcnt vmcnt(min(n, N)) for a wave-uniform n >= 0 (the count is an
+// immediate: a chain of scalar compares picks it).
+template <int N>
+__device__ __forceinline__ void wait_vm_at_most(int n) {
+    if constexpr (N == 0) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    } else {
+        if (n >= N)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+        else
+            wait_vm_at_most<N - 1>(n);
+    }
 }
 
 // two fp32 -> two bf16 (round to nearest even), packed low-first: one
@@ -216,7 +237,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     const int steps = max(lenA, nB);
 
     const int tid = threadIdx.x;
-    const int wv = tid >> 6, lane = tid & 63;
+    // wave-uniform by construction; readfirstlane lets the compiler know it,
+    // so the walk's branches (and its waits) stay scalar
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int chain = wv >> 2, w4 = wv & 3;
     const int q = lane >> 4, c = lane & 15;
     const int my_len = chain ? nB : lenA;
@@ -229,37 +252,40 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     const float c2 = fabsf(a.scale_log2);
 
     // ---- the wave's columns and running state
-    int crow[2], chead[2], cpos[2];
+    int cpos[2];
+    int cur_j = 0;   // the wave's column tile
     bool cok[2];
     bf16x8_t qb[2][DC];
     f32x4_t o[2][DB];
     float m[2], lsum[2];
     int wmin = 0, wmax = -1;   // first and last position among the wave's valid columns
-    auto set_columns = [&](int j) {
+    // column c of the wave's 32 in column tile j -> its row, head and q row
+    auto column_of = [&](int j, int cw, int &row, int &head) {
+        const int col = min(kCols * j + 32 * w4 + cw, ncols - 1);
+        row = col / G;
+        head = h * G + col % G;
+    };
+    auto set_geometry = [&](int j) {
         const int colw = kCols * j + 32 * w4;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-            const int col = colw + 16 * cb + c;
-            cok[cb] = col < ncols;
-            crow[cb] = cok[cb] ? col / G : 0;
-            chead[cb] = cok[cb] ? h * G + col % G : 0;
-            cpos[cb] = cok[cb] ? base_pos + crow[cb] : -1;
-            const uint4 *src = reinterpret_cast<const uint4 *>(
-                a.q + ((int64_t)(r0 + crow[cb]) * a.num_qo_heads + chead[cb]) * D + 8 * q);
-#pragma unroll
-            for (int dc = 0; dc < DC; ++dc) {
-                uint4 v = cok[cb] ? src[4 * dc] : make_uint4(0u, 0u, 0u, 0u);
-                v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
-                qb[cb][dc] = as_bf16x8(v);
-            }
+            cok[cb] = colw + 16 * cb + c < ncols;
+            int row, head;
+            column_of(j, 16 * cb + c, row, head);
+            cpos[cb] = cok[cb] ? base_pos + row : -1;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
                 o[cb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             m[cb] = kInitMax;   // running maximum of the column (log2 domain)
             lsum[cb] = 0.f;     // this lane's share of the column's weight sum
         }
+        cur_j = j;
         wmin = base_pos + min(colw, ncols - 1) / G;
         wmax = colw < ncols ? base_pos + (min(ncols, colw + 32) - 1) / G : -1;
+    };
+    auto flip = [&](uint4 v) {
+        v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
+        return as_bf16x8(v);
     };
     auto finalize = [&]() {
 #pragma unroll
@@ -269,8 +295,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             if (!cok[cb])
                 continue;
             const float inv = 1.f / ls;
-            uint16_t *orow =
-                a.out + ((int64_t)(r0 + crow[cb]) * a.num_qo_heads + chead[cb]) * D;
+            int row, head;
+            column_of(cur_j, 16 * cb + c, row, head);
+            const int64_t orow_i = (int64_t)(r0 + row) * a.num_qo_heads + head;
+            uint16_t *orow = a.out + orow_i * D;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 // lane holds O^T[16 db + 4 q + r][c]
@@ -279,78 +307,204 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 *reinterpret_cast<uint2 *>(orow + 16 * db + 4 * q) = make_uint2(w0, w1);
             }
             if (a.lse != nullptr && q == 0)
-                a.lse[(int64_t)(r0 + crow[cb]) * a.num_qo_heads + chead[cb]] =
+                a.lse[orow_i] =
                     (m[cb] + __log2f(ls)) * 0.6931471805599453f;
         }
     };
-    set_columns(chain ? jh : jl);
 
-    // ---- copies of one step's page ids and K / V rows into the ring
-    const int pmask = a.page_size - 1;   // page sizes are powers of two
-    const bool fresh = a.k_new != nullptr;
-    auto issue_pages = [&](int s) {   // wave 0 of the chain
-        if (w4 != 0)
-            return;
-        const int t0 = tok_tile(s) * kTileTok;
-        const int pi = min((t0 >> a.page_shift) + lane, np - 1);
-        copy4_to_lds(pages + pi, ring_lds + Gm::PAGES + (s % kRing) * (kPageSlot * 4));
-    };
-    auto issue_kv = [&](int s) {
-        const int t0 = tok_tile(s) * kTileTok;
-        const int slot = s % kRing;
-        const int *ps = reinterpret_cast<const int *>(ring + Gm::PAGES + slot * (kPageSlot * 4));
-        const uint32_t kdst = ring_lds + slot * Gm::SLOT;
-#pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-            const int ci = w4 + 4 * i;                      // copy within the tile
-            const int r = RPC * ci + lane / CPR;            // row within the tile
-            const int ch = lane % CPR;                      // chunk slot in LDS
-            const int tok = min(t0 + r, len - 1);           // past the end: the last token (masked)
-            const uint16_t *kr, *vr;
-            if (fresh && tok >= base_pos) {
-                kr = a.k_new + (int64_t)(r0 + tok - base_pos) * a.row_stride + h * D;
-                vr = a.v_new + (int64_t)(r0 + tok - base_pos) * a.row_stride + h * D;
-            } else {
-                int page = ps[(tok - t0) >> a.page_shift];
-                page = (page >= 0 && page < a.num_pages) ? page : 0;   // bad table: no fault
-                kr = a.cache + (int64_t)page * a.page_stride + (int64_t)(tok & pmask) * a.row_stride +
-                     h * D;
-                vr = kr + a.half_stride;
-            }
-            copy16_to_lds(kr + 8 * (ch ^ swz_k<D>(r)), kdst + ci * 1024);
-            copy16_to_lds(vr + 8 * (ch ^ swz_v<D>(r)), kdst + Gm::TILE + ci * 1024);
-        }
-    };
-
-    // ---- lane-constant LDS read offsets
-    // K: row 16 tb + c, logical chunk 4 dc + q
-    int koff[DC];
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc)
-        koff[dc] = c * RB + 16 * ((4 * dc + q) ^ swz_k<D>(c));
+    // ---- LDS read offsets within a slot, as a lane base and an XOR term (the
+    // chunk permutation commutes with the chunk's place: 4 dc + q = 4 dc | q
+    // and 2 db + hb = 2 db | hb, and the permutations of K and V keep those
+    // low bits apart), so that each offset costs one xor-add
+    // K: row 16 tb + c, logical chunk 4 dc + q (also the q rows of chain A's
+    // second column tile, one row per column)
+    const int kbase = c * RB;
+    const int kx = 16 * (q ^ swz_k<D>(c));
+    auto koff = [&](int dc) { return (kx ^ (64 * dc)) + kbase; };
     // V (transposed reads): row 4 q + c / 4 (+16), d = 16 db + 4 (c % 4)
-    int voff[DB];
+    const int vr_ = 4 * q + (c >> 2);
+    const int vbase = vr_ * RB + 16 * ((c & 3) >> 1) + 8 * (c & 1);
+    const int vx = 16 * swz_v<D>(vr_);   // even chunk permutation: keeps bit 0 (hb)
+    auto voff = [&](int db) { return (vx ^ (32 * db)) + vbase; };
+
+    // the first column tile's q rows, straight from global memory
     {
-        const int r = 4 * q + (c >> 2);
+        const int j = chain ? jh : jl;
+        set_geometry(j);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-            voff[db] = r * RB + 16 * ((2 * db + ((c & 3) >> 1)) ^ swz_v<D>(r)) + 8 * (c & 1);
+        for (int cb = 0; cb < 2; ++cb) {
+            int row, head;
+            column_of(j, 16 * cb + c, row, head);
+            const uint4 *src = reinterpret_cast<const uint4 *>(
+                a.q + ((int64_t)(r0 + row) * a.num_qo_heads + head) * D + 8 * q);
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc)
+                qb[cb][dc] = flip(src[4 * dc]);
+        }
     }
 
-    auto compute = [&](int s) {
+    // ---- copies.  Copy i of a wave moves rows RPC (w4 + 4 i) .. + RPC - 1 of
+    // a token tile; lane l holds row + l / CPR, LDS chunk l % CPR, which is
+    // logical chunk (l % CPR) ^ swz(row) of the source row.
+    const int pmask = a.page_size - 1;   // page sizes are powers of two
+    const bool fresh = a.k_new != nullptr;
+    const bool big_pages = a.page_size >= RPC;   // a copy's rows share a page
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    static_assert(kRing == 3, "the walk is unrolled by three");
+    const int rr = lane / CPR;   // row within a copy
+    // source chunk offsets (elements) of K and V of copy i
+    auto kel = [&](int i) { return 8 * ((lane % CPR) ^ swz_k<D>(RPC * (w4 + 4 * i) + rr)); };
+    auto vel = [&](int i) { return 8 * ((lane % CPR) ^ swz_v<D>(RPC * (w4 + 4 * i) + rr)); };
+    uint32_t kvo[CPW], vvo[CPW]; // the same plus the row, in bytes from the copy's first row
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        kvo[i] = 2u * (uint32_t)(rr * a.row_stride + kel(i));
+        vvo[i] = 2u * (uint32_t)(rr * a.row_stride + vel(i));
+    }
+    // new rows come from k_new / v_new: row r0 + tok - base_pos
+    const uint16_t *knew_b = fresh ? a.k_new + ((int64_t)r0 - base_pos) * a.row_stride + h * D
+                                   : a.cache;
+    const int64_t vnew_d = fresh ? (a.v_new - a.k_new) : 0;   // v_new row - k_new row
+    const uint16_t *cache_h = a.cache + h * D;
+    typedef __attribute__((address_space(4))) const int32_t const_i32;
+    const const_i32 *pages_s = (const const_i32 *)(pages);   // scalar loads
+    // page id of each copy's first row, per ring slot (scalar registers)
+    int pgr[kRing][CPW];
+    auto load_pages = [&](auto slotc, int s) {
+        constexpr int SL = decltype(slotc)::value;
         const int t0 = tok_tile(s) * kTileTok;
-        if (t0 > wmax)   // no token of the tile is visible to the wave's columns
-            return;
-        const char *kb = ring + (s % kRing) * Gm::SLOT;
-        const char *vb = kb + Gm::TILE;
-        // S^T blocks: tokens 16 tb + (rows of the MFMA), columns of block cb
-        f32x4_t sc[2][2];
+#pragma unroll
+        for (int i = 0; i < CPW; ++i)
+            pgr[SL][i] = pages_s[min(t0 + RPC * (w4 + 4 * i), len - 1) >> a.page_shift];
+    };
+    auto page_base = [&](int page, int tok0) {   // first element of token tok0's row (head h)
+        const int pg = (uint32_t)page < (uint32_t)a.num_pages ? page : 0;   // bad id: no fault
+        return (int64_t)pg * a.page_stride + (int64_t)(tok0 & pmask) * a.row_stride + h * D;
+    };
+    auto issue_kv = [&](auto slotc, int s) {
+        constexpr int SL = decltype(slotc)::value;
+        const int t0 = tok_tile(s) * kTileTok;
+        const uint32_t kdst = ring_lds + SL * Gm::SLOT;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int tok0 = t0 + RPC * (w4 + 4 * i);
+            const uint32_t lk = kdst + (w4 + 4 * i) * 1024, lv = lk + Gm::TILE;
+            if (big_pages && tok0 + RPC <= len &&
+                (!fresh || tok0 >= base_pos || tok0 + RPC <= base_pos)) {
+                // one page (or k_new run) for the whole copy: scalar base
+                const uint16_t *bk;
+                int64_t vd;
+                if (fresh && tok0 >= base_pos) {
+                    bk = knew_b + (int64_t)tok0 * a.row_stride;
+                    vd = vnew_d;
+                } else {
+                    bk = a.cache + page_base(pgr[SL][i], tok0);
+                    vd = a.half_stride;
+                }
+                copy16_to_lds_s(bk, kvo[i], lk);
+                copy16_to_lds_s(bk + vd, vvo[i], lv);
+            } else {
+                // rows over a page, prefix or entry boundary: per lane, past
+                // the end the last token again (masked)
+                const int tok = min(tok0 + rr, len - 1);
+                const uint16_t *kr;
+                int64_t vd;
+                if (fresh && tok >= base_pos) {
+                    kr = knew_b + (int64_t)tok * a.row_stride;
+                    vd = vnew_d;
+                } else {
+                    kr = a.cache + page_base(pages[tok >> a.page_shift], tok);
+                    vd = a.half_stride;
+                }
+                copy16_to_lds(kr + kel(i), lk);
+                copy16_to_lds(kr + vd + vel(i), lv);
+            }
+        }
+    };
+    // The append: the first workgroup of the (entry, KV head) writes every
+    // new row it copied (chain B its walk, chain A the steps on column tile
+    // jh), from LDS, once the tile has landed.  Returns the number of vector
+    // stores issued for certain (per-lane stores are not counted: a count too
+    // low only makes the next wait longer).
+    const bool writer = a.cache_w != nullptr && kk == 0;
+    auto append_tile = [&](auto slotc, int s) {
+        constexpr int SL = decltype(slotc)::value;
+        int nst = 0;
+        const int t0 = tok_tile(s) * kTileTok;
+        const char *kslot = ring + SL * Gm::SLOT;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int tok0 = t0 + RPC * (w4 + 4 * i);
+            if (tok0 + RPC <= base_pos || tok0 >= base_pos + nc)
+                continue;   // no new row in this copy
+            const uint4 vk = *reinterpret_cast<const uint4 *>(kslot + (w4 + 4 * i) * 1024 + 16 * lane);
+            const uint4 vv =
+                *reinterpret_cast<const uint4 *>(kslot + Gm::TILE + (w4 + 4 * i) * 1024 + 16 * lane);
+            if (big_pages && tok0 >= base_pos && tok0 + RPC <= base_pos + nc) {
+                uint16_t *bk = a.cache_w + page_base(pgr[SL][i], tok0);
+                store16_s(bk, kvo[i], vk);
+                store16_s(bk + a.half_stride, vvo[i], vv);
+                nst += 2;
+            } else {
+                const int tok = tok0 + rr;
+                if (tok >= base_pos && tok < base_pos + nc) {
+                    const int page = pages[tok >> a.page_shift];
+                    if ((uint32_t)page < (uint32_t)a.num_pages) {
+                        uint16_t *bk = a.cache_w + page_base(page, tok);
+                        *reinterpret_cast<uint4 *>(bk + kel(i)) = vk;
+                        *reinterpret_cast<uint4 *>(bk + a.half_stride + vel(i)) = vv;
+                    }
+                }
+            }
+        }
+        return nst;
+    };
+
+    // chain A's second column tile: its q rows through LDS (copied now, read
+    // at the switch), rows swizzled like K
+    char *qa_lds = smem + 2 * Gm::RING + w4 * (32 * RB);
+    const bool a_switch = chain == 0 && nA2 > 0;
+    if (a_switch) {
+#pragma unroll
+        for (int j = 0; j < 32 / RPC; ++j) {
+            const int r = RPC * j + rr;
+            int row, head;
+            column_of(jh, r, row, head);
+            copy16_to_lds(a.q + ((int64_t)(r0 + row) * a.num_qo_heads + head) * D +
+                              8 * ((lane % CPR) ^ swz_k<D>(r)),
+                          (uint32_t)(uintptr_t)qa_lds + j * 1024);
+        }
+    }
+    auto switch_columns = [&]() {
+        set_geometry(jh);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int dc = 0; dc < DC; ++dc)
+                qb[cb][dc] =
+                    flip(*reinterpret_cast<const uint4 *>(qa_lds + 16 * cb * RB + koff(dc)));
+    };
+
+    // The work of a token tile: its scores (qk), then the softmax and the
+    // second product (softmax_pv).
+    typedef f32x4_t Scores[2][2];   // S^T blocks: tokens 16 tb + MFMA rows, columns of block cb
+    auto slot_base = [&](auto slotc) {
+        // the slot's offset is hidden from the optimiser: otherwise it keeps a
+        // copy of every lane offset per slot in registers across the walk
+        int off = decltype(slotc)::value * Gm::SLOT;
+        asm volatile("" : "+s"(off));
+        return ring + off;
+    };
+    auto qk = [&](auto slotc, Scores &sc) {
+        const char *kb = slot_base(slotc);
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             bf16x8_t ka[DC];
 #pragma unroll
             for (int dc = 0; dc < DC; ++dc)
-                ka[dc] = as_bf16x8(*reinterpret_cast<const uint4 *>(kb + 16 * tb * RB + koff[dc]));
+                ka[dc] = as_bf16x8(*reinterpret_cast<const uint4 *>(kb + 16 * tb * RB + koff(dc)));
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) {
                 f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -360,9 +514,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                 sc[tb][cb] = acc;
             }
         }
-        // online softmax per column; P^T operands in the token order above.
-        // Tiles wholly below every position of the wave need no mask.
-        const bool masked = t0 + kTileTok - 1 > wmin;
+    };
+    // MASK: some token of the tile lies past some column's position
+    using Masked = std::true_type;
+    using Plain = std::false_type;
+    auto softmax_pv = [&](auto maskc, auto slotc, int t0, const Scores &sc) {
+        constexpr bool MASK = decltype(maskc)::value;
+        const char *vb = slot_base(slotc) + Gm::TILE;
+        // online softmax per column; P^T operands in the token order above
         bf16x8_t phi[2], plo[2];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
@@ -370,8 +529,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             float tmax = -__builtin_inff();
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int t = t0 + 16 * (e >> 2) + 4 * q + (e & 3);
-                vis[e] = !masked || t <= cpos[cb];
+                vis[e] = !MASK || t0 + 16 * (e >> 2) + 4 * q + (e & 3) <= cpos[cb];
                 tmax = fmaxf(tmax, vis[e] ? sc[e >> 2][cb][e & 3] : -__builtin_inff());
             }
             // lazy maximum: raised (to the tile's column maximum) only when a
@@ -410,9 +568,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t *)(vb + voff[db]));
+                (lds_i16x4_t *)(vb + voff(db)));
             const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t *)(vb + voff[db] + 16 * RB));
+                (lds_i16x4_t *)(vb + voff(db) + 16 * RB));
             const bf16x8_t va = __builtin_bit_cast(
                 bf16x8_t, u32x4_t{__builtin_bit_cast(uint2, v0).x, __builtin_bit_cast(uint2, v0).y,
                                   __builtin_bit_cast(uint2, v1).x, __builtin_bit_cast(uint2, v1).y});
@@ -424,83 +582,80 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    // ---- the walk.  Per step s, in this order: wait for the step's rows (and
-    // the page ids two steps ahead), barrier, issue the page ids of step s + 3
-    // and the rows of step s + 2, compute step s.  Waves of both chains meet
-    // at every barrier.
+    // ---- the walk.  Per step s, in this order: wait for the rows of step s,
+    // barrier, issue the rows of step s + 2, write the new rows of step s into
+    // the cache (the first workgroup), load the page ids of step s + 3, then
+    // the scores, softmax and second product of step s.  Waves of both chains
+    // meet at every barrier.
     if (0 < my_len)
-        issue_pages(0);
+        load_pages(S0{}, 0);
     if (1 < my_len)
-        issue_pages(1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-    if (0 < my_len)
-        issue_kv(0);
+        load_pages(S1{}, 1);
     if (2 < my_len)
-        issue_pages(2);
+        load_pages(S2{}, 2);
+    if (0 < my_len)
+        issue_kv(S0{}, 0);
     if (1 < my_len)
-        issue_kv(1);
+        issue_kv(S1{}, 1);
+    auto visible = [&](int s) { return tok_tile(s) * kTileTok <= wmax; };
+    auto masked = [&](int s) { return tok_tile(s) * kTileTok + kTileTok - 1 > wmin; };
 
-    // the append: this workgroup's share of the (entry, KV head)'s new rows,
-    // four 16-byte chunks per thread in flight
-    if (a.cache_w != nullptr) {
-        const int share = (T + 1) / 2;
-        const int j0 = (int)((int64_t)nc * kk / share), j1 = (int)((int64_t)nc * (kk + 1) / share);
-        const int jobs = (j1 - j0) * 2 * CPR;
-        // job -> source and destination (null: no job, or a bad page id);
-        // past the last job the source is the last job's (a plain load)
-        auto job_ptrs = [&](int job, const uint4 *&src, uint4 *&dst) {
-            const bool live = job < jobs;
-            job = min(job, jobs - 1);
-            const int row = j0 + job / (2 * CPR);
-            const int is_v = (job / CPR) & 1, ch = job % CPR;
-            const int tok = base_pos + row;
-            const int page = pages[tok >> a.page_shift];
-            src = reinterpret_cast<const uint4 *>((is_v ? a.v_new : a.k_new) +
-                                                  (int64_t)(r0 + row) * a.row_stride + h * D) + ch;
-            dst = nullptr;
-            if (live && page >= 0 && page < a.num_pages)
-                dst = reinterpret_cast<uint4 *>(a.cache_w + (int64_t)page * a.page_stride +
-                                                (is_v ? a.half_stride : 0) +
-                                                (int64_t)(tok & pmask) * a.row_stride + h * D) + ch;
-        };
-        for (int i0 = tid; i0 < jobs; i0 += 4 * kThreads) {
-            const uint4 *s0, *s1, *s2, *s3;
-            uint4 *d0, *d1, *d2, *d3;
-            job_ptrs(i0, s0, d0);
-            job_ptrs(i0 + kThreads, s1, d1);
-            job_ptrs(i0 + 2 * kThreads, s2, d2);
-            job_ptrs(i0 + 3 * kThreads, s3, d3);
-            const uint4 v0 = *s0, v1 = *s1, v2 = *s2, v3 = *s3;
-            if (d0)
-                *d0 = v0;
-            if (d1)
-                *d1 = v1;
-            if (d2)
-                *d2 = v2;
-            if (d3)
-                *d3 = v3;
+    // the tile of step s: chain A's switch of column tiles, then the scores,
+    // softmax and second product when the tile is visible
+    auto compute_step = [&](auto slotc, int s) {
+        if (a_switch && s == nA1) {
+            // chain A moves from its own column tile to the pair's other one
+            finalize();
+            switch_columns();
         }
-    }
+        if (!visible(s))   // no token of the tile is visible to the wave's columns
+            return;
+        const int t0 = tok_tile(s) * kTileTok;
+        Scores sc;
+        qk(slotc, sc);
+        if (masked(s))
+            softmax_pv(Masked{}, slotc, t0, sc);
+        else
+            softmax_pv(Plain{}, slotc, t0, sc);
+    };
 
-    for (int s = 0; s < steps; ++s) {
+    int nst = 0;   // vector stores issued after the last copies (counted for the wait)
+    auto step = [&](auto slotc, int s) {
+        constexpr int SL = decltype(slotc)::value;
+        using Next2 = std::integral_constant<int, (SL + 2) % kRing>;
+        // the rows of step s have landed once no more are outstanding than
+        // the copies of step s + 1 and the stores issued since
         if (s + 1 < my_len)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CPW));
+            wait_vm_at_most<4 * CPW>(2 * CPW + nst);
         else
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
+        nst = 0;
         if (s >= my_len)
-            continue;
-        if (s + 3 < my_len)
-            issue_pages(s + 3);
-        if (s + 2 < my_len)
-            issue_kv(s + 2);
-        if (chain == 0 && s == nA1 && nA2 > 0) {
-            // chain A moves from its own column tile to the pair's other one
-            finalize();
-            set_columns(jh);
-        }
-        compute(s);
+            return;
+        // chain B issues its copies first and computes after, chain A the
+        // other way round: the two waves on a SIMD then run the matrix
+        // products of one under the vector and scalar work of the other
+        auto issue = [&]() {
+            if (s + 2 < my_len)
+                issue_kv(Next2{}, s + 2);
+            if (writer && (chain == 1 || jl == jh || s >= nA1))
+                nst = append_tile(slotc, s);
+            if (s + 3 < my_len)
+                load_pages(slotc, s + 3);
+        };
+        if (chain == 1)
+            issue();
+        compute_step(slotc, s);
+        if (chain == 0)
+            issue();
+    };
+    for (int s = 0; s < steps; s += kRing) {
+        step(S0{}, s);
+        if (s + 1 < steps)
+            step(S1{}, s + 1);
+        if (s + 2 < steps)
+            step(S2{}, s + 2);
     }
     __syncthreads();
 
