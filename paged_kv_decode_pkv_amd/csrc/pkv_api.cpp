@@ -382,7 +382,8 @@ int pkv_prefill(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void
         num_qo_heads > kMaxHeads || desc.num_kv_heads > kMaxHeads ||
         num_qo_heads % desc.num_kv_heads != 0 || max_q_rows < 1 || !isfinite(sm_scale))
         return PKV_ERR_BAD_SHAPE;
-    if (!pkv::prefill_supported(desc.head_dim) || batch > 65535)
+    if (!pkv::prefill_supported(desc.head_dim) || batch > 65535 ||
+        2 * page_elems(desc) > (int64_t)UINT32_MAX)
         return PKV_ERR_UNSUPPORTED;
     if (batch == 0)
         return PKV_OK;

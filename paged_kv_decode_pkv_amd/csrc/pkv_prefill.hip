@@ -345,14 +345,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 
     // ---- copies.  Copy i of a wave moves rows RPC (w4 + 4 i) .. + RPC - 1 of
     // a token tile; lane l holds row + l / CPR, LDS chunk l % CPR, which is
-    // logical chunk (l % CPR) ^ swz(row) of the source row.
+    // logical chunk (l % CPR) ^ swz(row) of the source row.  Token tile s
+    // goes to ring slot s % kRing.
     const int pmask = a.page_size - 1;   // page sizes are powers of two
     const bool fresh = a.k_new != nullptr;
     const bool big_pages = a.page_size >= RPC;   // a copy's rows share a page
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
-    static_assert(kRing == 3, "the walk is unrolled by three");
     const int rr = lane / CPR;   // row within a copy
     // source chunk offsets (elements) of K and V of copy i
     auto kel = [&](int i) { return 8 * ((lane % CPR) ^ swz_k<D>(RPC * (w4 + 4 * i) + rr)); };
@@ -363,105 +360,90 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         kvo[i] = 2u * (uint32_t)(rr * a.row_stride + kel(i));
         vvo[i] = 2u * (uint32_t)(rr * a.row_stride + vel(i));
     }
-    // new rows come from k_new / v_new: row r0 + tok - base_pos
-    const uint16_t *knew_b = fresh ? a.k_new + ((int64_t)r0 - base_pos) * a.row_stride + h * D
-                                   : a.cache;
-    const int64_t vnew_d = fresh ? (a.v_new - a.k_new) : 0;   // v_new row - k_new row
-    const uint16_t *cache_h = a.cache + h * D;
+    // Byte addressing.  New rows come from k_new / v_new (row r0 + tok -
+    // base_pos), the others from their page.
+    const uint32_t rs_b = 2u * (uint32_t)a.row_stride;   // bytes per token row (all heads)
+    const char *knew_t = reinterpret_cast<const char *>(
+        fresh ? a.k_new + ((int64_t)r0 - base_pos) * a.row_stride + h * D : a.cache);
+    const int64_t vnew_b = fresh ? 2 * (a.v_new - a.k_new) : 0;   // v_new row - k_new row
+    const char *cache_hb = reinterpret_cast<const char *>(a.cache + h * D);
+    // page and half-page strides in bytes: under 4 GiB (the host checks)
+    const uint32_t ps_b = 2u * (uint32_t)a.page_stride, hs_b = 2u * (uint32_t)a.half_stride;
+    uint32_t roff[CPW];   // bytes from a tile's first row to copy i's first row
+#pragma unroll
+    for (int i = 0; i < CPW; ++i)
+        roff[i] = (uint32_t)(RPC * (w4 + 4 * i)) * rs_b;
     typedef __attribute__((address_space(4))) const int32_t const_i32;
-    const const_i32 *pages_s = (const const_i32 *)(pages);   // scalar loads
-    // page id of each copy's first row, per ring slot (scalar registers)
-    int pgr[kRing][CPW];
-    auto load_pages = [&](auto slotc, int s) {
-        constexpr int SL = decltype(slotc)::value;
+    const const_i32 *pages_s = (const const_i32 *)(pages);   // scalar loads of the same ids
+    typedef int PageIds[CPW];   // page id of each copy's first row (scalar registers)
+    auto load_pages = [&](int s, PageIds &pg) {
         const int t0 = tok_tile(s) * kTileTok;
 #pragma unroll
         for (int i = 0; i < CPW; ++i)
-            pgr[SL][i] = pages_s[min(t0 + RPC * (w4 + 4 * i), len - 1) >> a.page_shift];
+            pg[i] = pages_s[min(t0 + RPC * (w4 + 4 * i), len - 1) >> a.page_shift];
     };
     auto page_base = [&](int page, int tok0) {   // first element of token tok0's row (head h)
         const int pg = (uint32_t)page < (uint32_t)a.num_pages ? page : 0;   // bad id: no fault
         return (int64_t)pg * a.page_stride + (int64_t)(tok0 & pmask) * a.row_stride + h * D;
     };
-    auto issue_kv = [&](auto slotc, int s) {
-        constexpr int SL = decltype(slotc)::value;
+    // first byte of copy i's rows in the cache (one page holds them)
+    auto cached_base = [&](int page, int t0, int i) {
+        const uint32_t pg = (uint32_t)page < (uint32_t)a.num_pages ? (uint32_t)page : 0u;
+        return cache_hb + (uint64_t)pg * ps_b +
+               (uint32_t)((t0 + RPC * (w4 + 4 * i)) & pmask) * rs_b;
+    };
+    auto slot_of = [&](int s) { return (s % kRing) * Gm::SLOT; };   // ring slot, bytes
+    // A token tile is copied one way for all its rows: kFresh (all new rows,
+    // from k_new / v_new), kCached (no new row, every copy's rows in one
+    // page), or kEdge (per lane: tiles over the prefix or the entry's end, or
+    // pages shorter than a copy).
+    enum : int { kCached = 0, kFresh = 1, kEdge = 2 };
+    auto tile_mode = [&](int t0) {
+        if (t0 + kTileTok > len)
+            return (int)kEdge;
+        if (fresh && t0 >= base_pos)
+            return (int)kFresh;
+        if (big_pages && (!fresh || t0 + kTileTok <= base_pos))
+            return (int)kCached;
+        return (int)kEdge;
+    };
+    auto issue_kv = [&](int s, const PageIds &pg) {
         const int t0 = tok_tile(s) * kTileTok;
-        const uint32_t kdst = ring_lds + SL * Gm::SLOT;
+        const uint32_t kdst = ring_lds + slot_of(s) + w4 * 1024;
+        const int mode = tile_mode(t0);
+        if (mode == kFresh) {
+            const char *b = knew_t + (int64_t)t0 * rs_b;
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-            const int tok0 = t0 + RPC * (w4 + 4 * i);
-            const uint32_t lk = kdst + (w4 + 4 * i) * 1024, lv = lk + Gm::TILE;
-            if (big_pages && tok0 + RPC <= len &&
-                (!fresh || tok0 >= base_pos || tok0 + RPC <= base_pos)) {
-                // one page (or k_new run) for the whole copy: scalar base
-                const uint16_t *bk;
-                int64_t vd;
-                if (fresh && tok0 >= base_pos) {
-                    bk = knew_b + (int64_t)tok0 * a.row_stride;
-                    vd = vnew_d;
-                } else {
-                    bk = a.cache + page_base(pgr[SL][i], tok0);
-                    vd = a.half_stride;
-                }
-                copy16_to_lds_s(bk, kvo[i], lk);
-                copy16_to_lds_s(bk + vd, vvo[i], lv);
-            } else {
-                // rows over a page, prefix or entry boundary: per lane, past
-                // the end the last token again (masked)
-                const int tok = min(tok0 + rr, len - 1);
+            for (int i = 0; i < CPW; ++i) {
+                copy16_to_lds_s(b + roff[i], kvo[i], kdst + 4096 * i);
+                copy16_to_lds_s(b + roff[i] + vnew_b, vvo[i], kdst + Gm::TILE + 4096 * i);
+            }
+        } else if (mode == kCached) {
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                const char *b = cached_base(pg[i], t0, i);
+                copy16_to_lds_s(b, kvo[i], kdst + 4096 * i);
+                copy16_to_lds_s(b + hs_b, vvo[i], kdst + Gm::TILE + 4096 * i);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                // per lane; past the end the last token again (masked)
+                const int tok = min(t0 + RPC * (w4 + 4 * i) + rr, len - 1);
                 const uint16_t *kr;
                 int64_t vd;
                 if (fresh && tok >= base_pos) {
-                    kr = knew_b + (int64_t)tok * a.row_stride;
-                    vd = vnew_d;
+                    kr = reinterpret_cast<const uint16_t *>(knew_t) + (int64_t)tok * a.row_stride;
+                    vd = vnew_b / 2;
                 } else {
                     kr = a.cache + page_base(pages[tok >> a.page_shift], tok);
                     vd = a.half_stride;
                 }
-                copy16_to_lds(kr + kel(i), lk);
-                copy16_to_lds(kr + vd + vel(i), lv);
+                copy16_to_lds(kr + kel(i), kdst + 4096 * i);
+                copy16_to_lds(kr + vd + vel(i), kdst + Gm::TILE + 4096 * i);
             }
         }
     };
-    // The append: the first workgroup of the (entry, KV head) writes every
-    // new row it copied (chain B its walk, chain A the steps on column tile
-    // jh), from LDS, once the tile has landed.  Returns the number of vector
-    // stores issued for certain (per-lane stores are not counted: a count too
-    // low only makes the next wait longer).
-    const bool writer = a.cache_w != nullptr && kk == 0;
-    auto append_tile = [&](auto slotc, int s) {
-        constexpr int SL = decltype(slotc)::value;
-        int nst = 0;
-        const int t0 = tok_tile(s) * kTileTok;
-        const char *kslot = ring + SL * Gm::SLOT;
-#pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-            const int tok0 = t0 + RPC * (w4 + 4 * i);
-            if (tok0 + RPC <= base_pos || tok0 >= base_pos + nc)
-                continue;   // no new row in this copy
-            const uint4 vk = *reinterpret_cast<const uint4 *>(kslot + (w4 + 4 * i) * 1024 + 16 * lane);
-            const uint4 vv =
-                *reinterpret_cast<const uint4 *>(kslot + Gm::TILE + (w4 + 4 * i) * 1024 + 16 * lane);
-            if (big_pages && tok0 >= base_pos && tok0 + RPC <= base_pos + nc) {
-                uint16_t *bk = a.cache_w + page_base(pgr[SL][i], tok0);
-                store16_s(bk, kvo[i], vk);
-                store16_s(bk + a.half_stride, vvo[i], vv);
-                nst += 2;
-            } else {
-                const int tok = tok0 + rr;
-                if (tok >= base_pos && tok < base_pos + nc) {
-                    const int page = pages[tok >> a.page_shift];
-                    if ((uint32_t)page < (uint32_t)a.num_pages) {
-                        uint16_t *bk = a.cache_w + page_base(page, tok);
-                        *reinterpret_cast<uint4 *>(bk + kel(i)) = vk;
-                        *reinterpret_cast<uint4 *>(bk + a.half_stride + vel(i)) = vv;
-                    }
-                }
-            }
-        }
-        return nst;
-    };
-
     // chain A's second column tile: its q rows through LDS (copied now, read
     // at the switch), rows swizzled like K
     char *qa_lds = smem + 2 * Gm::RING + w4 * (32 * RB);
@@ -487,18 +469,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
                     flip(*reinterpret_cast<const uint4 *>(qa_lds + 16 * cb * RB + koff(dc)));
     };
 
-    // The work of a token tile: its scores (qk), then the softmax and the
-    // second product (softmax_pv).
+    // ---- the work of a token tile, in three parts: its scores (qk, matrix
+    // cores), the softmax (vector ALU) and the second product (pv, matrix
+    // cores).
     typedef f32x4_t Scores[2][2];   // S^T blocks: tokens 16 tb + MFMA rows, columns of block cb
-    auto slot_base = [&](auto slotc) {
-        // the slot's offset is hidden from the optimiser: otherwise it keeps a
-        // copy of every lane offset per slot in registers across the walk
-        int off = decltype(slotc)::value * Gm::SLOT;
-        asm volatile("" : "+s"(off));
-        return ring + off;
-    };
-    auto qk = [&](auto slotc, Scores &sc) {
-        const char *kb = slot_base(slotc);
+    typedef bf16x8_t Weights[2];    // P^T operands of the two column blocks
+    auto qk = [&](int s, Scores &sc) {
+        const char *kb = ring + slot_of(s);
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             bf16x8_t ka[DC];
@@ -515,14 +492,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             }
         }
     };
-    // MASK: some token of the tile lies past some column's position
+    // online softmax per column; P^T operands in the token order above.
+    // MASK: some token of the tile lies past some column's position.
     using Masked = std::true_type;
     using Plain = std::false_type;
-    auto softmax_pv = [&](auto maskc, auto slotc, int t0, const Scores &sc) {
+    auto softmax = [&](auto maskc, int t0, const Scores &sc, Weights &phi, Weights &plo) {
         constexpr bool MASK = decltype(maskc)::value;
-        const char *vb = slot_base(slotc) + Gm::TILE;
-        // online softmax per column; P^T operands in the token order above
-        bf16x8_t phi[2], plo[2];
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
             bool vis[8];
@@ -563,8 +538,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             phi[cb] = __builtin_bit_cast(bf16x8_t, u32x4_t{hw[0], hw[1], hw[2], hw[3]});
             plo[cb] = __builtin_bit_cast(bf16x8_t, u32x4_t{lw[0], lw[1], lw[2], lw[3]});
         }
-        // O^T += V^T P^T: lane gets V^T[16 db + c] at tokens 4 q .. 4 q + 3 and
-        // 16 + 4 q .. 16 + 4 q + 3
+    };
+    // O^T += V^T P^T: lane gets V^T[16 db + c] at tokens 4 q .. 4 q + 3 and
+    // 16 + 4 q .. 16 + 4 q + 3
+    auto pv = [&](int s, const Weights &phi, const Weights &plo) {
+        const char *vb = ring + slot_of(s) + Gm::TILE;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -581,83 +559,175 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
             }
         }
     };
-
-    // ---- the walk.  Per step s, in this order: wait for the rows of step s,
-    // barrier, issue the rows of step s + 2, write the new rows of step s into
-    // the cache (the first workgroup), load the page ids of step s + 3, then
-    // the scores, softmax and second product of step s.  Waves of both chains
-    // meet at every barrier.
-    if (0 < my_len)
-        load_pages(S0{}, 0);
-    if (1 < my_len)
-        load_pages(S1{}, 1);
-    if (2 < my_len)
-        load_pages(S2{}, 2);
-    if (0 < my_len)
-        issue_kv(S0{}, 0);
-    if (1 < my_len)
-        issue_kv(S1{}, 1);
     auto visible = [&](int s) { return tok_tile(s) * kTileTok <= wmax; };
     auto masked = [&](int s) { return tok_tile(s) * kTileTok + kTileTok - 1 > wmin; };
 
-    // the tile of step s: chain A's switch of column tiles, then the scores,
-    // softmax and second product when the tile is visible
-    auto compute_step = [&](auto slotc, int s) {
-        if (a_switch && s == nA1) {
-            // chain A moves from its own column tile to the pair's other one
-            finalize();
-            switch_columns();
-        }
-        if (!visible(s))   // no token of the tile is visible to the wave's columns
-            return;
-        const int t0 = tok_tile(s) * kTileTok;
-        Scores sc;
-        qk(slotc, sc);
-        if (masked(s))
-            softmax_pv(Masked{}, slotc, t0, sc);
-        else
-            softmax_pv(Plain{}, slotc, t0, sc);
+    // ---- the walk.  The two waves on a SIMD (one of each chain) alternate
+    // between vector and matrix work, phase by phase, with a barrier between
+    // phases:
+    //   phase 2s:      A: copies of step s + 2, softmax(s)   B: pv(s - 1), qk(s)
+    //   phase 2s + 1:  A: pv(s), qk(s + 1)                   B: copies of step s + 2, softmax(s)
+    // so the matrix products of one run under the other's vector work.  A
+    // wave waits for a tile's rows before the barrier of the phase whose
+    // products read them; at most the copies issued after them (one step's)
+    // may still be outstanding (the append's loads went out before every
+    // copy; its stores, at step 1, only make later waits longer).
+    // The append: the workgroups of an (entry, KV head) share its new rows,
+    // up to four 16-byte chunks per thread; the loads go out before the
+    // walk's copies and the stores early in the walk.
+    const bool append = a.cache_w != nullptr;
+    const int share = (T + 1) / 2;
+    const int j0 = (int)((int64_t)nc * kk / share), j1 = (int)((int64_t)nc * (kk + 1) / share);
+    const int jobs = append ? (j1 - j0) * 2 * CPR : 0;
+    // job: chunk job % CPR of the K (or V) row of new row j0 + job / (2 CPR);
+    // past the last job the last job's source is read again (a plain load)
+    auto job_src = [&](int job) {
+        job = min(job, jobs - 1);
+        const int row = j0 + job / (2 * CPR);
+        const int is_v = (job / CPR) & 1, ch = job % CPR;
+        return reinterpret_cast<const uint4 *>((is_v ? a.v_new : a.k_new) +
+                                               (int64_t)(r0 + row) * a.row_stride + h * D) + ch;
     };
+    auto job_page = [&](int job) {
+        job = min(job, jobs - 1);
+        return pages[(base_pos + j0 + job / (2 * CPR)) >> a.page_shift];
+    };
+    auto job_store = [&](int job, int page, uint4 v) {
+        if (job >= jobs || (uint32_t)page >= (uint32_t)a.num_pages)
+            return;   // no job, or a bad page id
+        const int row = j0 + job / (2 * CPR);
+        const int is_v = (job / CPR) & 1, ch = job % CPR;
+        const int tok = base_pos + row;
+        *reinterpret_cast<uint4 *>(a.cache_w + (int64_t)page * a.page_stride +
+                                   (is_v ? a.half_stride : 0) +
+                                   (int64_t)(tok & pmask) * a.row_stride + h * D + 8 * ch) = v;
+    };
+    uint4 av0, av1, av2, av3;
+    int ap0 = -1, ap1 = -1, ap2 = -1, ap3 = -1;
+    if (jobs > 0) {
+        av0 = *job_src(tid);
+        av1 = *job_src(tid + kThreads);
+        av2 = *job_src(tid + 2 * kThreads);
+        av3 = *job_src(tid + 3 * kThreads);
+        ap0 = job_page(tid);
+        ap1 = job_page(tid + kThreads);
+        ap2 = job_page(tid + 2 * kThreads);
+        ap3 = job_page(tid + 3 * kThreads);
+    }
 
-    int nst = 0;   // vector stores issued after the last copies (counted for the wait)
-    auto step = [&](auto slotc, int s) {
-        constexpr int SL = decltype(slotc)::value;
-        using Next2 = std::integral_constant<int, (SL + 2) % kRing>;
-        // the rows of step s have landed once no more are outstanding than
-        // the copies of step s + 1 and the stores issued since
-        if (s + 1 < my_len)
-            wait_vm_at_most<4 * CPW>(2 * CPW + nst);
+    PageIds pg0, pg1, pg2;   // page ids of steps s, s + 1, s + 2
+    if (0 < my_len)
+        load_pages(0, pg0);
+    if (1 < my_len)
+        load_pages(1, pg1);
+    if (2 < my_len)
+        load_pages(2, pg2);
+    if (0 < my_len)
+        issue_kv(0, pg0);
+    if (1 < my_len)
+        issue_kv(1, pg1);
+    auto wait_rows = [&](bool later_copies) {
+        // no more outstanding than the copies issued after the rows wanted
+        if (later_copies)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CPW));
         else
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __syncthreads();
-        nst = 0;
-        if (s >= my_len)
-            return;
-        // chain B issues its copies first and computes after, chain A the
-        // other way round: the two waves on a SIMD then run the matrix
-        // products of one under the vector and scalar work of the other
-        auto issue = [&]() {
-            if (s + 2 < my_len)
-                issue_kv(Next2{}, s + 2);
-            if (writer && (chain == 1 || jl == jh || s >= nA1))
-                nst = append_tile(slotc, s);
-            if (s + 3 < my_len)
-                load_pages(slotc, s + 3);
-        };
-        if (chain == 1)
-            issue();
-        compute_step(slotc, s);
-        if (chain == 0)
-            issue();
     };
-    for (int s = 0; s < steps; s += kRing) {
-        step(S0{}, s);
-        if (s + 1 < steps)
-            step(S1{}, s + 1);
-        if (s + 2 < steps)
-            step(S2{}, s + 2);
+    // copies of step s + 2, the page ids of step s + 3
+    auto issue_step = [&](int s) {
+        if (s + 2 < my_len)
+            issue_kv(s + 2, pg2);
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            pg0[i] = pg1[i];
+            pg1[i] = pg2[i];
+        }
+        if (s + 3 < my_len)
+            load_pages(s + 3, pg2);
+    };
+    auto softmax_step = [&](int s, const Scores &sc, Weights &phi, Weights &plo) {
+        if (!visible(s))
+            return;
+        const int t0 = tok_tile(s) * kTileTok;
+        if (masked(s))
+            softmax(Masked{}, t0, sc, phi, plo);
+        else
+            softmax(Plain{}, t0, sc, phi, plo);
+    };
+    // Each chain runs its own loop over steps (two phases each); both loops
+    // meet the same barriers, one per phase.
+    const int steps2 = max(lenA, nB + 1);   // steps of the longer timeline
+    // the append's stores go out at step 1 (by every wave), to run under the
+    // rest of the walk: the compiler waits there for their loads, which
+    // drains the copies then in flight once
+    auto append_stores = [&]() {
+        job_store(tid, ap0, av0);
+        job_store(tid + kThreads, ap1, av1);
+        job_store(tid + 2 * kThreads, ap2, av2);
+        job_store(tid + 3 * kThreads, ap3, av3);
+        for (int job = tid + 4 * kThreads; job < jobs; job += kThreads)
+            job_store(job, job_page(job), *job_src(job));
+    };
+    if (chain == 0) {
+        Scores sc;   // scores of the step's tile, from the previous phase
+        if (0 < lenA)
+            wait_rows(1 < lenA);
+        __syncthreads();
+        if (0 < lenA && visible(0))
+            qk(0, sc);
+        for (int s = 0; s < steps2; ++s) {
+            // phase 2s: copies, softmax(s)
+            __syncthreads();
+            if (s == 1)
+                append_stores();
+            Weights phi, plo;
+            if (s < lenA) {
+                issue_step(s);
+                softmax_step(s, sc, phi, plo);
+            }
+            // phase 2s + 1: pv(s), qk(s + 1)
+            if (s + 1 < lenA)
+                wait_rows(s + 2 < lenA);   // tile s + 1, for qk(s + 1)
+            __syncthreads();
+            if (s < lenA) {
+                if (visible(s))
+                    pv(s, phi, plo);
+                if (a_switch && s + 1 == nA1) {
+                    // chain A moves from its own column tile to the pair's other one
+                    finalize();
+                    switch_columns();
+                }
+                if (s + 1 < lenA && visible(s + 1))
+                    qk(s + 1, sc);
+            }
+        }
+    } else {
+        Weights phi, plo;   // the P^T operands of the previous step, for its pv
+        __syncthreads();
+        for (int s = 0; s < steps2; ++s) {
+            // phase 2s: pv(s - 1), qk(s)
+            if (s < nB)
+                wait_rows(s + 1 < nB);   // tile s, for qk(s)
+            __syncthreads();
+            if (s == 1)
+                append_stores();
+            Scores sc;
+            if (s >= 1 && s - 1 < nB && visible(s - 1))
+                pv(s - 1, phi, plo);
+            if (s < nB && visible(s))
+                qk(s, sc);
+            // phase 2s + 1: copies, softmax(s)
+            __syncthreads();
+            if (s < nB) {
+                issue_step(s);
+                softmax_step(s, sc, phi, plo);
+            }
+        }
     }
     __syncthreads();
+
+    if (steps2 < 2)
+        append_stores();
 
     if (!merge) {
         if (my_len > 0)
