@@ -474,23 +474,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     // cores).
     typedef f32x4_t Scores[2][2];   // S^T blocks: tokens 16 tb + MFMA rows, columns of block cb
     typedef bf16x8_t Weights[2];    // P^T operands of the two column blocks
+    // (the four accumulators take turns, so no product waits for the one
+    // just issued)
     auto qk = [&](int s, Scores &sc) {
         const char *kb = ring + slot_of(s);
+        bf16x8_t ka[2][DC];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            bf16x8_t ka[DC];
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int dc = 0; dc < DC; ++dc)
-                ka[dc] = as_bf16x8(*reinterpret_cast<const uint4 *>(kb + 16 * tb * RB + koff(dc)));
+                ka[tb][dc] = as_bf16x8(*reinterpret_cast<const uint4 *>(kb + 16 * tb * RB + koff(dc)));
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-                for (int dc = 0; dc < DC; ++dc)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[dc], qb[cb][dc], acc, 0, 0, 0);
-                sc[tb][cb] = acc;
-            }
-        }
+            for (int cb = 0; cb < 2; ++cb)
+                sc[tb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    sc[tb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[tb][dc], qb[cb][dc],
+                                                                         sc[tb][cb], 0, 0, 0);
     };
     // online softmax per column; P^T operands in the token order above.
     // MASK: some token of the tile lies past some column's position.
@@ -540,23 +546,37 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
         }
     };
     // O^T += V^T P^T: lane gets V^T[16 db + c] at tokens 4 q .. 4 q + 3 and
-    // 16 + 4 q .. 16 + 4 q + 3
+    // 16 + 4 q .. 16 + 4 q + 3.  Two d-blocks at a time: their four high-part
+    // products, then the four remainder products (an accumulator's second
+    // product three behind its first).
     auto pv = [&](int s, const Weights &phi, const Weights &plo) {
         const char *vb = ring + slot_of(s) + Gm::TILE;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t *)(vb + voff(db)));
-            const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t *)(vb + voff(db) + 16 * RB));
-            const bf16x8_t va = __builtin_bit_cast(
-                bf16x8_t, u32x4_t{__builtin_bit_cast(uint2, v0).x, __builtin_bit_cast(uint2, v0).y,
-                                  __builtin_bit_cast(uint2, v1).x, __builtin_bit_cast(uint2, v1).y});
+        for (int db = 0; db < DB; db += 2) {
+            bf16x8_t va[2];
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                o[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[cb], o[cb][db], 0, 0, 0);
-                o[cb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[cb], o[cb][db], 0, 0, 0);
+            for (int u = 0; u < 2; ++u) {
+                const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4_t *)(vb + voff(db + u)));
+                const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4_t *)(vb + voff(db + u) + 16 * RB));
+                va[u] = __builtin_bit_cast(
+                    bf16x8_t,
+                    u32x4_t{__builtin_bit_cast(uint2, v0).x, __builtin_bit_cast(uint2, v0).y,
+                            __builtin_bit_cast(uint2, v1).x, __builtin_bit_cast(uint2, v1).y});
             }
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    o[cb][db + u] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], phi[cb], o[cb][db + u], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    o[cb][db + u] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], plo[cb], o[cb][db + u], 0, 0, 0);
         }
     };
     auto visible = [&](int s) { return tok_tile(s) * kTileTok <= wmax; };
