@@ -74,9 +74,10 @@ def parse():
     ap.add_argument("--decode-rows", type=int, default=60,
                     help="decode entries (one row each) in the mixed step")
     ap.add_argument("--one-call", action="store_true",
-                    help="mixed step as one pkv_prefill over all entries (default: the "
-                         "decode entries through pkv_plan + pkv_run, the prompts through "
-                         "pkv_prefill)")
+                    help="mixed step as one pkv_mixed_run per layer over all entries, on "
+                         "one pkv_plan_mixed per step (default: the decode entries through "
+                         "pkv_plan + pkv_run, the prompts through pkv_prefill, on two "
+                         "tables)")
     ap.add_argument("--probe-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter scale)")
     return ap.parse_args()
@@ -511,6 +512,13 @@ def bench_prefill(args, torch):
     lse = torch.empty((nl, rows, hq), dtype=torch.float32, device=dev)
     maxr = int(nrows.max())
     split = nd > 0 and not args.one_call
+    mixed = nd > 0 and args.one_call
+    dmaxp = int(max((table.indptr[e + 1] - table.indptr[e] for e in range(nd)), default=1))
+    if mixed:
+        # one table, one plan per step over the rows: decode rows on the
+        # decode's schedule, prompts through the prefill, per layer one call
+        mws = torch.empty(max(pkv.workspace_size(pkv.cache_desc(cache), hq, rows, dmaxp, 0),
+                              256), dtype=torch.uint8, device=dev)
     if split:
         # the decode entries as a decode batch (plan once, fused append + decode
         # per layer), the prompt entries as a prefill batch: two tables over the
@@ -524,7 +532,6 @@ def bench_prefill(args, torch):
             return [torch.from_numpy(x).to(dev) for x in (ptr, idx, ll)]
         dec_e, pr_e = list(range(nd)), list(range(nd, b))
         dtab, ptab = sub_table(dec_e), sub_table(pr_e)
-        dmaxp = int(max(table.indptr[e + 1] - table.indptr[e] for e in dec_e))
         pqo = torch.from_numpy((np.concatenate([[0], np.cumsum(nrows[nd:])]) ).astype(
             np.int32)).to(dev)
         ws = torch.empty(max(pkv.workspace_size(pkv.cache_desc(cache), hq, nd, dmaxp, 0), 256),
@@ -540,6 +547,13 @@ def bench_prefill(args, torch):
                 pkv.prefill(cache, layer, Q[layer][nd:], pqo, *ptab, spec.sm_scale, pr,
                             k_new=KN[layer][nd:], v_new=VN[layer][nd:], out=out[layer][nd:],
                             lse=lse[layer][nd:])
+            return
+        if mixed:
+            plan = pkv.plan_mixed(cache, hq, qo, *tabs, rows, dmaxp, workspace=mws)
+            for layer in range(nl):
+                pkv.mixed_run(cache, layer, Q[layer], *tabs, plan, spec.sm_scale, maxr,
+                              k_new=KN[layer], v_new=VN[layer], out=out[layer],
+                              lse=lse[layer])
             return
         for layer in range(nl):
             pkv.prefill(cache, layer, Q[layer], qo, *tabs, spec.sm_scale, maxr,
@@ -594,12 +608,13 @@ def bench_prefill(args, torch):
                    "num_kv_heads": hkv, "head_dim": d, "page_size": ps,
                    "call": ("pkv_plan + per layer pkv_run (decode entries) and pkv_prefill "
                             "(prompt entries)") if split else
-                           "pkv_prefill (append + causal attention) over all entries",
+                           ("pkv_plan_mixed + per layer pkv_mixed_run over all entries"
+                            if mixed else "pkv_prefill over all entries"),
                    "hip_graph": True},
         "ms_per_step_p10_median_p90": [round(p10, 5), round(p50, 5), round(p90, 5)],
         "roofline": {"bound": "hbm",
-                     "kernel": ("run_kernel + prefill_kernel (+ append_rows_kernel)" if split
-                                else "prefill_kernel (+ append_rows_kernel)"),
+                     "kernel": ("run_kernel + prefill_kernel" if split or mixed
+                                else "prefill_kernel"),
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": by,
                      "avg_launch_us": round(launch_us, 3),

@@ -256,6 +256,50 @@ int pkv_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
             void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pkv_plan_mixed -- pkv_plan for a mixed step (new prompts riding a decode
+ * step, as pkv_prefill takes them): the entries with exactly one new row are
+ * decode rows and are planned like pkv_plan's entries, but under their row
+ * index r = qo_indptr[b] (a batch of total_rows rows); the rows of entries
+ * with several new rows get no decode work.  With pkv_mixed_run, a long
+ * decode row is split over workgroups and merged exactly as in pkv_run,
+ * while the prompts go through the prefill ("Supported Models", Qwen3-Omni /
+ * Qwen3-TTS notes: prompts and decode rows in one step; "How a program
+ * runs": the page tables are written once per step).
+ *  qo_indptr     int32 [batch + 1] as for pkv_prefill; total_rows =
+ *                qo_indptr[batch] (host value), at most 8192.
+ *  workspace     sized by pkv_decode_workspace_size(desc, num_qo_heads,
+ *                total_rows, max_pages_per_req, kv_chunk_pages).
+ * Other arguments and errors as for pkv_plan; batch <= 65535.
+ */
+int pkv_plan_mixed(pkv_cache_desc_t desc, int32_t num_qo_heads, const int32_t *qo_indptr,
+                   const int32_t *page_indptr, const int32_t *page_indices,
+                   const int32_t *last_page_len, int32_t batch, int32_t total_rows,
+                   int32_t max_pages_per_req, int32_t kv_chunk_pages, void *workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pkv_mixed_run -- one layer of a mixed step in one call, on a plan of
+ * pkv_plan_mixed: the decode rows through the decode run (with their append
+ * when k_new / v_new are given), then every entry with several new rows
+ * through the prefill (its append and causal attention).  Computes what
+ * pkv_prefill computes for the same arguments, the decode rows up to the
+ * rounding of the decode's split and merge; the cache writes are identical.
+ *  q, out, lse, k_new, v_new, qo_indptr, max_q_rows, sm_scale   as for
+ *                pkv_prefill ([total_rows, ...] arrays).
+ *  batch, total_rows, max_pages_per_req, kv_chunk_pages   as for the
+ *                pkv_plan_mixed call that wrote the workspace (whose rules
+ *                for pkv_run hold here too).
+ * Errors as for pkv_prefill and pkv_run; two launches in stream order.
+ */
+int pkv_mixed_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *q,
+                  int32_t num_qo_heads, const int32_t *qo_indptr, const void *k_new,
+                  const void *v_new, const int32_t *page_indptr, const int32_t *page_indices,
+                  const int32_t *last_page_len, int32_t batch, int32_t total_rows,
+                  int32_t max_q_rows, float sm_scale, void *out, float *lse,
+                  int32_t max_pages_per_req, int32_t kv_chunk_pages, void *workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+
+/*
  * pkv_run_qk_norm_rope -- pkv_run with the append (k_new, v_new required) and
  * the q/k RMSNorm and rotary embedding of pkv_qk_norm_rope_append folded into
  * the same pass: one launch per layer instead of two for Qwen3-style

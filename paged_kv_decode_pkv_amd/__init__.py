@@ -113,6 +113,11 @@ def _load():
     lib.pkv_run_qk_norm_rope.argtypes = [p, CacheDesc, i32, p, p, p, i32, i32, p, p, f32, f32,
                                          p, f32, p, p, i32, i32, p, sz, p]
     lib.pkv_run_qk_norm_rope.restype = ctypes.c_int
+    lib.pkv_plan_mixed.argtypes = [CacheDesc, i32, p, p, p, p, i32, i32, i32, i32, p, sz, p]
+    lib.pkv_plan_mixed.restype = ctypes.c_int
+    lib.pkv_mixed_run.argtypes = [p, CacheDesc, i32, p, i32, p, p, p, p, p, p, i32, i32, i32,
+                                  f32, p, p, i32, i32, p, sz, p]
+    lib.pkv_mixed_run.restype = ctypes.c_int
     lib.pkv_validate_page_table.argtypes = [p, p, p, i32, i32, i32, i32,
                                             ctypes.POINTER(i32)]
     lib.pkv_validate_page_table.restype = ctypes.c_int
@@ -500,6 +505,86 @@ def run(kv_cache, layer: int, q, plan_: DecodePlan, sm_scale: float, k_new=None,
                      _stream(stream))
     if rc != PKV_OK:
         raise PkvError(rc, "pkv_run")
+    return out, lse
+
+
+class MixedPlan(DecodePlan):
+    """A mixed step's decode schedule (pkv_plan_mixed): the decode rows of a
+    batch that also carries prompts, planned under their row indices."""
+
+    def __init__(self, workspace, batch, total_rows, num_qo_heads, max_pages_per_req,
+                 kv_chunk_pages, qo_indptr):
+        super().__init__(workspace, total_rows, num_qo_heads, max_pages_per_req,
+                         kv_chunk_pages)
+        self.entries = batch
+        self.qo_indptr = qo_indptr
+
+
+def plan_mixed(kv_cache, num_qo_heads: int, qo_indptr, page_indptr, page_indices,
+               last_page_len, total_rows: int, max_pages_per_req: int,
+               kv_chunk_pages: int = 0, workspace=None, stream=None) -> MixedPlan:
+    """Plan the decode rows of a mixed step (pkv_plan_mixed): entries with one
+    new row; total_rows = qo_indptr[-1].  Returns the plan for
+    :func:`mixed_run`."""
+    import torch
+    desc = cache_desc(kv_cache)
+    batch = int(last_page_len.shape[0])
+    if tuple(qo_indptr.shape) != (batch + 1,):
+        raise ValueError("qo_indptr must be [batch + 1]")
+    dev = kv_cache.device
+    need = workspace_size(desc, num_qo_heads, int(total_rows), max_pages_per_req,
+                          kv_chunk_pages)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    rc = lib.pkv_plan_mixed(desc, int(num_qo_heads),
+                            _dev_ptr(qo_indptr, "qo_indptr", torch.int32, dev),
+                            *_tables(kv_cache, page_indptr, page_indices, last_page_len),
+                            batch, int(total_rows), int(max_pages_per_req),
+                            int(kv_chunk_pages), _dev_ptr(workspace, "workspace", device=dev),
+                            workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != PKV_OK:
+        raise PkvError(rc, "pkv_plan_mixed")
+    return MixedPlan(workspace, batch, int(total_rows), int(num_qo_heads),
+                     int(max_pages_per_req), int(kv_chunk_pages), qo_indptr)
+
+
+def mixed_run(kv_cache, layer: int, q, page_indptr, page_indices, last_page_len,
+              plan_: MixedPlan, sm_scale: float, max_q_rows: int, k_new=None, v_new=None,
+              out=None, lse=None, with_lse: bool = True, stream=None):
+    """One layer of a mixed step in one call (pkv_mixed_run): decode rows on
+    the plan, prompts through the prefill; returns (out, lse) like
+    :func:`prefill`."""
+    import torch
+    desc = cache_desc(kv_cache)
+    rows, hq = plan_.batch, plan_.num_qo_heads
+    if q.dim() != 3 or q.shape[0] != rows or q.shape[1] != hq:
+        raise ValueError("q must be [total_rows, Hq, D] of the plan")
+    append = k_new is not None or v_new is not None
+    if append:
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            if t is None or tuple(t.shape) != (rows, desc.num_kv_heads, desc.head_dim):
+                raise ValueError(f"{name} must be [total_rows, Hkv, D]")
+    dev = kv_cache.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((rows, hq), dtype=torch.float32, device=dev)
+    null = ctypes.c_void_p(0)
+    ws = plan_.workspace
+    rc = lib.pkv_mixed_run(_dev_ptr(kv_cache, "kv_cache", torch.bfloat16), desc, int(layer),
+                           _dev_ptr(q, "q", torch.bfloat16, dev), hq,
+                           _dev_ptr(plan_.qo_indptr, "qo_indptr", torch.int32, dev),
+                           _dev_ptr(k_new, "k_new", torch.bfloat16, dev) if append else null,
+                           _dev_ptr(v_new, "v_new", torch.bfloat16, dev) if append else null,
+                           *_tables(kv_cache, page_indptr, page_indices, last_page_len),
+                           plan_.entries, rows, int(max_q_rows), float(sm_scale),
+                           _dev_ptr(out, "out", torch.bfloat16, dev),
+                           null if lse is None else _dev_ptr(lse, "lse", torch.float32, dev),
+                           plan_.max_pages_per_req, plan_.kv_chunk_pages,
+                           _dev_ptr(ws, "workspace", device=dev), ws.numel() * ws.element_size(),
+                           _stream(stream))
+    if rc != PKV_OK:
+        raise PkvError(rc, "pkv_mixed_run")
     return out, lse
 
 

@@ -54,6 +54,8 @@ struct Layout {
     int64_t max_tiles = 0;      // tiles of batch entries of max_pages_per_req pages
     int64_t slots = 0;          // partial rows per query head
     int64_t off_ent = 0, off_blocks = 0, off_part_o = 0, off_part_lse = 0;
+    int64_t off_list = 0;       // a mixed plan's prefill list
+    int32_t list_cap = 0;       // entry ids it holds
     int64_t ws_bytes = 0;
 };
 
@@ -99,7 +101,11 @@ Layout make_layout(const pkv_cache_desc_t &d, int32_t num_qo_heads, int32_t batc
     p.off_part_o = p.off_blocks + align256(block_ints4 * 16);
     const int64_t rows = p.slots * num_qo_heads;
     p.off_part_lse = p.off_part_o + align256(rows * d.head_dim * 2);
-    p.ws_bytes = p.off_part_lse + align256(rows * 8);
+    p.off_list = p.off_part_lse + align256(rows * 8);
+    // a mixed plan over `batch` rows lists at most batch / 2 entries with
+    // several rows (and one more under a malformed qo_indptr is dropped)
+    p.list_cap = batch / 2 + 1;
+    p.ws_bytes = p.off_list + align256(((int64_t)p.list_cap + 2) * 4);
     return p;
 }
 
@@ -161,10 +167,10 @@ int prepare(const pkv_cache_desc_t &desc, int32_t num_qo_heads, int32_t batch,
 // uses a record.
 int32_t plan_signature(const pkv_cache_desc_t &desc, int32_t num_qo_heads, int32_t batch,
                        int32_t max_pages_per_req, int32_t kv_chunk_pages, const Layout &lay,
-                       int num_blocks, int block_stride) {
+                       int num_blocks, int block_stride, bool mixed) {
     const int32_t v[] = {batch, num_qo_heads, desc.num_kv_heads, desc.page_size,
                          desc.head_dim, max_pages_per_req, kv_chunk_pages, desc.num_pages,
-                         num_blocks, block_stride, lay.tiles_per_page};
+                         num_blocks, block_stride, lay.tiles_per_page, mixed ? 1 : 0};
     uint32_t h = 2166136261u;
     for (int32_t x : v)
         for (int k = 0; k < 4; ++k) {
@@ -178,7 +184,7 @@ int32_t plan_signature(const pkv_cache_desc_t &desc, int32_t num_qo_heads, int32
 int prepare_plan(pkv_cache_desc_t desc, int32_t num_qo_heads, const int32_t *page_indptr,
                  const int32_t *page_indices, const int32_t *last_page_len, int32_t batch,
                  int32_t max_pages_per_req, int32_t kv_chunk_pages, void *workspace,
-                 size_t workspace_bytes, pkv::PlanArgs &a) {
+                 size_t workspace_bytes, pkv::PlanArgs &a, bool mixed = false) {
     int rc = check_decode_args(desc, 0, num_qo_heads, batch, 1.f, max_pages_per_req,
                                kv_chunk_pages);
     if (rc != PKV_OK)
@@ -199,8 +205,12 @@ int prepare_plan(pkv_cache_desc_t desc, int32_t num_qo_heads, const int32_t *pag
     a.ent = reinterpret_cast<int32_t *>(ws + lay.off_ent);
     a.cnt = reinterpret_cast<int32_t *>(ws);
     a.plan_sig = plan_signature(desc, num_qo_heads, batch, max_pages_per_req, kv_chunk_pages,
-                                lay, num_blocks, block_stride);
+                                lay, num_blocks, block_stride, mixed);
     a.batch = batch;
+    a.qo_indptr = nullptr;   // set by the mixed plan
+    a.num_entries = batch;
+    a.list = reinterpret_cast<int32_t *>(ws + lay.off_list);
+    a.list_cap = lay.list_cap;
     a.num_pages = desc.num_pages;
     a.page_size = desc.page_size;
     a.tiles_per_page = lay.tiles_per_page;
@@ -218,6 +228,8 @@ struct RunLaunch {
     pkv::RunArgs args;
     const int32_t *blocks = nullptr;
     const int32_t *ent = nullptr;
+    const int32_t *list = nullptr;   // a mixed plan's prefill list
+    int32_t list_cap = 0;
     int num_blocks = 0;
     int group = 0;
 };
@@ -226,7 +238,7 @@ int prepare_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void
                 const void *v_new, const void *q, int32_t num_qo_heads, int32_t batch,
                 float sm_scale, void *out, float *lse, int32_t max_pages_per_req,
                 int32_t kv_chunk_pages, void *workspace, size_t workspace_bytes,
-                RunLaunch &r) {
+                RunLaunch &r, bool mixed = false) {
     int rc = check_decode_args(desc, layer, num_qo_heads, batch, sm_scale, max_pages_per_req,
                                kv_chunk_pages);
     if (rc != PKV_OK)
@@ -259,7 +271,7 @@ int prepare_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void
     a.part_lse_bytes = lay.ws_bytes - lay.off_part_lse;
     a.cnt = reinterpret_cast<int32_t *>(ws);
     a.plan_sig = plan_signature(desc, num_qo_heads, batch, max_pages_per_req, kv_chunk_pages,
-                                lay, num_blocks, block_stride);
+                                lay, num_blocks, block_stride, mixed);
     a.num_pages = desc.num_pages;
     a.page_size = desc.page_size;
     a.page_stride = page_elems(desc);
@@ -277,6 +289,8 @@ int prepare_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void
     a.log2_theta = 0.0;
     r.blocks = reinterpret_cast<const int32_t *>(ws + lay.off_blocks);
     r.ent = reinterpret_cast<const int32_t *>(ws + lay.off_ent);
+    r.list = reinterpret_cast<const int32_t *>(ws + lay.off_list);
+    r.list_cap = lay.list_cap;
     r.num_blocks = num_blocks;
     r.group = num_qo_heads / desc.num_kv_heads;
     return PKV_OK;
@@ -316,6 +330,71 @@ int plan_and_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const voi
     if (rc != PKV_OK)
         return rc;
     return launch_run(r, desc, stream);
+}
+
+
+// Host checks of a prefill launch (pkv_prefill and the prefill half of
+// pkv_mixed_run); on success `a` is ready, and `any` says whether there is
+// work (batch > 0).
+int prepare_prefill(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *q,
+                    int32_t num_qo_heads, const int32_t *qo_indptr, const void *k_new,
+                    const void *v_new, const int32_t *page_indptr, const int32_t *page_indices,
+                    const int32_t *last_page_len, int32_t batch, int32_t max_q_rows,
+                    float sm_scale, void *out, float *lse, pkv::PrefillArgs &a, bool &any) {
+    any = false;
+    int rc = check_desc(desc);
+    if (rc != PKV_OK)
+        return rc;
+    if (layer < 0 || layer >= desc.num_layers || batch < 0 || num_qo_heads < 1 ||
+        num_qo_heads > kMaxHeads || desc.num_kv_heads > kMaxHeads ||
+        num_qo_heads % desc.num_kv_heads != 0 || max_q_rows < 1 || !isfinite(sm_scale))
+        return PKV_ERR_BAD_SHAPE;
+    if (!pkv::prefill_supported(desc.head_dim) || batch > 65535 ||
+        2 * page_elems(desc) > (int64_t)UINT32_MAX)
+        return PKV_ERR_UNSUPPORTED;
+    if (batch == 0)
+        return PKV_OK;
+    const bool append = k_new != nullptr || v_new != nullptr;
+    if (!kv_cache || !q || !qo_indptr || !page_indptr || !page_indices || !last_page_len ||
+        !out || (append && (!k_new || !v_new)))
+        return PKV_ERR_NULL_PTR;
+    if (!aligned16(kv_cache) || !aligned16(q) || !aligned16(out) ||
+        (append && (!aligned16(k_new) || !aligned16(v_new))))
+        return PKV_ERR_ALIGNMENT;
+    uint16_t *slab = static_cast<uint16_t *>(kv_cache) + (int64_t)layer * desc.num_pages * page_elems(desc);
+    a.cache = slab;
+    a.cache_w = append ? slab : nullptr;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k_new = static_cast<const uint16_t *>(k_new);
+    a.v_new = static_cast<const uint16_t *>(v_new);
+    a.out = static_cast<uint16_t *>(out);
+    a.lse = lse;
+    a.qo_indptr = qo_indptr;
+    a.indptr = page_indptr;
+    a.indices = page_indices;
+    a.last_len = last_page_len;
+    a.page_stride = page_elems(desc);
+    a.half_stride = desc.page_size * desc.num_kv_heads * desc.head_dim;
+    a.row_stride = desc.num_kv_heads * desc.head_dim;
+    a.num_pages = desc.num_pages;
+    a.page_size = desc.page_size;
+    a.num_qo_heads = num_qo_heads;
+    a.num_kv_heads = desc.num_kv_heads;
+    a.head_dim = desc.head_dim;
+    a.batch = batch;
+    a.max_rows = max_q_rows;
+    const int64_t col_tiles = ((int64_t)max_q_rows * (num_qo_heads / desc.num_kv_heads) + 127) / 128;
+    a.pair_tiles = (int32_t)((col_tiles + 1) / 2);
+    a.skip_single = 0;
+    a.list = nullptr;
+    a.list_sig = 0;
+    a.list_cap = 0;
+    a.page_shift = 0;
+    while ((1 << a.page_shift) < desc.page_size)
+        ++a.page_shift;
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    any = true;
+    return PKV_OK;
 }
 
 }  // namespace
@@ -375,56 +454,73 @@ int pkv_prefill(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void
                 const void *v_new, const int32_t *page_indptr, const int32_t *page_indices,
                 const int32_t *last_page_len, int32_t batch, int32_t max_q_rows,
                 float sm_scale, void *out, float *lse, hipStream_t stream) {
-    int rc = check_desc(desc);
+    pkv::PrefillArgs a;
+    bool any = false;
+    const int rc = prepare_prefill(kv_cache, desc, layer, q, num_qo_heads, qo_indptr, k_new,
+                                   v_new, page_indptr, page_indices, last_page_len, batch,
+                                   max_q_rows, sm_scale, out, lse, a, any);
+    if (rc != PKV_OK || !any)
+        return rc;
+    return hip_status(pkv::launch_prefill(a, stream));
+}
+
+int pkv_plan_mixed(pkv_cache_desc_t desc, int32_t num_qo_heads, const int32_t *qo_indptr,
+                   const int32_t *page_indptr, const int32_t *page_indices,
+                   const int32_t *last_page_len, int32_t batch, int32_t total_rows,
+                   int32_t max_pages_per_req, int32_t kv_chunk_pages, void *workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+    if (batch < 0 || total_rows < 0)
+        return PKV_ERR_BAD_SHAPE;
+    if (batch > 65535)
+        return PKV_ERR_UNSUPPORTED;
+    int rc = check_decode_args(desc, 0, num_qo_heads, total_rows, 1.f, max_pages_per_req,
+                               kv_chunk_pages);
+    if (rc != PKV_OK || total_rows == 0 || batch == 0)
+        return rc;
+    if (!qo_indptr)
+        return PKV_ERR_NULL_PTR;
+    pkv::PlanArgs a;
+    rc = prepare_plan(desc, num_qo_heads, page_indptr, page_indices, last_page_len, total_rows,
+                      max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes, a, true);
     if (rc != PKV_OK)
         return rc;
-    if (layer < 0 || layer >= desc.num_layers || batch < 0 || num_qo_heads < 1 ||
-        num_qo_heads > kMaxHeads || desc.num_kv_heads > kMaxHeads ||
-        num_qo_heads % desc.num_kv_heads != 0 || max_q_rows < 1 || !isfinite(sm_scale))
-        return PKV_ERR_BAD_SHAPE;
-    if (!pkv::prefill_supported(desc.head_dim) || batch > 65535 ||
-        2 * page_elems(desc) > (int64_t)UINT32_MAX)
-        return PKV_ERR_UNSUPPORTED;
-    if (batch == 0)
-        return PKV_OK;
-    const bool append = k_new != nullptr || v_new != nullptr;
-    if (!kv_cache || !q || !qo_indptr || !page_indptr || !page_indices || !last_page_len ||
-        !out || (append && (!k_new || !v_new)))
-        return PKV_ERR_NULL_PTR;
-    if (!aligned16(kv_cache) || !aligned16(q) || !aligned16(out) ||
-        (append && (!aligned16(k_new) || !aligned16(v_new))))
-        return PKV_ERR_ALIGNMENT;
-    pkv::PrefillArgs a;
-    uint16_t *slab = static_cast<uint16_t *>(kv_cache) + (int64_t)layer * desc.num_pages * page_elems(desc);
-    a.cache = slab;
-    a.cache_w = append ? slab : nullptr;
-    a.q = static_cast<const uint16_t *>(q);
-    a.k_new = static_cast<const uint16_t *>(k_new);
-    a.v_new = static_cast<const uint16_t *>(v_new);
-    a.out = static_cast<uint16_t *>(out);
-    a.lse = lse;
     a.qo_indptr = qo_indptr;
-    a.indptr = page_indptr;
-    a.indices = page_indices;
-    a.last_len = last_page_len;
-    a.page_stride = page_elems(desc);
-    a.half_stride = desc.page_size * desc.num_kv_heads * desc.head_dim;
-    a.row_stride = desc.num_kv_heads * desc.head_dim;
-    a.num_pages = desc.num_pages;
-    a.page_size = desc.page_size;
-    a.num_qo_heads = num_qo_heads;
-    a.num_kv_heads = desc.num_kv_heads;
-    a.head_dim = desc.head_dim;
-    a.batch = batch;
-    a.max_rows = max_q_rows;
-    const int64_t col_tiles = ((int64_t)max_q_rows * (num_qo_heads / desc.num_kv_heads) + 127) / 128;
-    a.pair_tiles = (int32_t)((col_tiles + 1) / 2);
-    a.skip_single = 0;
-    a.page_shift = 0;
-    while ((1 << a.page_shift) < desc.page_size)
-        ++a.page_shift;
-    a.scale_log2 = sm_scale * 1.4426950408889634f;
-    return hip_status(pkv::launch_prefill(a, stream));
+    a.num_entries = batch;
+    return hip_status(pkv::launch_plan(a, stream));
+}
+
+int pkv_mixed_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *q,
+                  int32_t num_qo_heads, const int32_t *qo_indptr, const void *k_new,
+                  const void *v_new, const int32_t *page_indptr, const int32_t *page_indices,
+                  const int32_t *last_page_len, int32_t batch, int32_t total_rows,
+                  int32_t max_q_rows, float sm_scale, void *out, float *lse,
+                  int32_t max_pages_per_req, int32_t kv_chunk_pages, void *workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+    if (total_rows < 0)
+        return PKV_ERR_BAD_SHAPE;
+    // every host check of both halves first
+    pkv::PrefillArgs pa;
+    bool any = false;
+    int rc = prepare_prefill(kv_cache, desc, layer, q, num_qo_heads, qo_indptr, k_new, v_new,
+                             page_indptr, page_indices, last_page_len, batch, max_q_rows,
+                             sm_scale, out, lse, pa, any);
+    if (rc != PKV_OK || !any || total_rows == 0)
+        return rc;
+    RunLaunch r;
+    rc = prepare_run(kv_cache, desc, layer, k_new, v_new, q, num_qo_heads, total_rows, sm_scale,
+                     out, lse, max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes, r,
+                     true);
+    if (rc != PKV_OK)
+        return rc;
+    rc = launch_run(r, desc, stream);
+    if (rc != PKV_OK)
+        return rc;
+    // the prompts the plan listed; the decode rows went through the run above
+    pa.skip_single = 1;
+    pa.list = r.list;
+    pa.list_sig = r.args.plan_sig;
+    pa.list_cap = r.list_cap;
+    return hip_status(pkv::launch_prefill(pa, stream));
 }
 
 }  // extern "C"

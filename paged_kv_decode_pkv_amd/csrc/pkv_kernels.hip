@@ -281,8 +281,20 @@ struct EntryShape {
     int tiles;  // tiles the decode covers (0: none, or over the page bound)
 };
 
-__device__ __forceinline__ EntryShape entry_shape(const PlanArgs &a, int b) {
+// The shape of planned entry b: with a row -> entry map (a mixed step), b is
+// a row and the shape that of the entry whose single row it is, or empty.
+__device__ __forceinline__ EntryShape entry_shape(const PlanArgs &a, const int *rowent, int b) {
     EntryShape e;
+    if (rowent != nullptr) {
+        b = rowent[b];
+        if (b < 0) {
+            e.p0 = 0;
+            e.n = 0;
+            e.last = 1;
+            e.tiles = 0;
+            return e;
+        }
+    }
     e.p0 = a.indptr[b];
     e.n = a.indptr[b + 1] - e.p0;
     int last = a.last_len[b];
@@ -407,6 +419,44 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
     __shared__ int s_wave[17];
     const bool fixed = a.chunk_tiles > 0;
     int *s_nz = s_start + a.batch + 1;
+    // mixed step: the row -> entry map after the arrays below
+    int *s_rowent = nullptr;
+    if (a.qo_indptr != nullptr) {
+        // past the arrays plan_lds_bytes sizes for the plain plan
+        s_rowent = s_start + (fixed ? 3 * a.batch + 1 + (a.batch <= kRankedBatch ? a.batch : 0)
+                                    : 2 * (a.batch + 1));
+        for (int r = threadIdx.x; r < a.batch; r += blockDim.x)
+            s_rowent[r] = -1;
+        __syncthreads();
+        for (int b = threadIdx.x; b < a.num_entries; b += blockDim.x) {
+            const int r0 = a.qo_indptr[b];
+            if (a.qo_indptr[b + 1] - r0 == 1 && (unsigned)r0 < (unsigned)a.batch)
+                s_rowent[r0] = b;
+        }
+        __syncthreads();
+        if (blockIdx.x == 0) {
+            // the prefill's list: entries with several new rows, in order
+            const int per = (a.num_entries + blockDim.x - 1) / blockDim.x;
+            const int e0 = min(a.num_entries, (int)threadIdx.x * per);
+            const int e1 = min(a.num_entries, e0 + per);
+            int local = 0;
+            for (int b = e0; b < e1; ++b)
+                local += a.qo_indptr[b + 1] - a.qo_indptr[b] > 1;
+            int total = 0;
+            int at = block_exclusive_scan(local, s_wave, total);
+            for (int b = e0; b < e1; ++b)
+                if (a.qo_indptr[b + 1] - a.qo_indptr[b] > 1) {
+                    if (at < a.list_cap)
+                        a.list[2 + at] = b;
+                    ++at;
+                }
+            if (threadIdx.x == 0) {
+                a.list[0] = a.plan_sig;
+                a.list[1] = min(total, a.list_cap);
+            }
+            __syncthreads();   // s_wave is reused
+        }
+    }
     int64_t T = 0;
     const int W = a.num_blocks;
     CostAxis ax{s_start, s_nz, a.batch, 0, 0, 1};
@@ -417,7 +467,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
         const int e1 = min(a.batch, e0 + per);
         int local = 0, localz = 0;
         for (int e = e0; e < e1; ++e) {
-            const int t = entry_shape(a, e).tiles;
+            const int t = entry_shape(a, s_rowent, e).tiles;
             s_start[e] = t;
             local += t;
             localz += t > 0;
@@ -460,7 +510,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
         const int e1 = min(a.batch, e0 + per);
         int local = 0, localp = 0;
         for (int e = e0; e < e1; ++e) {
-            const int t = entry_shape(a, e).tiles;
+            const int t = entry_shape(a, s_rowent, e).tiles;
             const int fl = t / a.chunk_tiles, ps = t - fl * a.chunk_tiles;
             s_start[e] = fl;
             if (ranked)
@@ -481,7 +531,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
             s_start[a.batch] = totf;
         __syncthreads();
         for (int e = e0; e < e1; ++e) {
-            const int t = entry_shape(a, e).tiles;
+            const int t = entry_shape(a, s_rowent, e).tiles;
             const int ps = t - (s_start[e + 1] - s_start[e]) * a.chunk_tiles;
             if (ps <= 0)
                 continue;
@@ -512,7 +562,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
 
     for (int64_t bb = tid; bb < a.batch; bb += nth) {
         const int b = (int)bb;
-        const EntryShape e = entry_shape(a, b);
+        const EntryShape e = entry_shape(a, s_rowent, b);
         int4 d = make_int4(0, 0, 0, 0);
         if (e.n > a.max_pages) {
             // over the bound: no tiles; the decode writes NaN rows and, when
@@ -581,7 +631,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
         bool seg_first, seg_last;
         if (fixed) {
             const int t = k - ct0;   // tile within the chunk
-            e = entry_shape(a, b);
+            e = entry_shape(a, s_rowent, b);
             lt = kc * a.chunk_tiles + t;
             seg_first = t == 0;
             seg_last = t == ctiles - 1;
@@ -590,7 +640,7 @@ __global__ __launch_bounds__(256) void plan_kernel(PlanArgs a) {
         } else {
             const int64_t gk = g0 + k;
             b = entry_of(s_start, a.batch - 1, gk);
-            e = entry_shape(a, b);
+            e = entry_shape(a, s_rowent, b);
             s0 = s_start[b];
             lt = (int)(gk - s0);
             seg_first = gk == (g0 > s0 ? g0 : s0);
@@ -1858,6 +1908,15 @@ hipError_t static_scratch(void **ptr) {
     return hipSuccess;
 }
 
+hipError_t compute_units(int *cus) {
+    int dev = 0;
+    DeviceFacts f;
+    const hipError_t err = device_facts(&dev, &f);
+    if (err == hipSuccess)
+        *cus = f.cus;
+    return err;
+}
+
 hipError_t launch_append(const AppendArgs &a, int batch, hipStream_t stream) {
     AppendArgs args = a;
     void *params[] = {&args};
@@ -1906,7 +1965,7 @@ hipError_t launch_plan(const PlanArgs &a, hipStream_t stream) {
     const int64_t work = items > other ? items : other;
     int64_t grid = (work + 255) / 256;
     grid = grid < 1 ? 1 : (grid > 1024 ? 1024 : grid);
-    const size_t lds = plan_lds_bytes(a.batch, a.chunk_tiles > 0);
+    const size_t lds = plan_lds_bytes(a.batch, a.chunk_tiles > 0, a.qo_indptr != nullptr);
     int dev = 0;
     DeviceFacts f;
     hipError_t err = device_facts(&dev, &f);

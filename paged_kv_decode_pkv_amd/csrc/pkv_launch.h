@@ -74,6 +74,16 @@ struct PlanArgs {
     int32_t chunk_tiles;      // fixed mode: tiles per chunk; 0 = balanced
     int32_t max_chunks;       // fixed mode: chunks per entry
     int32_t max_pages;        // entries listing more pages are poisoned
+    // Mixed step (qo_indptr non-null): `batch` counts rows, and row r is
+    // planned as the entry b whose single new row it is (qo_indptr[b] = r,
+    // qo_indptr[b + 1] = r + 1); the rows of entries with several new rows
+    // get no tiles.  num_entries entries; the page table is indexed by b.
+    const int32_t *qo_indptr;
+    int32_t num_entries;
+    // and the entries with several new rows, for the prefill half:
+    // {plan_sig, count, entry ids in order}, at most list_cap ids
+    int32_t *list;
+    int32_t list_cap;
 };
 
 struct RunArgs {
@@ -121,11 +131,11 @@ constexpr int kMaxPlanBatch = 8192;
 constexpr int kRankedBatch = 256;
 
 // Dynamic LDS bytes of the plan kernel.
-inline size_t plan_lds_bytes(int batch, bool fixed) {
+inline size_t plan_lds_bytes(int batch, bool fixed, bool mixed = false) {
     const size_t b = (size_t)batch;
-    if (!fixed)
-        return 2 * sizeof(int) * (b + 1);
-    return sizeof(int) * ((b + 1) + 2 * b + (batch <= kRankedBatch ? b : 0));
+    const size_t base = !fixed ? 2 * sizeof(int) * (b + 1)
+                               : sizeof(int) * ((b + 1) + 2 * b + (batch <= kRankedBatch ? b : 0));
+    return base + (mixed ? sizeof(int) * b : 0);   // mixed: the row -> entry map
 }
 constexpr int kMaxChunkPages = 1 << 16;
 // Upper bounds for sizing workspace without a device query.
@@ -253,7 +263,16 @@ struct PrefillArgs {
     int32_t skip_single;      // 1: entries with one new row are left to the decode
     int32_t page_shift;       // log2(page_size)
     float scale_log2;         // sm_scale * log2(e)
+    // Mixed step (non-null): the entries to compute, as a mixed plan wrote
+    // them: {signature, count, entry ids...}, at most list_cap ids; a list
+    // whose signature is not list_sig is ignored.
+    const int32_t *list;
+    int32_t list_sig;
+    int32_t list_cap;
 };
+
+// Compute units of the current device (queried once per device).
+hipError_t compute_units(int *cus);
 
 // True when the prefill kernels are built for head_dim.
 bool prefill_supported(int head_dim);

@@ -127,25 +127,6 @@ __device__ __forceinline__ void copy16_to_lds(const void *src, uint32_t lds) {
 __device__ __forceinline__ void copy16_to_lds_s(const void *base, uint32_t off, uint32_t lds) {
     asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
-// A 16-byte store to a wave-uniform base plus a per-lane byte offset.
-__device__ __forceinline__ void store16_s(void *base, uint32_t off, uint4 v) {
-    const u32x4_t d = {v.x, v.y, v.z, v.w};
-    asm volatile("global_store_dwordx4 %0, %1, %2" ::"v"(off), "v"(d), "s"(base) : "memory");
-}
-
-// s_waitcnt vmcnt(min(n, N)) for a wave-uniform n >= 0 (the count is an
-// immediate: a chain of scalar compares picks it).
-template <int N>
-__device__ __forceinline__ void wait_vm_at_most(int n) {
-    if constexpr (N == 0) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    } else {
-        if (n >= N)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
-        else
-            wait_vm_at_most<N - 1>(n);
-    }
-}
 
 // two fp32 -> two bf16 (round to nearest even), packed low-first: one
 // v_cvt_pk_bf16_f32 on gfx950
@@ -178,21 +159,15 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
 
 // ---------------------------------------------------------------------------
 // Causal attention of the new rows (and their append); see the file comment.
+// One work item: the column tile pair kk of entry b at KV head h, taken by
+// the whole workgroup (every wave returns from it; the exits are uniform).
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
+__device__ __forceinline__ void tile_pair(const PrefillArgs &a, const int b, const int h,
+                                          const int kk) {
     using Gm = Geo<D>;
     constexpr int DC = Gm::DC, DB = Gm::DB, CPR = Gm::CPR, RPC = Gm::RPC, CPW = Gm::CPW;
     constexpr int RB = 2 * D;   // bytes per row in LDS
     __shared__ __attribute__((aligned(1024))) char smem[Gm::LDS];
-
-    // workgroup -> (entry, KV head, pair k): blocks congruent mod 8 share an
-    // XCD, and each XCD takes a contiguous run of the linear order
-    const int nb = gridDim.x;
-    const int xcd = blockIdx.x & 7;
-    const int lin = xcd * (nb >> 3) + min(xcd, nb & 7) + (blockIdx.x >> 3);
-    const int pair = lin / a.pair_tiles;
-    const int kk = lin - pair * a.pair_tiles;
-    const int b = pair / a.num_kv_heads, h = pair - b * a.num_kv_heads;
     const int G = a.num_qo_heads / a.num_kv_heads;
 
     const int r0 = a.qo_indptr[b];
@@ -234,7 +209,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     // B merges A's partial when A walked part of B's column tile
     const bool merge = jl < jh ? nA2 > 0 : nA1 > 0;
     const int lenA = nA1 + nA2;
-    const int steps = max(lenA, nB);
 
     const int tid = threadIdx.x;
     // wave-uniform by construction; readfirstlane lets the compiler know it,
@@ -782,6 +756,51 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     finalize();
 }
 
+// A workgroup per (entry, KV head, pair k): blocks congruent mod 8 share an
+// XCD, and each XCD takes a contiguous run of the linear order.
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
+    const int nb = gridDim.x;
+    const int xcd = blockIdx.x & 7;
+    const int lin = xcd * (nb >> 3) + min(xcd, nb & 7) + (blockIdx.x >> 3);
+    const int pair = lin / a.pair_tiles;
+    const int kk = lin - pair * a.pair_tiles;
+    const int b = pair / a.num_kv_heads;
+    tile_pair<D>(a, b, pair - b * a.num_kv_heads, kk);
+}
+
+// Mixed step: only the entries the plan listed (those with several new
+// rows), so the decode rows cost no workgroups.  A grid of whole XCD rounds
+// walks the items: (entry, KV head) unit u goes to XCD u % 8, its pairs one
+// after another on that XCD (they share the unit's keys and values in its
+// L2).  A list of another plan (its signature differs) computes nothing.
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void prefill_list_kernel(PrefillArgs a) {
+    const int32_t *list = a.list;
+    if (list[0] != a.list_sig)
+        return;
+    const int count = list[1];
+    if (count < 0 || count > a.list_cap)
+        return;
+    const int64_t units = (int64_t)count * a.num_kv_heads;
+    const int x = blockIdx.x & 7;
+    for (int64_t j = blockIdx.x >> 3;; j += gridDim.x >> 3) {
+        const int64_t grp = j / a.pair_tiles;
+        const int64_t u = 8 * grp + x;
+        if (u >= units)
+            break;   // later items of this workgroup lie further on
+        const int e = (int)(u / a.num_kv_heads);
+        const int b = list[2 + e];
+        if ((unsigned)b < (unsigned)a.batch)
+            tile_pair<D>(a, b, (int)(u - (int64_t)e * a.num_kv_heads),
+                         (int)(j - grp * a.pair_tiles));
+        // the next item reuses the LDS: every copy has landed and every wave
+        // has read its last operands
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+    }
+}
+
 }  // namespace
 
 bool prefill_supported(int head_dim) { return head_dim == 64 || head_dim == 128; }
@@ -795,6 +814,18 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
         return hipErrorInvalidValue;
     PrefillArgs args = a;
     void *params[] = {&args};
+    if (a.list != nullptr) {
+        // one workgroup per compute unit (the LDS holds one), whole XCD rounds
+        int cus = 0;
+        const hipError_t err = compute_units(&cus);
+        if (err != hipSuccess)
+            return err;
+        const unsigned grid = cus >= 16 ? (unsigned)(cus & ~7) : 8u;
+        const void *k = a.head_dim == 128
+                            ? reinterpret_cast<const void *>(&prefill_list_kernel<128>)
+                            : reinterpret_cast<const void *>(&prefill_list_kernel<64>);
+        return hipLaunchKernel(k, dim3(grid), dim3(kThreads), params, 0, stream);
+    }
     const void *k = a.head_dim == 128 ? reinterpret_cast<const void *>(&prefill_kernel<128>)
                                       : reinterpret_cast<const void *>(&prefill_kernel<64>);
     return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(kThreads), params, 0, stream);

@@ -24,6 +24,7 @@ def test_every_declared_symbol_is_exported():
                           "pkv_decode_workspace_size",
                           "pkv_append_decode", "pkv_decode", "pkv_plan", "pkv_run",
                           "pkv_run_qk_norm_rope", "pkv_decode_static",
+                          "pkv_plan_mixed", "pkv_mixed_run",
                           "pkv_validate_page_table", "pkv_status_string",
                           "pkv_last_hip_error"}
     for n in names:
@@ -213,6 +214,41 @@ def test_run_validation(kw, code):
 def test_plan_and_run_batch_zero_are_noops():
     assert _plan(batch=0, tables=(NULL, NULL, NULL)) == 0
     assert _run(batch=0, q=NULL, out=NULL) == 0
+
+
+def _plan_mixed(hq=4, qo=FAKE, batch=3, rows=5, maxp=4, chunk=0, ws=NULL, wsb=0,
+                tables=(FAKE, FAKE, FAKE)):
+    return lib.pkv_plan_mixed(DESC, hq, qo, *tables, batch, rows, maxp, chunk, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(rows=-1), -2), (dict(hq=3), -2), (dict(maxp=0), -2),
+    (dict(batch=70000), -3), (dict(rows=9000), -3), (dict(qo=NULL), -1),
+    (dict(tables=(FAKE, NULL, FAKE)), -1), (dict(), -4),
+])
+def test_plan_mixed_validation(kw, code):
+    assert _plan_mixed(**kw) == code
+
+
+def _mixed_run(layer=0, q=FAKE, hq=4, qo=FAKE, k=FAKE, v=FAKE, batch=3, rows=5, maxr=4,
+               scale=0.125, out=FAKE, chunk=0, ws=NULL, wsb=0):
+    return lib.pkv_mixed_run(FAKE, DESC, layer, q, hq, qo, k, v, FAKE, FAKE, FAKE, batch,
+                             rows, maxr, scale, out, NULL, 4, chunk, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layer=2), -2), (dict(rows=-1), -2), (dict(hq=3), -2), (dict(maxr=0), -2),
+    (dict(scale=float("inf")), -2), (dict(qo=NULL), -1), (dict(q=NULL), -1),
+    (dict(k=NULL), -1), (dict(out=ctypes.c_void_p(0x100004)), -6),
+    (dict(), -4),                                  # the decode rows need their plan
+])
+def test_mixed_run_validation(kw, code):
+    assert _mixed_run(**kw) == code
+
+
+def test_mixed_batch_zero_is_noop():
+    assert _plan_mixed(batch=0, rows=0, qo=NULL, tables=(NULL, NULL, NULL)) == 0
+    assert _mixed_run(batch=0, rows=0, q=NULL, qo=NULL, k=NULL, v=NULL, out=NULL) == 0
 
 
 def test_validate_page_table():

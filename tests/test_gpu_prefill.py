@@ -174,3 +174,83 @@ def test_prefill_rows_past_max_rows():
             page = table.indices[table.indptr[e] + pos // 16]
             want[1, page, :, pos % 16] = full[1, page, :, pos % 16]
     np.testing.assert_array_equal(to_host_u16(cache_dev), want)
+
+
+# One-call mixed step (pkv_plan_mixed + pkv_mixed_run): decode rows (entries
+# with one new row) through the decode's balanced or fixed-run schedule, so a
+# long decode row is split over workgroups and merged; prompts through the
+# prefill.  Decode rows are held to the decode bars, prompt rows to the
+# prefill bars above, the cache bit for bit.
+MIXED = [
+    # seed, hq, hkv, ps, lengths, rows per entry, fixed run pages (0 balanced)
+    (21, 32, 8, 16, [9000, 600, 33, 64, 1, 40], [1, 512, 1, 64, 1, 0], 0),
+    (22, 32, 8, 16, [9000, 600, 33, 64, 1, 40], [1, 512, 1, 64, 1, 0], 16),
+    (23, 16, 2, 128, [20000, 300, 129, 5000], [1, 200, 1, 1], 0),         # G 8
+    (24, 8, 8, 1, [3000, 50, 7], [1, 50, 1], 0),                          # G 1, 1-token pages
+    (25, 24, 8, 16, [4000, 3000, 2000, 100], [1, 1, 1, 100], 32),         # G 3, fixed
+]
+
+
+def _mixed(table, cache, qo, q, kn, vn, scale, chunk, append=True, layer=1):
+    cache_dev = to_dev_u16(cache)
+    tabs = table_to_dev(table)
+    qo_dev = torch.from_numpy(qo).to(DEV)
+    rows = int(qo[-1])
+    maxr = int(np.max(np.diff(qo)))
+    pl = pkv.plan_mixed(cache_dev, q.shape[1], qo_dev, *tabs, rows, table.max_pages_per_req,
+                        chunk)
+    out, lse = pkv.mixed_run(cache_dev, layer, to_dev_u16(q), *tabs, pl, scale, max(maxr, 1),
+                             k_new=to_dev_u16(kn) if append else None,
+                             v_new=to_dev_u16(vn) if append else None)
+    torch.cuda.synchronize()
+    return cache_dev, out, lse
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("case", MIXED, ids=[f"m{c[0]}" for c in MIXED])
+def test_mixed_step_matches_oracle(case, d):
+    seed, hq, hkv, ps, lengths, nrows, chunk = case
+    print(f"mixed case {case} head_dim {d}", flush=True)
+    table, cache, qo, q, kn, vn = _case(seed, hq, hkv, ps, lengths, nrows, d=d)
+    scale = 1.0 / np.sqrt(d)
+    cache_dev, out, lse = _mixed(table, cache, qo, q, kn, vn, scale, chunk)
+    host = cache.copy()
+    oracle.append_rows(host, 1, kn, vn, qo, table.indptr, table.indices, table.last_len)
+    ro, rl = oracle.prefill(host, 1, q, qo, table.indptr, table.indices, table.last_len, scale)
+    np.testing.assert_array_equal(to_host_u16(cache_dev), host, err_msg="append")
+    n = np.diff(qo)
+    single = qo[:-1][n == 1]
+    multi = np.concatenate([np.arange(qo[e], qo[e + 1]) for e in range(len(n)) if n[e] > 1])
+    compare(out, lse, ro[single], rl[single], rows=single, what="decode rows")
+    idx = torch.from_numpy(multi).to(DEV)
+    check_rows(out[idx], lse[idx], ro[multi], rl[multi], what="prompt rows")
+
+
+def test_mixed_step_of_decode_rows_is_the_decode():
+    # every entry one new row: the mixed plan is the decode's plan and the
+    # results match pkv_plan + pkv_run bit for bit
+    table, cache, qo, q, kn, vn = _case(26, 32, 8, 16, [7000, 12, 900, 1, 300], [1] * 5)
+    scale = 1.0 / np.sqrt(D)
+    for chunk in (0, 16):
+        cache_dev, out, lse = _mixed(table, cache, qo, q, kn, vn, scale, chunk)
+        c2 = to_dev_u16(cache)
+        tabs = table_to_dev(table)
+        pl = pkv.plan(c2, 32, *tabs, table.max_pages_per_req, chunk)
+        o2, l2 = pkv.run(c2, 1, to_dev_u16(q), pl, scale, k_new=to_dev_u16(kn),
+                         v_new=to_dev_u16(vn))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_host_u16(cache_dev), to_host_u16(c2))
+        np.testing.assert_array_equal(to_host_u16(out), to_host_u16(o2))
+        assert torch.equal(lse, l2)
+
+
+def test_mixed_step_of_prompts_is_the_prefill():
+    # no entry with one new row: the decode half has no tiles and the results
+    # match pkv_prefill bit for bit
+    table, cache, qo, q, kn, vn = _case(27, 16, 4, 16, [300, 45, 64], [200, 45, 2])
+    scale = 0.1
+    cache_dev, out, lse = _mixed(table, cache, qo, q, kn, vn, scale, 0)
+    c2, o2, l2, host, ro, rl = _run(table, cache, qo, q, kn, vn, scale)
+    np.testing.assert_array_equal(to_host_u16(cache_dev), to_host_u16(c2))
+    np.testing.assert_array_equal(to_host_u16(out), to_host_u16(o2))
+    assert torch.equal(lse, l2)
