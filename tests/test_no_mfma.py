@@ -72,4 +72,40 @@ def test_matrix_cores_only_in_prefill(tmp_path):
     for kernel in ("run_kernel", "plan_kernel", "append_kernel", "norm_rope_kernel"):
         assert any(kernel in n for n in names), f"{kernel} not found"
     with_mfma = {n: c for n, c in counts.items() if c}
-    assert with_mfma and all("prefill_kernel" in n for n in with_mfma), with_mfma
+    assert with_mfma and all("prefill_kernel" in n or "prefill_list_kernel" in n
+                             for n in with_mfma), with_mfma
+
+
+def _scratch_by_kernel(asm: str) -> dict:
+    counts, current = {}, None
+    for line in asm.splitlines():
+        m = re.match(r"^[0-9a-f]+ <(.+)>:$", line)
+        if m:
+            current = m.group(1)
+            counts.setdefault(current, 0)
+        elif current is not None and "scratch_" in line:
+            counts[current] += 1
+    return counts
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+@pytest.mark.skipif(not os.path.exists(OBJDUMP), reason="ROCm llvm-objdump missing")
+def test_decode_kernels_use_no_scratch(tmp_path):
+    # The decode waits for its own direct-to-LDS copies by counting them; a
+    # scratch access in its loop would make the compiler wait for every
+    # outstanding copy (about a third of the streaming rate lost), so the
+    # decode kernels of head_dim 64 and of head_dim 128 with up to 4 query
+    # heads per KV head (every shape the workloads run) keep all their state in
+    # registers.
+    counts = {}
+    for i, code in enumerate(_gfx950_code_objects(open(LIB, "rb").read())):
+        co = tmp_path / f"pkv_gfx950_{i}.co"
+        co.write_bytes(code)
+        asm = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", str(co)], capture_output=True,
+                             text=True, check=True).stdout
+        for k, v in _scratch_by_kernel(asm).items():
+            counts[k] = counts.get(k, 0) + v
+    shapes = re.compile(r"run_kernelILi(64ELi[1-8]|128ELi[1-4])ELi")
+    checked = {n: c for n, c in counts.items() if shapes.search(n)}
+    assert len(checked) >= 12, sorted(counts)
+    assert not any(checked.values()), {n: c for n, c in checked.items() if c}
