@@ -61,7 +61,8 @@ def parse():
                     help="per layer the fused q/k RMSNorm + rotary + KV write, then a "
                          "decode-only pkv_run on its q")
     ap.add_argument("--mrope", action="store_true",
-                    help="with --qk-norm-rope: multimodal RoPE (positions (L-1, (L-1)/2, "
+                    help="with --qk-norm-rope or --fused-norm-rope: multimodal RoPE "
+                         "(positions (L-1, (L-1)/2, "
                          "(L-1)/3), contiguous 24:20:20 bands of pairs)")
     ap.add_argument("--fused-norm-rope", action="store_true",
                     help="per layer one pkv_run_qk_norm_rope: the decode with the append "
@@ -182,8 +183,8 @@ def main():
               "pos": torch.from_numpy((table.lengths - 1).astype(np.int32)).to(dev),
               "qo": torch.empty_like(Q), "eps": 1e-6, "theta": 1e6}
         if args.mrope:
-            if not args.qk_norm_rope:
-                raise SystemExit("--mrope goes with --qk-norm-rope")
+            if not (args.qk_norm_rope or args.fused_norm_rope):
+                raise SystemExit("--mrope goes with --qk-norm-rope or --fused-norm-rope")
             last = (table.lengths - 1).astype(np.int32)
             nr["pos3"] = torch.from_numpy(
                 np.stack([last, last // 2, last // 3], axis=1).astype(np.int32)).to(dev)
@@ -219,11 +220,17 @@ def main():
                    vp(lse[layer].data_ptr()), maxp, chunk, *ws_args, s)
             cl = []
             if args.fused_norm_rope:
-                cl.append((pkv.lib.pkv_run_qk_norm_rope,
-                           (vp(cache.data_ptr()), desc, layer, kn, vn, *qo, b,
-                            vp(nr["qw"][layer].data_ptr()), vp(nr["kw"][layer].data_ptr()),
-                            ctypes.c_float(nr["eps"]), ctypes.c_float(nr["theta"]),
-                            vp(nr["pos"].data_ptr()), *res), "pkv_run_qk_norm_rope"))
+                head = (vp(cache.data_ptr()), desc, layer, kn, vn, *qo, b,
+                        vp(nr["qw"][layer].data_ptr()), vp(nr["kw"][layer].data_ptr()),
+                        ctypes.c_float(nr["eps"]), ctypes.c_float(nr["theta"]))
+                if "axis" in nr:
+                    cl.append((pkv.lib.pkv_run_qk_norm_mrope,
+                               (*head, vp(nr["pos3"].data_ptr()),
+                                nr["axis"].ctypes.data_as(vp), *res), "pkv_run_qk_norm_mrope"))
+                else:
+                    cl.append((pkv.lib.pkv_run_qk_norm_rope,
+                               (*head, vp(nr["pos"].data_ptr()), *res),
+                               "pkv_run_qk_norm_rope"))
             elif args.qk_norm_rope:
                 qo = (vp(nr["qo"][layer].data_ptr()), hq)
                 head = (vp(cache.data_ptr()), desc, layer, vp(Q[layer].data_ptr()), hq, kn,
@@ -257,7 +264,9 @@ def main():
             layers.append(cl)
         return plan, layers
 
-    if args.fused_norm_rope:
+    if args.fused_norm_rope and args.mrope:
+        call_name = "pkv_run_qk_norm_mrope (norm + multimodal rotary + append + decode)"
+    elif args.fused_norm_rope:
         call_name = "pkv_run_qk_norm_rope (norm + rotary + append + decode)"
     elif args.qk_norm_rope and args.mrope:
         call_name = "pkv_qk_norm_mrope_append + pkv_run"

@@ -331,6 +331,30 @@ int pkv_run_qk_norm_rope(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
                          hipStream_t stream);
 
 /*
+ * pkv_run_qk_norm_mrope -- pkv_run_qk_norm_rope with multimodal RoPE, the
+ * Qwen3-Omni Thinker's variant ("Supported Models", Qwen3-Omni notes: q/k
+ * RMSNorm and multimodal RoPE with the KV write in one kernel): entry b has
+ * a (t, h, w) position and rotary pair i (elements i and i + D/2) turns by
+ *   a_i = positions[b, pair_axis[i]] * rope_theta^(-2i/D)
+ * as in pkv_qk_norm_mrope_append, but folded into the decode launch like
+ * pkv_run_qk_norm_rope.  With t = h = w it gives exactly
+ * pkv_run_qk_norm_rope's result.
+ *  positions   int32 [batch, 3], device, row-major (t, h, w).
+ *  pair_axis   uint8 [head_dim / 2], HOST, each 0, 1 or 2 (else
+ *              PKV_ERR_BAD_SHAPE; NULL: PKV_ERR_NULL_PTR).  Read during the
+ *              call only.
+ *  every other argument, and what is supported, as for pkv_run_qk_norm_rope.
+ */
+int pkv_run_qk_norm_mrope(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+                          const void *k_new, const void *v_new, const void *q,
+                          int32_t num_qo_heads, int32_t batch, const void *q_norm_weight,
+                          const void *k_norm_weight, float eps, float rope_theta,
+                          const int32_t *positions, const uint8_t *pair_axis, float sm_scale,
+                          void *out, float *lse, int32_t max_pages_per_req,
+                          int32_t kv_chunk_pages, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
  * pkv_decode -- grouped-query attention of one query row per entry over its
  * pages ("Adding a Model", section 1: run(q, kv_cache); "How a program
  * runs": lm_decode is one row per request).

@@ -113,6 +113,9 @@ def _load():
     lib.pkv_run_qk_norm_rope.argtypes = [p, CacheDesc, i32, p, p, p, i32, i32, p, p, f32, f32,
                                          p, f32, p, p, i32, i32, p, sz, p]
     lib.pkv_run_qk_norm_rope.restype = ctypes.c_int
+    lib.pkv_run_qk_norm_mrope.argtypes = [p, CacheDesc, i32, p, p, p, i32, i32, p, p, f32, f32,
+                                          p, p, f32, p, p, i32, i32, p, sz, p]
+    lib.pkv_run_qk_norm_mrope.restype = ctypes.c_int
     lib.pkv_plan_mixed.argtypes = [CacheDesc, i32, p, p, p, p, i32, i32, i32, i32, p, sz, p]
     lib.pkv_plan_mixed.restype = ctypes.c_int
     lib.pkv_mixed_run.argtypes = [p, CacheDesc, i32, p, i32, p, p, p, p, p, p, i32, i32, i32,
@@ -591,10 +594,12 @@ def mixed_run(kv_cache, layer: int, q, page_indptr, page_indices, last_page_len,
 def run_qk_norm_rope(kv_cache, layer: int, q, plan_: DecodePlan, sm_scale: float, k_new,
                      v_new, q_norm_weight, k_norm_weight, positions, eps: float = 1e-6,
                      rope_theta: float = 1e6, out=None, lse=None, with_lse: bool = True,
-                     stream=None):
+                     stream=None, pair_axis=None):
     """Decode one layer on a plan with the append and the q/k RMSNorm + rotary
     embedding folded in (pkv_run_qk_norm_rope): q, k_new are the raw
-    projections; returns (out, lse)."""
+    projections; returns (out, lse).  With pair_axis (a host sequence of
+    head_dim/2 values in {0, 1, 2}) the rotary embedding is multimodal
+    (pkv_run_qk_norm_mrope) and positions is [batch, 3] (t, h, w)."""
     import torch
     desc = cache_desc(kv_cache)
     batch, hq, d = plan_.batch, plan_.num_qo_heads, desc.head_dim
@@ -606,7 +611,14 @@ def run_qk_norm_rope(kv_cache, layer: int, q, plan_: DecodePlan, sm_scale: float
     for name, t in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
         if tuple(t.shape) != (d,):
             raise ValueError(f"{name} must be [{d}], got {tuple(t.shape)}")
-    if tuple(positions.shape) != (batch,):
+    multimodal = pair_axis is not None
+    if multimodal:
+        axis = np.ascontiguousarray(pair_axis, dtype=np.uint8)
+        if axis.shape != (d // 2,):
+            raise ValueError(f"pair_axis must hold {d // 2} values")
+        if tuple(positions.shape) != (batch, 3):
+            raise ValueError(f"positions must be [batch, 3], got {tuple(positions.shape)}")
+    elif tuple(positions.shape) != (batch,):
         raise ValueError(f"positions must be [batch], got {tuple(positions.shape)}")
     dev = kv_cache.device
     if out is None:
@@ -615,21 +627,26 @@ def run_qk_norm_rope(kv_cache, layer: int, q, plan_: DecodePlan, sm_scale: float
         lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
     null = ctypes.c_void_p(0)
     ws = plan_.workspace
-    rc = lib.pkv_run_qk_norm_rope(
-        _dev_ptr(kv_cache, "kv_cache", torch.bfloat16), desc, int(layer),
-        _dev_ptr(k_new, "k_new", torch.bfloat16, dev),
-        _dev_ptr(v_new, "v_new", torch.bfloat16, dev),
-        _dev_ptr(q, "q", torch.bfloat16, dev), hq, batch,
-        _dev_ptr(q_norm_weight, "q_norm_weight", torch.bfloat16, dev),
-        _dev_ptr(k_norm_weight, "k_norm_weight", torch.bfloat16, dev),
-        float(eps), float(rope_theta), _dev_ptr(positions, "positions", torch.int32, dev),
-        float(sm_scale), _dev_ptr(out, "out", torch.bfloat16, dev),
-        null if lse is None else _dev_ptr(lse, "lse", torch.float32, dev),
-        plan_.max_pages_per_req, plan_.kv_chunk_pages,
-        _dev_ptr(ws, "workspace", device=dev), ws.numel() * ws.element_size(),
-        _stream(stream))
+    head = (_dev_ptr(kv_cache, "kv_cache", torch.bfloat16), desc, int(layer),
+            _dev_ptr(k_new, "k_new", torch.bfloat16, dev),
+            _dev_ptr(v_new, "v_new", torch.bfloat16, dev),
+            _dev_ptr(q, "q", torch.bfloat16, dev), hq, batch,
+            _dev_ptr(q_norm_weight, "q_norm_weight", torch.bfloat16, dev),
+            _dev_ptr(k_norm_weight, "k_norm_weight", torch.bfloat16, dev),
+            float(eps), float(rope_theta), _dev_ptr(positions, "positions", torch.int32, dev))
+    tail = (float(sm_scale), _dev_ptr(out, "out", torch.bfloat16, dev),
+            null if lse is None else _dev_ptr(lse, "lse", torch.float32, dev),
+            plan_.max_pages_per_req, plan_.kv_chunk_pages,
+            _dev_ptr(ws, "workspace", device=dev), ws.numel() * ws.element_size(),
+            _stream(stream))
+    if multimodal:
+        name = "pkv_run_qk_norm_mrope"
+        rc = lib.pkv_run_qk_norm_mrope(*head, axis.ctypes.data_as(ctypes.c_void_p), *tail)
+    else:
+        name = "pkv_run_qk_norm_rope"
+        rc = lib.pkv_run_qk_norm_rope(*head, *tail)
     if rc != PKV_OK:
-        raise PkvError(rc, "pkv_run_qk_norm_rope")
+        raise PkvError(rc, name)
     return out, lse
 
 

@@ -285,6 +285,8 @@ int prepare_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void
     a.q_w = nullptr;
     a.k_w = nullptr;
     a.positions = nullptr;
+    a.pos_stride = 1;
+    a.axis_bits[0] = a.axis_bits[1] = a.axis_bits[2] = a.axis_bits[3] = 0;
     a.eps = 0.f;
     a.log2_theta = 0.0;
     r.blocks = reinterpret_cast<const int32_t *>(ws + lay.off_blocks);
@@ -329,6 +331,58 @@ int plan_and_run(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const voi
     rc = hip_status(pkv::launch_plan(pa, stream));
     if (rc != PKV_OK)
         return rc;
+    return launch_run(r, desc, stream);
+}
+
+
+// pkv_run_qk_norm_rope and its multimodal variant (pair_axis read on the
+// host: the component each rotary pair follows).
+int run_norm_rope(void *kv_cache, pkv_cache_desc_t desc, int32_t layer, const void *k_new,
+                  const void *v_new, const void *q, int32_t num_qo_heads, int32_t batch,
+                  const void *q_norm_weight, const void *k_norm_weight, float eps,
+                  float rope_theta, const int32_t *positions, const uint8_t *pair_axis,
+                  bool multimodal, float sm_scale, void *out, float *lse,
+                  int32_t max_pages_per_req, int32_t kv_chunk_pages, void *workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_decode_args(desc, layer, num_qo_heads, batch, sm_scale, max_pages_per_req,
+                               kv_chunk_pages);
+    if (rc != PKV_OK)
+        return rc;
+    if (!(eps >= 0.0f) || !isfinite(eps) || !(rope_theta > 0.0f) || !isfinite(rope_theta))
+        return PKV_ERR_BAD_SHAPE;
+    if (!pkv::run_norm_rope_supported(desc.head_dim, num_qo_heads / desc.num_kv_heads))
+        return PKV_ERR_UNSUPPORTED;
+    uint32_t axis_bits[4] = {0, 0, 0, 0};
+    if (multimodal) {
+        if (!pair_axis)
+            return PKV_ERR_NULL_PTR;
+        for (int i = 0; i < desc.head_dim / 2; ++i) {
+            if (pair_axis[i] > 2)
+                return PKV_ERR_BAD_SHAPE;
+            axis_bits[i / 16] |= (uint32_t)pair_axis[i] << (2 * (i % 16));
+        }
+    }
+    if (batch == 0)
+        return PKV_OK;
+    if (!k_new || !v_new || !q_norm_weight || !k_norm_weight || !positions)
+        return PKV_ERR_NULL_PTR;
+    if (!aligned16(q_norm_weight) || !aligned16(k_norm_weight))
+        return PKV_ERR_ALIGNMENT;
+    RunLaunch r;
+    rc = prepare_run(kv_cache, desc, layer, k_new, v_new, q, num_qo_heads, batch, sm_scale,
+                     out, lse, max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes,
+                     r);
+    if (rc != PKV_OK)
+        return rc;
+    pkv::RunArgs &a = r.args;
+    a.q_w = static_cast<const uint16_t *>(q_norm_weight);
+    a.k_w = static_cast<const uint16_t *>(k_norm_weight);
+    a.positions = positions;
+    a.eps = eps;
+    a.log2_theta = log2((double)rope_theta);
+    a.pos_stride = multimodal ? 3 : 1;
+    for (int i = 0; i < 4; ++i)
+        a.axis_bits[i] = axis_bits[i];
     return launch_run(r, desc, stream);
 }
 
@@ -636,33 +690,24 @@ int pkv_run_qk_norm_rope(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
                          const int32_t *positions, float sm_scale, void *out, float *lse,
                          int32_t max_pages_per_req, int32_t kv_chunk_pages, void *workspace,
                          size_t workspace_bytes, hipStream_t stream) {
-    int rc = check_decode_args(desc, layer, num_qo_heads, batch, sm_scale, max_pages_per_req,
-                               kv_chunk_pages);
-    if (rc != PKV_OK)
-        return rc;
-    if (!(eps >= 0.0f) || !isfinite(eps) || !(rope_theta > 0.0f) || !isfinite(rope_theta))
-        return PKV_ERR_BAD_SHAPE;
-    if (!pkv::run_norm_rope_supported(desc.head_dim, num_qo_heads / desc.num_kv_heads))
-        return PKV_ERR_UNSUPPORTED;
-    if (batch == 0)
-        return PKV_OK;
-    if (!k_new || !v_new || !q_norm_weight || !k_norm_weight || !positions)
-        return PKV_ERR_NULL_PTR;
-    if (!aligned16(q_norm_weight) || !aligned16(k_norm_weight))
-        return PKV_ERR_ALIGNMENT;
-    RunLaunch r;
-    rc = prepare_run(kv_cache, desc, layer, k_new, v_new, q, num_qo_heads, batch, sm_scale,
-                     out, lse, max_pages_per_req, kv_chunk_pages, workspace, workspace_bytes,
-                     r);
-    if (rc != PKV_OK)
-        return rc;
-    pkv::RunArgs &a = r.args;
-    a.q_w = static_cast<const uint16_t *>(q_norm_weight);
-    a.k_w = static_cast<const uint16_t *>(k_norm_weight);
-    a.positions = positions;
-    a.eps = eps;
-    a.log2_theta = log2((double)rope_theta);
-    return launch_run(r, desc, stream);
+    return run_norm_rope(kv_cache, desc, layer, k_new, v_new, q, num_qo_heads, batch,
+                         q_norm_weight, k_norm_weight, eps, rope_theta, positions, nullptr,
+                         false, sm_scale, out, lse, max_pages_per_req, kv_chunk_pages,
+                         workspace, workspace_bytes, stream);
+}
+
+int pkv_run_qk_norm_mrope(void *kv_cache, pkv_cache_desc_t desc, int32_t layer,
+                          const void *k_new, const void *v_new, const void *q,
+                          int32_t num_qo_heads, int32_t batch, const void *q_norm_weight,
+                          const void *k_norm_weight, float eps, float rope_theta,
+                          const int32_t *positions, const uint8_t *pair_axis, float sm_scale,
+                          void *out, float *lse, int32_t max_pages_per_req,
+                          int32_t kv_chunk_pages, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    return run_norm_rope(kv_cache, desc, layer, k_new, v_new, q, num_qo_heads, batch,
+                         q_norm_weight, k_norm_weight, eps, rope_theta, positions, pair_axis,
+                         true, sm_scale, out, lse, max_pages_per_req, kv_chunk_pages,
+                         workspace, workspace_bytes, stream);
 }
 
 size_t pkv_decode_workspace_size(pkv_cache_desc_t desc, int32_t num_qo_heads, int32_t batch,

@@ -862,13 +862,19 @@ __device__ __forceinline__ float wave_max(float x, int lane) {
 // rotate-half partner, D/2 away, is in the same lane).  y = x / sqrt(mean(x^2)
 // + eps) * w, then pair i = 8 j + t turns by pos * turns[i] (in turns, reduced
 // in fp64, sine and cosine in fp32); fp32 throughout, rounded to bf16 once.
+// Lane i computes the angle of pair i only and the lanes share the 64 cosines
+// and sines through LDS (the eight row groups need the same ones).
 // The weights and the rates come from LDS: a vector memory load in the tile
 // loop would count in vmcnt behind the tile copies in flight, and waiting for
 // it would drain them.
 //
 // Per-wave LDS block of the fused step: q weight [128] bf16, k weight [128]
-// bf16, rates [64] fp64.
-constexpr int kNormRopeLds = 1024;
+// bf16, the cosines [64] and sines [64] (fp32) of the current segment's
+// angles, then per staging buffer 16 bytes for the position
+// (or the (t, h, w) positions) of the entry whose segment starts in that
+// buffer's tile: they travel with the tile's copies, so the rotation at the
+// segment start waits for no load of its own.
+constexpr int kNormRopeLds = 1024 + 16 * kMaxStageBuffers;
 
 // sin and cos of 2 pi x for |x| <= 1/2 (x in turns): the nearest quarter turn
 // q comes off exactly, the rest r (|r| <= 1/8 turn, |2 pi r| <= pi/4) goes
@@ -892,17 +898,6 @@ __device__ __forceinline__ void sincos_turns(float x, float &s, float &c) {
     const float c1 = (qi & 1) ? sv : cv;
     s = (qi & 2) ? -s1 : s1;                    // q = 2, 3: sin negated
     c = (qi == 1 || qi == 2) ? -c1 : c1;        // q = 1, 2: cos negated
-}
-
-// cos and sin of the lane's eight angles at position pos.
-__device__ __forceinline__ void rope_angles(const char *nrl, int j, double pos, float (&cs)[8],
-                                            float (&sn)[8]) {
-    const double *turns = reinterpret_cast<const double *>(nrl + 512) + 8 * j;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const double tn = pos * turns[t];
-        sincos_turns((float)(tn - rint(tn)), sn[t], cs[t]);
-    }
 }
 
 // One row: RMSNorm with weight row wsel (0: q, 1: k) and the rotation by the
@@ -1007,13 +1002,54 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     // / (2 pi), computed here in fp64.
     const char *nrl = reinterpret_cast<const char *>(smem) + NBUF * buf_bytes +
                       w * kNormRopeLds;
+    // pair `lane`'s rate in turns per position, theta^(-lane/64) / (2 pi)
+    double pair_rate = 0.0;
     if constexpr (NR) {
         const uint32_t nb = lds0 + NBUF * buf_bytes + (uint32_t)(w * kNormRopeLds);
         copy_dword_to_lds(a.q_w + 2 * lane, nb);
         copy_dword_to_lds(a.k_w + 2 * lane, nb + 256);
-        reinterpret_cast<double *>(const_cast<char *>(nrl) + 512)[lane] =
-            exp2(-(double)lane * (a.log2_theta / 64.0)) * 0.15915494309189535;
+        pair_rate = exp2(-(double)lane * (a.log2_theta / 64.0)) * 0.15915494309189535;
     }
+    // The lane's eight rotary angles (pairs 8 j .. 8 j + 7) for positions
+    // p[0..2]: one position per entry (p[0]), or for multimodal RoPE the
+    // (t, h, w) component each pair follows.  Lane i turns pair i (the
+    // component it follows is picked once here, through scalar registers: a
+    // lane-varying index into the argument array would become a memory load)
+    // and the lanes exchange the results through the wave's LDS block.
+    uint32_t pair_axis = 0;
+    if constexpr (NR) {
+        if (a.pos_stride != 1) {
+            const uint32_t w0 = __builtin_amdgcn_readfirstlane(a.axis_bits[0]);
+            const uint32_t w1 = __builtin_amdgcn_readfirstlane(a.axis_bits[1]);
+            const uint32_t w2 = __builtin_amdgcn_readfirstlane(a.axis_bits[2]);
+            const uint32_t w3 = __builtin_amdgcn_readfirstlane(a.axis_bits[3]);
+            const int q4 = lane >> 4;   // word of pairs 16 q4 .. 16 q4 + 15
+            const uint32_t word = q4 == 0 ? w0 : (q4 == 1 ? w1 : (q4 == 2 ? w2 : w3));
+            pair_axis = (word >> (2 * (lane & 15))) & 3u;
+        }
+    }
+    auto angles_at = [&](const int32_t *p, float (&cs)[8], float (&sn)[8]) {
+        const double p0 = (double)p[0];
+        double pp = p0;
+        if (a.pos_stride != 1) {
+            const double p1 = (double)p[1], p2 = (double)p[2];
+            pp = pair_axis == 0 ? p0 : (pair_axis == 1 ? p1 : p2);
+        }
+        const double tn = pp * pair_rate;
+        float sv, cv;
+        sincos_turns((float)(tn - rint(tn)), sv, cv);
+        float *tab = reinterpret_cast<float *>(const_cast<char *>(nrl) + 512);
+        tab[lane] = cv;
+        tab[64 + lane] = sv;
+        const float4 c0 = *reinterpret_cast<const float4 *>(tab + 8 * j);
+        const float4 c1 = *reinterpret_cast<const float4 *>(tab + 8 * j + 4);
+        const float4 s0 = *reinterpret_cast<const float4 *>(tab + 64 + 8 * j);
+        const float4 s1 = *reinterpret_cast<const float4 *>(tab + 64 + 8 * j + 4);
+        cs[0] = c0.x; cs[1] = c0.y; cs[2] = c0.z; cs[3] = c0.w;
+        cs[4] = c1.x; cs[5] = c1.y; cs[6] = c1.z; cs[7] = c1.w;
+        sn[0] = s0.x; sn[1] = s0.y; sn[2] = s0.z; sn[3] = s0.w;
+        sn[4] = s1.x; sn[5] = s1.y; sn[6] = s1.z; sn[7] = s1.w;
+    };
     const __amdgpu_buffer_rsrc_t ro = partial_rsrc(a.part_o, a.part_o_bytes);
     const __amdgpu_buffer_rsrc_t rl = partial_rsrc(a.part_lse, a.part_lse_bytes);
     const int4 *blk = blocks + (int64_t)blockIdx.x * a.block_stride;
@@ -1166,6 +1202,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
         // of ring_ops their number right after the copies of buffer b's tile:
         // a tile has landed once at most ops - ring_ops[b] are outstanding.
         uint32_t ops = 0;
+        float seg_cs[8], seg_sn[8];   // fused norm/rotary: the segment's angles
         int ring_ops = 0;
 
         // This wave's share of the copies of tile `rec` into LDS buffer `buf`:
@@ -1174,7 +1211,9 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
         // from k_new / v_new.
         auto issue = [&](const int4 rec, int buf) {
             const int info = rec.y;
-            ops += ((info & kInfoSegFirst) ? QI : 0) + IPT;
+            // (with the fused norm/rotary, a segment start also copies the
+            // entry's positions: one more operation)
+            ops += ((info & kInfoSegFirst) ? QI + (NR ? 1 : 0) : 0) + IPT;
             if (lane == buf) {
                 ring_x = rec.x;
                 ring_y = rec.y;
@@ -1186,6 +1225,14 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             const int slot0 = (info >> kInfoSlotShift) & kInfoSlotMask;
             const uint32_t bb = lds0 + (uint32_t)buf * buf_bytes;
             if (info & kInfoSegFirst) {
+                if constexpr (NR) {
+                    // the entry's position(s) into this buffer's 16 bytes of
+                    // the wave's norm/rotary block
+                    if (lane < a.pos_stride)
+                        copy_dword_to_lds(positions + (int64_t)rec.z * a.pos_stride + lane,
+                                          lds0 + NBUF * buf_bytes +
+                                              (uint32_t)(w * kNormRopeLds + 1024 + buf * 16));
+                }
                 const char *qs = reinterpret_cast<const char *>(a.q) +
                                  ((int64_t)rec.z * a.num_qo_heads + hq0) * D * 2;
 #pragma unroll
@@ -1268,12 +1315,12 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                     // row group rg normalizes and rotates query head rg in
                     // place (the other groups compute a copy and keep it);
                     // the loads below then give every group all G heads
-                    float cs[8], sn[8];
-                    rope_angles(nrl, j, (double)positions[rec.z], cs, sn);
+                    angles_at(reinterpret_cast<const int32_t *>(nrl + 1024 + buf * 16), seg_cs,
+                              seg_sn);
                     uint4 *qrow = smem + buf * buf_units + qunit + (rg < G ? rg : 0) * (D / 8);
                     const uint4 v0 = qrow[0], v1 = qrow[8];
                     uint32_t x[2][4] = {{v0.x, v0.y, v0.z, v0.w}, {v1.x, v1.y, v1.z, v1.w}};
-                    norm_rope_row(x, nrl, 0, j, a.eps, cs, sn);
+                    norm_rope_row(x, nrl, 0, j, a.eps, seg_cs, seg_sn);
                     if (rg < G) {
                         qrow[0] = make_uint4(x[0][0], x[0][1], x[0][2], x[0][3]);
                         qrow[8] = make_uint4(x[1][0], x[1][1], x[1][2], x[1][3]);
@@ -1321,9 +1368,8 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                     // transformed row
                     uint32_t kk[2][4] = {{kx[0][0].x, kx[0][0].y, kx[0][0].z, kx[0][0].w},
                                          {kx[0][1].x, kx[0][1].y, kx[0][1].z, kx[0][1].w}};
-                    float cs[8], sn[8];
-                    rope_angles(nrl, j, (double)positions[rec.z], cs, sn);
-                    norm_rope_row(kk, nrl, 1, j, a.eps, cs, sn);
+                    // the segment's angles (the new row belongs to it)
+                    norm_rope_row(kk, nrl, 1, j, a.eps, seg_cs, seg_sn);
                     if (rg == nr) {
                         kx[0][0] = make_uint4(kk[0][0], kk[0][1], kk[0][2], kk[0][3]);
                         kx[0][1] = make_uint4(kk[1][0], kk[1][1], kk[1][2], kk[1][3]);
@@ -1563,8 +1609,11 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             }
         };
         // All tiles but the last; the last one follows on its own, so the
-        // registers of an early merge are live there only.
-        for (int k = 0; k < n - 1; ++k) {
+        // registers of an early merge are live there only (kernels without
+        // the early merge keep one copy of the loop: a second copy of the
+        // tile code costs instruction cache)
+        const int nloop = kEarly ? n - 1 : n;
+        for (int k = 0; k < nloop; ++k) {
             wait_tile(k);
             if constexpr (kEarly) {
                 if (etry2 && k == n - 2) {
@@ -1585,8 +1634,8 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             if (more && k % kSyncTiles == kSyncTiles - 1)
                 __builtin_amdgcn_s_barrier();
         }
-        wait_tile(n - 1);
         if constexpr (kEarly) {
+            wait_tile(n - 1);
             if (etry2) {
                 // the count read a tile ago: every other segment arrived, so
                 // this wave merges, and the partials load during the tile
@@ -1596,8 +1645,8 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                     load_early();
                 }
             }
+            compute_tile(n - 1, std::true_type{});
         }
-        compute_tile(n - 1, std::true_type{});
         // the last stores complete before the wave moves on
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         if (early) {
@@ -1850,7 +1899,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                 uint32_t kk[2][4] = {{kr[0].x, kr[0].y, kr[0].z, kr[0].w},
                                      {kr[1].x, kr[1].y, kr[1].z, kr[1].w}};
                 float cs[8], sn[8];
-                rope_angles(nrl, j, (double)positions[b], cs, sn);
+                angles_at(positions + (int64_t)b * a.pos_stride, cs, sn);
                 norm_rope_row(kk, nrl, 1, j, a.eps, cs, sn);
                 kr[0] = make_uint4(kk[0][0], kk[0][1], kk[0][2], kk[0][3]);
                 kr[1] = make_uint4(kk[1][0], kk[1][1], kk[1][2], kk[1][3]);

@@ -114,9 +114,13 @@ struct RunArgs {
     // appended k row (q_w null: off); see NormRopeArgs for the formulas.
     const uint16_t *q_w;      // [D]
     const uint16_t *k_w;      // [D]
-    const int32_t *positions; // [batch]
+    const int32_t *positions; // [batch], or [batch, 3] (t, h, w) for multimodal RoPE
     float eps;
     double log2_theta;        // log2 of the rotary base
+    int32_t pos_stride;       // 1, or 3 for multimodal RoPE
+    // multimodal RoPE: the position component (0, 1, 2) pair i follows, two
+    // bits per pair, pair i at bit 2 (i % 16) of word i / 16
+    uint32_t axis_bits[4];
 };
 
 // Largest batch the balanced plan handles (its tile prefix sums sit in LDS);

@@ -24,7 +24,7 @@ def test_every_declared_symbol_is_exported():
                           "pkv_decode_workspace_size",
                           "pkv_append_decode", "pkv_decode", "pkv_plan", "pkv_run",
                           "pkv_run_qk_norm_rope", "pkv_decode_static",
-                          "pkv_plan_mixed", "pkv_mixed_run",
+                          "pkv_plan_mixed", "pkv_mixed_run", "pkv_run_qk_norm_mrope",
                           "pkv_validate_page_table", "pkv_status_string",
                           "pkv_last_hip_error"}
     for n in names:
@@ -312,6 +312,25 @@ def test_run_norm_rope_batch_zero_is_noop():
 
 
 AXIS = (ctypes.c_uint8 * 32)(*([0] * 11 + [1] * 11 + [2] * 10))
+AXIS64 = (ctypes.c_uint8 * 64)(*([0] * 24 + [1] * 20 + [2] * 20))
+
+
+def _run_nmr(axis=AXIS64, desc=DESC128, batch=3, hq=8, pos=FAKE, theta=1e6, k=FAKE):
+    return lib.pkv_run_qk_norm_mrope(FAKE, desc, 0, k, FAKE, FAKE, hq, batch, FAKE, FAKE, 1e-6,
+                                     theta, pos, axis, 0.125, FAKE, NULL, 4, 0, NULL, 0, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(axis=None), -1), (dict(axis=(ctypes.c_uint8 * 64)(*([0] * 63 + [3]))), -2),
+    (dict(theta=-1.0), -2), (dict(hq=10), -3), (dict(desc=CacheDesc(2, 64, 16, 2, 64)), -3),
+    (dict(pos=NULL), -1), (dict(k=NULL), -1), (dict(), -4),
+])
+def test_run_norm_mrope_validation(kw, code):
+    assert _run_nmr(**kw) == code
+
+
+def test_run_norm_mrope_batch_zero_is_noop():
+    assert _run_nmr(batch=0, pos=NULL, k=NULL) == 0
 
 
 def _norm_mrope(axis=AXIS, desc=DESC, batch=3, q=FAKE, pos=FAKE, eps=1e-6):

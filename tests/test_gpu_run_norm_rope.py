@@ -66,7 +66,8 @@ def _case(seed, batch, hq, hkv, ps, lo, hi, npad=0, pos_max=None, layers=2):
     return table, cache, lds, qw, kw, positions
 
 
-def _gpu_run(table, cache, ld, qw, kw, positions, hq, theta, eps, chunk, layer, maxp=None):
+def _gpu_run(table, cache, ld, qw, kw, positions, hq, theta, eps, chunk, layer, maxp=None,
+             pair_axis=None):
     cache_dev = to_dev_u16(cache)
     tabs = table_to_dev(table)
     maxp = table.max_pages_per_req if maxp is None else maxp
@@ -75,16 +76,21 @@ def _gpu_run(table, cache, ld, qw, kw, positions, hq, theta, eps, chunk, layer, 
                                     to_dev_u16(ld.k_new), to_dev_u16(ld.v_new),
                                     to_dev_u16(qw), to_dev_u16(kw),
                                     torch.from_numpy(positions).to(DEV), eps=eps,
-                                    rope_theta=theta)
+                                    rope_theta=theta, pair_axis=pair_axis)
     torch.cuda.synchronize()
     return cache_dev, out, lse
 
 
-def _oracle(table, cache, ld, qw, kw, positions, theta, eps, layer):
+def _oracle(table, cache, ld, qw, kw, positions, theta, eps, layer, pair_axis=None):
     host = cache.copy()
-    q_ref, k_ref = oracle.qk_norm_rope_append(host, layer, ld.q, ld.k_new, ld.v_new, qw, kw,
-                                              eps, theta, positions, table.indptr,
-                                              table.indices, table.last_len)
+    if pair_axis is None:
+        q_ref, k_ref = oracle.qk_norm_rope_append(host, layer, ld.q, ld.k_new, ld.v_new, qw, kw,
+                                                  eps, theta, positions, table.indptr,
+                                                  table.indices, table.last_len)
+    else:
+        q_ref, k_ref = oracle.qk_norm_mrope_append(host, layer, ld.q, ld.k_new, ld.v_new, qw,
+                                                   kw, eps, theta, positions, pair_axis,
+                                                   table.indptr, table.indices, table.last_len)
     return host, q_ref, k_ref
 
 
@@ -214,3 +220,64 @@ def test_run_norm_rope_qwen3_4b_batch64():
                                       table.indices, table.last_len, spec.sm_scale, rb, rh)
     ib, ih = torch.from_numpy(rb).to(DEV), torch.from_numpy(rh).to(DEV)
     compare(out[ib, ih], lse[ib, ih], o_ref, l_ref, what="qwen3-4b fused norm/rotary")
+
+
+# Multimodal RoPE folded into the decode (pkv_run_qk_norm_mrope): the
+# Qwen3-Omni Thinker's contiguous 24:20:20 sections of the 64 pairs, an
+# interleaved map and a random one, against the oracle's multimodal step.
+MAPS = {
+    "sections": np.array([0] * 24 + [1] * 20 + [2] * 20, np.uint8),
+    "interleaved": np.arange(64, dtype=np.uint8) % 3,
+    "random": np.random.default_rng(77).integers(0, 3, size=64).astype(np.uint8),
+}
+MSHAPES = [
+    # seed, batch, hq, hkv, ps, lo, hi, npad, chunk
+    (41, 9, 32, 8, 16, 1, 900, 1, 0),      # G 4, balanced, a padding entry
+    (42, 6, 16, 8, 16, 1, 400, 0, 2),      # G 2, fixed runs
+    (43, 30, 32, 8, 16, 1, 3000, 2, 0),    # many split entries
+]
+
+
+def _positions3(rng, table, spread):
+    """(t, h, w) per entry: t the last position, h and w up to `spread` apart."""
+    t = (table.lengths - 1).astype(np.int64)
+    h = t - rng.integers(0, spread + 1, size=len(t))
+    w = t - rng.integers(0, spread + 1, size=len(t))
+    pos = np.stack([t, np.maximum(h, 0), np.maximum(w, 0)], axis=1).astype(np.int32)
+    pos[~table.active] = 0
+    return pos
+
+
+@pytest.mark.parametrize("name", list(MAPS))
+@pytest.mark.parametrize("shape", MSHAPES, ids=[f"s{s[0]}" for s in MSHAPES])
+def test_run_norm_mrope_matches_oracle(shape, name):
+    seed, batch, hq, hkv, ps, lo, hi, npad, chunk = shape
+    axis = MAPS[name]
+    print(f"run_qk_norm_mrope shape {shape} map {name}", flush=True)
+    table, cache, lds, qw, kw, _ = _case(seed, batch, hq, hkv, ps, lo, hi, npad)
+    positions = _positions3(np.random.default_rng(seed + 1000), table, 500)
+    ld = lds[1]
+    cache_dev, out, lse = _gpu_run(table, cache, ld, qw, kw, positions, hq, 1e6, 1e-6, chunk,
+                                   layer=1, pair_axis=axis)
+    host, q_ref, k_ref = _oracle(table, cache, ld, qw, kw, positions, 1e6, 1e-6, layer=1,
+                                 pair_axis=axis)
+    _check_cache(table, to_host_u16(cache_dev), host, k_ref, ld.v_new, 1, f"mrope {seed}")
+    act = np.flatnonzero(table.active)
+    rb, rh = np.repeat(act, hq), np.tile(np.arange(hq), len(act))
+    o_ref, l_ref = oracle.decode_rows(host, 1, oracle.bf16_round(q_ref), table.indptr,
+                                      table.indices, table.last_len, 1.0 / np.sqrt(D), rb, rh)
+    ib, ih = torch.from_numpy(rb).to(DEV), torch.from_numpy(rh).to(DEV)
+    compare(out[ib, ih], lse[ib, ih], o_ref, l_ref, what=f"mrope {seed} {name}")
+
+
+def test_run_norm_mrope_equal_components_is_plain_rope():
+    # t = h = w: the multimodal kernel gives the plain folded kernel's bits
+    table, cache, lds, qw, kw, positions = _case(44, 12, 32, 8, 16, 1, 1200, npad=1)
+    ld = lds[0]
+    pos3 = np.repeat(positions[:, None], 3, axis=1)
+    c1, o1, l1 = _gpu_run(table, cache, ld, qw, kw, positions, 32, 1e6, 1e-6, 0, layer=0)
+    c2, o2, l2 = _gpu_run(table, cache, ld, qw, kw, pos3, 32, 1e6, 1e-6, 0, layer=0,
+                          pair_axis=MAPS["random"])
+    np.testing.assert_array_equal(to_host_u16(c1), to_host_u16(c2))
+    np.testing.assert_array_equal(to_host_u16(o1), to_host_u16(o2))
+    assert torch.equal(l1, l2)
