@@ -36,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores, published
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + decode rows/sec"
 
 
@@ -621,14 +622,20 @@ def bench_prefill(args, torch):
                             if mixed else "pkv_prefill over all entries"),
                    "hip_graph": True},
         "ms_per_step_p10_median_p90": [round(p10, 5), round(p50, 5), round(p90, 5)],
-        "roofline": {"bound": "hbm",
+        # with decode rows the step streams their K/V (HBM-bound); prompts
+        # alone are a dense contraction, priced against the bf16 MFMA peak
+        "roofline": {"bound": "hbm" if nd > 0 else "mfma",
                      "kernel": ("run_kernel + prefill_kernel" if split or mixed
                                 else "prefill_kernel"),
-                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": by,
+                     "achieved": round(gbs, 1) if nd > 0 else round(tflops, 2),
+                     "peak": HBM_PEAK_GBS if nd > 0 else MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "GB/s" if nd > 0 else "TFLOP/s",
+                     "frac": round(gbs / HBM_PEAK_GBS if nd > 0
+                                   else tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "hbm_gbs": round(gbs, 1), "bytes_per_launch": by,
                      "avg_launch_us": round(launch_us, 3),
                      "flops_per_launch": flops, "tflops": round(tflops, 2),
-                     "mfma_bf16_peak_tflops": 2500.0,
+                     "mfma_bf16_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                      "timing": "HIP events between graph replays of the 36-layer step; "
                                "per layer = step / 36 (all launches of the layer)"},
     }
