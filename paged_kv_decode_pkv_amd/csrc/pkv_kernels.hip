@@ -194,13 +194,6 @@ __device__ __forceinline__ void atomic_inc_untracked(int32_t *p, int &old) {
                  : "memory");
 }
 
-// Reads *p at device scope (an atomic add of 0) into `old`, untracked in the
-// same way.
-__device__ __forceinline__ void atomic_read_untracked(int32_t *p, int &old) {
-    asm volatile("global_atomic_add %0, %1, %2, off sc0" : "+v"(old) : "v"(p), "v"(0)
-                 : "memory");
-}
-
 // fp32 -> fp16 (round to nearest even), two values packed low-first, and back.
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
@@ -829,23 +822,6 @@ __device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t r, uint32_t
     }
 }
 
-// The same values into LDS, as store_partial lays them out in memory.
-template <int N>
-__device__ __forceinline__ void store_partial_lds(char *p, const float *v, float s) {
-    if constexpr (N == 8) {
-        *reinterpret_cast<uint4 *>(p) =
-            make_uint4(pack_f16x2(v[0] * s, v[1] * s), pack_f16x2(v[2] * s, v[3] * s),
-                       pack_f16x2(v[4] * s, v[5] * s), pack_f16x2(v[6] * s, v[7] * s));
-    } else if constexpr (N == 4) {
-        *reinterpret_cast<uint2 *>(p) =
-            make_uint2(pack_f16x2(v[0] * s, v[1] * s), pack_f16x2(v[2] * s, v[3] * s));
-    } else if constexpr (N == 2) {
-        *reinterpret_cast<uint32_t *>(p) = pack_f16x2(v[0] * s, v[1] * s);
-    } else {
-        *reinterpret_cast<uint16_t *>(p) = __builtin_bit_cast(uint16_t, (_Float16)(v[0] * s));
-    }
-}
-
 // Maximum over all 64 lanes of a wave; every lane gets it.
 __device__ __forceinline__ float wave_max(float x, int lane) {
     x = fmaxf(x, dpp<0xB1>(x));    // lane ^ 1
@@ -957,12 +933,6 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     constexpr int QB = G * D * 2;              // q bytes of one KV head's query heads
     constexpr int QI = (QB + 1023) / 1024;     // copies for them
     static_assert(NC >= 1 && RPL >= 1 && V >= 1, "unsupported head_dim");
-    // Merges: lane handles UPL units of 8 consecutive outputs of the KV head's
-    // G x D; all of a round's SR segments are loaded at once.
-    constexpr int DU = D / 8;                   // units per query head
-    constexpr int NU = G * DU;
-    constexpr int UPL = (NU + 63) / 64;
-    constexpr int SR = 24 / UPL;
     static_assert(!NR || (D == 128 && LPR == 8), "the fused norm/rotary needs 8 lanes per row");
     // Vector memory stores a segment end issues (outputs and lse): they count
     // in vmcnt like the copies, so the waits below include them.
@@ -1076,19 +1046,6 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     // known to be complete, and old0 keeps what its counter held then.
     int sig_at = -1, old0 = 0;
     bool signaled0 = false;
-    // The block's last tile may end a split segment of an entry E.  Its waves
-    // read E's arrival count a tile before the end; a wave that finds every
-    // other segment of E arrived is E's merger: it loads their partials while
-    // it computes its last tile, keeps its own partial in LDS instead of
-    // writing it out, and merges right after the tile, without the stores,
-    // the count and the loads that would follow it.  That merge is the same
-    // arithmetic in the same order as the merge from memory (one round), so
-    // the result does not depend on which way an entry was merged.
-    constexpr bool kEarly = !NR && UPL == 1 && G * (2 * D + 8) <= kTileTokens * D * 2;
-    constexpr int ES = 16;   // segments an early merge holds in registers
-    bool early = false;
-    float2 elv[ES];
-    uint4 eov[ES];
 
     // Writes this lane's share of a finished segment: the outputs (whole
     // entry) or the partial of slot `slot` (fp16 outputs scaled by 2^-s, and
@@ -1096,7 +1053,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
     // of the lane's flattened [G][NC][8] accumulators; lt[g] is head g's sum
     // of weights.
     auto write_rows = [&](int b, int slot, bool whole, const float (&u)[V],
-                          const float (&lt)[G], char *lds_part) {
+                          const float (&lt)[G]) {
         float inv[G];
 #pragma unroll
         for (int g = 0; g < G; ++g)
@@ -1125,8 +1082,6 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             const int e = ((j + LPR * (k % NC)) << 3) + (f & 7);   // element within the head
             if (whole)
                 store_bf16<N>(a.out + (orow + g) * D + e, v, 1.f);
-            else if (lds_part != nullptr)
-                store_partial_lds<N>(lds_part + (g * D + e) * 2, v, sc);
             else
                 store_partial<N>(ro, ((prow + g) * D + e) * 2, v, sc);
         };
@@ -1151,9 +1106,6 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                 if (whole) {
                     if (a.lse != nullptr)
                         a.lse[orow + g] = lse2 * kLn2;
-                } else if (lds_part != nullptr) {
-                    *reinterpret_cast<float2 *>(lds_part + G * D * 2 + g * 8) =
-                        make_float2(lse2, sexp);
                 } else {
                     store_b64_coherent(rl, (prow + g) * 8, __float_as_uint(lse2),
                                        __float_as_uint(sexp));
@@ -1164,19 +1116,6 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
 
     if (n > 0) {
         auto rec_of = [&](int i) { return blk[1 + min(i, n - 1)]; };
-
-        const int4 lrec = rec_of(n - 1);
-        const bool etry = kEarly && n >= 2 && (lrec.y & kInfoSegLast) != 0 &&
-                          (lrec.y & kInfoSegWhole) == 0;
-        const int4 lent = etry ? ent[lrec.z] : make_int4(0, 0, 0, 0);
-        const bool etry2 = etry && lent.y >= 2 && lent.y <= ES;
-        int32_t *lcnt = a.cnt + (int64_t)lrec.z * a.num_kv_heads + h;
-        // this wave's region of the slot tile n - 2 used (no copy lands there
-        // again): the early merger's own partial, laid out as in memory
-        char *elds = reinterpret_cast<char *>(smem) + (uint32_t)((n + NBUF - 2) % NBUF) * buf_bytes +
-                     (uint32_t)(w * kTileTokens * D * 2);
-        int eseen = 0;
-        uint32_t eops = 0;
 
         // Per-lane byte offsets of this wave's copies: copy i (of IPW per
         // half) moves rows RPI i .. RPI i + RPI - 1 of head w, lane = row
@@ -1284,25 +1223,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
         const int buf_units = (int)(buf_bytes / 16);
         const int qunit = (2 * part_bytes + w * QI * 1024) / 16 + j;
 
-        // the partials of E's segments (this wave's own slot too: its stale
-        // values are never used) into registers
-        auto load_early = [&]() {
-            const int unit = min(lane, NU - 1);
-            const uint32_t row = (uint32_t)lent.x * a.num_qo_heads + hq0 + unit / DU;
-            const uint32_t sl = (uint32_t)a.num_qo_heads * 8;
-            const uint32_t so = (uint32_t)a.num_qo_heads * D * 2;
-#pragma unroll
-            for (int u = 0; u < ES; ++u)
-                if (u < lent.y) {
-                    elv[u] = load_f2_coherent(rl, row * 8 + (uint32_t)u * sl);
-                    eov[u] = load_b128_coherent(ro, (row * D + (unit % DU) * 8) * 2 +
-                                                        (uint32_t)u * so);
-                }
-            ops += 2 * lent.y;
-        };
-
-        auto compute_tile = [&](int k, auto last_c) {
-            constexpr bool kLastTile = decltype(last_c)::value;
+        auto compute_tile = [&](int k) {
             const int buf = k % NBUF;
             const int4 rec = make_int4(__builtin_amdgcn_readlane(ring_x, buf),
                                        __builtin_amdgcn_readlane(ring_y, buf),
@@ -1559,18 +1480,16 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                         u[i] = x2[i];
                 }
                 const bool whole = (info & kInfoSegWhole) != 0;
-                char *lp = kLastTile && early ? elds : nullptr;
-                write_rows(rec.z, rec.w, whole, u, lt, lp);
-                if (lp == nullptr)
-                    ops += whole ? kOutStores + (a.lse != nullptr ? HPR : 0) : kPartStores + HPR;
+                write_rows(rec.z, rec.w, whole, u, lt);
+                ops += whole ? kOutStores + (a.lse != nullptr ? HPR : 0) : kPartStores + HPR;
                 if (!whole) {
                     ++nsplit;
                     // the first split end is pend0, later ones pend1; the
                     // first signals when the copies of tile k + NBUF, issued
                     // after these stores, have landed.  Written as value
-                    // selects: branches would let the compiler merge the
-                    // stores into one through a selected address, which puts
-                    // these variables in scratch memory.
+                    // selects: branches can let the compiler merge the stores
+                    // into one through a selected address, which puts these
+                    // variables in scratch memory.
                     const bool first = pend0 < 0;
                     pend1 = first ? pend1 : rec.z;
                     sig_at = first && k + NBUF < n ? k + NBUF : sig_at;
@@ -1590,9 +1509,9 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                 issue(rec0[t], t);
         }
         int4 rn = rec_of(NBUF);
-        // Tile k has landed once at most the operations issued after its
-        // copies (NBUF - 1 tiles, their q rows, the stores since) remain.
-        auto wait_tile = [&](int k) {
+        for (int k = 0; k < n; ++k) {
+            // tile k has landed: at most the operations issued after its
+            // copies (NBUF - 1 tiles, their q rows, the stores since) remain
             const int after = (int)(ops - (uint32_t)__builtin_amdgcn_readlane(ring_ops, k % NBUF));
             if (after == IPT * (NBUF - 1))
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPT * (NBUF - 1)));
@@ -1607,23 +1526,7 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                 signaled0 = true;
                 ops += 1;
             }
-        };
-        // All tiles but the last; the last one follows on its own, so the
-        // registers of an early merge are live there only (kernels without
-        // the early merge keep one copy of the loop: a second copy of the
-        // tile code costs instruction cache)
-        const int nloop = kEarly ? n - 1 : n;
-        for (int k = 0; k < nloop; ++k) {
-            wait_tile(k);
-            if constexpr (kEarly) {
-                if (etry2 && k == n - 2) {
-                    if (lane == 0)
-                        atomic_read_untracked(lcnt, eseen);
-                    ops += 1;
-                    eops = ops;
-                }
-            }
-            compute_tile(k, std::false_type{});
+            compute_tile(k);
             const bool more = k + NBUF < n;   // uniform: the waves share the block
             if (more)
                 issue(rn, k % NBUF);
@@ -1634,64 +1537,8 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             if (more && k % kSyncTiles == kSyncTiles - 1)
                 __builtin_amdgcn_s_barrier();
         }
-        if constexpr (kEarly) {
-            wait_tile(n - 1);
-            if (etry2) {
-                // the count read a tile ago: every other segment arrived, so
-                // this wave merges, and the partials load during the tile
-                wait_vm_at_most<kMaxVmWait>((int)(ops - eops));
-                if (__builtin_amdgcn_readlane(eseen, 0) == lent.y - 1) {
-                    early = true;
-                    load_early();
-                }
-            }
-            compute_tile(n - 1, std::true_type{});
-        }
         // the last stores complete before the wave moves on
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        if (early) {
-            const int own = lrec.w - lent.x;   // this wave's segment among E's
-            const int unit = min(lane, NU - 1);
-            const int gq = unit / DU;
-            const uint4 xo = *reinterpret_cast<const uint4 *>(elds + (gq * D + (unit % DU) * 8) * 2);
-            const float2 lo2 = *reinterpret_cast<const float2 *>(elds + G * D * 2 + gq * 8);
-            float mr = kMInit;
-#pragma unroll
-            for (int u = 0; u < ES; ++u)
-                if (u < lent.y)
-                    mr = fmaxf(mr, u == own ? lo2.x : elv[u].x);
-            float zs = 0.f, o[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                o[q] = 0.f;
-#pragma unroll
-            for (int u = 0; u < ES; ++u) {
-                if (u >= lent.y)
-                    continue;
-                const float2 lv = u == own ? lo2 : elv[u];
-                const uint4 v = u == own ? xo : eov[u];
-                zs += exp2_fast(lv.x - mr);
-                const float wo = exp2_fast(lv.x + lv.y - mr);
-                const float x[8] = {f16_lo(v.x), f16_hi(v.x), f16_lo(v.y), f16_hi(v.y),
-                                    f16_lo(v.z), f16_hi(v.z), f16_lo(v.w), f16_hi(v.w)};
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    o[q] = fmaf(wo, x[q], o[q]);
-            }
-            if (lane < NU) {
-                const int64_t orow = (int64_t)lrec.z * a.num_qo_heads + hq0 + gq;
-                store_bf16<8>(a.out + orow * D + (unit % DU) * 8, o, 1.f / zs);
-                if (a.lse != nullptr && unit % DU == 0)
-                    a.lse[orow] = (mr + log2_fast(zs)) * kLn2;
-            }
-            if (lane == 0)
-                __hip_atomic_store(lcnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            // E's segment is merged: the arrivals below leave it out (value
-            // selects, as above)
-            const bool only = nsplit == 1;
-            pend0 = only ? -1 : pend0;
-            pend1 = only ? pend1 : -1;
-        }
     }
 
     // Split entries: count this wave's remaining partials in; the last of an
@@ -1713,65 +1560,18 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                                          __HIP_MEMORY_SCOPE_AGENT);
         const int arr0 = __builtin_amdgcn_readlane(signaled0 ? old0 : old, 0);
         const int arr1 = __builtin_amdgcn_readlane(old, 1);
+        // Merge: lane handles UPL units of 8 consecutive outputs of the KV
+        // head's G x D; all of a round's SR segments are loaded at once.
+        constexpr int DU = D / 8;                   // units per query head
+        constexpr int NU = G * DU;
+        constexpr int UPL = (NU + 63) / 64;
+        constexpr int SR = 24 / UPL;
         // The entries this wave arrived last for are merged one after the
-        // other: pend0, pend1, then, in a block that ended more than two
-        // split segments (fixed runs dealt several to a workgroup), the ones
-        // between, found from the block's records one lane per record, 64
-        // at a time, their arrivals counted together.
-        int stage = 0;             // 0: pend0, 1: pend1, 2: the segments between
-        int k0 = 0, idx_base = 0;  // next record round, split ends before it
-        uint64_t todo = 0;         // lanes of the round whose entry to merge
-        int rz = 0;                // per lane: the record's entry
-        int4 rem = make_int4(0, 0, 0, 0);   // and its descriptor
-        for (;;) {
-            int b;
-            int4 e;
-            int32_t *cp;
-            if (stage == 0) {
-                stage = 1;
-                if (arr0 != ent0.y - 1)
-                    continue;
-                b = pend0;
-                e = ent0;
-                cp = cnt0;
-            } else if (stage == 1) {
-                stage = 2;
-                if (pend1 < 0 || arr1 != ent1.y - 1)
-                    continue;
-                b = pend1;
-                e = ent1;
-                cp = cnt1;
-            } else {
-                while (todo == 0 && nsplit > 2 && k0 < n) {
-                    const int k = k0 + lane;
-                    k0 += 64;
-                    const int4 rec = k < n ? blk[1 + k] : make_int4(0, 0, 0, 0);
-                    const bool split_end =
-                        k < n && (rec.y & kInfoSegLast) != 0 && (rec.y & kInfoSegWhole) == 0;
-                    const uint64_t m = __builtin_amdgcn_ballot_w64(split_end);
-                    const int idx =
-                        idx_base + __builtin_popcountll(m & ((1ull << lane) - 1ull));
-                    idx_base += __builtin_popcountll(m);
-                    const bool mine = split_end && idx >= 1 && idx <= nsplit - 2;
-                    int oldm = -1;
-                    rz = rec.z;
-                    if (mine) {
-                        rem = ent[rec.z];
-                        oldm = __hip_atomic_fetch_add(a.cnt + (int64_t)rec.z * a.num_kv_heads + h,
-                                                      1, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                    todo = __builtin_amdgcn_ballot_w64(mine && oldm == rem.y - 1);
-                }
-                if (todo == 0)
-                    break;
-                const int l = __builtin_ctzll(todo);
-                todo &= todo - 1;
-                b = __builtin_amdgcn_readlane(rz, l);
-                e = make_int4(__builtin_amdgcn_readlane(rem.x, l),
-                              __builtin_amdgcn_readlane(rem.y, l), 0, 0);
-                cp = a.cnt + (int64_t)b * a.num_kv_heads + h;
-            }
+        // other: pend0, pend1 (each merge in line), then, in a block that
+        // ended more than two split segments (fixed runs dealt several to a
+        // workgroup), the ones between, found from the block's records one
+        // lane per record, 64 at a time, their arrivals counted together.
+        auto merge_entry = [&](const int b, const int4 e, int32_t *cp) {
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             const int ns = e.y;
             uint32_t lo[UPL], oo[UPL];   // byte offsets in slot e.x: lse pair, outputs
@@ -1806,23 +1606,6 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                         }
                     }
                 }
-                // the round's maximum first, so the sums are rescaled once
-                // a round and a segment costs two exponentials and its
-                // products
-#pragma unroll
-                for (int i = 0; i < UPL; ++i) {
-                    float mr = mm[i];
-#pragma unroll
-                    for (int u = 0; u < SR; ++u)
-                        if (s0 + u < ns)
-                            mr = fmaxf(mr, lv[u][i].x);
-                    const float al = exp2_fast(mm[i] - mr);
-                    zs[i] *= al;
-#pragma unroll
-                    for (int q = 0; q < 8; ++q)
-                        o[i][q] *= al;
-                    mm[i] = mr;
-                }
 #pragma unroll
                 for (int u = 0; u < SR; ++u) {
                     if (s0 + u >= ns)   // wave-uniform: absent segments cost nothing
@@ -1832,14 +1615,18 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
                         // weight of the segment: 2^(lse - m); its stored
                         // outputs carry a further factor 2^-s
                         const float l2 = lv[u][i].x;
-                        zs[i] += exp2_fast(l2 - mm[i]);
-                        const float wo = exp2_fast(l2 + lv[u][i].y - mm[i]);
+                        const float mn = fmaxf(mm[i], l2);
+                        const float al = exp2_fast(mm[i] - mn);
+                        const float wz = exp2_fast(l2 - mn);
+                        const float wo = exp2_fast(l2 + lv[u][i].y - mn);
+                        zs[i] = fmaf(zs[i], al, wz);
                         const uint4 v = ov[u][i];
                         const float x[8] = {f16_lo(v.x), f16_hi(v.x), f16_lo(v.y), f16_hi(v.y),
                                             f16_lo(v.z), f16_hi(v.z), f16_lo(v.w), f16_hi(v.w)};
 #pragma unroll
                         for (int q = 0; q < 8; ++q)
-                            o[i][q] = fmaf(wo, x[q], o[i][q]);
+                            o[i][q] = fmaf(wo, x[q], o[i][q] * al);
+                        mm[i] = mn;
                     }
                 }
             }
@@ -1857,6 +1644,41 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * 64) void run_kernel(
             }
             if (lane == 0)
                 __hip_atomic_store(cp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        if (arr0 == ent0.y - 1)
+            merge_entry(pend0, ent0, cnt0);
+        if (pend1 >= 0 && arr1 == ent1.y - 1)
+            merge_entry(pend1, ent1, cnt1);
+        if (nsplit > 2) {
+            int idx_base = 0;   // split ends before the current round
+            for (int k0 = 0; k0 < n; k0 += 64) {
+                const int k = k0 + lane;
+                const int4 rec = k < n ? blk[1 + k] : make_int4(0, 0, 0, 0);
+                const bool split_end =
+                    k < n && (rec.y & kInfoSegLast) != 0 && (rec.y & kInfoSegWhole) == 0;
+                const uint64_t m = __builtin_amdgcn_ballot_w64(split_end);
+                const int idx = idx_base + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+                idx_base += __builtin_popcountll(m);
+                const bool mine = split_end && idx >= 1 && idx <= nsplit - 2;
+                int oldm = -1;
+                int4 rem = make_int4(0, 0, 0, 0);
+                if (mine) {
+                    rem = ent[rec.z];
+                    oldm = __hip_atomic_fetch_add(a.cnt + (int64_t)rec.z * a.num_kv_heads + h, 1,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                uint64_t todo = __builtin_amdgcn_ballot_w64(mine && oldm == rem.y - 1);
+                while (todo != 0) {
+                    const int l = __builtin_ctzll(todo);
+                    todo &= todo - 1;
+                    const int b = __builtin_amdgcn_readlane(rec.z, l);
+                    const int4 e = make_int4(__builtin_amdgcn_readlane(rem.x, l),
+                                             __builtin_amdgcn_readlane(rem.y, l), 0, 0);
+                    merge_entry(b, e, a.cnt + (int64_t)b * a.num_kv_heads + h);
+                }
+                if (idx_base >= nsplit - 1)
+                    break;   // every split end between has been seen
+            }
         }
     }
 
