@@ -44,8 +44,8 @@
 //
 // Each chain stages its token tiles through a ring of three LDS slots with
 // direct-to-LDS copies (global_load_lds_dwordx4, 1 KiB a copy), so no
-// registers hold tiles in flight; the page ids of a tile go ahead of it into
-// a slot of their own the same way.  Rows sit unpadded in LDS with their
+// registers hold tiles in flight; a tile read from cached pages has its page
+// ids read a step ahead by scalar loads.  Rows sit unpadded in LDS with their
 // 16-byte chunks permuted by an XOR of the row index, chosen so that the
 // operand reads of a wave (K rows, and the transposed V reads) meet distinct
 // banks.  New rows are read from k_new / v_new, and the workgroups of an
@@ -350,12 +350,6 @@ __device__ __forceinline__ void tile_pair(const PrefillArgs &a, const int b, con
     typedef __attribute__((address_space(4))) const int32_t const_i32;
     const const_i32 *pages_s = (const const_i32 *)(pages);   // scalar loads of the same ids
     typedef int PageIds[CPW];   // page id of each copy's first row (scalar registers)
-    auto load_pages = [&](int s, PageIds &pg) {
-        const int t0 = tok_tile(s) * kTileTok;
-#pragma unroll
-        for (int i = 0; i < CPW; ++i)
-            pg[i] = pages_s[min(t0 + RPC * (w4 + 4 * i), len - 1) >> a.page_shift];
-    };
     auto page_base = [&](int page, int tok0) {   // first element of token tok0's row (head h)
         const int pg = (uint32_t)page < (uint32_t)a.num_pages ? page : 0;   // bad id: no fault
         return (int64_t)pg * a.page_stride + (int64_t)(tok0 & pmask) * a.row_stride + h * D;
@@ -380,6 +374,16 @@ __device__ __forceinline__ void tile_pair(const PrefillArgs &a, const int b, con
         if (big_pages && (!fresh || t0 + kTileTok <= base_pos))
             return (int)kCached;
         return (int)kEdge;
+    };
+    // only a cached tile takes its rows' pages from these ids (the others
+    // read none, or look them up per lane)
+    auto load_pages = [&](int s, PageIds &pg) {
+        const int t0 = tok_tile(s) * kTileTok;
+        if (tile_mode(t0) != kCached)
+            return;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i)
+            pg[i] = pages_s[min(t0 + RPC * (w4 + 4 * i), len - 1) >> a.page_shift];
     };
     auto issue_kv = [&](int s, const PageIds &pg) {
         const int t0 = tok_tile(s) * kTileTok;
@@ -453,11 +457,14 @@ __device__ __forceinline__ void tile_pair(const PrefillArgs &a, const int b, con
     auto qk = [&](int s, Scores &sc) {
         const char *kb = ring + slot_of(s);
         bf16x8_t ka[2][DC];
+        // every operand read goes out before the first product, in the order
+        // the products take them, so a product waits only for its own reads
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+        for (int dc = 0; dc < DC; ++dc)
 #pragma unroll
-            for (int dc = 0; dc < DC; ++dc)
+            for (int tb = 0; tb < 2; ++tb)
                 ka[tb][dc] = as_bf16x8(*reinterpret_cast<const uint4 *>(kb + 16 * tb * RB + koff(dc)));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -525,47 +532,49 @@ __device__ __forceinline__ void tile_pair(const PrefillArgs &a, const int b, con
     // product three behind its first).
     auto pv = [&](int s, const Weights &phi, const Weights &plo) {
         const char *vb = ring + slot_of(s) + Gm::TILE;
+        bf16x8_t va[DB];
+        // all operand reads first (as in qk)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t *)(vb + voff(db)));
+            const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t *)(vb + voff(db) + 16 * RB));
+            va[db] = __builtin_bit_cast(
+                bf16x8_t,
+                u32x4_t{__builtin_bit_cast(uint2, v0).x, __builtin_bit_cast(uint2, v0).y,
+                        __builtin_bit_cast(uint2, v1).x, __builtin_bit_cast(uint2, v1).y});
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < DB; db += 2) {
-            bf16x8_t va[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4_t *)(vb + voff(db + u)));
-                const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4_t *)(vb + voff(db + u) + 16 * RB));
-                va[u] = __builtin_bit_cast(
-                    bf16x8_t,
-                    u32x4_t{__builtin_bit_cast(uint2, v0).x, __builtin_bit_cast(uint2, v0).y,
-                            __builtin_bit_cast(uint2, v1).x, __builtin_bit_cast(uint2, v1).y});
-            }
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb)
-                    o[cb][db + u] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], phi[cb], o[cb][db + u], 0, 0, 0);
+                    o[cb][db + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db + u], phi[cb],
+                                                                            o[cb][db + u], 0, 0, 0);
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb)
-                    o[cb][db + u] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], plo[cb], o[cb][db + u], 0, 0, 0);
+                    o[cb][db + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db + u], plo[cb],
+                                                                            o[cb][db + u], 0, 0, 0);
         }
     };
     auto visible = [&](int s) { return tok_tile(s) * kTileTok <= wmax; };
     auto masked = [&](int s) { return tok_tile(s) * kTileTok + kTileTok - 1 > wmin; };
 
-    // ---- the walk.  The two waves on a SIMD (one of each chain) alternate
-    // between vector and matrix work, phase by phase, with a barrier between
-    // phases:
-    //   phase 2s:      A: copies of step s + 2, softmax(s)   B: pv(s - 1), qk(s)
-    //   phase 2s + 1:  A: pv(s), qk(s + 1)                   B: copies of step s + 2, softmax(s)
-    // so the matrix products of one run under the other's vector work.  A
-    // wave waits for a tile's rows before the barrier of the phase whose
-    // products read them; at most the copies issued after them (one step's)
-    // may still be outstanding (the append's loads went out before every
-    // copy; its stores, at step 1, only make later waits longer).
+    // ---- the walk: one barrier per step.  At step s a wave waits for its
+    // chain's tile s (the copies issued after it, one step's, may still be
+    // outstanding), then meets the barrier, after which tile s is in LDS for
+    // every wave and no wave still reads tile s - 1, whose slot takes the
+    // copies of tile s + 2; then it runs qk, softmax and pv of tile s.  The
+    // vector and matrix work of the two waves on a SIMD interleave as they
+    // come: on gfx950 the matrix products of one wave hide little of the
+    // other's vector work, so a fixed alternation between them would buy
+    // nothing and cost a second barrier per step.  The append's loads go out
+    // before every copy; its stores, at step 1, only make later waits longer.
     // The append: the workgroups of an (entry, KV head) share its new rows,
     // up to four 16-byte chunks per thread; the loads go out before the
     // walk's copies and the stores early in the walk.
@@ -609,7 +618,7 @@ __device__ __forceinline__ void tile_pair(const PrefillArgs &a, const int b, con
         ap3 = job_page(tid + 3 * kThreads);
     }
 
-    PageIds pg0, pg1, pg2;   // page ids of steps s, s + 1, s + 2
+    PageIds pg0 = {}, pg1 = {}, pg2 = {};   // page ids of steps s, s + 1, s + 2
     if (0 < my_len)
         load_pages(0, pg0);
     if (1 < my_len)
@@ -648,9 +657,7 @@ __device__ __forceinline__ void tile_pair(const PrefillArgs &a, const int b, con
         else
             softmax(Plain{}, t0, sc, phi, plo);
     };
-    // Each chain runs its own loop over steps (two phases each); both loops
-    // meet the same barriers, one per phase.
-    const int steps2 = max(lenA, nB + 1);   // steps of the longer timeline
+    const int steps = max(lenA, nB);   // steps of the longer chain
     // the append's stores go out at step 1 (by every wave), to run under the
     // rest of the walk: the compiler waits there for their loads, which
     // drains the copies then in flight once
@@ -662,65 +669,31 @@ __device__ __forceinline__ void tile_pair(const PrefillArgs &a, const int b, con
         for (int job = tid + 4 * kThreads; job < jobs; job += kThreads)
             job_store(job, job_page(job), *job_src(job));
     };
-    if (chain == 0) {
-        Scores sc;   // scores of the step's tile, from the previous phase
-        if (0 < lenA)
-            wait_rows(1 < lenA);
+    for (int s = 0; s < steps; ++s) {
+        if (s < my_len)
+            wait_rows(s + 1 < my_len);   // tile s
         __syncthreads();
-        if (0 < lenA && visible(0))
-            qk(0, sc);
-        for (int s = 0; s < steps2; ++s) {
-            // phase 2s: copies, softmax(s)
-            __syncthreads();
-            if (s == 1)
-                append_stores();
-            Weights phi, plo;
-            if (s < lenA) {
-                issue_step(s);
-                softmax_step(s, sc, phi, plo);
-            }
-            // phase 2s + 1: pv(s), qk(s + 1)
-            if (s + 1 < lenA)
-                wait_rows(s + 2 < lenA);   // tile s + 1, for qk(s + 1)
-            __syncthreads();
-            if (s < lenA) {
-                if (visible(s))
-                    pv(s, phi, plo);
-                if (a_switch && s + 1 == nA1) {
-                    // chain A moves from its own column tile to the pair's other one
-                    finalize();
-                    switch_columns();
-                }
-                if (s + 1 < lenA && visible(s + 1))
-                    qk(s + 1, sc);
-            }
-        }
-    } else {
-        Weights phi, plo;   // the P^T operands of the previous step, for its pv
-        __syncthreads();
-        for (int s = 0; s < steps2; ++s) {
-            // phase 2s: pv(s - 1), qk(s)
-            if (s < nB)
-                wait_rows(s + 1 < nB);   // tile s, for qk(s)
-            __syncthreads();
-            if (s == 1)
-                append_stores();
-            Scores sc;
-            if (s >= 1 && s - 1 < nB && visible(s - 1))
-                pv(s - 1, phi, plo);
-            if (s < nB && visible(s))
+        if (s == 1)
+            append_stores();
+        if (s < my_len) {
+            issue_step(s);
+            if (visible(s)) {
+                Scores sc;
+                Weights phi, plo;
                 qk(s, sc);
-            // phase 2s + 1: copies, softmax(s)
-            __syncthreads();
-            if (s < nB) {
-                issue_step(s);
                 softmax_step(s, sc, phi, plo);
+                pv(s, phi, plo);
+            }
+            if (a_switch && s + 1 == nA1) {
+                // chain A moves from its own column tile to the pair's other one
+                finalize();
+                switch_columns();
             }
         }
     }
     __syncthreads();
 
-    if (steps2 < 2)
+    if (steps < 2)
         append_stores();
 
     if (!merge) {
