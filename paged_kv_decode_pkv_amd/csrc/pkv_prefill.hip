@@ -29,8 +29,9 @@
 // 8 bytes that lane 4 e + i / 4 addressed, so four lanes addressing four
 // consecutive d of one token row give lane i four tokens of one d.  The
 // online softmax of a column stays within its four lanes.  P goes in as a
-// bf16 high part and a bf16 remainder (two products): a single bf16 P is off
-// by up to half a bf16 step of the output, the whole parity bar.
+// bf16 high part and a bf16 remainder (two products): with a single bf16 P
+// some outputs of unit-variance inputs already miss the per-element bar
+// (half a bf16 step of the output plus 1e-3).
 //
 // Balance.  Column tile j of an entry needs about j + 1 token tiles (its
 // rows' prefixes grow with j), so a workgroup of eight waves takes the pair
